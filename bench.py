@@ -1,0 +1,230 @@
+"""Benchmark of the mixed-adapter LoRA training step on one MI355X.
+
+One step = one pass of the hot path over a Qwen3-8B-width q/o projection
+(4096 -> 4096, bf16, fp32 accumulate): 16 rank-32 adapters (alpha 32) over
+8192 tokens in sorted 512-token segments; segment build, base GEMM + shrink +
+expand forward, base GEMM + adapter-gradient reductions + expand backward, and
+one AdamW step per adapter (lr 1e-4, betas 0.9/0.999, eps 1e-8) writing the
+bf16 copy the next forward reads.  Inputs are seeded synthetic data resident in
+HBM before timing; four rotated copies of (x, dY) keep the 256 MB Infinity
+Cache from serving repeat reads.
+
+Prints ONE JSON line on stdout.  `value` = tokens/s of the whole step.
+`roofline` is for the dominant kernel (the base GEMM), timed live with HIP
+events recorded by the library around each of its launches inside the timed
+steps.  `cpu_baseline` times the oracle (NumPy float64) on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+METRIC = "tokens/s mixed-adapter LoRA fwd+bwd at 8B shapes; % MFMA / HBM peak"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--tokens", type=int, default=8192)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target wall time of the oracle sample")
+    return ap.parse_args()
+
+
+def cpu_baseline(case, target_s):
+    """Time the oracle's forward + backward (+ Adam prorated) on the host."""
+    import numpy as np
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    import oracle.adam as OA
+    import oracle.lora as OL
+
+    x = case.x()
+    Wb = case.W()
+    dy = case.dy()
+    A = [case.A(i) for i in range(case.n_adapters)]
+    B = [case.B(i) for i in range(case.n_adapters)]
+    s = case.scales
+    # sample: whole adapters' segments (gradients need every token of an adapter)
+    per = case.n_tokens // case.n_adapters
+    n_ad_sample = case.n_adapters
+    t_layer = 0.0
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        a = reps % case.n_adapters
+        rows = np.nonzero(case.ids == a)[0]
+        ts = time.perf_counter()
+        y, u = OL.lora_forward(x[rows], Wb, A, B, s, case.ids[rows])
+        OL.lora_backward(dy[rows], x[rows], Wb, A, B, s, case.ids[rows])
+        t_layer += time.perf_counter() - ts
+        reps += 1
+        if time.perf_counter() - t0 > target_s or reps >= 4 * n_ad_sample:
+            break
+    tokens_done = reps * per
+    # Adam for one adapter, prorated per token
+    r0, r1 = case.adapter_range(0)
+    n_par = r1 - r0
+    g = np.random.default_rng(0).standard_normal(n_par)
+    ts = time.perf_counter()
+    OA.adam_step(np.zeros(n_par), g, np.zeros(n_par), np.zeros(n_par), 1, 1e-4)
+    t_adam_one = time.perf_counter() - ts
+    t_adam_per_token = t_adam_one * case.n_adapters / case.n_tokens
+    tps = tokens_done / (t_layer + t_adam_per_token * tokens_done)
+    return {"value": tps, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{reps} adapter segments x {per} tokens of the same workload "
+                      f"(fp64 NumPy fwd+bwd, {t_layer:.1f} s) + one adapter's AdamW prorated per token"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); every box here has "
+              "one MI355X, and the multi-GPU path is a design (DESIGN.md), not a measured run.",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import rl_lora_linear_amd.lib as L
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"[bench] generating inputs ({args.tokens} tokens)")
+    case = W.attn_proj(seed=2, n_tokens=args.tokens)
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from gpu_util import DevLayer, dev_bf16
+
+    dl = DevLayer(case)
+    N, d_in, d_out = case.n_tokens, case.d_in, case.d_out
+    n_ad = case.n_adapters
+    # rotated input sets
+    sets = []
+    for k in range(4):
+        xs = torch.roll(dl.x, shifts=k * 97, dims=0).contiguous()
+        dys = torch.roll(dl.dy, shifts=k * 89, dims=0).contiguous()
+        sets.append((xs, dys))
+    y = torch.empty((N, d_out), dtype=torch.bfloat16, device=dev)
+    u = torch.empty((N, dl.max_rank), dtype=torch.float32, device=dev)
+    dx = torch.empty((N, d_in), dtype=torch.bfloat16, device=dev)
+    grad = torch.zeros(case.pack_elems, dtype=torch.float32, device=dev)
+    master = dl.pack.float().clone()
+    m = torch.zeros_like(master)
+    v = torch.zeros_like(master)
+    ranges = [case.adapter_range(i) for i in range(n_ad)]
+    steps_done = [0]
+
+    def step(k):
+        xs, dys = sets[k % len(sets)]
+        L.lora_forward(dl.shape, xs, dl.W, dl.pack, dl.pack, dl.desc, dl.ids, y, u, dl.ws)
+        L.lora_backward(dl.shape, dys, xs, dl.Wt, dl.pack, dl.pack, dl.desc, dl.ids, u, dx, grad,
+                        grad, 0, dl.ws)
+        t = steps_done[0] + 1
+        for (a0, a1) in ranges:
+            L.adam_step(master[a0:a1], grad[a0:a1], m[a0:a1], v[a0:a1], t, 1e-4, 0.9, 0.999, 1e-8,
+                        0.0, dl.pack[a0:a1])
+        steps_done[0] = t
+
+    log(f"[bench] warmup {args.warmup}")
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    flags = L.lora_device_status(dl.ws)
+    if flags:
+        raise RuntimeError(f"device status flags {flags:#x}")
+
+    L.lora_timing_reset()
+    L.lora_timing_enable(True)
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(k)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    L.lora_timing_enable(False)
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    tokens_s = N / (ms_step / 1e3)
+
+    timers = {}
+    for name, tid in (("base_gemm", L.TIMER_BASE_GEMM), ("shrink", L.TIMER_SHRINK),
+                      ("expand", L.TIMER_EXPAND), ("grad", L.TIMER_GRAD), ("adam", L.TIMER_ADAM)):
+        tot, cnt = L.lora_timing_read(tid)
+        timers[name] = (tot, cnt)
+    gemm_ms, gemm_n = timers["base_gemm"]
+    gemm_avg_ms = gemm_ms / max(gemm_n, 1)
+    gemm_flops = 2.0 * N * d_in * d_out
+    achieved = gemm_flops / (gemm_avg_ms / 1e3) / 1e12
+
+    # algorithmic bytes of the HBM-bound kernels (per launch)
+    r = int(case.ranks[0])
+    shrink_bytes = (N * d_in * 2 + n_ad * r * d_in * 2 + N * dl.max_rank * 4)
+    expand_bytes = (2 * N * d_out * 2 + n_ad * d_out * r * 2 + N * dl.max_rank * 4)
+    grad_bytes = (N * d_out * 2 + N * dl.max_rank * 4 + n_ad * d_out * r * 4) + \
+                 (N * d_in * 2 + N * dl.max_rank * 4 + n_ad * r * d_in * 4)
+    adam_bytes = 28 * (ranges[0][1] - ranges[0][0])
+
+    def kentry(name, bytes_per_launch, launches_per_step):
+        tot, cnt = timers[name]
+        avg = tot / max(cnt, 1)
+        gbs = bytes_per_launch / (avg / 1e3) / 1e9 if avg > 0 else 0.0
+        return {"avg_ms": round(avg, 5), "launches": cnt, "bytes_per_launch": int(bytes_per_launch),
+                "GB_s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+
+    kernels = {
+        "base_gemm": {"avg_ms": round(gemm_avg_ms, 5), "launches": gemm_n,
+                      "TFLOP_s": round(achieved, 1), "frac_mfma": round(achieved / PEAK_BF16_TFLOPS, 4)},
+        "shrink": kentry("shrink", shrink_bytes, 2),
+        "expand": kentry("expand", expand_bytes, 2),
+        "grad_dA_dB": kentry("grad", grad_bytes, 1),
+        "adam_per_adapter": kentry("adam", adam_bytes, n_ad),
+    }
+    out = {
+        "metric": METRIC,
+        "value": round(tokens_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; random-init Qwen3-8B-width projection and adapters)",
+        "config": {"workload": "qwen3-8b q/o projection 4096->4096, 16 adapters rank 32 alpha 32, "
+                               f"{N} tokens (16 sorted segments), fwd+bwd+AdamW",
+                   "tokens": N, "d_in": d_in, "d_out": d_out, "adapters": n_ad, "rank": r},
+        "roofline": {"bound": "mfma", "kernel": "base GEMM (y = x W^T and dx = dy W, bf16 MFMA)",
+                     "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle)")
+        out["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

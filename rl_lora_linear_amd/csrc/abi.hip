@@ -1,0 +1,497 @@
+// C-ABI entry points: host-side validation, workspace carving and the launch
+// sequence of each call.  All work is enqueued on the caller's stream.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <cmath>
+#include <string>
+#include <vector>
+
+#include "common.hpp"
+#include "segments.hpp"
+#include "sgmv.hpp"
+
+// ------------------------------------------------------------------ errors
+namespace lora_host {
+
+static thread_local std::string g_err;
+
+void set_error(const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+}
+
+lora_status hip_check(hipError_t e, const char* what) {
+  if (e == hipSuccess) return LORA_OK;
+  set_error("%s: %s", what, hipGetErrorString(e));
+  return LORA_E_HIP;
+}
+
+lora_status launch_check(const char* what) { return hip_check(hipGetLastError(), what); }
+
+// ------------------------------------------------------------------ timing
+struct TimerState {
+  bool on = false;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> pairs[LORA_TIMER_COUNT];
+  size_t used[LORA_TIMER_COUNT] = {};
+};
+static TimerState g_tim;
+
+void timer_begin(int timer, hipStream_t s) {
+  if (!g_tim.on) return;
+  auto& v = g_tim.pairs[timer];
+  size_t& u = g_tim.used[timer];
+  if (u == v.size()) {
+    hipEvent_t a, b;
+    if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) return;
+    v.emplace_back(a, b);
+  }
+  hipEventRecord(v[u].first, s);
+}
+
+void timer_end(int timer, hipStream_t s) {
+  if (!g_tim.on) return;
+  auto& v = g_tim.pairs[timer];
+  size_t& u = g_tim.used[timer];
+  if (u >= v.size()) return;
+  hipEventRecord(v[u].second, s);
+  ++u;
+}
+
+}  // namespace lora_host
+
+using namespace lora_host;
+using lora::cdiv;
+
+static inline hipStream_t S(void* p) { return (hipStream_t)p; }
+
+#define TRY(expr)                  \
+  do {                             \
+    lora_status _st = (expr);      \
+    if (_st != LORA_OK) return _st; \
+  } while (0)
+
+// ------------------------------------------------------------------ layer workspace
+namespace {
+
+constexpr int kTmShrink = 16;
+constexpr int kTmExpand = 64;
+
+struct LayerWs {
+  char* seg;          // status word + segment scratch
+  size_t seg_bytes;
+  int32_t* perm;
+  int32_t* offsets;
+  uint8_t* active;
+  int32_t* pre16;
+  int32_t* pre64;
+  int32_t* prec;
+  uint16_t* AT;
+  uint16_t* BT;
+  float* v;
+  float* partial;
+  size_t total;
+};
+
+LayerWs carve_layer(const lora_shape& sh, void* ws, size_t bytes) {
+  Carve cv(ws, bytes);
+  LayerWs w{};
+  w.seg_bytes = segments_ws_bytes(sh.n_tokens, sh.n_adapters);
+  w.seg = cv.take<char>(w.seg_bytes);
+  w.perm = cv.take<int32_t>((size_t)std::max<int64_t>(sh.n_tokens, 1));
+  w.offsets = cv.take<int32_t>((size_t)sh.n_adapters + 1);
+  w.active = cv.take<uint8_t>((size_t)sh.n_adapters);
+  w.pre16 = cv.take<int32_t>((size_t)sh.n_adapters + 1);
+  w.pre64 = cv.take<int32_t>((size_t)sh.n_adapters + 1);
+  w.prec = cv.take<int32_t>((size_t)sh.n_adapters + 1);
+  w.AT = cv.take<uint16_t>((size_t)sh.a_pack_elems);
+  w.BT = cv.take<uint16_t>((size_t)sh.b_pack_elems);
+  w.v = cv.take<float>((size_t)std::max<int64_t>(sh.n_tokens, 1) * sh.max_rank);
+  w.partial = cv.take<float>((size_t)grad_partial_floats(sh.n_tokens, sh.n_adapters,
+                                                         std::max(sh.d_in, sh.d_out), sh.max_rank));
+  w.total = cv.used;
+  return w;
+}
+
+lora_status check_shape(const lora_shape* sh) {
+  LORA_ARG_CHECK(sh != nullptr, "shape is NULL");
+  LORA_ARG_CHECK(sh->n_tokens >= 0 && sh->n_tokens <= INT32_MAX / 2,
+                 "n_tokens %lld outside [0, 2^30)", (long long)sh->n_tokens);
+  LORA_ARG_CHECK(sh->d_in > 0 && sh->d_out > 0, "d_in and d_out must be positive");
+  LORA_ARG_CHECK(sh->n_adapters >= 1 && sh->n_adapters <= 16384, "n_adapters %d outside [1, 16384]",
+                 sh->n_adapters);
+  LORA_ARG_CHECK(sh->max_rank >= 8 && sh->max_rank <= 64 && sh->max_rank % 8 == 0,
+                 "max_rank %d must be a multiple of 8 in [8, 64]", sh->max_rank);
+  LORA_ARG_CHECK(sh->order == LORA_IDS_SORTED || sh->order == LORA_IDS_INTERLEAVED,
+                 "order %d is not a lora_id_order", sh->order);
+  LORA_ARG_CHECK(sh->reserved == 0, "reserved field must be 0");
+  LORA_ARG_CHECK(sh->a_pack_elems >= 0 && sh->b_pack_elems >= 0, "pack sizes must be >= 0");
+  if (sh->d_in % 64 || sh->d_out % 64 || sh->d_in > (1 << 20) || sh->d_out > (1 << 20)) {
+    set_error("d_in %lld and d_out %lld must be multiples of 64 and <= 2^20",
+              (long long)sh->d_in, (long long)sh->d_out);
+    return LORA_E_UNSUPPORTED;
+  }
+  return LORA_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+lora_status layer_segments(const lora_shape& sh, const lora_adapter_desc* desc,
+                           const int32_t* ids, const LayerWs& w, hipStream_t s) {
+  SegExtras ex{};
+  ex.desc = desc;
+  ex.d_in = sh.d_in;
+  ex.d_out = sh.d_out;
+  ex.a_elems = sh.a_pack_elems;
+  ex.b_elems = sh.b_pack_elems;
+  ex.max_rank = sh.max_rank;
+  ex.active = w.active;
+  ex.tm[0] = kTmShrink;
+  ex.pre[0] = w.pre16;
+  ex.tm[1] = kTmExpand;
+  ex.pre[1] = w.pre64;
+  ex.tm[2] = kGradChunk;
+  ex.pre[2] = w.prec;
+  return run_segments(ids, sh.n_tokens, sh.n_adapters, sh.order, w.perm, w.offsets, &ex, w.seg,
+                      w.seg_bytes, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t lora_workspace_bytes(const lora_shape* shape) {
+  if (check_shape(shape) != LORA_OK) return 0;
+  return carve_layer(*shape, nullptr, 0).total;
+}
+
+lora_status lora_workspace_init(void* ws, size_t ws_bytes, void* stream) {
+  if (!ws || ws_bytes < 256) {
+    set_error("workspace NULL or smaller than 256 bytes");
+    return LORA_E_WORKSPACE;
+  }
+  return launch_fill_i32((int32_t*)ws, 64, 0, S(stream));
+}
+
+lora_status lora_device_status(void* ws, int32_t* host_flags, void* stream) {
+  LORA_ARG_CHECK(ws != nullptr && host_flags != nullptr, "NULL workspace or flags pointer");
+  TRY(hip_check(hipStreamSynchronize(S(stream)), "hipStreamSynchronize"));
+  int32_t v = 0;
+  TRY(hip_check(hipMemcpy(&v, ws, sizeof(v), hipMemcpyDeviceToHost), "status read"));
+  const int32_t z = 0;
+  TRY(hip_check(hipMemcpy(ws, &z, sizeof(z), hipMemcpyHostToDevice), "status clear"));
+  *host_flags = v;
+  if (v) {
+    set_error("device content checks failed: flags 0x%x", v);
+    return LORA_E_DEVICE_CHECK;
+  }
+  return LORA_OK;
+}
+
+const char* lora_last_error(void) { return g_err.c_str(); }
+
+size_t lora_segments_workspace_bytes(int64_t n, int32_t n_keys) {
+  if (n < 0 || n_keys < 1 || n_keys > 16384) return 0;
+  return segments_ws_bytes(n, n_keys);
+}
+
+lora_status lora_segments(const int32_t* ids, int64_t n, int32_t n_keys, int32_t order,
+                          int32_t* perm, int32_t* offsets, void* ws, size_t ws_bytes,
+                          void* stream) {
+  LORA_ARG_CHECK(n >= 0 && n <= INT32_MAX / 2, "n %lld outside [0, 2^30)", (long long)n);
+  LORA_ARG_CHECK(n_keys >= 1 && n_keys <= 16384, "n_keys %d outside [1, 16384]", n_keys);
+  LORA_ARG_CHECK(order == LORA_IDS_SORTED || order == LORA_IDS_INTERLEAVED, "bad order %d", order);
+  LORA_ARG_CHECK(offsets != nullptr, "offsets is NULL");
+  LORA_ARG_CHECK(n == 0 || (ids != nullptr && perm != nullptr), "ids/perm NULL");
+  if (!ws || ws_bytes < segments_ws_bytes(n, n_keys)) {
+    set_error("segments: workspace too small (%zu < %zu)", ws_bytes, segments_ws_bytes(n, n_keys));
+    return LORA_E_WORKSPACE;
+  }
+  return run_segments(ids, n, n_keys, order, perm, offsets, nullptr, ws, ws_bytes, S(stream));
+}
+
+lora_status lora_transpose_bf16(const uint16_t* src, uint16_t* dst, int64_t rows, int64_t cols,
+                                void* stream) {
+  LORA_ARG_CHECK(src && dst && src != dst, "src/dst NULL or equal");
+  LORA_ARG_CHECK(rows > 0 && cols > 0, "rows and cols must be positive");
+  if (rows % 64 || cols % 64) {
+    set_error("transpose: rows %lld and cols %lld must be multiples of 64", (long long)rows,
+              (long long)cols);
+    return LORA_E_UNSUPPORTED;
+  }
+  return launch_transpose_bf16(src, dst, rows, cols, S(stream));
+}
+
+lora_status lora_forward(const lora_shape* shape, const uint16_t* x, const uint16_t* W,
+                         const uint16_t* A_pack, const uint16_t* B_pack,
+                         const lora_adapter_desc* desc, const int32_t* adapter_ids, uint16_t* y,
+                         float* u_saved, void* ws, size_t ws_bytes, void* stream) {
+  TRY(check_shape(shape));
+  const lora_shape& sh = *shape;
+  LORA_ARG_CHECK(W && A_pack && B_pack && desc, "W, A_pack, B_pack and desc must be non-NULL");
+  LORA_ARG_CHECK(sh.n_tokens == 0 || (x && adapter_ids && y && u_saved),
+                 "x, adapter_ids, y and u_saved must be non-NULL");
+  LORA_ARG_CHECK(sh.n_tokens == 0 || (aligned16(x) && aligned16(y) && aligned16(u_saved)),
+                 "x, y and u_saved must be 16-byte aligned");
+  LORA_ARG_CHECK(aligned16(W) && aligned16(A_pack) && aligned16(B_pack), "W and the packs must be 16-byte aligned");
+  LayerWs w = carve_layer(sh, ws, ws_bytes);
+  if (!ws || w.total > ws_bytes) {
+    set_error("lora_forward: workspace %zu bytes < %zu needed", ws_bytes, w.total);
+    return LORA_E_WORKSPACE;
+  }
+  hipStream_t s = S(stream);
+  const int N = (int)sh.n_tokens;
+  TRY(layer_segments(sh, desc, adapter_ids, w, s));
+  if (N == 0) return LORA_OK;
+  timer_begin(LORA_TIMER_BASE_GEMM, s);
+  TRY(gemm_nt_bf16(x, W, y, N, (int)sh.d_out, (int)sh.d_in, sh.d_in, sh.d_in, sh.d_out, s));
+  timer_end(LORA_TIMER_BASE_GEMM, s);
+  timer_begin(LORA_TIMER_SHRINK, s);
+  TRY(launch_shrink(x, sh.d_in, (int)sh.d_in, A_pack, 0, desc, w.active, w.perm, w.offsets,
+                    w.pre16, sh.n_adapters, sh.n_tokens, u_saved, sh.max_rank, s));
+  timer_end(LORA_TIMER_SHRINK, s);
+  timer_begin(LORA_TIMER_EXPAND, s);
+  TRY(launch_expand(u_saved, sh.max_rank, B_pack, 1, desc, w.perm, w.offsets, w.pre64,
+                    sh.n_adapters, sh.n_tokens, y, sh.d_out, (int)sh.d_out, s));
+  timer_end(LORA_TIMER_EXPAND, s);
+  return LORA_OK;
+}
+
+lora_status lora_backward(const lora_shape* shape, const uint16_t* dy, const uint16_t* x,
+                          const uint16_t* W_t, const uint16_t* A_pack, const uint16_t* B_pack,
+                          const lora_adapter_desc* desc, const int32_t* adapter_ids,
+                          const float* u_saved, uint16_t* dx, float* dA_pack, float* dB_pack,
+                          int accumulate, void* ws, size_t ws_bytes, void* stream) {
+  TRY(check_shape(shape));
+  const lora_shape& sh = *shape;
+  LORA_ARG_CHECK(W_t && A_pack && B_pack && desc && dA_pack && dB_pack,
+                 "W_t, packs, desc and gradient packs must be non-NULL");
+  LORA_ARG_CHECK(sh.n_tokens == 0 || (dy && x && adapter_ids && u_saved && dx),
+                 "dy, x, adapter_ids, u_saved and dx must be non-NULL");
+  LORA_ARG_CHECK(sh.n_tokens == 0 || (aligned16(dy) && aligned16(x) && aligned16(dx) && aligned16(u_saved)),
+                 "dy, x, dx and u_saved must be 16-byte aligned");
+  LORA_ARG_CHECK(aligned16(W_t) && aligned16(A_pack) && aligned16(B_pack) && aligned16(dA_pack) &&
+                     aligned16(dB_pack),
+                 "W_t and the packs must be 16-byte aligned");
+  LayerWs w = carve_layer(sh, ws, ws_bytes);
+  if (!ws || w.total > ws_bytes) {
+    set_error("lora_backward: workspace %zu bytes < %zu needed", ws_bytes, w.total);
+    return LORA_E_WORKSPACE;
+  }
+  hipStream_t s = S(stream);
+  const int N = (int)sh.n_tokens;
+  TRY(layer_segments(sh, desc, adapter_ids, w, s));
+  TRY(launch_adapter_transpose(A_pack, B_pack, desc, w.active, sh.n_adapters, sh.d_in, sh.d_out,
+                               w.AT, w.BT, s));
+  if (N > 0) {
+    timer_begin(LORA_TIMER_BASE_GEMM, s);
+    TRY(gemm_nt_bf16(dy, W_t, dx, N, (int)sh.d_in, (int)sh.d_out, sh.d_out, sh.d_out, sh.d_in, s));
+    timer_end(LORA_TIMER_BASE_GEMM, s);
+    timer_begin(LORA_TIMER_SHRINK, s);
+    TRY(launch_shrink(dy, sh.d_out, (int)sh.d_out, w.BT, 1, desc, w.active, w.perm, w.offsets,
+                      w.pre16, sh.n_adapters, sh.n_tokens, w.v, sh.max_rank, s));
+    timer_end(LORA_TIMER_SHRINK, s);
+  }
+  timer_begin(LORA_TIMER_GRAD, s);
+  TRY(launch_grad(0, u_saved, sh.max_rank, dy, sh.d_out, (int)sh.d_out, desc, w.active, w.perm,
+                  w.offsets, w.prec, sh.n_adapters, sh.n_tokens, dB_pack, w.partial, accumulate, s));
+  TRY(launch_grad(1, w.v, sh.max_rank, x, sh.d_in, (int)sh.d_in, desc, w.active, w.perm, w.offsets,
+                  w.prec, sh.n_adapters, sh.n_tokens, dA_pack, w.partial, accumulate, s));
+  timer_end(LORA_TIMER_GRAD, s);
+  if (N > 0) {
+    timer_begin(LORA_TIMER_EXPAND, s);
+    TRY(launch_expand(w.v, sh.max_rank, w.AT, 0, desc, w.perm, w.offsets, w.pre64, sh.n_adapters,
+                      sh.n_tokens, dx, sh.d_in, (int)sh.d_in, s));
+    timer_end(LORA_TIMER_EXPAND, s);
+  }
+  return LORA_OK;
+}
+
+// ------------------------------------------------------------------ logprobs
+static size_t logprob_ws(int64_t n, int64_t vocab, float** pm, float** ps, float** zt, void* ws,
+                         size_t bytes) {
+  Carve cv(ws, bytes);
+  cv.take<int32_t>(64);
+  const int64_t tiles = cdiv(vocab, 256);
+  float* a = cv.take<float>((size_t)tiles * std::max<int64_t>(n, 1));
+  float* b = cv.take<float>((size_t)tiles * std::max<int64_t>(n, 1));
+  float* c = cv.take<float>((size_t)std::max<int64_t>(n, 1));
+  if (pm) { *pm = a; *ps = b; *zt = c; }
+  return cv.used;
+}
+
+size_t token_logprobs_workspace_bytes(int64_t n, int64_t vocab) {
+  if (n < 0 || vocab <= 0) return 0;
+  return logprob_ws(n, vocab, nullptr, nullptr, nullptr, nullptr, 0);
+}
+
+static lora_status check_lp(int64_t n, int64_t hidden, int64_t vocab) {
+  LORA_ARG_CHECK(n >= 0 && n <= INT32_MAX / 2, "n %lld outside [0, 2^30)", (long long)n);
+  LORA_ARG_CHECK(hidden > 0 && vocab > 0, "hidden and vocab must be positive");
+  if (hidden % 64 || vocab % 64 || vocab > INT32_MAX / 2 || hidden > (1 << 20)) {
+    set_error("hidden %lld and vocab %lld must be multiples of 64", (long long)hidden, (long long)vocab);
+    return LORA_E_UNSUPPORTED;
+  }
+  return LORA_OK;
+}
+
+lora_status token_logprobs(int64_t n, int64_t hidden, int64_t vocab, const uint16_t* h,
+                           const uint16_t* lm_head, const int32_t* targets, float* logprobs,
+                           float* lse, void* ws, size_t ws_bytes, void* stream) {
+  TRY(check_lp(n, hidden, vocab));
+  LORA_ARG_CHECK(lm_head != nullptr, "lm_head is NULL");
+  LORA_ARG_CHECK(n == 0 || (h && targets && logprobs && lse), "h/targets/logprobs/lse NULL");
+  LORA_ARG_CHECK(aligned16(lm_head) && (n == 0 || aligned16(h)), "h and lm_head must be 16-byte aligned");
+  float *pm, *ps, *zt;
+  const size_t need = logprob_ws(n, vocab, &pm, &ps, &zt, ws, ws_bytes);
+  if (!ws || need > ws_bytes) {
+    set_error("token_logprobs: workspace %zu bytes < %zu needed", ws_bytes, need);
+    return LORA_E_WORKSPACE;
+  }
+  if (n == 0) return LORA_OK;
+  hipStream_t s = S(stream);
+  timer_begin(LORA_TIMER_LOGPROB_FWD, s);
+  TRY(gemm_nt_lse(h, lm_head, (int)n, (int)vocab, (int)hidden, hidden, hidden, pm, ps, zt, targets, s));
+  timer_end(LORA_TIMER_LOGPROB_FWD, s);
+  return launch_logprob_merge(pm, ps, zt, targets, n, (int)cdiv(vocab, 256), vocab, logprobs, lse,
+                              (int32_t*)ws, s);
+}
+
+size_t token_logprobs_backward_workspace_bytes(int64_t n, int64_t vocab, int64_t chunk_rows) {
+  if (n < 0 || vocab <= 0 || chunk_rows < 256) return 0;
+  Carve cv(nullptr, 0);
+  cv.take<int32_t>(64);
+  cv.take<uint16_t>((size_t)lora::align_up(chunk_rows, 256) * vocab);
+  return cv.used;
+}
+
+lora_status token_logprobs_backward(int64_t n, int64_t hidden, int64_t vocab, const uint16_t* h,
+                                    const uint16_t* lm_head, const uint16_t* lm_head_t,
+                                    const int32_t* targets, const float* lse, const float* dlogp,
+                                    uint16_t* dh, void* ws, size_t ws_bytes, void* stream) {
+  TRY(check_lp(n, hidden, vocab));
+  LORA_ARG_CHECK(lm_head && lm_head_t, "lm_head and lm_head_t must be non-NULL");
+  LORA_ARG_CHECK(n == 0 || (h && targets && lse && dlogp && dh), "h/targets/lse/dlogp/dh NULL");
+  LORA_ARG_CHECK(aligned16(lm_head) && aligned16(lm_head_t) && (n == 0 || (aligned16(h) && aligned16(dh))),
+                 "h, dh and the lm_head copies must be 16-byte aligned");
+  const size_t head = 256;
+  if (!ws || ws_bytes < head + (size_t)256 * vocab * 2) {
+    set_error("token_logprobs_backward: workspace must hold at least 256 rows of G (%zu bytes)",
+              head + (size_t)256 * vocab * 2);
+    return LORA_E_WORKSPACE;
+  }
+  int64_t chunk = (int64_t)((ws_bytes - head) / ((size_t)vocab * 2));
+  chunk = (chunk / 256) * 256;
+  if (chunk > lora::align_up(n, 256)) chunk = lora::align_up(n, 256);
+  uint16_t* G = (uint16_t*)((char*)ws + head);
+  hipStream_t s = S(stream);
+  for (int64_t c0 = 0; c0 < n; c0 += chunk) {
+    const int rows = (int)std::min<int64_t>(chunk, n - c0);
+    timer_begin(LORA_TIMER_LOGPROB_BWD, s);
+    TRY(gemm_nt_grad(h + c0 * hidden, lm_head, G, vocab, rows, (int)vocab, (int)hidden, hidden,
+                     hidden, targets + c0, lse + c0, dlogp + c0, s));
+    TRY(gemm_nt_bf16(G, lm_head_t, dh + c0 * hidden, rows, (int)hidden, (int)vocab, vocab, vocab,
+                     hidden, s));
+    timer_end(LORA_TIMER_LOGPROB_BWD, s);
+  }
+  return LORA_OK;
+}
+
+// ------------------------------------------------------------------ loss
+size_t loss_grad_workspace_bytes(int64_t n) {
+  if (n < 0) return 0;
+  return 256 + (size_t)std::max<int64_t>(1, cdiv(n, 1024)) * sizeof(double);
+}
+
+lora_status loss_grad(int32_t kind, int64_t n, const float* logprobs, const float* weights,
+                      const float* advantages, const float* sampler_logprobs,
+                      const float* custom_g, const loss_config* cfg, float* loss_out,
+                      float* dlogp, void* ws, size_t ws_bytes, void* stream) {
+  LORA_ARG_CHECK(kind >= LOSS_CROSS_ENTROPY && kind <= LOSS_CUSTOM, "unknown loss kind %d", kind);
+  LORA_ARG_CHECK(n >= 0, "n must be >= 0");
+  LORA_ARG_CHECK(loss_out != nullptr, "loss_out is NULL");
+  LORA_ARG_CHECK(n == 0 || (logprobs && weights && dlogp), "logprobs/weights/dlogp NULL");
+  if (kind == LOSS_IMPORTANCE_SAMPLING || kind == LOSS_PPO)
+    LORA_ARG_CHECK(n == 0 || (advantages && sampler_logprobs), "advantages and sampler_logprobs required");
+  if (kind == LOSS_CUSTOM) LORA_ARG_CHECK(n == 0 || custom_g, "custom_g required");
+  float lo = 0.2f, hi = 0.2f;
+  if (kind == LOSS_PPO) {
+    LORA_ARG_CHECK(cfg != nullptr, "ppo needs a loss_config");
+    LORA_ARG_CHECK(cfg->clip_low >= 0.f && cfg->clip_low < 1.f && cfg->clip_high >= 0.f,
+                   "clip bounds need 0 <= clip_low < 1 and clip_high >= 0");
+    lo = cfg->clip_low;
+    hi = cfg->clip_high;
+  }
+  if (!ws || ws_bytes < loss_grad_workspace_bytes(n)) {
+    set_error("loss_grad: workspace too small");
+    return LORA_E_WORKSPACE;
+  }
+  return launch_loss(kind, n, logprobs, weights, advantages, sampler_logprobs, custom_g, lo, hi,
+                     (double*)((char*)ws + 256), loss_out, dlogp, S(stream));
+}
+
+// ------------------------------------------------------------------ Adam
+lora_status adam_step(int64_t n, float* p, const float* g, float* m, float* v, int64_t step,
+                      float lr, float beta1, float beta2, float eps, float weight_decay,
+                      uint16_t* p_bf16, void* stream) {
+  LORA_ARG_CHECK(n >= 0, "n must be >= 0");
+  LORA_ARG_CHECK(n == 0 || (p && g && m && v), "p/g/m/v NULL");
+  LORA_ARG_CHECK(step >= 1, "step must be >= 1 (1-based per-adapter counter)");
+  LORA_ARG_CHECK(beta1 >= 0.f && beta1 < 1.f && beta2 >= 0.f && beta2 < 1.f, "betas must lie in [0, 1)");
+  const double bc1 = 1.0 - std::pow((double)beta1, (double)step);
+  const double bc2 = 1.0 - std::pow((double)beta2, (double)step);
+  const float step_size = (float)((double)lr / bc1);
+  const float inv_sqrt_bc2 = (float)(1.0 / std::sqrt(bc2));
+  hipStream_t s = S(stream);
+  timer_begin(LORA_TIMER_ADAM, s);
+  TRY(launch_adam(n, p, g, m, v, lr, beta1, beta2, eps, weight_decay, step_size, inv_sqrt_bc2,
+                  p_bf16, s));
+  timer_end(LORA_TIMER_ADAM, s);
+  return LORA_OK;
+}
+
+// ------------------------------------------------------------------ SwiGLU
+lora_status swiglu_forward(int64_t n, const uint16_t* gate, const uint16_t* up, uint16_t* h,
+                           void* stream) {
+  LORA_ARG_CHECK(n >= 0 && (n == 0 || (gate && up && h)), "bad swiglu_forward arguments");
+  LORA_ARG_CHECK(n == 0 || (aligned16(gate) && aligned16(up) && aligned16(h)), "swiglu buffers must be 16-byte aligned");
+  return launch_swiglu_fwd(n, gate, up, h, S(stream));
+}
+
+lora_status swiglu_backward(int64_t n, const uint16_t* dh, const uint16_t* gate,
+                            const uint16_t* up, uint16_t* dgate, uint16_t* dup, void* stream) {
+  LORA_ARG_CHECK(n >= 0 && (n == 0 || (dh && gate && up && dgate && dup)), "bad swiglu_backward arguments");
+  LORA_ARG_CHECK(n == 0 || (aligned16(dh) && aligned16(gate) && aligned16(up) && aligned16(dgate) && aligned16(dup)),
+                 "swiglu buffers must be 16-byte aligned");
+  return launch_swiglu_bwd(n, dh, gate, up, dgate, dup, S(stream));
+}
+
+// ------------------------------------------------------------------ timing
+void lora_timing_enable(int on) { g_tim.on = on != 0; }
+
+void lora_timing_reset(void) {
+  for (int i = 0; i < LORA_TIMER_COUNT; ++i) g_tim.used[i] = 0;
+}
+
+lora_status lora_timing_read(int32_t timer, double* total_ms, int64_t* launches) {
+  LORA_ARG_CHECK(timer >= 0 && timer < LORA_TIMER_COUNT, "unknown timer %d", timer);
+  LORA_ARG_CHECK(total_ms && launches, "NULL output pointer");
+  double tot = 0.0;
+  const size_t u = g_tim.used[timer];
+  for (size_t i = 0; i < u; ++i) {
+    auto& pr = g_tim.pairs[timer][i];
+    TRY(hip_check(hipEventSynchronize(pr.second), "hipEventSynchronize"));
+    float ms = 0.f;
+    TRY(hip_check(hipEventElapsedTime(&ms, pr.first, pr.second), "hipEventElapsedTime"));
+    tot += ms;
+  }
+  *total_ms = tot;
+  *launches = (int64_t)u;
+  return LORA_OK;
+}
+
+}  // extern "C"

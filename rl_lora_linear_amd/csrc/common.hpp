@@ -1,0 +1,115 @@
+// Shared device/host helpers for the gfx950 kernels of the LoRA hot path.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "lora_mi355x.h"
+
+namespace lora {
+
+// ---------------------------------------------------------------- vector types
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- bf16
+__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+__device__ __forceinline__ float bf2f_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf2f_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Round-to-nearest-even fp32 -> bf16 (quiet NaN preserved).
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x0040u);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ uint32_t pack2bf(float lo, float hi) {
+  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+}
+
+// Split an fp32 value into hi + lo bf16 parts (hi = RNE(x), lo = RNE(x - hi)).
+// hi + lo carries ~16 significant bits, so a product with an exact bf16 operand
+// accumulated by MFMA in fp32 loses ~2^-17 relative instead of 2^-9.
+__device__ __forceinline__ void split_bf16(float x, uint16_t& hi, uint16_t& lo) {
+  hi = f2bf(x);
+  lo = f2bf(x - bf2f(hi));
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
+  union { uint4 u; bf16x8 b; } c;
+  c.u = v;
+  return c.b;
+}
+
+// ---------------------------------------------------------------- MFMA
+__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------- status
+__device__ __forceinline__ void set_flag(int32_t* status, int32_t bit) {
+  // vector-memory atomic OR into the sticky status word
+  __hip_atomic_fetch_or(status, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---------------------------------------------------------------- misc
+__host__ __device__ __forceinline__ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+__host__ __device__ __forceinline__ int64_t align_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
+
+// Binary search: largest a in [0, n) with pre[a] <= i (pre non-decreasing, pre[0] = 0).
+__device__ __forceinline__ int find_bucket(const int32_t* pre, int n, int32_t i) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (pre[mid] <= i) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+}  // namespace lora
+
+// ---------------------------------------------------------------- host side
+namespace lora_host {
+
+void set_error(const char* fmt, ...);
+lora_status hip_check(hipError_t e, const char* what);
+lora_status launch_check(const char* what);
+
+// Kernel timing hooks (no-ops unless lora_timing_enable(1)).
+void timer_begin(int timer, hipStream_t s);
+void timer_end(int timer, hipStream_t s);
+
+struct Carve {
+  char* base;
+  size_t used;
+  size_t cap;
+  explicit Carve(void* b, size_t c) : base((char*)b), used(0), cap(c) {}
+  template <typename T>
+  T* take(size_t count) {
+    used = (size_t)lora::align_up((int64_t)used, 256);
+    T* p = base ? (T*)(base + used) : nullptr;
+    used += count * sizeof(T);
+    return p;
+  }
+  bool fits() const { return used <= cap; }
+};
+
+}  // namespace lora_host
+
+#define LORA_ARG_CHECK(cond, ...)                       \
+  do {                                                  \
+    if (!(cond)) {                                      \
+      lora_host::set_error(__VA_ARGS__);                \
+      return LORA_E_INVALID_ARG;                        \
+    }                                                   \
+  } while (0)

@@ -1,0 +1,331 @@
+// Bandwidth-bound kernels of the hot path on gfx950: the logsumexp merge, the
+// token loss, per-adapter AdamW, the SwiGLU glue, and a bf16 transpose for
+// keeping frozen operands in both layouts.
+#include "common.hpp"
+#include "sgmv.hpp"
+
+namespace lora {
+
+constexpr float kLog2eF = 1.4426950408889634f;
+constexpr float kLn2F = 0.6931471805599453f;
+
+// ------------------------------------------------------------------ logsumexp merge
+// One thread per token: merge the per-vocab-tile (max, sum) pairs in tile order
+// (TPU RL note, section 10 item 3: lse = m + log sum exp(z - m)), then
+// logprob = z[target] - lse.  Out-of-range targets give NaN and a status flag.
+__global__ __launch_bounds__(256) void logprob_merge_kernel(
+    const float* __restrict__ part_m, const float* __restrict__ part_s,
+    const float* __restrict__ zt, const int32_t* __restrict__ targets, int64_t n, int tiles,
+    int64_t vocab, float* __restrict__ logprobs, float* __restrict__ lse, int32_t* status) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= n) return;
+  float mx = -INFINITY;
+  for (int i = 0; i < tiles; ++i) mx = fmaxf(mx, part_m[(int64_t)i * n + t]);
+  float s = 0.f;
+  for (int i = 0; i < tiles; ++i) {
+    const float m = part_m[(int64_t)i * n + t];
+    if (m != -INFINITY) s += part_s[(int64_t)i * n + t] * exp2f((m - mx) * kLog2eF);
+  }
+  const float l = mx + log2f(s) * kLn2F;
+  lse[t] = l;
+  const int32_t y = targets[t];
+  if (y < 0 || y >= vocab) {
+    set_flag(status, LORA_FLAG_TARGET_RANGE);
+    logprobs[t] = __int_as_float(0x7FC00000);
+  } else {
+    logprobs[t] = zt[t] - l;
+  }
+}
+
+// ------------------------------------------------------------------ token loss
+// 1024 rows per block (4 per thread); the block's loss terms are summed in
+// fp64 by a fixed tree; a second single-block pass sums the block partials in
+// block order.  The result depends only on n and the inputs.
+constexpr int LOSS_ROWS = 1024;
+
+__global__ __launch_bounds__(256) void loss_rows_kernel(int kind, int64_t n,
+                                                        const float* __restrict__ logp,
+                                                        const float* __restrict__ w,
+                                                        const float* __restrict__ adv,
+                                                        const float* __restrict__ samp,
+                                                        const float* __restrict__ g, float clip_lo,
+                                                        float clip_hi, double* __restrict__ partial,
+                                                        float* __restrict__ dlogp) {
+  __shared__ double red[256];
+  double acc = 0.0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int64_t t = (int64_t)blockIdx.x * LOSS_ROWS + q * 256 + threadIdx.x;
+    if (t >= n) continue;
+    const float wt = w[t];
+    float d = 0.f;
+    double term = 0.0;
+    if (wt != 0.f) {  // masked rows are removed by selection
+      const float l = logp[t];
+      if (kind == LOSS_CROSS_ENTROPY) {
+        d = -wt;
+        term = -(double)wt * (double)l;
+      } else if (kind == LOSS_CUSTOM) {
+        const float gg = g[t];
+        d = gg;
+        term = (double)gg * (double)l;
+      } else {
+        const float A = adv[t];
+        const float rho = exp2f((l - samp[t]) * kLog2eF);
+        const float ra = rho * A;
+        if (kind == LOSS_IMPORTANCE_SAMPLING) {
+          d = -ra;
+          term = -(double)ra;
+        } else {
+          const float lo = 1.f - clip_lo, hi = 1.f + clip_hi;
+          const float rc = fminf(fmaxf(rho, lo), hi);
+          const float obj = fminf(ra, rc * A);
+          const bool inactive = (A > 0.f && rho > hi) || (A < 0.f && rho < lo);
+          d = inactive ? 0.f : -ra;
+          term = -(double)obj;
+        }
+      }
+    }
+    dlogp[t] = d;
+    acc += term;
+  }
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) partial[blockIdx.x] = red[0];
+}
+
+__global__ __launch_bounds__(256) void loss_sum_kernel(const double* __restrict__ partial,
+                                                       int nb, float* __restrict__ loss_out) {
+  __shared__ double red[256];
+  double acc = 0.0;
+  for (int i = threadIdx.x; i < nb; i += 256) acc += partial[i];
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) loss_out[0] = (float)red[0];
+}
+
+// ------------------------------------------------------------------ AdamW
+__device__ __forceinline__ void adam_one(float& p, float g, float& m, float& v, float lr,
+                                         float b1, float b2, float eps, float wd, float step_size,
+                                         float inv_sqrt_bc2) {
+  m = b1 * m + (1.f - b1) * g;
+  v = b2 * v + (1.f - b2) * g * g;
+  p = p - lr * wd * p;
+  const float denom = __fsqrt_rn(v) * inv_sqrt_bc2 + eps;
+  p = p - step_size * __fdiv_rn(m, denom);
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(256) void adam_kernel(int64_t n, float* __restrict__ p,
+                                                   const float* __restrict__ g,
+                                                   float* __restrict__ m, float* __restrict__ v,
+                                                   float lr, float b1, float b2, float eps,
+                                                   float wd, float step_size, float inv_sqrt_bc2,
+                                                   uint16_t* __restrict__ pb) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (VEC) {
+    const int64_t n4 = n / 4;
+    for (int64_t i = i0; i < n4; i += stride) {
+      float4 pp = ((float4*)p)[i], mm = ((float4*)m)[i], vv = ((float4*)v)[i];
+      const float4 gg = ((const float4*)g)[i];
+      adam_one(pp.x, gg.x, mm.x, vv.x, lr, b1, b2, eps, wd, step_size, inv_sqrt_bc2);
+      adam_one(pp.y, gg.y, mm.y, vv.y, lr, b1, b2, eps, wd, step_size, inv_sqrt_bc2);
+      adam_one(pp.z, gg.z, mm.z, vv.z, lr, b1, b2, eps, wd, step_size, inv_sqrt_bc2);
+      adam_one(pp.w, gg.w, mm.w, vv.w, lr, b1, b2, eps, wd, step_size, inv_sqrt_bc2);
+      ((float4*)p)[i] = pp;
+      ((float4*)m)[i] = mm;
+      ((float4*)v)[i] = vv;
+      if (pb) ((uint2*)pb)[i] = make_uint2(pack2bf(pp.x, pp.y), pack2bf(pp.z, pp.w));
+    }
+    for (int64_t i = n4 * 4 + i0; i < n; i += stride) {
+      float pp = p[i], mm = m[i], vv = v[i];
+      adam_one(pp, g[i], mm, vv, lr, b1, b2, eps, wd, step_size, inv_sqrt_bc2);
+      p[i] = pp; m[i] = mm; v[i] = vv;
+      if (pb) pb[i] = f2bf(pp);
+    }
+  } else {
+    for (int64_t i = i0; i < n; i += stride) {
+      float pp = p[i], mm = m[i], vv = v[i];
+      adam_one(pp, g[i], mm, vv, lr, b1, b2, eps, wd, step_size, inv_sqrt_bc2);
+      p[i] = pp; m[i] = mm; v[i] = vv;
+      if (pb) pb[i] = f2bf(pp);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ SwiGLU
+__device__ __forceinline__ float sigmoidf_(float z) { return 1.f / (1.f + exp2f(-z * kLog2eF)); }
+
+template <bool BWD>
+__global__ __launch_bounds__(256) void swiglu_kernel(int64_t n, const uint16_t* __restrict__ dh,
+                                                     const uint16_t* __restrict__ gt,
+                                                     const uint16_t* __restrict__ up,
+                                                     uint16_t* __restrict__ o1,
+                                                     uint16_t* __restrict__ o2) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t n8 = n / 8;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8 + (n % 8 ? 1 : 0);
+       i += stride) {
+    const bool full = i < n8;
+    uint16_t G[8], U[8], D[8];
+    if (full) {
+      const uint4 a = ((const uint4*)gt)[i], b = ((const uint4*)up)[i];
+      const uint32_t wa[4] = {a.x, a.y, a.z, a.w}, wb[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        G[q] = (uint16_t)(wa[q >> 1] >> ((q & 1) * 16));
+        U[q] = (uint16_t)(wb[q >> 1] >> ((q & 1) * 16));
+      }
+      if (BWD) {
+        const uint4 c = ((const uint4*)dh)[i];
+        const uint32_t wc[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+        for (int q = 0; q < 8; ++q) D[q] = (uint16_t)(wc[q >> 1] >> ((q & 1) * 16));
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int64_t e = i * 8 + q;
+        G[q] = e < n ? gt[e] : 0;
+        U[q] = e < n ? up[e] : 0;
+        D[q] = (BWD && e < n) ? dh[e] : 0;
+      }
+    }
+    uint16_t r1[8], r2[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const float z = bf2f(G[q]), u = bf2f(U[q]);
+      const float sg = sigmoidf_(z);
+      const float sl = z * sg;
+      if (!BWD) {
+        r1[q] = f2bf(sl * u);
+      } else {
+        const float d = bf2f(D[q]);
+        r1[q] = f2bf(d * u * (sg * (1.f + z * (1.f - sg))));
+        r2[q] = f2bf(d * sl);
+      }
+    }
+    if (full) {
+      ((uint4*)o1)[i] = make_uint4(r1[0] | (r1[1] << 16), r1[2] | (r1[3] << 16), r1[4] | (r1[5] << 16), r1[6] | (r1[7] << 16));
+      if (BWD)
+        ((uint4*)o2)[i] = make_uint4(r2[0] | (r2[1] << 16), r2[2] | (r2[3] << 16), r2[4] | (r2[5] << 16), r2[6] | (r2[7] << 16));
+    } else {
+      for (int q = 0; q < 8; ++q) {
+        const int64_t e = i * 8 + q;
+        if (e < n) {
+          o1[e] = r1[q];
+          if (BWD) o2[e] = r2[q];
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ transpose
+// dst[c][r] = src[r][c]; 64 x 64 tiles through LDS (padded to avoid conflicts).
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __restrict__ src,
+                                                             uint16_t* __restrict__ dst,
+                                                             int64_t rows, int64_t cols) {
+  __shared__ uint16_t tile[64][64 + 2];
+  const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int i = ty; i < 64; i += 4) tile[i][tx] = src[(r0 + i) * cols + c0 + tx];
+  __syncthreads();
+  for (int i = ty; i < 64; i += 4) dst[(c0 + i) * rows + r0 + tx] = tile[tx][i];
+}
+
+__global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+}  // namespace lora
+
+namespace lora_host {
+using namespace lora;
+
+static unsigned grid_for(int64_t work, int per_block, int cap = 4096) {
+  int64_t b = cdiv(work, per_block);
+  if (b < 1) b = 1;
+  if (b > cap) b = cap;
+  return (unsigned)b;
+}
+
+lora_status launch_logprob_merge(const float* part_m, const float* part_s, const float* zt,
+                                 const int32_t* targets, int64_t n, int tiles, int64_t vocab,
+                                 float* logprobs, float* lse, int32_t* status, hipStream_t s) {
+  if (n <= 0) return LORA_OK;
+  hipLaunchKernelGGL(logprob_merge_kernel, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, s, part_m,
+                     part_s, zt, targets, n, tiles, vocab, logprobs, lse, status);
+  return launch_check("logprob_merge");
+}
+
+lora_status launch_loss(int kind, int64_t n, const float* logp, const float* w, const float* adv,
+                        const float* samp, const float* g, float clip_lo, float clip_hi,
+                        double* partial, float* loss_out, float* dlogp, hipStream_t s) {
+  const int64_t nb = cdiv(n, LOSS_ROWS);
+  if (nb > 0) {
+    hipLaunchKernelGGL(loss_rows_kernel, dim3((unsigned)nb), dim3(256), 0, s, kind, n, logp, w,
+                       adv, samp, g, clip_lo, clip_hi, partial, dlogp);
+    lora_status st = launch_check("loss_rows");
+    if (st) return st;
+  }
+  hipLaunchKernelGGL(loss_sum_kernel, dim3(1), dim3(256), 0, s, partial, (int)nb, loss_out);
+  return launch_check("loss_sum");
+}
+
+lora_status launch_adam(int64_t n, float* p, const float* g, float* m, float* v, float lr,
+                        float beta1, float beta2, float eps, float wd, float step_size,
+                        float inv_sqrt_bc2, uint16_t* p_bf16, hipStream_t s) {
+  if (n <= 0) return LORA_OK;
+  const bool vec = ((uintptr_t)p | (uintptr_t)g | (uintptr_t)m | (uintptr_t)v) % 16 == 0 &&
+                   (p_bf16 == nullptr || (uintptr_t)p_bf16 % 8 == 0);
+  const unsigned grid = grid_for(vec ? n / 4 : n, 256, 2048);
+  if (vec)
+    hipLaunchKernelGGL(adam_kernel<true>, dim3(grid), dim3(256), 0, s, n, p, g, m, v, lr, beta1,
+                       beta2, eps, wd, step_size, inv_sqrt_bc2, p_bf16);
+  else
+    hipLaunchKernelGGL(adam_kernel<false>, dim3(grid), dim3(256), 0, s, n, p, g, m, v, lr, beta1,
+                       beta2, eps, wd, step_size, inv_sqrt_bc2, p_bf16);
+  return launch_check("adam");
+}
+
+lora_status launch_swiglu_fwd(int64_t n, const uint16_t* g, const uint16_t* u, uint16_t* h,
+                              hipStream_t s) {
+  if (n <= 0) return LORA_OK;
+  hipLaunchKernelGGL(swiglu_kernel<false>, dim3(grid_for(cdiv(n, 8), 256)), dim3(256), 0, s, n,
+                     (const uint16_t*)nullptr, g, u, h, (uint16_t*)nullptr);
+  return launch_check("swiglu_fwd");
+}
+
+lora_status launch_swiglu_bwd(int64_t n, const uint16_t* dh, const uint16_t* g,
+                              const uint16_t* u, uint16_t* dg, uint16_t* du, hipStream_t s) {
+  if (n <= 0) return LORA_OK;
+  hipLaunchKernelGGL(swiglu_kernel<true>, dim3(grid_for(cdiv(n, 8), 256)), dim3(256), 0, s, n, dh,
+                     g, u, dg, du);
+  return launch_check("swiglu_bwd");
+}
+
+lora_status launch_transpose_bf16(const uint16_t* src, uint16_t* dst, int64_t rows, int64_t cols,
+                                  hipStream_t s) {
+  hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)(cols / 64), (unsigned)(rows / 64)),
+                     dim3(256), 0, s, src, dst, rows, cols);
+  return launch_check("transpose_bf16");
+}
+
+lora_status launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s) {
+  hipLaunchKernelGGL(fill_i32_kernel, dim3(grid_for(n, 256, 1024)), dim3(256), 0, s, p, n, v);
+  return launch_check("fill_i32");
+}
+
+}  // namespace lora_host

@@ -1,0 +1,114 @@
+"""Helpers shared by the GPU parity tests: upload seeded cases, run the C-ABI
+calls through the binding, and the parity metric.
+
+Parity metric: max_e |gpu_e - ora_e| / max(|ora_e|, rms(ora)), compared with
+2e-2 for bf16 outputs and 1e-4 for fp32 outputs.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import workloads as W
+
+TOL_BF16 = 2e-2
+TOL_F32 = 1e-4
+
+
+def rel_err(gpu, ora) -> float:
+    g = np.asarray(gpu, np.float64).reshape(-1)
+    o = np.asarray(ora, np.float64).reshape(-1)
+    if o.size == 0:
+        return 0.0
+    rms = float(np.sqrt(np.mean(o * o)))
+    den = np.maximum(np.abs(o), rms)
+    den[den == 0] = 1.0
+    return float(np.max(np.abs(g - o) / den))
+
+
+def dev_bf16(bits: np.ndarray, device="cuda") -> torch.Tensor:
+    bits = np.ascontiguousarray(bits, dtype=np.uint16)
+    return torch.from_numpy(bits.view(np.int16)).to(device).view(torch.bfloat16)
+
+
+def bits_of(t: torch.Tensor) -> np.ndarray:
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def f64_of(t: torch.Tensor) -> np.ndarray:
+    if t.dtype == torch.bfloat16:
+        return W.bf16_bits_to_f64(bits_of(t))
+    return t.detach().cpu().numpy().astype(np.float64)
+
+
+def dev_f32(a, device="cuda") -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+
+
+def dev_i32(a, device="cuda") -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(device)
+
+
+class DevLayer:
+    """A LoraLayerCase resident on the GPU, with its workspace."""
+
+    def __init__(self, case: "W.LoraLayerCase", order: int = None, max_rank: int = None):
+        import rl_lora_linear_amd.lib as L
+        self.L = L
+        self.case = case
+        if order is None:
+            order = L.IDS_SORTED if case.order == "sorted" else L.IDS_INTERLEAVED
+        self.max_rank = max_rank or max(8, int(np.ceil(case.max_rank / 8) * 8))
+        self.shape = L.make_shape(case.n_tokens, case.d_in, case.d_out, case.pack_elems,
+                                  case.pack_elems, case.n_adapters, self.max_rank, order)
+        self.scales32 = case.scales.astype(np.float32)
+        self.x = dev_bf16(case.x_bits)
+        self.W = dev_bf16(case.W_bits)
+        self.Wt = torch.empty((case.d_in, case.d_out), dtype=torch.bfloat16, device="cuda")
+        L.lora_transpose_bf16(self.W, self.Wt)
+        self.pack = dev_bf16(case.pack_bits)
+        self.desc = L.make_desc(case.a_off, case.b_off, case.ranks, self.scales32)
+        self.ids = dev_i32(case.ids)
+        self.ws = L.empty_workspace(L.lora_workspace_bytes(self.shape))
+        self.dy = dev_bf16(case.dy_bits) if case.dy_bits is not None else None
+
+    def forward(self, x=None, pack=None, ids=None):
+        N, d_out = self.case.n_tokens, self.case.d_out
+        y = torch.empty((N, d_out), dtype=torch.bfloat16, device="cuda")
+        u = torch.full((N, self.max_rank), float("nan"), dtype=torch.float32, device="cuda")
+        p = self.pack if pack is None else pack
+        self.L.lora_forward(self.shape, self.x if x is None else x, self.W, p, p, self.desc,
+                            self.ids if ids is None else ids, y, u, self.ws)
+        return y, u
+
+    def backward(self, u, dy=None, x=None, pack=None, ids=None, accumulate=False, grad=None):
+        N = self.case.n_tokens
+        dx = torch.empty((N, self.case.d_in), dtype=torch.bfloat16, device="cuda")
+        if grad is None:
+            grad = torch.full((self.case.pack_elems,), float("nan"), dtype=torch.float32, device="cuda")
+        p = self.pack if pack is None else pack
+        self.L.lora_backward(self.shape, self.dy if dy is None else dy, self.x if x is None else x,
+                             self.Wt, p, p, self.desc, self.ids if ids is None else ids, u, dx,
+                             grad, grad, accumulate, self.ws)
+        return dx, grad
+
+    def status(self) -> int:
+        return self.L.lora_device_status(self.ws)
+
+    # oracle-side views (float64)
+    def oracle_args(self):
+        c = self.case
+        A = [c.A(i) for i in range(c.n_adapters)]
+        B = [c.B(i) for i in range(c.n_adapters)]
+        return c.x(), c.W(), A, B, self.scales32.astype(np.float64), c.ids
+
+    def split_grad(self, grad: np.ndarray):
+        """Per-adapter (dA, dB) views of a flat gradient pack."""
+        c = self.case
+        dA, dB = [], []
+        for i in range(c.n_adapters):
+            r = int(c.ranks[i])
+            a, b = int(c.a_off[i]), int(c.b_off[i])
+            dA.append(grad[a:a + r * c.d_in].reshape(r, c.d_in))
+            dB.append(grad[b:b + c.d_out * r].reshape(c.d_out, r))
+        return dA, dB

@@ -1,0 +1,182 @@
+"""GPU parity of the fused lm_head logprob (forward, backward), the token
+losses, AdamW and the SwiGLU glue against the oracle, through the C ABI."""
+import numpy as np
+import pytest
+
+import oracle.adam as OA
+import oracle.logprob as OP
+import oracle.loss as OLs
+import oracle.mlp as OM
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+from gpu_util import TOL_BF16, TOL_F32, bits_of, dev_bf16, dev_f32, dev_i32, f64_of, rel_err  # noqa: E402
+import rl_lora_linear_amd.lib as L  # noqa: E402
+
+
+def _lp_case(seed=40, n_groups=3, group_size=4, seq_len=50, hidden=320, vocab=1088):
+    # 600 tokens (ragged against 256-row tiles), vocab 1088 = 4 full tiles + 64 columns
+    return W.logprob_rl(seed=seed, hidden=hidden, vocab=vocab, n_groups=n_groups,
+                        group_size=group_size, seq_len=seq_len, sampler_sigma=0.5)
+
+
+def _run_logprobs(h, U, tgt):
+    n, vocab = h.shape[0], U.shape[0]
+    lp = torch.empty(n, dtype=torch.float32, device="cuda")
+    lse = torch.empty(n, dtype=torch.float32, device="cuda")
+    ws = L.empty_workspace(L.token_logprobs_workspace_bytes(n, vocab))
+    L.token_logprobs(h, U, tgt, lp, lse, ws)
+    return lp, lse, L.lora_device_status(ws)
+
+
+def test_token_logprobs_parity():
+    c = _lp_case()
+    h, U, tgt = dev_bf16(c.h_bits), dev_bf16(c.U_bits), dev_i32(c.targets)
+    lp, lse, flags = _run_logprobs(h, U, tgt)
+    assert flags == 0
+    lp_ref, lse_ref = OP.token_logprobs(W.bf16_bits_to_f64(c.h_bits), W.bf16_bits_to_f64(c.U_bits), c.targets)
+    assert rel_err(f64_of(lse), lse_ref) < TOL_F32
+    assert rel_err(f64_of(lp), lp_ref) < TOL_F32
+
+
+def test_token_logprobs_uniform_and_invalid_targets():
+    g = 1088
+    h = dev_bf16(W.to_bf16_bits(np.random.default_rng(0).standard_normal((300, 128))))
+    U = torch.zeros((g, 128), dtype=torch.bfloat16, device="cuda")
+    tgt = np.arange(300, dtype=np.int32) * 3
+    tgt[[5, 77]] = [-1, g]
+    lp, lse, flags = _run_logprobs(h, U, dev_i32(tgt))
+    assert flags & L.FLAG_TARGET_RANGE
+    lpn = lp.cpu().numpy()
+    assert np.isnan(lpn[5]) and np.isnan(lpn[77])
+    ok = np.ones(300, bool); ok[[5, 77]] = False
+    np.testing.assert_allclose(lpn[ok], -np.log(g), rtol=0, atol=2e-6)
+
+
+@pytest.mark.parametrize("chunk_rows", [256, 1024])
+def test_token_logprobs_backward_parity(chunk_rows):
+    c = _lp_case(41)
+    n, H, V = c.n_tokens, c.hidden, c.vocab
+    h, U, tgt = dev_bf16(c.h_bits), dev_bf16(c.U_bits), dev_i32(c.targets)
+    Ut = torch.empty((H, V), dtype=torch.bfloat16, device="cuda")
+    L.lora_transpose_bf16(U, Ut)
+    lp, lse, _ = _run_logprobs(h, U, tgt)
+    d = np.random.default_rng(3).standard_normal(n).astype(np.float32)
+    d[::7] = 0.0
+    dh = torch.empty((n, H), dtype=torch.bfloat16, device="cuda")
+    ws = L.empty_workspace(L.token_logprobs_backward_workspace_bytes(n, V, chunk_rows))
+    L.token_logprobs_backward(h, U, Ut, tgt, lse, dev_f32(d), dh, ws)
+    dh_ref = OP.token_logprobs_backward(W.bf16_bits_to_f64(c.h_bits), W.bf16_bits_to_f64(c.U_bits), c.targets, d)
+    dhg = f64_of(dh)
+    assert rel_err(dhg, dh_ref) < TOL_BF16
+    assert not np.any(dhg[::7])                       # dlogp == 0 rows are exact zeros
+
+
+@pytest.mark.parametrize("kind", [0, 1, 2, 3])
+def test_loss_grad_parity(kind):
+    c = _lp_case(42)
+    n = c.n_tokens
+    rng = np.random.default_rng(kind)
+    lp = (-rng.random(n) * 8).astype(np.float32)
+    samp = c.sampler_logprobs(lp)
+    w = c.action.copy()
+    if kind == OLs.CROSS_ENTROPY:
+        w = (w * rng.random(n)).astype(np.float32)     # fractional weights
+    adv, g = c.advantages, c.custom_g
+    # masked rows hold non-finite garbage: selection must keep them out
+    lp_in, samp_in, adv_in, g_in = lp.copy(), samp.copy(), adv.copy(), g.copy()
+    masked = np.nonzero(w == 0)[0][:5]
+    lp_in[masked[0]], samp_in[masked[1]], adv_in[masked[2]], g_in[masked[3]] = np.nan, np.inf, np.nan, -np.inf
+    loss = torch.empty(1, dtype=torch.float32, device="cuda")
+    dl = torch.empty(n, dtype=torch.float32, device="cuda")
+    ws = L.empty_workspace(L.loss_grad_workspace_bytes(n))
+    L.loss_grad(kind, dev_f32(lp_in), dev_f32(w), dev_f32(adv_in), dev_f32(samp_in), dev_f32(g_in),
+                (0.2, 0.2), loss, dl, ws)
+    L_ref, dl_ref = OLs.loss_grad(kind, lp_in, w, adv=adv_in, samp=samp_in, g=g_in, clip_low=0.2, clip_high=0.2)
+    dlg = dl.cpu().numpy().astype(np.float64)
+    assert np.all(dlg[w == 0] == 0.0) and np.isfinite(dlg).all()
+    if kind == OLs.PPO:
+        # where fp32 and fp64 can take the clip decision differently (ratio within
+        # 1e-5 of a bound), accept either valid gradient; compare the rest
+        rho = np.exp(lp.astype(np.float64) - samp)
+        near = (np.abs(rho - 0.8) < 1e-5) | (np.abs(rho - 1.2) < 1e-5)
+        alt = -rho * adv
+        ok = np.where(near, (np.abs(dlg - dl_ref) < 1e-5) | (np.abs(dlg - alt) < 1e-5) | (np.abs(dlg) < 1e-30), True)
+        assert ok.all()
+        assert rel_err(dlg[~near], dl_ref[~near]) < TOL_F32
+        clipped = (dl_ref == 0) & (w != 0) & (adv != 0)
+        assert clipped.sum() > 0                        # sigma 0.5 exercises the clip
+    else:
+        assert rel_err(dlg, dl_ref) < TOL_F32
+    assert abs(float(loss.item()) - L_ref) <= TOL_F32 * max(abs(L_ref), 1e-3)
+
+
+def test_custom_minus_w_is_ce_bitwise():
+    c = _lp_case(43)
+    n = c.n_tokens
+    lp = (-np.random.default_rng(1).random(n) * 8).astype(np.float32)
+    w = (c.action * np.random.default_rng(2).random(n)).astype(np.float32)
+    ws = L.empty_workspace(L.loss_grad_workspace_bytes(n))
+    outs = []
+    for kind, weights, g in ((OLs.CROSS_ENTROPY, w, None), (OLs.CUSTOM, (w != 0).astype(np.float32), -w)):
+        loss = torch.empty(1, dtype=torch.float32, device="cuda")
+        dl = torch.empty(n, dtype=torch.float32, device="cuda")
+        L.loss_grad(kind, dev_f32(lp), dev_f32(weights), None, None, None if g is None else dev_f32(g),
+                    None, loss, dl, ws)
+        outs.append((loss.cpu().numpy(), dl.cpu().numpy()))
+    assert np.array_equal(outs[0][0].view(np.uint32), outs[1][0].view(np.uint32))
+    assert np.array_equal(outs[0][1].view(np.uint32), outs[1][1].view(np.uint32))
+
+
+@pytest.mark.parametrize("n", [1, 7, 4096 + 3, 262144])
+def test_adam_parity_and_resume(n):
+    rng = np.random.default_rng(n)
+    p0 = rng.uniform(-1 / 64, 1 / 64, n).astype(np.float32)      # LoRA-A-like initial values
+    grads = [(rng.standard_normal(n) * 10 ** rng.uniform(-4, -1)).astype(np.float32) for _ in range(4)]
+    p, m, v = dev_f32(p0), torch.zeros(n, device="cuda"), torch.zeros(n, device="cuda")
+    pb = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    po, mo, vo = p0.astype(np.float64), np.zeros(n), np.zeros(n)
+    snap = None
+    for t, g in enumerate(grads, start=1):
+        pre = p.cpu().numpy().astype(np.float64)
+        L.adam_step(p, dev_f32(g), m, v, t, 1e-4, 0.9, 0.999, 1e-8, 0.01, pb)
+        # per-call parity: the oracle steps from the GPU's own state
+        po, mo2, vo2 = OA.adam_step(pre, g, mo, vo, t, 1e-4, 0.9, 0.999, 1e-8, 0.01)
+        # Delta p at 1e-4 of its scale, plus the fp32 spacing of p itself: the
+        # stored parameter cannot resolve a step finer than one ulp of p
+        dp, dp_ref = p.cpu().numpy() - pre, po - pre
+        scale = np.maximum(np.abs(dp_ref), np.sqrt(np.mean(dp_ref ** 2)))
+        ulp = np.spacing(np.abs(po).astype(np.float32)).astype(np.float64)
+        assert np.all(np.abs(dp - dp_ref) <= TOL_F32 * scale + ulp)
+        assert rel_err(m.cpu().numpy(), mo2) < TOL_F32 and rel_err(v.cpu().numpy(), vo2) < TOL_F32
+        mo, vo = m.cpu().numpy().astype(np.float64), v.cpu().numpy().astype(np.float64)
+        assert np.array_equal(bits_of(pb), W.to_bf16_bits(p.cpu().numpy()))
+        if t == 2:
+            snap = (p.clone(), m.clone(), v.clone())
+    # resume from the step-2 snapshot: bitwise identical to the straight run
+    p2, m2, v2 = snap
+    for t, g in enumerate(grads[2:], start=3):
+        L.adam_step(p2, dev_f32(g), m2, v2, t, 1e-4, 0.9, 0.999, 1e-8, 0.01, None)
+    assert torch.equal(p2, p) and torch.equal(m2, m) and torch.equal(v2, v)
+
+
+def test_swiglu_parity():
+    rng = np.random.default_rng(7)
+    n = 3 * 1000 + 5
+    gb = W.to_bf16_bits(rng.standard_normal(n) * 3)
+    ub = W.to_bf16_bits(rng.standard_normal(n))
+    db = W.to_bf16_bits(rng.standard_normal(n))
+    g, u, d = dev_bf16(gb), dev_bf16(ub), dev_bf16(db)
+    h = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    L.swiglu_forward(g, u, h)
+    gf, uf, df = (W.bf16_bits_to_f64(x) for x in (gb, ub, db))
+    assert rel_err(f64_of(h), OM.swiglu_forward(gf, uf)) < TOL_BF16
+    dg = torch.empty_like(h); du = torch.empty_like(h)
+    L.swiglu_backward(d, g, u, dg, du)
+    rg, ru = OM.swiglu_backward(df, gf, uf)
+    assert rel_err(f64_of(dg), rg) < TOL_BF16 and rel_err(f64_of(du), ru) < TOL_BF16
