@@ -55,7 +55,9 @@ def test_segments_flags_invalid_and_unsorted():
 # ---------------------------------------------------------------- layer cases
 def _case(kind):
     if kind == "tiny":        # the tiny oracle-check layer: d=256, 4 x r8, 512 sorted tokens
-        return W.tiny_chain(1).layer
+        lay = W.tiny_chain(1).layer
+        lay.dy_bits = W.to_bf16_bits(np.random.default_rng(11).standard_normal((lay.n_tokens, lay.d_out)))
+        return lay
     if kind == "ragged":      # 5 adapters, mixed ranks, interleaved, ragged everything
         rng = np.random.default_rng(21)
         ids = rng.integers(0, 5, size=700).astype(np.int32)
