@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target wall time of the oracle sample")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
+                    help="only run a plain device copy of MB megabytes 5 times (calibrates "
+                         "the FETCH_SIZE / WRITE_SIZE counters against known bytes) and exit")
     return ap.parse_args()
 
 
@@ -104,6 +107,16 @@ def main():
         sys.exit(2)
     import numpy as np
     import torch
+
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "launches": 5}))
+        return
 
     import rl_lora_linear_amd.lib as L
     import workloads as W

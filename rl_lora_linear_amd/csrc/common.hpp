@@ -62,6 +62,15 @@ __device__ __forceinline__ void set_flag(int32_t* status, int32_t bit) {
   __hip_atomic_fetch_or(status, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// ---------------------------------------------------------------- LDS swizzle
+// For LDS tiles whose rows hold eight 16-byte chunks: chunk c of row r lives at
+// physical chunk c ^ lds_sw(r), lds_sw(r) = (r & 7) ^ ((r >> 3) & 1).  The
+// 16-byte reads of 16 consecutive rows at one logical chunk then land in 16
+// distinct (row parity, chunk) slots -- conflict-free whether the LDS serves 8
+// or 16 lanes of a ds_read_b128 per clock (gfx950 serves 16; with plain (r & 7)
+// rows r and r + 8 collide).
+__device__ __forceinline__ int lds_sw(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+
 // ---------------------------------------------------------------- misc
 __host__ __device__ __forceinline__ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 __host__ __device__ __forceinline__ int64_t align_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }

@@ -7,11 +7,14 @@
 //
 // Block tile 256 x 256 x 64, 256 threads = 4 waves in a 2 x 2 grid, each wave
 // 128 x 128 as 4 x 4 tiles of v_mfma_f32_32x32x16_bf16 (256 fp32 accumulators
-// per lane).  Global -> register -> LDS staging, double-buffered (2 x 64 KB of
-// LDS), one barrier per K step; the global loads of step k+1 are issued before
-// the MFMAs of step k.  LDS rows are 128 B (64 bf16) and their 16-byte chunks
-// are XOR-swizzled by (row & 7), so the 16-byte fragment reads of 8 consecutive
-// rows hit distinct banks.  Tiles are ordered XCD-first (blocks are dispatched
+// per lane, in AGPRs).  Operand tiles move global -> LDS by LDS-DMA into a
+// 4-stage ring of k = 32 slices (128 KB), three stages ahead; one barrier
+// per stage; LDS fragment reads run one 16-wide k slice ahead of the MFMAs
+// (including the first slice of the next stage, read before the barrier).
+// LDS rows are 64 B and their 16-byte chunks are XOR-swizzled (g4) so the
+// fragment reads of 16 consecutive rows hit distinct banks.  The MFMA computes the transposed
+// sub-tile so that each lane ends with runs of 4 consecutive output columns
+// (8-byte stores; row reductions need one cross-lane step).  Tiles are ordered XCD-first (blocks are dispatched
 // round-robin over the 8 XCDs, so each XCD gets a contiguous tile range and
 // its own L2 sees the reuse) and then in groups of `group_m` row tiles.
 #include "common.hpp"
@@ -31,12 +34,54 @@ struct GemmEpi {
   const float* dlogp;     // EPI_GRAD: [M]
 };
 
-constexpr int GBM = 256, GBN = 256, GBK = 64;
-constexpr int G_CHUNKS = GBK / 8;            // 16-byte chunks per LDS row
-constexpr int G_TILE_U4 = GBM * G_CHUNKS;    // uint4 per operand tile
+constexpr int GBM = 256, GBN = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 
-__device__ __forceinline__ int lds_idx(int row, int chunk) { return row * G_CHUNKS + (chunk ^ (row & 7)); }
+
+// Operand movement: gfx950 LDS-DMA (global_load_lds_dwordx4), 4 LDS stages
+// of BK = 32 (each stage: A and B tiles of 256 rows x 64 B = 16 KB), issued
+// three steps ahead.  The DMA is issued from inline assembly with explicit
+// vmcnt waits: the compiler's own counter bookkeeping for LDS-DMA would force
+// a full wait before every LDS read (it cannot tell which stage a DMA writes).
+// Each wave issues exactly 8 DMA instructions per step (4 for A, 4 for B), so
+// "vmcnt <= 8" at the end of step k means every stage up to k + 2 has landed.
+// Rows past the matrix edge are clamped to the last row: they only feed
+// output rows or columns that are never stored.
+constexpr int SBK = 32;                    // k per stage
+constexpr int S_CH = SBK / 8;              // 16-byte chunks per LDS row (4)
+constexpr int S_TILE = 256 * S_CH;         // uint4 per operand tile per stage
+constexpr int NSTAGE = 4;
+
+// Swizzle of a 4-chunk LDS row: chunk c of row r is stored at c ^ g4(r).
+// The 16-byte reads of 16 consecutive rows at one logical chunk then hit 16
+// distinct (row mod 4, chunk) slots (conflict-free for 16 lanes per clock),
+// and 8 consecutive rows hit 8 distinct (row mod 2, chunk) slots.
+__device__ __forceinline__ int g4(int r) { return ((r >> 1) & 3) ^ ((r >> 3) & 1); }
+
+__shared__ uint4 g_stage[2 * NSTAGE * S_TILE];  // [A s0..s3][B s0..s3], 128 KB
+
+__device__ __forceinline__ uint32_t lds_addr(const uint4* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+}
+
+// One operand tile of one stage: 16 row blocks of 16 rows (64 slots each);
+// wave w issues blocks 4w..4w+3.  Lane L lands in slot L of its block: row
+// L/4, physical chunk L%4, so it fetches logical chunk (L%4) ^ g4(L/4).
+__device__ __forceinline__ void dma_stage(const uint16_t* __restrict__ src, int64_t ld, int r0,
+                                          int rlim, int k0, uint4* tile, int wave, int lane) {
+  const int lrow = lane >> 2;
+  const int chunk = (lane & 3) ^ g4(lrow);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int blk = wave * 4 + i;
+    int row = r0 + blk * 16 + lrow;
+    row = row < rlim ? row : rlim - 1;
+    const uint16_t* g = src + (int64_t)row * ld + k0 + chunk * 8;
+    const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr(tile + blk * 64));
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0v), "v"(g)
+                 : "memory");
+  }
+}
 
 template <int EPI>
 __global__ __launch_bounds__(256, 1) void gemm_nt_kernel(const uint16_t* __restrict__ A,
@@ -44,10 +89,6 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_kernel(const uint16_t* __restr
                                                          int N, int K, int64_t lda, int64_t ldb,
                                                          GemmEpi ep, int tiles_m, int tiles_n,
                                                          int group_m) {
-  extern __shared__ uint4 smem[];  // [2][A tile] [2][B tile]
-  uint4* As = smem;
-  uint4* Bs = smem + 2 * G_TILE_U4;
-
   // ---- tile id: XCD-contiguous, then grouped along M
   const int num = tiles_m * tiles_n;
   const int bid = blockIdx.x;
@@ -68,28 +109,9 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_kernel(const uint16_t* __restr
   const int wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
-  // ---- global load mapping: 8 threads per 128-byte row, 32 rows per pass
-  const int ld_row = tid >> 3, ld_chunk = tid & 7;
-  const uint16_t* a_base = A + (int64_t)(m0 + ld_row) * lda + ld_chunk * 8;
-  const uint16_t* b_base = B + (int64_t)(n0 + ld_row) * ldb + ld_chunk * 8;
-  const int64_t a_step = 32 * lda, b_step = 32 * ldb;
-  const int a_lim = M - m0 - ld_row;  // pass i is in range iff 32*i < a_lim
-  const int b_lim = N - n0 - ld_row;
-  uint4 ra[8], rb[8];
-
-#define GEMM_GLOAD(k0)                                                                 \
-  _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                       \
-    ra[i] = (32 * i < a_lim) ? *(const uint4*)(a_base + i * a_step + (k0))              \
-                             : make_uint4(0, 0, 0, 0);                                  \
-    rb[i] = (32 * i < b_lim) ? *(const uint4*)(b_base + i * b_step + (k0))              \
-                             : make_uint4(0, 0, 0, 0);                                  \
-  }
-#define GEMM_SSTORE(buf)                                                               \
-  _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                       \
-    As[(buf) * G_TILE_U4 + lds_idx(ld_row + 32 * i, ld_chunk)] = ra[i];                 \
-    Bs[(buf) * G_TILE_U4 + lds_idx(ld_row + 32 * i, ld_chunk)] = rb[i];                 \
-  }
-
+  // acc[i][j] holds the transposed 32x32 sub-tile: register g of lane l is
+  // C[m = wm*128 + i*32 + l%32][n = wn*128 + j*32 + 8*(g/4) + 4*(l/32) + g%4],
+  // so each lane owns runs of 4 consecutive output columns.
   f32x16 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -98,94 +120,150 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_kernel(const uint16_t* __restr
 #pragma unroll
       for (int g = 0; g < 16; ++g) acc[i][j][g] = 0.f;
 
-  const int KT = K / GBK;
-  GEMM_GLOAD(0);
-  GEMM_SSTORE(0);
-  __syncthreads();
+  const int KT = K / SBK;
+  uint4* sA = g_stage;
+  uint4* sB = g_stage + NSTAGE * S_TILE;
+
+  // prologue: stages 0..2 in flight, wait for 0 and 1
+#pragma unroll
+  for (int s = 0; s < NSTAGE - 1; ++s) {
+    const int k0 = min(s, KT - 1) * SBK;
+    dma_stage(A, lda, m0, M, k0, sA + s * S_TILE, wave, lane);
+    dma_stage(B, ldb, n0, N, k0, sB + s * S_TILE, wave, lane);
+  }
+  asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
 
   const int frag_row = lane & 31;   // row within a 32-row MFMA tile
-  const int frag_half = lane >> 5;  // which 8-wide k half of the 16-wide k slice
+  const int frag_half = lane >> 5;  // which 8-wide k half of a 16-wide k slice
+  const int sw = g4(frag_row);      // swizzle of every fragment row of this lane
+  int a_row[4], b_row[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    a_row[i] = (wm * 128 + i * 32 + frag_row) * S_CH;
+    b_row[i] = (wn * 128 + i * 32 + frag_row) * S_CH;
+  }
+  const int c0 = frag_half ^ sw;         // slice 0 chunk
+  const int c1 = (2 + frag_half) ^ sw;   // slice 1 chunk
 
-  for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < KT) { GEMM_GLOAD((kt + 1) * GBK); }
-    const uint4* At = As + buf * G_TILE_U4;
-    const uint4* Bt = Bs + buf * G_TILE_U4;
+  bf16x8 f0a[4], f0b[4], f1a[4], f1b[4];
 #pragma unroll
-    for (int kk = 0; kk < GBK / 16; ++kk) {
-      const int c = 2 * kk + frag_half;
-      bf16x8 af[4], bfr[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) af[i] = as_bf16x8(At[lds_idx(wm * 128 + i * 32 + frag_row, c)]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) bfr[j] = as_bf16x8(Bt[lds_idx(wn * 128 + j * 32 + frag_row, c)]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
-    }
-    if (kt + 1 < KT) { GEMM_SSTORE(buf ^ 1); }
-    __syncthreads();
+  for (int i = 0; i < 4; ++i) {
+    f0a[i] = as_bf16x8(sA[a_row[i] + c0]);
+    f0b[i] = as_bf16x8(sB[b_row[i] + c0]);
   }
 
-#undef GEMM_GLOAD
-#undef GEMM_SSTORE
-
-  // ---- epilogues.  Accumulator layout of a 32x32 tile: register g of lane l
-  // holds row 8*(g/4) + 4*(l/32) + (g%4), column l%32.
-  const int col_l = lane & 31;
-  const int row_q = 4 * (lane >> 5);
-
-  if constexpr (EPI == EPI_BF16) {
+  for (int kt = 0; kt < KT; ++kt) {
+    const int s = kt & (NSTAGE - 1);
+    const uint4* At = sA + s * S_TILE;
+    const uint4* Bt = sB + s * S_TILE;
+    {  // DMA of step kt + 3 into the stage consumed at step kt - 1 (re-fetch past the end)
+      const int sn = (kt + NSTAGE - 1) & (NSTAGE - 1);
+      const int k0 = min(kt + NSTAGE - 1, KT - 1) * SBK;
+      dma_stage(A, lda, m0, M, k0, sA + sn * S_TILE, wave, lane);
+      dma_stage(B, ldb, n0, N, k0, sB + sn * S_TILE, wave, lane);
+    }
+    // phase 0: read slice 1 of this stage; MFMAs of slice 0
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f1a[i] = as_bf16x8(At[a_row[i] + c1]);
+      f1b[i] = as_bf16x8(Bt[b_row[i] + c1]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int col = n0 + wn * 128 + j * 32 + col_l;
-        if (col >= N) continue;
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(f0b[j], f0a[i], acc[i][j]);
+    __builtin_amdgcn_sched_barrier(0);
+    // phase 1: read slice 0 of the next stage (complete since the last
+    // barrier; on the last step the values are simply unused); MFMAs of
+    // slice 1.  Unconditional, so no branch forces a full LDS wait.
+    {
+      const uint4* An = sA + ((s + 1) & (NSTAGE - 1)) * S_TILE;
+      const uint4* Bn = sB + ((s + 1) & (NSTAGE - 1)) * S_TILE;
 #pragma unroll
-        for (int g = 0; g < 16; ++g) {
-          const int row = m0 + wm * 128 + i * 32 + 8 * (g >> 2) + row_q + (g & 3);
-          if (row < M) ep.C[(int64_t)row * ep.ldc + col] = f2bf(acc[i][j][g]);
-        }
+      for (int i = 0; i < 4; ++i) {
+        f0a[i] = as_bf16x8(An[a_row[i] + c0]);
+        f0b[i] = as_bf16x8(Bn[b_row[i] + c0]);
       }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(f1b[j], f1a[i], acc[i][j]);
+    __builtin_amdgcn_sched_barrier(0);
+    // stage kt + 2 has landed for this wave; after the barrier, for all waves
+    asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no DMA may outlive the block
+
+  // ---- epilogues
+  const int m_l = lane & 31;
+  const int n_q = 4 * (lane >> 5);
+
+  if constexpr (EPI == EPI_BF16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = m0 + wm * 128 + i * 32 + m_l;
+      if (row >= M) continue;
+      uint16_t* crow = ep.C + (int64_t)row * ep.ldc;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = n0 + wn * 128 + j * 32 + 8 * q + n_q;
+          if (col >= N) continue;
+          const uint2 v = make_uint2(pack2bf(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
+                                     pack2bf(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]));
+          *(uint2*)(crow + col) = v;
+        }
+    }
   } else if constexpr (EPI == EPI_LSE) {
-    __shared__ int32_t tgt_s[GBM];
     __shared__ float2 red_s[2][GBM];
-    for (int r = tid; r < GBM; r += 256) tgt_s[r] = (m0 + r < M) ? ep.targets[m0 + r] : -1;
-    __syncthreads();
     const int cbase = n0 + wn * 128;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+      const int rl = wm * 128 + i * 32 + m_l;
+      const int row = m0 + rl;
+      // this lane's 64 values of row `row`: columns cbase + j*32 + 8q + n_q + e
+      float mx = -INFINITY;
 #pragma unroll
-      for (int g = 0; g < 16; ++g) {
-        const int rl = wm * 128 + i * 32 + 8 * (g >> 2) + row_q + (g & 3);
-        float mx = -INFINITY;
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (cbase + j * 32 + 8 * q + n_q + e < N) mx = fmaxf(mx, acc[i][j][4 * q + e]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      float sm = 0.f;
+      if (mx != -INFINITY) {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          if (cbase + j * 32 + col_l < N) mx = fmaxf(mx, acc[i][j][g]);
 #pragma unroll
-        for (int o = 1; o < 32; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-        float sm = 0.f;
-        if (mx != -INFINITY) {
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (cbase + j * 32 + 8 * q + n_q + e < N)
+                sm += exp2f((acc[i][j][4 * q + e] - mx) * kLog2e);
+      }
+      sm += __shfl_xor(sm, 32);
+      if (row < M) {
+        const int yo = ep.targets[row] - cbase;
+        // column offset yo = j*32 + 8q + n_q + e
+        if (yo >= 0 && yo < 128 && cbase + yo < N && ((yo >> 2) & 1) == (lane >> 5)) {
+          const int jj = yo >> 5, qq = (yo >> 3) & 3, ee = yo & 3;
+          float zv = 0.f;
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            if (cbase + j * 32 + col_l < N) sm += exp2f((acc[i][j][g] - mx) * kLog2e);
-        }
 #pragma unroll
-        for (int o = 1; o < 32; o <<= 1) sm += __shfl_xor(sm, o);
-        const int y = tgt_s[rl];
-        const int yo = y - cbase;
-        if (yo >= 0 && yo < 128 && (yo & 31) == col_l && m0 + rl < M) {
-          const int jj = yo >> 5;
-          float zv = acc[i][0][g];
+            for (int q = 0; q < 4; ++q)
 #pragma unroll
-          for (int j = 1; j < 4; ++j)
-            if (j == jj) zv = acc[i][j][g];
-          if (y < N) ep.zt[m0 + rl] = zv;
+              for (int e = 0; e < 4; ++e)
+                if (j == jj && q == qq && e == ee) zv = acc[i][j][4 * q + e];
+          ep.zt[row] = zv;
         }
-        if (col_l == 0) red_s[wn][rl] = make_float2(mx, sm);
       }
+      if (lane < 32) red_s[wn][rl] = make_float2(mx, sm);
     }
     __syncthreads();
     for (int r = tid; r < GBM; r += 256) {
@@ -199,39 +277,33 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_kernel(const uint16_t* __restr
       ep.part_s[(int64_t)tn * M + m0 + r] = sm;
     }
   } else {  // EPI_GRAD
-    __shared__ int32_t tgt_s[GBM];
-    __shared__ float lse_s[GBM];
-    __shared__ float d_s[GBM];
-    for (int r = tid; r < GBM; r += 256) {
-      const bool ok = m0 + r < M;
-      int y = ok ? ep.targets[m0 + r] : -1;
-      float d = ok ? ep.dlogp[m0 + r] : 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = m0 + wm * 128 + i * 32 + m_l;
+      if (row >= M) continue;
+      int y = ep.targets[row];
+      float d = ep.dlogp[row];
       if (y < 0 || y >= N) d = 0.f;  // invalid target: zero row
-      tgt_s[r] = y;
-      lse_s[r] = ok ? ep.lse[m0 + r] : 0.f;
-      d_s[r] = d;
-    }
-    __syncthreads();
+      const float l = ep.lse[row];
+      uint16_t* grow = ep.C + (int64_t)row * ep.ldc;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int g = 0; g < 16; ++g) {
-        const int rl = wm * 128 + i * 32 + 8 * (g >> 2) + row_q + (g & 3);
-        if (m0 + rl >= M) continue;
-        const float d = d_s[rl], l = lse_s[rl];
-        const int y = tgt_s[rl];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int col = n0 + wn * 128 + j * 32 + col_l;
+        for (int q = 0; q < 4; ++q) {
+          const int col = n0 + wn * 128 + j * 32 + 8 * q + n_q;
           if (col >= N) continue;
-          float gv = 0.f;
-          if (d != 0.f) {
-            const float p = exp2f((acc[i][j][g] - l) * kLog2e);
-            gv = d * ((col == y ? 1.f : 0.f) - p);
+          float gv[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            gv[e] = 0.f;
+            if (d != 0.f) {
+              const float p = exp2f((acc[i][j][4 * q + e] - l) * kLog2e);
+              gv[e] = d * ((col + e == y ? 1.f : 0.f) - p);
+            }
           }
-          ep.C[(int64_t)(m0 + rl) * ep.ldc + col] = f2bf(gv);
+          *(uint2*)(grow + col) = make_uint2(pack2bf(gv[0], gv[1]), pack2bf(gv[2], gv[3]));
         }
-      }
+    }
   }
 }
 
@@ -241,7 +313,7 @@ namespace lora_host {
 
 using namespace lora;
 
-static int pick_group_m(int tiles_m) { return tiles_m < 8 ? tiles_m : 8; }
+static int pick_group_m(int tiles_m) { return tiles_m < 4 ? tiles_m : 4; }
 
 template <int EPI>
 static lora_status launch_gemm(const uint16_t* A, const uint16_t* B, int M, int N, int K,
@@ -251,7 +323,7 @@ static lora_status launch_gemm(const uint16_t* A, const uint16_t* B, int M, int 
   const int tiles_m = (int)cdiv(M, GBM), tiles_n = (int)cdiv(N, GBN);
   if (group_m <= 0) group_m = pick_group_m(tiles_m);
   if (group_m > tiles_m) group_m = tiles_m;
-  const size_t lds = 4 * G_TILE_U4 * sizeof(uint4);
+  const size_t lds = 0;  // operand tiles are static LDS objects
   static bool attr_set = false;
   if (!attr_set) {
     hipFuncSetAttribute((const void*)gemm_nt_kernel<EPI>,

@@ -25,8 +25,8 @@
 
 namespace lora {
 
-// XOR-swizzled index of a 16-byte chunk in an LDS tile whose rows hold 8 chunks.
-__device__ __forceinline__ int sw8(int row, int chunk) { return row * 8 + (chunk ^ (row & 7)); }
+// Swizzled index of a 16-byte chunk in an LDS tile whose rows hold 8 chunks.
+__device__ __forceinline__ int sw8(int row, int chunk) { return row * 8 + (chunk ^ lds_sw(row)); }
 
 struct TileInfo {
   int a;
@@ -339,7 +339,7 @@ __global__ __launch_bounds__(256) void grad_kernel(
         float f = (ok && c < r) ? pp[c] : 0.f;
         uint16_t h, l;
         split_bf16(f, h, l);
-        const int idx = c * 64 + (((pt >> 3) ^ (c & 7)) << 3) + (pt & 7);
+        const int idx = c * 64 + (((pt >> 3) ^ lds_sw(c)) << 3) + (pt & 7);
         Ph16[idx] = h;
         Pl16[idx] = l;
       }
