@@ -247,17 +247,15 @@ lora_status lora_forward(const lora_shape* shape, const uint16_t* x, const uint1
   const int N = (int)sh.n_tokens;
   TRY(layer_segments(sh, desc, adapter_ids, w, s));
   if (N == 0) return LORA_OK;
-  timer_begin(LORA_TIMER_BASE_GEMM, s);
-  TRY(gemm_nt_bf16(x, W, y, N, (int)sh.d_out, (int)sh.d_in, sh.d_in, sh.d_in, sh.d_out, s));
-  timer_end(LORA_TIMER_BASE_GEMM, s);
   timer_begin(LORA_TIMER_SHRINK, s);
   TRY(launch_shrink(x, sh.d_in, (int)sh.d_in, A_pack, 0, desc, w.active, w.perm, w.offsets,
                     w.pre16, sh.n_adapters, sh.n_tokens, u_saved, sh.max_rank, s));
   timer_end(LORA_TIMER_SHRINK, s);
-  timer_begin(LORA_TIMER_EXPAND, s);
-  TRY(launch_expand(u_saved, sh.max_rank, B_pack, 1, desc, w.perm, w.offsets, w.pre64,
-                    sh.n_adapters, sh.n_tokens, y, sh.d_out, (int)sh.d_out, s));
-  timer_end(LORA_TIMER_EXPAND, s);
+  // base GEMM over rows in segment order with the expand y += s B_a u fused
+  LoraFuse f{w.perm, u_saved, sh.max_rank, 1, B_pack, desc, w.active, w.offsets, sh.n_adapters};
+  timer_begin(LORA_TIMER_BASE_GEMM, s);
+  TRY(gemm_nt_lora(x, W, y, N, (int)sh.d_out, (int)sh.d_in, sh.d_in, sh.d_in, sh.d_out, f, s));
+  timer_end(LORA_TIMER_BASE_GEMM, s);
   return LORA_OK;
 }
 
@@ -288,13 +286,15 @@ lora_status lora_backward(const lora_shape* shape, const uint16_t* dy, const uin
   TRY(launch_adapter_transpose(A_pack, B_pack, desc, w.active, sh.n_adapters, sh.d_in, sh.d_out,
                                w.AT, w.BT, s));
   if (N > 0) {
-    timer_begin(LORA_TIMER_BASE_GEMM, s);
-    TRY(gemm_nt_bf16(dy, W_t, dx, N, (int)sh.d_in, (int)sh.d_out, sh.d_out, sh.d_out, sh.d_in, s));
-    timer_end(LORA_TIMER_BASE_GEMM, s);
     timer_begin(LORA_TIMER_SHRINK, s);
     TRY(launch_shrink(dy, sh.d_out, (int)sh.d_out, w.BT, 1, desc, w.active, w.perm, w.offsets,
                       w.pre16, sh.n_adapters, sh.n_tokens, w.v, sh.max_rank, s));
     timer_end(LORA_TIMER_SHRINK, s);
+    // dX = dY W over rows in segment order with the expand dX += s A_a^T v fused
+    LoraFuse f{w.perm, w.v, sh.max_rank, 0, w.AT, desc, w.active, w.offsets, sh.n_adapters};
+    timer_begin(LORA_TIMER_BASE_GEMM, s);
+    TRY(gemm_nt_lora(dy, W_t, dx, N, (int)sh.d_in, (int)sh.d_out, sh.d_out, sh.d_out, sh.d_in, f, s));
+    timer_end(LORA_TIMER_BASE_GEMM, s);
   }
   timer_begin(LORA_TIMER_GRAD, s);
   TRY(launch_grad(0, u_saved, sh.max_rank, dy, sh.d_out, (int)sh.d_out, desc, w.active, w.perm,
@@ -302,12 +302,6 @@ lora_status lora_backward(const lora_shape* shape, const uint16_t* dy, const uin
   TRY(launch_grad(1, w.v, sh.max_rank, x, sh.d_in, (int)sh.d_in, desc, w.active, w.perm, w.offsets,
                   w.prec, sh.n_adapters, sh.n_tokens, dA_pack, w.partial, accumulate, s));
   timer_end(LORA_TIMER_GRAD, s);
-  if (N > 0) {
-    timer_begin(LORA_TIMER_EXPAND, s);
-    TRY(launch_expand(w.v, sh.max_rank, w.AT, 0, desc, w.perm, w.offsets, w.pre64, sh.n_adapters,
-                      sh.n_tokens, dx, sh.d_in, (int)sh.d_in, s));
-    timer_end(LORA_TIMER_EXPAND, s);
-  }
   return LORA_OK;
 }
 

@@ -18,6 +18,7 @@
 // round-robin over the 8 XCDs, so each XCD gets a contiguous tile range and
 // its own L2 sees the reuse) and then in groups of `group_m` row tiles.
 #include "common.hpp"
+#include "sgmv.hpp"
 
 namespace lora {
 
@@ -26,6 +27,19 @@ enum { EPI_BF16 = 0, EPI_LSE = 1, EPI_GRAD = 2 };
 struct GemmEpi {
   uint16_t* C;            // EPI_BF16 / EPI_GRAD output
   int64_t ldc;
+  // Rows in segment order: row m of A and C is token perm[m] (nullable).
+  const int32_t* perm;
+  // EPI_BF16 with the LoRA expand fused (nullable vec = plain GEMM): for the
+  // row at segment position m, owned by adapter a, add s_a * vec[tok] . M_a^T
+  // where M_a [N][r_a] sits at (use_b_off ? b_off : a_off) of the pack lmat.
+  const float* vec;       // [tokens][vec_ld] fp32, token order
+  int vec_ld;
+  int use_b_off;
+  const uint16_t* lmat;
+  const lora_adapter_desc* desc;
+  const uint8_t* active;
+  const int32_t* offsets; // [n_ad + 1] segment offsets (positions)
+  int n_ad;
   float* part_m;          // EPI_LSE: [tiles_n][M]
   float* part_s;          // EPI_LSE: [tiles_n][M]
   float* zt;              // EPI_LSE: [M] target logit
@@ -67,19 +81,81 @@ __device__ __forceinline__ uint32_t lds_addr(const uint4* p) {
 // One operand tile of one stage: 16 row blocks of 16 rows (64 slots each);
 // wave w issues blocks 4w..4w+3.  Lane L lands in slot L of its block: row
 // L/4, physical chunk L%4, so it fetches logical chunk (L%4) ^ g4(L/4).
-__device__ __forceinline__ void dma_stage(const uint16_t* __restrict__ src, int64_t ld, int r0,
-                                          int rlim, int k0, uint4* tile, int wave, int lane) {
-  const int lrow = lane >> 2;
-  const int chunk = (lane & 3) ^ g4(lrow);
+// rowp[i] is this lane's source row (block 4w+i) at k = 0, chunk included.
+__device__ __forceinline__ void dma_rows(const uint16_t* const (&rowp)[4], int k0, uint4* tile,
+                                         int wave) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int blk = wave * 4 + i;
-    int row = r0 + blk * 16 + lrow;
-    row = row < rlim ? row : rlim - 1;
-    const uint16_t* g = src + (int64_t)row * ld + k0 + chunk * 8;
-    const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr(tile + blk * 64));
+    const uint16_t* g = rowp[i] + k0;
+    const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr(tile + (wave * 4 + i) * 64));
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0v), "v"(g)
                  : "memory");
+  }
+}
+
+// Fused LoRA expand: for every adapter a owning rows of this tile (rows are
+// segment positions, so a 256-row tile spans one adapter or a few), add
+// s_a * vec[tok] . M_a^T to the accumulators as an extra MFMA K-slab of depth
+// r_a.  The fp32 vector is scaled by s_a and split into hi + lo bf16 parts
+// (two MFMAs) so the slab keeps ~16 significant bits; M_a is bf16-exact.
+// Rows of other adapters contribute zero fragments.
+__device__ __forceinline__ void lora_slab(const GemmEpi& ep, int m0, int n0, int M, int N, int wm,
+                                       int wn, int lane, f32x16 (&acc)[4][4]) {
+  const int m_l = lane & 31;
+  const int half = lane >> 5;
+  const int n_end = ep.offsets[ep.n_ad];  // positions past it are tokens with invalid ids
+  const int last = min(m0 + GBM, min(M, n_end)) - 1;
+  if (last < m0) return;
+  const int a0 = find_bucket(ep.offsets, ep.n_ad + 1, m0);
+  const int a1 = find_bucket(ep.offsets, ep.n_ad + 1, last);
+  int ad[4], tk[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = m0 + wm * 128 + i * 32 + m_l;
+    const bool ok = row < M && row < n_end;
+    ad[i] = ok ? find_bucket(ep.offsets, ep.n_ad + 1, row) : -1;
+    tk[i] = ok ? (ep.perm ? ep.perm[row] : row) : 0;
+  }
+  for (int a = a0; a <= a1; ++a) {
+    if (!ep.active[a] || ep.offsets[a + 1] == ep.offsets[a]) continue;
+    const lora_adapter_desc d = ep.desc[a];
+    const int r = d.rank;
+    const uint16_t* mat = ep.lmat + (ep.use_b_off ? d.b_off : d.a_off);
+    for (int sl = 0; sl * 16 < r; ++sl) {
+      const int c = sl * 16 + 8 * half;
+      const bool cok = c < r;
+      bf16x8 ah[4], al[4], bm[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint4 h = make_uint4(0, 0, 0, 0), l = make_uint4(0, 0, 0, 0);
+        if (ad[i] == a && cok) {
+          const float4* vp = (const float4*)(ep.vec + (int64_t)tk[i] * ep.vec_ld + c);
+          const float4 x0 = vp[0], x1 = vp[1];
+          const float f[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+          uint16_t hh[8], ll[8];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) split_bf16(d.scale * f[q], hh[q], ll[q]);
+          h = make_uint4(hh[0] | (hh[1] << 16), hh[2] | (hh[3] << 16), hh[4] | (hh[5] << 16), hh[6] | (hh[7] << 16));
+          l = make_uint4(ll[0] | (ll[1] << 16), ll[2] | (ll[3] << 16), ll[4] | (ll[5] << 16), ll[6] | (ll[7] << 16));
+        }
+        ah[i] = as_bf16x8(h);
+        al[i] = as_bf16x8(l);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int n = n0 + wn * 128 + j * 32 + m_l;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (n < N && cok) v = *(const uint4*)(mat + (int64_t)n * r + c);
+        bm[j] = as_bf16x8(v);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc[i][j] = mfma32(bm[j], ah[i], acc[i][j]);
+          acc[i][j] = mfma32(bm[j], al[i], acc[i][j]);
+        }
+    }
   }
 }
 
@@ -124,12 +200,30 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_kernel(const uint16_t* __restr
   uint4* sA = g_stage;
   uint4* sB = g_stage + NSTAGE * S_TILE;
 
+  // this lane's DMA source rows (rows past the edge clamped to the last row:
+  // they only feed outputs that are never stored)
+  const uint16_t* rowA[4];
+  const uint16_t* rowB[4];
+  {
+    const int lrow = lane >> 2;
+    const int chunk = (lane & 3) ^ g4(lrow);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int blk = wave * 4 + i;
+      int ra = min(m0 + blk * 16 + lrow, M - 1);
+      if (ep.perm) ra = ep.perm[ra];
+      const int rb = min(n0 + blk * 16 + lrow, N - 1);
+      rowA[i] = A + (int64_t)ra * lda + chunk * 8;
+      rowB[i] = B + (int64_t)rb * ldb + chunk * 8;
+    }
+  }
+
   // prologue: stages 0..2 in flight, wait for 0 and 1
 #pragma unroll
   for (int s = 0; s < NSTAGE - 1; ++s) {
     const int k0 = min(s, KT - 1) * SBK;
-    dma_stage(A, lda, m0, M, k0, sA + s * S_TILE, wave, lane);
-    dma_stage(B, ldb, n0, N, k0, sB + s * S_TILE, wave, lane);
+    dma_rows(rowA, k0, sA + s * S_TILE, wave);
+    dma_rows(rowB, k0, sB + s * S_TILE, wave);
   }
   asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
 
@@ -159,8 +253,8 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_kernel(const uint16_t* __restr
     {  // DMA of step kt + 3 into the stage consumed at step kt - 1 (re-fetch past the end)
       const int sn = (kt + NSTAGE - 1) & (NSTAGE - 1);
       const int k0 = min(kt + NSTAGE - 1, KT - 1) * SBK;
-      dma_stage(A, lda, m0, M, k0, sA + sn * S_TILE, wave, lane);
-      dma_stage(B, ldb, n0, N, k0, sB + sn * S_TILE, wave, lane);
+      dma_rows(rowA, k0, sA + sn * S_TILE, wave);
+      dma_rows(rowB, k0, sB + sn * S_TILE, wave);
     }
     // phase 0: read slice 1 of this stage; MFMAs of slice 0
 #pragma unroll
@@ -202,11 +296,17 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_kernel(const uint16_t* __restr
   const int n_q = 4 * (lane >> 5);
 
   if constexpr (EPI == EPI_BF16) {
+    int tok[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = m0 + wm * 128 + i * 32 + m_l;
-      if (row >= M) continue;
-      uint16_t* crow = ep.C + (int64_t)row * ep.ldc;
+      tok[i] = row < M ? (ep.perm ? ep.perm[row] : row) : -1;
+    }
+    if (ep.vec) lora_slab(ep, m0, n0, M, N, wm, wn, lane, acc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (tok[i] < 0) continue;
+      uint16_t* crow = ep.C + (int64_t)tok[i] * ep.ldc;
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -340,6 +440,24 @@ lora_status gemm_nt_bf16(const uint16_t* A, const uint16_t* B, uint16_t* C, int 
   GemmEpi ep{};
   ep.C = C;
   ep.ldc = ldc;
+  return launch_gemm<EPI_BF16>(A, B, M, N, K, lda, ldb, ep, s, group_m);
+}
+
+lora_status gemm_nt_lora(const uint16_t* A, const uint16_t* B, uint16_t* C, int M, int N, int K,
+                         int64_t lda, int64_t ldb, int64_t ldc, const LoraFuse& f, hipStream_t s,
+                         int group_m) {
+  GemmEpi ep{};
+  ep.C = C;
+  ep.ldc = ldc;
+  ep.perm = f.perm;
+  ep.vec = f.vec;
+  ep.vec_ld = f.vec_ld;
+  ep.use_b_off = f.use_b_off;
+  ep.lmat = f.lmat;
+  ep.desc = f.desc;
+  ep.active = f.active;
+  ep.offsets = f.offsets;
+  ep.n_ad = f.n_ad;
   return launch_gemm<EPI_BF16>(A, B, M, N, K, lda, ldb, ep, s, group_m);
 }
 

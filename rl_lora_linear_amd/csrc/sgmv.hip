@@ -10,10 +10,8 @@
 //
 //   shrink   out[t][c] = sum_k in[t][k] M_a[c][k]      (u = A_a x, v = B_a^T g)
 //            16 rows per block, the four waves split K, one LDS reduction.
-//   expand   out[t][j] += s_a sum_c vec[t][c] M_a[j][c] (y += s B_a u, dx += s A_a^T v)
-//            64 rows x 256 columns per block; fp32 vec split into hi+lo bf16
-//            for MFMA; the fp32 delta is staged in LDS so the bf16
-//            read-modify-write of `out` is coalesced 16-byte vectors.
+//   (the expand y += s B_a u / dx += s A_a^T v runs inside the base GEMM's
+//    epilogue: gemm.hip, lora_slab)
 //   grad     T[c][j] = s_a sum_{t in chunk} P[t][c] Q[t][j]  (dB_a, dA_a)
 //            one block per (token chunk of an adapter, 256 columns); Q rows are
 //            register-transposed into LDS so both MFMA operands are
@@ -146,88 +144,6 @@ __global__ __launch_bounds__(256) void shrink_kernel(
     float* o = out + (int64_t)t * r_max + cg;
     // r_max is a multiple of 8, so the 4-float group is either inside or outside
     *(float4*)o = make_float4(v[0], v[1], v[2], v[3]);
-  }
-}
-
-// ------------------------------------------------------------------ expand
-// grid = (tile bound for 64-row tiles, ceil(n_cols / 256)).  Wave w owns rows
-// 16w..16w+15 of the tile and all 256 columns (16 MFMA tiles of 16x16).
-__global__ __launch_bounds__(256) void expand_kernel(
-    const float* __restrict__ vec, int r_max, const uint16_t* __restrict__ mat_pack,
-    int use_b_off, const lora_adapter_desc* __restrict__ desc, const int32_t* __restrict__ perm,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ pre64, int n_ad,
-    uint16_t* __restrict__ out, int64_t ld_out, int n_cols) {
-  TileInfo ti;
-  if (!tile_of(pre64, offsets, n_ad, blockIdx.x, 64, ti)) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const lora_adapter_desc d = desc[ti.a];
-  const int r = d.rank;
-  const float scale = d.scale;
-  const uint16_t* mat = mat_pack + (use_b_off ? d.b_off : d.a_off);
-  const int j0 = blockIdx.y * 256;
-
-  const int row = lane & 15;
-  const int prow = wave * 16 + row;
-  const int tok = prow < ti.rows ? perm[ti.p0 + prow] : -1;
-  const int ko = 8 * (lane >> 4);
-
-  f32x4 acc[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int kbn = (r + 31) / 32;
-  for (int kb = 0; kb < kbn; ++kb) {
-    const int c0 = kb * 32 + ko;
-    uint4 hi = make_uint4(0, 0, 0, 0), lo = make_uint4(0, 0, 0, 0);
-    if (tok >= 0 && c0 < r) {
-      const float4* vp = (const float4*)(vec + (int64_t)tok * r_max + c0);
-      float4 a = vp[0], b = vp[1];
-      float f[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-      uint16_t h[8], l[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) split_bf16(f[q], h[q], l[q]);
-      hi = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
-      lo = make_uint4(l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16), l[6] | (l[7] << 16));
-    }
-    const bf16x8 xh = as_bf16x8(hi), xl = as_bf16x8(lo);
-#pragma unroll
-    for (int nt = 0; nt < 16; ++nt) {
-      const int j = j0 + nt * 16 + (lane & 15);
-      uint4 mv = make_uint4(0, 0, 0, 0);
-      if (j < n_cols && c0 < r) mv = *(const uint4*)(mat + (int64_t)j * r + c0);
-      const bf16x8 mb = as_bf16x8(mv);
-      acc[nt] = mfma16(xh, mb, acc[nt]);
-      acc[nt] = mfma16(xl, mb, acc[nt]);
-    }
-  }
-
-  // stage the fp32 delta: this wave's 16 rows x 256 columns
-  __shared__ float stage[4][16][256 + 4];
-#pragma unroll
-  for (int nt = 0; nt < 16; ++nt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) stage[wave][4 * (lane >> 4) + i][nt * 16 + (lane & 15)] = acc[nt][i];
-  __syncthreads();
-  // read-modify-write: 32 lanes x 8 columns per row, two rows per pass
-  for (int pass = 0; pass < 8; ++pass) {
-    const int rr = pass * 2 + (lane >> 5);
-    const int pr = wave * 16 + rr;
-    if (pr >= ti.rows) continue;
-    const int t = perm[ti.p0 + pr];
-    const int cc = (lane & 31) * 8;
-    const int j = j0 + cc;
-    if (j >= n_cols) continue;
-    uint4* op = (uint4*)(out + (int64_t)t * ld_out + j);
-    uint4 o = *op;
-    const float* sp = &stage[wave][rr][cc];
-    uint32_t w[4] = {o.x, o.y, o.z, o.w};
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float a = bf2f_lo(w[q]) + scale * sp[2 * q];
-      const float b = bf2f_hi(w[q]) + scale * sp[2 * q + 1];
-      w[q] = pack2bf(a, b);
-    }
-    *op = make_uint4(w[0], w[1], w[2], w[3]);
   }
 }
 
@@ -474,19 +390,6 @@ lora_status launch_shrink(const uint16_t* in, int64_t ld_in, int K, const uint16
                      mat_pack, use_b_off, desc, active, perm, offsets, pre16, n_ad, n_tokens, out,
                      r_max);
   return launch_check("shrink");
-}
-
-lora_status launch_expand(const float* vec, int r_max, const uint16_t* mat_pack, int use_b_off,
-                          const lora_adapter_desc* desc, const int32_t* perm,
-                          const int32_t* offsets, const int32_t* pre64, int n_ad,
-                          int64_t n_tokens, uint16_t* out, int64_t ld_out, int n_cols,
-                          hipStream_t s) {
-  if (n_tokens <= 0) return LORA_OK;
-  const int64_t bound = cdiv(n_tokens, 64) + n_ad;
-  hipLaunchKernelGGL(expand_kernel, dim3((unsigned)bound, (unsigned)cdiv(n_cols, 256)), dim3(256),
-                     0, s, vec, r_max, mat_pack, use_b_off, desc, perm, offsets, pre64, n_ad, out,
-                     ld_out, n_cols);
-  return launch_check("expand");
 }
 
 lora_status launch_grad(int mode, const float* P, int r_max, const uint16_t* Q, int64_t ld_q,

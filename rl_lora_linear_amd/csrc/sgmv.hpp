@@ -7,6 +7,21 @@ namespace lora_host {
 
 lora_status gemm_nt_bf16(const uint16_t* A, const uint16_t* B, uint16_t* C, int M, int N, int K,
                          int64_t lda, int64_t ldb, int64_t ldc, hipStream_t s, int group_m = 0);
+// Row gather/scatter through perm and the fused LoRA expand of the base GEMM.
+struct LoraFuse {
+  const int32_t* perm;      // segment order -> token
+  const float* vec;         // per-token fp32 vector [tokens][vec_ld]
+  int vec_ld;
+  int use_b_off;            // factor at b_off (B_a [N][r]) or a_off (A_a^T [N][r])
+  const uint16_t* lmat;
+  const lora_adapter_desc* desc;
+  const uint8_t* active;
+  const int32_t* offsets;
+  int n_ad;
+};
+lora_status gemm_nt_lora(const uint16_t* A, const uint16_t* B, uint16_t* C, int M, int N, int K,
+                         int64_t lda, int64_t ldb, int64_t ldc, const LoraFuse& f, hipStream_t s,
+                         int group_m = 0);
 lora_status gemm_nt_lse(const uint16_t* A, const uint16_t* B, int M, int N, int K, int64_t lda,
                         int64_t ldb, float* part_m, float* part_s, float* zt,
                         const int32_t* targets, hipStream_t s, int group_m = 0);
@@ -18,11 +33,6 @@ lora_status launch_shrink(const uint16_t* in, int64_t ld_in, int K, const uint16
                           int use_b_off, const lora_adapter_desc* desc, const uint8_t* active,
                           const int32_t* perm, const int32_t* offsets, const int32_t* pre16,
                           int n_ad, int64_t n_tokens, float* out, int r_max, hipStream_t s);
-lora_status launch_expand(const float* vec, int r_max, const uint16_t* mat_pack, int use_b_off,
-                          const lora_adapter_desc* desc, const int32_t* perm,
-                          const int32_t* offsets, const int32_t* pre64, int n_ad,
-                          int64_t n_tokens, uint16_t* out, int64_t ld_out, int n_cols,
-                          hipStream_t s);
 lora_status launch_grad(int mode, const float* P, int r_max, const uint16_t* Q, int64_t ld_q,
                         int D, const lora_adapter_desc* desc, const uint8_t* active,
                         const int32_t* perm, const int32_t* offsets, const int32_t* chunk_pre,
