@@ -78,8 +78,7 @@ static inline hipStream_t S(void* p) { return (hipStream_t)p; }
 // ------------------------------------------------------------------ layer workspace
 namespace {
 
-constexpr int kTmShrink = 16;
-constexpr int kTmExpand = 64;
+constexpr int kTmShrink = 32;   // rows per shrink tile (matches the kernel)
 
 struct LayerWs {
   char* seg;          // status word + segment scratch
@@ -87,8 +86,7 @@ struct LayerWs {
   int32_t* perm;
   int32_t* offsets;
   uint8_t* active;
-  int32_t* pre16;
-  int32_t* pre64;
+  int32_t* pre32;
   int32_t* prec;
   uint16_t* AT;
   uint16_t* BT;
@@ -105,8 +103,7 @@ LayerWs carve_layer(const lora_shape& sh, void* ws, size_t bytes) {
   w.perm = cv.take<int32_t>((size_t)std::max<int64_t>(sh.n_tokens, 1));
   w.offsets = cv.take<int32_t>((size_t)sh.n_adapters + 1);
   w.active = cv.take<uint8_t>((size_t)sh.n_adapters);
-  w.pre16 = cv.take<int32_t>((size_t)sh.n_adapters + 1);
-  w.pre64 = cv.take<int32_t>((size_t)sh.n_adapters + 1);
+  w.pre32 = cv.take<int32_t>((size_t)sh.n_adapters + 1);
   w.prec = cv.take<int32_t>((size_t)sh.n_adapters + 1);
   w.AT = cv.take<uint16_t>((size_t)sh.a_pack_elems);
   w.BT = cv.take<uint16_t>((size_t)sh.b_pack_elems);
@@ -151,9 +148,9 @@ lora_status layer_segments(const lora_shape& sh, const lora_adapter_desc* desc,
   ex.max_rank = sh.max_rank;
   ex.active = w.active;
   ex.tm[0] = kTmShrink;
-  ex.pre[0] = w.pre16;
-  ex.tm[1] = kTmExpand;
-  ex.pre[1] = w.pre64;
+  ex.pre[0] = w.pre32;
+  ex.tm[1] = 1;
+  ex.pre[1] = nullptr;
   ex.tm[2] = kGradChunk;
   ex.pre[2] = w.prec;
   return run_segments(ids, sh.n_tokens, sh.n_adapters, sh.order, w.perm, w.offsets, &ex, w.seg,
@@ -249,7 +246,7 @@ lora_status lora_forward(const lora_shape* shape, const uint16_t* x, const uint1
   if (N == 0) return LORA_OK;
   timer_begin(LORA_TIMER_SHRINK, s);
   TRY(launch_shrink(x, sh.d_in, (int)sh.d_in, A_pack, 0, desc, w.active, w.perm, w.offsets,
-                    w.pre16, sh.n_adapters, sh.n_tokens, u_saved, sh.max_rank, s));
+                    w.pre32, sh.n_adapters, sh.n_tokens, u_saved, sh.max_rank, s));
   timer_end(LORA_TIMER_SHRINK, s);
   // base GEMM over rows in segment order with the expand y += s B_a u fused
   LoraFuse f{w.perm, u_saved, sh.max_rank, 1, B_pack, desc, w.active, w.offsets, sh.n_adapters};
@@ -288,7 +285,7 @@ lora_status lora_backward(const lora_shape* shape, const uint16_t* dy, const uin
   if (N > 0) {
     timer_begin(LORA_TIMER_SHRINK, s);
     TRY(launch_shrink(dy, sh.d_out, (int)sh.d_out, w.BT, 1, desc, w.active, w.perm, w.offsets,
-                      w.pre16, sh.n_adapters, sh.n_tokens, w.v, sh.max_rank, s));
+                      w.pre32, sh.n_adapters, sh.n_tokens, w.v, sh.max_rank, s));
     timer_end(LORA_TIMER_SHRINK, s);
     // dX = dY W over rows in segment order with the expand dX += s A_a^T v fused
     LoraFuse f{w.perm, w.v, sh.max_rank, 0, w.AT, desc, w.active, w.offsets, sh.n_adapters};

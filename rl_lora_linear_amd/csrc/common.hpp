@@ -115,6 +115,12 @@ struct Carve {
 
 }  // namespace lora_host
 
+#define TRY_HIP(expr)                                               \
+  do {                                                              \
+    lora_status _hs = lora_host::hip_check((expr), #expr);          \
+    if (_hs != LORA_OK) return _hs;                                 \
+  } while (0)
+
 #define LORA_ARG_CHECK(cond, ...)                       \
   do {                                                  \
     if (!(cond)) {                                      \

@@ -9,12 +9,13 @@
 // kernels gather rows through perm.
 //
 //   shrink   out[t][c] = sum_k in[t][k] M_a[c][k]      (u = A_a x, v = B_a^T g)
-//            16 rows per block, the four waves split K, one LDS reduction.
+//            32 rows per block streamed through an LDS-DMA ring.
 //   (the expand y += s B_a u / dx += s A_a^T v runs inside the base GEMM's
 //    epilogue: gemm.hip, lora_slab)
 //   grad     T[c][j] = s_a sum_{t in chunk} P[t][c] Q[t][j]  (dB_a, dA_a)
-//            one block per (token chunk of an adapter, 256 columns); Q rows are
-//            register-transposed into LDS so both MFMA operands are
+//            one block per (token chunk of an adapter, 256 columns); Q and P
+//            stream through an LDS-DMA ring and Q is transposed on the LDS
+//            read (ds_read_b64_tr_b16) so both MFMA operands are
 //            K(=token)-contiguous; P (fp32) is split hi+lo.  Adapters with one
 //            chunk write the result directly, others write chunk partials that
 //            `grad_finalize` sums in chunk order (deterministic, no atomics).
@@ -43,57 +44,154 @@ __device__ __forceinline__ bool tile_of(const int32_t* pre, const int32_t* offse
 }
 
 // ------------------------------------------------------------------ shrink
+// out[t][c] = sum_k in[t][k] M_a[c][k] for the 32 rows of one adapter tile.
+// Rows (gathered through perm) and the factor rows M_a[0..r) stream through a
+// 5-stage LDS ring of k = 128 slices by LDS-DMA (issued from inline assembly,
+// four stages ahead, explicit vmcnt waits; the compiler cannot track which
+// stage a DMA writes).  Each LDS row is 256 B = 16 chunks, chunk c stored at
+// c ^ (row & 15), so the fragment reads of 16 consecutive rows are
+// conflict-free.  Wave w multiplies k-sub-block w (32 k) of every stage; the
+// four partial products are summed in LDS in wave order at the end.
+constexpr int SH_TM = 32;
+constexpr int SH_KC = 128;
+constexpr int SH_NST = 5;
+constexpr int SH_XSLOTS = SH_TM * 16;          // uint4 slots of the row tile per stage
+
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+}
+
+__device__ __forceinline__ void dma16(const void* g, uint32_t m0v) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0v), "v"(g) : "memory");
+}
+
+template <int VM>
+__device__ __forceinline__ void wait_vm_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(VM) : "memory");
+}
+
 template <int NB>
-__device__ __forceinline__ void shrink_body(const uint16_t* __restrict__ in, int64_t ld_in, int K,
-                                            const uint16_t* __restrict__ mat, int r, int tok,
-                                            int lane, int wave, f32x4* acc) {
-  const int KB = K / 32;
-  const int kb0 = wave * KB / 4, kb1 = (wave + 1) * KB / 4;
-  const int ko = 8 * (lane >> 4);
-  const int c = lane & 15;
-  const uint16_t* xrow = in + (int64_t)(tok >= 0 ? tok : 0) * ld_in + ko;
-  const uint16_t* mrow[NB];
-  bool mok[NB];
+__device__ __forceinline__ void shrink_tile(const uint16_t* __restrict__ in, int64_t ld_in, int K,
+                                            const uint16_t* __restrict__ mat, int r,
+                                            const int32_t* __restrict__ perm, int p0, int rows,
+                                            uint4* lds, float* __restrict__ out, int r_max) {
+  constexpr int MSLOTS = NB * 16 * 16;                 // factor tile slots per stage
+  constexpr int STAGE = SH_XSLOTS + MSLOTS;
+  constexpr int PER_WAVE = 2 + NB;                     // DMA instructions per wave per stage
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int KT = (K + SH_KC - 1) / SH_KC;
+
+  // DMA sources of this lane: 2 row-tile instructions, NB factor instructions
+  const uint16_t* xsrc[2];
+  int xchunk[2];
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    mok[nb] = (nb * 16 + c) < r;
-    mrow[nb] = mat + (int64_t)(mok[nb] ? nb * 16 + c : 0) * K + ko;
+  for (int i = 0; i < 2; ++i) {
+    const int row = (wave * 2 + i) * 4 + (lane >> 4);
+    const int t = perm[p0 + (row < rows ? row : 0)];
+    xchunk[i] = (lane & 15) ^ (row & 15);
+    xsrc[i] = in + (int64_t)t * ld_in;
   }
-  const uint4 z = make_uint4(0, 0, 0, 0);
-  int kb = kb0;
-  for (; kb + 4 <= kb1; kb += 4) {
-    uint4 xv[4], mv[4][NB];
+  const uint16_t* msrc[NB];
+  int mchunk[NB];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      xv[u] = tok >= 0 ? *(const uint4*)(xrow + (kb + u) * 32) : z;
+  for (int i = 0; i < NB; ++i) {
+    const int c = (wave * NB + i) * 4 + (lane >> 4);
+    mchunk[i] = (lane & 15) ^ (c & 15);
+    msrc[i] = mat + (int64_t)(c < r ? c : r - 1) * K;
+  }
+  auto issue = [&](int st, int kt) {
+    const int k0 = kt * SH_KC;
+    uint4* base = lds + st * STAGE;
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) mv[u][nb] = mok[nb] ? *(const uint4*)(mrow[nb] + (kb + u) * 32) : z;
+    for (int i = 0; i < 2; ++i) {
+      const int k = min(k0 + xchunk[i] * 8, K - 8);
+      dma16(xsrc[i] + k, __builtin_amdgcn_readfirstlane(lds_u32(base + (wave * 2 + i) * 64)));
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) acc[nb] = mfma16(as_bf16x8(xv[u]), as_bf16x8(mv[u][nb]), acc[nb]);
-  }
-  for (; kb < kb1; ++kb) {
-    uint4 xv = tok >= 0 ? *(const uint4*)(xrow + kb * 32) : z;
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      uint4 mv = mok[nb] ? *(const uint4*)(mrow[nb] + kb * 32) : z;
-      acc[nb] = mfma16(as_bf16x8(xv), as_bf16x8(mv), acc[nb]);
+    for (int i = 0; i < NB; ++i) {
+      const int k = min(k0 + mchunk[i] * 8, K - 8);
+      dma16(msrc[i] + k, __builtin_amdgcn_readfirstlane(lds_u32(base + SH_XSLOTS + (wave * NB + i) * 64)));
     }
+  };
+
+#pragma unroll
+  for (int st = 0; st < SH_NST - 1; ++st) issue(st, min(st, KT - 1));
+  wait_vm_barrier<(SH_NST - 2) * PER_WAVE>();
+
+  f32x4 acc[2][NB];
+#pragma unroll
+  for (int g = 0; g < 2; ++g)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[g][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int fr = lane & 15;
+  const int ch = 4 * wave + (lane >> 4);  // logical chunk of this lane's fragments
+
+  for (int kt = 0; kt < KT; ++kt) {
+    const int st = kt % SH_NST;
+    issue((kt + SH_NST - 1) % SH_NST, min(kt + SH_NST - 1, KT - 1));
+    const uint4* xt = lds + st * STAGE;
+    const uint4* mt = xt + SH_XSLOTS;
+    if (kt * SH_KC + wave * 32 < K) {
+      bf16x8 xa[2], mb[NB];
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const int row = g * 16 + fr;
+        xa[g] = as_bf16x8(xt[row * 16 + (ch ^ (row & 15))]);
+      }
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const int c = b * 16 + fr;
+        mb[b] = as_bf16x8(mt[c * 16 + (ch ^ (c & 15))]);
+      }
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) acc[g][b] = mfma16(xa[g], mb[b], acc[g][b]);
+    }
+    wait_vm_barrier<(SH_NST - 2) * PER_WAVE>();
+  }
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+
+  // cross-wave reduction in wave order; acc[g][b][i] = D[16g + 4*(lane/16) + i][16b + lane%16]
+  float* red = (float*)lds;  // [4][SH_TM][64]
+#pragma unroll
+  for (int g = 0; g < 2; ++g)
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        red[(wave * SH_TM + g * 16 + 4 * (lane >> 4) + i) * 64 + b * 16 + (lane & 15)] = acc[g][b][i];
+  __syncthreads();
+  for (int e = tid; e < SH_TM * (r_max / 4); e += 256) {
+    const int row = e / (r_max / 4), cg = (e % (r_max / 4)) * 4;
+    if (row >= rows) continue;
+    float v[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int c = cg + q;
+      float sacc = 0.f;
+      if (c < r) {
+        sacc = red[(0 * SH_TM + row) * 64 + c] + red[(1 * SH_TM + row) * 64 + c];
+        sacc += red[(2 * SH_TM + row) * 64 + c];
+        sacc += red[(3 * SH_TM + row) * 64 + c];
+      }
+      v[q] = sacc;
+    }
+    *(float4*)(out + (int64_t)perm[p0 + row] * r_max + cg) = make_float4(v[0], v[1], v[2], v[3]);
   }
 }
 
-// grid.x = tile bound; grid.y = 2: y == 0 computes tiles, y == 1 zeroes the
-// rows of tokens that belong to no active adapter (positions >= offsets[n_ad]
-// or inside an inactive adapter's segment).
+// grid.x = tile bound; grid.y = 2: y == 0 computes 32-row adapter tiles,
+// y == 1 zeroes the rows of tokens that belong to no active adapter
+// (positions >= offsets[n_ad] or inside an inactive adapter's segment).
 __global__ __launch_bounds__(256) void shrink_kernel(
     const uint16_t* __restrict__ in, int64_t ld_in, int K, const uint16_t* __restrict__ mat_pack,
     int use_b_off, const lora_adapter_desc* __restrict__ desc, const uint8_t* __restrict__ active,
     const int32_t* __restrict__ perm, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ pre16, int n_ad, int64_t n_tokens, float* __restrict__ out,
+    const int32_t* __restrict__ pre32, int n_ad, int64_t n_tokens, float* __restrict__ out,
     int r_max) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  extern __shared__ uint4 sh_lds[];
+  const int tid = threadIdx.x;
   if (blockIdx.y == 1) {
     const int64_t p = (int64_t)blockIdx.x * 256 + tid;
     if (p >= n_tokens) return;
@@ -106,85 +204,153 @@ __global__ __launch_bounds__(256) void shrink_kernel(
     return;
   }
   TileInfo ti;
-  if (!tile_of(pre16, offsets, n_ad, blockIdx.x, 16, ti)) return;
+  if (!tile_of(pre32, offsets, n_ad, blockIdx.x, SH_TM, ti)) return;
   const lora_adapter_desc d = desc[ti.a];
   const int r = d.rank;
   const uint16_t* mat = mat_pack + (use_b_off ? d.b_off : d.a_off);
-  const int row = lane & 15;
-  const int tok = row < ti.rows ? perm[ti.p0 + row] : -1;
-
-  f32x4 acc[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int nb = (r + 15) / 16;
-  if (nb == 1) shrink_body<1>(in, ld_in, K, mat, r, tok, lane, wave, acc);
-  else if (nb == 2) shrink_body<2>(in, ld_in, K, mat, r, tok, lane, wave, acc);
-  else if (nb == 3) shrink_body<3>(in, ld_in, K, mat, r, tok, lane, wave, acc);
-  else shrink_body<4>(in, ld_in, K, mat, r, tok, lane, wave, acc);
-
-  // cross-wave reduction in a fixed order.  acc[nb][i] = D[4*(lane/16)+i][nb*16 + lane%16]
-  __shared__ float red[4][16][64];
-#pragma unroll
-  for (int b = 0; b < 4; ++b)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) red[wave][4 * (lane >> 4) + i][b * 16 + (lane & 15)] = acc[b][i];
-  __syncthreads();
-  const int orow = tid >> 4, cg = (tid & 15) * 4;
-  if (orow < ti.rows && cg < r_max) {
-    const int t = perm[ti.p0 + orow];
-    float v[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int c = cg + q;
-      float s = red[0][orow][c] + red[1][orow][c];
-      s += red[2][orow][c];
-      s += red[3][orow][c];
-      v[q] = c < r ? s : 0.f;
-    }
-    float* o = out + (int64_t)t * r_max + cg;
-    // r_max is a multiple of 8, so the 4-float group is either inside or outside
-    *(float4*)o = make_float4(v[0], v[1], v[2], v[3]);
-  }
+  if (nb == 1) shrink_tile<1>(in, ld_in, K, mat, r, perm, ti.p0, ti.rows, sh_lds, out, r_max);
+  else if (nb == 2) shrink_tile<2>(in, ld_in, K, mat, r, perm, ti.p0, ti.rows, sh_lds, out, r_max);
+  else if (nb == 3) shrink_tile<3>(in, ld_in, K, mat, r, perm, ti.p0, ti.rows, sh_lds, out, r_max);
+  else shrink_tile<4>(in, ld_in, K, mat, r, perm, ti.p0, ti.rows, sh_lds, out, r_max);
 }
 
 // ------------------------------------------------------------------ grad
 constexpr int GR_TC = 1024;   // tokens per chunk (per-adapter split for balance)
-constexpr int GR_TT = 64;     // tokens staged per step
+constexpr int GR_TT = 32;     // tokens per stage
 constexpr int GR_NJ = 256;    // output columns per block
+constexpr int GR_NST = 5;     // LDS ring depth (DMA four stages ahead)
+constexpr int GR_QSLOTS = GR_TT * 32;   // 32 token rows x 512 B of Q
+constexpr int GR_PSLOTS = GR_TT * 16;   // 32 token rows x 64 fp32 of P
+constexpr int GR_STAGE = GR_QSLOTS + GR_PSLOTS;
+constexpr int GR_PER_WAVE = 6;          // DMA instructions per wave per stage (4 Q + 2 P)
 
+// Q tile swizzle: chunk c of token row t is stored at c ^ fq(t).  A transposed
+// 8-byte read (ds_read_b64_tr_b16) by 16 lanes touches 4 consecutive rows x
+// 32 B; fq spreads those rows (and the rows of the next 16-lane group, 8 rows
+// further) over distinct banks.
+__device__ __forceinline__ int gr_fq(int t) { return (2 * (t & 3)) | (8 * ((t >> 3) & 1)); }
+// P tile swizzle (16 chunks per row): the four 16-lane groups read rows 8 apart.
+__device__ __forceinline__ int gr_fp(int t) { return 4 * ((t >> 3) & 3); }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint2 tr_read(const uint4* base, uint32_t byte_off) {
+  s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)((__attribute__((address_space(3))) char*)(
+                                                     (__attribute__((address_space(3))) void*)base) +
+                                                 byte_off));
+  union { s16x4 s; uint2 u; } c;
+  c.s = v;
+  return c.u;
+}
+
+// T[c][j] = s_a sum_{t in chunk} P[t][c] Q[t][j] for one chunk of one adapter
+// and 256 columns j.  MFMA K is the token axis: each 32-token stage is one
+// v_mfma_f32_16x16x32 per (16 columns, 16 ranks, hi|lo).  Q fragments come from
+// the row-major LDS tile through the transposing read: in a 16-lane group,
+// lane 4q + b addresses row (t0 + q), columns 4b..4b+3, and lane i receives
+// column i of rows t0..t0+3.  P fragments are 8 strided fp32 LDS reads,
+// zeroed past the chunk's last token, split hi+lo in registers.
 // mode 0 (dB): out layout [D][r] (c fastest): MFMA M = c, N = j.
 // mode 1 (dA): out layout [r][D] (j fastest): MFMA M = j, N = c.
 template <int NCB, int MODE>
-__device__ __forceinline__ void grad_mma(const uint4* Qt, const uint4* Ph, const uint4* Pl,
-                                         int lane, int wave, f32x4 (&acc)[4][4]) {
+__device__ __forceinline__ void grad_tile(const float* __restrict__ P, int r_max,
+                                          const uint16_t* __restrict__ Q, int64_t ld_q, int D,
+                                          const int32_t* tok_s, int rows, int r, int j0,
+                                          uint4* lds, f32x4 (&acc)[4][4]) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int KT = (rows + GR_TT - 1) / GR_TT;
+  const int pcn = r_max / 4;  // valid 16-byte chunks of a P row
+  // DMA sources: Q rows (w*4+i)*2 + L/32, chunk L%32; P rows (w*2+i)*4 + L/16, chunk L%16
+  int qrow[4], qcol[4], prow[2], pch[2];
 #pragma unroll
-  for (int kb = 0; kb < GR_TT / 32; ++kb) {
-    const int ch = kb * 4 + (lane >> 4);
-    bf16x8 q[4], ph[NCB], pl[NCB];
+  for (int i = 0; i < 4; ++i) {
+    const int row = (wave * 4 + i) * 2 + (lane >> 5);
+    qrow[i] = row;
+    qcol[i] = min(j0 + (((lane & 31) ^ gr_fq(row)) * 8), D - 8);
+  }
 #pragma unroll
-    for (int jt = 0; jt < 4; ++jt) {
-      const int j = wave * 64 + jt * 16 + (lane & 15);
-      q[jt] = as_bf16x8(Qt[sw8(j, ch)]);
+  for (int i = 0; i < 2; ++i) {
+    const int row = (wave * 2 + i) * 4 + (lane >> 4);
+    prow[i] = row;
+    pch[i] = min((lane & 15) ^ gr_fp(row), pcn - 1);
+  }
+  auto issue = [&](int st, int kt) {
+    uint4* base = lds + st * GR_STAGE;
+    const int t0 = kt * GR_TT;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tr = min(t0 + qrow[i], rows - 1);
+      const uint16_t* g = Q + (int64_t)tok_s[tr] * ld_q + qcol[i];
+      dma16(g, __builtin_amdgcn_readfirstlane(lds_u32(base + (wave * 4 + i) * 64)));
     }
 #pragma unroll
-    for (int ct = 0; ct < NCB; ++ct) {
-      const int c = ct * 16 + (lane & 15);
-      ph[ct] = as_bf16x8(Ph[sw8(c, ch)]);
-      pl[ct] = as_bf16x8(Pl[sw8(c, ch)]);
+    for (int i = 0; i < 2; ++i) {
+      const int tr = min(t0 + prow[i], rows - 1);
+      const float* g = P + (int64_t)tok_s[tr] * r_max + pch[i] * 4;
+      dma16(g, __builtin_amdgcn_readfirstlane(lds_u32(base + GR_QSLOTS + (wave * 2 + i) * 64)));
+    }
+  };
+
+#pragma unroll
+  for (int st = 0; st < GR_NST - 1; ++st) issue(st, min(st, KT - 1));
+  wait_vm_barrier<(GR_NST - 2) * GR_PER_WAVE>();
+
+  const int g16 = lane >> 4;   // 16-lane group: tokens 8*g16 .. 8*g16+7 of the stage
+  const int li = lane & 15;
+  for (int kt = 0; kt < KT; ++kt) {
+    const int st = kt % GR_NST;
+    issue((kt + GR_NST - 1) % GR_NST, min(kt + GR_NST - 1, KT - 1));
+    const uint4* qt = lds + st * GR_STAGE;
+    const float* pt = (const float*)(qt + GR_QSLOTS);
+    // Q fragments: 4 column sub-tiles of this wave's 64 columns
+    bf16x8 qf[4];
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt) {
+      uint2 hv[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int t = 8 * g16 + 4 * h + (li >> 2);
+        const int jl = wave * 64 + jt * 16 + 4 * (li & 3);
+        const uint32_t off = t * 512 + (((jl >> 3) ^ gr_fq(t)) << 4) + ((jl & 7) << 1);
+        hv[h] = tr_read(qt, off);
+      }
+      qf[jt] = as_bf16x8(make_uint4(hv[0].x, hv[0].y, hv[1].x, hv[1].y));
+    }
+    // P fragments: tokens 8*g16 + q, rank column cb*16 + li
+    bf16x8 ph[NCB], pl[NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      const int c = cb * 16 + li;
+      uint16_t hh[8], ll[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int t = 8 * g16 + q;
+        float f = pt[t * 64 + (((c >> 2) ^ gr_fp(t)) << 2) + (c & 3)];
+        if (kt * GR_TT + t >= rows || c >= r) f = 0.f;
+        split_bf16(f, hh[q], ll[q]);
+      }
+      ph[cb] = as_bf16x8(make_uint4(hh[0] | (hh[1] << 16), hh[2] | (hh[3] << 16),
+                                    hh[4] | (hh[5] << 16), hh[6] | (hh[7] << 16)));
+      pl[cb] = as_bf16x8(make_uint4(ll[0] | (ll[1] << 16), ll[2] | (ll[3] << 16),
+                                    ll[4] | (ll[5] << 16), ll[6] | (ll[7] << 16)));
     }
 #pragma unroll
     for (int jt = 0; jt < 4; ++jt)
 #pragma unroll
-      for (int ct = 0; ct < NCB; ++ct) {
+      for (int cb = 0; cb < NCB; ++cb) {
         if (MODE == 0) {
-          acc[jt][ct] = mfma16(ph[ct], q[jt], acc[jt][ct]);
-          acc[jt][ct] = mfma16(pl[ct], q[jt], acc[jt][ct]);
+          acc[jt][cb] = mfma16(ph[cb], qf[jt], acc[jt][cb]);
+          acc[jt][cb] = mfma16(pl[cb], qf[jt], acc[jt][cb]);
         } else {
-          acc[jt][ct] = mfma16(q[jt], ph[ct], acc[jt][ct]);
-          acc[jt][ct] = mfma16(q[jt], pl[ct], acc[jt][ct]);
+          acc[jt][cb] = mfma16(qf[jt], ph[cb], acc[jt][cb]);
+          acc[jt][cb] = mfma16(qf[jt], pl[cb], acc[jt][cb]);
         }
       }
+    wait_vm_barrier<(GR_NST - 2) * GR_PER_WAVE>();
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no DMA may outlive the block
 }
 
 // grid = (chunk-slot bound, ceil(D / 256)).
@@ -194,85 +360,37 @@ __global__ __launch_bounds__(256) void grad_kernel(
     const lora_adapter_desc* __restrict__ desc, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ chunk_pre, int n_ad,
     float* __restrict__ out_pack, float* __restrict__ partial, int accumulate) {
+  extern __shared__ uint4 gr_lds[];
+  // the chunk's token ids, cached in LDS: the DMA loop may issue no
+  // compiler-tracked global loads (their waits would also wait for the DMA)
+  __shared__ int32_t tok_s[GR_TC];
   const int slot = blockIdx.x;
   TileInfo ti;
   if (!tile_of(chunk_pre, offsets, n_ad, slot, GR_TC, ti)) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = threadIdx.x; i < ti.rows; i += 256) tok_s[i] = perm[ti.p0 + i];
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const lora_adapter_desc d = desc[ti.a];
   const int r = d.rank;
   const int j0 = blockIdx.y * GR_NJ;
   const int nchunks = chunk_pre[ti.a + 1] - chunk_pre[ti.a];
-
-  __shared__ uint4 Qt[GR_NJ * 8];   // [256 j][64 t] bf16, swizzled
-  __shared__ uint4 Ph[64 * 8];      // [64 c][64 t]
-  __shared__ uint4 Pl[64 * 8];
-  uint16_t* Ph16 = (uint16_t*)Ph;
-  uint16_t* Pl16 = (uint16_t*)Pl;
 
   f32x4 acc[4][4];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int jc = tid & 31;        // 8-column group of Q
-  const int toct = tid >> 5;      // 8-token group
-  const int pt = tid >> 2;        // P staging: token
-  const int pcg = (tid & 3) * 16; // P staging: first of 16 columns
   const int ncb = (r + 15) / 16;
-
-  for (int t0 = 0; t0 < ti.rows; t0 += GR_TT) {
-    // ---- stage Q^T: 8 tokens x 8 columns per thread, transposed in registers
-    uint32_t w[8][4];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int tr = t0 + toct * 8 + i;
-      const int j = j0 + jc * 8;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (tr < ti.rows && j < D) v = *(const uint4*)(Q + (int64_t)perm[ti.p0 + tr] * ld_q + j);
-      w[i][0] = v.x; w[i][1] = v.y; w[i][2] = v.z; w[i][3] = v.w;
-    }
-#pragma unroll
-    for (int qc = 0; qc < 8; ++qc) {
-      const int wd = qc >> 1, sh = (qc & 1) * 16;
-      uint32_t o[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t lo = (w[2 * k][wd] >> sh) & 0xFFFFu;
-        const uint32_t hi = (w[2 * k + 1][wd] >> sh) & 0xFFFFu;
-        o[k] = lo | (hi << 16);
-      }
-      Qt[sw8(jc * 8 + qc, toct)] = make_uint4(o[0], o[1], o[2], o[3]);
-    }
-    // ---- stage P^T as hi/lo bf16: token pt, columns pcg..pcg+15
-    {
-      const int tr = t0 + pt;
-      const bool ok = tr < ti.rows;
-      const float* pp = P + (int64_t)(ok ? perm[ti.p0 + tr] : 0) * r_max;
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int c = pcg + q;
-        float f = (ok && c < r) ? pp[c] : 0.f;
-        uint16_t h, l;
-        split_bf16(f, h, l);
-        const int idx = c * 64 + (((pt >> 3) ^ lds_sw(c)) << 3) + (pt & 7);
-        Ph16[idx] = h;
-        Pl16[idx] = l;
-      }
-    }
-    __syncthreads();
-    if (ncb == 1) grad_mma<1, MODE>(Qt, Ph, Pl, lane, wave, acc);
-    else if (ncb == 2) grad_mma<2, MODE>(Qt, Ph, Pl, lane, wave, acc);
-    else if (ncb == 3) grad_mma<3, MODE>(Qt, Ph, Pl, lane, wave, acc);
-    else grad_mma<4, MODE>(Qt, Ph, Pl, lane, wave, acc);
-    __syncthreads();
-  }
+  if (ncb == 1) grad_tile<1, MODE>(P, r_max, Q, ld_q, D, tok_s, ti.rows, r, j0, gr_lds, acc);
+  else if (ncb == 2) grad_tile<2, MODE>(P, r_max, Q, ld_q, D, tok_s, ti.rows, r, j0, gr_lds, acc);
+  else if (ncb == 3) grad_tile<3, MODE>(P, r_max, Q, ld_q, D, tok_s, ti.rows, r, j0, gr_lds, acc);
+  else grad_tile<4, MODE>(P, r_max, Q, ld_q, D, tok_s, ti.rows, r, j0, gr_lds, acc);
 
   // ---- write.  Region of this adapter: D*r floats.
   const int64_t base = MODE == 0 ? d.b_off : d.a_off;
   const bool direct = nchunks == 1;
   float* dst = direct ? out_pack + base : partial + (int64_t)slot * D * r_max;
-  const float s = d.scale;
+  const float sc = d.scale;
 #pragma unroll
   for (int jt = 0; jt < 4; ++jt)
 #pragma unroll
@@ -284,7 +402,7 @@ __global__ __launch_bounds__(256) void grad_kernel(
         const int j = j0 + wave * 64 + jt * 16 + (lane & 15);
         if (c >= r || j >= D) continue;
         float4* p = (float4*)(dst + (int64_t)j * r + c);
-        float4 v = make_float4(s * acc[jt][ct][0], s * acc[jt][ct][1], s * acc[jt][ct][2], s * acc[jt][ct][3]);
+        float4 v = make_float4(sc * acc[jt][ct][0], sc * acc[jt][ct][1], sc * acc[jt][ct][2], sc * acc[jt][ct][3]);
         if (direct && accumulate) {
           float4 o = *p;
           v.x += o.x; v.y += o.y; v.z += o.z; v.w += o.w;
@@ -296,7 +414,7 @@ __global__ __launch_bounds__(256) void grad_kernel(
         const int c = ct * 16 + (lane & 15);
         if (c >= r || j >= D) continue;
         float4* p = (float4*)(dst + (int64_t)c * D + j);
-        float4 v = make_float4(s * acc[jt][ct][0], s * acc[jt][ct][1], s * acc[jt][ct][2], s * acc[jt][ct][3]);
+        float4 v = make_float4(sc * acc[jt][ct][0], sc * acc[jt][ct][1], sc * acc[jt][ct][2], sc * acc[jt][ct][3]);
         if (direct && accumulate) {
           float4 o = *p;
           v.x += o.x; v.y += o.y; v.z += o.z; v.w += o.w;
@@ -382,12 +500,21 @@ using namespace lora;
 
 lora_status launch_shrink(const uint16_t* in, int64_t ld_in, int K, const uint16_t* mat_pack,
                           int use_b_off, const lora_adapter_desc* desc, const uint8_t* active,
-                          const int32_t* perm, const int32_t* offsets, const int32_t* pre16,
+                          const int32_t* perm, const int32_t* offsets, const int32_t* pre32,
                           int n_ad, int64_t n_tokens, float* out, int r_max, hipStream_t s) {
   if (n_tokens <= 0) return LORA_OK;
-  const int64_t bound = cdiv(n_tokens, 16) + n_ad;
-  hipLaunchKernelGGL(shrink_kernel, dim3((unsigned)bound, 2), dim3(256), 0, s, in, ld_in, K,
-                     mat_pack, use_b_off, desc, active, perm, offsets, pre16, n_ad, n_tokens, out,
+  const int64_t bound = std::max(cdiv(n_tokens, SH_TM) + n_ad, cdiv(n_tokens, 256));
+  const int nb_max = (r_max + 15) / 16;
+  const size_t lds = std::max<size_t>((size_t)SH_NST * (SH_XSLOTS + nb_max * 256) * sizeof(uint4),
+                                      (size_t)4 * SH_TM * 64 * sizeof(float));
+  static size_t attr = 0;
+  if (attr < lds) {
+    TRY_HIP(hipFuncSetAttribute((const void*)shrink_kernel,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
+    attr = lds;
+  }
+  hipLaunchKernelGGL(shrink_kernel, dim3((unsigned)bound, 2), dim3(256), lds, s, in, ld_in, K,
+                     mat_pack, use_b_off, desc, active, perm, offsets, pre32, n_ad, n_tokens, out,
                      r_max);
   return launch_check("shrink");
 }
@@ -400,11 +527,20 @@ lora_status launch_grad(int mode, const float* P, int r_max, const uint16_t* Q, 
   if (n_tokens > 0) {
     const int64_t bound = cdiv(n_tokens, GR_TC) + n_ad;
     dim3 grid((unsigned)bound, (unsigned)cdiv(D, GR_NJ));
+    const size_t lds = (size_t)GR_NST * GR_STAGE * sizeof(uint4);
+    static bool attr = false;
+    if (!attr) {
+      TRY_HIP(hipFuncSetAttribute((const void*)grad_kernel<0>,
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
+      TRY_HIP(hipFuncSetAttribute((const void*)grad_kernel<1>,
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
+      attr = true;
+    }
     if (mode == 0)
-      hipLaunchKernelGGL(grad_kernel<0>, grid, dim3(256), 0, s, P, r_max, Q, ld_q, D, desc, perm,
+      hipLaunchKernelGGL(grad_kernel<0>, grid, dim3(256), lds, s, P, r_max, Q, ld_q, D, desc, perm,
                          offsets, chunk_pre, n_ad, out_pack, partial, accumulate);
     else
-      hipLaunchKernelGGL(grad_kernel<1>, grid, dim3(256), 0, s, P, r_max, Q, ld_q, D, desc, perm,
+      hipLaunchKernelGGL(grad_kernel<1>, grid, dim3(256), lds, s, P, r_max, Q, ld_q, D, desc, perm,
                          offsets, chunk_pre, n_ad, out_pack, partial, accumulate);
     lora_status st = launch_check("grad");
     if (st) return st;

@@ -31,7 +31,7 @@ lora_status gemm_nt_grad(const uint16_t* A, const uint16_t* B, uint16_t* G, int6
 
 lora_status launch_shrink(const uint16_t* in, int64_t ld_in, int K, const uint16_t* mat_pack,
                           int use_b_off, const lora_adapter_desc* desc, const uint8_t* active,
-                          const int32_t* perm, const int32_t* offsets, const int32_t* pre16,
+                          const int32_t* perm, const int32_t* offsets, const int32_t* pre32,
                           int n_ad, int64_t n_tokens, float* out, int r_max, hipStream_t s);
 lora_status launch_grad(int mode, const float* P, int r_max, const uint16_t* Q, int64_t ld_q,
                         int D, const lora_adapter_desc* desc, const uint8_t* active,
