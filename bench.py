@@ -138,7 +138,7 @@ def main():
         dys = torch.roll(dl.dy, shifts=k * 89, dims=0).contiguous()
         sets.append((xs, dys))
     y = torch.empty((N, d_out), dtype=torch.bfloat16, device=dev)
-    u = torch.empty((N, dl.max_rank), dtype=torch.float32, device=dev)
+    u = torch.empty((2, N, dl.max_rank), dtype=torch.bfloat16, device=dev)   # hi/lo planes
     dx = torch.empty((N, d_in), dtype=torch.bfloat16, device=dev)
     grad = torch.zeros(case.pack_elems, dtype=torch.float32, device=dev)
     master = dl.pack.float().clone()
@@ -153,9 +153,9 @@ def main():
         L.lora_backward(dl.shape, dys, xs, dl.Wt, dl.pack, dl.pack, dl.desc, dl.ids, u, dx, grad,
                         grad, 0, dl.ws)
         t = steps_done[0] + 1
-        for (a0, a1) in ranges:
-            L.adam_step(master[a0:a1], grad[a0:a1], m[a0:a1], v[a0:a1], t, 1e-4, 0.9, 0.999, 1e-8,
-                        0.0, dl.pack[a0:a1])
+        # every adapter in the batch takes its own AdamW step, one launch
+        L.adam_step_multi([(a0, a1 - a0, t) for (a0, a1) in ranges], master, grad, m, v, 1e-4,
+                          0.9, 0.999, 1e-8, 0.0, p_bf16=dl.pack)
         steps_done[0] = t
 
     log(f"[bench] warmup {args.warmup}")
@@ -195,7 +195,7 @@ def main():
     expand_bytes = (2 * N * d_out * 2 + n_ad * d_out * r * 2 + N * dl.max_rank * 4)
     grad_bytes = (N * d_out * 2 + N * dl.max_rank * 4 + n_ad * d_out * r * 4) + \
                  (N * d_in * 2 + N * dl.max_rank * 4 + n_ad * r * d_in * 4)
-    adam_bytes = 28 * (ranges[0][1] - ranges[0][0])
+    adam_bytes = 30 * sum(a1 - a0 for a0, a1 in ranges)   # p,m,v r+w, g r, bf16 copy w
 
     def kentry(name, bytes_per_launch, launches_per_step):
         tot, cnt = timers[name]
@@ -210,7 +210,7 @@ def main():
         "shrink": kentry("shrink", shrink_bytes, 2),
         "expand": kentry("expand", expand_bytes, 2),
         "grad_dA_dB": kentry("grad", grad_bytes, 1),
-        "adam_per_adapter": kentry("adam", adam_bytes, n_ad),
+        "adam_all_adapters": kentry("adam", adam_bytes, 1),
     }
     out = {
         "metric": METRIC,

@@ -101,7 +101,7 @@ typedef struct {
   int64_t a_pack_elems;  /* elements readable from the A pack (bound for descriptor checks) */
   int64_t b_pack_elems;  /* elements readable from the B pack */
   int32_t n_adapters;    /* 1 .. 16384 */
-  int32_t max_rank;      /* 8 .. 64, multiple of 8: u/v row stride and rank bound */
+  int32_t max_rank;      /* 16 .. 64, multiple of 16: u/v row stride and rank bound */
   int32_t order;         /* lora_id_order: a promise about adapter_ids, checked on device */
   int32_t reserved;      /* must be 0 */
 } lora_shape;
@@ -159,14 +159,18 @@ lora_status lora_transpose_bf16(const uint16_t* src, uint16_t* dst, int64_t rows
  *   adapter_ids int32 [N]
  *   y       bf16 [N][d_out] out   (bf16 of the fp32-accumulated base product,
  *                                  then the fp32 delta added and rounded again)
- *   u_saved fp32 [N][max_rank] out  u_t in columns 0..r_a-1, zeros after; rows
- *                                  of invalid tokens are all zero.  Keep it for
- *                                  lora_backward.
+ *   u_saved bf16 [2][N][max_rank] out  the scaled s_a u_t as two planes:
+ *                                  plane 0 holds hi = bf16(s_a u_t), plane 1
+ *                                  lo = bf16(s_a u_t - hi) (both round to
+ *                                  nearest even), so hi + lo carries s_a u_t to
+ *                                  ~2^-16 relative.  Columns r_a.. and rows of
+ *                                  invalid tokens are zero.  4*N*max_rank
+ *                                  bytes; keep it for lora_backward.
  * Tokens need not be sorted: LORA_IDS_INTERLEAVED gathers rows by adapter. */
 lora_status lora_forward(const lora_shape* shape, const uint16_t* x, const uint16_t* W,
                          const uint16_t* A_pack, const uint16_t* B_pack,
                          const lora_adapter_desc* desc, const int32_t* adapter_ids,
-                         uint16_t* y, float* u_saved, void* ws, size_t ws_bytes, void* stream);
+                         uint16_t* y, uint16_t* u_saved, void* ws, size_t ws_bytes, void* stream);
 
 /* Backward for upstream g = dL/dy (OpenTinker, "3 Approach": adapter-local
  * gradients; the base W is frozen so there is no dW):
@@ -176,7 +180,7 @@ lora_status lora_forward(const lora_shape* shape, const uint16_t* x, const uint1
  *   dy      bf16 [N][d_out]      x bf16 [N][d_in]
  *   W_t     bf16 [d_in][d_out]   the frozen base weight TRANSPOSED (see
  *                                lora_transpose_bf16)
- *   u_saved fp32 [N][max_rank]   from lora_forward with the same inputs
+ *   u_saved bf16 [2][N][max_rank] from lora_forward with the same inputs
  *   dx      bf16 [N][d_in] out
  *   dA_pack, dB_pack fp32 out    same offsets as the A/B packs (may be one
  *                                buffer).  accumulate = 0 overwrites every
@@ -190,7 +194,7 @@ lora_status lora_forward(const lora_shape* shape, const uint16_t* x, const uint1
 lora_status lora_backward(const lora_shape* shape, const uint16_t* dy, const uint16_t* x,
                           const uint16_t* W_t, const uint16_t* A_pack, const uint16_t* B_pack,
                           const lora_adapter_desc* desc, const int32_t* adapter_ids,
-                          const float* u_saved, uint16_t* dx, float* dA_pack, float* dB_pack,
+                          const uint16_t* u_saved, uint16_t* dx, float* dA_pack, float* dB_pack,
                           int accumulate, void* ws, size_t ws_bytes, void* stream);
 
 /* ---- fused lm_head + target logprob ----------------------------------- */
@@ -267,6 +271,18 @@ lora_status loss_grad(int32_t kind, int64_t n, const float* logprobs, const floa
 lora_status adam_step(int64_t n, float* p, const float* g, float* m, float* v, int64_t step,
                       float lr, float beta1, float beta2, float eps, float weight_decay,
                       uint16_t* p_bf16, void* stream);
+
+/* Several adapters' AdamW steps in one launch: segment i updates elements
+ * [offset, offset + count) of p, g, m, v (and p_bf16) exactly as adam_step
+ * with step = segs[i].step would (same host-side bias factors, same
+ * per-element arithmetic, so results are bitwise those of one adam_step call
+ * per segment).  segs is a HOST array; segments must not overlap.  Each
+ * adapter keeps its own step counter (OpenTinker, "3 Approach": optimizer
+ * state local to each adapter).  n_seg >= 0. */
+typedef struct { int64_t offset; int64_t count; int64_t step; } adam_segment;
+lora_status adam_step_multi(int32_t n_seg, const adam_segment* segs, float* p, const float* g,
+                            float* m, float* v, float lr, float beta1, float beta2, float eps,
+                            float weight_decay, uint16_t* p_bf16, void* stream);
 
 /* ---- MLP glue --------------------------------------------------------- */
 

@@ -90,7 +90,8 @@ struct LayerWs {
   int32_t* prec;
   uint16_t* AT;
   uint16_t* BT;
-  float* v;
+  uint16_t* v;        // scaled v = s_a B_a^T dy as bf16 hi/lo planes [2][N][max_rank]
+  uint16_t* zero;     // 256 zero bytes (source of the rows past a gradient chunk)
   float* partial;
   size_t total;
 };
@@ -107,7 +108,8 @@ LayerWs carve_layer(const lora_shape& sh, void* ws, size_t bytes) {
   w.prec = cv.take<int32_t>((size_t)sh.n_adapters + 1);
   w.AT = cv.take<uint16_t>((size_t)sh.a_pack_elems);
   w.BT = cv.take<uint16_t>((size_t)sh.b_pack_elems);
-  w.v = cv.take<float>((size_t)std::max<int64_t>(sh.n_tokens, 1) * sh.max_rank);
+  w.v = cv.take<uint16_t>((size_t)2 * std::max<int64_t>(sh.n_tokens, 1) * sh.max_rank);
+  w.zero = cv.take<uint16_t>(128);
   w.partial = cv.take<float>((size_t)grad_partial_floats(sh.n_tokens, sh.n_adapters,
                                                          std::max(sh.d_in, sh.d_out), sh.max_rank));
   w.total = cv.used;
@@ -121,8 +123,8 @@ lora_status check_shape(const lora_shape* sh) {
   LORA_ARG_CHECK(sh->d_in > 0 && sh->d_out > 0, "d_in and d_out must be positive");
   LORA_ARG_CHECK(sh->n_adapters >= 1 && sh->n_adapters <= 16384, "n_adapters %d outside [1, 16384]",
                  sh->n_adapters);
-  LORA_ARG_CHECK(sh->max_rank >= 8 && sh->max_rank <= 64 && sh->max_rank % 8 == 0,
-                 "max_rank %d must be a multiple of 8 in [8, 64]", sh->max_rank);
+  LORA_ARG_CHECK(sh->max_rank >= 16 && sh->max_rank <= 64 && sh->max_rank % 16 == 0,
+                 "max_rank %d must be a multiple of 16 in [16, 64]", sh->max_rank);
   LORA_ARG_CHECK(sh->order == LORA_IDS_SORTED || sh->order == LORA_IDS_INTERLEAVED,
                  "order %d is not a lora_id_order", sh->order);
   LORA_ARG_CHECK(sh->reserved == 0, "reserved field must be 0");
@@ -226,7 +228,7 @@ lora_status lora_transpose_bf16(const uint16_t* src, uint16_t* dst, int64_t rows
 lora_status lora_forward(const lora_shape* shape, const uint16_t* x, const uint16_t* W,
                          const uint16_t* A_pack, const uint16_t* B_pack,
                          const lora_adapter_desc* desc, const int32_t* adapter_ids, uint16_t* y,
-                         float* u_saved, void* ws, size_t ws_bytes, void* stream) {
+                         uint16_t* u_saved, void* ws, size_t ws_bytes, void* stream) {
   TRY(check_shape(shape));
   const lora_shape& sh = *shape;
   LORA_ARG_CHECK(W && A_pack && B_pack && desc, "W, A_pack, B_pack and desc must be non-NULL");
@@ -246,10 +248,11 @@ lora_status lora_forward(const lora_shape* shape, const uint16_t* x, const uint1
   if (N == 0) return LORA_OK;
   timer_begin(LORA_TIMER_SHRINK, s);
   TRY(launch_shrink(x, sh.d_in, (int)sh.d_in, A_pack, 0, desc, w.active, w.perm, w.offsets,
-                    w.pre32, sh.n_adapters, sh.n_tokens, u_saved, sh.max_rank, s));
+                    w.pre32, sh.n_adapters, sh.n_tokens, u_saved, sh.max_rank, w.zero, s));
   timer_end(LORA_TIMER_SHRINK, s);
-  // base GEMM over rows in segment order with the expand y += s B_a u fused
-  LoraFuse f{w.perm, u_saved, sh.max_rank, 1, B_pack, desc, w.active, w.offsets, sh.n_adapters};
+  // base GEMM over rows in segment order with the expand y += B_a (s u) fused
+  LoraFuse f{w.perm, u_saved, sh.n_tokens * sh.max_rank, sh.max_rank, 1, B_pack, desc, w.active,
+             w.offsets, sh.n_adapters};
   timer_begin(LORA_TIMER_BASE_GEMM, s);
   TRY(gemm_nt_lora(x, W, y, N, (int)sh.d_out, (int)sh.d_in, sh.d_in, sh.d_in, sh.d_out, f, s));
   timer_end(LORA_TIMER_BASE_GEMM, s);
@@ -259,7 +262,7 @@ lora_status lora_forward(const lora_shape* shape, const uint16_t* x, const uint1
 lora_status lora_backward(const lora_shape* shape, const uint16_t* dy, const uint16_t* x,
                           const uint16_t* W_t, const uint16_t* A_pack, const uint16_t* B_pack,
                           const lora_adapter_desc* desc, const int32_t* adapter_ids,
-                          const float* u_saved, uint16_t* dx, float* dA_pack, float* dB_pack,
+                          const uint16_t* u_saved, uint16_t* dx, float* dA_pack, float* dB_pack,
                           int accumulate, void* ws, size_t ws_bytes, void* stream) {
   TRY(check_shape(shape));
   const lora_shape& sh = *shape;
@@ -285,19 +288,21 @@ lora_status lora_backward(const lora_shape* shape, const uint16_t* dy, const uin
   if (N > 0) {
     timer_begin(LORA_TIMER_SHRINK, s);
     TRY(launch_shrink(dy, sh.d_out, (int)sh.d_out, w.BT, 1, desc, w.active, w.perm, w.offsets,
-                      w.pre32, sh.n_adapters, sh.n_tokens, w.v, sh.max_rank, s));
+                      w.pre32, sh.n_adapters, sh.n_tokens, w.v, sh.max_rank, w.zero, s));
     timer_end(LORA_TIMER_SHRINK, s);
-    // dX = dY W over rows in segment order with the expand dX += s A_a^T v fused
-    LoraFuse f{w.perm, w.v, sh.max_rank, 0, w.AT, desc, w.active, w.offsets, sh.n_adapters};
+    // dX = dY W over rows in segment order with the expand dX += A_a^T (s v) fused
+    LoraFuse f{w.perm, w.v, sh.n_tokens * sh.max_rank, sh.max_rank, 0, w.AT, desc, w.active,
+               w.offsets, sh.n_adapters};
     timer_begin(LORA_TIMER_BASE_GEMM, s);
     TRY(gemm_nt_lora(dy, W_t, dx, N, (int)sh.d_in, (int)sh.d_out, sh.d_out, sh.d_out, sh.d_in, f, s));
     timer_end(LORA_TIMER_BASE_GEMM, s);
   }
   timer_begin(LORA_TIMER_GRAD, s);
-  TRY(launch_grad(0, u_saved, sh.max_rank, dy, sh.d_out, (int)sh.d_out, desc, w.active, w.perm,
-                  w.offsets, w.prec, sh.n_adapters, sh.n_tokens, dB_pack, w.partial, accumulate, s));
-  TRY(launch_grad(1, w.v, sh.max_rank, x, sh.d_in, (int)sh.d_in, desc, w.active, w.perm, w.offsets,
-                  w.prec, sh.n_adapters, sh.n_tokens, dA_pack, w.partial, accumulate, s));
+  TRY(launch_grad(0, u_saved, sh.max_rank, w.zero, dy, sh.d_out, (int)sh.d_out, desc, w.active,
+                  w.perm, w.offsets, w.prec, sh.n_adapters, sh.n_tokens, dB_pack, w.partial,
+                  accumulate, s));
+  TRY(launch_grad(1, w.v, sh.max_rank, w.zero, x, sh.d_in, (int)sh.d_in, desc, w.active, w.perm,
+                  w.offsets, w.prec, sh.n_adapters, sh.n_tokens, dA_pack, w.partial, accumulate, s));
   timer_end(LORA_TIMER_GRAD, s);
   return LORA_OK;
 }
@@ -441,6 +446,34 @@ lora_status adam_step(int64_t n, float* p, const float* g, float* m, float* v, i
   timer_begin(LORA_TIMER_ADAM, s);
   TRY(launch_adam(n, p, g, m, v, lr, beta1, beta2, eps, weight_decay, step_size, inv_sqrt_bc2,
                   p_bf16, s));
+  timer_end(LORA_TIMER_ADAM, s);
+  return LORA_OK;
+}
+
+lora_status adam_step_multi(int32_t n_seg, const adam_segment* segs, float* p, const float* g,
+                            float* m, float* v, float lr, float beta1, float beta2, float eps,
+                            float weight_decay, uint16_t* p_bf16, void* stream) {
+  LORA_ARG_CHECK(n_seg >= 0, "n_seg must be >= 0");
+  if (n_seg == 0) return LORA_OK;
+  LORA_ARG_CHECK(segs != nullptr, "segs is NULL");
+  LORA_ARG_CHECK(p && g && m && v, "p/g/m/v NULL");
+  LORA_ARG_CHECK(beta1 >= 0.f && beta1 < 1.f && beta2 >= 0.f && beta2 < 1.f, "betas must lie in [0, 1)");
+  std::vector<int64_t> off(n_seg), cnt(n_seg);
+  std::vector<float> ss(n_seg), ib(n_seg);
+  for (int i = 0; i < n_seg; ++i) {
+    LORA_ARG_CHECK(segs[i].offset >= 0 && segs[i].count >= 0, "segment %d: negative offset/count", i);
+    LORA_ARG_CHECK(segs[i].step >= 1, "segment %d: step must be >= 1", i);
+    off[i] = segs[i].offset;
+    cnt[i] = segs[i].count;
+    const double bc1 = 1.0 - std::pow((double)beta1, (double)segs[i].step);
+    const double bc2 = 1.0 - std::pow((double)beta2, (double)segs[i].step);
+    ss[i] = (float)((double)lr / bc1);
+    ib[i] = (float)(1.0 / std::sqrt(bc2));
+  }
+  hipStream_t s = S(stream);
+  timer_begin(LORA_TIMER_ADAM, s);
+  TRY(launch_adam_multi(n_seg, off.data(), cnt.data(), ss.data(), ib.data(), p, g, m, v, lr, beta1,
+                        beta2, eps, weight_decay, p_bf16, s));
   timer_end(LORA_TIMER_ADAM, s);
   return LORA_OK;
 }

@@ -24,22 +24,29 @@ __device__ __forceinline__ float bf2f_lo(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float bf2f_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
 // Round-to-nearest-even fp32 -> bf16 (quiet NaN preserved).
-__device__ __forceinline__ uint16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x0040u);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
+// fp32 -> bf16 round-to-nearest-even on the gfx950 conversion unit
+// (v_cvt_pk_bf16_f32, two values per instruction; NaN stays NaN).
+typedef __bf16 bf16x2_hw __attribute__((ext_vector_type(2)));
+typedef float f32x2_hw __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack2bf(float lo, float hi) {
-  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+  const f32x2_hw v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_hw));
+}
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
-// Split an fp32 value into hi + lo bf16 parts (hi = RNE(x), lo = RNE(x - hi)).
+// Split fp32 values into hi + lo bf16 parts (hi = RNE(x), lo = RNE(x - hi)).
 // hi + lo carries ~16 significant bits, so a product with an exact bf16 operand
-// accumulated by MFMA in fp32 loses ~2^-17 relative instead of 2^-9.
+// accumulated by MFMA in fp32 loses ~2^-16 relative instead of 2^-8.
 __device__ __forceinline__ void split_bf16(float x, uint16_t& hi, uint16_t& lo) {
   hi = f2bf(x);
   lo = f2bf(x - bf2f(hi));
+}
+// Two values at once: hi = packed RNE(a), RNE(b); lo = packed residuals.
+__device__ __forceinline__ void split2_bf16(float a, float b, uint32_t& hi, uint32_t& lo) {
+  hi = pack2bf(a, b);
+  lo = pack2bf(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xFFFF0000u));
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {

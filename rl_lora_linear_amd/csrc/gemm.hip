@@ -32,7 +32,8 @@ struct GemmEpi {
   // EPI_BF16 with the LoRA expand fused (nullable vec = plain GEMM): for the
   // row at segment position m, owned by adapter a, add s_a * vec[tok] . M_a^T
   // where M_a [N][r_a] sits at (use_b_off ? b_off : a_off) of the pack lmat.
-  const float* vec;       // [tokens][vec_ld] fp32, token order
+  const uint16_t* vec;    // scaled vector, bf16 hi plane [tokens][vec_ld], token order
+  int64_t vec_plane;      // lo plane at vec + vec_plane
   int vec_ld;
   int use_b_off;
   const uint16_t* lmat;
@@ -129,14 +130,9 @@ __device__ __forceinline__ void lora_slab(const GemmEpi& ep, int m0, int n0, int
       for (int i = 0; i < 4; ++i) {
         uint4 h = make_uint4(0, 0, 0, 0), l = make_uint4(0, 0, 0, 0);
         if (ad[i] == a && cok) {
-          const float4* vp = (const float4*)(ep.vec + (int64_t)tk[i] * ep.vec_ld + c);
-          const float4 x0 = vp[0], x1 = vp[1];
-          const float f[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-          uint16_t hh[8], ll[8];
-#pragma unroll
-          for (int q = 0; q < 8; ++q) split_bf16(d.scale * f[q], hh[q], ll[q]);
-          h = make_uint4(hh[0] | (hh[1] << 16), hh[2] | (hh[3] << 16), hh[4] | (hh[5] << 16), hh[6] | (hh[7] << 16));
-          l = make_uint4(ll[0] | (ll[1] << 16), ll[2] | (ll[3] << 16), ll[4] | (ll[5] << 16), ll[6] | (ll[7] << 16));
+          const uint16_t* vp = ep.vec + (int64_t)tk[i] * ep.vec_ld + c;
+          h = *(const uint4*)vp;
+          l = *(const uint4*)(vp + ep.vec_plane);
         }
         ah[i] = as_bf16x8(h);
         al[i] = as_bf16x8(l);
@@ -451,6 +447,7 @@ lora_status gemm_nt_lora(const uint16_t* A, const uint16_t* B, uint16_t* C, int 
   ep.ldc = ldc;
   ep.perm = f.perm;
   ep.vec = f.vec;
+  ep.vec_plane = f.vec_plane;
   ep.vec_ld = f.vec_ld;
   ep.use_b_off = f.use_b_off;
   ep.lmat = f.lmat;

@@ -162,6 +162,77 @@ __global__ __launch_bounds__(256) void adam_kernel(int64_t n, float* __restrict_
   }
 }
 
+// Batched AdamW: up to ADAM_SEGS segments per launch, described in the kernel
+// arguments.  Block b belongs to the segment whose block range holds it; each
+// block streams 4 x 256 x 4 elements with float4 vectors (scalar path if a
+// segment is not 16-byte aligned).
+constexpr int ADAM_SEGS = 64;
+constexpr int ADAM_BLOCK_ELEMS = 4096;
+struct AdamSegs {
+  int64_t off[ADAM_SEGS];
+  int64_t cnt[ADAM_SEGS];
+  int32_t blk0[ADAM_SEGS + 1];
+  float step_size[ADAM_SEGS];
+  float inv_sqrt_bc2[ADAM_SEGS];
+  int32_t n;
+};
+
+__global__ __launch_bounds__(256) void adam_multi_kernel(AdamSegs sg, float* __restrict__ p,
+                                                         const float* __restrict__ g,
+                                                         float* __restrict__ m,
+                                                         float* __restrict__ v, float lr, float b1,
+                                                         float b2, float eps, float wd,
+                                                         uint16_t* __restrict__ pb) {
+  const int b = blockIdx.x;
+  int s = 0;
+  while (s + 1 < sg.n && sg.blk0[s + 1] <= b) ++s;
+  const int64_t base = sg.off[s];
+  const int64_t n = sg.cnt[s];
+  const float ss = sg.step_size[s], ib = sg.inv_sqrt_bc2[s];
+  const int64_t e0 = (int64_t)(b - sg.blk0[s]) * ADAM_BLOCK_ELEMS;
+  const bool vec = ((base & 3) == 0) && (((uintptr_t)p | (uintptr_t)g | (uintptr_t)m | (uintptr_t)v) % 16 == 0);
+  if (vec) {
+#pragma unroll
+    for (int q = 0; q < ADAM_BLOCK_ELEMS / 1024; ++q) {
+      const int64_t e = e0 + ((int64_t)q * 256 + threadIdx.x) * 4;
+      if (e + 4 <= n) {
+        const int64_t i = (base + e) / 4;
+        float4 pp = ((float4*)p)[i], mm = ((float4*)m)[i], vv = ((float4*)v)[i];
+        const float4 gg = ((const float4*)g)[i];
+        adam_one(pp.x, gg.x, mm.x, vv.x, lr, b1, b2, eps, wd, ss, ib);
+        adam_one(pp.y, gg.y, mm.y, vv.y, lr, b1, b2, eps, wd, ss, ib);
+        adam_one(pp.z, gg.z, mm.z, vv.z, lr, b1, b2, eps, wd, ss, ib);
+        adam_one(pp.w, gg.w, mm.w, vv.w, lr, b1, b2, eps, wd, ss, ib);
+        ((float4*)p)[i] = pp;
+        ((float4*)m)[i] = mm;
+        ((float4*)v)[i] = vv;
+        if (pb) {
+          if ((((uintptr_t)(pb + base + e)) & 7) == 0) {
+            *(uint2*)(pb + base + e) = make_uint2(pack2bf(pp.x, pp.y), pack2bf(pp.z, pp.w));
+          } else {
+            pb[base + e] = f2bf(pp.x); pb[base + e + 1] = f2bf(pp.y);
+            pb[base + e + 2] = f2bf(pp.z); pb[base + e + 3] = f2bf(pp.w);
+          }
+        }
+      } else {
+        for (int64_t k = e; k < n && k < e + 4; ++k) {
+          float pp = p[base + k], mm = m[base + k], vv = v[base + k];
+          adam_one(pp, g[base + k], mm, vv, lr, b1, b2, eps, wd, ss, ib);
+          p[base + k] = pp; m[base + k] = mm; v[base + k] = vv;
+          if (pb) pb[base + k] = f2bf(pp);
+        }
+      }
+    }
+  } else {
+    for (int64_t k = e0 + threadIdx.x; k < min(n, e0 + ADAM_BLOCK_ELEMS); k += 256) {
+      float pp = p[base + k], mm = m[base + k], vv = v[base + k];
+      adam_one(pp, g[base + k], mm, vv, lr, b1, b2, eps, wd, ss, ib);
+      p[base + k] = pp; m[base + k] = mm; v[base + k] = vv;
+      if (pb) pb[base + k] = f2bf(pp);
+    }
+  }
+}
+
 // ------------------------------------------------------------------ SwiGLU
 __device__ __forceinline__ float sigmoidf_(float z) { return 1.f / (1.f + exp2f(-z * kLog2eF)); }
 
@@ -298,6 +369,32 @@ lora_status launch_adam(int64_t n, float* p, const float* g, float* m, float* v,
     hipLaunchKernelGGL(adam_kernel<false>, dim3(grid), dim3(256), 0, s, n, p, g, m, v, lr, beta1,
                        beta2, eps, wd, step_size, inv_sqrt_bc2, p_bf16);
   return launch_check("adam");
+}
+
+lora_status launch_adam_multi(int n_seg, const int64_t* off, const int64_t* cnt,
+                              const float* step_size, const float* inv_sqrt_bc2, float* p,
+                              const float* g, float* m, float* v, float lr, float beta1,
+                              float beta2, float eps, float wd, uint16_t* p_bf16, hipStream_t s) {
+  for (int s0 = 0; s0 < n_seg; s0 += ADAM_SEGS) {
+    AdamSegs sg{};
+    sg.n = std::min(ADAM_SEGS, n_seg - s0);
+    int32_t blocks = 0;
+    for (int i = 0; i < sg.n; ++i) {
+      sg.off[i] = off[s0 + i];
+      sg.cnt[i] = cnt[s0 + i];
+      sg.step_size[i] = step_size[s0 + i];
+      sg.inv_sqrt_bc2[i] = inv_sqrt_bc2[s0 + i];
+      sg.blk0[i] = blocks;
+      blocks += (int32_t)cdiv(cnt[s0 + i], ADAM_BLOCK_ELEMS);
+    }
+    sg.blk0[sg.n] = blocks;
+    if (blocks == 0) continue;
+    hipLaunchKernelGGL(adam_multi_kernel, dim3(blocks), dim3(256), 0, s, sg, p, g, m, v, lr, beta1,
+                       beta2, eps, wd, p_bf16);
+    lora_status st = launch_check("adam_multi");
+    if (st) return st;
+  }
+  return LORA_OK;
 }
 
 lora_status launch_swiglu_fwd(int64_t n, const uint16_t* g, const uint16_t* u, uint16_t* h,

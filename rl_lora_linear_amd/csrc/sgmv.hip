@@ -72,9 +72,10 @@ __device__ __forceinline__ void wait_vm_barrier() {
 
 template <int NB>
 __device__ __forceinline__ void shrink_tile(const uint16_t* __restrict__ in, int64_t ld_in, int K,
-                                            const uint16_t* __restrict__ mat, int r,
+                                            const uint16_t* __restrict__ mat, int r, float scale,
                                             const int32_t* __restrict__ perm, int p0, int rows,
-                                            uint4* lds, float* __restrict__ out, int r_max) {
+                                            uint4* lds, uint16_t* __restrict__ out, int64_t plane,
+                                            int r_max) {
   constexpr int MSLOTS = NB * 16 * 16;                 // factor tile slots per stage
   constexpr int STAGE = SH_XSLOTS + MSLOTS;
   constexpr int PER_WAVE = 2 + NB;                     // DMA instructions per wave per stage
@@ -175,9 +176,14 @@ __device__ __forceinline__ void shrink_tile(const uint16_t* __restrict__ in, int
         sacc += red[(2 * SH_TM + row) * 64 + c];
         sacc += red[(3 * SH_TM + row) * 64 + c];
       }
-      v[q] = sacc;
+      v[q] = scale * sacc;
     }
-    *(float4*)(out + (int64_t)perm[p0 + row] * r_max + cg) = make_float4(v[0], v[1], v[2], v[3]);
+    uint32_t h01, l01, h23, l23;
+    split2_bf16(v[0], v[1], h01, l01);
+    split2_bf16(v[2], v[3], h23, l23);
+    uint16_t* o = out + (int64_t)perm[p0 + row] * r_max + cg;
+    *(uint2*)o = make_uint2(h01, h23);
+    *(uint2*)(o + plane) = make_uint2(l01, l23);
   }
 }
 
@@ -188,18 +194,21 @@ __global__ __launch_bounds__(256) void shrink_kernel(
     const uint16_t* __restrict__ in, int64_t ld_in, int K, const uint16_t* __restrict__ mat_pack,
     int use_b_off, const lora_adapter_desc* __restrict__ desc, const uint8_t* __restrict__ active,
     const int32_t* __restrict__ perm, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ pre32, int n_ad, int64_t n_tokens, float* __restrict__ out,
-    int r_max) {
+    const int32_t* __restrict__ pre32, int n_ad, int64_t n_tokens, uint16_t* __restrict__ out,
+    int r_max, uint4* __restrict__ zero) {
   extern __shared__ uint4 sh_lds[];
   const int tid = threadIdx.x;
   if (blockIdx.y == 1) {
+    if (blockIdx.x == 0 && zero != nullptr && tid < 16) zero[tid] = make_uint4(0, 0, 0, 0);
     const int64_t p = (int64_t)blockIdx.x * 256 + tid;
     if (p >= n_tokens) return;
     bool dead = p >= offsets[n_ad];
     if (!dead) dead = !active[find_bucket(offsets, n_ad + 1, (int32_t)p)];
     if (dead) {
-      float* o = out + (int64_t)perm[p] * r_max;
-      for (int c = 0; c < r_max; ++c) o[c] = 0.f;
+      const int64_t plane = n_tokens * r_max;
+      uint4* o = (uint4*)(out + (int64_t)perm[p] * r_max);
+      uint4* ol = (uint4*)(out + plane + (int64_t)perm[p] * r_max);
+      for (int c = 0; c < r_max / 8; ++c) o[c] = ol[c] = make_uint4(0, 0, 0, 0);
     }
     return;
   }
@@ -209,10 +218,12 @@ __global__ __launch_bounds__(256) void shrink_kernel(
   const int r = d.rank;
   const uint16_t* mat = mat_pack + (use_b_off ? d.b_off : d.a_off);
   const int nb = (r + 15) / 16;
-  if (nb == 1) shrink_tile<1>(in, ld_in, K, mat, r, perm, ti.p0, ti.rows, sh_lds, out, r_max);
-  else if (nb == 2) shrink_tile<2>(in, ld_in, K, mat, r, perm, ti.p0, ti.rows, sh_lds, out, r_max);
-  else if (nb == 3) shrink_tile<3>(in, ld_in, K, mat, r, perm, ti.p0, ti.rows, sh_lds, out, r_max);
-  else shrink_tile<4>(in, ld_in, K, mat, r, perm, ti.p0, ti.rows, sh_lds, out, r_max);
+  const int64_t plane = n_tokens * r_max;
+  const float sc = d.scale;
+  if (nb == 1) shrink_tile<1>(in, ld_in, K, mat, r, sc, perm, ti.p0, ti.rows, sh_lds, out, plane, r_max);
+  else if (nb == 2) shrink_tile<2>(in, ld_in, K, mat, r, sc, perm, ti.p0, ti.rows, sh_lds, out, plane, r_max);
+  else if (nb == 3) shrink_tile<3>(in, ld_in, K, mat, r, sc, perm, ti.p0, ti.rows, sh_lds, out, plane, r_max);
+  else shrink_tile<4>(in, ld_in, K, mat, r, sc, perm, ti.p0, ti.rows, sh_lds, out, plane, r_max);
 }
 
 // ------------------------------------------------------------------ grad
@@ -221,17 +232,26 @@ constexpr int GR_TT = 32;     // tokens per stage
 constexpr int GR_NJ = 256;    // output columns per block
 constexpr int GR_NST = 5;     // LDS ring depth (DMA four stages ahead)
 constexpr int GR_QSLOTS = GR_TT * 32;   // 32 token rows x 512 B of Q
-constexpr int GR_PSLOTS = GR_TT * 16;   // 32 token rows x 64 fp32 of P
-constexpr int GR_STAGE = GR_QSLOTS + GR_PSLOTS;
-constexpr int GR_PER_WAVE = 6;          // DMA instructions per wave per stage (4 Q + 2 P)
+constexpr int GR_QDMA = 4;              // Q DMA instructions per wave per stage
+// The P tile of a stage holds both bf16 planes (hi, lo) of 32 tokens, each
+// token row 4*PN 16-byte chunks wide (PN = 1: ranks <= 32, PN = 2: <= 64).
+template <int PN> struct GrP {
+  static constexpr int PW = 4 * PN;                 // chunks per token row
+  static constexpr int SLOTS = 2 * GR_TT * PW;      // 256 * PN
+  static constexpr int STAGE = GR_QSLOTS + SLOTS;
+  static constexpr int PER_WAVE = GR_QDMA + PN;     // DMA instructions per wave per stage
+  // pair (32-byte) swizzle: the 8 token rows that one transposing read of 32
+  // lanes touches (t0..t0+3 and t0+8..t0+11) land on distinct banks
+  static __device__ __forceinline__ int sw(int t) {
+    return PN == 1 ? ((t >> 3) & 1) : (((t >> 1) & 1) | (((t >> 3) & 1) << 1));
+  }
+};
 
 // Q tile swizzle: chunk c of token row t is stored at c ^ fq(t).  A transposed
 // 8-byte read (ds_read_b64_tr_b16) by 16 lanes touches 4 consecutive rows x
 // 32 B; fq spreads those rows (and the rows of the next 16-lane group, 8 rows
 // further) over distinct banks.
 __device__ __forceinline__ int gr_fq(int t) { return (2 * (t & 3)) | (8 * ((t >> 3) & 1)); }
-// P tile swizzle (16 chunks per row): the four 16-lane groups read rows 8 apart.
-__device__ __forceinline__ int gr_fp(int t) { return 4 * ((t >> 3) & 3); }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
@@ -245,65 +265,82 @@ __device__ __forceinline__ uint2 tr_read(const uint4* base, uint32_t byte_off) {
   return c.u;
 }
 
-// T[c][j] = s_a sum_{t in chunk} P[t][c] Q[t][j] for one chunk of one adapter
-// and 256 columns j.  MFMA K is the token axis: each 32-token stage is one
-// v_mfma_f32_16x16x32 per (16 columns, 16 ranks, hi|lo).  Q fragments come from
-// the row-major LDS tile through the transposing read: in a 16-lane group,
-// lane 4q + b addresses row (t0 + q), columns 4b..4b+3, and lane i receives
-// column i of rows t0..t0+3.  P fragments are 8 strided fp32 LDS reads,
-// zeroed past the chunk's last token, split hi+lo in registers.
+// T[c][j] = sum_{t in chunk} P[t][c] Q[t][j] for one chunk of one adapter and
+// 256 columns j.  P is the scaled per-token vector stored as two bf16 planes
+// (hi, lo; hi + lo carries ~16 bits), so both MFMA operands are bf16 and the
+// product is exact up to fp32 accumulation.  MFMA K is the token axis: each
+// 32-token stage is one v_mfma_f32_16x16x32 per (16 columns, 16 ranks, plane).
+// Both operands come from row-major LDS tiles through the transposing read: in
+// a 16-lane group, lane 4q + b addresses row (t0 + q), columns 4b..4b+3, and
+// lane i receives column i of rows t0..t0+3.  Tokens past the chunk end read a
+// zero row for P, so they add nothing.
 // mode 0 (dB): out layout [D][r] (c fastest): MFMA M = c, N = j.
 // mode 1 (dA): out layout [r][D] (j fastest): MFMA M = j, N = c.
-template <int NCB, int MODE>
-__device__ __forceinline__ void grad_tile(const float* __restrict__ P, int r_max,
+template <int NCB, int MODE, int PN>
+__device__ __forceinline__ void grad_tile(const uint16_t* __restrict__ P, int64_t plane, int r_max,
+                                          const uint16_t* __restrict__ zero,
                                           const uint16_t* __restrict__ Q, int64_t ld_q, int D,
-                                          const int32_t* tok_s, int rows, int r, int j0,
-                                          uint4* lds, f32x4 (&acc)[4][4]) {
+                                          const int32_t* tok_s, int rows, int j0, uint4* lds,
+                                          f32x4 (&acc)[4][4]) {
+  using G = GrP<PN>;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int KT = (rows + GR_TT - 1) / GR_TT;
-  const int pcn = r_max / 4;  // valid 16-byte chunks of a P row
-  // DMA sources: Q rows (w*4+i)*2 + L/32, chunk L%32; P rows (w*2+i)*4 + L/16, chunk L%16
-  int qrow[4], qcol[4], prow[2], pch[2];
+  // DMA sources.  Q: instruction i of wave w fills rows (4w + i)*2 + L/32,
+  // chunk L%32.  P: slot s = (w*PN + i)*64 + L holds plane s / (32*PW), token
+  // row (s / PW) % 32, physical chunk s % PW.
+  int qrow[GR_QDMA], qcol[GR_QDMA];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = (wave * 4 + i) * 2 + (lane >> 5);
+  for (int i = 0; i < GR_QDMA; ++i) {
+    const int row = (wave * GR_QDMA + i) * 2 + (lane >> 5);
     qrow[i] = row;
     qcol[i] = min(j0 + (((lane & 31) ^ gr_fq(row)) * 8), D - 8);
   }
+  int prow[PN];
+  int64_t poff[PN];
+  int pzoff[PN];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int row = (wave * 2 + i) * 4 + (lane >> 4);
-    prow[i] = row;
-    pch[i] = min((lane & 15) ^ gr_fp(row), pcn - 1);
+  for (int i = 0; i < PN; ++i) {
+    const int s = (wave * PN + i) * 64 + lane;
+    const int pl = s / (GR_TT * G::PW);
+    const int t = (s / G::PW) % GR_TT;
+    const int c = min((s % G::PW) ^ (2 * G::sw(t)), r_max / 8 - 1);
+    prow[i] = t;
+    poff[i] = pl * plane + c * 8;
+    pzoff[i] = c * 8;
   }
   auto issue = [&](int st, int kt) {
-    uint4* base = lds + st * GR_STAGE;
+    uint4* base = lds + st * G::STAGE;
     const int t0 = kt * GR_TT;
+    int qt[GR_QDMA], pt[PN];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int tr = min(t0 + qrow[i], rows - 1);
-      const uint16_t* g = Q + (int64_t)tok_s[tr] * ld_q + qcol[i];
-      dma16(g, __builtin_amdgcn_readfirstlane(lds_u32(base + (wave * 4 + i) * 64)));
+    for (int i = 0; i < GR_QDMA; ++i) qt[i] = tok_s[min(t0 + qrow[i], rows - 1)];
+#pragma unroll
+    for (int i = 0; i < PN; ++i) {
+      const int tp = tok_s[min(t0 + prow[i], rows - 1)];   // unconditional read: no branch
+      pt[i] = t0 + prow[i] < rows ? tp : -1;
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int tr = min(t0 + prow[i], rows - 1);
-      const float* g = P + (int64_t)tok_s[tr] * r_max + pch[i] * 4;
-      dma16(g, __builtin_amdgcn_readfirstlane(lds_u32(base + GR_QSLOTS + (wave * 2 + i) * 64)));
+    for (int i = 0; i < GR_QDMA; ++i)
+      dma16(Q + (int64_t)qt[i] * ld_q + qcol[i],
+            __builtin_amdgcn_readfirstlane(lds_u32(base + (wave * GR_QDMA + i) * 64)));
+#pragma unroll
+    for (int i = 0; i < PN; ++i) {
+      const uint16_t* g = pt[i] >= 0 ? P + (int64_t)pt[i] * r_max + poff[i] : zero + pzoff[i];
+      dma16(g, __builtin_amdgcn_readfirstlane(lds_u32(base + GR_QSLOTS + (wave * PN + i) * 64)));
     }
   };
 
 #pragma unroll
   for (int st = 0; st < GR_NST - 1; ++st) issue(st, min(st, KT - 1));
-  wait_vm_barrier<(GR_NST - 2) * GR_PER_WAVE>();
+  wait_vm_barrier<(GR_NST - 2) * G::PER_WAVE>();
 
   const int g16 = lane >> 4;   // 16-lane group: tokens 8*g16 .. 8*g16+7 of the stage
   const int li = lane & 15;
   for (int kt = 0; kt < KT; ++kt) {
     const int st = kt % GR_NST;
     issue((kt + GR_NST - 1) % GR_NST, min(kt + GR_NST - 1, KT - 1));
-    const uint4* qt = lds + st * GR_STAGE;
-    const float* pt = (const float*)(qt + GR_QSLOTS);
+    const uint4* qt = lds + st * G::STAGE;
+    const uint4* ptile = qt + GR_QSLOTS;
     // Q fragments: 4 column sub-tiles of this wave's 64 columns
     bf16x8 qf[4];
 #pragma unroll
@@ -318,45 +355,45 @@ __device__ __forceinline__ void grad_tile(const float* __restrict__ P, int r_max
       }
       qf[jt] = as_bf16x8(make_uint4(hv[0].x, hv[0].y, hv[1].x, hv[1].y));
     }
-    // P fragments: tokens 8*g16 + q, rank column cb*16 + li
-    bf16x8 ph[NCB], pl[NCB];
+    // P fragments (both planes): tokens 8*g16 .. +7, rank column cb*16 + li
+    bf16x8 pf[2][NCB];
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-      const int c = cb * 16 + li;
-      uint16_t hh[8], ll[8];
+    for (int pl = 0; pl < 2; ++pl)
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int t = 8 * g16 + q;
-        float f = pt[t * 64 + (((c >> 2) ^ gr_fp(t)) << 2) + (c & 3)];
-        if (kt * GR_TT + t >= rows || c >= r) f = 0.f;
-        split_bf16(f, hh[q], ll[q]);
+      for (int cb = 0; cb < NCB; ++cb) {
+        uint2 hv[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int t = 8 * g16 + 4 * h + (li >> 2);
+          const int col = cb * 16 + 4 * (li & 3);
+          const int pc = (col >> 3) ^ (2 * G::sw(t));
+          const uint32_t off = ((pl * GR_TT + t) * G::PW + pc) * 16 + ((col & 7) << 1);
+          hv[h] = tr_read(ptile, off);
+        }
+        pf[pl][cb] = as_bf16x8(make_uint4(hv[0].x, hv[0].y, hv[1].x, hv[1].y));
       }
-      ph[cb] = as_bf16x8(make_uint4(hh[0] | (hh[1] << 16), hh[2] | (hh[3] << 16),
-                                    hh[4] | (hh[5] << 16), hh[6] | (hh[7] << 16)));
-      pl[cb] = as_bf16x8(make_uint4(ll[0] | (ll[1] << 16), ll[2] | (ll[3] << 16),
-                                    ll[4] | (ll[5] << 16), ll[6] | (ll[7] << 16)));
-    }
 #pragma unroll
     for (int jt = 0; jt < 4; ++jt)
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
         if (MODE == 0) {
-          acc[jt][cb] = mfma16(ph[cb], qf[jt], acc[jt][cb]);
-          acc[jt][cb] = mfma16(pl[cb], qf[jt], acc[jt][cb]);
+          acc[jt][cb] = mfma16(pf[0][cb], qf[jt], acc[jt][cb]);
+          acc[jt][cb] = mfma16(pf[1][cb], qf[jt], acc[jt][cb]);
         } else {
-          acc[jt][cb] = mfma16(qf[jt], ph[cb], acc[jt][cb]);
-          acc[jt][cb] = mfma16(qf[jt], pl[cb], acc[jt][cb]);
+          acc[jt][cb] = mfma16(qf[jt], pf[0][cb], acc[jt][cb]);
+          acc[jt][cb] = mfma16(qf[jt], pf[1][cb], acc[jt][cb]);
         }
       }
-    wait_vm_barrier<(GR_NST - 2) * GR_PER_WAVE>();
+    wait_vm_barrier<(GR_NST - 2) * G::PER_WAVE>();
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no DMA may outlive the block
 }
 
 // grid = (chunk-slot bound, ceil(D / 256)).
-template <int MODE>
+template <int MODE, int PN>
 __global__ __launch_bounds__(256) void grad_kernel(
-    const float* __restrict__ P, int r_max, const uint16_t* __restrict__ Q, int64_t ld_q, int D,
+    const uint16_t* __restrict__ P, int64_t plane, int r_max, const uint16_t* __restrict__ zero,
+    const uint16_t* __restrict__ Q, int64_t ld_q, int D,
     const lora_adapter_desc* __restrict__ desc, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ chunk_pre, int n_ad,
     float* __restrict__ out_pack, float* __restrict__ partial, int accumulate) {
@@ -381,16 +418,20 @@ __global__ __launch_bounds__(256) void grad_kernel(
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int ncb = (r + 15) / 16;
-  if (ncb == 1) grad_tile<1, MODE>(P, r_max, Q, ld_q, D, tok_s, ti.rows, r, j0, gr_lds, acc);
-  else if (ncb == 2) grad_tile<2, MODE>(P, r_max, Q, ld_q, D, tok_s, ti.rows, r, j0, gr_lds, acc);
-  else if (ncb == 3) grad_tile<3, MODE>(P, r_max, Q, ld_q, D, tok_s, ti.rows, r, j0, gr_lds, acc);
-  else grad_tile<4, MODE>(P, r_max, Q, ld_q, D, tok_s, ti.rows, r, j0, gr_lds, acc);
+  if (PN == 1) {
+    if (ncb == 1) grad_tile<1, MODE, PN>(P, plane, r_max, zero, Q, ld_q, D, tok_s, ti.rows, j0, gr_lds, acc);
+    else grad_tile<2, MODE, PN>(P, plane, r_max, zero, Q, ld_q, D, tok_s, ti.rows, j0, gr_lds, acc);
+  } else {
+    if (ncb == 1) grad_tile<1, MODE, PN>(P, plane, r_max, zero, Q, ld_q, D, tok_s, ti.rows, j0, gr_lds, acc);
+    else if (ncb == 2) grad_tile<2, MODE, PN>(P, plane, r_max, zero, Q, ld_q, D, tok_s, ti.rows, j0, gr_lds, acc);
+    else if (ncb == 3) grad_tile<3, MODE, PN>(P, plane, r_max, zero, Q, ld_q, D, tok_s, ti.rows, j0, gr_lds, acc);
+    else grad_tile<4, MODE, PN>(P, plane, r_max, zero, Q, ld_q, D, tok_s, ti.rows, j0, gr_lds, acc);
+  }
 
   // ---- write.  Region of this adapter: D*r floats.
   const int64_t base = MODE == 0 ? d.b_off : d.a_off;
   const bool direct = nchunks == 1;
   float* dst = direct ? out_pack + base : partial + (int64_t)slot * D * r_max;
-  const float sc = d.scale;
 #pragma unroll
   for (int jt = 0; jt < 4; ++jt)
 #pragma unroll
@@ -402,7 +443,7 @@ __global__ __launch_bounds__(256) void grad_kernel(
         const int j = j0 + wave * 64 + jt * 16 + (lane & 15);
         if (c >= r || j >= D) continue;
         float4* p = (float4*)(dst + (int64_t)j * r + c);
-        float4 v = make_float4(sc * acc[jt][ct][0], sc * acc[jt][ct][1], sc * acc[jt][ct][2], sc * acc[jt][ct][3]);
+        float4 v = make_float4(acc[jt][ct][0], acc[jt][ct][1], acc[jt][ct][2], acc[jt][ct][3]);
         if (direct && accumulate) {
           float4 o = *p;
           v.x += o.x; v.y += o.y; v.z += o.z; v.w += o.w;
@@ -414,7 +455,7 @@ __global__ __launch_bounds__(256) void grad_kernel(
         const int c = ct * 16 + (lane & 15);
         if (c >= r || j >= D) continue;
         float4* p = (float4*)(dst + (int64_t)c * D + j);
-        float4 v = make_float4(sc * acc[jt][ct][0], sc * acc[jt][ct][1], sc * acc[jt][ct][2], sc * acc[jt][ct][3]);
+        float4 v = make_float4(acc[jt][ct][0], acc[jt][ct][1], acc[jt][ct][2], acc[jt][ct][3]);
         if (direct && accumulate) {
           float4 o = *p;
           v.x += o.x; v.y += o.y; v.z += o.z; v.w += o.w;
@@ -501,7 +542,8 @@ using namespace lora;
 lora_status launch_shrink(const uint16_t* in, int64_t ld_in, int K, const uint16_t* mat_pack,
                           int use_b_off, const lora_adapter_desc* desc, const uint8_t* active,
                           const int32_t* perm, const int32_t* offsets, const int32_t* pre32,
-                          int n_ad, int64_t n_tokens, float* out, int r_max, hipStream_t s) {
+                          int n_ad, int64_t n_tokens, uint16_t* out, int r_max, void* zero,
+                          hipStream_t s) {
   if (n_tokens <= 0) return LORA_OK;
   const int64_t bound = std::max(cdiv(n_tokens, SH_TM) + n_ad, cdiv(n_tokens, 256));
   const int nb_max = (r_max + 15) / 16;
@@ -515,34 +557,49 @@ lora_status launch_shrink(const uint16_t* in, int64_t ld_in, int K, const uint16
   }
   hipLaunchKernelGGL(shrink_kernel, dim3((unsigned)bound, 2), dim3(256), lds, s, in, ld_in, K,
                      mat_pack, use_b_off, desc, active, perm, offsets, pre32, n_ad, n_tokens, out,
-                     r_max);
+                     r_max, (uint4*)zero);
   return launch_check("shrink");
 }
 
-lora_status launch_grad(int mode, const float* P, int r_max, const uint16_t* Q, int64_t ld_q,
-                        int D, const lora_adapter_desc* desc, const uint8_t* active,
-                        const int32_t* perm, const int32_t* offsets, const int32_t* chunk_pre,
-                        int n_ad, int64_t n_tokens, float* out_pack, float* partial,
-                        int accumulate, hipStream_t s) {
+template <int MODE, int PN>
+lora_status launch_grad_t(dim3 grid, const uint16_t* P, int64_t plane, int r_max,
+                          const uint16_t* zero, const uint16_t* Q, int64_t ld_q, int D,
+                          const lora_adapter_desc* desc, const int32_t* perm,
+                          const int32_t* offsets, const int32_t* chunk_pre, int n_ad,
+                          float* out_pack, float* partial, int accumulate, hipStream_t s) {
+  const size_t lds = (size_t)GR_NST * GrP<PN>::STAGE * sizeof(uint4);
+  static bool attr = false;
+  if (!attr) {
+    TRY_HIP(hipFuncSetAttribute((const void*)grad_kernel<MODE, PN>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
+    attr = true;
+  }
+  hipLaunchKernelGGL((grad_kernel<MODE, PN>), grid, dim3(256), lds, s, P, plane, r_max, zero, Q,
+                     ld_q, D, desc, perm, offsets, chunk_pre, n_ad, out_pack, partial, accumulate);
+  return launch_check("grad");
+}
+
+lora_status launch_grad(int mode, const uint16_t* P, int r_max, const void* zero,
+                        const uint16_t* Q, int64_t ld_q, int D, const lora_adapter_desc* desc,
+                        const uint8_t* active, const int32_t* perm, const int32_t* offsets,
+                        const int32_t* chunk_pre, int n_ad, int64_t n_tokens, float* out_pack,
+                        float* partial, int accumulate, hipStream_t s) {
   if (n_tokens > 0) {
     const int64_t bound = cdiv(n_tokens, GR_TC) + n_ad;
     dim3 grid((unsigned)bound, (unsigned)cdiv(D, GR_NJ));
-    const size_t lds = (size_t)GR_NST * GR_STAGE * sizeof(uint4);
-    static bool attr = false;
-    if (!attr) {
-      TRY_HIP(hipFuncSetAttribute((const void*)grad_kernel<0>,
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
-      TRY_HIP(hipFuncSetAttribute((const void*)grad_kernel<1>,
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
-      attr = true;
-    }
-    if (mode == 0)
-      hipLaunchKernelGGL(grad_kernel<0>, grid, dim3(256), lds, s, P, r_max, Q, ld_q, D, desc, perm,
-                         offsets, chunk_pre, n_ad, out_pack, partial, accumulate);
+    const int64_t plane = n_tokens * r_max;
+    const uint16_t* z = (const uint16_t*)zero;
+    lora_status st;
+    if (r_max <= 32)
+      st = mode == 0 ? launch_grad_t<0, 1>(grid, P, plane, r_max, z, Q, ld_q, D, desc, perm, offsets,
+                                           chunk_pre, n_ad, out_pack, partial, accumulate, s)
+                     : launch_grad_t<1, 1>(grid, P, plane, r_max, z, Q, ld_q, D, desc, perm, offsets,
+                                           chunk_pre, n_ad, out_pack, partial, accumulate, s);
     else
-      hipLaunchKernelGGL(grad_kernel<1>, grid, dim3(256), lds, s, P, r_max, Q, ld_q, D, desc, perm,
-                         offsets, chunk_pre, n_ad, out_pack, partial, accumulate);
-    lora_status st = launch_check("grad");
+      st = mode == 0 ? launch_grad_t<0, 2>(grid, P, plane, r_max, z, Q, ld_q, D, desc, perm, offsets,
+                                           chunk_pre, n_ad, out_pack, partial, accumulate, s)
+                     : launch_grad_t<1, 2>(grid, P, plane, r_max, z, Q, ld_q, D, desc, perm, offsets,
+                                           chunk_pre, n_ad, out_pack, partial, accumulate, s);
     if (st) return st;
   }
   const int64_t per = (int64_t)D * r_max;

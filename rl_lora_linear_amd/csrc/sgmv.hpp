@@ -10,7 +10,8 @@ lora_status gemm_nt_bf16(const uint16_t* A, const uint16_t* B, uint16_t* C, int 
 // Row gather/scatter through perm and the fused LoRA expand of the base GEMM.
 struct LoraFuse {
   const int32_t* perm;      // segment order -> token
-  const float* vec;         // per-token fp32 vector [tokens][vec_ld]
+  const uint16_t* vec;      // per-token scaled vector: bf16 hi plane [tokens][vec_ld],
+  int64_t vec_plane;        // lo plane at vec + vec_plane
   int vec_ld;
   int use_b_off;            // factor at b_off (B_a [N][r]) or a_off (A_a^T [N][r])
   const uint16_t* lmat;
@@ -32,12 +33,13 @@ lora_status gemm_nt_grad(const uint16_t* A, const uint16_t* B, uint16_t* G, int6
 lora_status launch_shrink(const uint16_t* in, int64_t ld_in, int K, const uint16_t* mat_pack,
                           int use_b_off, const lora_adapter_desc* desc, const uint8_t* active,
                           const int32_t* perm, const int32_t* offsets, const int32_t* pre32,
-                          int n_ad, int64_t n_tokens, float* out, int r_max, hipStream_t s);
-lora_status launch_grad(int mode, const float* P, int r_max, const uint16_t* Q, int64_t ld_q,
-                        int D, const lora_adapter_desc* desc, const uint8_t* active,
-                        const int32_t* perm, const int32_t* offsets, const int32_t* chunk_pre,
-                        int n_ad, int64_t n_tokens, float* out_pack, float* partial,
-                        int accumulate, hipStream_t s);
+                          int n_ad, int64_t n_tokens, uint16_t* out, int r_max, void* zero,
+                          hipStream_t s);
+lora_status launch_grad(int mode, const uint16_t* P, int r_max, const void* zero,
+                        const uint16_t* Q, int64_t ld_q, int D, const lora_adapter_desc* desc,
+                        const uint8_t* active, const int32_t* perm, const int32_t* offsets,
+                        const int32_t* chunk_pre, int n_ad, int64_t n_tokens, float* out_pack,
+                        float* partial, int accumulate, hipStream_t s);
 int64_t grad_partial_floats(int64_t n_tokens, int n_ad, int64_t D, int r_max);
 lora_status launch_adapter_transpose(const uint16_t* A_pack, const uint16_t* B_pack,
                                      const lora_adapter_desc* desc, const uint8_t* active,
@@ -56,6 +58,10 @@ lora_status launch_loss(int kind, int64_t n, const float* logp, const float* w, 
 lora_status launch_adam(int64_t n, float* p, const float* g, float* m, float* v, float lr,
                         float beta1, float beta2, float eps, float wd, float step_size,
                         float inv_sqrt_bc2, uint16_t* p_bf16, hipStream_t s);
+lora_status launch_adam_multi(int n_seg, const int64_t* off, const int64_t* cnt,
+                              const float* step_size, const float* inv_sqrt_bc2, float* p,
+                              const float* g, float* m, float* v, float lr, float beta1,
+                              float beta2, float eps, float wd, uint16_t* p_bf16, hipStream_t s);
 lora_status launch_swiglu_fwd(int64_t n, const uint16_t* g, const uint16_t* u, uint16_t* h,
                               hipStream_t s);
 lora_status launch_swiglu_bwd(int64_t n, const uint16_t* dh, const uint16_t* g,

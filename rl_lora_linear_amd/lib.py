@@ -30,7 +30,8 @@ EXPORTS = [
     "lora_segments_workspace_bytes", "lora_segments", "lora_transpose_bf16", "lora_forward",
     "lora_backward", "token_logprobs_workspace_bytes", "token_logprobs",
     "token_logprobs_backward_workspace_bytes", "token_logprobs_backward",
-    "loss_grad_workspace_bytes", "loss_grad", "adam_step", "swiglu_forward", "swiglu_backward",
+    "loss_grad_workspace_bytes", "loss_grad", "adam_step", "adam_step_multi", "swiglu_forward",
+    "swiglu_backward",
     "lora_timing_enable", "lora_timing_reset", "lora_timing_read",
 ]
 
@@ -46,6 +47,10 @@ class LoraShape(ctypes.Structure):
                 ("a_pack_elems", ctypes.c_int64), ("b_pack_elems", ctypes.c_int64),
                 ("n_adapters", ctypes.c_int32), ("max_rank", ctypes.c_int32),
                 ("order", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class AdamSegment(ctypes.Structure):
+    _fields_ = [("offset", ctypes.c_int64), ("count", ctypes.c_int64), ("step", ctypes.c_int64)]
 
 
 class LossConfig(ctypes.Structure):
@@ -85,6 +90,8 @@ def _load() -> ctypes.CDLL:
         "loss_grad": (_I32, [_I32, _I64, _P, _P, _P, _P, _P, ctypes.POINTER(LossConfig), _P, _P, _P,
                              _SZ, _P]),
         "adam_step": (_I32, [_I64, _P, _P, _P, _P, _I64, _F, _F, _F, _F, _F, _P, _P]),
+        "adam_step_multi": (_I32, [_I32, ctypes.POINTER(AdamSegment), _P, _P, _P, _P, _F, _F, _F, _F,
+                                   _F, _P, _P]),
         "swiglu_forward": (_I32, [_I64, _P, _P, _P, _P]),
         "swiglu_backward": (_I32, [_I64, _P, _P, _P, _P, _P, _P]),
         "lora_timing_enable": (None, [_I32]),
@@ -227,6 +234,23 @@ def adam_step(p, g, m, v, step, lr, beta1=0.9, beta2=0.999, eps=1e-8, weight_dec
               p_bf16=None, stream=None):
     _check(LIB.adam_step(p.numel(), _ptr(p), _ptr(g), _ptr(m), _ptr(v), int(step), lr, beta1,
                          beta2, eps, weight_decay, _ptr(p_bf16), _stream(stream)))
+
+
+def adam_step_multi(segments, p, g, m, v, lr, beta1=0.9, beta2=0.999, eps=1e-8,
+                    weight_decay=0.0, p_bf16=None, stream=None):
+    """segments: list of (offset, count, step) into the flat p/g/m/v buffers."""
+    n = p.numel()
+    for t in (g, m, v):
+        if t.numel() != n:
+            raise LoraError(LORA_E_INVALID_ARG, "p, g, m, v must have the same length")
+    if p_bf16 is not None and p_bf16.numel() != n:
+        raise LoraError(LORA_E_INVALID_ARG, "p_bf16 must have the length of p")
+    for o, c, _ in segments:
+        if o < 0 or c < 0 or o + c > n:
+            raise LoraError(LORA_E_INVALID_ARG, f"segment ({o}, {c}) outside a buffer of {n}")
+    arr = (AdamSegment * max(1, len(segments)))(*[AdamSegment(int(o), int(c), int(t)) for o, c, t in segments])
+    _check(LIB.adam_step_multi(len(segments), arr, _ptr(p), _ptr(g), _ptr(m), _ptr(v), lr, beta1,
+                               beta2, eps, weight_decay, _ptr(p_bf16), _stream(stream)))
 
 
 def swiglu_forward(gate, up, h, stream=None):

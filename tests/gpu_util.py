@@ -58,7 +58,7 @@ class DevLayer:
         self.case = case
         if order is None:
             order = L.IDS_SORTED if case.order == "sorted" else L.IDS_INTERLEAVED
-        self.max_rank = max_rank or max(8, int(np.ceil(case.max_rank / 8) * 8))
+        self.max_rank = max_rank or max(16, int(np.ceil(case.max_rank / 16) * 16))
         self.shape = L.make_shape(case.n_tokens, case.d_in, case.d_out, case.pack_elems,
                                   case.pack_elems, case.n_adapters, self.max_rank, order)
         self.scales32 = case.scales.astype(np.float32)
@@ -75,7 +75,8 @@ class DevLayer:
     def forward(self, x=None, pack=None, ids=None):
         N, d_out = self.case.n_tokens, self.case.d_out
         y = torch.empty((N, d_out), dtype=torch.bfloat16, device="cuda")
-        u = torch.full((N, self.max_rank), float("nan"), dtype=torch.float32, device="cuda")
+        # saved vector: bf16 hi/lo planes of s_a u_t, poisoned with NaN first
+        u = torch.full((2, N, self.max_rank), float("nan"), dtype=torch.bfloat16, device="cuda")
         p = self.pack if pack is None else pack
         self.L.lora_forward(self.shape, self.x if x is None else x, self.W, p, p, self.desc,
                             self.ids if ids is None else ids, y, u, self.ws)
@@ -91,6 +92,17 @@ class DevLayer:
                              self.Wt, p, p, self.desc, self.ids if ids is None else ids, u, dx,
                              grad, grad, accumulate, self.ws)
         return dx, grad
+
+    def u_values(self, u, ids=None) -> np.ndarray:
+        """u_t = A_a x_t (float64, [N][max_rank]) from the saved hi/lo planes of
+        s_a u_t; tokens without a valid adapter keep the stored value (zero)."""
+        planes = f64_of(u)
+        su = planes[0] + planes[1]
+        ids = self.case.ids if ids is None else np.asarray(ids)
+        ok = (ids >= 0) & (ids < self.case.n_adapters)
+        s = np.ones(len(ids))
+        s[ok] = self.scales32[ids[ok]].astype(np.float64)
+        return su / s[:, None]
 
     def status(self) -> int:
         return self.L.lora_device_status(self.ws)

@@ -46,16 +46,17 @@ def test_library_exports_every_declared_symbol(L):
 
 def test_host_validation_returns_before_any_launch(L):
     lib = L.LIB
-    sh = L.make_shape(512, 256, 256, 4096, 4096, 4, 8)
+    sh = L.make_shape(512, 256, 256, 4096, 4096, 4, 16)
     assert L.lora_workspace_bytes(sh) > 0
     P = ctypes.c_void_p(16)     # never dereferenced: validation fails first
     st = lib.lora_forward(ctypes.byref(sh), P, None, P, P, P, P, P, P, P, 1 << 30, None)
     assert st == L.LORA_E_INVALID_ARG and b"non-NULL" in lib.lora_last_error()
-    bad = L.make_shape(512, 100, 256, 4096, 4096, 4, 8)
+    bad = L.make_shape(512, 100, 256, 4096, 4096, 4, 16)
     st = lib.lora_forward(ctypes.byref(bad), P, P, P, P, P, P, P, P, P, 1 << 30, None)
     assert st == L.LORA_E_UNSUPPORTED
-    bad = L.make_shape(512, 256, 256, 4096, 4096, 4, 12)
-    assert lib.lora_workspace_bytes(ctypes.byref(bad)) == 0
+    for r_bad in (8, 12, 24, 80):       # max_rank must be a multiple of 16 in [16, 64]
+        bad = L.make_shape(512, 256, 256, 4096, 4096, 4, r_bad)
+        assert lib.lora_workspace_bytes(ctypes.byref(bad)) == 0
     st = lib.lora_forward(ctypes.byref(sh), P, P, P, P, P, P, P, P, P, 64, None)
     assert st == L.LORA_E_WORKSPACE
     st = lib.lora_backward(ctypes.byref(sh), P, P, P, P, P, P, P, P, P, P, P, 0, P, 64, None)
@@ -71,7 +72,7 @@ def test_host_validation_returns_before_any_launch(L):
 
 
 def test_workspace_sizes_monotone(L):
-    small = L.lora_workspace_bytes(L.make_shape(512, 256, 256, 4096, 4096, 4, 8))
+    small = L.lora_workspace_bytes(L.make_shape(512, 256, 256, 4096, 4096, 4, 16))
     big = L.lora_workspace_bytes(L.make_shape(8192, 4096, 4096, 16 * 32 * 8192, 16 * 32 * 8192, 16, 32))
     assert 0 < small < big
     assert L.lora_segments_workspace_bytes(0, 4) > 0 and L.lora_segments_workspace_bytes(-1, 4) == 0

@@ -165,6 +165,52 @@ def test_adam_parity_and_resume(n):
     assert torch.equal(p2, p) and torch.equal(m2, m) and torch.equal(v2, v)
 
 
+def test_adam_multi_matches_per_segment():
+    """One batched launch over many adapters == one adam_step per adapter,
+    bitwise; elements outside every segment stay untouched.  70 segments
+    (more than one launch's worth), unaligned offsets, an empty segment and
+    per-segment step counters."""
+    rng = np.random.default_rng(70)
+    counts = [int(c) for c in rng.integers(0, 9000, 70)]
+    counts[5] = 0
+    counts[6] = 3
+    segs, off = [], 5                              # offset 5: float4 path off for some segments
+    for i, c in enumerate(counts):
+        segs.append((off, c, 1 + (i * 7) % 13))
+        off += c + int(rng.integers(0, 3))         # gaps between segments
+    n = off + 11
+    p0 = rng.uniform(-0.02, 0.02, n).astype(np.float32)
+    g0 = (rng.standard_normal(n) * 1e-2).astype(np.float32)
+    m0 = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+    v0 = (rng.uniform(0, 1e-5, n)).astype(np.float32)
+    args = (1e-4, 0.9, 0.999, 1e-8, 0.01)
+    p, m, v, g = dev_f32(p0), dev_f32(m0), dev_f32(v0), dev_f32(g0)
+    pb = torch.zeros(n, dtype=torch.bfloat16, device="cuda")
+    L.adam_step_multi(segs, p, g, m, v, *args, p_bf16=pb)
+    p2, m2, v2 = dev_f32(p0), dev_f32(m0), dev_f32(v0)
+    pb2 = torch.zeros(n, dtype=torch.bfloat16, device="cuda")
+    for o, c, t in segs:
+        L.adam_step(p2[o:o + c], g[o:o + c], m2[o:o + c], v2[o:o + c], t, *args, pb2[o:o + c])
+    torch.cuda.synchronize()
+    assert torch.equal(p, p2) and torch.equal(m, m2) and torch.equal(v, v2)
+    assert np.array_equal(bits_of(pb), bits_of(pb2))
+    inside = np.zeros(n, bool)
+    for o, c, _ in segs:
+        inside[o:o + c] = True
+    assert np.array_equal(p.cpu().numpy()[~inside], p0[~inside])
+    assert np.all(bits_of(pb)[~inside] == 0)
+    # one segment against the oracle directly
+    o, c, t = segs[9]
+    po, mo, vo = OA.adam_step(p0[o:o + c].astype(np.float64), g0[o:o + c], m0[o:o + c], v0[o:o + c],
+                              t, *args)
+    assert rel_err(m.cpu().numpy()[o:o + c], mo) < TOL_F32
+    assert rel_err(v.cpu().numpy()[o:o + c], vo) < TOL_F32
+    dp, dp_ref = p.cpu().numpy()[o:o + c] - p0[o:o + c], po - p0[o:o + c]
+    scale = np.maximum(np.abs(dp_ref), np.sqrt(np.mean(dp_ref ** 2)))
+    ulp = np.spacing(np.abs(po).astype(np.float32)).astype(np.float64)
+    assert np.all(np.abs(dp - dp_ref) <= TOL_F32 * scale + ulp)
+
+
 def test_swiglu_parity():
     rng = np.random.default_rng(7)
     n = 3 * 1000 + 5
