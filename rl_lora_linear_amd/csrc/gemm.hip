@@ -17,6 +17,8 @@
 // (8-byte stores; row reductions need one cross-lane step).  Tiles are ordered XCD-first (blocks are dispatched
 // round-robin over the 8 XCDs, so each XCD gets a contiguous tile range and
 // its own L2 sees the reuse) and then in groups of `group_m` row tiles.
+#include <type_traits>
+
 #include "common.hpp"
 #include "sgmv.hpp"
 
@@ -79,19 +81,14 @@ __device__ __forceinline__ uint32_t lds_addr(const uint4* p) {
   return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
 }
 
-// One operand tile of one stage: 16 row blocks of 16 rows (64 slots each);
-// wave w issues blocks 4w..4w+3.  Lane L lands in slot L of its block: row
-// L/4, physical chunk L%4, so it fetches logical chunk (L%4) ^ g4(L/4).
-// rowp[i] is this lane's source row (block 4w+i) at k = 0, chunk included.
-__device__ __forceinline__ void dma_rows(const uint16_t* const (&rowp)[4], int k0, uint4* tile,
-                                         int wave) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint16_t* g = rowp[i] + k0;
-    const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr(tile + (wave * 4 + i) * 64));
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0v), "v"(g)
-                 : "memory");
-  }
+// One 16-byte LDS-DMA per lane: global (base + voff) -> LDS (m0v + 16 * lane).
+// base is wave-uniform (SGPR pair), voff a per-lane 32-bit byte offset.
+// Operand tiles: 16 row blocks of 16 rows (64 slots each); wave w issues
+// blocks 4w..4w+3.  Lane L lands in slot L of its block: row L/4, physical
+// chunk L%4, so it fetches logical chunk (L%4) ^ g4(L/4).
+__device__ __forceinline__ void dma16s(uint32_t voff, const void* base, uint32_t m0v) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0v), "v"(voff), "s"(base)
+               : "memory");
 }
 
 // Fused LoRA expand: for every adapter a owning rows of this tile (rows are
@@ -196,30 +193,46 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_kernel(const uint16_t* __restr
   uint4* sA = g_stage;
   uint4* sB = g_stage + NSTAGE * S_TILE;
 
-  // this lane's DMA source rows (rows past the edge clamped to the last row:
-  // they only feed outputs that are never stored)
-  const uint16_t* rowA[4];
-  const uint16_t* rowB[4];
+  // This lane's DMA sources as 32-bit byte offsets from a wave-uniform base
+  // (the SGPR-addressed form of the DMA: stepping k costs one scalar add and
+  // no vector work).  A rows gathered through perm are offsets from A itself
+  // (the host checks they fit in 32 bits); other rows are offsets from the
+  // tile's first row.  Rows past the edge are clamped to the last row: they
+  // only feed outputs that are never stored.
+  uint32_t offA[4], offB[4];
+  const uint16_t* baseA = ep.perm ? A : A + (int64_t)m0 * lda;
+  const uint16_t* baseB = B + (int64_t)n0 * ldb;
   {
     const int lrow = lane >> 2;
     const int chunk = (lane & 3) ^ g4(lrow);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int blk = wave * 4 + i;
-      int ra = min(m0 + blk * 16 + lrow, M - 1);
-      if (ep.perm) ra = ep.perm[ra];
+      const int ra = min(m0 + blk * 16 + lrow, M - 1);
       const int rb = min(n0 + blk * 16 + lrow, N - 1);
-      rowA[i] = A + (int64_t)ra * lda + chunk * 8;
-      rowB[i] = B + (int64_t)rb * ldb + chunk * 8;
+      const int64_t oa = ep.perm ? (int64_t)ep.perm[ra] * lda : (int64_t)(ra - m0) * lda;
+      offA[i] = (uint32_t)((oa + chunk * 8) * 2);
+      offB[i] = (uint32_t)(((int64_t)(rb - n0) * ldb + chunk * 8) * 2);
     }
   }
+  const uint32_t ldsA = __builtin_amdgcn_readfirstlane(lds_addr(sA + wave * 4 * 64));
+  const uint32_t ldsB = __builtin_amdgcn_readfirstlane(lds_addr(sB + wave * 4 * 64));
+  // DMA of operand rows (block i of this wave) for k0 into stage st
+  auto dmaA = [&](int st, int i, const uint16_t* kb) {
+    dma16s(offA[i], kb, ldsA + (uint32_t)(st * S_TILE + i * 64) * 16u);
+  };
+  auto dmaB = [&](int st, int i, const uint16_t* kb) {
+    dma16s(offB[i], kb, ldsB + (uint32_t)(st * S_TILE + i * 64) * 16u);
+  };
 
   // prologue: stages 0..2 in flight, wait for 0 and 1
 #pragma unroll
   for (int s = 0; s < NSTAGE - 1; ++s) {
     const int k0 = min(s, KT - 1) * SBK;
-    dma_rows(rowA, k0, sA + s * S_TILE, wave);
-    dma_rows(rowB, k0, sB + s * S_TILE, wave);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dmaA(s, i, baseA + k0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dmaB(s, i, baseB + k0);
   }
   asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
 
@@ -242,49 +255,66 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_kernel(const uint16_t* __restr
     f0b[i] = as_bf16x8(sB[b_row[i] + c0]);
   }
 
-  for (int kt = 0; kt < KT; ++kt) {
-    const int s = kt & (NSTAGE - 1);
-    const uint4* At = sA + s * S_TILE;
-    const uint4* Bt = sB + s * S_TILE;
-    {  // DMA of step kt + 3 into the stage consumed at step kt - 1 (re-fetch past the end)
-      const int sn = (kt + NSTAGE - 1) & (NSTAGE - 1);
-      const int k0 = min(kt + NSTAGE - 1, KT - 1) * SBK;
-      dma_rows(rowA, k0, sA + sn * S_TILE, wave);
-      dma_rows(rowB, k0, sB + sn * S_TILE, wave);
-    }
-    // phase 0: read slice 1 of this stage; MFMAs of slice 0
+  // One k step on stage S (static, so every LDS address is base + immediate).
+  // Each phase is 8 groups of 2 MFMAs; the LDS fragment reads for the next
+  // phase go into the first four groups and this step's four A (phase 0) or
+  // B (phase 1) DMA instructions into the last four, so the vector-memory,
+  // LDS and scalar work issues in the shadow of the matrix pipe instead of in
+  // a burst before it.  sched_barrier keeps the groups in this order.
+  auto step = [&](auto S_, int kt) {
+    constexpr int S = decltype(S_)::value;
+    constexpr int SN = (S + NSTAGE - 1) & (NSTAGE - 1);   // stage refilled now (read at kt - 1)
+    constexpr int S1 = (S + 1) & (NSTAGE - 1);            // next stage
+    const uint4* At = sA + S * S_TILE;
+    const uint4* Bt = sB + S * S_TILE;
+    const uint4* An = sA + S1 * S_TILE;
+    const uint4* Bn = sB + S1 * S_TILE;
+    const int k0 = min(kt + NSTAGE - 1, KT - 1) * SBK;
+    const uint16_t* ka = baseA + k0;
+    const uint16_t* kb = baseB + k0;
+    // phase 0: MFMAs of slice 0; reads of slice 1; A DMAs
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f1a[i] = as_bf16x8(At[a_row[i] + c1]);
-      f1b[i] = as_bf16x8(Bt[b_row[i] + c1]);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(f0b[j], f0a[i], acc[i][j]);
-    __builtin_amdgcn_sched_barrier(0);
-    // phase 1: read slice 0 of the next stage (complete since the last
-    // barrier; on the last step the values are simply unused); MFMAs of
-    // slice 1.  Unconditional, so no branch forces a full LDS wait.
-    {
-      const uint4* An = sA + ((s + 1) & (NSTAGE - 1)) * S_TILE;
-      const uint4* Bn = sB + ((s + 1) & (NSTAGE - 1)) * S_TILE;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        f0a[i] = as_bf16x8(An[a_row[i] + c0]);
-        f0b[i] = as_bf16x8(Bn[b_row[i] + c0]);
+    for (int g = 0; g < 8; ++g) {
+      const int i = g >> 1, j0 = (g & 1) * 2;
+      acc[i][j0] = mfma32(f0b[j0], f0a[i], acc[i][j0]);
+      acc[i][j0 + 1] = mfma32(f0b[j0 + 1], f0a[i], acc[i][j0 + 1]);
+      if (g < 4) {
+        f1a[g] = as_bf16x8(At[a_row[g] + c1]);
+        f1b[g] = as_bf16x8(Bt[b_row[g] + c1]);
+      } else {
+        dmaA(SN, g - 4, ka);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_barrier(0);
+    // phase 1: MFMAs of slice 1; reads of slice 0 of the next stage (landed
+    // at the last barrier; on the last step simply unused); B DMAs
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(f1b[j], f1a[i], acc[i][j]);
-    __builtin_amdgcn_sched_barrier(0);
+    for (int g = 0; g < 8; ++g) {
+      const int i = g >> 1, j0 = (g & 1) * 2;
+      acc[i][j0] = mfma32(f1b[j0], f1a[i], acc[i][j0]);
+      acc[i][j0 + 1] = mfma32(f1b[j0 + 1], f1a[i], acc[i][j0 + 1]);
+      if (g < 4) {
+        f0a[g] = as_bf16x8(An[a_row[g] + c0]);
+        f0b[g] = as_bf16x8(Bn[b_row[g] + c0]);
+      } else {
+        dmaB(SN, g - 4, kb);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
     // stage kt + 2 has landed for this wave; after the barrier, for all waves
     asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+  };
+
+  int kt = 0;
+  for (; kt + NSTAGE <= KT; kt += NSTAGE) {
+    step(std::integral_constant<int, 0>{}, kt);
+    step(std::integral_constant<int, 1>{}, kt + 1);
+    step(std::integral_constant<int, 2>{}, kt + 2);
+    step(std::integral_constant<int, 3>{}, kt + 3);
   }
+  if (kt < KT) step(std::integral_constant<int, 0>{}, kt++);
+  if (kt < KT) step(std::integral_constant<int, 1>{}, kt++);
+  if (kt < KT) step(std::integral_constant<int, 2>{}, kt++);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no DMA may outlive the block
 
   // ---- epilogues
@@ -416,6 +446,11 @@ static lora_status launch_gemm(const uint16_t* A, const uint16_t* B, int M, int 
                                int64_t lda, int64_t ldb, const GemmEpi& ep, hipStream_t s,
                                int group_m) {
   if (M <= 0 || N <= 0) return LORA_OK;
+  if (ep.perm && (int64_t)M * lda * 2 >= ((int64_t)1 << 32)) {
+    set_error("gemm: gathered operand of %lld bytes exceeds the 4 GiB the row offsets address",
+              (long long)((int64_t)M * lda * 2));
+    return LORA_E_UNSUPPORTED;
+  }
   const int tiles_m = (int)cdiv(M, GBM), tiles_n = (int)cdiv(N, GBN);
   if (group_m <= 0) group_m = pick_group_m(tiles_m);
   if (group_m > tiles_m) group_m = tiles_m;
