@@ -24,7 +24,7 @@ ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 CFLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",
+    f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++20", "-Wall", "-Wno-unused-function",
     "-Wno-unused-variable", "-Wno-unused-but-set-variable",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     f"-I{INCLUDE}", f"-I{CSRC}",

@@ -84,6 +84,7 @@ struct LayerWs {
   char* seg;          // status word + segment scratch
   size_t seg_bytes;
   int32_t* perm;
+  int32_t* adpos;     // adapter of each segment position (-1: none)
   int32_t* offsets;
   uint8_t* active;
   int32_t* pre32;
@@ -102,6 +103,7 @@ LayerWs carve_layer(const lora_shape& sh, void* ws, size_t bytes) {
   w.seg_bytes = segments_ws_bytes(sh.n_tokens, sh.n_adapters);
   w.seg = cv.take<char>(w.seg_bytes);
   w.perm = cv.take<int32_t>((size_t)std::max<int64_t>(sh.n_tokens, 1));
+  w.adpos = cv.take<int32_t>((size_t)std::max<int64_t>(sh.n_tokens, 1));
   w.offsets = cv.take<int32_t>((size_t)sh.n_adapters + 1);
   w.active = cv.take<uint8_t>((size_t)sh.n_adapters);
   w.pre32 = cv.take<int32_t>((size_t)sh.n_adapters + 1);
@@ -155,6 +157,7 @@ lora_status layer_segments(const lora_shape& sh, const lora_adapter_desc* desc,
   ex.pre[1] = nullptr;
   ex.tm[2] = kGradChunk;
   ex.pre[2] = w.prec;
+  ex.adpos = w.adpos;
   return run_segments(ids, sh.n_tokens, sh.n_adapters, sh.order, w.perm, w.offsets, &ex, w.seg,
                       w.seg_bytes, s);
 }
@@ -247,12 +250,12 @@ lora_status lora_forward(const lora_shape* shape, const uint16_t* x, const uint1
   TRY(layer_segments(sh, desc, adapter_ids, w, s));
   if (N == 0) return LORA_OK;
   timer_begin(LORA_TIMER_SHRINK, s);
-  TRY(launch_shrink(x, sh.d_in, (int)sh.d_in, A_pack, 0, desc, w.active, w.perm, w.offsets,
+  TRY(launch_shrink(x, sh.d_in, (int)sh.d_in, A_pack, 0, desc, w.adpos, w.perm, w.offsets,
                     w.pre32, sh.n_adapters, sh.n_tokens, u_saved, sh.max_rank, w.zero, s));
   timer_end(LORA_TIMER_SHRINK, s);
   // base GEMM over rows in segment order with the expand y += B_a (s u) fused
-  LoraFuse f{w.perm, u_saved, sh.n_tokens * sh.max_rank, sh.max_rank, 1, B_pack, desc, w.active,
-             w.offsets, sh.n_adapters};
+  LoraFuse f{w.perm, u_saved, sh.n_tokens * sh.max_rank, sh.max_rank, 1, B_pack, desc, w.adpos,
+             sh.n_adapters};
   timer_begin(LORA_TIMER_BASE_GEMM, s);
   TRY(gemm_nt_lora(x, W, y, N, (int)sh.d_out, (int)sh.d_in, sh.d_in, sh.d_in, sh.d_out, f, s));
   timer_end(LORA_TIMER_BASE_GEMM, s);
@@ -287,12 +290,12 @@ lora_status lora_backward(const lora_shape* shape, const uint16_t* dy, const uin
                                w.AT, w.BT, s));
   if (N > 0) {
     timer_begin(LORA_TIMER_SHRINK, s);
-    TRY(launch_shrink(dy, sh.d_out, (int)sh.d_out, w.BT, 1, desc, w.active, w.perm, w.offsets,
+    TRY(launch_shrink(dy, sh.d_out, (int)sh.d_out, w.BT, 1, desc, w.adpos, w.perm, w.offsets,
                       w.pre32, sh.n_adapters, sh.n_tokens, w.v, sh.max_rank, w.zero, s));
     timer_end(LORA_TIMER_SHRINK, s);
     // dX = dY W over rows in segment order with the expand dX += A_a^T (s v) fused
-    LoraFuse f{w.perm, w.v, sh.n_tokens * sh.max_rank, sh.max_rank, 0, w.AT, desc, w.active,
-               w.offsets, sh.n_adapters};
+    LoraFuse f{w.perm, w.v, sh.n_tokens * sh.max_rank, sh.max_rank, 0, w.AT, desc, w.adpos,
+               sh.n_adapters};
     timer_begin(LORA_TIMER_BASE_GEMM, s);
     TRY(gemm_nt_lora(dy, W_t, dx, N, (int)sh.d_in, (int)sh.d_out, sh.d_out, sh.d_out, sh.d_in, f, s));
     timer_end(LORA_TIMER_BASE_GEMM, s);

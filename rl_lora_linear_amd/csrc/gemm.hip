@@ -18,6 +18,7 @@
 // round-robin over the 8 XCDs, so each XCD gets a contiguous tile range and
 // its own L2 sees the reuse) and then in groups of `group_m` row tiles.
 #include <type_traits>
+#include <utility>
 
 #include "common.hpp"
 #include "sgmv.hpp"
@@ -41,7 +42,7 @@ struct GemmEpi {
   const uint16_t* lmat;
   const lora_adapter_desc* desc;
   const uint8_t* active;
-  const int32_t* offsets; // [n_ad + 1] segment offsets (positions)
+  const int32_t* adpos;   // [M] adapter of each row position, -1 for rows without one
   int n_ad;
   float* part_m;          // EPI_LSE: [tiles_n][M]
   float* part_s;          // EPI_LSE: [tiles_n][M]
@@ -68,6 +69,9 @@ constexpr int SBK = 32;                    // k per stage
 constexpr int S_CH = SBK / 8;              // 16-byte chunks per LDS row (4)
 constexpr int S_TILE = 256 * S_CH;         // uint4 per operand tile per stage
 constexpr int NSTAGE = 4;
+// DMA instructions a wave may leave in flight at the end of a k step: the
+// stages after k + 2 (8 per stage)
+constexpr int VM_AHEAD = (NSTAGE - 3) * 8;
 
 // Swizzle of a 4-chunk LDS row: chunk c of row r is stored at c ^ g4(r).
 // The 16-byte reads of 16 consecutive rows at one logical chunk then hit 16
@@ -75,7 +79,7 @@ constexpr int NSTAGE = 4;
 // and 8 consecutive rows hit 8 distinct (row mod 2, chunk) slots.
 __device__ __forceinline__ int g4(int r) { return ((r >> 1) & 3) ^ ((r >> 3) & 1); }
 
-__shared__ uint4 g_stage[2 * NSTAGE * S_TILE];  // [A s0..s3][B s0..s3], 128 KB
+__shared__ uint4 g_stage[2 * NSTAGE * S_TILE];  // [A stages][B stages], 32 KB per stage
 
 __device__ __forceinline__ uint32_t lds_addr(const uint4* p) {
   return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
@@ -91,63 +95,67 @@ __device__ __forceinline__ void dma16s(uint32_t voff, const void* base, uint32_t
                : "memory");
 }
 
-// Fused LoRA expand: for every adapter a owning rows of this tile (rows are
-// segment positions, so a 256-row tile spans one adapter or a few), add
-// s_a * vec[tok] . M_a^T to the accumulators as an extra MFMA K-slab of depth
-// r_a.  The fp32 vector is scaled by s_a and split into hi + lo bf16 parts
-// (two MFMAs) so the slab keeps ~16 significant bits; M_a is bf16-exact.
-// Rows of other adapters contribute zero fragments.
-__device__ __forceinline__ void lora_slab(const GemmEpi& ep, int m0, int n0, int M, int N, int wm,
-                                       int wn, int lane, f32x16 (&acc)[4][4]) {
+// Fused LoRA expand: for every adapter a owning rows of this wave's 128 rows
+// (rows are segment positions, so they span one adapter or a few), add
+// (s_a u_tok) . M_a^T to the accumulators as an extra MFMA K-slab of depth r_a.
+// The scaled vector is stored as bf16 hi and lo planes, one MFMA each, so the
+// slab keeps ~16 significant bits; M_a is bf16-exact.  tok[i] / ad[i] are the
+// token and adapter (-1: none) of this lane's fragment rows, loaded before
+// the k loop.  Fragments of two rank slices are loaded before their MFMAs.
+__device__ __forceinline__ void lora_slab(const GemmEpi& ep, int n0, int N, int wn, int lane,
+                                          const int (&tok)[4], const int (&ad)[4],
+                                          f32x16 (&acc)[4][4]) {
   const int m_l = lane & 31;
   const int half = lane >> 5;
-  const int n_end = ep.offsets[ep.n_ad];  // positions past it are tokens with invalid ids
-  const int last = min(m0 + GBM, min(M, n_end)) - 1;
-  if (last < m0) return;
-  const int a0 = find_bucket(ep.offsets, ep.n_ad + 1, m0);
-  const int a1 = find_bucket(ep.offsets, ep.n_ad + 1, last);
-  int ad[4], tk[4];
+  int lo = INT32_MAX, hi = -1;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = m0 + wm * 128 + i * 32 + m_l;
-    const bool ok = row < M && row < n_end;
-    ad[i] = ok ? find_bucket(ep.offsets, ep.n_ad + 1, row) : -1;
-    tk[i] = ok ? (ep.perm ? ep.perm[row] : row) : 0;
+  for (int i = 0; i < 4; ++i)
+    if (ad[i] >= 0) lo = min(lo, ad[i]), hi = max(hi, ad[i]);
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    lo = min(lo, __shfl_xor(lo, o));
+    hi = max(hi, __shfl_xor(hi, o));
   }
+  const int a0 = __builtin_amdgcn_readfirstlane(lo), a1 = __builtin_amdgcn_readfirstlane(hi);
   for (int a = a0; a <= a1; ++a) {
-    if (!ep.active[a] || ep.offsets[a + 1] == ep.offsets[a]) continue;
+    bool mine = false;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mine |= ad[i] == a;
+    if (!__any(mine)) continue;                     // adapter absent from this wave's rows
     const lora_adapter_desc d = ep.desc[a];
     const int r = d.rank;
     const uint16_t* mat = ep.lmat + (ep.use_b_off ? d.b_off : d.a_off);
-    for (int sl = 0; sl * 16 < r; ++sl) {
-      const int c = sl * 16 + 8 * half;
-      const bool cok = c < r;
-      bf16x8 ah[4], al[4], bm[4];
+    for (int sl = 0; sl * 16 < r; sl += 2) {
+      uint4 h[2][4], l[2][4], v[2][4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        uint4 h = make_uint4(0, 0, 0, 0), l = make_uint4(0, 0, 0, 0);
-        if (ad[i] == a && cok) {
-          const uint16_t* vp = ep.vec + (int64_t)tk[i] * ep.vec_ld + c;
-          h = *(const uint4*)vp;
-          l = *(const uint4*)(vp + ep.vec_plane);
+      for (int p = 0; p < 2; ++p) {
+        const int c = (sl + p) * 16 + 8 * half;
+        const bool cok = c < r;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          h[p][i] = l[p][i] = make_uint4(0, 0, 0, 0);
+          if (ad[i] == a && cok) {
+            const uint16_t* vp = ep.vec + (int64_t)tok[i] * ep.vec_ld + c;
+            h[p][i] = *(const uint4*)vp;
+            l[p][i] = *(const uint4*)(vp + ep.vec_plane);
+          }
         }
-        ah[i] = as_bf16x8(h);
-        al[i] = as_bf16x8(l);
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int n = n0 + wn * 128 + j * 32 + m_l;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (n < N && cok) v = *(const uint4*)(mat + (int64_t)n * r + c);
-        bm[j] = as_bf16x8(v);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          acc[i][j] = mfma32(bm[j], ah[i], acc[i][j]);
-          acc[i][j] = mfma32(bm[j], al[i], acc[i][j]);
+          const int n = n0 + wn * 128 + j * 32 + m_l;
+          v[p][j] = make_uint4(0, 0, 0, 0);
+          if (n < N && cok) v[p][j] = *(const uint4*)(mat + (int64_t)n * r + c);
         }
+      }
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            acc[i][j] = mfma32(as_bf16x8(v[p][j]), as_bf16x8(h[p][i]), acc[i][j]);
+            acc[i][j] = mfma32(as_bf16x8(v[p][j]), as_bf16x8(l[p][i]), acc[i][j]);
+          }
     }
   }
 }
@@ -189,6 +197,17 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_kernel(const uint16_t* __restr
 #pragma unroll
       for (int g = 0; g < 16; ++g) acc[i][j][g] = 0.f;
 
+  // epilogue row metadata, loaded now so its latency hides under the k loop
+  const int m_l = lane & 31;
+  const int n_q = 4 * (lane >> 5);
+  int tok[4], ad[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = m0 + wm * 128 + i * 32 + m_l;
+    tok[i] = row < M ? (ep.perm ? ep.perm[row] : row) : -1;
+    ad[i] = (EPI == EPI_BF16 && ep.vec && row < M) ? ep.adpos[row] : -1;
+  }
+
   const int KT = K / SBK;
   uint4* sA = g_stage;
   uint4* sB = g_stage + NSTAGE * S_TILE;
@@ -225,7 +244,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_kernel(const uint16_t* __restr
     dma16s(offB[i], kb, ldsB + (uint32_t)(st * S_TILE + i * 64) * 16u);
   };
 
-  // prologue: stages 0..2 in flight, wait for 0 and 1
+  // prologue: stages 0..NSTAGE-2 in flight, wait for 0 and 1
 #pragma unroll
   for (int s = 0; s < NSTAGE - 1; ++s) {
     const int k0 = min(s, KT - 1) * SBK;
@@ -234,7 +253,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_kernel(const uint16_t* __restr
 #pragma unroll
     for (int i = 0; i < 4; ++i) dmaB(s, i, baseB + k0);
   }
-  asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(VM_AHEAD) : "memory");
 
   const int frag_row = lane & 31;   // row within a 32-row MFMA tile
   const int frag_half = lane >> 5;  // which 8-wide k half of a 16-wide k slice
@@ -263,8 +282,8 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_kernel(const uint16_t* __restr
   // a burst before it.  sched_barrier keeps the groups in this order.
   auto step = [&](auto S_, int kt) {
     constexpr int S = decltype(S_)::value;
-    constexpr int SN = (S + NSTAGE - 1) & (NSTAGE - 1);   // stage refilled now (read at kt - 1)
-    constexpr int S1 = (S + 1) & (NSTAGE - 1);            // next stage
+    constexpr int SN = (S + NSTAGE - 1) % NSTAGE;   // stage refilled now (read at kt - 1)
+    constexpr int S1 = (S + 1) % NSTAGE;            // next stage
     const uint4* At = sA + S * S_TILE;
     const uint4* Bt = sB + S * S_TILE;
     const uint4* An = sA + S1 * S_TILE;
@@ -302,33 +321,24 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_kernel(const uint16_t* __restr
       __builtin_amdgcn_sched_barrier(0);
     }
     // stage kt + 2 has landed for this wave; after the barrier, for all waves
-    asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(VM_AHEAD) : "memory");
   };
 
+  // steps in rounds of NSTAGE (stage index static), then the remaining steps
   int kt = 0;
-  for (; kt + NSTAGE <= KT; kt += NSTAGE) {
-    step(std::integral_constant<int, 0>{}, kt);
-    step(std::integral_constant<int, 1>{}, kt + 1);
-    step(std::integral_constant<int, 2>{}, kt + 2);
-    step(std::integral_constant<int, 3>{}, kt + 3);
-  }
-  if (kt < KT) step(std::integral_constant<int, 0>{}, kt++);
-  if (kt < KT) step(std::integral_constant<int, 1>{}, kt++);
-  if (kt < KT) step(std::integral_constant<int, 2>{}, kt++);
+  for (; kt + NSTAGE <= KT; kt += NSTAGE)
+    [&]<int... S>(std::integer_sequence<int, S...>) {
+      (step(std::integral_constant<int, S>{}, kt + S), ...);
+    }(std::make_integer_sequence<int, NSTAGE>{});
+  [&]<int... S>(std::integer_sequence<int, S...>) {
+    ((kt < KT ? (step(std::integral_constant<int, S>{}, kt), ++kt) : 0), ...);
+  }(std::make_integer_sequence<int, NSTAGE - 1>{});
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no DMA may outlive the block
 
   // ---- epilogues
-  const int m_l = lane & 31;
-  const int n_q = 4 * (lane >> 5);
 
   if constexpr (EPI == EPI_BF16) {
-    int tok[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = m0 + wm * 128 + i * 32 + m_l;
-      tok[i] = row < M ? (ep.perm ? ep.perm[row] : row) : -1;
-    }
-    if (ep.vec) lora_slab(ep, m0, n0, M, N, wm, wn, lane, acc);
+    if (ep.vec) lora_slab(ep, n0, N, wn, lane, tok, ad, acc);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (tok[i] < 0) continue;
@@ -345,7 +355,10 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_kernel(const uint16_t* __restr
         }
     }
   } else if constexpr (EPI == EPI_LSE) {
-    __shared__ float2 red_s[2][GBM];
+    // (max, sum) pairs of the two column halves, in the now idle operand ring;
+    // the barrier keeps the last fragment reads of other waves ahead of it
+    float2 (*red_s)[GBM] = (float2 (*)[GBM])g_stage;
+    __syncthreads();
     const int cbase = n0 + wn * 128;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -487,8 +500,7 @@ lora_status gemm_nt_lora(const uint16_t* A, const uint16_t* B, uint16_t* C, int 
   ep.use_b_off = f.use_b_off;
   ep.lmat = f.lmat;
   ep.desc = f.desc;
-  ep.active = f.active;
-  ep.offsets = f.offsets;
+  ep.adpos = f.adpos;
   ep.n_ad = f.n_ad;
   return launch_gemm<EPI_BF16>(A, B, M, N, K, lda, ldb, ep, s, group_m);
 }

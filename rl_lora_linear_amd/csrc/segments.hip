@@ -139,7 +139,8 @@ __global__ __launch_bounds__(1024) void seg_offsets_kernel(const int32_t* __rest
 
 __global__ __launch_bounds__(SEG_CHUNK) void seg_scatter_kernel(
     const int32_t* __restrict__ ids, int64_t n, int n_keys, const int32_t* __restrict__ hist,
-    int n_chunks, const int32_t* __restrict__ offsets, int32_t* __restrict__ perm) {
+    int n_chunks, const int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
+    const uint8_t* __restrict__ active, int32_t* __restrict__ adpos) {
   __shared__ int32_t k_s[SEG_CHUNK];
   const int c = blockIdx.x;
   const int64_t t = (int64_t)c * SEG_CHUNK + threadIdx.x;
@@ -156,6 +157,7 @@ __global__ __launch_bounds__(SEG_CHUNK) void seg_scatter_kernel(
   const int32_t base = (key < n_keys ? offsets[key] : offsets[n_keys]) +
                        hist[(int64_t)key * n_chunks + c];
   perm[base + rank] = (int32_t)t;
+  if (adpos) adpos[base + rank] = (key < n_keys && (!active || active[key])) ? key : -1;
 }
 
 }  // namespace lora
@@ -215,7 +217,8 @@ lora_status run_segments(const int32_t* ids, int64_t n, int32_t n_keys, int32_t 
   if (st) return st;
   if (n > 0) {
     hipLaunchKernelGGL(seg_scatter_kernel, dim3((unsigned)chunks), dim3(SEG_CHUNK), 0, s, ids, n,
-                       n_keys, hist, (int)chunks, offsets, perm);
+                       n_keys, hist, (int)chunks, offsets, perm,
+                       (ex && ex->desc) ? ex->active : nullptr, ex ? ex->adpos : nullptr);
     st = launch_check("seg_scatter");
   }
   return st;

@@ -18,6 +18,8 @@ struct SegExtras {
   uint8_t* active;     // out [n_keys]
   int32_t tm[3];       // rows per tile/chunk for up to three tilings
   int32_t* pre[3];     // out [n_keys + 1] each: exclusive prefix of ceil(count / tm)
+  int32_t* adpos;      // out [n] (nullable): key of each sorted position, -1 for
+                       // invalid ids and inactive keys
 };
 
 size_t segments_ws_bytes(int64_t n, int32_t n_keys);

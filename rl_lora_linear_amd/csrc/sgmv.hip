@@ -43,6 +43,21 @@ __device__ __forceinline__ bool tile_of(const int32_t* pre, const int32_t* offse
   return true;
 }
 
+// Work items [0, total) of a one-block-per-CU grid, handed out so that each
+// XCD walks a contiguous item range (the dispatcher places block b on XCD
+// b % 8; items of one XCD then read one contiguous stretch of memory, which
+// the memory system serves markedly faster than an interleaved one).
+// gridDim.x must be a multiple of 8.
+struct ItemRange {
+  int first, step, end;
+};
+__device__ __forceinline__ ItemRange xcd_items(int total) {
+  const int xcd = blockIdx.x & 7, loc = blockIdx.x >> 3;
+  const int base = total >> 3, rem = total & 7;
+  const int start = xcd * base + min(xcd, rem);
+  return ItemRange{start + loc, (int)(gridDim.x >> 3), start + base + (xcd < rem ? 1 : 0)};
+}
+
 // ------------------------------------------------------------------ shrink
 // out[t][c] = sum_k in[t][k] M_a[c][k] for the 32 rows of one adapter tile.
 // Rows (gathered through perm) and the factor rows M_a[0..r) stream through a
@@ -54,7 +69,11 @@ __device__ __forceinline__ bool tile_of(const int32_t* pre, const int32_t* offse
 // four partial products are summed in LDS in wave order at the end.
 constexpr int SH_TM = 32;
 constexpr int SH_KC = 128;
-constexpr int SH_NST = 5;
+// Ring depth (deeper rings measured no faster).
+template <int NB>
+constexpr int sh_nst() {
+  return 5;
+}
 constexpr int SH_XSLOTS = SH_TM * 16;          // uint4 slots of the row tile per stage
 
 __device__ __forceinline__ uint32_t lds_u32(const void* p) {
@@ -79,6 +98,7 @@ __device__ __forceinline__ void shrink_tile(const uint16_t* __restrict__ in, int
   constexpr int MSLOTS = NB * 16 * 16;                 // factor tile slots per stage
   constexpr int STAGE = SH_XSLOTS + MSLOTS;
   constexpr int PER_WAVE = 2 + NB;                     // DMA instructions per wave per stage
+  constexpr int NST = sh_nst<NB>();
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int KT = (K + SH_KC - 1) / SH_KC;
 
@@ -116,8 +136,8 @@ __device__ __forceinline__ void shrink_tile(const uint16_t* __restrict__ in, int
   };
 
 #pragma unroll
-  for (int st = 0; st < SH_NST - 1; ++st) issue(st, min(st, KT - 1));
-  wait_vm_barrier<(SH_NST - 2) * PER_WAVE>();
+  for (int st = 0; st < NST - 1; ++st) issue(st, min(st, KT - 1));
+  wait_vm_barrier<(NST - 2) * PER_WAVE>();
 
   f32x4 acc[2][NB];
 #pragma unroll
@@ -128,8 +148,8 @@ __device__ __forceinline__ void shrink_tile(const uint16_t* __restrict__ in, int
   const int ch = 4 * wave + (lane >> 4);  // logical chunk of this lane's fragments
 
   for (int kt = 0; kt < KT; ++kt) {
-    const int st = kt % SH_NST;
-    issue((kt + SH_NST - 1) % SH_NST, min(kt + SH_NST - 1, KT - 1));
+    const int st = kt % NST;
+    issue((kt + NST - 1) % NST, min(kt + NST - 1, KT - 1));
     const uint4* xt = lds + st * STAGE;
     const uint4* mt = xt + SH_XSLOTS;
     if (kt * SH_KC + wave * 32 < K) {
@@ -149,7 +169,7 @@ __device__ __forceinline__ void shrink_tile(const uint16_t* __restrict__ in, int
 #pragma unroll
         for (int b = 0; b < NB; ++b) acc[g][b] = mfma16(xa[g], mb[b], acc[g][b]);
     }
-    wait_vm_barrier<(SH_NST - 2) * PER_WAVE>();
+    wait_vm_barrier<(NST - 2) * PER_WAVE>();
   }
   asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
 
@@ -187,50 +207,46 @@ __device__ __forceinline__ void shrink_tile(const uint16_t* __restrict__ in, int
   }
 }
 
-// grid.x = tile bound; grid.y = 2: y == 0 computes 32-row adapter tiles,
-// y == 1 zeroes the rows of tokens that belong to no active adapter
-// (positions >= offsets[n_ad] or inside an inactive adapter's segment).
+// One block per CU.  Blocks take the 32-row adapter tiles (pre32[n_ad] of
+// them) XCD-contiguously, then zero, grid-stride, the rows of tokens that
+// belong to no active adapter (adpos == -1), and block 0 clears `zero`.
 __global__ __launch_bounds__(256) void shrink_kernel(
     const uint16_t* __restrict__ in, int64_t ld_in, int K, const uint16_t* __restrict__ mat_pack,
-    int use_b_off, const lora_adapter_desc* __restrict__ desc, const uint8_t* __restrict__ active,
+    int use_b_off, const lora_adapter_desc* __restrict__ desc, const int32_t* __restrict__ adpos,
     const int32_t* __restrict__ perm, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ pre32, int n_ad, int64_t n_tokens, uint16_t* __restrict__ out,
     int r_max, uint4* __restrict__ zero) {
   extern __shared__ uint4 sh_lds[];
   const int tid = threadIdx.x;
-  if (blockIdx.y == 1) {
-    if (blockIdx.x == 0 && zero != nullptr && tid < 16) zero[tid] = make_uint4(0, 0, 0, 0);
-    const int64_t p = (int64_t)blockIdx.x * 256 + tid;
-    if (p >= n_tokens) return;
-    bool dead = p >= offsets[n_ad];
-    if (!dead) dead = !active[find_bucket(offsets, n_ad + 1, (int32_t)p)];
-    if (dead) {
-      const int64_t plane = n_tokens * r_max;
-      uint4* o = (uint4*)(out + (int64_t)perm[p] * r_max);
-      uint4* ol = (uint4*)(out + plane + (int64_t)perm[p] * r_max);
-      for (int c = 0; c < r_max / 8; ++c) o[c] = ol[c] = make_uint4(0, 0, 0, 0);
-    }
-    return;
-  }
-  TileInfo ti;
-  if (!tile_of(pre32, offsets, n_ad, blockIdx.x, SH_TM, ti)) return;
-  const lora_adapter_desc d = desc[ti.a];
-  const int r = d.rank;
-  const uint16_t* mat = mat_pack + (use_b_off ? d.b_off : d.a_off);
-  const int nb = (r + 15) / 16;
   const int64_t plane = n_tokens * r_max;
-  const float sc = d.scale;
-  if (nb == 1) shrink_tile<1>(in, ld_in, K, mat, r, sc, perm, ti.p0, ti.rows, sh_lds, out, plane, r_max);
-  else if (nb == 2) shrink_tile<2>(in, ld_in, K, mat, r, sc, perm, ti.p0, ti.rows, sh_lds, out, plane, r_max);
-  else if (nb == 3) shrink_tile<3>(in, ld_in, K, mat, r, sc, perm, ti.p0, ti.rows, sh_lds, out, plane, r_max);
-  else shrink_tile<4>(in, ld_in, K, mat, r, sc, perm, ti.p0, ti.rows, sh_lds, out, plane, r_max);
+  const ItemRange ir = xcd_items(pre32[n_ad]);
+  for (int item = ir.first; item < ir.end; item += ir.step) {
+    TileInfo ti;
+    tile_of(pre32, offsets, n_ad, item, SH_TM, ti);
+    const lora_adapter_desc d = desc[ti.a];
+    const int r = d.rank;
+    const uint16_t* mat = mat_pack + (use_b_off ? d.b_off : d.a_off);
+    const int nb = (r + 15) / 16;
+    const float sc = d.scale;
+    __syncthreads();   // the previous item's LDS reads are done before the ring refills
+    if (nb == 1) shrink_tile<1>(in, ld_in, K, mat, r, sc, perm, ti.p0, ti.rows, sh_lds, out, plane, r_max);
+    else if (nb == 2) shrink_tile<2>(in, ld_in, K, mat, r, sc, perm, ti.p0, ti.rows, sh_lds, out, plane, r_max);
+    else if (nb == 3) shrink_tile<3>(in, ld_in, K, mat, r, sc, perm, ti.p0, ti.rows, sh_lds, out, plane, r_max);
+    else shrink_tile<4>(in, ld_in, K, mat, r, sc, perm, ti.p0, ti.rows, sh_lds, out, plane, r_max);
+  }
+  if (blockIdx.x == 0 && zero != nullptr && tid < 16) zero[tid] = make_uint4(0, 0, 0, 0);
+  for (int64_t p = (int64_t)blockIdx.x * 256 + tid; p < n_tokens; p += (int64_t)gridDim.x * 256) {
+    if (adpos[p] >= 0) continue;
+    uint4* o = (uint4*)(out + (int64_t)perm[p] * r_max);
+    uint4* ol = (uint4*)(out + plane + (int64_t)perm[p] * r_max);
+    for (int c = 0; c < r_max / 8; ++c) o[c] = ol[c] = make_uint4(0, 0, 0, 0);
+  }
 }
 
 // ------------------------------------------------------------------ grad
 constexpr int GR_TC = 1024;   // tokens per chunk (per-adapter split for balance)
 constexpr int GR_TT = 32;     // tokens per stage
 constexpr int GR_NJ = 256;    // output columns per block
-constexpr int GR_NST = 5;     // LDS ring depth (DMA four stages ahead)
 constexpr int GR_QSLOTS = GR_TT * 32;   // 32 token rows x 512 B of Q
 constexpr int GR_QDMA = 4;              // Q DMA instructions per wave per stage
 // The P tile of a stage holds both bf16 planes (hi, lo) of 32 tokens, each
@@ -240,6 +256,7 @@ template <int PN> struct GrP {
   static constexpr int SLOTS = 2 * GR_TT * PW;      // 256 * PN
   static constexpr int STAGE = GR_QSLOTS + SLOTS;
   static constexpr int PER_WAVE = GR_QDMA + PN;     // DMA instructions per wave per stage
+  static constexpr int NST = 5;                     // ring depth (deeper measured no faster)
   // pair (32-byte) swizzle: the 8 token rows that one transposing read of 32
   // lanes touches (t0..t0+3 and t0+8..t0+11) land on distinct banks
   static __device__ __forceinline__ int sw(int t) {
@@ -331,14 +348,14 @@ __device__ __forceinline__ void grad_tile(const uint16_t* __restrict__ P, int64_
   };
 
 #pragma unroll
-  for (int st = 0; st < GR_NST - 1; ++st) issue(st, min(st, KT - 1));
-  wait_vm_barrier<(GR_NST - 2) * G::PER_WAVE>();
+  for (int st = 0; st < G::NST - 1; ++st) issue(st, min(st, KT - 1));
+  wait_vm_barrier<(G::NST - 2) * G::PER_WAVE>();
 
   const int g16 = lane >> 4;   // 16-lane group: tokens 8*g16 .. 8*g16+7 of the stage
   const int li = lane & 15;
   for (int kt = 0; kt < KT; ++kt) {
-    const int st = kt % GR_NST;
-    issue((kt + GR_NST - 1) % GR_NST, min(kt + GR_NST - 1, KT - 1));
+    const int st = kt % G::NST;
+    issue((kt + G::NST - 1) % G::NST, min(kt + G::NST - 1, KT - 1));
     const uint4* qt = lds + st * G::STAGE;
     const uint4* ptile = qt + GR_QSLOTS;
     // Q fragments: 4 column sub-tiles of this wave's 64 columns
@@ -384,32 +401,27 @@ __device__ __forceinline__ void grad_tile(const uint16_t* __restrict__ P, int64_
           acc[jt][cb] = mfma16(qf[jt], pf[1][cb], acc[jt][cb]);
         }
       }
-    wait_vm_barrier<(GR_NST - 2) * G::PER_WAVE>();
+    wait_vm_barrier<(G::NST - 2) * G::PER_WAVE>();
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no DMA may outlive the block
 }
 
-// grid = (chunk-slot bound, ceil(D / 256)).
 template <int MODE, int PN>
-__global__ __launch_bounds__(256) void grad_kernel(
+__device__ __forceinline__ void grad_item(
     const uint16_t* __restrict__ P, int64_t plane, int r_max, const uint16_t* __restrict__ zero,
     const uint16_t* __restrict__ Q, int64_t ld_q, int D,
     const lora_adapter_desc* __restrict__ desc, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ chunk_pre, int n_ad,
-    float* __restrict__ out_pack, float* __restrict__ partial, int accumulate) {
-  extern __shared__ uint4 gr_lds[];
-  // the chunk's token ids, cached in LDS: the DMA loop may issue no
-  // compiler-tracked global loads (their waits would also wait for the DMA)
-  __shared__ int32_t tok_s[GR_TC];
-  const int slot = blockIdx.x;
+    float* __restrict__ out_pack, float* __restrict__ partial, int accumulate, int slot, int j0,
+    int32_t* tok_s, uint4* gr_lds) {
   TileInfo ti;
-  if (!tile_of(chunk_pre, offsets, n_ad, slot, GR_TC, ti)) return;
+  tile_of(chunk_pre, offsets, n_ad, slot, GR_TC, ti);
+  __syncthreads();   // every wave is done with the previous item's tokens and ring
   for (int i = threadIdx.x; i < ti.rows; i += 256) tok_s[i] = perm[ti.p0 + i];
   __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const lora_adapter_desc d = desc[ti.a];
   const int r = d.rank;
-  const int j0 = blockIdx.y * GR_NJ;
   const int nchunks = chunk_pre[ti.a + 1] - chunk_pre[ti.a];
 
   f32x4 acc[4][4];
@@ -463,6 +475,30 @@ __global__ __launch_bounds__(256) void grad_kernel(
         *p = v;
       }
     }
+}
+
+// One block per CU.  Items are (gradient chunk, 256-column block) pairs,
+// column block fastest (the column blocks of a chunk read the same token
+// rows), taken XCD-contiguously.
+template <int MODE, int PN>
+__global__ __launch_bounds__(256) void grad_kernel(
+    const uint16_t* __restrict__ P, int64_t plane, int r_max, const uint16_t* __restrict__ zero,
+    const uint16_t* __restrict__ Q, int64_t ld_q, int D,
+    const lora_adapter_desc* __restrict__ desc, const int32_t* __restrict__ perm,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ chunk_pre, int n_ad,
+    float* __restrict__ out_pack, float* __restrict__ partial, int accumulate) {
+  extern __shared__ uint4 gr_lds[];
+  // the chunk's token ids, cached in LDS: the DMA loop may issue no
+  // compiler-tracked global loads (their waits would also wait for the DMA)
+  __shared__ int32_t tok_s[GR_TC];
+  const int ncol = (D + GR_NJ - 1) / GR_NJ;
+  const ItemRange ir = xcd_items(chunk_pre[n_ad] * ncol);
+  for (int item = ir.first; item < ir.end; item += ir.step) {
+    const int slot = item / ncol;
+    const int j0 = (item - slot * ncol) * GR_NJ;
+    grad_item<MODE, PN>(P, plane, r_max, zero, Q, ld_q, D, desc, perm, offsets, chunk_pre, n_ad,
+                        out_pack, partial, accumulate, slot, j0, tok_s, gr_lds);
+  }
 }
 
 // grid = (n_ad, blocks over D*r_max/1024).  Sums the chunk partials of
@@ -539,24 +575,37 @@ __global__ __launch_bounds__(256) void adapter_transpose_kernel(
 namespace lora_host {
 using namespace lora;
 
+// Blocks of a one-block-per-CU grid: the device's CU count rounded down to a
+// multiple of 8 (one stretch per XCD).
+static unsigned persistent_blocks() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8)
+    cus = 256;
+  return (unsigned)(cus & ~7);
+}
+
 lora_status launch_shrink(const uint16_t* in, int64_t ld_in, int K, const uint16_t* mat_pack,
-                          int use_b_off, const lora_adapter_desc* desc, const uint8_t* active,
+                          int use_b_off, const lora_adapter_desc* desc, const int32_t* adpos,
                           const int32_t* perm, const int32_t* offsets, const int32_t* pre32,
                           int n_ad, int64_t n_tokens, uint16_t* out, int r_max, void* zero,
                           hipStream_t s) {
   if (n_tokens <= 0) return LORA_OK;
-  const int64_t bound = std::max(cdiv(n_tokens, SH_TM) + n_ad, cdiv(n_tokens, 256));
   const int nb_max = (r_max + 15) / 16;
-  const size_t lds = std::max<size_t>((size_t)SH_NST * (SH_XSLOTS + nb_max * 256) * sizeof(uint4),
-                                      (size_t)4 * SH_TM * 64 * sizeof(float));
+  const size_t ring[4] = {(size_t)sh_nst<1>() * (SH_XSLOTS + 256) * 16,
+                          (size_t)sh_nst<2>() * (SH_XSLOTS + 512) * 16,
+                          (size_t)sh_nst<3>() * (SH_XSLOTS + 768) * 16,
+                          (size_t)sh_nst<4>() * (SH_XSLOTS + 1024) * 16};
+  size_t lds = (size_t)4 * SH_TM * 64 * sizeof(float);
+  for (int nb = 1; nb <= nb_max; ++nb) lds = std::max(lds, ring[nb - 1]);
   static size_t attr = 0;
   if (attr < lds) {
     TRY_HIP(hipFuncSetAttribute((const void*)shrink_kernel,
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
     attr = lds;
   }
-  hipLaunchKernelGGL(shrink_kernel, dim3((unsigned)bound, 2), dim3(256), lds, s, in, ld_in, K,
-                     mat_pack, use_b_off, desc, active, perm, offsets, pre32, n_ad, n_tokens, out,
+  hipLaunchKernelGGL(shrink_kernel, dim3(persistent_blocks()), dim3(256), lds, s, in, ld_in, K,
+                     mat_pack, use_b_off, desc, adpos, perm, offsets, pre32, n_ad, n_tokens, out,
                      r_max, (uint4*)zero);
   return launch_check("shrink");
 }
@@ -567,7 +616,7 @@ lora_status launch_grad_t(dim3 grid, const uint16_t* P, int64_t plane, int r_max
                           const lora_adapter_desc* desc, const int32_t* perm,
                           const int32_t* offsets, const int32_t* chunk_pre, int n_ad,
                           float* out_pack, float* partial, int accumulate, hipStream_t s) {
-  const size_t lds = (size_t)GR_NST * GrP<PN>::STAGE * sizeof(uint4);
+  const size_t lds = (size_t)GrP<PN>::NST * GrP<PN>::STAGE * sizeof(uint4);
   static bool attr = false;
   if (!attr) {
     TRY_HIP(hipFuncSetAttribute((const void*)grad_kernel<MODE, PN>,
@@ -585,8 +634,7 @@ lora_status launch_grad(int mode, const uint16_t* P, int r_max, const void* zero
                         const int32_t* chunk_pre, int n_ad, int64_t n_tokens, float* out_pack,
                         float* partial, int accumulate, hipStream_t s) {
   if (n_tokens > 0) {
-    const int64_t bound = cdiv(n_tokens, GR_TC) + n_ad;
-    dim3 grid((unsigned)bound, (unsigned)cdiv(D, GR_NJ));
+    dim3 grid(persistent_blocks());
     const int64_t plane = n_tokens * r_max;
     const uint16_t* z = (const uint16_t*)zero;
     lora_status st;

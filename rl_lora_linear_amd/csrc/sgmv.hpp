@@ -16,8 +16,7 @@ struct LoraFuse {
   int use_b_off;            // factor at b_off (B_a [N][r]) or a_off (A_a^T [N][r])
   const uint16_t* lmat;
   const lora_adapter_desc* desc;
-  const uint8_t* active;
-  const int32_t* offsets;
+  const int32_t* adpos;     // [tokens] adapter of each segment position, -1 for none
   int n_ad;
 };
 lora_status gemm_nt_lora(const uint16_t* A, const uint16_t* B, uint16_t* C, int M, int N, int K,
@@ -31,7 +30,7 @@ lora_status gemm_nt_grad(const uint16_t* A, const uint16_t* B, uint16_t* G, int6
                          const float* lse, const float* dlogp, hipStream_t s, int group_m = 0);
 
 lora_status launch_shrink(const uint16_t* in, int64_t ld_in, int K, const uint16_t* mat_pack,
-                          int use_b_off, const lora_adapter_desc* desc, const uint8_t* active,
+                          int use_b_off, const lora_adapter_desc* desc, const int32_t* adpos,
                           const int32_t* perm, const int32_t* offsets, const int32_t* pre32,
                           int n_ad, int64_t n_tokens, uint16_t* out, int r_max, void* zero,
                           hipStream_t s);
