@@ -30,6 +30,22 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 
 METRIC = "tokens/s mixed-adapter LoRA fwd+bwd at 8B shapes; % MFMA / HBM peak"
 
+# HBM bytes per base-GEMM launch at this workload, from rocprofv3 FETCH_SIZE and
+# WRITE_SIZE passes scaled by a 512 MiB copy's readings (x2 fetch, x1 write):
+# profiles/gemm_nt_traffic_8192x4096x4096.md.  Valid only for the kernel source the
+# counters were taken on (sha256 prefix of gemm.hip + common.hpp); else reported null.
+GEMM_TRAFFIC = {"bytes_per_launch": 476.6e6, "src_sha256": "8b2602c785a3972a"}
+
+
+def gemm_traffic():
+    import hashlib
+    csrc = os.path.join(ROOT, "rl_lora_linear_amd", "csrc")
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "common.hpp"):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return GEMM_TRAFFIC["bytes_per_launch"] if h.hexdigest()[:16] == GEMM_TRAFFIC["src_sha256"] else None
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -230,7 +246,8 @@ def main():
                    "tokens": N, "d_in": d_in, "d_out": d_out, "adapters": n_ad, "rank": r},
         "roofline": {"bound": "mfma", "kernel": "base GEMM (y = x W^T and dx = dy W, bf16 MFMA)",
                      "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": gemm_traffic(),
+                     "traffic_unit": "HBM bytes per launch (rocprofv3 counters)"},
         "kernels": kernels,
     }
     if not args.no_cpu_baseline:
