@@ -84,7 +84,8 @@ typedef enum {
 typedef enum { LORA_IDS_SORTED = 0, LORA_IDS_INTERLEAVED = 1 } lora_id_order;
 
 /* One adapter.  Device array of n_adapters entries (24 bytes each).
- * rank: 8..64 and a multiple of 8, and <= lora_shape.max_rank.
+ * rank: 8..64 and a multiple of 8, and <= lora_shape.max_rank; 0 marks an unused
+ * slot (the adapter is inactive, without a flag).
  * scale: s_i = alpha_i / r_i, applied to the LoRA delta and its gradients. */
 typedef struct {
   int64_t a_off;   /* element offset of A_i [rank][d_in] in the A pack */
@@ -293,6 +294,85 @@ lora_status swiglu_forward(int64_t n, const uint16_t* gate, const uint16_t* up, 
 /* dg = dh * u * silu'(g), du = dh * silu(g). */
 lora_status swiglu_backward(int64_t n, const uint16_t* dh, const uint16_t* gate,
                             const uint16_t* up, uint16_t* dgate, uint16_t* dup, void* stream);
+
+/* ---- routed experts (mixture-of-experts layer) ------------------------ */
+
+/* A top-k routed SwiGLU expert layer whose three projections (gate, up, down)
+ * each carry the token's LoRA adapter on every expert (TPU RL note, section
+ * 12 "Mixture-of-experts, and where adapters attach"; tinker-ticks "Step
+ * time": the MoE pool touches every expert weight).  For token t with experts
+ * e_1..e_K and weights w_1..w_K:
+ *   y_t = sum_k w_k down_e(silu(gate_e x_t) * up_e x_t),
+ *   proj_e(z) = W_e z + s B_{e,a} (A_{e,a} z),  a = adapter_ids[t].
+ * Assignments j = t*K + k are sorted by the key e*(n_adapters + 1) + a; each
+ * expert's rows run as one segment of a grouped GEMM and each (expert,
+ * adapter) pair as one LoRA segment.  Routing weights are constants in the
+ * backward (the router is not differentiated).
+ * Layouts (bf16): W_gate, W_up [E][F][H]; W_down [E][H][F]; the backward takes
+ * the per-expert transposes W_gate_t, W_up_t [E][H][F] and W_down_t [E][F][H]
+ * (lora_transpose_bf16 per expert).  Descriptor tables are
+ * [n_experts][n_adapters] per projection (gate/up: A [r][H], B [F][r]; down:
+ * A [r][F], B [H][r]); an entry with rank 0 means "no adapter" for that pair.
+ * A pair is active only when its entries are valid in all three tables
+ * (otherwise LORA_FLAG_BAD_DESC and no LoRA for it).  Adapter ids out of range
+ * give the base experts only (LORA_FLAG_ID_RANGE); an expert id out of range
+ * drops that assignment (LORA_FLAG_ID_RANGE). */
+typedef struct {
+  int64_t n_tokens;        /* N */
+  int64_t hidden;          /* H: multiple of 64 */
+  int64_t d_ff;            /* F (expert intermediate): multiple of 64 */
+  int64_t gate_pack_elems; /* pack sizes, for descriptor bounds checks */
+  int64_t up_pack_elems;
+  int64_t down_pack_elems;
+  int32_t n_experts;       /* E: 1 .. 1024 */
+  int32_t top_k;           /* K: 1 .. min(16, E); N*K < 2^30 */
+  int32_t n_adapters;      /* E * (n_adapters + 1) <= 16384 */
+  int32_t max_rank;        /* 16 .. 64, multiple of 16 */
+} moe_shape;
+
+/* Top-k routing of fp32 logits [n][n_experts]: experts int32 [n][top_k] by
+ * descending logit (ties to the lower expert index; logits must be finite),
+ * weights fp32 [n][top_k] = softmax over the chosen k (the full softmax
+ * renormalised over its top k).  Expert ids are exact. */
+lora_status moe_route(int64_t n, int32_t n_experts, int32_t top_k, const float* logits,
+                      int32_t* experts, float* weights, void* stream);
+
+/* Workspace for moe_forward / moe_backward, and the caller-owned buffer the
+ * forward fills and the backward reads.  0 on an invalid shape.
+ * "Position order": the assignments j = t*K + k stably sorted by key
+ * e*(n_adapters + 1) + a (a = n_adapters for an adapter id out of range),
+ * assignments with an expert id out of range last.  Saved layout, each region
+ * starting at a multiple of 256 bytes in this order: g, u, h (bf16 [N*K][F] in
+ * position order: gate and up pre-activations, silu(g)*u), then the scaled
+ * LoRA vectors s*u of gate, up and down (bf16 hi/lo planes [2][N*K][max_rank]). */
+size_t moe_workspace_bytes(const moe_shape* shape);
+size_t moe_saved_bytes(const moe_shape* shape);
+
+/*   x bf16 [N][H], experts int32 [N][K], weights fp32 [N][K], adapter_ids [N]
+ *   y bf16 [N][H] out (fp32 weighted sum over the K experts, rounded once)
+ *   saved: moe_saved_bytes bytes, 16-byte aligned, kept for moe_backward. */
+lora_status moe_forward(const moe_shape* shape, const uint16_t* x, const int32_t* experts,
+                        const float* weights, const int32_t* adapter_ids, const uint16_t* W_gate,
+                        const uint16_t* W_up, const uint16_t* W_down, const uint16_t* gate_pack,
+                        const uint16_t* up_pack, const uint16_t* down_pack,
+                        const lora_adapter_desc* gate_desc, const lora_adapter_desc* up_desc,
+                        const lora_adapter_desc* down_desc, uint16_t* y, void* saved, void* ws,
+                        size_t ws_bytes, void* stream);
+
+/*   dy bf16 [N][H]; dx bf16 [N][H] out; d*_pack fp32 gradient packs with the
+ *   A/B packs' offsets: accumulate = 0 overwrites every active pair's region
+ *   (zeros for pairs without assignments), != 0 adds into it.  Deterministic.
+ *   trace (nullable): bf16 [3][N*K][F] out, the stage tensors dh, dg, du in
+ *   position order (for per-stage verification). */
+lora_status moe_backward(const moe_shape* shape, const uint16_t* dy, const uint16_t* x,
+                         const int32_t* experts, const float* weights, const int32_t* adapter_ids,
+                         const uint16_t* W_gate_t, const uint16_t* W_up_t,
+                         const uint16_t* W_down_t, const uint16_t* gate_pack,
+                         const uint16_t* up_pack, const uint16_t* down_pack,
+                         const lora_adapter_desc* gate_desc, const lora_adapter_desc* up_desc,
+                         const lora_adapter_desc* down_desc, const void* saved, uint16_t* dx,
+                         float* dgate_pack, float* dup_pack, float* ddown_pack, int accumulate,
+                         uint16_t* trace, void* ws, size_t ws_bytes, void* stream);
 
 /* ---- kernel timing (measurement) ------------------------------------- */
 

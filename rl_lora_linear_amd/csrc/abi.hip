@@ -144,11 +144,8 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 lora_status layer_segments(const lora_shape& sh, const lora_adapter_desc* desc,
                            const int32_t* ids, const LayerWs& w, hipStream_t s) {
   SegExtras ex{};
-  ex.desc = desc;
-  ex.d_in = sh.d_in;
-  ex.d_out = sh.d_out;
-  ex.a_elems = sh.a_pack_elems;
-  ex.b_elems = sh.b_pack_elems;
+  ex.tab[0] = SegDescs{desc, sh.d_in, sh.d_out, sh.a_pack_elems, sh.b_pack_elems};
+  ex.n_tabs = 1;
   ex.max_rank = sh.max_rank;
   ex.active = w.active;
   ex.tm[0] = kTmShrink;
@@ -250,14 +247,24 @@ lora_status lora_forward(const lora_shape* shape, const uint16_t* x, const uint1
   TRY(layer_segments(sh, desc, adapter_ids, w, s));
   if (N == 0) return LORA_OK;
   timer_begin(LORA_TIMER_SHRINK, s);
-  TRY(launch_shrink(x, sh.d_in, (int)sh.d_in, A_pack, 0, desc, w.adpos, w.perm, w.offsets,
-                    w.pre32, sh.n_adapters, sh.n_tokens, u_saved, sh.max_rank, w.zero, s));
+  TRY(launch_shrink(x, sh.d_in, (int)sh.d_in, A_pack, 0, desc, w.adpos, w.perm, w.perm, nullptr,
+                    w.offsets, w.pre32, sh.n_adapters, sh.n_tokens, u_saved, sh.max_rank, w.zero,
+                    s));
   timer_end(LORA_TIMER_SHRINK, s);
   // base GEMM over rows in segment order with the expand y += B_a (s u) fused
-  LoraFuse f{w.perm, u_saved, sh.n_tokens * sh.max_rank, sh.max_rank, 1, B_pack, desc, w.adpos,
-             sh.n_adapters};
+  GemmRows f;
+  f.a_rows = f.c_rows = w.perm;
+  f.a_rows_bound = sh.n_tokens;
+  f.vec = u_saved;
+  f.vec_plane = sh.n_tokens * sh.max_rank;
+  f.vec_ld = sh.max_rank;
+  f.use_b_off = 1;
+  f.lmat = B_pack;
+  f.desc = desc;
+  f.adpos = w.adpos;
+  f.n_ad = sh.n_adapters;
   timer_begin(LORA_TIMER_BASE_GEMM, s);
-  TRY(gemm_nt_lora(x, W, y, N, (int)sh.d_out, (int)sh.d_in, sh.d_in, sh.d_in, sh.d_out, f, s));
+  TRY(gemm_nt_rows(x, W, y, N, (int)sh.d_out, (int)sh.d_in, sh.d_in, sh.d_in, sh.d_out, f, s));
   timer_end(LORA_TIMER_BASE_GEMM, s);
   return LORA_OK;
 }
@@ -290,21 +297,31 @@ lora_status lora_backward(const lora_shape* shape, const uint16_t* dy, const uin
                                w.AT, w.BT, s));
   if (N > 0) {
     timer_begin(LORA_TIMER_SHRINK, s);
-    TRY(launch_shrink(dy, sh.d_out, (int)sh.d_out, w.BT, 1, desc, w.adpos, w.perm, w.offsets,
-                      w.pre32, sh.n_adapters, sh.n_tokens, w.v, sh.max_rank, w.zero, s));
+    TRY(launch_shrink(dy, sh.d_out, (int)sh.d_out, w.BT, 1, desc, w.adpos, w.perm, w.perm,
+                      nullptr, w.offsets, w.pre32, sh.n_adapters, sh.n_tokens, w.v, sh.max_rank,
+                      w.zero, s));
     timer_end(LORA_TIMER_SHRINK, s);
     // dX = dY W over rows in segment order with the expand dX += A_a^T (s v) fused
-    LoraFuse f{w.perm, w.v, sh.n_tokens * sh.max_rank, sh.max_rank, 0, w.AT, desc, w.adpos,
-               sh.n_adapters};
+    GemmRows f;
+    f.a_rows = f.c_rows = w.perm;
+    f.a_rows_bound = sh.n_tokens;
+    f.vec = w.v;
+    f.vec_plane = sh.n_tokens * sh.max_rank;
+    f.vec_ld = sh.max_rank;
+    f.use_b_off = 0;
+    f.lmat = w.AT;
+    f.desc = desc;
+    f.adpos = w.adpos;
+    f.n_ad = sh.n_adapters;
     timer_begin(LORA_TIMER_BASE_GEMM, s);
-    TRY(gemm_nt_lora(dy, W_t, dx, N, (int)sh.d_in, (int)sh.d_out, sh.d_out, sh.d_out, sh.d_in, f, s));
+    TRY(gemm_nt_rows(dy, W_t, dx, N, (int)sh.d_in, (int)sh.d_out, sh.d_out, sh.d_out, sh.d_in, f, s));
     timer_end(LORA_TIMER_BASE_GEMM, s);
   }
   timer_begin(LORA_TIMER_GRAD, s);
   TRY(launch_grad(0, u_saved, sh.max_rank, w.zero, dy, sh.d_out, (int)sh.d_out, desc, w.active,
-                  w.perm, w.offsets, w.prec, sh.n_adapters, sh.n_tokens, dB_pack, w.partial,
+                  w.perm, 0, w.offsets, w.prec, sh.n_adapters, sh.n_tokens, dB_pack, w.partial,
                   accumulate, s));
-  TRY(launch_grad(1, w.v, sh.max_rank, w.zero, x, sh.d_in, (int)sh.d_in, desc, w.active, w.perm,
+  TRY(launch_grad(1, w.v, sh.max_rank, w.zero, x, sh.d_in, (int)sh.d_in, desc, w.active, w.perm, 0,
                   w.offsets, w.prec, sh.n_adapters, sh.n_tokens, dA_pack, w.partial, accumulate, s));
   timer_end(LORA_TIMER_GRAD, s);
   return LORA_OK;
@@ -495,6 +512,345 @@ lora_status swiglu_backward(int64_t n, const uint16_t* dh, const uint16_t* gate,
   LORA_ARG_CHECK(n == 0 || (aligned16(dh) && aligned16(gate) && aligned16(up) && aligned16(dgate) && aligned16(dup)),
                  "swiglu buffers must be 16-byte aligned");
   return launch_swiglu_bwd(n, dh, gate, up, dgate, dup, S(stream));
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------------ MoE
+static lora_status check_moe(const moe_shape* sh) {
+  LORA_ARG_CHECK(sh != nullptr, "moe shape is NULL");
+  LORA_ARG_CHECK(sh->n_tokens >= 0 && sh->n_tokens * sh->top_k <= INT32_MAX / 2,
+                 "n_tokens * top_k must be < 2^30");
+  LORA_ARG_CHECK(sh->n_experts >= 1 && sh->n_experts <= 1024, "n_experts %d outside [1, 1024]",
+                 sh->n_experts);
+  LORA_ARG_CHECK(sh->top_k >= 1 && sh->top_k <= 16 && sh->top_k <= sh->n_experts,
+                 "top_k %d outside [1, min(16, n_experts)]", sh->top_k);
+  LORA_ARG_CHECK(sh->n_adapters >= 1 && (int64_t)sh->n_experts * (sh->n_adapters + 1) <= 16384,
+                 "n_adapters %d: n_experts * (n_adapters + 1) must be <= 16384", sh->n_adapters);
+  LORA_ARG_CHECK(sh->max_rank >= 16 && sh->max_rank <= 64 && sh->max_rank % 16 == 0,
+                 "max_rank %d must be a multiple of 16 in [16, 64]", sh->max_rank);
+  LORA_ARG_CHECK(sh->gate_pack_elems >= 0 && sh->up_pack_elems >= 0 && sh->down_pack_elems >= 0,
+                 "pack sizes must be >= 0");
+  if (sh->hidden <= 0 || sh->d_ff <= 0 || sh->hidden % 64 || sh->d_ff % 64 ||
+      sh->hidden > (1 << 20) || sh->d_ff > (1 << 20)) {
+    set_error("hidden %lld and d_ff %lld must be positive multiples of 64 and <= 2^20",
+              (long long)sh->hidden, (long long)sh->d_ff);
+    return LORA_E_UNSUPPORTED;
+  }
+  return LORA_OK;
+}
+
+namespace {
+
+// Assignments j = t*K + k sorted by key e*(n_ad + 1) + a ("position" order).
+struct MoeWs {
+  char* seg;
+  size_t seg_bytes;
+  int32_t* keys;     // [NK]
+  int32_t* perm;     // position -> assignment
+  int32_t* adpos;    // position -> key (-1: none)
+  int32_t* tokrow;   // position -> token
+  int32_t* inv;      // assignment -> position
+  int32_t* offsets;  // [n_keys + 1]
+  uint8_t* active;   // [n_keys]
+  int32_t* pre32;
+  int32_t* prec;
+  int32_t* gpre;     // [E + 1]
+  lora_adapter_desc* desc[3];  // per-key tables (gate, up, down) with "no adapter" entries
+  uint16_t* zero;
+  uint16_t* o;       // forward: expert outputs [NK][H] bf16
+  float* wpos;       // backward: routing weight per position
+  uint16_t* v[3];    // backward: s*v planes per projection [2][NK][R] (down: s*w*v)
+  uint16_t* uw;      // backward: w * (s u_down) planes
+  uint16_t* dh;      // [NK][F]
+  uint16_t* dg;      // [NK][F]
+  uint16_t* du;      // [NK][F]
+  uint16_t* dxg;     // [NK][H]
+  uint16_t* dxu;     // [NK][H]
+  uint16_t* AT[3];
+  uint16_t* BT[3];
+  float* partial;
+  size_t total;
+};
+
+struct MoeSaved {
+  uint16_t* g;       // gate pre-activation [NK][F] bf16
+  uint16_t* u;       // up pre-activation
+  uint16_t* h;       // silu(g) * u
+  uint16_t* su[3];   // s*u planes per projection [2][NK][R]
+  size_t total;
+};
+
+MoeSaved carve_saved(const moe_shape& sh, void* p) {
+  Carve cv(p, 0);
+  const size_t NK = (size_t)std::max<int64_t>(sh.n_tokens * sh.top_k, 1);
+  MoeSaved m{};
+  m.g = cv.take<uint16_t>(NK * sh.d_ff);
+  m.u = cv.take<uint16_t>(NK * sh.d_ff);
+  m.h = cv.take<uint16_t>(NK * sh.d_ff);
+  for (int i = 0; i < 3; ++i) m.su[i] = cv.take<uint16_t>(2 * NK * sh.max_rank);
+  m.total = cv.used;
+  return m;
+}
+
+MoeWs carve_moe(const moe_shape& sh, void* ws, size_t bytes, bool backward) {
+  Carve cv(ws, bytes);
+  MoeWs w{};
+  const int64_t NK = std::max<int64_t>(sh.n_tokens * sh.top_k, 1);
+  const int32_t n_keys = sh.n_experts * (sh.n_adapters + 1);
+  const int64_t packs[3] = {sh.gate_pack_elems, sh.up_pack_elems, sh.down_pack_elems};
+  w.seg_bytes = segments_ws_bytes(NK, n_keys);
+  w.seg = cv.take<char>(w.seg_bytes);
+  w.keys = cv.take<int32_t>(NK);
+  w.perm = cv.take<int32_t>(NK);
+  w.adpos = cv.take<int32_t>(NK);
+  w.tokrow = cv.take<int32_t>(NK);
+  w.inv = cv.take<int32_t>(NK);
+  w.offsets = cv.take<int32_t>((size_t)n_keys + 1);
+  w.active = cv.take<uint8_t>((size_t)n_keys);
+  w.pre32 = cv.take<int32_t>((size_t)n_keys + 1);
+  w.prec = cv.take<int32_t>((size_t)n_keys + 1);
+  w.gpre = cv.take<int32_t>((size_t)sh.n_experts + 1);
+  for (int i = 0; i < 3; ++i) w.desc[i] = cv.take<lora_adapter_desc>((size_t)n_keys);
+  w.zero = cv.take<uint16_t>(128);
+  if (!backward) {
+    w.o = cv.take<uint16_t>((size_t)NK * sh.hidden);
+  } else {
+    w.wpos = cv.take<float>(NK);
+    for (int i = 0; i < 3; ++i) w.v[i] = cv.take<uint16_t>((size_t)2 * NK * sh.max_rank);
+    w.uw = cv.take<uint16_t>((size_t)2 * NK * sh.max_rank);
+    w.dh = cv.take<uint16_t>((size_t)NK * sh.d_ff);
+    w.dg = cv.take<uint16_t>((size_t)NK * sh.d_ff);
+    w.du = cv.take<uint16_t>((size_t)NK * sh.d_ff);
+    w.dxg = cv.take<uint16_t>((size_t)NK * sh.hidden);
+    w.dxu = cv.take<uint16_t>((size_t)NK * sh.hidden);
+    for (int i = 0; i < 3; ++i) {
+      w.AT[i] = cv.take<uint16_t>((size_t)packs[i]);
+      w.BT[i] = cv.take<uint16_t>((size_t)packs[i]);
+    }
+    w.partial = cv.take<float>((size_t)grad_partial_floats(NK, n_keys,
+                                                          std::max(sh.hidden, sh.d_ff),
+                                                          sh.max_rank));
+  }
+  w.total = cv.used;
+  return w;
+}
+
+// Composite keys, per-key descriptor tables and the sorted assignment order.
+lora_status moe_segments(const moe_shape& sh, const int32_t* experts, const int32_t* ids,
+                         const lora_adapter_desc* const desc[3], const MoeWs& w, hipStream_t s) {
+  const int64_t NK = sh.n_tokens * sh.top_k;
+  const int n_keys = sh.n_experts * (sh.n_adapters + 1);
+  TRY(launch_moe_keys(experts, ids, NK, sh.top_k, sh.n_experts, sh.n_adapters, w.keys,
+                      (int32_t*)w.seg, s));
+  lora_adapter_desc* const dst[3] = {w.desc[0], w.desc[1], w.desc[2]};
+  TRY(launch_moe_desc(desc, dst, sh.n_experts, sh.n_adapters, s));
+  SegExtras ex{};
+  ex.tab[0] = SegDescs{w.desc[0], sh.hidden, sh.d_ff, sh.gate_pack_elems, sh.gate_pack_elems};
+  ex.tab[1] = SegDescs{w.desc[1], sh.hidden, sh.d_ff, sh.up_pack_elems, sh.up_pack_elems};
+  ex.tab[2] = SegDescs{w.desc[2], sh.d_ff, sh.hidden, sh.down_pack_elems, sh.down_pack_elems};
+  ex.n_tabs = 3;
+  ex.max_rank = sh.max_rank;
+  ex.active = w.active;
+  ex.tm[0] = kTmShrink;
+  ex.pre[0] = w.pre32;
+  ex.tm[1] = 1;
+  ex.pre[1] = nullptr;
+  ex.tm[2] = kGradChunk;
+  ex.pre[2] = w.prec;
+  ex.adpos = w.adpos;
+  ex.row_div = sh.top_k;
+  ex.tokrow = w.tokrow;
+  ex.inv = w.inv;
+  ex.group = sh.n_adapters + 1;
+  ex.n_groups = sh.n_experts;
+  ex.gpre = w.gpre;
+  return run_segments(w.keys, NK, n_keys, LORA_IDS_INTERLEAVED, w.perm, w.offsets, &ex, w.seg,
+                      w.seg_bytes, s);
+}
+
+// One grouped expert projection over the sorted assignments: rows gathered
+// through a_rows (nullable), base weights per expert, the LoRA expand fused.
+lora_status moe_project(const moe_shape& sh, const MoeWs& w, const uint16_t* A,
+                        const int32_t* a_rows, int64_t a_rows_bound, const uint16_t* W,
+                        int64_t n_out, int64_t k_in, const uint16_t* planes,
+                        const uint16_t* lmat, int use_b_off, const lora_adapter_desc* desc,
+                        const float* rowscale, uint16_t* C, hipStream_t s) {
+  const int64_t NK = sh.n_tokens * sh.top_k;
+  GemmRows f;
+  f.a_rows = a_rows;
+  f.a_rows_bound = a_rows_bound;
+  f.rowscale = rowscale;
+  f.g_tile = w.gpre;
+  f.g_off = w.offsets;
+  f.g_stride = sh.n_adapters + 1;
+  f.n_groups = sh.n_experts;
+  f.ldb_group = n_out * k_in;
+  f.tiles_m_bound = (int)(cdiv(NK, 256) + sh.n_experts);
+  f.vec = planes;
+  f.vec_plane = NK * sh.max_rank;
+  f.vec_ld = sh.max_rank;
+  f.use_b_off = use_b_off;
+  f.lmat = lmat;
+  f.desc = desc;
+  f.adpos = w.adpos;
+  f.n_ad = sh.n_experts * (sh.n_adapters + 1);
+  return gemm_nt_rows(A, W, C, (int)NK, (int)n_out, (int)k_in, k_in, k_in, n_out, f, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+lora_status moe_route(int64_t n, int32_t n_experts, int32_t top_k, const float* logits,
+                      int32_t* experts, float* weights, void* stream) {
+  LORA_ARG_CHECK(n >= 0, "n must be >= 0");
+  LORA_ARG_CHECK(n_experts >= 1 && n_experts <= 1024, "n_experts %d outside [1, 1024]", n_experts);
+  LORA_ARG_CHECK(top_k >= 1 && top_k <= 16 && top_k <= n_experts,
+                 "top_k %d outside [1, min(16, n_experts)]", top_k);
+  LORA_ARG_CHECK(n == 0 || (logits && experts && weights), "logits/experts/weights NULL");
+  return launch_moe_route(logits, n, n_experts, top_k, experts, weights, S(stream));
+}
+
+size_t moe_workspace_bytes(const moe_shape* shape) {
+  if (check_moe(shape) != LORA_OK) return 0;
+  return std::max(carve_moe(*shape, nullptr, 0, false).total,
+                  carve_moe(*shape, nullptr, 0, true).total);
+}
+
+size_t moe_saved_bytes(const moe_shape* shape) {
+  if (check_moe(shape) != LORA_OK) return 0;
+  return carve_saved(*shape, nullptr).total;
+}
+
+lora_status moe_forward(const moe_shape* shape, const uint16_t* x, const int32_t* experts,
+                        const float* weights, const int32_t* adapter_ids, const uint16_t* W_gate,
+                        const uint16_t* W_up, const uint16_t* W_down, const uint16_t* gate_pack,
+                        const uint16_t* up_pack, const uint16_t* down_pack,
+                        const lora_adapter_desc* gate_desc, const lora_adapter_desc* up_desc,
+                        const lora_adapter_desc* down_desc, uint16_t* y, void* saved, void* ws,
+                        size_t ws_bytes, void* stream) {
+  TRY(check_moe(shape));
+  const moe_shape& sh = *shape;
+  LORA_ARG_CHECK(W_gate && W_up && W_down && gate_pack && up_pack && down_pack && gate_desc &&
+                     up_desc && down_desc,
+                 "weights, packs and descriptor tables must be non-NULL");
+  LORA_ARG_CHECK(sh.n_tokens == 0 || (x && experts && weights && adapter_ids && y && saved),
+                 "x, experts, weights, adapter_ids, y and saved must be non-NULL");
+  LORA_ARG_CHECK(aligned16(x) && aligned16(y) && aligned16(saved) && aligned16(W_gate) &&
+                     aligned16(W_up) && aligned16(W_down) && aligned16(gate_pack) &&
+                     aligned16(up_pack) && aligned16(down_pack),
+                 "activations, weights, packs and saved must be 16-byte aligned");
+  MoeWs w = carve_moe(sh, ws, ws_bytes, false);
+  if (!ws || w.total > ws_bytes) {
+    set_error("moe_forward: workspace %zu bytes < %zu needed", ws_bytes, w.total);
+    return LORA_E_WORKSPACE;
+  }
+  if (sh.n_tokens == 0) return LORA_OK;
+  hipStream_t s = S(stream);
+  const MoeSaved sv = carve_saved(sh, saved);
+  const int64_t NK = sh.n_tokens * sh.top_k, H = sh.hidden, F = sh.d_ff;
+  const int R = sh.max_rank;
+  const int n_keys = sh.n_experts * (sh.n_adapters + 1);
+  const lora_adapter_desc* const descs[3] = {gate_desc, up_desc, down_desc};
+  TRY(moe_segments(sh, experts, adapter_ids, descs, w, s));
+  // gate and up: s*u planes from the gathered token rows, then the grouped GEMM
+  const uint16_t* packs[2] = {gate_pack, up_pack};
+  const uint16_t* Ws[2] = {W_gate, W_up};
+  uint16_t* pre[2] = {sv.g, sv.u};
+  for (int i = 0; i < 2; ++i) {
+    TRY(launch_shrink(x, H, (int)H, packs[i], 0, w.desc[i], w.adpos, w.tokrow, nullptr, nullptr,
+                      w.offsets, w.pre32, n_keys, NK, sv.su[i], R, w.zero, s));
+    TRY(moe_project(sh, w, x, w.tokrow, sh.n_tokens, Ws[i], F, H, sv.su[i], packs[i], 1,
+                    w.desc[i], nullptr, pre[i], s));
+  }
+  TRY(launch_swiglu_fwd(NK * F, sv.g, sv.u, sv.h, s));
+  // down, then the weighted combine back to tokens
+  TRY(launch_shrink(sv.h, F, (int)F, down_pack, 0, w.desc[2], w.adpos, nullptr, nullptr, nullptr,
+                    w.offsets, w.pre32, n_keys, NK, sv.su[2], R, w.zero, s));
+  TRY(moe_project(sh, w, sv.h, nullptr, NK, W_down, H, F, sv.su[2], down_pack, 1, w.desc[2],
+                  nullptr, w.o, s));
+  return launch_moe_combine(w.o, nullptr, weights, w.inv, w.keys, sh.n_tokens, sh.top_k, H, y, s);
+}
+
+lora_status moe_backward(const moe_shape* shape, const uint16_t* dy, const uint16_t* x,
+                         const int32_t* experts, const float* weights, const int32_t* adapter_ids,
+                         const uint16_t* W_gate_t, const uint16_t* W_up_t,
+                         const uint16_t* W_down_t, const uint16_t* gate_pack,
+                         const uint16_t* up_pack, const uint16_t* down_pack,
+                         const lora_adapter_desc* gate_desc, const lora_adapter_desc* up_desc,
+                         const lora_adapter_desc* down_desc, const void* saved, uint16_t* dx,
+                         float* dgate_pack, float* dup_pack, float* ddown_pack, int accumulate,
+                         uint16_t* trace, void* ws, size_t ws_bytes, void* stream) {
+  TRY(check_moe(shape));
+  const moe_shape& sh = *shape;
+  LORA_ARG_CHECK(W_gate_t && W_up_t && W_down_t && gate_pack && up_pack && down_pack &&
+                     gate_desc && up_desc && down_desc && dgate_pack && dup_pack && ddown_pack,
+                 "weights, packs, descriptor tables and gradient packs must be non-NULL");
+  LORA_ARG_CHECK(sh.n_tokens == 0 || (dy && x && experts && weights && adapter_ids && saved && dx),
+                 "dy, x, experts, weights, adapter_ids, saved and dx must be non-NULL");
+  LORA_ARG_CHECK(aligned16(dy) && aligned16(x) && aligned16(dx) && aligned16(saved) &&
+                     aligned16(W_gate_t) && aligned16(W_up_t) && aligned16(W_down_t) &&
+                     aligned16(gate_pack) && aligned16(up_pack) && aligned16(down_pack) &&
+                     aligned16(dgate_pack) && aligned16(dup_pack) && aligned16(ddown_pack),
+                 "activations, weights, packs and saved must be 16-byte aligned");
+  MoeWs w = carve_moe(sh, ws, ws_bytes, true);
+  if (!ws || w.total > ws_bytes) {
+    set_error("moe_backward: workspace %zu bytes < %zu needed", ws_bytes, w.total);
+    return LORA_E_WORKSPACE;
+  }
+  if (trace) {   // the caller keeps dh, dg, du
+    LORA_ARG_CHECK(aligned16(trace), "trace must be 16-byte aligned");
+    const int64_t nf = sh.n_tokens * sh.top_k * sh.d_ff;
+    w.dh = trace;
+    w.dg = trace + nf;
+    w.du = trace + 2 * nf;
+  }
+  hipStream_t s = S(stream);
+  const MoeSaved sv = carve_saved(sh, const_cast<void*>(saved));
+  const int64_t NK = sh.n_tokens * sh.top_k, H = sh.hidden, F = sh.d_ff;
+  const int R = sh.max_rank;
+  const int n_keys = sh.n_experts * (sh.n_adapters + 1);
+  const lora_adapter_desc* const descs[3] = {gate_desc, up_desc, down_desc};
+  TRY(moe_segments(sh, experts, adapter_ids, descs, w, s));
+  const uint16_t* packs[3] = {gate_pack, up_pack, down_pack};
+  float* grads[3] = {dgate_pack, dup_pack, ddown_pack};
+  const int64_t d_in[3] = {H, H, F}, d_out[3] = {F, F, H};
+  for (int i = 0; i < 3; ++i)
+    TRY(launch_adapter_transpose(packs[i], packs[i], w.desc[i], w.active, n_keys, d_in[i],
+                                 d_out[i], w.AT[i], w.BT[i], s));
+  if (NK > 0) {
+    TRY(launch_moe_gather_w(weights, w.perm, NK, w.wpos, s));
+    // down: do_j = w_j dy_t.  v = s w B^T dy_t; dh = w (dy_t W_down) + A^T v
+    TRY(launch_shrink(dy, H, (int)H, w.BT[2], 1, w.desc[2], w.adpos, w.tokrow, nullptr, w.wpos,
+                      w.offsets, w.pre32, n_keys, NK, w.v[2], R, w.zero, s));
+    TRY(moe_project(sh, w, dy, w.tokrow, sh.n_tokens, W_down_t, F, H, w.v[2], w.AT[2], 0,
+                    w.desc[2], w.wpos, w.dh, s));
+    // dB_down = sum dy_t (w s u)^T; dA_down = sum (s w v) h^T
+    TRY(launch_planes_scale(sv.su[2], w.wpos, NK, R, w.uw, s));
+  }
+  TRY(launch_grad(0, w.uw, R, w.zero, dy, H, (int)H, w.desc[2], w.active, w.tokrow, 1, w.offsets,
+                  w.prec, n_keys, NK, grads[2], w.partial, accumulate, s));
+  TRY(launch_grad(1, w.v[2], R, w.zero, sv.h, F, (int)F, w.desc[2], w.active, nullptr, 1,
+                  w.offsets, w.prec, n_keys, NK, grads[2], w.partial, accumulate, s));
+  if (NK > 0) TRY(launch_swiglu_bwd(NK * F, w.dh, sv.g, sv.u, w.dg, w.du, s));
+  // gate and up: v = s B^T d; dx_j = d W + A^T v; dB = sum d (s u)^T; dA = sum v x_t^T
+  uint16_t* dpre[2] = {w.dg, w.du};
+  uint16_t* dxp[2] = {w.dxg, w.dxu};
+  const uint16_t* Wts[2] = {W_gate_t, W_up_t};
+  for (int i = 0; i < 2; ++i) {
+    if (NK > 0) {
+      TRY(launch_shrink(dpre[i], F, (int)F, w.BT[i], 1, w.desc[i], w.adpos, nullptr, nullptr,
+                        nullptr, w.offsets, w.pre32, n_keys, NK, w.v[i], R, w.zero, s));
+      TRY(moe_project(sh, w, dpre[i], nullptr, NK, Wts[i], H, F, w.v[i], w.AT[i], 0, w.desc[i],
+                      nullptr, dxp[i], s));
+    }
+    TRY(launch_grad(0, sv.su[i], R, w.zero, dpre[i], F, (int)F, w.desc[i], w.active, nullptr, 1,
+                    w.offsets, w.prec, n_keys, NK, grads[i], w.partial, accumulate, s));
+    TRY(launch_grad(1, w.v[i], R, w.zero, x, H, (int)H, w.desc[i], w.active, w.tokrow, 1,
+                    w.offsets, w.prec, n_keys, NK, grads[i], w.partial, accumulate, s));
+  }
+  return launch_moe_combine(w.dxg, w.dxu, nullptr, w.inv, w.keys, sh.n_tokens, sh.top_k, H, dx, s);
 }
 
 // ------------------------------------------------------------------ timing

@@ -30,8 +30,20 @@ enum { EPI_BF16 = 0, EPI_LSE = 1, EPI_GRAD = 2 };
 struct GemmEpi {
   uint16_t* C;            // EPI_BF16 / EPI_GRAD output
   int64_t ldc;
-  // Rows in segment order: row m of A and C is token perm[m] (nullable).
-  const int32_t* perm;
+  // Row maps (nullable = identity): position m reads A row a_rows[m] and
+  // writes C row c_rows[m] (the LoRA vector row too); rowscale[m] multiplies
+  // the base product of row m before the LoRA slab is added.
+  const int32_t* a_rows;
+  const int32_t* c_rows;
+  const float* rowscale;
+  // Grouped rows (g_tile non-null): positions form n_groups consecutive groups,
+  // group g spanning [g_off[g*g_stride], g_off[(g+1)*g_stride]) and multiplying
+  // its own B at B + g*ldb_group; g_tile[g] = first 256-row tile of group g.
+  const int32_t* g_tile;
+  const int32_t* g_off;
+  int g_stride;
+  int n_groups;
+  int64_t ldb_group;
   // EPI_BF16 with the LoRA expand fused (nullable vec = plain GEMM): for the
   // row at segment position m, owned by adapter a, add s_a * vec[tok] . M_a^T
   // where M_a [N][r_a] sits at (use_b_off ? b_off : a_off) of the pack lmat.
@@ -179,7 +191,16 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_kernel(const uint16_t* __restr
   const int in = t - grp * gsz;
   const int tm = first_m + in % gm;
   const int tn = in / gm;
-  const int m0 = tm * GBM, n0 = tn * GBN;
+  int m0 = tm * GBM;
+  const int n0 = tn * GBN;
+  int Mlim = M;   // positions >= Mlim are past this tile's row range
+  if (ep.g_tile) {
+    if (tm >= ep.g_tile[ep.n_groups]) return;   // past the last group's tiles
+    const int g = find_bucket(ep.g_tile, ep.n_groups + 1, tm);
+    m0 = ep.g_off[g * ep.g_stride] + (tm - ep.g_tile[g]) * GBM;
+    Mlim = ep.g_off[(g + 1) * ep.g_stride];
+    B += (int64_t)g * ep.ldb_group;
+  }
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -201,11 +222,13 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_kernel(const uint16_t* __restr
   const int m_l = lane & 31;
   const int n_q = 4 * (lane >> 5);
   int tok[4], ad[4];
+  float rs[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = m0 + wm * 128 + i * 32 + m_l;
-    tok[i] = row < M ? (ep.perm ? ep.perm[row] : row) : -1;
-    ad[i] = (EPI == EPI_BF16 && ep.vec && row < M) ? ep.adpos[row] : -1;
+    tok[i] = row < Mlim ? (ep.c_rows ? ep.c_rows[row] : row) : -1;
+    ad[i] = (EPI == EPI_BF16 && ep.vec && row < Mlim) ? ep.adpos[row] : -1;
+    rs[i] = (EPI == EPI_BF16 && ep.rowscale && row < Mlim) ? ep.rowscale[row] : 1.f;
   }
 
   const int KT = K / SBK;
@@ -219,7 +242,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_kernel(const uint16_t* __restr
   // tile's first row.  Rows past the edge are clamped to the last row: they
   // only feed outputs that are never stored.
   uint32_t offA[4], offB[4];
-  const uint16_t* baseA = ep.perm ? A : A + (int64_t)m0 * lda;
+  const uint16_t* baseA = ep.a_rows ? A : A + (int64_t)m0 * lda;
   const uint16_t* baseB = B + (int64_t)n0 * ldb;
   {
     const int lrow = lane >> 2;
@@ -227,9 +250,9 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_kernel(const uint16_t* __restr
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int blk = wave * 4 + i;
-      const int ra = min(m0 + blk * 16 + lrow, M - 1);
+      const int ra = min(m0 + blk * 16 + lrow, Mlim - 1);
       const int rb = min(n0 + blk * 16 + lrow, N - 1);
-      const int64_t oa = ep.perm ? (int64_t)ep.perm[ra] * lda : (int64_t)(ra - m0) * lda;
+      const int64_t oa = ep.a_rows ? (int64_t)ep.a_rows[ra] * lda : (int64_t)(ra - m0) * lda;
       offA[i] = (uint32_t)((oa + chunk * 8) * 2);
       offB[i] = (uint32_t)(((int64_t)(rb - n0) * ldb + chunk * 8) * 2);
     }
@@ -338,6 +361,14 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_kernel(const uint16_t* __restr
   // ---- epilogues
 
   if constexpr (EPI == EPI_BF16) {
+    if (ep.rowscale) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int g = 0; g < 16; ++g) acc[i][j][g] *= rs[i];
+    }
     if (ep.vec) lora_slab(ep, n0, N, wn, lane, tok, ad, acc);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -457,14 +488,15 @@ static int pick_group_m(int tiles_m) { return tiles_m < 4 ? tiles_m : 4; }
 template <int EPI>
 static lora_status launch_gemm(const uint16_t* A, const uint16_t* B, int M, int N, int K,
                                int64_t lda, int64_t ldb, const GemmEpi& ep, hipStream_t s,
-                               int group_m) {
+                               int group_m, int64_t a_rows_bound = 0, int tiles_m_bound = 0) {
   if (M <= 0 || N <= 0) return LORA_OK;
-  if (ep.perm && (int64_t)M * lda * 2 >= ((int64_t)1 << 32)) {
+  if (ep.a_rows && (int64_t)a_rows_bound * lda * 2 >= ((int64_t)1 << 32)) {
     set_error("gemm: gathered operand of %lld bytes exceeds the 4 GiB the row offsets address",
-              (long long)((int64_t)M * lda * 2));
+              (long long)(a_rows_bound * lda * 2));
     return LORA_E_UNSUPPORTED;
   }
-  const int tiles_m = (int)cdiv(M, GBM), tiles_n = (int)cdiv(N, GBN);
+  const int tiles_m = ep.g_tile ? tiles_m_bound : (int)cdiv(M, GBM), tiles_n = (int)cdiv(N, GBN);
+  if (tiles_m <= 0) return LORA_OK;
   if (group_m <= 0) group_m = pick_group_m(tiles_m);
   if (group_m > tiles_m) group_m = tiles_m;
   const size_t lds = 0;  // operand tiles are static LDS objects
@@ -487,13 +519,20 @@ lora_status gemm_nt_bf16(const uint16_t* A, const uint16_t* B, uint16_t* C, int 
   return launch_gemm<EPI_BF16>(A, B, M, N, K, lda, ldb, ep, s, group_m);
 }
 
-lora_status gemm_nt_lora(const uint16_t* A, const uint16_t* B, uint16_t* C, int M, int N, int K,
-                         int64_t lda, int64_t ldb, int64_t ldc, const LoraFuse& f, hipStream_t s,
+lora_status gemm_nt_rows(const uint16_t* A, const uint16_t* B, uint16_t* C, int M, int N, int K,
+                         int64_t lda, int64_t ldb, int64_t ldc, const GemmRows& f, hipStream_t s,
                          int group_m) {
   GemmEpi ep{};
   ep.C = C;
   ep.ldc = ldc;
-  ep.perm = f.perm;
+  ep.a_rows = f.a_rows;
+  ep.c_rows = f.c_rows;
+  ep.rowscale = f.rowscale;
+  ep.g_tile = f.g_tile;
+  ep.g_off = f.g_off;
+  ep.g_stride = f.g_stride;
+  ep.n_groups = f.n_groups;
+  ep.ldb_group = f.ldb_group;
   ep.vec = f.vec;
   ep.vec_plane = f.vec_plane;
   ep.vec_ld = f.vec_ld;
@@ -502,7 +541,8 @@ lora_status gemm_nt_lora(const uint16_t* A, const uint16_t* B, uint16_t* C, int 
   ep.desc = f.desc;
   ep.adpos = f.adpos;
   ep.n_ad = f.n_ad;
-  return launch_gemm<EPI_BF16>(A, B, M, N, K, lda, ldb, ep, s, group_m);
+  return launch_gemm<EPI_BF16>(A, B, M, N, K, lda, ldb, ep, s, group_m, f.a_rows_bound,
+                               f.tiles_m_bound);
 }
 
 lora_status gemm_nt_lse(const uint16_t* A, const uint16_t* B, int M, int N, int K, int64_t lda,

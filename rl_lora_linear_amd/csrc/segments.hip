@@ -43,25 +43,39 @@ __global__ void seg_zero_kernel(int32_t* __restrict__ p, int64_t n) {
 }
 
 // One thread per key: exclusive prefix of the key's chunk counts (in place)
-// and its total.  With descriptors, also decide whether adapter k is usable:
-// rank 8..64, a multiple of 8 and <= max_rank; offsets non-negative,
-// 8-element aligned and inside the packs.  Unusable adapters set
-// LORA_FLAG_BAD_DESC and are treated as having no tokens by the LoRA kernels.
+// and its total.  With descriptor tables, also decide whether key k is
+// usable: in every table, rank 8..64, a multiple of 8 and <= max_rank;
+// offsets non-negative, 8-element aligned and inside the packs.  A rank of 0
+// marks "no adapter" (inactive, no flag); other unusable entries set
+// LORA_FLAG_BAD_DESC.  Inactive keys are treated as having no tokens by the
+// LoRA kernels.
+struct SegTabs {
+  lora_host::SegDescs tab[3];
+  int32_t n_tabs;
+};
+
 __global__ void seg_keyscan_kernel(int32_t* __restrict__ hist, int n_keys, int n_chunks,
-                                   int32_t* __restrict__ totals,
-                                   const lora_adapter_desc* __restrict__ desc, int64_t d_in,
-                                   int64_t d_out, int64_t a_elems, int64_t b_elems, int max_rank,
+                                   int32_t* __restrict__ totals, SegTabs tabs, int max_rank,
                                    uint8_t* __restrict__ active, int32_t* status) {
   const int k = blockIdx.x * blockDim.x + threadIdx.x;
   if (k > n_keys) return;
-  if (desc && k < n_keys) {
-    const lora_adapter_desc d = desc[k];
-    const int64_t r = d.rank;
-    bool ok = r >= 8 && r <= 64 && (r % 8) == 0 && r <= max_rank && d.a_off >= 0 &&
-              d.b_off >= 0 && (d.a_off % 8) == 0 && (d.b_off % 8) == 0 &&
-              d.a_off + r * d_in <= a_elems && d.b_off + d_out * r <= b_elems;
-    if (!ok) set_flag(status, LORA_FLAG_BAD_DESC);
-    active[k] = ok ? 1 : 0;
+  if (tabs.n_tabs > 0 && k < n_keys) {
+    bool on = true;
+    for (int i = 0; i < tabs.n_tabs; ++i) {
+      const lora_host::SegDescs& t = tabs.tab[i];
+      const lora_adapter_desc d = t.desc[k];
+      const int64_t r = d.rank;
+      if (r == 0) {
+        on = false;
+        continue;
+      }
+      const bool ok = r >= 8 && r <= 64 && (r % 8) == 0 && r <= max_rank && d.a_off >= 0 &&
+                      d.b_off >= 0 && (d.a_off % 8) == 0 && (d.b_off % 8) == 0 &&
+                      d.a_off + r * t.d_in <= t.a_elems && d.b_off + t.d_out * r <= t.b_elems;
+      if (!ok) set_flag(status, LORA_FLAG_BAD_DESC);
+      on = on && ok;
+    }
+    active[k] = on ? 1 : 0;
   }
   int32_t* row = hist + (int64_t)k * n_chunks;
   int32_t run = 0;
@@ -140,7 +154,8 @@ __global__ __launch_bounds__(1024) void seg_offsets_kernel(const int32_t* __rest
 __global__ __launch_bounds__(SEG_CHUNK) void seg_scatter_kernel(
     const int32_t* __restrict__ ids, int64_t n, int n_keys, const int32_t* __restrict__ hist,
     int n_chunks, const int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
-    const uint8_t* __restrict__ active, int32_t* __restrict__ adpos) {
+    const uint8_t* __restrict__ active, int32_t* __restrict__ adpos, int row_div,
+    int32_t* __restrict__ tokrow, int32_t* __restrict__ inv) {
   __shared__ int32_t k_s[SEG_CHUNK];
   const int c = blockIdx.x;
   const int64_t t = (int64_t)c * SEG_CHUNK + threadIdx.x;
@@ -158,6 +173,31 @@ __global__ __launch_bounds__(SEG_CHUNK) void seg_scatter_kernel(
                        hist[(int64_t)key * n_chunks + c];
   perm[base + rank] = (int32_t)t;
   if (adpos) adpos[base + rank] = (key < n_keys && (!active || active[key])) ? key : -1;
+  if (row_div > 0) {
+    tokrow[base + rank] = (int32_t)(t / row_div);
+    inv[t] = base + rank;
+  }
+}
+
+// One block: gpre[g] = sum over groups g' < g of ceil(rows of g' / 256), where
+// group g is keys [g*group, (g+1)*group).  n_groups <= 1024.
+__global__ __launch_bounds__(1024) void seg_group_tiles_kernel(const int32_t* __restrict__ offsets,
+                                                               int group, int n_groups,
+                                                               int32_t* __restrict__ gpre) {
+  __shared__ int32_t s_v[1024];
+  const int g = threadIdx.x;
+  int32_t v = 0;
+  if (g < n_groups) v = (offsets[(g + 1) * group] - offsets[g * group] + 255) / 256;
+  s_v[g] = v;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int32_t x = g >= o ? s_v[g - o] : 0;
+    __syncthreads();
+    s_v[g] += x;
+    __syncthreads();
+  }
+  if (g < n_groups) gpre[g + 1] = s_v[g];
+  if (g == 0) gpre[0] = 0;
 }
 
 }  // namespace lora
@@ -199,11 +239,14 @@ lora_status run_segments(const int32_t* ids, int64_t n, int32_t n_keys, int32_t 
     lora_status st = launch_check("seg_zero");
     if (st) return st;
   }
+  SegTabs tabs{};
+  if (ex) {
+    tabs.n_tabs = ex->n_tabs;
+    for (int i = 0; i < ex->n_tabs; ++i) tabs.tab[i] = ex->tab[i];
+  }
   hipLaunchKernelGGL(seg_keyscan_kernel, dim3((unsigned)cdiv(n_keys + 1, 256)), dim3(256), 0, s,
-                     hist, n_keys, (int)chunks, totals, ex ? ex->desc : nullptr,
-                     ex ? ex->d_in : 0, ex ? ex->d_out : 0, ex ? ex->a_elems : 0,
-                     ex ? ex->b_elems : 0, ex ? ex->max_rank : 0, ex ? ex->active : nullptr,
-                     status);
+                     hist, n_keys, (int)chunks, totals, tabs, ex ? ex->max_rank : 0,
+                     ex ? ex->active : nullptr, status);
   lora_status st = launch_check("seg_keyscan");
   if (st) return st;
   Tilings tl{};
@@ -212,14 +255,21 @@ lora_status run_segments(const int32_t* ids, int64_t n, int32_t n_keys, int32_t 
     tl.pre[i] = ex ? ex->pre[i] : nullptr;
   }
   hipLaunchKernelGGL(seg_offsets_kernel, dim3(1), dim3(1024), 0, s, totals, n_keys, offsets,
-                     (ex && ex->desc) ? ex->active : nullptr, tl);
+                     (ex && ex->n_tabs > 0) ? ex->active : nullptr, tl);
   st = launch_check("seg_offsets");
   if (st) return st;
   if (n > 0) {
     hipLaunchKernelGGL(seg_scatter_kernel, dim3((unsigned)chunks), dim3(SEG_CHUNK), 0, s, ids, n,
                        n_keys, hist, (int)chunks, offsets, perm,
-                       (ex && ex->desc) ? ex->active : nullptr, ex ? ex->adpos : nullptr);
+                       (ex && ex->n_tabs > 0) ? ex->active : nullptr, ex ? ex->adpos : nullptr,
+                       ex ? ex->row_div : 0, ex ? ex->tokrow : nullptr, ex ? ex->inv : nullptr);
     st = launch_check("seg_scatter");
+    if (st) return st;
+  }
+  if (ex && ex->gpre) {
+    hipLaunchKernelGGL(seg_group_tiles_kernel, dim3(1), dim3(1024), 0, s, offsets, ex->group,
+                       ex->n_groups, ex->gpre);
+    st = launch_check("seg_group_tiles");
   }
   return st;
 }

@@ -89,10 +89,18 @@ __device__ __forceinline__ void wait_vm_barrier() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(VM) : "memory");
 }
 
+// Row maps of a shrink: position p reads input row in[p] and writes output
+// row out[p] (identity when null); rowscale[p] (nullable) multiplies s_a.
+struct ShrinkRows {
+  const int32_t* in;
+  const int32_t* out;
+  const float* rowscale;
+};
+
 template <int NB>
 __device__ __forceinline__ void shrink_tile(const uint16_t* __restrict__ in, int64_t ld_in, int K,
                                             const uint16_t* __restrict__ mat, int r, float scale,
-                                            const int32_t* __restrict__ perm, int p0, int rows,
+                                            const ShrinkRows rm, int p0, int rows,
                                             uint4* lds, uint16_t* __restrict__ out, int64_t plane,
                                             int r_max) {
   constexpr int MSLOTS = NB * 16 * 16;                 // factor tile slots per stage
@@ -108,7 +116,8 @@ __device__ __forceinline__ void shrink_tile(const uint16_t* __restrict__ in, int
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int row = (wave * 2 + i) * 4 + (lane >> 4);
-    const int t = perm[p0 + (row < rows ? row : 0)];
+    const int pr = p0 + (row < rows ? row : 0);
+    const int t = rm.in ? rm.in[pr] : pr;
     xchunk[i] = (lane & 15) ^ (row & 15);
     xsrc[i] = in + (int64_t)t * ld_in;
   }
@@ -186,6 +195,8 @@ __device__ __forceinline__ void shrink_tile(const uint16_t* __restrict__ in, int
   for (int e = tid; e < SH_TM * (r_max / 4); e += 256) {
     const int row = e / (r_max / 4), cg = (e % (r_max / 4)) * 4;
     if (row >= rows) continue;
+    const int prow = p0 + row;
+    const float sc_row = rm.rowscale ? scale * rm.rowscale[prow] : scale;
     float v[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -196,12 +207,12 @@ __device__ __forceinline__ void shrink_tile(const uint16_t* __restrict__ in, int
         sacc += red[(2 * SH_TM + row) * 64 + c];
         sacc += red[(3 * SH_TM + row) * 64 + c];
       }
-      v[q] = scale * sacc;
+      v[q] = sc_row * sacc;
     }
     uint32_t h01, l01, h23, l23;
     split2_bf16(v[0], v[1], h01, l01);
     split2_bf16(v[2], v[3], h23, l23);
-    uint16_t* o = out + (int64_t)perm[p0 + row] * r_max + cg;
+    uint16_t* o = out + (int64_t)(rm.out ? rm.out[prow] : prow) * r_max + cg;
     *(uint2*)o = make_uint2(h01, h23);
     *(uint2*)(o + plane) = make_uint2(l01, l23);
   }
@@ -213,7 +224,7 @@ __device__ __forceinline__ void shrink_tile(const uint16_t* __restrict__ in, int
 __global__ __launch_bounds__(256) void shrink_kernel(
     const uint16_t* __restrict__ in, int64_t ld_in, int K, const uint16_t* __restrict__ mat_pack,
     int use_b_off, const lora_adapter_desc* __restrict__ desc, const int32_t* __restrict__ adpos,
-    const int32_t* __restrict__ perm, const int32_t* __restrict__ offsets,
+    const ShrinkRows rm, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ pre32, int n_ad, int64_t n_tokens, uint16_t* __restrict__ out,
     int r_max, uint4* __restrict__ zero) {
   extern __shared__ uint4 sh_lds[];
@@ -229,16 +240,17 @@ __global__ __launch_bounds__(256) void shrink_kernel(
     const int nb = (r + 15) / 16;
     const float sc = d.scale;
     __syncthreads();   // the previous item's LDS reads are done before the ring refills
-    if (nb == 1) shrink_tile<1>(in, ld_in, K, mat, r, sc, perm, ti.p0, ti.rows, sh_lds, out, plane, r_max);
-    else if (nb == 2) shrink_tile<2>(in, ld_in, K, mat, r, sc, perm, ti.p0, ti.rows, sh_lds, out, plane, r_max);
-    else if (nb == 3) shrink_tile<3>(in, ld_in, K, mat, r, sc, perm, ti.p0, ti.rows, sh_lds, out, plane, r_max);
-    else shrink_tile<4>(in, ld_in, K, mat, r, sc, perm, ti.p0, ti.rows, sh_lds, out, plane, r_max);
+    if (nb == 1) shrink_tile<1>(in, ld_in, K, mat, r, sc, rm, ti.p0, ti.rows, sh_lds, out, plane, r_max);
+    else if (nb == 2) shrink_tile<2>(in, ld_in, K, mat, r, sc, rm, ti.p0, ti.rows, sh_lds, out, plane, r_max);
+    else if (nb == 3) shrink_tile<3>(in, ld_in, K, mat, r, sc, rm, ti.p0, ti.rows, sh_lds, out, plane, r_max);
+    else shrink_tile<4>(in, ld_in, K, mat, r, sc, rm, ti.p0, ti.rows, sh_lds, out, plane, r_max);
   }
   if (blockIdx.x == 0 && zero != nullptr && tid < 16) zero[tid] = make_uint4(0, 0, 0, 0);
   for (int64_t p = (int64_t)blockIdx.x * 256 + tid; p < n_tokens; p += (int64_t)gridDim.x * 256) {
     if (adpos[p] >= 0) continue;
-    uint4* o = (uint4*)(out + (int64_t)perm[p] * r_max);
-    uint4* ol = (uint4*)(out + plane + (int64_t)perm[p] * r_max);
+    const int64_t orow = rm.out ? rm.out[p] : p;
+    uint4* o = (uint4*)(out + orow * r_max);
+    uint4* ol = (uint4*)(out + plane + orow * r_max);
     for (int c = 0; c < r_max / 8; ++c) o[c] = ol[c] = make_uint4(0, 0, 0, 0);
   }
 }
@@ -297,8 +309,8 @@ template <int NCB, int MODE, int PN>
 __device__ __forceinline__ void grad_tile(const uint16_t* __restrict__ P, int64_t plane, int r_max,
                                           const uint16_t* __restrict__ zero,
                                           const uint16_t* __restrict__ Q, int64_t ld_q, int D,
-                                          const int32_t* tok_s, int rows, int j0, uint4* lds,
-                                          f32x4 (&acc)[4][4]) {
+                                          const int32_t* tok_s, int p_base, int rows, int j0,
+                                          uint4* lds, f32x4 (&acc)[4][4]) {
   using G = GrP<PN>;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int KT = (rows + GR_TT - 1) / GR_TT;
@@ -333,7 +345,9 @@ __device__ __forceinline__ void grad_tile(const uint16_t* __restrict__ P, int64_
     for (int i = 0; i < GR_QDMA; ++i) qt[i] = tok_s[min(t0 + qrow[i], rows - 1)];
 #pragma unroll
     for (int i = 0; i < PN; ++i) {
-      const int tp = tok_s[min(t0 + prow[i], rows - 1)];   // unconditional read: no branch
+      // P row: the chunk's token (tok_s) or, with p_base >= 0, the position itself
+      const int tp = p_base >= 0 ? p_base + min(t0 + prow[i], rows - 1)
+                                 : tok_s[min(t0 + prow[i], rows - 1)];   // unconditional: no branch
       pt[i] = t0 + prow[i] < rows ? tp : -1;
     }
 #pragma unroll
@@ -410,14 +424,15 @@ template <int MODE, int PN>
 __device__ __forceinline__ void grad_item(
     const uint16_t* __restrict__ P, int64_t plane, int r_max, const uint16_t* __restrict__ zero,
     const uint16_t* __restrict__ Q, int64_t ld_q, int D,
-    const lora_adapter_desc* __restrict__ desc, const int32_t* __restrict__ perm,
+    const lora_adapter_desc* __restrict__ desc, const int32_t* __restrict__ q_rows, int p_ident,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ chunk_pre, int n_ad,
     float* __restrict__ out_pack, float* __restrict__ partial, int accumulate, int slot, int j0,
     int32_t* tok_s, uint4* gr_lds) {
   TileInfo ti;
   tile_of(chunk_pre, offsets, n_ad, slot, GR_TC, ti);
   __syncthreads();   // every wave is done with the previous item's tokens and ring
-  for (int i = threadIdx.x; i < ti.rows; i += 256) tok_s[i] = perm[ti.p0 + i];
+  for (int i = threadIdx.x; i < ti.rows; i += 256) tok_s[i] = q_rows ? q_rows[ti.p0 + i] : ti.p0 + i;
+  const int p_base = p_ident ? ti.p0 : -1;
   __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const lora_adapter_desc d = desc[ti.a];
@@ -431,13 +446,13 @@ __device__ __forceinline__ void grad_item(
     for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int ncb = (r + 15) / 16;
   if (PN == 1) {
-    if (ncb == 1) grad_tile<1, MODE, PN>(P, plane, r_max, zero, Q, ld_q, D, tok_s, ti.rows, j0, gr_lds, acc);
-    else grad_tile<2, MODE, PN>(P, plane, r_max, zero, Q, ld_q, D, tok_s, ti.rows, j0, gr_lds, acc);
+    if (ncb == 1) grad_tile<1, MODE, PN>(P, plane, r_max, zero, Q, ld_q, D, tok_s, p_base, ti.rows, j0, gr_lds, acc);
+    else grad_tile<2, MODE, PN>(P, plane, r_max, zero, Q, ld_q, D, tok_s, p_base, ti.rows, j0, gr_lds, acc);
   } else {
-    if (ncb == 1) grad_tile<1, MODE, PN>(P, plane, r_max, zero, Q, ld_q, D, tok_s, ti.rows, j0, gr_lds, acc);
-    else if (ncb == 2) grad_tile<2, MODE, PN>(P, plane, r_max, zero, Q, ld_q, D, tok_s, ti.rows, j0, gr_lds, acc);
-    else if (ncb == 3) grad_tile<3, MODE, PN>(P, plane, r_max, zero, Q, ld_q, D, tok_s, ti.rows, j0, gr_lds, acc);
-    else grad_tile<4, MODE, PN>(P, plane, r_max, zero, Q, ld_q, D, tok_s, ti.rows, j0, gr_lds, acc);
+    if (ncb == 1) grad_tile<1, MODE, PN>(P, plane, r_max, zero, Q, ld_q, D, tok_s, p_base, ti.rows, j0, gr_lds, acc);
+    else if (ncb == 2) grad_tile<2, MODE, PN>(P, plane, r_max, zero, Q, ld_q, D, tok_s, p_base, ti.rows, j0, gr_lds, acc);
+    else if (ncb == 3) grad_tile<3, MODE, PN>(P, plane, r_max, zero, Q, ld_q, D, tok_s, p_base, ti.rows, j0, gr_lds, acc);
+    else grad_tile<4, MODE, PN>(P, plane, r_max, zero, Q, ld_q, D, tok_s, p_base, ti.rows, j0, gr_lds, acc);
   }
 
   // ---- write.  Region of this adapter: D*r floats.
@@ -484,7 +499,7 @@ template <int MODE, int PN>
 __global__ __launch_bounds__(256) void grad_kernel(
     const uint16_t* __restrict__ P, int64_t plane, int r_max, const uint16_t* __restrict__ zero,
     const uint16_t* __restrict__ Q, int64_t ld_q, int D,
-    const lora_adapter_desc* __restrict__ desc, const int32_t* __restrict__ perm,
+    const lora_adapter_desc* __restrict__ desc, const int32_t* __restrict__ q_rows, int p_ident,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ chunk_pre, int n_ad,
     float* __restrict__ out_pack, float* __restrict__ partial, int accumulate) {
   extern __shared__ uint4 gr_lds[];
@@ -496,7 +511,8 @@ __global__ __launch_bounds__(256) void grad_kernel(
   for (int item = ir.first; item < ir.end; item += ir.step) {
     const int slot = item / ncol;
     const int j0 = (item - slot * ncol) * GR_NJ;
-    grad_item<MODE, PN>(P, plane, r_max, zero, Q, ld_q, D, desc, perm, offsets, chunk_pre, n_ad,
+    grad_item<MODE, PN>(P, plane, r_max, zero, Q, ld_q, D, desc, q_rows, p_ident, offsets,
+                        chunk_pre, n_ad,
                         out_pack, partial, accumulate, slot, j0, tok_s, gr_lds);
   }
 }
@@ -587,9 +603,9 @@ static unsigned persistent_blocks() {
 
 lora_status launch_shrink(const uint16_t* in, int64_t ld_in, int K, const uint16_t* mat_pack,
                           int use_b_off, const lora_adapter_desc* desc, const int32_t* adpos,
-                          const int32_t* perm, const int32_t* offsets, const int32_t* pre32,
-                          int n_ad, int64_t n_tokens, uint16_t* out, int r_max, void* zero,
-                          hipStream_t s) {
+                          const int32_t* in_rows, const int32_t* out_rows, const float* rowscale,
+                          const int32_t* offsets, const int32_t* pre32, int n_ad,
+                          int64_t n_tokens, uint16_t* out, int r_max, void* zero, hipStream_t s) {
   if (n_tokens <= 0) return LORA_OK;
   const int nb_max = (r_max + 15) / 16;
   const size_t ring[4] = {(size_t)sh_nst<1>() * (SH_XSLOTS + 256) * 16,
@@ -605,15 +621,15 @@ lora_status launch_shrink(const uint16_t* in, int64_t ld_in, int K, const uint16
     attr = lds;
   }
   hipLaunchKernelGGL(shrink_kernel, dim3(persistent_blocks()), dim3(256), lds, s, in, ld_in, K,
-                     mat_pack, use_b_off, desc, adpos, perm, offsets, pre32, n_ad, n_tokens, out,
-                     r_max, (uint4*)zero);
+                     mat_pack, use_b_off, desc, adpos, ShrinkRows{in_rows, out_rows, rowscale},
+                     offsets, pre32, n_ad, n_tokens, out, r_max, (uint4*)zero);
   return launch_check("shrink");
 }
 
 template <int MODE, int PN>
 lora_status launch_grad_t(dim3 grid, const uint16_t* P, int64_t plane, int r_max,
                           const uint16_t* zero, const uint16_t* Q, int64_t ld_q, int D,
-                          const lora_adapter_desc* desc, const int32_t* perm,
+                          const lora_adapter_desc* desc, const int32_t* q_rows, int p_ident,
                           const int32_t* offsets, const int32_t* chunk_pre, int n_ad,
                           float* out_pack, float* partial, int accumulate, hipStream_t s) {
   const size_t lds = (size_t)GrP<PN>::NST * GrP<PN>::STAGE * sizeof(uint4);
@@ -624,29 +640,31 @@ lora_status launch_grad_t(dim3 grid, const uint16_t* P, int64_t plane, int r_max
     attr = true;
   }
   hipLaunchKernelGGL((grad_kernel<MODE, PN>), grid, dim3(256), lds, s, P, plane, r_max, zero, Q,
-                     ld_q, D, desc, perm, offsets, chunk_pre, n_ad, out_pack, partial, accumulate);
+                     ld_q, D, desc, q_rows, p_ident, offsets, chunk_pre, n_ad, out_pack, partial,
+                     accumulate);
   return launch_check("grad");
 }
 
 lora_status launch_grad(int mode, const uint16_t* P, int r_max, const void* zero,
                         const uint16_t* Q, int64_t ld_q, int D, const lora_adapter_desc* desc,
-                        const uint8_t* active, const int32_t* perm, const int32_t* offsets,
-                        const int32_t* chunk_pre, int n_ad, int64_t n_tokens, float* out_pack,
-                        float* partial, int accumulate, hipStream_t s) {
+                        const uint8_t* active, const int32_t* q_rows, int p_ident,
+                        const int32_t* offsets, const int32_t* chunk_pre, int n_ad,
+                        int64_t n_tokens, float* out_pack, float* partial, int accumulate,
+                        hipStream_t s) {
   if (n_tokens > 0) {
     dim3 grid(persistent_blocks());
     const int64_t plane = n_tokens * r_max;
     const uint16_t* z = (const uint16_t*)zero;
     lora_status st;
     if (r_max <= 32)
-      st = mode == 0 ? launch_grad_t<0, 1>(grid, P, plane, r_max, z, Q, ld_q, D, desc, perm, offsets,
+      st = mode == 0 ? launch_grad_t<0, 1>(grid, P, plane, r_max, z, Q, ld_q, D, desc, q_rows, p_ident, offsets,
                                            chunk_pre, n_ad, out_pack, partial, accumulate, s)
-                     : launch_grad_t<1, 1>(grid, P, plane, r_max, z, Q, ld_q, D, desc, perm, offsets,
+                     : launch_grad_t<1, 1>(grid, P, plane, r_max, z, Q, ld_q, D, desc, q_rows, p_ident, offsets,
                                            chunk_pre, n_ad, out_pack, partial, accumulate, s);
     else
-      st = mode == 0 ? launch_grad_t<0, 2>(grid, P, plane, r_max, z, Q, ld_q, D, desc, perm, offsets,
+      st = mode == 0 ? launch_grad_t<0, 2>(grid, P, plane, r_max, z, Q, ld_q, D, desc, q_rows, p_ident, offsets,
                                            chunk_pre, n_ad, out_pack, partial, accumulate, s)
-                     : launch_grad_t<1, 2>(grid, P, plane, r_max, z, Q, ld_q, D, desc, perm, offsets,
+                     : launch_grad_t<1, 2>(grid, P, plane, r_max, z, Q, ld_q, D, desc, q_rows, p_ident, offsets,
                                            chunk_pre, n_ad, out_pack, partial, accumulate, s);
     if (st) return st;
   }

@@ -7,20 +7,37 @@ namespace lora_host {
 
 lora_status gemm_nt_bf16(const uint16_t* A, const uint16_t* B, uint16_t* C, int M, int N, int K,
                          int64_t lda, int64_t ldb, int64_t ldc, hipStream_t s, int group_m = 0);
-// Row gather/scatter through perm and the fused LoRA expand of the base GEMM.
-struct LoraFuse {
-  const int32_t* perm;      // segment order -> token
-  const uint16_t* vec;      // per-token scaled vector: bf16 hi plane [tokens][vec_ld],
-  int64_t vec_plane;        // lo plane at vec + vec_plane
-  int vec_ld;
-  int use_b_off;            // factor at b_off (B_a [N][r]) or a_off (A_a^T [N][r])
-  const uint16_t* lmat;
-  const lora_adapter_desc* desc;
-  const int32_t* adpos;     // [tokens] adapter of each segment position, -1 for none
-  int n_ad;
+// Row maps, row groups and the fused LoRA expand of the base GEMM.  Position m
+// (0 <= m < M) reads A row a_rows[m] and writes C row c_rows[m] (identity when
+// null); rowscale[m] scales its base product.  With g_tile set, positions form
+// n_groups consecutive groups (experts), group g = [g_off[g*g_stride],
+// g_off[(g+1)*g_stride]) with its own B at B + g*ldb_group, tiled from
+// g_tile[g]; tiles_m_bound bounds g_tile[n_groups].  With vec set, the expand
+// adds (s u) . M_a^T from the bf16 hi/lo planes (lo at vec + vec_plane, row
+// c_rows[m]) and the factor M_a at (use_b_off ? b_off : a_off) of lmat, for
+// a = adpos[m] (-1: none).
+struct GemmRows {
+  const int32_t* a_rows = nullptr;
+  int64_t a_rows_bound = 0;   // rows of A (checks the 32-bit gather offsets)
+  const int32_t* c_rows = nullptr;
+  const float* rowscale = nullptr;
+  const int32_t* g_tile = nullptr;
+  const int32_t* g_off = nullptr;
+  int g_stride = 1;
+  int n_groups = 0;
+  int64_t ldb_group = 0;
+  int tiles_m_bound = 0;
+  const uint16_t* vec = nullptr;
+  int64_t vec_plane = 0;
+  int vec_ld = 0;
+  int use_b_off = 0;
+  const uint16_t* lmat = nullptr;
+  const lora_adapter_desc* desc = nullptr;
+  const int32_t* adpos = nullptr;
+  int n_ad = 0;
 };
-lora_status gemm_nt_lora(const uint16_t* A, const uint16_t* B, uint16_t* C, int M, int N, int K,
-                         int64_t lda, int64_t ldb, int64_t ldc, const LoraFuse& f, hipStream_t s,
+lora_status gemm_nt_rows(const uint16_t* A, const uint16_t* B, uint16_t* C, int M, int N, int K,
+                         int64_t lda, int64_t ldb, int64_t ldc, const GemmRows& f, hipStream_t s,
                          int group_m = 0);
 lora_status gemm_nt_lse(const uint16_t* A, const uint16_t* B, int M, int N, int K, int64_t lda,
                         int64_t ldb, float* part_m, float* part_s, float* zt,
@@ -29,16 +46,23 @@ lora_status gemm_nt_grad(const uint16_t* A, const uint16_t* B, uint16_t* G, int6
                          int N, int K, int64_t lda, int64_t ldb, const int32_t* targets,
                          const float* lse, const float* dlogp, hipStream_t s, int group_m = 0);
 
+// out[out_rows[p]] = bf16 hi/lo planes of s_a * rowscale[p] * (M_a in[in_rows[p]])
+// over positions p < n_tokens (row maps and rowscale nullable); rows of
+// positions without an adapter are zeroed, and `zero` (256 B, nullable) too.
 lora_status launch_shrink(const uint16_t* in, int64_t ld_in, int K, const uint16_t* mat_pack,
                           int use_b_off, const lora_adapter_desc* desc, const int32_t* adpos,
-                          const int32_t* perm, const int32_t* offsets, const int32_t* pre32,
-                          int n_ad, int64_t n_tokens, uint16_t* out, int r_max, void* zero,
-                          hipStream_t s);
+                          const int32_t* in_rows, const int32_t* out_rows, const float* rowscale,
+                          const int32_t* offsets, const int32_t* pre32, int n_ad,
+                          int64_t n_tokens, uint16_t* out, int r_max, void* zero, hipStream_t s);
+// Per key a: T_a = sum over a's positions p of P[p_row] Q[q_rows[p]]^T (mode 0:
+// [D][r] at b_off; mode 1: [r][D] at a_off), P the bf16 hi/lo planes.  P row:
+// the position itself with p_ident, else q_rows[p].  q_rows nullable.
 lora_status launch_grad(int mode, const uint16_t* P, int r_max, const void* zero,
                         const uint16_t* Q, int64_t ld_q, int D, const lora_adapter_desc* desc,
-                        const uint8_t* active, const int32_t* perm, const int32_t* offsets,
-                        const int32_t* chunk_pre, int n_ad, int64_t n_tokens, float* out_pack,
-                        float* partial, int accumulate, hipStream_t s);
+                        const uint8_t* active, const int32_t* q_rows, int p_ident,
+                        const int32_t* offsets, const int32_t* chunk_pre, int n_ad,
+                        int64_t n_tokens, float* out_pack, float* partial, int accumulate,
+                        hipStream_t s);
 int64_t grad_partial_floats(int64_t n_tokens, int n_ad, int64_t D, int r_max);
 lora_status launch_adapter_transpose(const uint16_t* A_pack, const uint16_t* B_pack,
                                      const lora_adapter_desc* desc, const uint8_t* active,
@@ -68,5 +92,20 @@ lora_status launch_swiglu_bwd(int64_t n, const uint16_t* dh, const uint16_t* g,
 lora_status launch_transpose_bf16(const uint16_t* src, uint16_t* dst, int64_t rows, int64_t cols,
                                   hipStream_t s);
 lora_status launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
+
+// moe.hip
+lora_status launch_moe_route(const float* logits, int64_t n, int E, int K, int32_t* experts,
+                             float* weights, hipStream_t s);
+lora_status launch_moe_keys(const int32_t* experts, const int32_t* ids, int64_t n_assign, int K,
+                            int E, int n_ad, int32_t* keys, int32_t* status, hipStream_t s);
+lora_status launch_moe_desc(const lora_adapter_desc* const src[3], lora_adapter_desc* const dst[3],
+                            int E, int n_ad, hipStream_t s);
+lora_status launch_moe_gather_w(const float* w, const int32_t* perm, int64_t n, float* wpos,
+                                hipStream_t s);
+lora_status launch_moe_combine(const uint16_t* a, const uint16_t* b, const float* w,
+                               const int32_t* inv, const int32_t* keys, int64_t n_tok, int K,
+                               int64_t H, uint16_t* out, hipStream_t s);
+lora_status launch_planes_scale(const uint16_t* src, const float* wpos, int64_t n, int R,
+                                uint16_t* dst, hipStream_t s);
 
 }  // namespace lora_host

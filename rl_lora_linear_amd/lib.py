@@ -31,7 +31,8 @@ EXPORTS = [
     "lora_backward", "token_logprobs_workspace_bytes", "token_logprobs",
     "token_logprobs_backward_workspace_bytes", "token_logprobs_backward",
     "loss_grad_workspace_bytes", "loss_grad", "adam_step", "adam_step_multi", "swiglu_forward",
-    "swiglu_backward",
+    "swiglu_backward", "moe_route", "moe_workspace_bytes", "moe_saved_bytes", "moe_forward",
+    "moe_backward",
     "lora_timing_enable", "lora_timing_reset", "lora_timing_read",
 ]
 
@@ -47,6 +48,14 @@ class LoraShape(ctypes.Structure):
                 ("a_pack_elems", ctypes.c_int64), ("b_pack_elems", ctypes.c_int64),
                 ("n_adapters", ctypes.c_int32), ("max_rank", ctypes.c_int32),
                 ("order", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class MoeShape(ctypes.Structure):
+    _fields_ = [("n_tokens", ctypes.c_int64), ("hidden", ctypes.c_int64), ("d_ff", ctypes.c_int64),
+                ("gate_pack_elems", ctypes.c_int64), ("up_pack_elems", ctypes.c_int64),
+                ("down_pack_elems", ctypes.c_int64), ("n_experts", ctypes.c_int32),
+                ("top_k", ctypes.c_int32), ("n_adapters", ctypes.c_int32),
+                ("max_rank", ctypes.c_int32)]
 
 
 class AdamSegment(ctypes.Structure):
@@ -93,6 +102,11 @@ def _load() -> ctypes.CDLL:
         "adam_step_multi": (_I32, [_I32, ctypes.POINTER(AdamSegment), _P, _P, _P, _P, _F, _F, _F, _F,
                                    _F, _P, _P]),
         "swiglu_forward": (_I32, [_I64, _P, _P, _P, _P]),
+        "moe_route": (_I32, [_I64, _I32, _I32, _P, _P, _P, _P]),
+        "moe_workspace_bytes": (_SZ, [ctypes.POINTER(MoeShape)]),
+        "moe_saved_bytes": (_SZ, [ctypes.POINTER(MoeShape)]),
+        "moe_forward": (_I32, [ctypes.POINTER(MoeShape)] + [_P] * 16 + [_SZ, _P]),
+        "moe_backward": (_I32, [ctypes.POINTER(MoeShape)] + [_P] * 19 + [_I32, _P, _P, _SZ, _P]),
         "swiglu_backward": (_I32, [_I64, _P, _P, _P, _P, _P, _P]),
         "lora_timing_enable": (None, [_I32]),
         "lora_timing_reset": (None, []),
@@ -251,6 +265,44 @@ def adam_step_multi(segments, p, g, m, v, lr, beta1=0.9, beta2=0.999, eps=1e-8,
     arr = (AdamSegment * max(1, len(segments)))(*[AdamSegment(int(o), int(c), int(t)) for o, c, t in segments])
     _check(LIB.adam_step_multi(len(segments), arr, _ptr(p), _ptr(g), _ptr(m), _ptr(v), lr, beta1,
                                beta2, eps, weight_decay, _ptr(p_bf16), _stream(stream)))
+
+
+def moe_route(logits, top_k, experts, weights, stream=None):
+    n, E = logits.shape
+    _check(LIB.moe_route(n, E, top_k, _ptr(logits), _ptr(experts), _ptr(weights), _stream(stream)))
+
+
+def moe_workspace_bytes(shape: MoeShape) -> int:
+    n = LIB.moe_workspace_bytes(ctypes.byref(shape))
+    if n == 0:
+        raise LoraError(LORA_E_INVALID_ARG, LIB.lora_last_error().decode())
+    return n
+
+
+def moe_saved_bytes(shape: MoeShape) -> int:
+    n = LIB.moe_saved_bytes(ctypes.byref(shape))
+    if n == 0:
+        raise LoraError(LORA_E_INVALID_ARG, LIB.lora_last_error().decode())
+    return n
+
+
+def moe_forward(shape, x, experts, weights, ids, W_gate, W_up, W_down, packs, descs, y, saved, ws,
+                stream=None):
+    """packs, descs: (gate, up, down) triples."""
+    _check(LIB.moe_forward(ctypes.byref(shape), _ptr(x), _ptr(experts), _ptr(weights), _ptr(ids),
+                           _ptr(W_gate), _ptr(W_up), _ptr(W_down), *[_ptr(p) for p in packs],
+                           *[_ptr(d) for d in descs], _ptr(y), _ptr(saved), _ptr(ws), _nbytes(ws),
+                           _stream(stream)))
+
+
+def moe_backward(shape, dy, x, experts, weights, ids, W_gate_t, W_up_t, W_down_t, packs, descs,
+                 saved, dx, grads, accumulate, ws, trace=None, stream=None):
+    """packs, descs, grads: (gate, up, down) triples; trace: optional bf16 [3][N*K][F]."""
+    _check(LIB.moe_backward(ctypes.byref(shape), _ptr(dy), _ptr(x), _ptr(experts), _ptr(weights),
+                            _ptr(ids), _ptr(W_gate_t), _ptr(W_up_t), _ptr(W_down_t),
+                            *[_ptr(p) for p in packs], *[_ptr(d) for d in descs], _ptr(saved),
+                            _ptr(dx), *[_ptr(g) for g in grads], int(accumulate), _ptr(trace),
+                            _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
 def swiglu_forward(gate, up, h, stream=None):
