@@ -60,6 +60,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target wall time of the oracle sample")
+    ap.add_argument("--workload", default="qo_proj", choices=["qo_proj", "mlp", "logprob", "moe"],
+                    help="qo_proj (default): the q/o projection step the headline metric is "
+                         "quoted on; mlp / logprob / moe: the other workloads, one JSON line each "
+                         "(no CPU baseline)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
                     help="only run a plain device copy of MB megabytes 5 times (calibrates "
                          "the FETCH_SIZE / WRITE_SIZE counters against known bytes) and exit")
@@ -132,6 +136,16 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "launches": 5}))
+        return
+
+    if args.workload != "qo_proj":
+        import rl_lora_linear_amd.workload_bench as WB
+        torch.cuda.set_device(0)
+        out = getattr(WB, args.workload)(args.steps, args.warmup, log)
+        out.update({"n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                    "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+                    "dtype": "bf16", "data": "synthetic (seeded, generated on the device)"})
+        print(json.dumps(out), flush=True)
         return
 
     import rl_lora_linear_amd.lib as L

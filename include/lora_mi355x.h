@@ -294,6 +294,10 @@ lora_status swiglu_forward(int64_t n, const uint16_t* gate, const uint16_t* up, 
 /* dg = dh * u * silu'(g), du = dh * silu(g). */
 lora_status swiglu_backward(int64_t n, const uint16_t* dh, const uint16_t* gate,
                             const uint16_t* up, uint16_t* dgate, uint16_t* dup, void* stream);
+/* out = a + b elementwise (bf16 in, fp32 sum, one round-to-nearest-even): the
+ * MLP's dx is the sum of the gate and up projections' dx.  out may alias a or b. */
+lora_status bf16_add(int64_t n, const uint16_t* a, const uint16_t* b, uint16_t* out,
+                     void* stream);
 
 /* ---- routed experts (mixture-of-experts layer) ------------------------ */
 

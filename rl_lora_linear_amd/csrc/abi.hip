@@ -695,7 +695,10 @@ lora_status moe_project(const moe_shape& sh, const MoeWs& w, const uint16_t* A,
   f.desc = desc;
   f.adpos = w.adpos;
   f.n_ad = sh.n_experts * (sh.n_adapters + 1);
-  return gemm_nt_rows(A, W, C, (int)NK, (int)n_out, (int)k_in, k_in, k_in, n_out, f, s);
+  timer_begin(LORA_TIMER_BASE_GEMM, s);
+  TRY(gemm_nt_rows(A, W, C, (int)NK, (int)n_out, (int)k_in, k_in, k_in, n_out, f, s));
+  timer_end(LORA_TIMER_BASE_GEMM, s);
+  return LORA_OK;
 }
 
 }  // namespace
@@ -851,6 +854,14 @@ lora_status moe_backward(const moe_shape* shape, const uint16_t* dy, const uint1
                     w.offsets, w.prec, n_keys, NK, grads[i], w.partial, accumulate, s));
   }
   return launch_moe_combine(w.dxg, w.dxu, nullptr, w.inv, w.keys, sh.n_tokens, sh.top_k, H, dx, s);
+}
+
+lora_status bf16_add(int64_t n, const uint16_t* a, const uint16_t* b, uint16_t* out,
+                     void* stream) {
+  LORA_ARG_CHECK(n >= 0 && (n == 0 || (a && b && out)), "bad bf16_add arguments");
+  LORA_ARG_CHECK(n == 0 || (aligned16(a) && aligned16(b) && aligned16(out)),
+                 "bf16_add buffers must be 16-byte aligned");
+  return launch_add_bf16(n, a, b, out, S(stream));
 }
 
 // ------------------------------------------------------------------ timing

@@ -413,6 +413,33 @@ lora_status launch_swiglu_bwd(int64_t n, const uint16_t* dh, const uint16_t* g,
   return launch_check("swiglu_bwd");
 }
 
+// out = bf16(a + b), the sum taken in fp32 (one rounding); 8 elements per step.
+__global__ __launch_bounds__(256) void add_bf16_kernel(int64_t n, const uint16_t* __restrict__ a,
+                                                       const uint16_t* __restrict__ b,
+                                                       uint16_t* __restrict__ out) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t n8 = n / 8;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8; i += stride) {
+    const uint4 x = ((const uint4*)a)[i], y = ((const uint4*)b)[i];
+    const uint32_t wx[4] = {x.x, x.y, x.z, x.w}, wy[4] = {y.x, y.y, y.z, y.w};
+    uint32_t r[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      r[q] = pack2bf(bf2f_lo(wx[q]) + bf2f_lo(wy[q]), bf2f_hi(wx[q]) + bf2f_hi(wy[q]));
+    ((uint4*)out)[i] = make_uint4(r[0], r[1], r[2], r[3]);
+  }
+  for (int64_t e = n8 * 8 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += stride)
+    out[e] = f2bf(bf2f(a[e]) + bf2f(b[e]));
+}
+
+lora_status launch_add_bf16(int64_t n, const uint16_t* a, const uint16_t* b, uint16_t* out,
+                            hipStream_t s) {
+  if (n <= 0) return LORA_OK;
+  hipLaunchKernelGGL(add_bf16_kernel, dim3(grid_for(cdiv(n, 8), 256)), dim3(256), 0, s, n, a, b,
+                     out);
+  return launch_check("add_bf16");
+}
+
 lora_status launch_transpose_bf16(const uint16_t* src, uint16_t* dst, int64_t rows, int64_t cols,
                                   hipStream_t s) {
   hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)(cols / 64), (unsigned)(rows / 64)),

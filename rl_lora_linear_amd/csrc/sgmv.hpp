@@ -89,6 +89,8 @@ lora_status launch_swiglu_fwd(int64_t n, const uint16_t* g, const uint16_t* u, u
                               hipStream_t s);
 lora_status launch_swiglu_bwd(int64_t n, const uint16_t* dh, const uint16_t* g,
                               const uint16_t* u, uint16_t* dg, uint16_t* du, hipStream_t s);
+lora_status launch_add_bf16(int64_t n, const uint16_t* a, const uint16_t* b, uint16_t* out,
+                            hipStream_t s);
 lora_status launch_transpose_bf16(const uint16_t* src, uint16_t* dst, int64_t rows, int64_t cols,
                                   hipStream_t s);
 lora_status launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);

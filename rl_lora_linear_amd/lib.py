@@ -31,7 +31,7 @@ EXPORTS = [
     "lora_backward", "token_logprobs_workspace_bytes", "token_logprobs",
     "token_logprobs_backward_workspace_bytes", "token_logprobs_backward",
     "loss_grad_workspace_bytes", "loss_grad", "adam_step", "adam_step_multi", "swiglu_forward",
-    "swiglu_backward", "moe_route", "moe_workspace_bytes", "moe_saved_bytes", "moe_forward",
+    "swiglu_backward", "bf16_add", "moe_route", "moe_workspace_bytes", "moe_saved_bytes", "moe_forward",
     "moe_backward",
     "lora_timing_enable", "lora_timing_reset", "lora_timing_read",
 ]
@@ -102,6 +102,7 @@ def _load() -> ctypes.CDLL:
         "adam_step_multi": (_I32, [_I32, ctypes.POINTER(AdamSegment), _P, _P, _P, _P, _F, _F, _F, _F,
                                    _F, _P, _P]),
         "swiglu_forward": (_I32, [_I64, _P, _P, _P, _P]),
+        "bf16_add": (_I32, [_I64, _P, _P, _P, _P]),
         "moe_route": (_I32, [_I64, _I32, _I32, _P, _P, _P, _P]),
         "moe_workspace_bytes": (_SZ, [ctypes.POINTER(MoeShape)]),
         "moe_saved_bytes": (_SZ, [ctypes.POINTER(MoeShape)]),
@@ -265,6 +266,10 @@ def adam_step_multi(segments, p, g, m, v, lr, beta1=0.9, beta2=0.999, eps=1e-8,
     arr = (AdamSegment * max(1, len(segments)))(*[AdamSegment(int(o), int(c), int(t)) for o, c, t in segments])
     _check(LIB.adam_step_multi(len(segments), arr, _ptr(p), _ptr(g), _ptr(m), _ptr(v), lr, beta1,
                                beta2, eps, weight_decay, _ptr(p_bf16), _stream(stream)))
+
+
+def bf16_add(a, b, out, stream=None):
+    _check(LIB.bf16_add(a.numel(), _ptr(a), _ptr(b), _ptr(out), _stream(stream)))
 
 
 def moe_route(logits, top_k, experts, weights, stream=None):

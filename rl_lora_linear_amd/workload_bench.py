@@ -1,0 +1,239 @@
+"""Timed steps of the MLP, fused-logprob and routed-expert workloads (device
+inputs, seeded and synthetic, generated on the GPU).  Used by bench.py
+--workload; every step runs through the library's C entry points."""
+from __future__ import annotations
+
+import time
+
+import numpy as np
+import torch
+
+from . import lib as L
+
+PEAK_BF16_TFLOPS = 2500.0
+
+
+def _randn(gen, shape, std, dtype=torch.bfloat16):
+    return (torch.randn(shape, generator=gen, device="cuda", dtype=torch.float32) * std).to(dtype)
+
+
+def _timed(step, steps, warmup, log):
+    for k in range(warmup):
+        step(k)
+    torch.cuda.synchronize()
+    L.lora_timing_reset()
+    L.lora_timing_enable(True)
+    log(f"[bench] timing {steps} steps")
+    t0 = time.perf_counter()
+    for k in range(steps):
+        step(k)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    L.lora_timing_enable(False)
+    return (t1 - t0) * 1e3 / steps
+
+
+def _timer(tid):
+    tot, cnt = L.lora_timing_read(tid)
+    return tot / max(cnt, 1), cnt
+
+
+def _pack(gen, ranks, d_in, d_out):
+    """One projection's adapter pack (A_i then B_i per adapter) and its offsets."""
+    a_off, b_off, off = [], [], 0
+    for r in ranks:
+        a_off.append(off)
+        b_off.append(off + r * d_in)
+        off += r * (d_in + d_out)
+    pack = torch.empty(off, dtype=torch.bfloat16, device="cuda")
+    for i, r in enumerate(ranks):
+        pack[a_off[i]:b_off[i]] = ((torch.rand(r * d_in, generator=gen, device="cuda") * 2 - 1)
+                                   / np.sqrt(d_in)).to(torch.bfloat16)
+        pack[b_off[i]:b_off[i] + d_out * r] = _randn(gen, (d_out * r,), 0.01)
+    return pack, np.asarray(a_off), np.asarray(b_off)
+
+
+def mlp(steps, warmup, log, n=32768, d=4096, f=12288, n_ad=64):
+    """SwiGLU MLP, 64 adapters with ranks from {8,16,32,64}, interleaved ids:
+    forward (gate, up, SwiGLU, down) + backward (down, SwiGLU, gate, up, dx sum)."""
+    gen = torch.Generator(device="cuda").manual_seed(3)
+    rng = np.random.default_rng(3)
+    ranks = rng.choice(np.asarray([8, 16, 32, 64]), size=n_ad).astype(np.int32)
+    scales = (32.0 / ranks).astype(np.float32)
+    ids = torch.from_numpy(rng.integers(0, n_ad, size=n).astype(np.int32)).cuda()
+    R = 64
+    proj = {}
+    for name, (di, do) in (("gate", (d, f)), ("up", (d, f)), ("down", (f, d))):
+        Wt = _randn(gen, (do, di), 0.02)
+        Wtt = torch.empty((di, do), dtype=torch.bfloat16, device="cuda")
+        L.lora_transpose_bf16(Wt, Wtt)
+        pack, ao, bo = _pack(gen, ranks, di, do)
+        shape = L.make_shape(n, di, do, pack.numel(), pack.numel(), n_ad, R, L.IDS_INTERLEAVED)
+        proj[name] = dict(W=Wt, Wt=Wtt, pack=pack, desc=L.make_desc(ao, bo, ranks, scales),
+                          shape=shape, ws=L.empty_workspace(L.lora_workspace_bytes(shape)),
+                          u=torch.empty((2, n, R), dtype=torch.bfloat16, device="cuda"),
+                          grad=torch.zeros(pack.numel(), dtype=torch.float32, device="cuda"))
+    xs = [_randn(gen, (n, d), 1.0) for _ in range(2)]
+    dys = [_randn(gen, (n, d), 1.0) for _ in range(2)]
+    g = torch.empty((n, f), dtype=torch.bfloat16, device="cuda")
+    u, h, dh, dg, du = (torch.empty_like(g) for _ in range(5))
+    y = torch.empty((n, d), dtype=torch.bfloat16, device="cuda")
+    dxg, dxu, dx = (torch.empty_like(y) for _ in range(3))
+
+    def fwd(p, x, out):
+        L.lora_forward(p["shape"], x, p["W"], p["pack"], p["pack"], p["desc"], ids, out, p["u"], p["ws"])
+
+    def bwd(p, dyy, x, dxx):
+        L.lora_backward(p["shape"], dyy, x, p["Wt"], p["pack"], p["pack"], p["desc"], ids, p["u"],
+                        dxx, p["grad"], p["grad"], 0, p["ws"])
+
+    def step(k):
+        x, dyy = xs[k % 2], dys[k % 2]
+        fwd(proj["gate"], x, g)
+        fwd(proj["up"], x, u)
+        L.swiglu_forward(g, u, h)
+        fwd(proj["down"], h, y)
+        bwd(proj["down"], dyy, h, dh)
+        L.swiglu_backward(dh, g, u, dg, du)
+        bwd(proj["gate"], dg, x, dxg)
+        bwd(proj["up"], du, x, dxu)
+        L.bf16_add(dxg, dxu, dx)
+
+    log(f"[bench] mlp {n} tokens, d {d}, d_ff {f}, {n_ad} adapters")
+    ms = _timed(step, steps, warmup, log)
+    for p in proj.values():
+        if L.lora_device_status(p["ws"]):
+            raise RuntimeError("device status flags set")
+    gemm_ms, gemm_n = _timer(L.TIMER_BASE_GEMM)
+    flops_launch = 2.0 * n * d * f
+    tf = flops_launch / (gemm_ms / 1e3) / 1e12
+    return {
+        "metric": "tokens/s mixed-adapter LoRA MLP fwd+bwd", "value": round(n / (ms / 1e3), 1),
+        "unit": "tokens/s", "ms_per_step": round(ms, 4),
+        "config": {"workload": f"qwen3-8b MLP gate/up {d}->{f}, down {f}->{d}, {n_ad} adapters "
+                               f"ranks {{8,16,32,64}} alpha 32, {n} tokens interleaved ids, fwd+bwd",
+                   "rank_counts": {int(r): int((ranks == r).sum()) for r in (8, 16, 32, 64)}},
+        "roofline": {"bound": "mfma", "kernel": "base GEMMs (6 per step, 2*N*d*d_ff each)",
+                     "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf / PEAK_BF16_TFLOPS, 4), "avg_ms": round(gemm_ms, 4),
+                     "launches": gemm_n},
+        "kernels": {name: {"avg_ms": round(_timer(t)[0], 5), "launches": _timer(t)[1]}
+                    for name, t in (("shrink", L.TIMER_SHRINK), ("grad", L.TIMER_GRAD))},
+    }
+
+
+def logprob(steps, warmup, log, n_seq=64, seq=256, H=4096, V=151936, chunk=4096):
+    """Fused lm_head logprob + PPO loss + logprob backward, 16 groups x 4 x 256."""
+    gen = torch.Generator(device="cuda").manual_seed(4)
+    n = n_seq * seq
+    hs = [_randn(gen, (n, H), 1.0) for _ in range(2)]
+    U = _randn(gen, (V, H), 0.02)
+    Ut = torch.empty((H, V), dtype=torch.bfloat16, device="cuda")
+    L.lora_transpose_bf16(U, Ut)
+    tg = torch.randint(0, V, (n,), generator=gen, device="cuda", dtype=torch.int32)
+    prompt = int(0.4 * seq)
+    act = torch.zeros(n_seq, seq, device="cuda")
+    act[:, prompt:] = 1
+    act = act.reshape(-1).contiguous()
+    rew = (torch.rand(n_seq, generator=gen, device="cuda") < 0.3).float().reshape(16, 4)
+    adv = (rew - rew.mean(dim=1, keepdim=True)).reshape(n_seq, 1).expand(n_seq, seq).reshape(-1)
+    adv = (adv * act).contiguous()
+    lp = torch.empty(n, device="cuda")
+    lse = torch.empty(n, device="cuda")
+    ws_f = L.empty_workspace(L.token_logprobs_workspace_bytes(n, V))
+    L.token_logprobs(hs[0], U, tg, lp, lse, ws_f)
+    samp = (lp + torch.randn(n, generator=gen, device="cuda") * 0.05 * act).contiguous()
+    ws_l = L.empty_workspace(L.loss_grad_workspace_bytes(n))
+    ws_b = L.empty_workspace(L.token_logprobs_backward_workspace_bytes(n, V, chunk))
+    loss = torch.empty(1, device="cuda")
+    dl = torch.empty(n, device="cuda")
+    dh = torch.empty((n, H), dtype=torch.bfloat16, device="cuda")
+
+    def step(k):
+        h = hs[k % 2]
+        L.token_logprobs(h, U, tg, lp, lse, ws_f)
+        L.loss_grad(L.LOSS_PPO, lp, act, adv, samp, None, (0.2, 0.2), loss, dl, ws_l)
+        L.token_logprobs_backward(h, U, Ut, tg, lse, dl, dh, ws_b)   # chunk from ws size
+
+    log(f"[bench] logprob {n} tokens, H {H}, V {V}")
+    ms = _timed(step, steps, warmup, log)
+    f_ms, f_n = _timer(L.TIMER_LOGPROB_FWD)
+    b_ms, b_n = _timer(L.TIMER_LOGPROB_BWD)     # one record per token chunk
+    b_step_ms = b_ms * b_n / steps
+    flops = 2.0 * n * V * H
+    tf_f = flops / (f_ms / 1e3) / 1e12
+    tf_b = 2 * flops / (b_step_ms / 1e3) / 1e12
+    return {
+        "metric": "tokens/s fused lm_head logprob + PPO loss + logprob backward",
+        "value": round(n / (ms / 1e3), 1), "unit": "tokens/s", "ms_per_step": round(ms, 4),
+        "config": {"workload": f"hidden {H} -> vocab {V}, {n} tokens = 16 groups x 4 x {seq}, "
+                               f"prompt {prompt}/{seq}, PPO clip 0.2, backward chunk {chunk} rows"},
+        "roofline": {"bound": "mfma", "kernel": "lm_head GEMM with online logsumexp (forward)",
+                     "achieved": round(tf_f, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf_f / PEAK_BF16_TFLOPS, 4), "avg_ms": round(f_ms, 4)},
+        "kernels": {"logprob_backward": {"ms_per_step": round(b_step_ms, 4), "chunks": b_n // steps,
+                                         "TFLOP_s": round(tf_b, 1),
+                                         "frac_mfma": round(tf_b / PEAK_BF16_TFLOPS, 4)}},
+    }
+
+
+def moe(steps, warmup, log, n=16384, H=2048, F=768, E=128, K=8, n_ad=8, r=32):
+    """Qwen3-30B-A3B-style routed layer: top-8 of 128 experts, 8 rank-32 adapters
+    on every expert's gate/up/down; route + forward + backward."""
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    rng = np.random.default_rng(5)
+    logits = torch.randn((n, E), generator=gen, device="cuda")
+    ids = torch.from_numpy(rng.integers(0, n_ad, size=n).astype(np.int32)).cuda()
+    Wg, Wu = _randn(gen, (E, F, H), 0.02), _randn(gen, (E, F, H), 0.02)
+    Wd = _randn(gen, (E, H, F), 0.02)
+    Wgt, Wut = (torch.empty((E, H, F), dtype=torch.bfloat16, device="cuda") for _ in range(2))
+    Wdt = torch.empty((E, F, H), dtype=torch.bfloat16, device="cuda")
+    for e in range(E):
+        L.lora_transpose_bf16(Wg[e], Wgt[e])
+        L.lora_transpose_bf16(Wu[e], Wut[e])
+        L.lora_transpose_bf16(Wd[e], Wdt[e])
+    packs, descs = [], []
+    for (di, do) in ((H, F), (H, F), (F, H)):
+        per = r * (di + do)
+        pack = torch.empty(n_ad * E * per, dtype=torch.bfloat16, device="cuda")
+        pack.copy_(_randn(gen, (pack.numel(),), 0.01))
+        a_off = np.array([(a * E + e) * per for e in range(E) for a in range(n_ad)])
+        packs.append(pack)
+        descs.append(L.make_desc(a_off, a_off + r * di, np.full(a_off.size, r, np.int32),
+                                 np.full(a_off.size, 32.0 / r, np.float32)))
+    shape = L.MoeShape(n, H, F, packs[0].numel(), packs[1].numel(), packs[2].numel(), E, K, n_ad, r)
+    ws = L.empty_workspace(L.moe_workspace_bytes(shape))
+    saved = torch.empty(L.moe_saved_bytes(shape), dtype=torch.uint8, device="cuda")
+    xs = [_randn(gen, (n, H), 1.0) for _ in range(2)]
+    dys = [_randn(gen, (n, H), 1.0) for _ in range(2)]
+    ex = torch.empty((n, K), dtype=torch.int32, device="cuda")
+    w = torch.empty((n, K), device="cuda")
+    y = torch.empty((n, H), dtype=torch.bfloat16, device="cuda")
+    dx = torch.empty_like(y)
+    grads = [torch.zeros(p.numel(), dtype=torch.float32, device="cuda") for p in packs]
+
+    def step(k):
+        L.moe_route(logits, K, ex, w)
+        L.moe_forward(shape, xs[k % 2], ex, w, ids, Wg, Wu, Wd, packs, descs, y, saved, ws)
+        L.moe_backward(shape, dys[k % 2], xs[k % 2], ex, w, ids, Wgt, Wut, Wdt, packs, descs, saved,
+                       dx, grads, 0, ws)
+
+    log(f"[bench] moe {n} tokens, {E} experts top-{K}, H {H}, F {F}, {n_ad} adapters r{r}")
+    ms = _timed(step, steps, warmup, log)
+    if L.lora_device_status(ws):
+        raise RuntimeError("device status flags set")
+    gemm_ms, gemm_n = _timer(L.TIMER_BASE_GEMM)
+    flops_launch = 2.0 * n * K * H * F      # each grouped projection GEMM
+    tf = flops_launch / (gemm_ms / 1e3) / 1e12
+    return {
+        "metric": "tokens/s mixed-adapter LoRA routed-expert layer fwd+bwd",
+        "value": round(n / (ms / 1e3), 1), "unit": "tokens/s", "ms_per_step": round(ms, 4),
+        "config": {"workload": f"qwen3-30b-a3b-style MoE: {E} experts top-{K}, hidden {H}, "
+                               f"expert intermediate {F}, {n_ad} adapters r{r} alpha 32 on every "
+                               f"expert's gate/up/down, {n} tokens random adapter ids; "
+                               "route + fwd + bwd"},
+        "roofline": {"bound": "mfma", "kernel": "grouped expert GEMMs (6 per step, 2*N*K*H*F each)",
+                     "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf / PEAK_BF16_TFLOPS, 4), "avg_ms": round(gemm_ms, 4),
+                     "launches": gemm_n},
+    }
