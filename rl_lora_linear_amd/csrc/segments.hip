@@ -179,6 +179,224 @@ __global__ __launch_bounds__(SEG_CHUNK) void seg_scatter_kernel(
   }
 }
 
+// The whole builder in one block of 1024 threads for small batches (one
+// launch instead of four).  Chunks are the 64 tokens of one wave: a wave
+// counts each distinct key of its chunk with one ballot (no same-address LDS
+// atomics, which serialise badly when a chunk's keys are all equal), the
+// per-key prefix over chunks and the key scan follow, and a token's place is
+// offsets[key] + its chunk's prefix + the lanes below it holding the same key.
+constexpr int SEG_SMALL_N = 16384;
+constexpr int SEG_SMALL_KEYS = 1024;
+constexpr int SEG_SMALL_HIST = 12288;   // chunks * (n_keys + 1) bound (48 KB of LDS)
+
+__device__ __forceinline__ void block_scan4_1024(int32_t (&acc)[4], int32_t (*s_v)[1024]) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) s_v[q][tid] = acc[q];
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    int32_t x[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) x[q] = tid >= o ? s_v[q][tid - o] : 0;
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 4; ++q) s_v[q][tid] += x[q];
+    __syncthreads();
+  }
+}
+
+// Lanes of this wave (among `active`) holding the same key as this lane.
+__device__ __forceinline__ uint64_t same_key_lanes(int key, uint64_t active) {
+  uint64_t mine = 0, rem = active;
+  while (rem) {
+    const int leader = __ffsll((long long)rem) - 1;
+    const int lk = __shfl(key, leader);
+    const uint64_t m = __ballot(key == lk) & active;
+    if (key == lk) mine = m;
+    rem &= ~m;
+  }
+  return mine;
+}
+
+__global__ __launch_bounds__(1024) void seg_small_kernel(
+    const int32_t* __restrict__ ids, int n, int n_keys, int sorted, SegTabs tabs, int max_rank,
+    uint8_t* __restrict__ active, Tilings tl, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ perm, int32_t* __restrict__ adpos, int row_div,
+    int32_t* __restrict__ tokrow, int32_t* __restrict__ inv, int32_t* status) {
+  __shared__ int32_t s_v[4][1024];
+  __shared__ int32_t s_off[SEG_SMALL_KEYS + 1];
+  __shared__ uint8_t s_act[SEG_SMALL_KEYS + 1];
+  __shared__ int32_t s_ids[SEG_SMALL_N];
+  extern __shared__ int32_t s_hist[];   // [chunks of 64][n_keys + 1]
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int K1 = n_keys + 1;
+  const int chunks = (n + 63) / 64;
+  const int rounds = (n + 1023) / 1024;
+  {  // all id loads in flight at once, then into LDS
+    int32_t v[SEG_SMALL_N / 1024];
+#pragma unroll
+    for (int r = 0; r < SEG_SMALL_N / 1024; ++r) {
+      const int t = r * 1024 + tid;
+      v[r] = t < n ? ids[t] : 0;
+    }
+#pragma unroll
+    for (int r = 0; r < SEG_SMALL_N / 1024; ++r)
+      if (r * 1024 + tid < n) s_ids[r * 1024 + tid] = v[r];
+  }
+  for (int i = tid; i < chunks * K1; i += 1024) s_hist[i] = 0;
+  __syncthreads();
+  for (int r = 0; r < rounds; ++r) {
+    const int t = r * 1024 + tid;
+    const bool in = t < n;
+    int key = n_keys;
+    if (in) {
+      const int32_t id = s_ids[t];
+      key = (id >= 0 && id < n_keys) ? id : n_keys;
+      if (key == n_keys) set_flag(status, LORA_FLAG_ID_RANGE);
+      if (sorted && t + 1 < n && s_ids[t + 1] < id) set_flag(status, LORA_FLAG_UNSORTED);
+    }
+    const uint64_t act = __ballot(in);
+    const uint64_t same = same_key_lanes(key, act);
+    // the lowest lane of each key group writes the chunk's count
+    if (in && (same & ((1ull << lane) - 1)) == 0) s_hist[(t >> 6) * K1 + key] = __popcll(same);
+  }
+  __syncthreads();
+  // per key, one wave: prefix over chunks (in place, 64 chunks per step with a
+  // wave scan) and the total (kept in s_off)
+  for (int k = tid >> 6; k <= n_keys; k += 16) {
+    int32_t base = 0;
+    for (int c0 = 0; c0 < chunks; c0 += 64) {
+      const int c = c0 + lane;
+      const int32_t v = c < chunks ? s_hist[c * K1 + k] : 0;
+      int32_t x = v;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int32_t y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+      }
+      if (c < chunks) s_hist[c * K1 + k] = base + x - v;
+      base += __shfl(x, 63);
+    }
+    if (lane == 0) s_off[k] = base;
+  }
+  __syncthreads();
+  // per key: validation
+  for (int k = tid; k <= n_keys; k += 1024) {
+    bool on = true;
+    if (k < n_keys && tabs.n_tabs > 0) {
+      for (int i = 0; i < tabs.n_tabs; ++i) {
+        const lora_host::SegDescs& tb = tabs.tab[i];
+        const lora_adapter_desc d = tb.desc[k];
+        const int64_t rk = d.rank;
+        if (rk == 0) {
+          on = false;
+          continue;
+        }
+        const bool ok = rk >= 8 && rk <= 64 && (rk % 8) == 0 && rk <= max_rank && d.a_off >= 0 &&
+                        d.b_off >= 0 && (d.a_off % 8) == 0 && (d.b_off % 8) == 0 &&
+                        d.a_off + rk * tb.d_in <= tb.a_elems && d.b_off + tb.d_out * rk <= tb.b_elems;
+        if (!ok) set_flag(status, LORA_FLAG_BAD_DESC);
+        on = on && ok;
+      }
+      active[k] = on ? 1 : 0;
+    }
+    s_act[k] = on ? 1 : 0;
+  }
+  __syncthreads();
+  // exclusive scan over keys: offsets and the tile prefix arrays
+  if (n_keys <= 64) {   // one wave, no barriers
+    if (tid < 64) {
+      const int k = lane;
+      const bool kin = k < n_keys;
+      const int32_t cnt = kin ? s_off[k] : 0;
+      const bool on = kin && s_act[k] != 0;
+      int32_t v[4] = {cnt, 0, 0, 0};
+#pragma unroll
+      for (int i = 0; i < 3; ++i)
+        if (tl.pre[i]) v[1 + i] = on ? (cnt + tl.tm[i] - 1) / tl.tm[i] : 0;
+      int32_t x[4] = {v[0], v[1], v[2], v[3]};
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int32_t y = __shfl_up(x[q], o);
+          if (lane >= o) x[q] += y;
+        }
+      if (kin) {
+        offsets[k] = x[0] - v[0];
+        s_off[k] = x[0] - v[0];
+#pragma unroll
+        for (int i = 0; i < 3; ++i)
+          if (tl.pre[i]) tl.pre[i][k] = x[1 + i] - v[1 + i];
+      }
+      if (lane == 63) {
+        offsets[n_keys] = x[0];
+        s_off[n_keys] = x[0];
+#pragma unroll
+        for (int i = 0; i < 3; ++i)
+          if (tl.pre[i]) tl.pre[i][n_keys] = x[1 + i];
+      }
+    }
+    __syncthreads();
+  } else {
+  const int per = (n_keys + 1023) / 1024;
+  const int k0 = min(tid * per, n_keys), k1 = min(k0 + per, n_keys);
+  int32_t acc[4] = {0, 0, 0, 0};
+  for (int k = k0; k < k1; ++k) {
+    const int32_t cnt = s_off[k];
+    const bool on = s_act[k] != 0;
+    acc[0] += cnt;
+#pragma unroll
+    for (int i = 0; i < 3; ++i)
+      if (tl.pre[i]) acc[1 + i] += on ? (cnt + tl.tm[i] - 1) / tl.tm[i] : 0;
+  }
+  block_scan4_1024(acc, s_v);
+  int32_t run[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) run[q] = tid ? s_v[q][tid - 1] : 0;
+  for (int k = k0; k < k1; ++k) {
+    const int32_t cnt = s_off[k];
+    const bool on = s_act[k] != 0;
+    offsets[k] = run[0];
+    s_off[k] = run[0];
+    run[0] += cnt;
+#pragma unroll
+    for (int i = 0; i < 3; ++i)
+      if (tl.pre[i]) {
+        tl.pre[i][k] = run[1 + i];
+        run[1 + i] += on ? (cnt + tl.tm[i] - 1) / tl.tm[i] : 0;
+      }
+  }
+  if (tid == 1023) {
+    offsets[n_keys] = s_v[0][1023];
+    s_off[n_keys] = s_v[0][1023];
+#pragma unroll
+    for (int i = 0; i < 3; ++i)
+      if (tl.pre[i]) tl.pre[i][n_keys] = s_v[1 + i][1023];
+  }
+  __syncthreads();
+  }
+  // scatter, stable within each key
+  for (int r = 0; r < rounds; ++r) {
+    const int t = r * 1024 + tid;
+    const bool in = t < n;
+    int key = n_keys;
+    if (in) {
+      const int32_t id = s_ids[t];
+      key = (id >= 0 && id < n_keys) ? id : n_keys;
+    }
+    const uint64_t same = same_key_lanes(key, __ballot(in));
+    if (!in) continue;
+    const int pos = s_off[key] + s_hist[(t >> 6) * K1 + key] + __popcll(same & ((1ull << lane) - 1));
+    perm[pos] = t;
+    if (adpos) adpos[pos] = (key < n_keys && s_act[key]) ? key : -1;
+    if (row_div > 0) {
+      tokrow[pos] = t / row_div;
+      inv[t] = pos;
+    }
+  }
+}
+
 // One block: gpre[g] = sum over groups g' < g of ceil(rows of g' / 256), where
 // group g is keys [g*group, (g+1)*group).  n_groups <= 1024.
 __global__ __launch_bounds__(1024) void seg_group_tiles_kernel(const int32_t* __restrict__ offsets,
@@ -226,6 +444,41 @@ lora_status run_segments(const int32_t* ids, int64_t n, int32_t n_keys, int32_t 
     set_error("segments: workspace of %zu bytes < %zu needed", ws_bytes, cv.used);
     return LORA_E_WORKSPACE;
   }
+  SegTabs tabs{};
+  if (ex) {
+    tabs.n_tabs = ex->n_tabs;
+    for (int i = 0; i < ex->n_tabs; ++i) tabs.tab[i] = ex->tab[i];
+  }
+  Tilings tl{};
+  for (int i = 0; i < 3; ++i) {
+    tl.tm[i] = (ex && ex->pre[i]) ? ex->tm[i] : 1;
+    tl.pre[i] = ex ? ex->pre[i] : nullptr;
+  }
+  const int64_t chunks64 = cdiv(n, 64);
+  if (n > 0 && n <= SEG_SMALL_N && n_keys <= SEG_SMALL_KEYS &&
+      chunks64 * (n_keys + 1) <= SEG_SMALL_HIST) {
+    // one launch
+    const size_t hl = (size_t)chunks64 * (n_keys + 1) * sizeof(int32_t);
+    static size_t attr = 0;
+    if (attr < hl) {
+      TRY_HIP(hipFuncSetAttribute((const void*)seg_small_kernel,
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)hl));
+      attr = hl;
+    }
+    hipLaunchKernelGGL(seg_small_kernel, dim3(1), dim3(1024), hl, s, ids, (int)n, n_keys,
+                       order == LORA_IDS_SORTED ? 1 : 0, tabs, ex ? ex->max_rank : 0,
+                       ex ? ex->active : nullptr, tl, offsets, perm, ex ? ex->adpos : nullptr,
+                       ex ? ex->row_div : 0, ex ? ex->tokrow : nullptr, ex ? ex->inv : nullptr,
+                       status);
+    lora_status st = launch_check("seg_small");
+    if (st) return st;
+    if (ex && ex->gpre) {
+      hipLaunchKernelGGL(seg_group_tiles_kernel, dim3(1), dim3(1024), 0, s, offsets, ex->group,
+                         ex->n_groups, ex->gpre);
+      st = launch_check("seg_group_tiles");
+    }
+    return st;
+  }
   const size_t lds = (size_t)(n_keys + 1) * sizeof(int32_t);
   if (n > 0) {
     hipLaunchKernelGGL(seg_hist_kernel, dim3((unsigned)chunks), dim3(SEG_CHUNK), lds, s, ids, n,
@@ -239,21 +492,11 @@ lora_status run_segments(const int32_t* ids, int64_t n, int32_t n_keys, int32_t 
     lora_status st = launch_check("seg_zero");
     if (st) return st;
   }
-  SegTabs tabs{};
-  if (ex) {
-    tabs.n_tabs = ex->n_tabs;
-    for (int i = 0; i < ex->n_tabs; ++i) tabs.tab[i] = ex->tab[i];
-  }
   hipLaunchKernelGGL(seg_keyscan_kernel, dim3((unsigned)cdiv(n_keys + 1, 256)), dim3(256), 0, s,
                      hist, n_keys, (int)chunks, totals, tabs, ex ? ex->max_rank : 0,
                      ex ? ex->active : nullptr, status);
   lora_status st = launch_check("seg_keyscan");
   if (st) return st;
-  Tilings tl{};
-  for (int i = 0; i < 3; ++i) {
-    tl.tm[i] = (ex && ex->pre[i]) ? ex->tm[i] : 1;
-    tl.pre[i] = ex ? ex->pre[i] : nullptr;
-  }
   hipLaunchKernelGGL(seg_offsets_kernel, dim3(1), dim3(1024), 0, s, totals, n_keys, offsets,
                      (ex && ex->n_tabs > 0) ? ex->active : nullptr, tl);
   st = launch_check("seg_offsets");

@@ -22,7 +22,8 @@ import rl_lora_linear_amd.lib as L  # noqa: E402
 # ---------------------------------------------------------------- segments
 @pytest.mark.parametrize("n,n_keys,order,seed", [
     (0, 4, L.IDS_INTERLEAVED, 0), (1, 1, L.IDS_SORTED, 1), (255, 3, L.IDS_INTERLEAVED, 2),
-    (257, 16, L.IDS_SORTED, 3), (4097, 64, L.IDS_INTERLEAVED, 4), (20000, 1024, L.IDS_INTERLEAVED, 5),
+    (257, 16, L.IDS_SORTED, 3), (4097, 64, L.IDS_INTERLEAVED, 4), (3000, 200, L.IDS_INTERLEAVED, 7),
+    (16384, 16, L.IDS_SORTED, 8), (20000, 1024, L.IDS_INTERLEAVED, 5),
     (131072, 1024, L.IDS_INTERLEAVED, 6)])
 def test_segments_bit_exact(n, n_keys, order, seed):
     rng = np.random.default_rng(seed)
