@@ -14,7 +14,9 @@
 // LDS rows are 64 B and their 16-byte chunks are XOR-swizzled (g4) so the
 // fragment reads of 16 consecutive rows hit distinct banks.  The MFMA computes the transposed
 // sub-tile so that each lane ends with runs of 4 consecutive output columns
-// (8-byte stores; row reductions need one cross-lane step).  Tiles are ordered XCD-first (blocks are dispatched
+// (row reductions need one cross-lane step).  The bf16 epilogue stages the
+// tile in the idle ring and writes whole 512-byte rows (scattered 16-byte
+// stores of 32 rows per instruction cost ~10 us more per 8192x4096 output).  Tiles are ordered XCD-first (blocks are dispatched
 // round-robin over the 8 XCDs, so each XCD gets a contiguous tile range and
 // its own L2 sees the reuse) and then in groups of `group_m` row tiles.
 #include <type_traits>
@@ -223,12 +225,23 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_kernel(const uint16_t* __restr
   const int n_q = 4 * (lane >> 5);
   int tok[4], ad[4];
   float rs[4];
+  int gy[4];          // EPI_GRAD: target, dlogp, lse of the fragment rows
+  float gd[4], gl[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = m0 + wm * 128 + i * 32 + m_l;
     tok[i] = row < Mlim ? (ep.c_rows ? ep.c_rows[row] : row) : -1;
     ad[i] = (EPI == EPI_BF16 && ep.vec && row < Mlim) ? ep.adpos[row] : -1;
     rs[i] = (EPI == EPI_BF16 && ep.rowscale && row < Mlim) ? ep.rowscale[row] : 1.f;
+    gy[i] = -1;
+    gd[i] = 0.f;
+    gl[i] = 0.f;
+    if (EPI == EPI_GRAD && row < M) {
+      gy[i] = ep.targets[row];
+      gd[i] = ep.dlogp[row];
+      gl[i] = ep.lse[row];
+      if (gy[i] < 0 || gy[i] >= N) gd[i] = 0.f;   // invalid target: zero row
+    }
   }
 
   const int KT = K / SBK;
@@ -370,20 +383,37 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_kernel(const uint16_t* __restr
           for (int g = 0; g < 16; ++g) acc[i][j][g] *= rs[i];
     }
     if (ep.vec) lora_slab(ep, n0, N, wn, lane, tok, ad, acc);
+    // stage the bf16 tile in the idle ring (256 rows x 512 B), 16-byte chunks
+    // swizzled by row, then write whole 512-byte rows (2 rows per wave store)
+    __shared__ int s_crow[GBM];
+    char* T = (char*)g_stage;
+    __syncthreads();
+    if (wn == 0 && lane < 32) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s_crow[wm * 128 + i * 32 + lane] = tok[i];
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      if (tok[i] < 0) continue;
-      uint16_t* crow = ep.C + (int64_t)tok[i] * ep.ldc;
+      const int row = wm * 128 + i * 32 + m_l;
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int col = n0 + wn * 128 + j * 32 + 8 * q + n_q;
-          if (col >= N) continue;
+          const int chunk = wn * 16 + j * 4 + q;
           const uint2 v = make_uint2(pack2bf(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
                                      pack2bf(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]));
-          *(uint2*)(crow + col) = v;
+          *(uint2*)(T + row * 512 + ((chunk ^ (row & 31)) << 4) + ((lane >> 5) << 3)) = v;
         }
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int k = 0; k < 32; ++k) {
+      const int row = wave * 64 + 2 * k + (lane >> 5);
+      const int c = lane & 31;
+      const int crow = s_crow[row];
+      const int col = n0 + c * 8;
+      const uint4 v = *(const uint4*)(T + row * 512 + ((c ^ (row & 31)) << 4));
+      if (crow >= 0 && col < N) *(uint4*)(ep.C + (int64_t)crow * ep.ldc + col) = v;
     }
   } else if constexpr (EPI == EPI_LSE) {
     // (max, sum) pairs of the two column halves, in the now idle operand ring;
@@ -446,33 +476,42 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_kernel(const uint16_t* __restr
       ep.part_m[(int64_t)tn * M + m0 + r] = mx;
       ep.part_s[(int64_t)tn * M + m0 + r] = sm;
     }
-  } else {  // EPI_GRAD
+  } else {  // EPI_GRAD: G = d (onehot(y) - exp(z - lse)), staged and stored like EPI_BF16
+    __shared__ int s_grow[GBM];
+    char* T = (char*)g_stage;
+    __syncthreads();
+    if (wn == 0 && lane < 32) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s_grow[wm * 128 + i * 32 + lane] = tok[i];
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int row = m0 + wm * 128 + i * 32 + m_l;
-      if (row >= M) continue;
-      int y = ep.targets[row];
-      float d = ep.dlogp[row];
-      if (y < 0 || y >= N) d = 0.f;  // invalid target: zero row
-      const float l = ep.lse[row];
-      uint16_t* grow = ep.C + (int64_t)row * ep.ldc;
+      const int row = wm * 128 + i * 32 + m_l;
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int col = n0 + wn * 128 + j * 32 + 8 * q + n_q;
-          if (col >= N) continue;
+          const int chunk = wn * 16 + j * 4 + q;
+          const int col = n0 + chunk * 8 + n_q;
           float gv[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            gv[e] = 0.f;
-            if (d != 0.f) {
-              const float p = exp2f((acc[i][j][4 * q + e] - l) * kLog2e);
-              gv[e] = d * ((col + e == y ? 1.f : 0.f) - p);
-            }
+            const float pr = exp2f((acc[i][j][4 * q + e] - gl[i]) * kLog2e);
+            gv[e] = gd[i] == 0.f ? 0.f : gd[i] * ((col + e == gy[i] ? 1.f : 0.f) - pr);
           }
-          *(uint2*)(grow + col) = make_uint2(pack2bf(gv[0], gv[1]), pack2bf(gv[2], gv[3]));
+          *(uint2*)(T + row * 512 + ((chunk ^ (row & 31)) << 4) + ((lane >> 5) << 3)) =
+              make_uint2(pack2bf(gv[0], gv[1]), pack2bf(gv[2], gv[3]));
         }
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int k = 0; k < 32; ++k) {
+      const int row = wave * 64 + 2 * k + (lane >> 5);
+      const int c = lane & 31;
+      const int grow = s_grow[row];
+      const int col = n0 + c * 8;
+      const uint4 v = *(const uint4*)(T + row * 512 + ((c ^ (row & 31)) << 4));
+      if (grow >= 0 && col < N) *(uint4*)(ep.C + (int64_t)grow * ep.ldc + col) = v;
     }
   }
 }
