@@ -5,9 +5,10 @@
 //             logit, for the lm_head online logsumexp        (token_logprobs)
 //   EPI_GRAD  G = d (onehot(y) - exp(C - lse)) stored bf16   (logprob backward)
 //
-// Block tile 256 x 256 x 64, 256 threads = 4 waves in a 2 x 2 grid, each wave
-// 128 x 128 as 4 x 4 tiles of v_mfma_f32_32x32x16_bf16 (256 fp32 accumulators
-// per lane, in AGPRs).  Operand tiles move global -> LDS by LDS-DMA into a
+// Block tile 256 x 256, 512 threads = 8 waves (two per SIMD) in a 2 x 4 grid,
+// each wave 128 x 64 as 4 x 2 tiles of v_mfma_f32_32x32x16_bf16 (128 fp32
+// accumulators per lane, in AGPRs).  Two waves per SIMD let one wave's
+// epilogue, waits and LDS traffic overlap the other's MFMAs.  Operand tiles move global -> LDS by LDS-DMA into a
 // 4-stage ring of k = 32 slices (128 KB), three stages ahead; one barrier
 // per stage; LDS fragment reads run one 16-wide k slice ahead of the MFMAs
 // (including the first slice of the next stage, read before the barrier).
@@ -85,7 +86,9 @@ constexpr int S_TILE = 256 * S_CH;         // uint4 per operand tile per stage
 constexpr int NSTAGE = 4;
 // DMA instructions a wave may leave in flight at the end of a k step: the
 // stages after k + 2 (8 per stage)
-constexpr int VM_AHEAD = (NSTAGE - 3) * 8;
+constexpr int VM_AHEAD = (NSTAGE - 3) * 4;
+constexpr int GTHREADS = 512;   // 8 waves
+constexpr int WN = 64;          // output columns per wave
 
 // Swizzle of a 4-chunk LDS row: chunk c of row r is stored at c ^ g4(r).
 // The 16-byte reads of 16 consecutive rows at one logical chunk then hit 16
@@ -115,10 +118,10 @@ __device__ __forceinline__ void dma16s(uint32_t voff, const void* base, uint32_t
 // The scaled vector is stored as bf16 hi and lo planes, one MFMA each, so the
 // slab keeps ~16 significant bits; M_a is bf16-exact.  tok[i] / ad[i] are the
 // token and adapter (-1: none) of this lane's fragment rows, loaded before
-// the k loop.  Fragments of two rank slices are loaded before their MFMAs.
+// the k loop.
 __device__ __forceinline__ void lora_slab(const GemmEpi& ep, int n0, int N, int wn, int lane,
                                           const int (&tok)[4], const int (&ad)[4],
-                                          f32x16 (&acc)[4][4]) {
+                                          f32x16 (&acc)[4][2]) {
   const int m_l = lane & 31;
   const int half = lane >> 5;
   int lo = INT32_MAX, hi = -1;
@@ -139,43 +142,38 @@ __device__ __forceinline__ void lora_slab(const GemmEpi& ep, int n0, int N, int 
     const lora_adapter_desc d = ep.desc[a];
     const int r = d.rank;
     const uint16_t* mat = ep.lmat + (ep.use_b_off ? d.b_off : d.a_off);
-    for (int sl = 0; sl * 16 < r; sl += 2) {
-      uint4 h[2][4], l[2][4], v[2][4];
+    for (int sl = 0; sl * 16 < r; ++sl) {
+      const int c = sl * 16 + 8 * half;
+      const bool cok = c < r;
+      uint4 h[4], l[4], v[2];
 #pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        const int c = (sl + p) * 16 + 8 * half;
-        const bool cok = c < r;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          h[p][i] = l[p][i] = make_uint4(0, 0, 0, 0);
-          if (ad[i] == a && cok) {
-            const uint16_t* vp = ep.vec + (int64_t)tok[i] * ep.vec_ld + c;
-            h[p][i] = *(const uint4*)vp;
-            l[p][i] = *(const uint4*)(vp + ep.vec_plane);
-          }
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int n = n0 + wn * 128 + j * 32 + m_l;
-          v[p][j] = make_uint4(0, 0, 0, 0);
-          if (n < N && cok) v[p][j] = *(const uint4*)(mat + (int64_t)n * r + c);
+      for (int i = 0; i < 4; ++i) {
+        h[i] = l[i] = make_uint4(0, 0, 0, 0);
+        if (ad[i] == a && cok) {
+          const uint16_t* vp = ep.vec + (int64_t)tok[i] * ep.vec_ld + c;
+          h[i] = *(const uint4*)vp;
+          l[i] = *(const uint4*)(vp + ep.vec_plane);
         }
       }
 #pragma unroll
-      for (int p = 0; p < 2; ++p)
+      for (int j = 0; j < 2; ++j) {
+        const int n = n0 + wn * WN + j * 32 + m_l;
+        v[j] = make_uint4(0, 0, 0, 0);
+        if (n < N && cok) v[j] = *(const uint4*)(mat + (int64_t)n * r + c);
+      }
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            acc[i][j] = mfma32(as_bf16x8(v[p][j]), as_bf16x8(h[p][i]), acc[i][j]);
-            acc[i][j] = mfma32(as_bf16x8(v[p][j]), as_bf16x8(l[p][i]), acc[i][j]);
-          }
+        for (int j = 0; j < 2; ++j) {
+          acc[i][j] = mfma32(as_bf16x8(v[j]), as_bf16x8(h[i]), acc[i][j]);
+          acc[i][j] = mfma32(as_bf16x8(v[j]), as_bf16x8(l[i]), acc[i][j]);
+        }
     }
   }
 }
 
 template <int EPI>
-__global__ __launch_bounds__(256, 1) void gemm_nt_kernel(const uint16_t* __restrict__ A,
+__global__ __launch_bounds__(GTHREADS, 1) void gemm_nt_kernel(const uint16_t* __restrict__ A,
                                                          const uint16_t* __restrict__ B, int M,
                                                          int N, int K, int64_t lda, int64_t ldb,
                                                          GemmEpi ep, int tiles_m, int tiles_n,
@@ -207,16 +205,16 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_kernel(const uint16_t* __restr
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
 
   // acc[i][j] holds the transposed 32x32 sub-tile: register g of lane l is
-  // C[m = wm*128 + i*32 + l%32][n = wn*128 + j*32 + 8*(g/4) + 4*(l/32) + g%4],
+  // C[m = wm*128 + i*32 + l%32][n = wn*64 + j*32 + 8*(g/4) + 4*(l/32) + g%4],
   // so each lane owns runs of 4 consecutive output columns.
-  f32x16 acc[4][4];
+  f32x16 acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int g = 0; g < 16; ++g) acc[i][j][g] = 0.f;
 
@@ -225,7 +223,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_kernel(const uint16_t* __restr
   const int n_q = 4 * (lane >> 5);
   int tok[4], ad[4];
   float rs[4];
-  int gy[4];          // EPI_GRAD: target, dlogp, lse of the fragment rows
+  int gy[4];          // EPI_LSE / EPI_GRAD: target; EPI_GRAD: dlogp, lse of the rows
   float gd[4], gl[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -236,6 +234,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_kernel(const uint16_t* __restr
     gy[i] = -1;
     gd[i] = 0.f;
     gl[i] = 0.f;
+    if (EPI == EPI_LSE && row < M) gy[i] = ep.targets[row];
     if (EPI == EPI_GRAD && row < M) {
       gy[i] = ep.targets[row];
       gd[i] = ep.dlogp[row];
@@ -254,15 +253,15 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_kernel(const uint16_t* __restr
   // (the host checks they fit in 32 bits); other rows are offsets from the
   // tile's first row.  Rows past the edge are clamped to the last row: they
   // only feed outputs that are never stored.
-  uint32_t offA[4], offB[4];
+  uint32_t offA[2], offB[2];
   const uint16_t* baseA = ep.a_rows ? A : A + (int64_t)m0 * lda;
   const uint16_t* baseB = B + (int64_t)n0 * ldb;
   {
     const int lrow = lane >> 2;
     const int chunk = (lane & 3) ^ g4(lrow);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int blk = wave * 4 + i;
+    for (int i = 0; i < 2; ++i) {
+      const int blk = wave * 2 + i;
       const int ra = min(m0 + blk * 16 + lrow, Mlim - 1);
       const int rb = min(n0 + blk * 16 + lrow, N - 1);
       const int64_t oa = ep.a_rows ? (int64_t)ep.a_rows[ra] * lda : (int64_t)(ra - m0) * lda;
@@ -270,8 +269,8 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_kernel(const uint16_t* __restr
       offB[i] = (uint32_t)(((int64_t)(rb - n0) * ldb + chunk * 8) * 2);
     }
   }
-  const uint32_t ldsA = __builtin_amdgcn_readfirstlane(lds_addr(sA + wave * 4 * 64));
-  const uint32_t ldsB = __builtin_amdgcn_readfirstlane(lds_addr(sB + wave * 4 * 64));
+  const uint32_t ldsA = __builtin_amdgcn_readfirstlane(lds_addr(sA + wave * 2 * 64));
+  const uint32_t ldsB = __builtin_amdgcn_readfirstlane(lds_addr(sB + wave * 2 * 64));
   // DMA of operand rows (block i of this wave) for k0 into stage st
   auto dmaA = [&](int st, int i, const uint16_t* kb) {
     dma16s(offA[i], kb, ldsA + (uint32_t)(st * S_TILE + i * 64) * 16u);
@@ -285,37 +284,35 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_kernel(const uint16_t* __restr
   for (int s = 0; s < NSTAGE - 1; ++s) {
     const int k0 = min(s, KT - 1) * SBK;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dmaA(s, i, baseA + k0);
+    for (int i = 0; i < 2; ++i) dmaA(s, i, baseA + k0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dmaB(s, i, baseB + k0);
+    for (int i = 0; i < 2; ++i) dmaB(s, i, baseB + k0);
   }
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(VM_AHEAD) : "memory");
 
   const int frag_row = lane & 31;   // row within a 32-row MFMA tile
   const int frag_half = lane >> 5;  // which 8-wide k half of a 16-wide k slice
   const int sw = g4(frag_row);      // swizzle of every fragment row of this lane
-  int a_row[4], b_row[4];
+  int a_row[4], b_row[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    a_row[i] = (wm * 128 + i * 32 + frag_row) * S_CH;
-    b_row[i] = (wn * 128 + i * 32 + frag_row) * S_CH;
-  }
+  for (int i = 0; i < 4; ++i) a_row[i] = (wm * 128 + i * 32 + frag_row) * S_CH;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) b_row[j] = (wn * WN + j * 32 + frag_row) * S_CH;
   const int c0 = frag_half ^ sw;         // slice 0 chunk
   const int c1 = (2 + frag_half) ^ sw;   // slice 1 chunk
 
-  bf16x8 f0a[4], f0b[4], f1a[4], f1b[4];
+  bf16x8 f0a[4], f0b[2], f1a[4], f1b[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    f0a[i] = as_bf16x8(sA[a_row[i] + c0]);
-    f0b[i] = as_bf16x8(sB[b_row[i] + c0]);
-  }
+  for (int i = 0; i < 4; ++i) f0a[i] = as_bf16x8(sA[a_row[i] + c0]);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) f0b[j] = as_bf16x8(sB[b_row[j] + c0]);
 
   // One k step on stage S (static, so every LDS address is base + immediate).
-  // Each phase is 8 groups of 2 MFMAs; the LDS fragment reads for the next
-  // phase go into the first four groups and this step's four A (phase 0) or
-  // B (phase 1) DMA instructions into the last four, so the vector-memory,
-  // LDS and scalar work issues in the shadow of the matrix pipe instead of in
-  // a burst before it.  sched_barrier keeps the groups in this order.
+  // Each phase is 8 groups of one MFMA; the LDS fragment reads for the next
+  // phase go into the first six groups and this step's two A (phase 0) or B
+  // (phase 1) DMA instructions into the last two, so the vector-memory, LDS
+  // and scalar work issues in the shadow of the matrix pipe instead of in a
+  // burst before it.  sched_barrier keeps the groups in this order.
   auto step = [&](auto S_, int kt) {
     constexpr int S = decltype(S_)::value;
     constexpr int SN = (S + NSTAGE - 1) % NSTAGE;   // stage refilled now (read at kt - 1)
@@ -327,33 +324,25 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_kernel(const uint16_t* __restr
     const int k0 = min(kt + NSTAGE - 1, KT - 1) * SBK;
     const uint16_t* ka = baseA + k0;
     const uint16_t* kb = baseB + k0;
-    // phase 0: MFMAs of slice 0; reads of slice 1; A DMAs
+    // phase 0: MFMAs of slice 0; reads of slice 1 (groups 0-5); A DMAs (6, 7)
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
-      const int i = g >> 1, j0 = (g & 1) * 2;
-      acc[i][j0] = mfma32(f0b[j0], f0a[i], acc[i][j0]);
-      acc[i][j0 + 1] = mfma32(f0b[j0 + 1], f0a[i], acc[i][j0 + 1]);
-      if (g < 4) {
-        f1a[g] = as_bf16x8(At[a_row[g] + c1]);
-        f1b[g] = as_bf16x8(Bt[b_row[g] + c1]);
-      } else {
-        dmaA(SN, g - 4, ka);
-      }
+      const int i = g >> 1, j = g & 1;
+      acc[i][j] = mfma32(f0b[j], f0a[i], acc[i][j]);
+      if (g < 4) f1a[g] = as_bf16x8(At[a_row[g] + c1]);
+      else if (g < 6) f1b[g - 4] = as_bf16x8(Bt[b_row[g - 4] + c1]);
+      else dmaA(SN, g - 6, ka);
       __builtin_amdgcn_sched_barrier(0);
     }
     // phase 1: MFMAs of slice 1; reads of slice 0 of the next stage (landed
     // at the last barrier; on the last step simply unused); B DMAs
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
-      const int i = g >> 1, j0 = (g & 1) * 2;
-      acc[i][j0] = mfma32(f1b[j0], f1a[i], acc[i][j0]);
-      acc[i][j0 + 1] = mfma32(f1b[j0 + 1], f1a[i], acc[i][j0 + 1]);
-      if (g < 4) {
-        f0a[g] = as_bf16x8(An[a_row[g] + c0]);
-        f0b[g] = as_bf16x8(Bn[b_row[g] + c0]);
-      } else {
-        dmaB(SN, g - 4, kb);
-      }
+      const int i = g >> 1, j = g & 1;
+      acc[i][j] = mfma32(f1b[j], f1a[i], acc[i][j]);
+      if (g < 4) f0a[g] = as_bf16x8(An[a_row[g] + c0]);
+      else if (g < 6) f0b[g - 4] = as_bf16x8(Bn[b_row[g - 4] + c0]);
+      else dmaB(SN, g - 6, kb);
       __builtin_amdgcn_sched_barrier(0);
     }
     // stage kt + 2 has landed for this wave; after the barrier, for all waves
@@ -373,62 +362,69 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_kernel(const uint16_t* __restr
 
   // ---- epilogues
 
+  // Output tiles are staged in the idle ring (256 rows x 512 B, 16-byte chunks
+  // swizzled by row) and written as whole 512-byte rows, 2 rows per wave store.
+  // s_row holds each staged row's destination (-1: not stored).
+  __shared__ int s_row[GBM];
+  char* T = (char*)g_stage;
+  auto stage_rows = [&]() {
+    if (wn == 0 && lane < 32) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s_row[wm * 128 + i * 32 + lane] = tok[i];
+    }
+  };
+  auto stage = [&](int i, int j, int q, uint2 v) {
+    const int row = wm * 128 + i * 32 + m_l;
+    const int chunk = wn * (WN / 8) + j * 4 + q;
+    *(uint2*)(T + row * 512 + ((chunk ^ (row & 31)) << 4) + ((lane >> 5) << 3)) = v;
+  };
+  auto store_rows = [&]() {
+#pragma unroll 4
+    for (int k = 0; k < GBM / 16; ++k) {
+      const int row = wave * (GBM / 8) + 2 * k + (lane >> 5);
+      const int c = lane & 31;
+      const int crow = s_row[row];
+      const int col = n0 + c * 8;
+      const uint4 v = *(const uint4*)(T + row * 512 + ((c ^ (row & 31)) << 4));
+      if (crow >= 0 && col < N) *(uint4*)(ep.C + (int64_t)crow * ep.ldc + col) = v;
+    }
+  };
+
   if constexpr (EPI == EPI_BF16) {
     if (ep.rowscale) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
           for (int g = 0; g < 16; ++g) acc[i][j][g] *= rs[i];
     }
     if (ep.vec) lora_slab(ep, n0, N, wn, lane, tok, ad, acc);
-    // stage the bf16 tile in the idle ring (256 rows x 512 B), 16-byte chunks
-    // swizzled by row, then write whole 512-byte rows (2 rows per wave store)
-    __shared__ int s_crow[GBM];
-    char* T = (char*)g_stage;
+    __syncthreads();   // every wave is done reading the ring
+    stage_rows();
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          stage(i, j, q, make_uint2(pack2bf(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
+                                    pack2bf(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])));
     __syncthreads();
-    if (wn == 0 && lane < 32) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) s_crow[wm * 128 + i * 32 + lane] = tok[i];
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = wm * 128 + i * 32 + m_l;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int chunk = wn * 16 + j * 4 + q;
-          const uint2 v = make_uint2(pack2bf(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
-                                     pack2bf(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]));
-          *(uint2*)(T + row * 512 + ((chunk ^ (row & 31)) << 4) + ((lane >> 5) << 3)) = v;
-        }
-    }
-    __syncthreads();
-#pragma unroll 4
-    for (int k = 0; k < 32; ++k) {
-      const int row = wave * 64 + 2 * k + (lane >> 5);
-      const int c = lane & 31;
-      const int crow = s_crow[row];
-      const int col = n0 + c * 8;
-      const uint4 v = *(const uint4*)(T + row * 512 + ((c ^ (row & 31)) << 4));
-      if (crow >= 0 && col < N) *(uint4*)(ep.C + (int64_t)crow * ep.ldc + col) = v;
-    }
+    store_rows();
   } else if constexpr (EPI == EPI_LSE) {
-    // (max, sum) pairs of the two column halves, in the now idle operand ring;
-    // the barrier keeps the last fragment reads of other waves ahead of it
-    float2 (*red_s)[GBM] = (float2 (*)[GBM])g_stage;
-    __syncthreads();
-    const int cbase = n0 + wn * 128;
+    // (max, sum) pairs of the four 64-column quarters, then merged per row in
+    // quarter order (deterministic)
+    __shared__ float2 red_s[4][GBM];
+    const int cbase = n0 + wn * WN;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int rl = wm * 128 + i * 32 + m_l;
       const int row = m0 + rl;
-      // this lane's 64 values of row `row`: columns cbase + j*32 + 8q + n_q + e
+      // this lane's 32 values of row `row`: columns cbase + j*32 + 8q + n_q + e
       float mx = -INFINITY;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q)
 #pragma unroll
@@ -438,7 +434,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_kernel(const uint16_t* __restr
       float sm = 0.f;
       if (mx != -INFINITY) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
           for (int q = 0; q < 4; ++q)
 #pragma unroll
@@ -448,13 +444,13 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_kernel(const uint16_t* __restr
       }
       sm += __shfl_xor(sm, 32);
       if (row < M) {
-        const int yo = ep.targets[row] - cbase;
+        const int yo = gy[i] - cbase;
         // column offset yo = j*32 + 8q + n_q + e
-        if (yo >= 0 && yo < 128 && cbase + yo < N && ((yo >> 2) & 1) == (lane >> 5)) {
+        if (yo >= 0 && yo < WN && cbase + yo < N && ((yo >> 2) & 1) == (lane >> 5)) {
           const int jj = yo >> 5, qq = (yo >> 3) & 3, ee = yo & 3;
           float zv = 0.f;
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
+          for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int q = 0; q < 4; ++q)
 #pragma unroll
@@ -466,53 +462,38 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_kernel(const uint16_t* __restr
       if (lane < 32) red_s[wn][rl] = make_float2(mx, sm);
     }
     __syncthreads();
-    for (int r = tid; r < GBM; r += 256) {
+    for (int r = tid; r < GBM; r += GTHREADS) {
       if (m0 + r >= M) continue;
-      float2 a = red_s[0][r], b = red_s[1][r];
-      float mx = fmaxf(a.x, b.x);
+      float mx = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) mx = fmaxf(mx, red_s[w][r].x);
       float sm = 0.f;
-      if (a.x != -INFINITY) sm += a.y * exp2f((a.x - mx) * kLog2e);
-      if (b.x != -INFINITY) sm += b.y * exp2f((b.x - mx) * kLog2e);
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        if (red_s[w][r].x != -INFINITY) sm += red_s[w][r].y * exp2f((red_s[w][r].x - mx) * kLog2e);
       ep.part_m[(int64_t)tn * M + m0 + r] = mx;
       ep.part_s[(int64_t)tn * M + m0 + r] = sm;
     }
   } else {  // EPI_GRAD: G = d (onehot(y) - exp(z - lse)), staged and stored like EPI_BF16
-    __shared__ int s_grow[GBM];
-    char* T = (char*)g_stage;
     __syncthreads();
-    if (wn == 0 && lane < 32) {
+    stage_rows();
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s_grow[wm * 128 + i * 32 + lane] = tok[i];
-    }
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = wm * 128 + i * 32 + m_l;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int chunk = wn * 16 + j * 4 + q;
-          const int col = n0 + chunk * 8 + n_q;
+          const int col = n0 + wn * WN + j * 32 + 8 * q + n_q;
           float gv[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const float pr = exp2f((acc[i][j][4 * q + e] - gl[i]) * kLog2e);
             gv[e] = gd[i] == 0.f ? 0.f : gd[i] * ((col + e == gy[i] ? 1.f : 0.f) - pr);
           }
-          *(uint2*)(T + row * 512 + ((chunk ^ (row & 31)) << 4) + ((lane >> 5) << 3)) =
-              make_uint2(pack2bf(gv[0], gv[1]), pack2bf(gv[2], gv[3]));
+          stage(i, j, q, make_uint2(pack2bf(gv[0], gv[1]), pack2bf(gv[2], gv[3])));
         }
-    }
     __syncthreads();
-#pragma unroll 4
-    for (int k = 0; k < 32; ++k) {
-      const int row = wave * 64 + 2 * k + (lane >> 5);
-      const int c = lane & 31;
-      const int grow = s_grow[row];
-      const int col = n0 + c * 8;
-      const uint4 v = *(const uint4*)(T + row * 512 + ((c ^ (row & 31)) << 4));
-      if (grow >= 0 && col < N) *(uint4*)(ep.C + (int64_t)grow * ep.ldc + col) = v;
-    }
+    store_rows();
   }
 }
 
@@ -545,7 +526,7 @@ static lora_status launch_gemm(const uint16_t* A, const uint16_t* B, int M, int 
                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     attr_set = true;
   }
-  hipLaunchKernelGGL(gemm_nt_kernel<EPI>, dim3(tiles_m * tiles_n), dim3(256), lds, s, A, B, M, N,
+  hipLaunchKernelGGL(gemm_nt_kernel<EPI>, dim3(tiles_m * tiles_n), dim3(GTHREADS), lds, s, A, B, M, N,
                      K, lda, ldb, ep, tiles_m, tiles_n, group_m);
   return launch_check("gemm_nt");
 }
