@@ -89,8 +89,6 @@ struct LayerWs {
   uint8_t* active;
   int32_t* pre32;
   int32_t* prec;
-  uint16_t* AT;
-  uint16_t* BT;
   uint16_t* v;        // scaled v = s_a B_a^T dy as bf16 hi/lo planes [2][N][max_rank]
   uint16_t* zero;     // 256 zero bytes (source of the rows past a gradient chunk)
   float* partial;
@@ -108,8 +106,6 @@ LayerWs carve_layer(const lora_shape& sh, void* ws, size_t bytes) {
   w.active = cv.take<uint8_t>((size_t)sh.n_adapters);
   w.pre32 = cv.take<int32_t>((size_t)sh.n_adapters + 1);
   w.prec = cv.take<int32_t>((size_t)sh.n_adapters + 1);
-  w.AT = cv.take<uint16_t>((size_t)sh.a_pack_elems);
-  w.BT = cv.take<uint16_t>((size_t)sh.b_pack_elems);
   w.v = cv.take<uint16_t>((size_t)2 * std::max<int64_t>(sh.n_tokens, 1) * sh.max_rank);
   w.zero = cv.take<uint16_t>(128);
   w.partial = cv.take<float>((size_t)grad_partial_floats(sh.n_tokens, sh.n_adapters,
@@ -293,11 +289,9 @@ lora_status lora_backward(const lora_shape* shape, const uint16_t* dy, const uin
   hipStream_t s = S(stream);
   const int N = (int)sh.n_tokens;
   TRY(layer_segments(sh, desc, adapter_ids, w, s));
-  TRY(launch_adapter_transpose(A_pack, B_pack, desc, w.active, sh.n_adapters, sh.d_in, sh.d_out,
-                               w.AT, w.BT, s));
   if (N > 0) {
     timer_begin(LORA_TIMER_SHRINK, s);
-    TRY(launch_shrink(dy, sh.d_out, (int)sh.d_out, w.BT, 1, desc, w.adpos, w.perm, w.perm,
+    TRY(launch_shrink(dy, sh.d_out, (int)sh.d_out, B_pack, 1, desc, w.adpos, w.perm, w.perm,
                       nullptr, w.offsets, w.pre32, sh.n_adapters, sh.n_tokens, w.v, sh.max_rank,
                       w.zero, s));
     timer_end(LORA_TIMER_SHRINK, s);
@@ -309,7 +303,8 @@ lora_status lora_backward(const lora_shape* shape, const uint16_t* dy, const uin
     f.vec_plane = sh.n_tokens * sh.max_rank;
     f.vec_ld = sh.max_rank;
     f.use_b_off = 0;
-    f.lmat = w.AT;
+    f.lmat_ld = sh.d_in;
+    f.lmat = A_pack;
     f.desc = desc;
     f.adpos = w.adpos;
     f.n_ad = sh.n_adapters;
@@ -567,8 +562,6 @@ struct MoeWs {
   uint16_t* du;      // [NK][F]
   uint16_t* dxg;     // [NK][H]
   uint16_t* dxu;     // [NK][H]
-  uint16_t* AT[3];
-  uint16_t* BT[3];
   float* partial;
   size_t total;
 };
@@ -624,10 +617,6 @@ MoeWs carve_moe(const moe_shape& sh, void* ws, size_t bytes, bool backward) {
     w.du = cv.take<uint16_t>((size_t)NK * sh.d_ff);
     w.dxg = cv.take<uint16_t>((size_t)NK * sh.hidden);
     w.dxu = cv.take<uint16_t>((size_t)NK * sh.hidden);
-    for (int i = 0; i < 3; ++i) {
-      w.AT[i] = cv.take<uint16_t>((size_t)packs[i]);
-      w.BT[i] = cv.take<uint16_t>((size_t)packs[i]);
-    }
     w.partial = cv.take<float>((size_t)grad_partial_floats(NK, n_keys,
                                                           std::max(sh.hidden, sh.d_ff),
                                                           sh.max_rank));
@@ -691,6 +680,7 @@ lora_status moe_project(const moe_shape& sh, const MoeWs& w, const uint16_t* A,
   f.vec_plane = NK * sh.max_rank;
   f.vec_ld = sh.max_rank;
   f.use_b_off = use_b_off;
+  f.lmat_ld = n_out;   // A_e,a is [r][n_out] when the expand runs from A
   f.lmat = lmat;
   f.desc = desc;
   f.adpos = w.adpos;
@@ -818,16 +808,12 @@ lora_status moe_backward(const moe_shape* shape, const uint16_t* dy, const uint1
   TRY(moe_segments(sh, experts, adapter_ids, descs, w, s));
   const uint16_t* packs[3] = {gate_pack, up_pack, down_pack};
   float* grads[3] = {dgate_pack, dup_pack, ddown_pack};
-  const int64_t d_in[3] = {H, H, F}, d_out[3] = {F, F, H};
-  for (int i = 0; i < 3; ++i)
-    TRY(launch_adapter_transpose(packs[i], packs[i], w.desc[i], w.active, n_keys, d_in[i],
-                                 d_out[i], w.AT[i], w.BT[i], s));
   if (NK > 0) {
     TRY(launch_moe_gather_w(weights, w.perm, NK, w.wpos, s));
     // down: do_j = w_j dy_t.  v = s w B^T dy_t; dh = w (dy_t W_down) + A^T v
-    TRY(launch_shrink(dy, H, (int)H, w.BT[2], 1, w.desc[2], w.adpos, w.tokrow, nullptr, w.wpos,
+    TRY(launch_shrink(dy, H, (int)H, down_pack, 1, w.desc[2], w.adpos, w.tokrow, nullptr, w.wpos,
                       w.offsets, w.pre32, n_keys, NK, w.v[2], R, w.zero, s));
-    TRY(moe_project(sh, w, dy, w.tokrow, sh.n_tokens, W_down_t, F, H, w.v[2], w.AT[2], 0,
+    TRY(moe_project(sh, w, dy, w.tokrow, sh.n_tokens, W_down_t, F, H, w.v[2], down_pack, 0,
                     w.desc[2], w.wpos, w.dh, s));
     // dB_down = sum dy_t (w s u)^T; dA_down = sum (s w v) h^T
     TRY(launch_planes_scale(sv.su[2], w.wpos, NK, R, w.uw, s));
@@ -843,9 +829,9 @@ lora_status moe_backward(const moe_shape* shape, const uint16_t* dy, const uint1
   const uint16_t* Wts[2] = {W_gate_t, W_up_t};
   for (int i = 0; i < 2; ++i) {
     if (NK > 0) {
-      TRY(launch_shrink(dpre[i], F, (int)F, w.BT[i], 1, w.desc[i], w.adpos, nullptr, nullptr,
+      TRY(launch_shrink(dpre[i], F, (int)F, packs[i], 1, w.desc[i], w.adpos, nullptr, nullptr,
                         nullptr, w.offsets, w.pre32, n_keys, NK, w.v[i], R, w.zero, s));
-      TRY(moe_project(sh, w, dpre[i], nullptr, NK, Wts[i], H, F, w.v[i], w.AT[i], 0, w.desc[i],
+      TRY(moe_project(sh, w, dpre[i], nullptr, NK, Wts[i], H, F, w.v[i], packs[i], 0, w.desc[i],
                       nullptr, dxp[i], s));
     }
     TRY(launch_grad(0, sv.su[i], R, w.zero, dpre[i], F, (int)F, w.desc[i], w.active, nullptr, 1,

@@ -55,6 +55,22 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
   return c.b;
 }
 
+// ---------------------------------------------------------------- LDS transposing read
+// ds_read_b64_tr_b16: in each 16-lane group, lane 4q + j addresses row t0 + q,
+// columns 4j..4j+3 of a row-major bf16 tile; lane i of the group receives
+// column i of rows t0..t0+3.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint2 tr_read(const uint4* base, uint32_t byte_off) {
+  s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)((__attribute__((address_space(3))) char*)(
+                                                     (__attribute__((address_space(3))) void*)base) +
+                                                 byte_off));
+  union { s16x4 s; uint2 u; } c;
+  c.s = v;
+  return c.u;
+}
+
 // ---------------------------------------------------------------- MFMA
 __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);

@@ -49,11 +49,13 @@ struct GemmEpi {
   int64_t ldb_group;
   // EPI_BF16 with the LoRA expand fused (nullable vec = plain GEMM): for the
   // row at segment position m, owned by adapter a, add s_a * vec[tok] . M_a^T
-  // where M_a [N][r_a] sits at (use_b_off ? b_off : a_off) of the pack lmat.
+  // with M_a [N][r_a] = B_a at b_off of the pack lmat (use_b_off = 1), or
+  // M_a = A_a^T read in place from A_a [r_a][lmat_ld] at a_off (use_b_off = 0).
   const uint16_t* vec;    // scaled vector, bf16 hi plane [tokens][vec_ld], token order
   int64_t vec_plane;      // lo plane at vec + vec_plane
   int vec_ld;
   int use_b_off;
+  int64_t lmat_ld;
   const uint16_t* lmat;
   const lora_adapter_desc* desc;
   const uint8_t* active;
@@ -119,9 +121,16 @@ __device__ __forceinline__ void dma16s(uint32_t voff, const void* base, uint32_t
 // slab keeps ~16 significant bits; M_a is bf16-exact.  tok[i] / ad[i] are the
 // token and adapter (-1: none) of this lane's fragment rows, loaded before
 // the k loop.
+// With M_a = A_a^T (use_b_off = 0) the factor block of a 16-rank slice (16
+// rows of A_a x the wave's 64 columns) is loaded row-wise into a per-wave LDS
+// tile (144-byte rows: the transposing reads of 4 rows hit distinct banks) and
+// read back transposed, 8 consecutive ranks of one column per lane.
+constexpr int SLAB_LD = 72;   // bf16 per LDS row of the slab tile
 __device__ __forceinline__ void lora_slab(const GemmEpi& ep, int n0, int N, int wn, int lane,
-                                          const int (&tok)[4], const int (&ad)[4],
+                                          int wave, const int (&tok)[4], const int (&ad)[4],
                                           f32x16 (&acc)[4][2]) {
+  __shared__ uint4 s_slab[GTHREADS / 64][16 * SLAB_LD / 8];
+  uint4* slab = s_slab[wave];
   const int m_l = lane & 31;
   const int half = lane >> 5;
   int lo = INT32_MAX, hi = -1;
@@ -155,11 +164,36 @@ __device__ __forceinline__ void lora_slab(const GemmEpi& ep, int n0, int N, int 
           l[i] = *(const uint4*)(vp + ep.vec_plane);
         }
       }
+      if (ep.use_b_off) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int n = n0 + wn * WN + j * 32 + m_l;
-        v[j] = make_uint4(0, 0, 0, 0);
-        if (n < N && cok) v[j] = *(const uint4*)(mat + (int64_t)n * r + c);
+        for (int j = 0; j < 2; ++j) {
+          const int n = n0 + wn * WN + j * 32 + m_l;
+          v[j] = make_uint4(0, 0, 0, 0);
+          if (n < N && cok) v[j] = *(const uint4*)(mat + (int64_t)n * r + c);
+        }
+      } else {
+        // rows sl*16 .. +15 of A_a (zero past rank r), columns nw .. nw + 63
+        // (zero past N), 16 bytes per lane and load
+        const int nw = n0 + wn * WN;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int q = lane + 64 * t;
+          const int row = q >> 3, cc = q & 7;
+          uint4 val = make_uint4(0, 0, 0, 0);
+          if (sl * 16 + row < r && nw + cc * 8 < N)
+            val = *(const uint4*)(mat + (int64_t)(sl * 16 + row) * ep.lmat_ld + nw + cc * 8);
+          slab[row * (SLAB_LD / 8) + cc] = val;
+        }
+        // lane: column j*32 + m_l, ranks 8*half + 0..3 and 4..7 of the slice
+        const int q = (lane >> 2) & 3, jj = lane & 3;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int col = j * 32 + 16 * ((lane >> 4) & 1) + 4 * jj;
+          const uint32_t off = (uint32_t)(((8 * half + q) * SLAB_LD + col) * 2);
+          const uint2 lo4 = tr_read(slab, off);
+          const uint2 hi4 = tr_read(slab, off + 4 * SLAB_LD * 2);
+          v[j] = make_uint4(lo4.x, lo4.y, hi4.x, hi4.y);
+        }
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -178,16 +212,21 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_nt_kernel(const uint16_t* __
                                                          int N, int K, int64_t lda, int64_t ldb,
                                                          GemmEpi ep, int tiles_m, int tiles_n,
                                                          int group_m) {
-  // ---- tile id: XCD-contiguous, then grouped along M
-  const int num = tiles_m * tiles_n;
+  // ---- tile id: XCD-contiguous, then grouped along M.  Grouped launches are
+  // sized for a bound on the row tiles; the live count comes from the device
+  // prefix, and the live tiles are split evenly over the XCDs (the surplus
+  // blocks of every XCD exit), so no XCD is left with only dead tiles.
+  const int live_m = ep.g_tile ? ep.g_tile[ep.n_groups] : tiles_m;   // <= tiles_m
+  const int num = live_m * tiles_n;
   const int bid = blockIdx.x;
   const int xcd = bid & 7, loc = bid >> 3;
   const int per = num >> 3, rem = num & 7;
+  if (loc >= per + (xcd < rem ? 1 : 0)) return;
   const int t = (xcd < rem) ? xcd * (per + 1) + loc : rem * (per + 1) + (xcd - rem) * per + loc;
   const int gsz = group_m * tiles_n;
   const int grp = t / gsz;
   const int first_m = grp * group_m;
-  const int gm = min(tiles_m - first_m, group_m);
+  const int gm = min(live_m - first_m, group_m);
   const int in = t - grp * gsz;
   const int tm = first_m + in % gm;
   const int tn = in / gm;
@@ -195,7 +234,6 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_nt_kernel(const uint16_t* __
   const int n0 = tn * GBN;
   int Mlim = M;   // positions >= Mlim are past this tile's row range
   if (ep.g_tile) {
-    if (tm >= ep.g_tile[ep.n_groups]) return;   // past the last group's tiles
     const int g = find_bucket(ep.g_tile, ep.n_groups + 1, tm);
     m0 = ep.g_off[g * ep.g_stride] + (tm - ep.g_tile[g]) * GBM;
     Mlim = ep.g_off[(g + 1) * ep.g_stride];
@@ -399,7 +437,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_nt_kernel(const uint16_t* __
 #pragma unroll
           for (int g = 0; g < 16; ++g) acc[i][j][g] *= rs[i];
     }
-    if (ep.vec) lora_slab(ep, n0, N, wn, lane, tok, ad, acc);
+    if (ep.vec) lora_slab(ep, n0, N, wn, lane, wave, tok, ad, acc);
     __syncthreads();   // every wave is done reading the ring
     stage_rows();
 #pragma unroll
@@ -557,6 +595,7 @@ lora_status gemm_nt_rows(const uint16_t* A, const uint16_t* B, uint16_t* C, int 
   ep.vec_plane = f.vec_plane;
   ep.vec_ld = f.vec_ld;
   ep.use_b_off = f.use_b_off;
+  ep.lmat_ld = f.lmat_ld;
   ep.lmat = f.lmat;
   ep.desc = f.desc;
   ep.adpos = f.adpos;

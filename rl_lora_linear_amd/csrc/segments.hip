@@ -5,7 +5,7 @@
 //   seg_hist     one block per chunk of 256 tokens: LDS histogram of the
 //                chunk's keys (key n_keys collects invalid ids) -> hist[key][chunk];
 //                range check and, for sorted input, the monotonicity check.
-//   seg_keyscan  one thread per key: exclusive prefix over its chunks (in place)
+//   seg_keyscan  one wave per key: exclusive prefix over its chunks (in place)
 //                and the key total.
 //   seg_offsets  one block: exclusive scan of the key totals -> offsets, plus
 //                the per-key tile/chunk prefix sums the LoRA kernels index by.
@@ -42,24 +42,27 @@ __global__ void seg_zero_kernel(int32_t* __restrict__ p, int64_t n) {
   for (int64_t j = i; j < n; j += (int64_t)gridDim.x * blockDim.x) p[j] = 0;
 }
 
-// One thread per key: exclusive prefix of the key's chunk counts (in place)
-// and its total.  With descriptor tables, also decide whether key k is
-// usable: in every table, rank 8..64, a multiple of 8 and <= max_rank;
-// offsets non-negative, 8-element aligned and inside the packs.  A rank of 0
-// marks "no adapter" (inactive, no flag); other unusable entries set
-// LORA_FLAG_BAD_DESC.  Inactive keys are treated as having no tokens by the
-// LoRA kernels.
+// One wave per key: exclusive prefix of the key's chunk counts (in place, 64
+// chunks per pass so the row is read and written coalesced) and its total.
+// With descriptor tables, also decide whether key k is usable: in every table,
+// rank 8..64, a multiple of 8 and <= max_rank; offsets non-negative, 8-element
+// aligned and inside the packs.  A rank of 0 marks "no adapter" (inactive, no
+// flag); other unusable entries set LORA_FLAG_BAD_DESC.  Inactive keys are
+// treated as having no tokens by the LoRA kernels.
 struct SegTabs {
   lora_host::SegDescs tab[3];
   int32_t n_tabs;
 };
 
-__global__ void seg_keyscan_kernel(int32_t* __restrict__ hist, int n_keys, int n_chunks,
-                                   int32_t* __restrict__ totals, SegTabs tabs, int max_rank,
-                                   uint8_t* __restrict__ active, int32_t* status) {
-  const int k = blockIdx.x * blockDim.x + threadIdx.x;
+constexpr int KEYSCAN_WAVES = 4;
+
+__global__ __launch_bounds__(KEYSCAN_WAVES * kWave) void seg_keyscan_kernel(
+    int32_t* __restrict__ hist, int n_keys, int n_chunks, int32_t* __restrict__ totals,
+    SegTabs tabs, int max_rank, uint8_t* __restrict__ active, int32_t* status) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int k = blockIdx.x * KEYSCAN_WAVES + (int)(threadIdx.x / kWave);  // wave-uniform
   if (k > n_keys) return;
-  if (tabs.n_tabs > 0 && k < n_keys) {
+  if (tabs.n_tabs > 0 && k < n_keys && lane == 0) {
     bool on = true;
     for (int i = 0; i < tabs.n_tabs; ++i) {
       const lora_host::SegDescs& t = tabs.tab[i];
@@ -79,12 +82,19 @@ __global__ void seg_keyscan_kernel(int32_t* __restrict__ hist, int n_keys, int n
   }
   int32_t* row = hist + (int64_t)k * n_chunks;
   int32_t run = 0;
-  for (int c = 0; c < n_chunks; ++c) {
-    int32_t v = row[c];
-    row[c] = run;
-    run += v;
+  for (int c0 = 0; c0 < n_chunks; c0 += kWave) {
+    const int c = c0 + lane;
+    const int32_t v = c < n_chunks ? row[c] : 0;
+    int32_t x = v;  // inclusive scan across the wave
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int32_t y = __shfl_up(x, o, kWave);
+      if (lane >= o) x += y;
+    }
+    if (c < n_chunks) row[c] = run + x - v;
+    run += __shfl(x, kWave - 1, kWave);
   }
-  totals[k] = run;
+  if (lane == 0) totals[k] = run;
 }
 
 // One block of 1024 threads: exclusive scan of the key totals -> offsets.
@@ -492,7 +502,8 @@ lora_status run_segments(const int32_t* ids, int64_t n, int32_t n_keys, int32_t 
     lora_status st = launch_check("seg_zero");
     if (st) return st;
   }
-  hipLaunchKernelGGL(seg_keyscan_kernel, dim3((unsigned)cdiv(n_keys + 1, 256)), dim3(256), 0, s,
+  hipLaunchKernelGGL(seg_keyscan_kernel, dim3((unsigned)cdiv(n_keys + 1, KEYSCAN_WAVES)),
+                     dim3(KEYSCAN_WAVES * kWave), 0, s,
                      hist, n_keys, (int)chunks, totals, tabs, ex ? ex->max_rank : 0,
                      ex ? ex->active : nullptr, status);
   lora_status st = launch_check("seg_keyscan");

@@ -60,13 +60,18 @@ __device__ __forceinline__ ItemRange xcd_items(int total) {
 
 // ------------------------------------------------------------------ shrink
 // out[t][c] = sum_k in[t][k] M_a[c][k] for the 32 rows of one adapter tile.
-// Rows (gathered through perm) and the factor rows M_a[0..r) stream through a
-// 5-stage LDS ring of k = 128 slices by LDS-DMA (issued from inline assembly,
-// four stages ahead, explicit vmcnt waits; the compiler cannot track which
-// stage a DMA writes).  Each LDS row is 256 B = 16 chunks, chunk c stored at
-// c ^ (row & 15), so the fragment reads of 16 consecutive rows are
+// Rows (gathered through perm) and the factor M_a stream through a 5-stage
+// LDS ring of k = 128 slices by LDS-DMA (issued from inline assembly, four
+// stages ahead, explicit vmcnt waits; the compiler cannot track which stage a
+// DMA writes).  Each LDS row of the token tile is 256 B = 16 chunks, chunk c
+// stored at c ^ (row & 15), so the fragment reads of 16 consecutive rows are
 // conflict-free.  Wave w multiplies k-sub-block w (32 k) of every stage; the
 // four partial products are summed in LDS in wave order at the end.
+// The factor is either A_a (KM = false: [r][K], one LDS row per rank, stored
+// like the token rows) or B_a read in place for M_a = B_a^T (KM = true:
+// B_a is [K][r], so a k slice is one contiguous block of 128 x r values; it
+// is copied flat and the MFMA operand, 8 consecutive k of one rank, comes
+// from two transposing reads ds_read_b64_tr_b16).
 constexpr int SH_TM = 32;
 constexpr int SH_KC = 128;
 // Ring depth (deeper rings measured no faster).
@@ -97,7 +102,7 @@ struct ShrinkRows {
   const float* rowscale;
 };
 
-template <int NB>
+template <int NB, bool KM>
 __device__ __forceinline__ void shrink_tile(const uint16_t* __restrict__ in, int64_t ld_in, int K,
                                             const uint16_t* __restrict__ mat, int r, float scale,
                                             const ShrinkRows rm, int p0, int rows,
@@ -121,14 +126,22 @@ __device__ __forceinline__ void shrink_tile(const uint16_t* __restrict__ in, int
     xchunk[i] = (lane & 15) ^ (row & 15);
     xsrc[i] = in + (int64_t)t * ld_in;
   }
+  // factor sources: KM = false, rank row c, chunk mchunk; KM = true, flat
+  // element offset of this lane's 16 bytes within a k slice (128 rows of r)
   const uint16_t* msrc[NB];
   int mchunk[NB];
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
-    const int c = (wave * NB + i) * 4 + (lane >> 4);
-    mchunk[i] = (lane & 15) ^ (c & 15);
-    msrc[i] = mat + (int64_t)(c < r ? c : r - 1) * K;
+    if constexpr (KM) {
+      msrc[i] = mat;
+      mchunk[i] = ((wave * NB + i) * 64 + lane) * 8;
+    } else {
+      const int c = (wave * NB + i) * 4 + (lane >> 4);
+      mchunk[i] = (lane & 15) ^ (c & 15);
+      msrc[i] = mat + (int64_t)(c < r ? c : r - 1) * K;
+    }
   }
+  const int64_t m_last = (int64_t)K * r - 8;   // KM: last 16-byte source of the factor
   auto issue = [&](int st, int kt) {
     const int k0 = kt * SH_KC;
     uint4* base = lds + st * STAGE;
@@ -139,8 +152,16 @@ __device__ __forceinline__ void shrink_tile(const uint16_t* __restrict__ in, int
     }
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
-      const int k = min(k0 + mchunk[i] * 8, K - 8);
-      dma16(msrc[i] + k, __builtin_amdgcn_readfirstlane(lds_u32(base + SH_XSLOTS + (wave * NB + i) * 64)));
+      const uint32_t dst =
+          __builtin_amdgcn_readfirstlane(lds_u32(base + SH_XSLOTS + (wave * NB + i) * 64));
+      if constexpr (KM) {
+        // past the factor's last row: clamped; those values only meet k >= K,
+        // which no wave multiplies
+        dma16(msrc[i] + min((int64_t)k0 * r + mchunk[i], m_last), dst);
+      } else {
+        const int k = min(k0 + mchunk[i] * 8, K - 8);
+        dma16(msrc[i] + k, dst);
+      }
     }
   };
 
@@ -170,8 +191,19 @@ __device__ __forceinline__ void shrink_tile(const uint16_t* __restrict__ in, int
       }
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
-        const int c = b * 16 + fr;
-        mb[b] = as_bf16x8(mt[c * 16 + (ch ^ (c & 15))]);
+        if constexpr (KM) {
+          // rows k = 8 ch + {0..3} and {4..7}; in each 16-lane group, lane 4q + j
+          // addresses row k0 + q, ranks 16 b + 4 j .. + 3, and receives rank
+          // 16 b + (lane & 15) of the four rows
+          const int q = (lane >> 2) & 3, j = lane & 3;
+          const uint32_t off = (uint32_t)(((8 * ch + q) * r + 16 * b + 4 * j) * 2);
+          const uint2 lo = tr_read(mt, off);
+          const uint2 hi = tr_read(mt, off + (uint32_t)(4 * r * 2));
+          mb[b] = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+        } else {
+          const int c = b * 16 + fr;
+          mb[b] = as_bf16x8(mt[c * 16 + (ch ^ (c & 15))]);
+        }
       }
 #pragma unroll
       for (int g = 0; g < 2; ++g)
@@ -223,7 +255,7 @@ __device__ __forceinline__ void shrink_tile(const uint16_t* __restrict__ in, int
 // belong to no active adapter (adpos == -1), and block 0 clears `zero`.
 __global__ __launch_bounds__(256) void shrink_kernel(
     const uint16_t* __restrict__ in, int64_t ld_in, int K, const uint16_t* __restrict__ mat_pack,
-    int use_b_off, const lora_adapter_desc* __restrict__ desc, const int32_t* __restrict__ adpos,
+    int from_b, const lora_adapter_desc* __restrict__ desc, const int32_t* __restrict__ adpos,
     const ShrinkRows rm, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ pre32, int n_ad, int64_t n_tokens, uint16_t* __restrict__ out,
     int r_max, uint4* __restrict__ zero) {
@@ -236,14 +268,24 @@ __global__ __launch_bounds__(256) void shrink_kernel(
     tile_of(pre32, offsets, n_ad, item, SH_TM, ti);
     const lora_adapter_desc d = desc[ti.a];
     const int r = d.rank;
-    const uint16_t* mat = mat_pack + (use_b_off ? d.b_off : d.a_off);
+    const uint16_t* mat = mat_pack + (from_b ? d.b_off : d.a_off);
     const int nb = (r + 15) / 16;
     const float sc = d.scale;
     __syncthreads();   // the previous item's LDS reads are done before the ring refills
-    if (nb == 1) shrink_tile<1>(in, ld_in, K, mat, r, sc, rm, ti.p0, ti.rows, sh_lds, out, plane, r_max);
-    else if (nb == 2) shrink_tile<2>(in, ld_in, K, mat, r, sc, rm, ti.p0, ti.rows, sh_lds, out, plane, r_max);
-    else if (nb == 3) shrink_tile<3>(in, ld_in, K, mat, r, sc, rm, ti.p0, ti.rows, sh_lds, out, plane, r_max);
-    else shrink_tile<4>(in, ld_in, K, mat, r, sc, rm, ti.p0, ti.rows, sh_lds, out, plane, r_max);
+#define SHRINK_TILE(NB, KM) \
+  shrink_tile<NB, KM>(in, ld_in, K, mat, r, sc, rm, ti.p0, ti.rows, sh_lds, out, plane, r_max)
+    if (from_b) {
+      if (nb == 1) SHRINK_TILE(1, true);
+      else if (nb == 2) SHRINK_TILE(2, true);
+      else if (nb == 3) SHRINK_TILE(3, true);
+      else SHRINK_TILE(4, true);
+    } else {
+      if (nb == 1) SHRINK_TILE(1, false);
+      else if (nb == 2) SHRINK_TILE(2, false);
+      else if (nb == 3) SHRINK_TILE(3, false);
+      else SHRINK_TILE(4, false);
+    }
+#undef SHRINK_TILE
   }
   if (blockIdx.x == 0 && zero != nullptr && tid < 16) zero[tid] = make_uint4(0, 0, 0, 0);
   for (int64_t p = (int64_t)blockIdx.x * 256 + tid; p < n_tokens; p += (int64_t)gridDim.x * 256) {
@@ -281,18 +323,6 @@ template <int PN> struct GrP {
 // 32 B; fq spreads those rows (and the rows of the next 16-lane group, 8 rows
 // further) over distinct banks.
 __device__ __forceinline__ int gr_fq(int t) { return (2 * (t & 3)) | (8 * ((t >> 3) & 1)); }
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ uint2 tr_read(const uint4* base, uint32_t byte_off) {
-  s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s16x4*)((__attribute__((address_space(3))) char*)(
-                                                     (__attribute__((address_space(3))) void*)base) +
-                                                 byte_off));
-  union { s16x4 s; uint2 u; } c;
-  c.s = v;
-  return c.u;
-}
 
 // T[c][j] = sum_{t in chunk} P[t][c] Q[t][j] for one chunk of one adapter and
 // 256 columns j.  P is the scaled per-token vector stored as two bf16 planes
@@ -551,41 +581,6 @@ __global__ __launch_bounds__(256) void grad_finalize_kernel(
   }
 }
 
-// ------------------------------------------------------------------ adapter transposes
-// AT[a_off + k*r + c] = A[a_off + c*d_in + k]  (A_a^T, [d_in][r])
-// BT[b_off + c*d_out + j] = B[b_off + j*r + c]  (B_a^T, [r][d_out])
-__global__ __launch_bounds__(256) void adapter_transpose_kernel(
-    const uint16_t* __restrict__ A_pack, const uint16_t* __restrict__ B_pack,
-    const lora_adapter_desc* __restrict__ desc, const uint8_t* __restrict__ active, int64_t d_in,
-    int64_t d_out, uint16_t* __restrict__ AT, uint16_t* __restrict__ BT) {
-  const int a = blockIdx.x;
-  if (!active[a]) return;
-  const lora_adapter_desc d = desc[a];
-  const int r = d.rank;
-  const int groups = r / 8;
-  // A^T: one thread per (k, group of 8 c): 8 strided reads, one 16-byte write
-  for (int64_t e = (int64_t)blockIdx.y * 256 + threadIdx.x; e < d_in * groups;
-       e += (int64_t)gridDim.y * 256) {
-    const int64_t k = e / groups;
-    const int g = (int)(e % groups);
-    uint16_t v[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) v[q] = A_pack[d.a_off + (int64_t)(g * 8 + q) * d_in + k];
-    *(uint4*)(AT + d.a_off + k * r + g * 8) =
-        make_uint4(v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16));
-  }
-  // B^T: one thread per j: one 16-byte read per group, r scattered 2-byte writes
-  for (int64_t j = (int64_t)blockIdx.y * 256 + threadIdx.x; j < d_out; j += (int64_t)gridDim.y * 256) {
-    for (int g = 0; g < groups; ++g) {
-      const uint4 v = *(const uint4*)(B_pack + d.b_off + j * r + g * 8);
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int q = 0; q < 8; ++q)
-        BT[d.b_off + (int64_t)(g * 8 + q) * d_out + j] = (uint16_t)(w[q >> 1] >> ((q & 1) * 16));
-    }
-  }
-}
-
 }  // namespace lora
 
 namespace lora_host {
@@ -602,7 +597,7 @@ static unsigned persistent_blocks() {
 }
 
 lora_status launch_shrink(const uint16_t* in, int64_t ld_in, int K, const uint16_t* mat_pack,
-                          int use_b_off, const lora_adapter_desc* desc, const int32_t* adpos,
+                          int from_b, const lora_adapter_desc* desc, const int32_t* adpos,
                           const int32_t* in_rows, const int32_t* out_rows, const float* rowscale,
                           const int32_t* offsets, const int32_t* pre32, int n_ad,
                           int64_t n_tokens, uint16_t* out, int r_max, void* zero, hipStream_t s) {
@@ -621,7 +616,7 @@ lora_status launch_shrink(const uint16_t* in, int64_t ld_in, int K, const uint16
     attr = lds;
   }
   hipLaunchKernelGGL(shrink_kernel, dim3(persistent_blocks()), dim3(256), lds, s, in, ld_in, K,
-                     mat_pack, use_b_off, desc, adpos, ShrinkRows{in_rows, out_rows, rowscale},
+                     mat_pack, from_b, desc, adpos, ShrinkRows{in_rows, out_rows, rowscale},
                      offsets, pre32, n_ad, n_tokens, out, r_max, (uint4*)zero);
   return launch_check("shrink");
 }
@@ -679,14 +674,5 @@ int64_t grad_partial_floats(int64_t n_tokens, int n_ad, int64_t D, int r_max) {
   return (cdiv(n_tokens, GR_TC) + n_ad) * D * r_max;
 }
 
-lora_status launch_adapter_transpose(const uint16_t* A_pack, const uint16_t* B_pack,
-                                     const lora_adapter_desc* desc, const uint8_t* active,
-                                     int n_ad, int64_t d_in, int64_t d_out, uint16_t* AT,
-                                     uint16_t* BT, hipStream_t s) {
-  const unsigned gy = (unsigned)std::max<int64_t>(1, std::min<int64_t>(64, cdiv(std::max(d_in * 8, d_out), 256)));
-  hipLaunchKernelGGL(adapter_transpose_kernel, dim3(n_ad, gy), dim3(256), 0, s, A_pack, B_pack,
-                     desc, active, d_in, d_out, AT, BT);
-  return launch_check("adapter_transpose");
-}
 
 }  // namespace lora_host

@@ -30,7 +30,8 @@ struct GemmRows {
   const uint16_t* vec = nullptr;
   int64_t vec_plane = 0;
   int vec_ld = 0;
-  int use_b_off = 0;
+  int use_b_off = 0;        // 1: M_a = B_a [N][r] at b_off; 0: A_a [r][lmat_ld] at a_off
+  int64_t lmat_ld = 0;
   const uint16_t* lmat = nullptr;
   const lora_adapter_desc* desc = nullptr;
   const int32_t* adpos = nullptr;
@@ -47,10 +48,12 @@ lora_status gemm_nt_grad(const uint16_t* A, const uint16_t* B, uint16_t* G, int6
                          const float* lse, const float* dlogp, hipStream_t s, int group_m = 0);
 
 // out[out_rows[p]] = bf16 hi/lo planes of s_a * rowscale[p] * (M_a in[in_rows[p]])
-// over positions p < n_tokens (row maps and rowscale nullable); rows of
-// positions without an adapter are zeroed, and `zero` (256 B, nullable) too.
+// over positions p < n_tokens (row maps and rowscale nullable), with M_a = A_a
+// ([r][K] at a_off) or, from_b, M_a = B_a^T (B_a [K][r] at b_off, read in
+// place); rows of positions without an adapter are zeroed, and `zero` (256 B,
+// nullable) too.
 lora_status launch_shrink(const uint16_t* in, int64_t ld_in, int K, const uint16_t* mat_pack,
-                          int use_b_off, const lora_adapter_desc* desc, const int32_t* adpos,
+                          int from_b, const lora_adapter_desc* desc, const int32_t* adpos,
                           const int32_t* in_rows, const int32_t* out_rows, const float* rowscale,
                           const int32_t* offsets, const int32_t* pre32, int n_ad,
                           int64_t n_tokens, uint16_t* out, int r_max, void* zero, hipStream_t s);
@@ -64,10 +67,7 @@ lora_status launch_grad(int mode, const uint16_t* P, int r_max, const void* zero
                         int64_t n_tokens, float* out_pack, float* partial, int accumulate,
                         hipStream_t s);
 int64_t grad_partial_floats(int64_t n_tokens, int n_ad, int64_t D, int r_max);
-lora_status launch_adapter_transpose(const uint16_t* A_pack, const uint16_t* B_pack,
-                                     const lora_adapter_desc* desc, const uint8_t* active,
-                                     int n_ad, int64_t d_in, int64_t d_out, uint16_t* AT,
-                                     uint16_t* BT, hipStream_t s);
+
 
 constexpr int kGradChunk = 1024;  // tokens per gradient chunk (matches the kernel)
 
