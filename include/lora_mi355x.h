@@ -346,9 +346,10 @@ lora_status moe_route(int64_t n, int32_t n_experts, int32_t top_k, const float* 
  * "Position order": the assignments j = t*K + k stably sorted by key
  * e*(n_adapters + 1) + a (a = n_adapters for an adapter id out of range),
  * assignments with an expert id out of range last.  Saved layout, each region
- * starting at a multiple of 256 bytes in this order: g, u, h (bf16 [N*K][F] in
- * position order: gate and up pre-activations, silu(g)*u), then the scaled
- * LoRA vectors s*u of gate, up and down (bf16 hi/lo planes [2][N*K][max_rank]). */
+ * starting at a multiple of 256 bytes in this order: gu (bf16 [N*K][2F] in
+ * position order, each row the gate pre-activation then the up
+ * pre-activation), h (bf16 [N*K][F], silu(gate)*up), then the scaled LoRA
+ * vectors s*u of gate, up and down (bf16 hi/lo planes [2][N*K][max_rank]). */
 size_t moe_workspace_bytes(const moe_shape* shape);
 size_t moe_saved_bytes(const moe_shape* shape);
 
@@ -366,8 +367,9 @@ lora_status moe_forward(const moe_shape* shape, const uint16_t* x, const int32_t
 /*   dy bf16 [N][H]; dx bf16 [N][H] out; d*_pack fp32 gradient packs with the
  *   A/B packs' offsets: accumulate = 0 overwrites every active pair's region
  *   (zeros for pairs without assignments), != 0 adds into it.  Deterministic.
- *   trace (nullable): bf16 [3][N*K][F] out, the stage tensors dh, dg, du in
- *   position order (for per-stage verification). */
+ *   trace (nullable): bf16 [3*N*K*F] out, the stage tensors in position
+ *   order (for per-stage verification): dh [N*K][F], then [N*K][2F] rows of
+ *   d(gate pre-activation) followed by d(up pre-activation). */
 lora_status moe_backward(const moe_shape* shape, const uint16_t* dy, const uint16_t* x,
                          const int32_t* experts, const float* weights, const int32_t* adapter_ids,
                          const uint16_t* W_gate_t, const uint16_t* W_up_t,

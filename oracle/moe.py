@@ -18,7 +18,8 @@ A [r, F], B [H, r].
 `store(name, js, value)` (default: return value) is called wherever an
 implementation keeps a per-assignment intermediate: name is one of "g", "u"
 (gate/up pre-activations), "h", "o" (expert output), "dh", "dg", "du",
-"dx_gate", "dx_up"; js are the assignment indices of the rows.  Whatever it
+"dx_e" (the assignment's dx, gate and up parts summed); js are the assignment
+indices of the rows.  Whatever it
 returns is used from there on, so a test can continue the oracle from a
 device layer's own stored bits (per-call parity through a fused layer) and
 compare each intermediate on the way; with the default the functions are the
@@ -117,8 +118,8 @@ def moe_backward(dy, x, experts, weights, ids, Wg, Wu, Wd, A, B, scale, saved, s
         for p, Wp, d in (("gate", Wg, dg), ("up", Wu, du)):
             Ap, Bp = A[p][a][e], B[p][a][e]
             vp = d @ Bp
-            dxs += st("dx_" + p, js, d @ Wp[e] + scale * vp @ Ap)
+            dxs += d @ Wp[e] + scale * vp @ Ap
             dB[p][a][e] += scale * d.T @ (xs @ Ap.T)
             dA[p][a][e] += scale * vp.T @ xs
-        np.add.at(dx, ts, dxs)
+        np.add.at(dx, ts, st("dx_e", js, dxs))
     return dx, dA, dB

@@ -558,18 +558,15 @@ struct MoeWs {
   uint16_t* v[3];    // backward: s*v planes per projection [2][NK][R] (down: s*w*v)
   uint16_t* uw;      // backward: w * (s u_down) planes
   uint16_t* dh;      // [NK][F]
-  uint16_t* dg;      // [NK][F]
-  uint16_t* du;      // [NK][F]
-  uint16_t* dxg;     // [NK][H]
-  uint16_t* dxu;     // [NK][H]
+  uint16_t* dgu;     // [NK][2F]: d(gate pre-activation) | d(up pre-activation)
+  uint16_t* dxp;     // [NK][H]: per-assignment dx (gate and up parts summed)
   float* partial;
   size_t total;
 };
 
 struct MoeSaved {
-  uint16_t* g;       // gate pre-activation [NK][F] bf16
-  uint16_t* u;       // up pre-activation
-  uint16_t* h;       // silu(g) * u
+  uint16_t* gu;      // [NK][2F] bf16: gate pre-activation | up pre-activation
+  uint16_t* h;       // [NK][F] silu(gate) * up
   uint16_t* su[3];   // s*u planes per projection [2][NK][R]
   size_t total;
 };
@@ -578,8 +575,7 @@ MoeSaved carve_saved(const moe_shape& sh, void* p) {
   Carve cv(p, 0);
   const size_t NK = (size_t)std::max<int64_t>(sh.n_tokens * sh.top_k, 1);
   MoeSaved m{};
-  m.g = cv.take<uint16_t>(NK * sh.d_ff);
-  m.u = cv.take<uint16_t>(NK * sh.d_ff);
+  m.gu = cv.take<uint16_t>(NK * 2 * sh.d_ff);
   m.h = cv.take<uint16_t>(NK * sh.d_ff);
   for (int i = 0; i < 3; ++i) m.su[i] = cv.take<uint16_t>(2 * NK * sh.max_rank);
   m.total = cv.used;
@@ -613,10 +609,8 @@ MoeWs carve_moe(const moe_shape& sh, void* ws, size_t bytes, bool backward) {
     for (int i = 0; i < 3; ++i) w.v[i] = cv.take<uint16_t>((size_t)2 * NK * sh.max_rank);
     w.uw = cv.take<uint16_t>((size_t)2 * NK * sh.max_rank);
     w.dh = cv.take<uint16_t>((size_t)NK * sh.d_ff);
-    w.dg = cv.take<uint16_t>((size_t)NK * sh.d_ff);
-    w.du = cv.take<uint16_t>((size_t)NK * sh.d_ff);
-    w.dxg = cv.take<uint16_t>((size_t)NK * sh.hidden);
-    w.dxu = cv.take<uint16_t>((size_t)NK * sh.hidden);
+    w.dgu = cv.take<uint16_t>((size_t)NK * 2 * sh.d_ff);
+    w.dxp = cv.take<uint16_t>((size_t)NK * sh.hidden);
     w.partial = cv.take<float>((size_t)grad_partial_floats(NK, n_keys,
                                                           std::max(sh.hidden, sh.d_ff),
                                                           sh.max_rank));
@@ -658,15 +652,38 @@ lora_status moe_segments(const moe_shape& sh, const int32_t* experts, const int3
                       w.seg_bytes, s);
 }
 
+// Second weight set of a fused pair of expert projections (gate and up):
+// split = 1: a second product of n_out columns written at column n_out
+// (forward, [gate | up] rows); split = 2: K = 2 k_in, the second half of each
+// A row against W2 (backward dX, both expands added).
+struct MoePair {
+  int split = 0;
+  const uint16_t* W2 = nullptr;
+  const uint16_t* planes2 = nullptr;
+  const uint16_t* lmat2 = nullptr;
+  const lora_adapter_desc* desc2 = nullptr;
+};
+
 // One grouped expert projection over the sorted assignments: rows gathered
 // through a_rows (nullable), base weights per expert, the LoRA expand fused.
 lora_status moe_project(const moe_shape& sh, const MoeWs& w, const uint16_t* A,
                         const int32_t* a_rows, int64_t a_rows_bound, const uint16_t* W,
                         int64_t n_out, int64_t k_in, const uint16_t* planes,
                         const uint16_t* lmat, int use_b_off, const lora_adapter_desc* desc,
-                        const float* rowscale, uint16_t* C, hipStream_t s) {
+                        const float* rowscale, uint16_t* C, hipStream_t s,
+                        const MoePair& pair = MoePair{}) {
   const int64_t NK = sh.n_tokens * sh.top_k;
   GemmRows f;
+  f.B2 = pair.W2;
+  f.vec2 = pair.planes2;
+  f.lmat2 = pair.lmat2;
+  f.desc2 = pair.desc2;
+  f.n_split = pair.split == 1;
+  f.c_off2 = pair.split == 1 ? n_out : 0;
+  f.k_split = pair.split == 2 ? (int)k_in : 0;
+  const int64_t K = pair.split == 2 ? 2 * k_in : k_in;      // columns of A read
+  const int64_t lda = a_rows ? k_in : K;                      // gathered rows: x itself
+  const int64_t ldc = pair.split == 1 ? 2 * n_out : n_out;
   f.a_rows = a_rows;
   f.a_rows_bound = a_rows_bound;
   f.rowscale = rowscale;
@@ -686,7 +703,7 @@ lora_status moe_project(const moe_shape& sh, const MoeWs& w, const uint16_t* A,
   f.adpos = w.adpos;
   f.n_ad = sh.n_experts * (sh.n_adapters + 1);
   timer_begin(LORA_TIMER_BASE_GEMM, s);
-  TRY(gemm_nt_rows(A, W, C, (int)NK, (int)n_out, (int)k_in, k_in, k_in, n_out, f, s));
+  TRY(gemm_nt_rows(A, W, C, (int)NK, (int)n_out, (int)K, lda, k_in, ldc, f, s));
   timer_end(LORA_TIMER_BASE_GEMM, s);
   return LORA_OK;
 }
@@ -747,17 +764,27 @@ lora_status moe_forward(const moe_shape* shape, const uint16_t* x, const int32_t
   const int n_keys = sh.n_experts * (sh.n_adapters + 1);
   const lora_adapter_desc* const descs[3] = {gate_desc, up_desc, down_desc};
   TRY(moe_segments(sh, experts, adapter_ids, descs, w, s));
-  // gate and up: s*u planes from the gathered token rows, then the grouped GEMM
-  const uint16_t* packs[2] = {gate_pack, up_pack};
-  const uint16_t* Ws[2] = {W_gate, W_up};
-  uint16_t* pre[2] = {sv.g, sv.u};
-  for (int i = 0; i < 2; ++i) {
-    TRY(launch_shrink(x, H, (int)H, packs[i], 0, w.desc[i], w.adpos, w.tokrow, nullptr, nullptr,
-                      w.offsets, w.pre32, n_keys, NK, sv.su[i], R, w.zero, s));
-    TRY(moe_project(sh, w, x, w.tokrow, sh.n_tokens, Ws[i], F, H, sv.su[i], packs[i], 1,
-                    w.desc[i], nullptr, pre[i], s));
+  // gate and up: s*u planes from the gathered token rows (one pass over x when
+  // both fit one tile), then one grouped GEMM writing [gate | up] rows
+  if (R <= 32) {
+    TRY(launch_shrink(x, H, (int)H, gate_pack, 0, w.desc[0], w.adpos, w.tokrow, nullptr, nullptr,
+                      w.offsets, w.pre32, n_keys, NK, sv.su[0], R, w.zero, s, up_pack, w.desc[1],
+                      sv.su[1]));
+  } else {
+    TRY(launch_shrink(x, H, (int)H, gate_pack, 0, w.desc[0], w.adpos, w.tokrow, nullptr, nullptr,
+                      w.offsets, w.pre32, n_keys, NK, sv.su[0], R, w.zero, s));
+    TRY(launch_shrink(x, H, (int)H, up_pack, 0, w.desc[1], w.adpos, w.tokrow, nullptr, nullptr,
+                      w.offsets, w.pre32, n_keys, NK, sv.su[1], R, w.zero, s));
   }
-  TRY(launch_swiglu_fwd(NK * F, sv.g, sv.u, sv.h, s));
+  MoePair gu;
+  gu.split = 1;
+  gu.W2 = W_up;
+  gu.planes2 = sv.su[1];
+  gu.lmat2 = up_pack;
+  gu.desc2 = w.desc[1];
+  TRY(moe_project(sh, w, x, w.tokrow, sh.n_tokens, W_gate, F, H, sv.su[0], gate_pack, 1,
+                  w.desc[0], nullptr, sv.gu, s, gu));
+  TRY(launch_swiglu_rows_fwd(NK, F, sv.gu, sv.h, s));
   // down, then the weighted combine back to tokens
   TRY(launch_shrink(sv.h, F, (int)F, down_pack, 0, w.desc[2], w.adpos, nullptr, nullptr, nullptr,
                     w.offsets, w.pre32, n_keys, NK, sv.su[2], R, w.zero, s));
@@ -792,12 +819,10 @@ lora_status moe_backward(const moe_shape* shape, const uint16_t* dy, const uint1
     set_error("moe_backward: workspace %zu bytes < %zu needed", ws_bytes, w.total);
     return LORA_E_WORKSPACE;
   }
-  if (trace) {   // the caller keeps dh, dg, du
+  if (trace) {   // the caller keeps dh and [dgate | dup]
     LORA_ARG_CHECK(aligned16(trace), "trace must be 16-byte aligned");
-    const int64_t nf = sh.n_tokens * sh.top_k * sh.d_ff;
     w.dh = trace;
-    w.dg = trace + nf;
-    w.du = trace + 2 * nf;
+    w.dgu = trace + sh.n_tokens * sh.top_k * sh.d_ff;
   }
   hipStream_t s = S(stream);
   const MoeSaved sv = carve_saved(sh, const_cast<void*>(saved));
@@ -822,24 +847,31 @@ lora_status moe_backward(const moe_shape* shape, const uint16_t* dy, const uint1
                   w.prec, n_keys, NK, grads[2], w.partial, accumulate, s));
   TRY(launch_grad(1, w.v[2], R, w.zero, sv.h, F, (int)F, w.desc[2], w.active, nullptr, 1,
                   w.offsets, w.prec, n_keys, NK, grads[2], w.partial, accumulate, s));
-  if (NK > 0) TRY(launch_swiglu_bwd(NK * F, w.dh, sv.g, sv.u, w.dg, w.du, s));
-  // gate and up: v = s B^T d; dx_j = d W + A^T v; dB = sum d (s u)^T; dA = sum v x_t^T
-  uint16_t* dpre[2] = {w.dg, w.du};
-  uint16_t* dxp[2] = {w.dxg, w.dxu};
-  const uint16_t* Wts[2] = {W_gate_t, W_up_t};
+  if (NK > 0) {
+    TRY(launch_swiglu_rows_bwd(NK, F, w.dh, sv.gu, w.dgu, s));
+    // gate and up: v = s B^T d per projection; dx_j = [dg | du] [W_gate; W_up]
+    // (one K-concatenated GEMM) + A_gate^T v_gate + A_up^T v_up
+    for (int i = 0; i < 2; ++i)
+      TRY(launch_shrink(w.dgu + i * F, 2 * F, (int)F, packs[i], 1, w.desc[i], w.adpos, nullptr,
+                        nullptr, nullptr, w.offsets, w.pre32, n_keys, NK, w.v[i], R, w.zero, s));
+    MoePair gu;
+    gu.split = 2;
+    gu.W2 = W_up_t;
+    gu.planes2 = w.v[1];
+    gu.lmat2 = up_pack;
+    gu.desc2 = w.desc[1];
+    TRY(moe_project(sh, w, w.dgu, nullptr, NK, W_gate_t, H, F, w.v[0], gate_pack, 0, w.desc[0],
+                    nullptr, w.dxp, s, gu));
+  }
+  // dB = sum d (s u)^T; dA = sum (s v) x_t^T
   for (int i = 0; i < 2; ++i) {
-    if (NK > 0) {
-      TRY(launch_shrink(dpre[i], F, (int)F, packs[i], 1, w.desc[i], w.adpos, nullptr, nullptr,
-                        nullptr, w.offsets, w.pre32, n_keys, NK, w.v[i], R, w.zero, s));
-      TRY(moe_project(sh, w, dpre[i], nullptr, NK, Wts[i], H, F, w.v[i], packs[i], 0, w.desc[i],
-                      nullptr, dxp[i], s));
-    }
-    TRY(launch_grad(0, sv.su[i], R, w.zero, dpre[i], F, (int)F, w.desc[i], w.active, nullptr, 1,
-                    w.offsets, w.prec, n_keys, NK, grads[i], w.partial, accumulate, s));
+    TRY(launch_grad(0, sv.su[i], R, w.zero, w.dgu + i * F, 2 * F, (int)F, w.desc[i], w.active,
+                    nullptr, 1, w.offsets, w.prec, n_keys, NK, grads[i], w.partial, accumulate, s));
     TRY(launch_grad(1, w.v[i], R, w.zero, x, H, (int)H, w.desc[i], w.active, w.tokrow, 1,
                     w.offsets, w.prec, n_keys, NK, grads[i], w.partial, accumulate, s));
   }
-  return launch_moe_combine(w.dxg, w.dxu, nullptr, w.inv, w.keys, sh.n_tokens, sh.top_k, H, dx, s);
+  return launch_moe_combine(w.dxp, nullptr, nullptr, w.inv, w.keys, sh.n_tokens, sh.top_k, H, dx,
+                            s);
 }
 
 lora_status bf16_add(int64_t n, const uint16_t* a, const uint16_t* b, uint16_t* out,

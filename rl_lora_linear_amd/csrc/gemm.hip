@@ -58,6 +58,19 @@ struct GemmEpi {
   int64_t lmat_ld;
   const uint16_t* lmat;
   const lora_adapter_desc* desc;
+  // A second weight operand B2 (same ldb and group stride as B), two ways:
+  //   n_tiles1 > 0 (N split): column tiles >= n_tiles1 are the second product,
+  //     reading B2 and writing output columns c_off2 + n; its LoRA expand uses
+  //     the second set (vec2, lmat2, desc2);
+  //   k_split > 0 (K split, a multiple of 32): k >= k_split reads B2 at
+  //     column k - k_split, and both LoRA sets are added to every row.
+  const uint16_t* B2;
+  int n_tiles1;
+  int64_t c_off2;
+  int k_split;
+  const uint16_t* vec2;
+  const uint16_t* lmat2;
+  const lora_adapter_desc* desc2;
   const uint8_t* active;
   const int32_t* adpos;   // [M] adapter of each row position, -1 for rows without one
   int n_ad;
@@ -126,8 +139,10 @@ __device__ __forceinline__ void dma16s(uint32_t voff, const void* base, uint32_t
 // tile (144-byte rows: the transposing reads of 4 rows hit distinct banks) and
 // read back transposed, 8 consecutive ranks of one column per lane.
 constexpr int SLAB_LD = 72;   // bf16 per LDS row of the slab tile
-__device__ __forceinline__ void lora_slab(const GemmEpi& ep, int n0, int N, int wn, int lane,
-                                          int wave, const int (&tok)[4], const int (&ad)[4],
+__device__ __forceinline__ void lora_slab(const GemmEpi& ep, const uint16_t* vec,
+                                          const uint16_t* lmat, const lora_adapter_desc* desc,
+                                          int n0, int N, int wn, int lane, int wave,
+                                          const int (&tok)[4], const int (&ad)[4],
                                           f32x16 (&acc)[4][2]) {
   __shared__ uint4 s_slab[GTHREADS / 64][16 * SLAB_LD / 8];
   uint4* slab = s_slab[wave];
@@ -148,9 +163,9 @@ __device__ __forceinline__ void lora_slab(const GemmEpi& ep, int n0, int N, int 
 #pragma unroll
     for (int i = 0; i < 4; ++i) mine |= ad[i] == a;
     if (!__any(mine)) continue;                     // adapter absent from this wave's rows
-    const lora_adapter_desc d = ep.desc[a];
+    const lora_adapter_desc d = desc[a];
     const int r = d.rank;
-    const uint16_t* mat = ep.lmat + (ep.use_b_off ? d.b_off : d.a_off);
+    const uint16_t* mat = lmat + (ep.use_b_off ? d.b_off : d.a_off);
     for (int sl = 0; sl * 16 < r; ++sl) {
       const int c = sl * 16 + 8 * half;
       const bool cok = c < r;
@@ -159,7 +174,7 @@ __device__ __forceinline__ void lora_slab(const GemmEpi& ep, int n0, int N, int 
       for (int i = 0; i < 4; ++i) {
         h[i] = l[i] = make_uint4(0, 0, 0, 0);
         if (ad[i] == a && cok) {
-          const uint16_t* vp = ep.vec + (int64_t)tok[i] * ep.vec_ld + c;
+          const uint16_t* vp = vec + (int64_t)tok[i] * ep.vec_ld + c;
           h[i] = *(const uint4*)vp;
           l[i] = *(const uint4*)(vp + ep.vec_plane);
         }
@@ -229,15 +244,22 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_nt_kernel(const uint16_t* __
   const int gm = min(live_m - first_m, group_m);
   const int in = t - grp * gsz;
   const int tm = first_m + in % gm;
-  const int tn = in / gm;
+  int tn = in / gm;
+  const bool second = ep.n_tiles1 > 0 && tn >= ep.n_tiles1;   // N split: second product
+  if (second) {
+    tn -= ep.n_tiles1;
+    B = ep.B2;
+  }
   int m0 = tm * GBM;
   const int n0 = tn * GBN;
   int Mlim = M;   // positions >= Mlim are past this tile's row range
+  const uint16_t* B2g = ep.B2;   // K split: second operand of this tile's group
   if (ep.g_tile) {
     const int g = find_bucket(ep.g_tile, ep.n_groups + 1, tm);
     m0 = ep.g_off[g * ep.g_stride] + (tm - ep.g_tile[g]) * GBM;
     Mlim = ep.g_off[(g + 1) * ep.g_stride];
     B += (int64_t)g * ep.ldb_group;
+    if (ep.k_split > 0) B2g = ep.B2 + (int64_t)g * ep.ldb_group;
   }
 
   const int tid = threadIdx.x;
@@ -294,6 +316,10 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_nt_kernel(const uint16_t* __
   uint32_t offA[2], offB[2];
   const uint16_t* baseA = ep.a_rows ? A : A + (int64_t)m0 * lda;
   const uint16_t* baseB = B + (int64_t)n0 * ldb;
+  // K split: k >= ksplit reads the second operand (same row offsets)
+  const int ksplit = ep.k_split > 0 ? ep.k_split : K;
+  const uint16_t* baseB2 = ep.k_split > 0 ? B2g + (int64_t)n0 * ldb : baseB;
+  auto bsrc = [&](int k0) { return k0 < ksplit ? baseB + k0 : baseB2 + (k0 - ksplit); };
   {
     const int lrow = lane >> 2;
     const int chunk = (lane & 3) ^ g4(lrow);
@@ -324,7 +350,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_nt_kernel(const uint16_t* __
 #pragma unroll
     for (int i = 0; i < 2; ++i) dmaA(s, i, baseA + k0);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) dmaB(s, i, baseB + k0);
+    for (int i = 0; i < 2; ++i) dmaB(s, i, bsrc(k0));
   }
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(VM_AHEAD) : "memory");
 
@@ -361,7 +387,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_nt_kernel(const uint16_t* __
     const uint4* Bn = sB + S1 * S_TILE;
     const int k0 = min(kt + NSTAGE - 1, KT - 1) * SBK;
     const uint16_t* ka = baseA + k0;
-    const uint16_t* kb = baseB + k0;
+    const uint16_t* kb = bsrc(k0);
     // phase 0: MFMAs of slice 0; reads of slice 1 (groups 0-5); A DMAs (6, 7)
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
@@ -405,6 +431,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_nt_kernel(const uint16_t* __
   // s_row holds each staged row's destination (-1: not stored).
   __shared__ int s_row[GBM];
   char* T = (char*)g_stage;
+  const int64_t cbase = second ? ep.c_off2 : 0;   // output column of this product's column 0
   auto stage_rows = [&]() {
     if (wn == 0 && lane < 32) {
 #pragma unroll
@@ -424,7 +451,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_nt_kernel(const uint16_t* __
       const int crow = s_row[row];
       const int col = n0 + c * 8;
       const uint4 v = *(const uint4*)(T + row * 512 + ((c ^ (row & 31)) << 4));
-      if (crow >= 0 && col < N) *(uint4*)(ep.C + (int64_t)crow * ep.ldc + col) = v;
+      if (crow >= 0 && col < N) *(uint4*)(ep.C + (int64_t)crow * ep.ldc + cbase + col) = v;
     }
   };
 
@@ -437,7 +464,17 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_nt_kernel(const uint16_t* __
 #pragma unroll
           for (int g = 0; g < 16; ++g) acc[i][j][g] *= rs[i];
     }
-    if (ep.vec) lora_slab(ep, n0, N, wn, lane, wave, tok, ad, acc);
+    if (ep.vec) {
+      // one expand (set 2 for the second product of an N split), or both sets
+      // for a K split; a loop, so the slab is instantiated once
+      const int sets = (ep.k_split > 0 && ep.vec2) ? 2 : 1;
+#pragma unroll 1
+      for (int set = 0; set < sets; ++set) {
+        const bool two = second || set == 1;
+        lora_slab(ep, two ? ep.vec2 : ep.vec, two ? ep.lmat2 : ep.lmat, two ? ep.desc2 : ep.desc,
+                  n0, N, wn, lane, wave, tok, ad, acc);
+      }
+    }
     __syncthreads();   // every wave is done reading the ring
     stage_rows();
 #pragma unroll
@@ -553,7 +590,16 @@ static lora_status launch_gemm(const uint16_t* A, const uint16_t* B, int M, int 
               (long long)(a_rows_bound * lda * 2));
     return LORA_E_UNSUPPORTED;
   }
-  const int tiles_m = ep.g_tile ? tiles_m_bound : (int)cdiv(M, GBM), tiles_n = (int)cdiv(N, GBN);
+  const int tiles_m = ep.g_tile ? tiles_m_bound : (int)cdiv(M, GBM);
+  const int tiles_n = (int)cdiv(N, GBN) * (ep.n_tiles1 > 0 ? 2 : 1);
+  if (ep.k_split > 0 && (ep.k_split % SBK || ep.k_split >= K || !ep.B2)) {
+    set_error("gemm: K split %d must be a multiple of %d below K = %d, with B2", ep.k_split, SBK, K);
+    return LORA_E_INVALID_ARG;
+  }
+  if (ep.n_tiles1 > 0 && !ep.B2) {
+    set_error("gemm: N split needs B2");
+    return LORA_E_INVALID_ARG;
+  }
   if (tiles_m <= 0) return LORA_OK;
   if (group_m <= 0) group_m = pick_group_m(tiles_m);
   if (group_m > tiles_m) group_m = tiles_m;
@@ -598,6 +644,13 @@ lora_status gemm_nt_rows(const uint16_t* A, const uint16_t* B, uint16_t* C, int 
   ep.lmat_ld = f.lmat_ld;
   ep.lmat = f.lmat;
   ep.desc = f.desc;
+  ep.B2 = f.B2;
+  ep.n_tiles1 = f.n_split ? (int)cdiv(N, GBN) : 0;
+  ep.c_off2 = f.c_off2;
+  ep.k_split = f.k_split;
+  ep.vec2 = f.vec2;
+  ep.lmat2 = f.lmat2;
+  ep.desc2 = f.desc2;
   ep.adpos = f.adpos;
   ep.n_ad = f.n_ad;
   return launch_gemm<EPI_BF16>(A, B, M, N, K, lda, ldb, ep, s, group_m, f.a_rows_bound,

@@ -102,12 +102,21 @@ struct ShrinkRows {
   const float* rowscale;
 };
 
+// Second factor of a dual shrink (same input rows, another adapter table, KM
+// = false only): tile ranks [c2, c2 + r) come from mat and go to out.
+struct ShrinkSecond {
+  const uint16_t* mat;   // null: single shrink
+  int r, c2;
+  float scale;
+  uint16_t* out;
+};
+
 template <int NB, bool KM>
 __device__ __forceinline__ void shrink_tile(const uint16_t* __restrict__ in, int64_t ld_in, int K,
                                             const uint16_t* __restrict__ mat, int r, float scale,
-                                            const ShrinkRows rm, int p0, int rows,
-                                            uint4* lds, uint16_t* __restrict__ out, int64_t plane,
-                                            int r_max) {
+                                            const ShrinkSecond sec, const ShrinkRows rm, int p0,
+                                            int rows, uint4* lds, uint16_t* __restrict__ out,
+                                            int64_t plane, int r_max) {
   constexpr int MSLOTS = NB * 16 * 16;                 // factor tile slots per stage
   constexpr int STAGE = SH_XSLOTS + MSLOTS;
   constexpr int PER_WAVE = 2 + NB;                     // DMA instructions per wave per stage
@@ -138,7 +147,12 @@ __device__ __forceinline__ void shrink_tile(const uint16_t* __restrict__ in, int
     } else {
       const int c = (wave * NB + i) * 4 + (lane >> 4);
       mchunk[i] = (lane & 15) ^ (c & 15);
-      msrc[i] = mat + (int64_t)(c < r ? c : r - 1) * K;
+      if (sec.mat && c >= sec.c2) {
+        const int c2 = c - sec.c2;
+        msrc[i] = sec.mat + (int64_t)(c2 < sec.r ? c2 : sec.r - 1) * K;
+      } else {
+        msrc[i] = mat + (int64_t)(c < r ? c : r - 1) * K;
+      }
     }
   }
   const int64_t m_last = (int64_t)K * r - 8;   // KM: last 16-byte source of the factor
@@ -224,30 +238,36 @@ __device__ __forceinline__ void shrink_tile(const uint16_t* __restrict__ in, int
       for (int i = 0; i < 4; ++i)
         red[(wave * SH_TM + g * 16 + 4 * (lane >> 4) + i) * 64 + b * 16 + (lane & 15)] = acc[g][b][i];
   __syncthreads();
-  for (int e = tid; e < SH_TM * (r_max / 4); e += 256) {
-    const int row = e / (r_max / 4), cg = (e % (r_max / 4)) * 4;
-    if (row >= rows) continue;
-    const int prow = p0 + row;
-    const float sc_row = rm.rowscale ? scale * rm.rowscale[prow] : scale;
-    float v[4];
+  // tile ranks [c0, c0 + rr) scaled and split into the planes of dst
+  auto emit = [&](uint16_t* __restrict__ dst, int c0, int rr, float sc) {
+    for (int e = tid; e < SH_TM * (r_max / 4); e += 256) {
+      const int row = e / (r_max / 4), cg = (e % (r_max / 4)) * 4;
+      if (row >= rows) continue;
+      const int prow = p0 + row;
+      const float sc_row = rm.rowscale ? sc * rm.rowscale[prow] : sc;
+      float v[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int c = cg + q;
-      float sacc = 0.f;
-      if (c < r) {
-        sacc = red[(0 * SH_TM + row) * 64 + c] + red[(1 * SH_TM + row) * 64 + c];
-        sacc += red[(2 * SH_TM + row) * 64 + c];
-        sacc += red[(3 * SH_TM + row) * 64 + c];
+      for (int q = 0; q < 4; ++q) {
+        const int c = cg + q;
+        float sacc = 0.f;
+        if (c < rr) {
+          const int rc = c0 + c;
+          sacc = red[(0 * SH_TM + row) * 64 + rc] + red[(1 * SH_TM + row) * 64 + rc];
+          sacc += red[(2 * SH_TM + row) * 64 + rc];
+          sacc += red[(3 * SH_TM + row) * 64 + rc];
+        }
+        v[q] = sc_row * sacc;
       }
-      v[q] = sc_row * sacc;
+      uint32_t h01, l01, h23, l23;
+      split2_bf16(v[0], v[1], h01, l01);
+      split2_bf16(v[2], v[3], h23, l23);
+      uint16_t* o = dst + (int64_t)(rm.out ? rm.out[prow] : prow) * r_max + cg;
+      *(uint2*)o = make_uint2(h01, h23);
+      *(uint2*)(o + plane) = make_uint2(l01, l23);
     }
-    uint32_t h01, l01, h23, l23;
-    split2_bf16(v[0], v[1], h01, l01);
-    split2_bf16(v[2], v[3], h23, l23);
-    uint16_t* o = out + (int64_t)(rm.out ? rm.out[prow] : prow) * r_max + cg;
-    *(uint2*)o = make_uint2(h01, h23);
-    *(uint2*)(o + plane) = make_uint2(l01, l23);
-  }
+  };
+  emit(out, 0, r, scale);
+  if (!KM && sec.mat) emit(sec.out, sec.c2, sec.r, sec.scale);
 }
 
 // One block per CU.  Blocks take the 32-row adapter tiles (pre32[n_ad] of
@@ -258,7 +278,8 @@ __global__ __launch_bounds__(256) void shrink_kernel(
     int from_b, const lora_adapter_desc* __restrict__ desc, const int32_t* __restrict__ adpos,
     const ShrinkRows rm, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ pre32, int n_ad, int64_t n_tokens, uint16_t* __restrict__ out,
-    int r_max, uint4* __restrict__ zero) {
+    int r_max, uint4* __restrict__ zero, const uint16_t* __restrict__ mat_pack2,
+    const lora_adapter_desc* __restrict__ desc2, uint16_t* __restrict__ out2) {
   extern __shared__ uint4 sh_lds[];
   const int tid = threadIdx.x;
   const int64_t plane = n_tokens * r_max;
@@ -269,11 +290,20 @@ __global__ __launch_bounds__(256) void shrink_kernel(
     const lora_adapter_desc d = desc[ti.a];
     const int r = d.rank;
     const uint16_t* mat = mat_pack + (from_b ? d.b_off : d.a_off);
-    const int nb = (r + 15) / 16;
+    int nb = (r + 15) / 16;
     const float sc = d.scale;
+    ShrinkSecond sec{nullptr, 0, 0, 0.f, out2};
+    if (mat_pack2) {   // dual (A factors only; the host keeps both ranks <= 32)
+      const lora_adapter_desc d2 = desc2[ti.a];
+      sec.mat = mat_pack2 + d2.a_off;
+      sec.r = d2.rank;
+      sec.c2 = 16 * nb;
+      sec.scale = d2.scale;
+      nb += (d2.rank + 15) / 16;
+    }
     __syncthreads();   // the previous item's LDS reads are done before the ring refills
 #define SHRINK_TILE(NB, KM) \
-  shrink_tile<NB, KM>(in, ld_in, K, mat, r, sc, rm, ti.p0, ti.rows, sh_lds, out, plane, r_max)
+  shrink_tile<NB, KM>(in, ld_in, K, mat, r, sc, sec, rm, ti.p0, ti.rows, sh_lds, out, plane, r_max)
     if (from_b) {
       if (nb == 1) SHRINK_TILE(1, true);
       else if (nb == 2) SHRINK_TILE(2, true);
@@ -291,9 +321,12 @@ __global__ __launch_bounds__(256) void shrink_kernel(
   for (int64_t p = (int64_t)blockIdx.x * 256 + tid; p < n_tokens; p += (int64_t)gridDim.x * 256) {
     if (adpos[p] >= 0) continue;
     const int64_t orow = rm.out ? rm.out[p] : p;
-    uint4* o = (uint4*)(out + orow * r_max);
-    uint4* ol = (uint4*)(out + plane + orow * r_max);
-    for (int c = 0; c < r_max / 8; ++c) o[c] = ol[c] = make_uint4(0, 0, 0, 0);
+    for (int k = 0; k < (out2 ? 2 : 1); ++k) {
+      uint16_t* ob = k ? out2 : out;
+      uint4* o = (uint4*)(ob + orow * r_max);
+      uint4* ol = (uint4*)(ob + plane + orow * r_max);
+      for (int c = 0; c < r_max / 8; ++c) o[c] = ol[c] = make_uint4(0, 0, 0, 0);
+    }
   }
 }
 
@@ -600,9 +633,15 @@ lora_status launch_shrink(const uint16_t* in, int64_t ld_in, int K, const uint16
                           int from_b, const lora_adapter_desc* desc, const int32_t* adpos,
                           const int32_t* in_rows, const int32_t* out_rows, const float* rowscale,
                           const int32_t* offsets, const int32_t* pre32, int n_ad,
-                          int64_t n_tokens, uint16_t* out, int r_max, void* zero, hipStream_t s) {
+                          int64_t n_tokens, uint16_t* out, int r_max, void* zero, hipStream_t s,
+                          const uint16_t* mat_pack2, const lora_adapter_desc* desc2,
+                          uint16_t* out2) {
   if (n_tokens <= 0) return LORA_OK;
-  const int nb_max = (r_max + 15) / 16;
+  if (mat_pack2 && (from_b || r_max > 32 || !desc2 || !out2)) {
+    set_error("shrink: a dual shrink takes two A tables with ranks <= 32");
+    return LORA_E_INVALID_ARG;
+  }
+  const int nb_max = (mat_pack2 ? 2 : 1) * ((r_max + 15) / 16);
   const size_t ring[4] = {(size_t)sh_nst<1>() * (SH_XSLOTS + 256) * 16,
                           (size_t)sh_nst<2>() * (SH_XSLOTS + 512) * 16,
                           (size_t)sh_nst<3>() * (SH_XSLOTS + 768) * 16,
@@ -617,7 +656,8 @@ lora_status launch_shrink(const uint16_t* in, int64_t ld_in, int K, const uint16
   }
   hipLaunchKernelGGL(shrink_kernel, dim3(persistent_blocks()), dim3(256), lds, s, in, ld_in, K,
                      mat_pack, from_b, desc, adpos, ShrinkRows{in_rows, out_rows, rowscale},
-                     offsets, pre32, n_ad, n_tokens, out, r_max, (uint4*)zero);
+                     offsets, pre32, n_ad, n_tokens, out, r_max, (uint4*)zero, mat_pack2, desc2,
+                     out2);
   return launch_check("shrink");
 }
 

@@ -34,6 +34,17 @@ struct GemmRows {
   int64_t lmat_ld = 0;
   const uint16_t* lmat = nullptr;
   const lora_adapter_desc* desc = nullptr;
+  // Second weight operand B2 (same ldb / group stride as B), either
+  //   n_split: a second product of N columns in the same launch (B2, output
+  //            columns c_off2.., LoRA set 2), or
+  //   k_split: K = k_split + K2 with k >= k_split read from B2 (both LoRA sets).
+  const uint16_t* B2 = nullptr;
+  int n_split = 0;
+  int64_t c_off2 = 0;
+  int k_split = 0;
+  const uint16_t* vec2 = nullptr;
+  const uint16_t* lmat2 = nullptr;
+  const lora_adapter_desc* desc2 = nullptr;
   const int32_t* adpos = nullptr;
   int n_ad = 0;
 };
@@ -51,12 +62,15 @@ lora_status gemm_nt_grad(const uint16_t* A, const uint16_t* B, uint16_t* G, int6
 // over positions p < n_tokens (row maps and rowscale nullable), with M_a = A_a
 // ([r][K] at a_off) or, from_b, M_a = B_a^T (B_a [K][r] at b_off, read in
 // place); rows of positions without an adapter are zeroed, and `zero` (256 B,
-// nullable) too.
+// nullable) too.  Dual (mat_pack2 non-null, A factors, r_max <= 32): the same
+// input rows also give out2 from the second table desc2 / mat_pack2.
 lora_status launch_shrink(const uint16_t* in, int64_t ld_in, int K, const uint16_t* mat_pack,
                           int from_b, const lora_adapter_desc* desc, const int32_t* adpos,
                           const int32_t* in_rows, const int32_t* out_rows, const float* rowscale,
                           const int32_t* offsets, const int32_t* pre32, int n_ad,
-                          int64_t n_tokens, uint16_t* out, int r_max, void* zero, hipStream_t s);
+                          int64_t n_tokens, uint16_t* out, int r_max, void* zero, hipStream_t s,
+                          const uint16_t* mat_pack2 = nullptr,
+                          const lora_adapter_desc* desc2 = nullptr, uint16_t* out2 = nullptr);
 // Per key a: T_a = sum over a's positions p of P[p_row] Q[q_rows[p]]^T (mode 0:
 // [D][r] at b_off; mode 1: [r][D] at a_off), P the bf16 hi/lo planes.  P row:
 // the position itself with p_ident, else q_rows[p].  q_rows nullable.
@@ -89,6 +103,12 @@ lora_status launch_swiglu_fwd(int64_t n, const uint16_t* g, const uint16_t* u, u
                               hipStream_t s);
 lora_status launch_swiglu_bwd(int64_t n, const uint16_t* dh, const uint16_t* g,
                               const uint16_t* u, uint16_t* dg, uint16_t* du, hipStream_t s);
+// Rows of [gate | up] (gu [rows][2F]): h [rows][F] = silu(gate) * up; the
+// backward writes [dgate | dup] rows (dgu [rows][2F]) from dh [rows][F].
+lora_status launch_swiglu_rows_fwd(int64_t rows, int64_t F, const uint16_t* gu, uint16_t* h,
+                                   hipStream_t s);
+lora_status launch_swiglu_rows_bwd(int64_t rows, int64_t F, const uint16_t* dh,
+                                   const uint16_t* gu, uint16_t* dgu, hipStream_t s);
 lora_status launch_add_bf16(int64_t n, const uint16_t* a, const uint16_t* b, uint16_t* out,
                             hipStream_t s);
 lora_status launch_transpose_bf16(const uint16_t* src, uint16_t* dst, int64_t rows, int64_t cols,

@@ -223,8 +223,11 @@ def moe(steps, warmup, log, n=16384, H=2048, F=768, E=128, K=8, n_ad=8, r=32):
     if L.lora_device_status(ws):
         raise RuntimeError("device status flags set")
     gemm_ms, gemm_n = _timer(L.TIMER_BASE_GEMM)
-    flops_launch = 2.0 * n * K * H * F      # each grouped projection GEMM
-    tf = flops_launch / (gemm_ms / 1e3) / 1e12
+    # 6 expert projections of 2*N*K*H*F each per step, run as 4 grouped GEMM
+    # launches (gate+up fused in the forward, the gate and up dX in one K-concatenated GEMM)
+    flops_step = 6 * 2.0 * n * K * H * F
+    gemm_step_ms = gemm_ms * gemm_n / steps
+    tf = flops_step / (gemm_step_ms / 1e3) / 1e12
     return {
         "metric": "tokens/s mixed-adapter LoRA routed-expert layer fwd+bwd",
         "value": round(n / (ms / 1e3), 1), "unit": "tokens/s", "ms_per_step": round(ms, 4),
@@ -232,8 +235,10 @@ def moe(steps, warmup, log, n=16384, H=2048, F=768, E=128, K=8, n_ad=8, r=32):
                                f"expert intermediate {F}, {n_ad} adapters r{r} alpha 32 on every "
                                f"expert's gate/up/down, {n} tokens random adapter ids; "
                                "route + fwd + bwd"},
-        "roofline": {"bound": "mfma", "kernel": "grouped expert GEMMs (6 per step, 2*N*K*H*F each)",
+        "roofline": {"bound": "mfma",
+                     "kernel": "grouped expert GEMMs (6 projections of 2*N*K*H*F per step in "
+                               "4 launches)",
                      "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tf / PEAK_BF16_TFLOPS, 4), "avg_ms": round(gemm_ms, 4),
-                     "launches": gemm_n},
+                     "gemm_ms_per_step": round(gemm_step_ms, 4), "launches": gemm_n},
     }

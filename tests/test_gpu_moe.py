@@ -5,7 +5,7 @@ stores in bf16, continues from the GPU's stored bits (g, u, h from the saved
 buffer; dh, dg, du from the backward's trace), while each of those
 intermediates is itself compared with the oracle's value at the bf16
 tolerance.  Intermediates the layer does not expose (expert outputs, per-
-assignment dx parts) are rounded to bf16 at the same point."""
+assignment dx) are rounded to bf16 at the same point."""
 import numpy as np
 import pytest
 import torch
@@ -43,15 +43,23 @@ def position_of(c, experts, ids):
 
 
 def saved_views(dm, saved):
-    """g, u, h (float64 [N*K][F], position order) from the saved buffer."""
+    """g, u, h (float64 [N*K][F], position order) from the saved buffer: rows of
+    [gate | up] pre-activations, then h."""
     c = dm.c
     nk, F = c.n_tokens * c.top_k, c.d_ff
     raw = saved.cpu().numpy()
-    out, off = [], 0
-    for _ in range(3):
-        out.append(W.bf16_bits_to_f64(raw[off:off + nk * F * 2].view(np.uint16)).reshape(nk, F))
-        off += _align(nk * F * 2)
-    return out
+    gu = W.bf16_bits_to_f64(raw[:nk * 2 * F * 2].view(np.uint16)).reshape(nk, 2 * F)
+    off = _align(nk * 2 * F * 2)
+    h = W.bf16_bits_to_f64(raw[off:off + nk * F * 2].view(np.uint16)).reshape(nk, F)
+    return gu[:, :F], gu[:, F:], h
+
+
+def trace_views(c, trace):
+    """dh, dg, du (float64 [N*K][F], position order) from the backward trace."""
+    nk, F = c.n_tokens * c.top_k, c.d_ff
+    flat = W.bf16_bits_to_f64(bits_of(trace)).reshape(-1)
+    dgu = flat[nk * F:].reshape(nk, 2 * F)
+    return flat[:nk * F].reshape(nk, F), dgu[:, :F], dgu[:, F:]
 
 
 class StageStore:
@@ -202,10 +210,10 @@ def run_parity(dm, ex, w, y, dx, grads, trace, ids=None):
     pos = position_of(c, e_np, ids)
     g, u, h = saved_views(dm, dm.saved)
     nk, F = c.n_tokens * c.top_k, c.d_ff
-    tr = W.bf16_bits_to_f64(bits_of(trace)).reshape(3, nk, F)
+    dh, dg, du = trace_views(c, trace)
     Wg, Wu, Wd, A, B, s = dm.oracle_params()
     x = W.bf16_bits_to_f64(c.x_bits)
-    st = StageStore(pos, {"g": g, "u": u, "h": h, "dh": tr[0], "dg": tr[1], "du": tr[2]})
+    st = StageStore(pos, {"g": g, "u": u, "h": h, "dh": dh, "dg": dg, "du": du})
     y_ref, saved = OE.moe_forward(x, e_np, w_np, ids, Wg, Wu, Wd, A, B, s, store=st)
     assert rel_err(f64_of(y), y_ref) < TOL_BF16
     dy = W.bf16_bits_to_f64(c.dy_bits)
