@@ -238,13 +238,25 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_nt_kernel(const uint16_t* __
   const int per = num >> 3, rem = num & 7;
   if (loc >= per + (xcd < rem ? 1 : 0)) return;
   const int t = (xcd < rem) ? xcd * (per + 1) + loc : rem * (per + 1) + (xcd - rem) * per + loc;
-  const int gsz = group_m * tiles_n;
-  const int grp = t / gsz;
-  const int first_m = grp * group_m;
-  const int gm = min(live_m - first_m, group_m);
-  const int in = t - grp * gsz;
-  const int tm = first_m + in % gm;
-  int tn = in / gm;
+  int tm, tn, g = 0;
+  if (ep.g_tile) {
+    // grouped: tiles run group by group (group g owns tiles g_tile[g] * tiles_n
+    // .. g_tile[g + 1] * tiles_n), row tiles fastest, so the tiles one XCD runs
+    // at a time share their group's weight panels and row panels in its L2
+    g = find_bucket(ep.g_tile, ep.n_groups + 1, t / tiles_n);
+    const int nr = ep.g_tile[g + 1] - ep.g_tile[g];
+    const int in = t - ep.g_tile[g] * tiles_n;
+    tm = in % nr;   // row tile within the group
+    tn = in / nr;
+  } else {
+    const int gsz = group_m * tiles_n;
+    const int grp = t / gsz;
+    const int first_m = grp * group_m;
+    const int gm = min(live_m - first_m, group_m);
+    const int in = t - grp * gsz;
+    tm = first_m + in % gm;
+    tn = in / gm;
+  }
   const bool second = ep.n_tiles1 > 0 && tn >= ep.n_tiles1;   // N split: second product
   if (second) {
     tn -= ep.n_tiles1;
@@ -255,8 +267,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_nt_kernel(const uint16_t* __
   int Mlim = M;   // positions >= Mlim are past this tile's row range
   const uint16_t* B2g = ep.B2;   // K split: second operand of this tile's group
   if (ep.g_tile) {
-    const int g = find_bucket(ep.g_tile, ep.n_groups + 1, tm);
-    m0 = ep.g_off[g * ep.g_stride] + (tm - ep.g_tile[g]) * GBM;
+    m0 = ep.g_off[g * ep.g_stride] + tm * GBM;
     Mlim = ep.g_off[(g + 1) * ep.g_stride];
     B += (int64_t)g * ep.ldb_group;
     if (ep.k_split > 0) B2g = ep.B2 + (int64_t)g * ep.ldb_group;
@@ -264,7 +275,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_nt_kernel(const uint16_t* __
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 2, wn = wave & 3;
 
   // acc[i][j] holds the transposed 32x32 sub-tile: register g of lane l is
@@ -413,15 +424,31 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_nt_kernel(const uint16_t* __
     asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(VM_AHEAD) : "memory");
   };
 
-  // steps in rounds of NSTAGE (stage index static), then the remaining steps
+  // A wave whose 128 rows all lie past the tile's row range (the tail tile of
+  // a group or of the matrix) keeps the other waves' DMA and barrier cadence
+  // but skips the fragment reads and MFMAs.
+  const bool live = m0 + wm * 128 < Mlim;
   int kt = 0;
-  for (; kt + NSTAGE <= KT; kt += NSTAGE)
+  if (live) {
+    // steps in rounds of NSTAGE (stage index static), then the remaining steps
+    for (; kt + NSTAGE <= KT; kt += NSTAGE)
+      [&]<int... S>(std::integer_sequence<int, S...>) {
+        (step(std::integral_constant<int, S>{}, kt + S), ...);
+      }(std::make_integer_sequence<int, NSTAGE>{});
     [&]<int... S>(std::integer_sequence<int, S...>) {
-      (step(std::integral_constant<int, S>{}, kt + S), ...);
-    }(std::make_integer_sequence<int, NSTAGE>{});
-  [&]<int... S>(std::integer_sequence<int, S...>) {
-    ((kt < KT ? (step(std::integral_constant<int, S>{}, kt), ++kt) : 0), ...);
-  }(std::make_integer_sequence<int, NSTAGE - 1>{});
+      ((kt < KT ? (step(std::integral_constant<int, S>{}, kt), ++kt) : 0), ...);
+    }(std::make_integer_sequence<int, NSTAGE - 1>{});
+  } else {
+    for (; kt < KT; ++kt) {
+      const int k0 = min(kt + NSTAGE - 1, KT - 1) * SBK;
+      const int sn = (kt + NSTAGE - 1) % NSTAGE;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) dmaA(sn, i, baseA + k0);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) dmaB(sn, i, bsrc(k0));
+      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(VM_AHEAD) : "memory");
+    }
+  }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no DMA may outlive the block
 
   // ---- epilogues
