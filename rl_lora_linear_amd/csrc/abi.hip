@@ -613,7 +613,7 @@ MoeWs carve_moe(const moe_shape& sh, void* ws, size_t bytes, bool backward) {
     w.dxp = cv.take<uint16_t>((size_t)NK * sh.hidden);
     w.partial = cv.take<float>((size_t)grad_partial_floats(NK, n_keys,
                                                           std::max(sh.hidden, sh.d_ff),
-                                                          sh.max_rank));
+                                                          2 * sh.max_rank));
   }
   w.total = cv.used;
   return w;
@@ -863,12 +863,19 @@ lora_status moe_backward(const moe_shape* shape, const uint16_t* dy, const uint1
     TRY(moe_project(sh, w, w.dgu, nullptr, NK, W_gate_t, H, F, w.v[0], gate_pack, 0, w.desc[0],
                     nullptr, w.dxp, s, gu));
   }
-  // dB = sum d (s u)^T; dA = sum (s v) x_t^T
-  for (int i = 0; i < 2; ++i) {
+  // dB = sum d (s u)^T; dA = sum (s v) x_t^T (gate and up in one pass over x
+  // when both fit one tile)
+  for (int i = 0; i < 2; ++i)
     TRY(launch_grad(0, sv.su[i], R, w.zero, w.dgu + i * F, 2 * F, (int)F, w.desc[i], w.active,
                     nullptr, 1, w.offsets, w.prec, n_keys, NK, grads[i], w.partial, accumulate, s));
-    TRY(launch_grad(1, w.v[i], R, w.zero, x, H, (int)H, w.desc[i], w.active, w.tokrow, 1,
-                    w.offsets, w.prec, n_keys, NK, grads[i], w.partial, accumulate, s));
+  if (R <= 32) {
+    TRY(launch_grad(1, w.v[0], R, w.zero, x, H, (int)H, w.desc[0], w.active, w.tokrow, 1,
+                    w.offsets, w.prec, n_keys, NK, grads[0], w.partial, accumulate, s, w.v[1],
+                    w.desc[1], grads[1]));
+  } else {
+    for (int i = 0; i < 2; ++i)
+      TRY(launch_grad(1, w.v[i], R, w.zero, x, H, (int)H, w.desc[i], w.active, w.tokrow, 1,
+                      w.offsets, w.prec, n_keys, NK, grads[i], w.partial, accumulate, s));
   }
   return launch_moe_combine(w.dxp, nullptr, nullptr, w.inv, w.keys, sh.n_tokens, sh.top_k, H, dx,
                             s);

@@ -368,9 +368,11 @@ __device__ __forceinline__ int gr_fq(int t) { return (2 * (t & 3)) | (8 * ((t >>
 // zero row for P, so they add nothing.
 // mode 0 (dB): out layout [D][r] (c fastest): MFMA M = c, N = j.
 // mode 1 (dA): out layout [r][D] (j fastest): MFMA M = j, N = c.
+// Dual P (mode 1): a second set of planes at element offset p2_off from P,
+// with the same row stride r_max; tile ranks [r_max, 2 r_max) come from it.
 template <int NCB, int MODE, int PN>
 __device__ __forceinline__ void grad_tile(const uint16_t* __restrict__ P, int64_t plane, int r_max,
-                                          const uint16_t* __restrict__ zero,
+                                          int64_t p2_off, const uint16_t* __restrict__ zero,
                                           const uint16_t* __restrict__ Q, int64_t ld_q, int D,
                                           const int32_t* tok_s, int p_base, int rows, int j0,
                                           uint4* lds, f32x4 (&acc)[4][4]) {
@@ -390,14 +392,16 @@ __device__ __forceinline__ void grad_tile(const uint16_t* __restrict__ P, int64_
   int prow[PN];
   int64_t poff[PN];
   int pzoff[PN];
+  const int pchunks = (p2_off ? 2 : 1) * (r_max / 8);   // 16-byte chunks per token row
 #pragma unroll
   for (int i = 0; i < PN; ++i) {
     const int s = (wave * PN + i) * 64 + lane;
     const int pl = s / (GR_TT * G::PW);
     const int t = (s / G::PW) % GR_TT;
-    const int c = min((s % G::PW) ^ (2 * G::sw(t)), r_max / 8 - 1);
+    const int c = min((s % G::PW) ^ (2 * G::sw(t)), pchunks - 1);
+    const bool second = c >= r_max / 8;
     prow[i] = t;
-    poff[i] = pl * plane + c * 8;
+    poff[i] = pl * plane + (second ? p2_off + (c - r_max / 8) * 8 : c * 8);
     pzoff[i] = c * 8;
   }
   auto issue = [&](int st, int kt) {
@@ -483,6 +487,14 @@ __device__ __forceinline__ void grad_tile(const uint16_t* __restrict__ P, int64_
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no DMA may outlive the block
 }
 
+// Second table of a dual (mode 1) reduction: ranks [r_max, 2 r_max) of the
+// tile are T for desc2 / out2 (P planes at p2_off); off when desc2 is null.
+struct GradDual {
+  const lora_adapter_desc* desc2;
+  float* out2;
+  int64_t p2_off;
+};
+
 template <int MODE, int PN>
 __device__ __forceinline__ void grad_item(
     const uint16_t* __restrict__ P, int64_t plane, int r_max, const uint16_t* __restrict__ zero,
@@ -490,7 +502,7 @@ __device__ __forceinline__ void grad_item(
     const lora_adapter_desc* __restrict__ desc, const int32_t* __restrict__ q_rows, int p_ident,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ chunk_pre, int n_ad,
     float* __restrict__ out_pack, float* __restrict__ partial, int accumulate, int slot, int j0,
-    int32_t* tok_s, uint4* gr_lds) {
+    int32_t* tok_s, uint4* gr_lds, const GradDual du) {
   TileInfo ti;
   tile_of(chunk_pre, offsets, n_ad, slot, GR_TC, ti);
   __syncthreads();   // every wave is done with the previous item's tokens and ring
@@ -500,28 +512,37 @@ __device__ __forceinline__ void grad_item(
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const lora_adapter_desc d = desc[ti.a];
   const int r = d.rank;
+  const bool dual = MODE == 1 && du.desc2 != nullptr;
+  const lora_adapter_desc d2 = dual ? du.desc2[ti.a] : d;
   const int nchunks = chunk_pre[ti.a + 1] - chunk_pre[ti.a];
+  const int rt = dual ? 2 * r_max : r_max;   // tile ranks (partial row count)
+  const int64_t p2 = dual ? du.p2_off : 0;
 
   f32x4 acc[4][4];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int ncb = (r + 15) / 16;
+  const int ncb = dual ? (r_max + d2.rank + 15) / 16 : (r + 15) / 16;
+#define GRAD_TILE(NCB) \
+  grad_tile<NCB, MODE, PN>(P, plane, r_max, p2, zero, Q, ld_q, D, tok_s, p_base, ti.rows, j0, gr_lds, acc)
   if (PN == 1) {
-    if (ncb == 1) grad_tile<1, MODE, PN>(P, plane, r_max, zero, Q, ld_q, D, tok_s, p_base, ti.rows, j0, gr_lds, acc);
-    else grad_tile<2, MODE, PN>(P, plane, r_max, zero, Q, ld_q, D, tok_s, p_base, ti.rows, j0, gr_lds, acc);
+    if (ncb == 1) GRAD_TILE(1);
+    else GRAD_TILE(2);
   } else {
-    if (ncb == 1) grad_tile<1, MODE, PN>(P, plane, r_max, zero, Q, ld_q, D, tok_s, p_base, ti.rows, j0, gr_lds, acc);
-    else if (ncb == 2) grad_tile<2, MODE, PN>(P, plane, r_max, zero, Q, ld_q, D, tok_s, p_base, ti.rows, j0, gr_lds, acc);
-    else if (ncb == 3) grad_tile<3, MODE, PN>(P, plane, r_max, zero, Q, ld_q, D, tok_s, p_base, ti.rows, j0, gr_lds, acc);
-    else grad_tile<4, MODE, PN>(P, plane, r_max, zero, Q, ld_q, D, tok_s, p_base, ti.rows, j0, gr_lds, acc);
+    if (ncb == 1) GRAD_TILE(1);
+    else if (ncb == 2) GRAD_TILE(2);
+    else if (ncb == 3) GRAD_TILE(3);
+    else GRAD_TILE(4);
   }
+#undef GRAD_TILE
 
   // ---- write.  Region of this adapter: D*r floats.
   const int64_t base = MODE == 0 ? d.b_off : d.a_off;
   const bool direct = nchunks == 1;
-  float* dst = direct ? out_pack + base : partial + (int64_t)slot * D * r_max;
+  float* dst = direct ? out_pack + base : partial + (int64_t)slot * D * rt;
+  // dual, direct: ranks >= r_max go to the second table's region
+  float* dst2 = direct && dual ? du.out2 + d2.a_off : nullptr;
 #pragma unroll
   for (int jt = 0; jt < 4; ++jt)
 #pragma unroll
@@ -543,8 +564,10 @@ __device__ __forceinline__ void grad_item(
         // D[j][c]: lane holds j = jt*16 + 4*(lane/16) + i, c = ct*16 + lane%16
         const int j = j0 + wave * 64 + jt * 16 + 4 * (lane >> 4);
         const int c = ct * 16 + (lane & 15);
-        if (c >= r || j >= D) continue;
-        float4* p = (float4*)(dst + (int64_t)c * D + j);
+        const bool hi = dual && c >= r_max;   // rank c - r_max of the second table
+        if ((hi ? c - r_max >= d2.rank : c >= r) || j >= D) continue;
+        float4* p = (float4*)(hi && direct ? dst2 + (int64_t)(c - r_max) * D + j
+                                           : dst + (int64_t)c * D + j);
         float4 v = make_float4(acc[jt][ct][0], acc[jt][ct][1], acc[jt][ct][2], acc[jt][ct][3]);
         if (direct && accumulate) {
           float4 o = *p;
@@ -564,7 +587,7 @@ __global__ __launch_bounds__(256) void grad_kernel(
     const uint16_t* __restrict__ Q, int64_t ld_q, int D,
     const lora_adapter_desc* __restrict__ desc, const int32_t* __restrict__ q_rows, int p_ident,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ chunk_pre, int n_ad,
-    float* __restrict__ out_pack, float* __restrict__ partial, int accumulate) {
+    float* __restrict__ out_pack, float* __restrict__ partial, int accumulate, GradDual du) {
   extern __shared__ uint4 gr_lds[];
   // the chunk's token ids, cached in LDS: the DMA loop may issue no
   // compiler-tracked global loads (their waits would also wait for the DMA)
@@ -576,7 +599,7 @@ __global__ __launch_bounds__(256) void grad_kernel(
     const int j0 = (item - slot * ncol) * GR_NJ;
     grad_item<MODE, PN>(P, plane, r_max, zero, Q, ld_q, D, desc, q_rows, p_ident, offsets,
                         chunk_pre, n_ad,
-                        out_pack, partial, accumulate, slot, j0, tok_s, gr_lds);
+                        out_pack, partial, accumulate, slot, j0, tok_s, gr_lds, du);
   }
 }
 
@@ -586,7 +609,7 @@ __global__ __launch_bounds__(256) void grad_kernel(
 __global__ __launch_bounds__(256) void grad_finalize_kernel(
     const lora_adapter_desc* __restrict__ desc, const uint8_t* __restrict__ active,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ chunk_pre, int D,
-    int r_max, int mode, float* __restrict__ out_pack, const float* __restrict__ partial,
+    int64_t slot_floats, int mode, float* __restrict__ out_pack, const float* __restrict__ partial,
     int accumulate) {
   const int a = blockIdx.x;
   if (!active[a]) return;
@@ -602,7 +625,7 @@ __global__ __launch_bounds__(256) void grad_finalize_kernel(
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
     if (!zero) {
       for (int q = 0; q < ns; ++q) {
-        const float4 p = *(const float4*)(partial + (int64_t)(s0 + q) * D * r_max + e);
+        const float4 p = *(const float4*)(partial + (int64_t)(s0 + q) * slot_floats + e);
         v.x += p.x; v.y += p.y; v.z += p.z; v.w += p.w;
       }
       if (accumulate) {
@@ -666,7 +689,8 @@ lora_status launch_grad_t(dim3 grid, const uint16_t* P, int64_t plane, int r_max
                           const uint16_t* zero, const uint16_t* Q, int64_t ld_q, int D,
                           const lora_adapter_desc* desc, const int32_t* q_rows, int p_ident,
                           const int32_t* offsets, const int32_t* chunk_pre, int n_ad,
-                          float* out_pack, float* partial, int accumulate, hipStream_t s) {
+                          float* out_pack, float* partial, int accumulate, GradDual du,
+                          hipStream_t s) {
   const size_t lds = (size_t)GrP<PN>::NST * GrP<PN>::STAGE * sizeof(uint4);
   static bool attr = false;
   if (!attr) {
@@ -676,7 +700,7 @@ lora_status launch_grad_t(dim3 grid, const uint16_t* P, int64_t plane, int r_max
   }
   hipLaunchKernelGGL((grad_kernel<MODE, PN>), grid, dim3(256), lds, s, P, plane, r_max, zero, Q,
                      ld_q, D, desc, q_rows, p_ident, offsets, chunk_pre, n_ad, out_pack, partial,
-                     accumulate);
+                     accumulate, du);
   return launch_check("grad");
 }
 
@@ -685,28 +709,38 @@ lora_status launch_grad(int mode, const uint16_t* P, int r_max, const void* zero
                         const uint8_t* active, const int32_t* q_rows, int p_ident,
                         const int32_t* offsets, const int32_t* chunk_pre, int n_ad,
                         int64_t n_tokens, float* out_pack, float* partial, int accumulate,
-                        hipStream_t s) {
+                        hipStream_t s, const uint16_t* P2, const lora_adapter_desc* desc2,
+                        float* out2) {
+  const bool dual = P2 != nullptr;
+  if (dual && (mode != 1 || r_max > 32 || !desc2 || !out2)) {
+    set_error("grad: a dual reduction takes two mode-1 tables with ranks <= 32");
+    return LORA_E_INVALID_ARG;
+  }
+  const int rt = dual ? 2 * r_max : r_max;   // tile ranks
   if (n_tokens > 0) {
     dim3 grid(persistent_blocks());
     const int64_t plane = n_tokens * r_max;
     const uint16_t* z = (const uint16_t*)zero;
+    const GradDual du{desc2, out2, dual ? (int64_t)(P2 - P) : 0};
     lora_status st;
-    if (r_max <= 32)
-      st = mode == 0 ? launch_grad_t<0, 1>(grid, P, plane, r_max, z, Q, ld_q, D, desc, q_rows, p_ident, offsets,
-                                           chunk_pre, n_ad, out_pack, partial, accumulate, s)
-                     : launch_grad_t<1, 1>(grid, P, plane, r_max, z, Q, ld_q, D, desc, q_rows, p_ident, offsets,
-                                           chunk_pre, n_ad, out_pack, partial, accumulate, s);
+#define LAUNCH_GRAD(M, PN)                                                                     \
+  launch_grad_t<M, PN>(grid, P, plane, r_max, z, Q, ld_q, D, desc, q_rows, p_ident, offsets, \
+                       chunk_pre, n_ad, out_pack, partial, accumulate, du, s)
+    if (rt <= 32)
+      st = mode == 0 ? LAUNCH_GRAD(0, 1) : LAUNCH_GRAD(1, 1);
     else
-      st = mode == 0 ? launch_grad_t<0, 2>(grid, P, plane, r_max, z, Q, ld_q, D, desc, q_rows, p_ident, offsets,
-                                           chunk_pre, n_ad, out_pack, partial, accumulate, s)
-                     : launch_grad_t<1, 2>(grid, P, plane, r_max, z, Q, ld_q, D, desc, q_rows, p_ident, offsets,
-                                           chunk_pre, n_ad, out_pack, partial, accumulate, s);
+      st = mode == 0 ? LAUNCH_GRAD(0, 2) : LAUNCH_GRAD(1, 2);
+#undef LAUNCH_GRAD
     if (st) return st;
   }
-  const int64_t per = (int64_t)D * r_max;
-  const unsigned gy = (unsigned)std::max<int64_t>(1, std::min<int64_t>(64, cdiv(per, 1024)));
+  const int64_t slot = (int64_t)D * rt;   // floats per chunk partial
+  const unsigned gy = (unsigned)std::max<int64_t>(1, std::min<int64_t>(64, cdiv((int64_t)D * r_max, 1024)));
   hipLaunchKernelGGL(grad_finalize_kernel, dim3(n_ad, gy), dim3(256), 0, s, desc, active, offsets,
-                     chunk_pre, D, r_max, mode, out_pack, partial, accumulate);
+                     chunk_pre, D, slot, mode, out_pack, partial, accumulate);
+  lora_status st = launch_check("grad_finalize");
+  if (st || !dual) return st;
+  hipLaunchKernelGGL(grad_finalize_kernel, dim3(n_ad, gy), dim3(256), 0, s, desc2, active, offsets,
+                     chunk_pre, D, slot, mode, out2, partial + (int64_t)r_max * D, accumulate);
   return launch_check("grad_finalize");
 }
 

@@ -79,7 +79,11 @@ lora_status launch_grad(int mode, const uint16_t* P, int r_max, const void* zero
                         const uint8_t* active, const int32_t* q_rows, int p_ident,
                         const int32_t* offsets, const int32_t* chunk_pre, int n_ad,
                         int64_t n_tokens, float* out_pack, float* partial, int accumulate,
-                        hipStream_t s);
+                        hipStream_t s, const uint16_t* P2 = nullptr,
+                        const lora_adapter_desc* desc2 = nullptr, float* out2 = nullptr);
+// Dual (mode 1, r_max <= 32): P2 (same layout as P, in the same allocation)
+// with desc2 gives the second table's T into out2 in the same pass over Q;
+// the partial buffer then needs grad_partial_floats(.., 2 * r_max).
 int64_t grad_partial_floats(int64_t n_tokens, int n_ad, int64_t D, int r_max);
 
 

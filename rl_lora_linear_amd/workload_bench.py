@@ -18,19 +18,28 @@ def _randn(gen, shape, std, dtype=torch.bfloat16):
 
 
 def _timed(step, steps, warmup, log):
+    """ms per step with no instrumentation; then a second pass of `steps`
+    steps with the library's HIP-event timers on (kernel durations, read with
+    _timer).  Returns (ms, instrumented ms)."""
     for k in range(warmup):
         step(k)
     torch.cuda.synchronize()
-    L.lora_timing_reset()
-    L.lora_timing_enable(True)
-    log(f"[bench] timing {steps} steps")
-    t0 = time.perf_counter()
-    for k in range(steps):
-        step(k)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    L.lora_timing_enable(False)
-    return (t1 - t0) * 1e3 / steps
+
+    def run(instrumented):
+        L.lora_timing_reset()
+        L.lora_timing_enable(instrumented)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(steps):
+            step(k)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        L.lora_timing_enable(False)
+        return (t1 - t0) * 1e3 / steps
+
+    log(f"[bench] timing {steps} steps, then {steps} instrumented steps")
+    ms = run(False)
+    return ms, run(True)
 
 
 def _timer(tid):
@@ -100,7 +109,7 @@ def mlp(steps, warmup, log, n=32768, d=4096, f=12288, n_ad=64):
         L.bf16_add(dxg, dxu, dx)
 
     log(f"[bench] mlp {n} tokens, d {d}, d_ff {f}, {n_ad} adapters")
-    ms = _timed(step, steps, warmup, log)
+    ms, ms_instr = _timed(step, steps, warmup, log)
     for p in proj.values():
         if L.lora_device_status(p["ws"]):
             raise RuntimeError("device status flags set")
@@ -109,7 +118,7 @@ def mlp(steps, warmup, log, n=32768, d=4096, f=12288, n_ad=64):
     tf = flops_launch / (gemm_ms / 1e3) / 1e12
     return {
         "metric": "tokens/s mixed-adapter LoRA MLP fwd+bwd", "value": round(n / (ms / 1e3), 1),
-        "unit": "tokens/s", "ms_per_step": round(ms, 4),
+        "unit": "tokens/s", "ms_per_step": round(ms, 4), "ms_per_step_instrumented": round(ms_instr, 4),
         "config": {"workload": f"qwen3-8b MLP gate/up {d}->{f}, down {f}->{d}, {n_ad} adapters "
                                f"ranks {{8,16,32,64}} alpha 32, {n} tokens interleaved ids, fwd+bwd",
                    "rank_counts": {int(r): int((ranks == r).sum()) for r in (8, 16, 32, 64)}},
@@ -156,7 +165,7 @@ def logprob(steps, warmup, log, n_seq=64, seq=256, H=4096, V=151936, chunk=4096)
         L.token_logprobs_backward(h, U, Ut, tg, lse, dl, dh, ws_b)   # chunk from ws size
 
     log(f"[bench] logprob {n} tokens, H {H}, V {V}")
-    ms = _timed(step, steps, warmup, log)
+    ms, ms_instr = _timed(step, steps, warmup, log)
     f_ms, f_n = _timer(L.TIMER_LOGPROB_FWD)
     b_ms, b_n = _timer(L.TIMER_LOGPROB_BWD)     # one record per token chunk
     b_step_ms = b_ms * b_n / steps
@@ -165,7 +174,7 @@ def logprob(steps, warmup, log, n_seq=64, seq=256, H=4096, V=151936, chunk=4096)
     tf_b = 2 * flops / (b_step_ms / 1e3) / 1e12
     return {
         "metric": "tokens/s fused lm_head logprob + PPO loss + logprob backward",
-        "value": round(n / (ms / 1e3), 1), "unit": "tokens/s", "ms_per_step": round(ms, 4),
+        "value": round(n / (ms / 1e3), 1), "unit": "tokens/s", "ms_per_step": round(ms, 4), "ms_per_step_instrumented": round(ms_instr, 4),
         "config": {"workload": f"hidden {H} -> vocab {V}, {n} tokens = 16 groups x 4 x {seq}, "
                                f"prompt {prompt}/{seq}, PPO clip 0.2, backward chunk {chunk} rows"},
         "roofline": {"bound": "mfma", "kernel": "lm_head GEMM with online logsumexp (forward)",
@@ -219,7 +228,7 @@ def moe(steps, warmup, log, n=16384, H=2048, F=768, E=128, K=8, n_ad=8, r=32):
                        dx, grads, 0, ws)
 
     log(f"[bench] moe {n} tokens, {E} experts top-{K}, H {H}, F {F}, {n_ad} adapters r{r}")
-    ms = _timed(step, steps, warmup, log)
+    ms, ms_instr = _timed(step, steps, warmup, log)
     if L.lora_device_status(ws):
         raise RuntimeError("device status flags set")
     gemm_ms, gemm_n = _timer(L.TIMER_BASE_GEMM)
@@ -230,7 +239,7 @@ def moe(steps, warmup, log, n=16384, H=2048, F=768, E=128, K=8, n_ad=8, r=32):
     tf = flops_step / (gemm_step_ms / 1e3) / 1e12
     return {
         "metric": "tokens/s mixed-adapter LoRA routed-expert layer fwd+bwd",
-        "value": round(n / (ms / 1e3), 1), "unit": "tokens/s", "ms_per_step": round(ms, 4),
+        "value": round(n / (ms / 1e3), 1), "unit": "tokens/s", "ms_per_step": round(ms, 4), "ms_per_step_instrumented": round(ms_instr, 4),
         "config": {"workload": f"qwen3-30b-a3b-style MoE: {E} experts top-{K}, hidden {H}, "
                                f"expert intermediate {F}, {n_ad} adapters r{r} alpha 32 on every "
                                f"expert's gate/up/down, {n} tokens random adapter ids; "
