@@ -7,19 +7,22 @@
 //
 // Block tile 256 x 256, 512 threads = 8 waves (two per SIMD) in a 2 x 4 grid,
 // each wave 128 x 64 as 4 x 2 tiles of v_mfma_f32_32x32x16_bf16 (128 fp32
-// accumulators per lane, in AGPRs).  Two waves per SIMD let one wave's
-// epilogue, waits and LDS traffic overlap the other's MFMAs.  Operand tiles move global -> LDS by LDS-DMA into a
-// 4-stage ring of k = 32 slices (128 KB), three stages ahead; one barrier
-// per stage; LDS fragment reads run one 16-wide k slice ahead of the MFMAs
-// (including the first slice of the next stage, read before the barrier).
-// LDS rows are 64 B and their 16-byte chunks are XOR-swizzled (g4) so the
-// fragment reads of 16 consecutive rows hit distinct banks.  The MFMA computes the transposed
-// sub-tile so that each lane ends with runs of 4 consecutive output columns
-// (row reductions need one cross-lane step).  The bf16 epilogue stages the
-// tile in the idle ring and writes whole 512-byte rows (scattered 16-byte
-// stores of 32 rows per instruction cost ~10 us more per 8192x4096 output).  Tiles are ordered XCD-first (blocks are dispatched
-// round-robin over the 8 XCDs, so each XCD gets a contiguous tile range and
-// its own L2 sees the reuse) and then in groups of `group_m` row tiles.
+// accumulators per lane).  Two waves per SIMD let one wave's epilogue, waits
+// and LDS traffic overlap the other's MFMAs.  Operand tiles move global ->
+// LDS by LDS-DMA into two stages of k = 64 (whole 128-byte lines per row:
+// with 64-byte rows the texture path stalled on twice the requests, and the
+// clock fell with it); all of the next stage's DMA issues in the first phase
+// of a step, one barrier per step.  LDS fragment reads run one 16-wide k
+// slice ahead of the MFMAs.  LDS rows are 128 B with their 16-byte chunks
+// XOR-swizzled (lds_sw) so the fragment reads of 16 consecutive rows hit
+// distinct banks.  The MFMA computes the transposed sub-tile so that each
+// lane ends with runs of 4 consecutive output columns (row reductions need
+// one cross-lane step).  The bf16 epilogue stages the tile in the idle
+// stages and writes whole 512-byte rows (scattered 16-byte stores of 32 rows
+// per instruction cost ~10 us more per 8192x4096 output).  Tiles are ordered
+// XCD-first (blocks are dispatched round-robin over the 8 XCDs, so each XCD
+// gets a contiguous tile range and its own L2 sees the reuse) and then in
+// groups of `group_m` row tiles (grouped launches: group by group).
 #include <type_traits>
 #include <utility>
 
@@ -86,32 +89,40 @@ constexpr int GBM = 256, GBN = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 
 
-// Operand movement: gfx950 LDS-DMA (global_load_lds_dwordx4), 4 LDS stages
-// of BK = 32 (each stage: A and B tiles of 256 rows x 64 B = 16 KB), issued
-// three steps ahead.  The DMA is issued from inline assembly with explicit
-// vmcnt waits: the compiler's own counter bookkeeping for LDS-DMA would force
-// a full wait before every LDS read (it cannot tell which stage a DMA writes).
-// Each wave issues exactly 8 DMA instructions per step (4 for A, 4 for B), so
-// "vmcnt <= 8" at the end of step k means every stage up to k + 2 has landed.
-// Rows past the matrix edge are clamped to the last row: they only feed
-// output rows or columns that are never stored.
-constexpr int SBK = 32;                    // k per stage
-constexpr int S_CH = SBK / 8;              // 16-byte chunks per LDS row (4)
-constexpr int S_TILE = 256 * S_CH;         // uint4 per operand tile per stage
-constexpr int NSTAGE = 4;
-// DMA instructions a wave may leave in flight at the end of a k step: the
-// stages after k + 2 (8 per stage)
-constexpr int VM_AHEAD = (NSTAGE - 3) * 4;
-constexpr int GTHREADS = 512;   // 8 waves
-constexpr int WN = 64;          // output columns per wave
+// Operand movement: gfx950 LDS-DMA (global_load_lds_dwordx4) into two LDS
+// stages of BK = 64 (each stage: A and B tiles of 256 rows x 128 B = 32 KB),
+// double-buffered: step k computes on stage k % 2 while the DMA fills the
+// other with k + 1.  A 64-wide k slice is one whole 128-byte line per row, so
+// each DMA instruction moves 8 full lines (16 half lines with 32-wide slices
+// cost the texture path twice the requests per byte).  The DMA is issued from
+// inline assembly with explicit vmcnt waits: the compiler's own counter
+// bookkeeping for LDS-DMA would force a full wait before every LDS read (it
+// cannot tell which stage a DMA writes).  Rows past the matrix edge are
+// clamped to the last row: they only feed output rows or columns that are
+// never stored.
+constexpr int SBK = 64;                    // k per stage
+constexpr int S_CH = SBK / 8;              // 16-byte chunks per LDS row (8)
+constexpr int S_TILE = 256 * S_CH;         // uint4 per operand tile per stage (32 KB)
+constexpr int NSTAGE = 2;
+constexpr int WN = 64;                     // output columns per wave
+constexpr int NJ = WN / 32;                // 32-column MFMA tiles per wave
+constexpr int NWN = GBN / WN;              // waves along N
+constexpr int NWAVES = 2 * NWN;            // waves: two along M, 128 rows each
+constexpr int GTHREADS = 64 * NWAVES;
+constexpr int DMA_PER_OP = GBM / (8 * NWAVES);   // DMA instructions (8 rows each) per wave,
+                                                 // operand and stage
 
-// Swizzle of a 4-chunk LDS row: chunk c of row r is stored at c ^ g4(r).
-// The 16-byte reads of 16 consecutive rows at one logical chunk then hit 16
-// distinct (row mod 4, chunk) slots (conflict-free for 16 lanes per clock),
-// and 8 consecutive rows hit 8 distinct (row mod 2, chunk) slots.
-__device__ __forceinline__ int g4(int r) { return ((r >> 1) & 3) ^ ((r >> 3) & 1); }
-
-__shared__ uint4 g_stage[2 * NSTAGE * S_TILE];  // [A stages][B stages], 32 KB per stage
+// After the k loop (and a barrier) the operand stages hold the epilogue's
+// scratch: the staged output tile, the per-wave LoRA slab tiles and the row
+// map (or the logsumexp partials).
+constexpr int EPI_SLAB = GBM * 512;                        // bytes: after the staged tile
+constexpr int SLAB_LD = WN + 8;                            // bf16 per LDS row of a slab tile
+constexpr int SLAB_BYTES = 16 * SLAB_LD * 2;               // per wave
+constexpr int EPI_ROW = EPI_SLAB + NWAVES * SLAB_BYTES;
+constexpr int RING_BYTES = 2 * NSTAGE * S_TILE * 16;
+constexpr int LDS_BYTES = RING_BYTES > EPI_ROW + GBM * 4 ? RING_BYTES : EPI_ROW + GBM * 4;
+static_assert(EPI_SLAB + NWN * GBM * 8 <= LDS_BYTES, "logsumexp partials exceed the LDS block");
+__shared__ uint4 g_stage[LDS_BYTES / 16];   // [A stages][B stages], then epilogue scratch
 
 __device__ __forceinline__ uint32_t lds_addr(const uint4* p) {
   return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
@@ -119,9 +130,6 @@ __device__ __forceinline__ uint32_t lds_addr(const uint4* p) {
 
 // One 16-byte LDS-DMA per lane: global (base + voff) -> LDS (m0v + 16 * lane).
 // base is wave-uniform (SGPR pair), voff a per-lane 32-bit byte offset.
-// Operand tiles: 16 row blocks of 16 rows (64 slots each); wave w issues
-// blocks 4w..4w+3.  Lane L lands in slot L of its block: row L/4, physical
-// chunk L%4, so it fetches logical chunk (L%4) ^ g4(L/4).
 __device__ __forceinline__ void dma16s(uint32_t voff, const void* base, uint32_t m0v) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0v), "v"(voff), "s"(base)
                : "memory");
@@ -135,17 +143,15 @@ __device__ __forceinline__ void dma16s(uint32_t voff, const void* base, uint32_t
 // token and adapter (-1: none) of this lane's fragment rows, loaded before
 // the k loop.
 // With M_a = A_a^T (use_b_off = 0) the factor block of a 16-rank slice (16
-// rows of A_a x the wave's 64 columns) is loaded row-wise into a per-wave LDS
-// tile (144-byte rows: the transposing reads of 4 rows hit distinct banks) and
-// read back transposed, 8 consecutive ranks of one column per lane.
-constexpr int SLAB_LD = 72;   // bf16 per LDS row of the slab tile
+// rows of A_a x the wave's WN columns) is loaded row-wise into the wave's LDS
+// tile `slab` (rows padded by 16 bytes: the transposing reads of 4 rows hit
+// distinct banks) and read back transposed, 8 consecutive ranks of one column
+// per lane.
 __device__ __forceinline__ void lora_slab(const GemmEpi& ep, const uint16_t* vec,
                                           const uint16_t* lmat, const lora_adapter_desc* desc,
-                                          int n0, int N, int wn, int lane, int wave,
+                                          int n0, int N, int wn, int lane, uint4* slab,
                                           const int (&tok)[4], const int (&ad)[4],
-                                          f32x16 (&acc)[4][2]) {
-  __shared__ uint4 s_slab[GTHREADS / 64][16 * SLAB_LD / 8];
-  uint4* slab = s_slab[wave];
+                                          f32x16 (&acc)[4][NJ]) {
   const int m_l = lane & 31;
   const int half = lane >> 5;
   int lo = INT32_MAX, hi = -1;
@@ -169,7 +175,7 @@ __device__ __forceinline__ void lora_slab(const GemmEpi& ep, const uint16_t* vec
     for (int sl = 0; sl * 16 < r; ++sl) {
       const int c = sl * 16 + 8 * half;
       const bool cok = c < r;
-      uint4 h[4], l[4], v[2];
+      uint4 h[4], l[4], v[NJ];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         h[i] = l[i] = make_uint4(0, 0, 0, 0);
@@ -181,19 +187,19 @@ __device__ __forceinline__ void lora_slab(const GemmEpi& ep, const uint16_t* vec
       }
       if (ep.use_b_off) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < NJ; ++j) {
           const int n = n0 + wn * WN + j * 32 + m_l;
           v[j] = make_uint4(0, 0, 0, 0);
           if (n < N && cok) v[j] = *(const uint4*)(mat + (int64_t)n * r + c);
         }
       } else {
-        // rows sl*16 .. +15 of A_a (zero past rank r), columns nw .. nw + 63
+        // rows sl*16 .. +15 of A_a (zero past rank r), columns nw .. nw + WN - 1
         // (zero past N), 16 bytes per lane and load
         const int nw = n0 + wn * WN;
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
+        for (int t = 0; t < NJ; ++t) {
           const int q = lane + 64 * t;
-          const int row = q >> 3, cc = q & 7;
+          const int row = q / (WN / 8), cc = q % (WN / 8);
           uint4 val = make_uint4(0, 0, 0, 0);
           if (sl * 16 + row < r && nw + cc * 8 < N)
             val = *(const uint4*)(mat + (int64_t)(sl * 16 + row) * ep.lmat_ld + nw + cc * 8);
@@ -202,7 +208,7 @@ __device__ __forceinline__ void lora_slab(const GemmEpi& ep, const uint16_t* vec
         // lane: column j*32 + m_l, ranks 8*half + 0..3 and 4..7 of the slice
         const int q = (lane >> 2) & 3, jj = lane & 3;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < NJ; ++j) {
           const int col = j * 32 + 16 * ((lane >> 4) & 1) + 4 * jj;
           const uint32_t off = (uint32_t)(((8 * half + q) * SLAB_LD + col) * 2);
           const uint2 lo4 = tr_read(slab, off);
@@ -213,7 +219,7 @@ __device__ __forceinline__ void lora_slab(const GemmEpi& ep, const uint16_t* vec
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < NJ; ++j) {
           acc[i][j] = mfma32(as_bf16x8(v[j]), as_bf16x8(h[i]), acc[i][j]);
           acc[i][j] = mfma32(as_bf16x8(v[j]), as_bf16x8(l[i]), acc[i][j]);
         }
@@ -276,16 +282,16 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_nt_kernel(const uint16_t* __
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 2, wn = wave & 3;
+  const int wm = wave / NWN, wn = wave % NWN;
 
   // acc[i][j] holds the transposed 32x32 sub-tile: register g of lane l is
   // C[m = wm*128 + i*32 + l%32][n = wn*64 + j*32 + 8*(g/4) + 4*(l/32) + g%4],
   // so each lane owns runs of 4 consecutive output columns.
-  f32x16 acc[4][2];
+  f32x16 acc[4][NJ];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int g = 0; g < 16; ++g) acc[i][j][g] = 0.f;
 
@@ -324,29 +330,29 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_nt_kernel(const uint16_t* __
   // (the host checks they fit in 32 bits); other rows are offsets from the
   // tile's first row.  Rows past the edge are clamped to the last row: they
   // only feed outputs that are never stored.
-  uint32_t offA[2], offB[2];
+  // Instruction i of wave w fills rows 8 (w DMA_PER_OP + i) .. + 7 of a
+  // stage: lane L lands in row L / 8, physical chunk L % 8, i.e. logical
+  // chunk (L % 8) ^ lds_sw(row).
+  uint32_t offA[DMA_PER_OP], offB[DMA_PER_OP];
   const uint16_t* baseA = ep.a_rows ? A : A + (int64_t)m0 * lda;
   const uint16_t* baseB = B + (int64_t)n0 * ldb;
   // K split: k >= ksplit reads the second operand (same row offsets)
   const int ksplit = ep.k_split > 0 ? ep.k_split : K;
   const uint16_t* baseB2 = ep.k_split > 0 ? B2g + (int64_t)n0 * ldb : baseB;
   auto bsrc = [&](int k0) { return k0 < ksplit ? baseB + k0 : baseB2 + (k0 - ksplit); };
-  {
-    const int lrow = lane >> 2;
-    const int chunk = (lane & 3) ^ g4(lrow);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int blk = wave * 2 + i;
-      const int ra = min(m0 + blk * 16 + lrow, Mlim - 1);
-      const int rb = min(n0 + blk * 16 + lrow, N - 1);
-      const int64_t oa = ep.a_rows ? (int64_t)ep.a_rows[ra] * lda : (int64_t)(ra - m0) * lda;
-      offA[i] = (uint32_t)((oa + chunk * 8) * 2);
-      offB[i] = (uint32_t)(((int64_t)(rb - n0) * ldb + chunk * 8) * 2);
-    }
+  for (int i = 0; i < DMA_PER_OP; ++i) {
+    const int row = (wave * DMA_PER_OP + i) * 8 + (lane >> 3);
+    const int chunk = (lane & 7) ^ lds_sw(row);
+    const int ra = min(m0 + row, Mlim - 1);
+    const int rb = min(n0 + row, N - 1);
+    const int64_t oa = ep.a_rows ? (int64_t)ep.a_rows[ra] * lda : (int64_t)(ra - m0) * lda;
+    offA[i] = (uint32_t)((oa + chunk * 8) * 2);
+    offB[i] = (uint32_t)(((int64_t)(rb - n0) * ldb + chunk * 8) * 2);
   }
-  const uint32_t ldsA = __builtin_amdgcn_readfirstlane(lds_addr(sA + wave * 2 * 64));
-  const uint32_t ldsB = __builtin_amdgcn_readfirstlane(lds_addr(sB + wave * 2 * 64));
-  // DMA of operand rows (block i of this wave) for k0 into stage st
+  const uint32_t ldsA = __builtin_amdgcn_readfirstlane(lds_addr(sA + wave * DMA_PER_OP * 8 * S_CH));
+  const uint32_t ldsB = __builtin_amdgcn_readfirstlane(lds_addr(sB + wave * DMA_PER_OP * 8 * S_CH));
+  // DMA of operand rows (instruction i of this wave) for k0 into stage st
   auto dmaA = [&](int st, int i, const uint16_t* kb) {
     dma16s(offA[i], kb, ldsA + (uint32_t)(st * S_TILE + i * 64) * 16u);
   };
@@ -354,74 +360,73 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_nt_kernel(const uint16_t* __
     dma16s(offB[i], kb, ldsB + (uint32_t)(st * S_TILE + i * 64) * 16u);
   };
 
-  // prologue: stages 0..NSTAGE-2 in flight, wait for 0 and 1
+  // prologue: stage 0 landed and visible to every wave
 #pragma unroll
-  for (int s = 0; s < NSTAGE - 1; ++s) {
-    const int k0 = min(s, KT - 1) * SBK;
+  for (int i = 0; i < DMA_PER_OP; ++i) dmaA(0, i, baseA);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) dmaA(s, i, baseA + k0);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) dmaB(s, i, bsrc(k0));
-  }
-  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(VM_AHEAD) : "memory");
+  for (int i = 0; i < DMA_PER_OP; ++i) dmaB(0, i, bsrc(0));
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
 
   const int frag_row = lane & 31;   // row within a 32-row MFMA tile
   const int frag_half = lane >> 5;  // which 8-wide k half of a 16-wide k slice
-  const int sw = g4(frag_row);      // swizzle of every fragment row of this lane
-  int a_row[4], b_row[2];
+  const int sw = lds_sw(frag_row);  // swizzle of every fragment row of this lane
+  int a_row[4], b_row[NJ];
 #pragma unroll
   for (int i = 0; i < 4; ++i) a_row[i] = (wm * 128 + i * 32 + frag_row) * S_CH;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) b_row[j] = (wn * WN + j * 32 + frag_row) * S_CH;
-  const int c0 = frag_half ^ sw;         // slice 0 chunk
-  const int c1 = (2 + frag_half) ^ sw;   // slice 1 chunk
-
-  bf16x8 f0a[4], f0b[2], f1a[4], f1b[2];
+  for (int j = 0; j < NJ; ++j) b_row[j] = (wn * WN + j * 32 + frag_row) * S_CH;
+  int cq[4];   // physical chunk of this lane's fragment in 16-wide slice q
 #pragma unroll
-  for (int i = 0; i < 4; ++i) f0a[i] = as_bf16x8(sA[a_row[i] + c0]);
-#pragma unroll
-  for (int j = 0; j < 2; ++j) f0b[j] = as_bf16x8(sB[b_row[j] + c0]);
+  for (int q = 0; q < 4; ++q) cq[q] = (2 * q + frag_half) ^ sw;
 
-  // One k step on stage S (static, so every LDS address is base + immediate).
-  // Each phase is 8 groups of one MFMA; the LDS fragment reads for the next
-  // phase go into the first six groups and this step's two A (phase 0) or B
-  // (phase 1) DMA instructions into the last two, so the vector-memory, LDS
-  // and scalar work issues in the shadow of the matrix pipe instead of in a
-  // burst before it.  sched_barrier keeps the groups in this order.
+  bf16x8 fa[2][4], fb[2][NJ];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) fa[0][i] = as_bf16x8(sA[a_row[i] + cq[0]]);
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) fb[0][j] = as_bf16x8(sB[b_row[j] + cq[0]]);
+
+  // One k step (64 k, 4 slices of 16) on stage S (static, so every LDS
+  // address is base + immediate).  Each slice is a phase of 4 NJ groups of
+  // one MFMA; the LDS fragment reads for the next slice go into the first
+  // groups, and the step's 2 DMA_PER_OP DMA instructions (the other stage, k
+  // step kt + 1) one per group of the first phase, so the vector-memory, LDS
+  // and scalar work issues in the shadow of the matrix pipe and the DMA has
+  // most of the step to land.  sched_barrier keeps the groups
+  // in this order.  After the wait and the barrier the next stage is visible
+  // and its first slice is read.
   auto step = [&](auto S_, int kt) {
     constexpr int S = decltype(S_)::value;
-    constexpr int SN = (S + NSTAGE - 1) % NSTAGE;   // stage refilled now (read at kt - 1)
-    constexpr int S1 = (S + 1) % NSTAGE;            // next stage
+    constexpr int SN = 1 - S;
     const uint4* At = sA + S * S_TILE;
     const uint4* Bt = sB + S * S_TILE;
-    const uint4* An = sA + S1 * S_TILE;
-    const uint4* Bn = sB + S1 * S_TILE;
-    const int k0 = min(kt + NSTAGE - 1, KT - 1) * SBK;
+    const bool more = kt + 1 < KT;
+    const int k0 = (more ? kt + 1 : kt) * SBK;
     const uint16_t* ka = baseA + k0;
     const uint16_t* kb = bsrc(k0);
-    // phase 0: MFMAs of slice 0; reads of slice 1 (groups 0-5); A DMAs (6, 7)
 #pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      const int i = g >> 1, j = g & 1;
-      acc[i][j] = mfma32(f0b[j], f0a[i], acc[i][j]);
-      if (g < 4) f1a[g] = as_bf16x8(At[a_row[g] + c1]);
-      else if (g < 6) f1b[g - 4] = as_bf16x8(Bt[b_row[g - 4] + c1]);
-      else dmaA(SN, g - 6, ka);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // phase 1: MFMAs of slice 1; reads of slice 0 of the next stage (landed
-    // at the last barrier; on the last step simply unused); B DMAs
+    for (int q = 0; q < 4; ++q) {
+      const int cur = q & 1, nxt = cur ^ 1;
+      static_assert(4 * NJ == 2 * DMA_PER_OP, "one DMA per group of the first phase");
 #pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      const int i = g >> 1, j = g & 1;
-      acc[i][j] = mfma32(f1b[j], f1a[i], acc[i][j]);
-      if (g < 4) f0a[g] = as_bf16x8(An[a_row[g] + c0]);
-      else if (g < 6) f0b[g - 4] = as_bf16x8(Bn[b_row[g - 4] + c0]);
-      else dmaB(SN, g - 6, kb);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int g = 0; g < 4 * NJ; ++g) {
+        const int i = g / NJ, j = g % NJ;
+        acc[i][j] = mfma32(fb[cur][j], fa[cur][i], acc[i][j]);
+        if (q < 3 && g < 4) fa[nxt][g] = as_bf16x8(At[a_row[g] + cq[q + 1]]);
+        else if (q < 3 && g < 4 + NJ) fb[nxt][g - 4] = as_bf16x8(Bt[b_row[g - 4] + cq[q + 1]]);
+        if (q == 0 && more) {   // the whole next stage as early as possible
+          if (g < DMA_PER_OP) dmaA(SN, g, ka);
+          else dmaB(SN, g - DMA_PER_OP, kb);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
-    // stage kt + 2 has landed for this wave; after the barrier, for all waves
-    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(VM_AHEAD) : "memory");
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    const uint4* An = sA + SN * S_TILE;
+    const uint4* Bn = sB + SN * S_TILE;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[0][i] = as_bf16x8(An[a_row[i] + cq[0]]);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) fb[0][j] = as_bf16x8(Bn[b_row[j] + cq[0]]);
   };
 
   // A wave whose 128 rows all lie past the tile's row range (the tail tile of
@@ -430,23 +435,22 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_nt_kernel(const uint16_t* __
   const bool live = m0 + wm * 128 < Mlim;
   int kt = 0;
   if (live) {
-    // steps in rounds of NSTAGE (stage index static), then the remaining steps
-    for (; kt + NSTAGE <= KT; kt += NSTAGE)
-      [&]<int... S>(std::integer_sequence<int, S...>) {
-        (step(std::integral_constant<int, S>{}, kt + S), ...);
-      }(std::make_integer_sequence<int, NSTAGE>{});
-    [&]<int... S>(std::integer_sequence<int, S...>) {
-      ((kt < KT ? (step(std::integral_constant<int, S>{}, kt), ++kt) : 0), ...);
-    }(std::make_integer_sequence<int, NSTAGE - 1>{});
+    for (; kt + 2 <= KT; kt += 2) {
+      step(std::integral_constant<int, 0>{}, kt);
+      step(std::integral_constant<int, 1>{}, kt + 1);
+    }
+    if (kt < KT) step(std::integral_constant<int, 0>{}, kt);
   } else {
     for (; kt < KT; ++kt) {
-      const int k0 = min(kt + NSTAGE - 1, KT - 1) * SBK;
-      const int sn = (kt + NSTAGE - 1) % NSTAGE;
+      if (kt + 1 < KT) {
+        const int k0 = (kt + 1) * SBK;
+        const int sn = (kt + 1) & 1;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) dmaA(sn, i, baseA + k0);
+        for (int i = 0; i < DMA_PER_OP; ++i) dmaA(sn, i, baseA + k0);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) dmaB(sn, i, bsrc(k0));
-      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(VM_AHEAD) : "memory");
+        for (int i = 0; i < DMA_PER_OP; ++i) dmaB(sn, i, bsrc(k0));
+      }
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
     }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no DMA may outlive the block
@@ -456,8 +460,8 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_nt_kernel(const uint16_t* __
   // Output tiles are staged in the idle ring (256 rows x 512 B, 16-byte chunks
   // swizzled by row) and written as whole 512-byte rows, 2 rows per wave store.
   // s_row holds each staged row's destination (-1: not stored).
-  __shared__ int s_row[GBM];
   char* T = (char*)g_stage;
+  int* s_row = (int*)(T + EPI_ROW);
   const int64_t cbase = second ? ep.c_off2 : 0;   // output column of this product's column 0
   auto stage_rows = [&]() {
     if (wn == 0 && lane < 32) {
@@ -472,8 +476,8 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_nt_kernel(const uint16_t* __
   };
   auto store_rows = [&]() {
 #pragma unroll 4
-    for (int k = 0; k < GBM / 16; ++k) {
-      const int row = wave * (GBM / 8) + 2 * k + (lane >> 5);
+    for (int k = 0; k < GBM / NWAVES / 2; ++k) {
+      const int row = wave * (GBM / NWAVES) + 2 * k + (lane >> 5);
       const int c = lane & 31;
       const int crow = s_row[row];
       const int col = n0 + c * 8;
@@ -487,27 +491,28 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_nt_kernel(const uint16_t* __
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < NJ; ++j)
 #pragma unroll
           for (int g = 0; g < 16; ++g) acc[i][j][g] *= rs[i];
     }
+    __syncthreads();   // every wave is done reading the ring
     if (ep.vec) {
       // one expand (set 2 for the second product of an N split), or both sets
       // for a K split; a loop, so the slab is instantiated once
       const int sets = (ep.k_split > 0 && ep.vec2) ? 2 : 1;
+      uint4* slab = (uint4*)(T + EPI_SLAB + wave * SLAB_BYTES);
 #pragma unroll 1
       for (int set = 0; set < sets; ++set) {
         const bool two = second || set == 1;
         lora_slab(ep, two ? ep.vec2 : ep.vec, two ? ep.lmat2 : ep.lmat, two ? ep.desc2 : ep.desc,
-                  n0, N, wn, lane, wave, tok, ad, acc);
+                  n0, N, wn, lane, slab, tok, ad, acc);
       }
     }
-    __syncthreads();   // every wave is done reading the ring
     stage_rows();
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < NJ; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q)
           stage(i, j, q, make_uint2(pack2bf(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
@@ -515,9 +520,10 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_nt_kernel(const uint16_t* __
     __syncthreads();
     store_rows();
   } else if constexpr (EPI == EPI_LSE) {
-    // (max, sum) pairs of the four 64-column quarters, then merged per row in
-    // quarter order (deterministic)
-    __shared__ float2 red_s[4][GBM];
+    // (max, sum) pairs of the NWN column slices of the waves, then merged per
+    // row in slice order (deterministic)
+    __syncthreads();   // every wave is done reading the ring
+    float2 (*red_s)[GBM] = (float2 (*)[GBM])(T + EPI_SLAB);
     const int cbase = n0 + wn * WN;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -526,7 +532,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_nt_kernel(const uint16_t* __
       // this lane's 32 values of row `row`: columns cbase + j*32 + 8q + n_q + e
       float mx = -INFINITY;
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < NJ; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q)
 #pragma unroll
@@ -536,7 +542,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_nt_kernel(const uint16_t* __
       float sm = 0.f;
       if (mx != -INFINITY) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < NJ; ++j)
 #pragma unroll
           for (int q = 0; q < 4; ++q)
 #pragma unroll
@@ -552,7 +558,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_nt_kernel(const uint16_t* __
           const int jj = yo >> 5, qq = (yo >> 3) & 3, ee = yo & 3;
           float zv = 0.f;
 #pragma unroll
-          for (int j = 0; j < 2; ++j)
+          for (int j = 0; j < NJ; ++j)
 #pragma unroll
             for (int q = 0; q < 4; ++q)
 #pragma unroll
@@ -568,10 +574,10 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_nt_kernel(const uint16_t* __
       if (m0 + r >= M) continue;
       float mx = -INFINITY;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) mx = fmaxf(mx, red_s[w][r].x);
+      for (int w = 0; w < NWN; ++w) mx = fmaxf(mx, red_s[w][r].x);
       float sm = 0.f;
 #pragma unroll
-      for (int w = 0; w < 4; ++w)
+      for (int w = 0; w < NWN; ++w)
         if (red_s[w][r].x != -INFINITY) sm += red_s[w][r].y * exp2f((red_s[w][r].x - mx) * kLog2e);
       ep.part_m[(int64_t)tn * M + m0 + r] = mx;
       ep.part_s[(int64_t)tn * M + m0 + r] = sm;
@@ -582,7 +588,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_nt_kernel(const uint16_t* __
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < NJ; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int col = n0 + wn * WN + j * 32 + 8 * q + n_q;
