@@ -37,7 +37,7 @@ METRIC = "tokens/s mixed-adapter LoRA fwd+bwd at 8B shapes; % MFMA / HBM peak"
 # WRITE_SIZE passes scaled by a 512 MiB copy's readings (x2 fetch, x1 write):
 # profiles/gemm_nt_traffic_8192x4096x4096.md.  Valid only for the kernel source the
 # counters were taken on (sha256 prefix of gemm.hip + common.hpp); else reported null.
-GEMM_TRAFFIC = {"bytes_per_launch": 476.4e6, "src_sha256": "d55dba18c4be082b"}
+GEMM_TRAFFIC = {"bytes_per_launch": 484.8e6, "src_sha256": "1194a31138651e21"}
 
 
 def gemm_traffic():
