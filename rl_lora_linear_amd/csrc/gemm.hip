@@ -391,7 +391,9 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_nt_kernel(const uint16_t* __
   // groups, and the step's 2 DMA_PER_OP DMA instructions (the other stage, k
   // step kt + 1) one per group of the first phase, so the vector-memory, LDS
   // and scalar work issues in the shadow of the matrix pipe and the DMA has
-  // most of the step to land.  sched_barrier keeps the groups
+  // most of the step to land.  The step's one barrier sits in the middle of
+  // its last phase, whose second half reads the next stage's first slice
+  // under the remaining MFMAs.  sched_barrier keeps the groups
   // in this order.  After the wait and the barrier the next stage is visible
   // and its first slice is read.
   auto step = [&](auto S_, int kt) {
@@ -399,20 +401,40 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_nt_kernel(const uint16_t* __
     constexpr int SN = 1 - S;
     const uint4* At = sA + S * S_TILE;
     const uint4* Bt = sB + S * S_TILE;
+    const uint4* An = sA + SN * S_TILE;
+    const uint4* Bn = sB + SN * S_TILE;
     const bool more = kt + 1 < KT;
     const int k0 = (more ? kt + 1 : kt) * SBK;
     const uint16_t* ka = baseA + k0;
     const uint16_t* kb = bsrc(k0);
+    constexpr int G = 4 * NJ;   // MFMA groups per phase
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int cur = q & 1, nxt = cur ^ 1;
-      static_assert(4 * NJ == 2 * DMA_PER_OP, "one DMA per group of the first phase");
+      static_assert(G == 2 * DMA_PER_OP, "one DMA per group of the first phase");
 #pragma unroll
-      for (int g = 0; g < 4 * NJ; ++g) {
+      for (int g = 0; g < G; ++g) {
         const int i = g / NJ, j = g % NJ;
+        if (q == 3 && g == G / 2) {
+          // this wave's reads of stage S are complete and its DMA of stage SN
+          // has landed; after the barrier both hold for every wave, so the
+          // rest of the phase reads the next stage's first slice and the next
+          // step may refill stage S
+          asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        }
         acc[i][j] = mfma32(fb[cur][j], fa[cur][i], acc[i][j]);
-        if (q < 3 && g < 4) fa[nxt][g] = as_bf16x8(At[a_row[g] + cq[q + 1]]);
-        else if (q < 3 && g < 4 + NJ) fb[nxt][g - 4] = as_bf16x8(Bt[b_row[g - 4] + cq[q + 1]]);
+        if (q < 3) {
+          if (g < 4) fa[nxt][g] = as_bf16x8(At[a_row[g] + cq[q + 1]]);
+          else if (g < 4 + NJ) fb[nxt][g - 4] = as_bf16x8(Bt[b_row[g - 4] + cq[q + 1]]);
+        } else if (g >= G / 2) {
+          // 4 + NJ reads over the last G / 2 groups
+#pragma unroll
+          for (int t = 0; t < 4 + NJ; ++t) {
+            if (t * (G / 2) / (4 + NJ) != g - G / 2) continue;
+            if (t < 4) fa[nxt][t] = as_bf16x8(An[a_row[t] + cq[0]]);
+            else fb[nxt][t - 4] = as_bf16x8(Bn[b_row[t - 4] + cq[0]]);
+          }
+        }
         if (q == 0 && more) {   // the whole next stage as early as possible
           if (g < DMA_PER_OP) dmaA(SN, g, ka);
           else dmaB(SN, g - DMA_PER_OP, kb);
@@ -420,13 +442,6 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_nt_kernel(const uint16_t* __
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-    const uint4* An = sA + SN * S_TILE;
-    const uint4* Bn = sB + SN * S_TILE;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) fa[0][i] = as_bf16x8(An[a_row[i] + cq[0]]);
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) fb[0][j] = as_bf16x8(Bn[b_row[j] + cq[0]]);
   };
 
   // A wave whose 128 rows all lie past the tile's row range (the tail tile of
