@@ -231,9 +231,16 @@ def run_parity(dm, ex, w, y, dx, grads, trace, ids=None):
                 assert rel_err(dB[a][e], dB_ref[p][a][e]) < TOL_F32, (p, a, e, "dB")
 
 
-@pytest.mark.parametrize("kind", ["small", "wide"])
+@pytest.mark.parametrize("kind", ["small", "wide", "rank48"])
 def test_moe_forward_backward_parity(kind):
-    c = _case() if kind == "small" else _case(n=700, H=320, F=128, E=6, K=3, n_ad=2, r=32, seed=22)
+    """small/wide: ranks 16 and 32 (gate and up share one pass over x in the
+    shrink and the dA reduction); rank48: max_rank 64, the two-pass path."""
+    if kind == "small":
+        c = _case()
+    elif kind == "wide":
+        c = _case(n=700, H=320, F=128, E=6, K=3, n_ad=2, r=32, seed=22)
+    else:
+        c = _case(n=400, H=192, F=256, E=5, K=2, n_ad=2, r=48, seed=25)
     dm = DevMoe(c)
     ex, w = dm.route()
     y = dm.forward(ex, w)
