@@ -557,7 +557,7 @@ struct MoeWs {
   float* wpos;       // backward: routing weight per position
   uint16_t* v[3];    // backward: s*v planes per projection [2][NK][R] (down: s*w*v)
   uint16_t* uw;      // backward: w * (s u_down) planes
-  uint16_t* dh;      // [NK][F]
+  uint16_t* dh;      // [NK][F] (the trace's, else not stored)
   uint16_t* dgu;     // [NK][2F]: d(gate pre-activation) | d(up pre-activation)
   uint16_t* dxp;     // [NK][H]: per-assignment dx (gate and up parts summed)
   float* partial;
@@ -608,7 +608,6 @@ MoeWs carve_moe(const moe_shape& sh, void* ws, size_t bytes, bool backward) {
     w.wpos = cv.take<float>(NK);
     for (int i = 0; i < 3; ++i) w.v[i] = cv.take<uint16_t>((size_t)2 * NK * sh.max_rank);
     w.uw = cv.take<uint16_t>((size_t)2 * NK * sh.max_rank);
-    w.dh = cv.take<uint16_t>((size_t)NK * sh.d_ff);
     w.dgu = cv.take<uint16_t>((size_t)NK * 2 * sh.d_ff);
     w.dxp = cv.take<uint16_t>((size_t)NK * sh.hidden);
     w.partial = cv.take<float>((size_t)grad_partial_floats(NK, n_keys,
@@ -653,15 +652,20 @@ lora_status moe_segments(const moe_shape& sh, const int32_t* experts, const int3
 }
 
 // Second weight set of a fused pair of expert projections (gate and up):
-// split = 1: a second product of n_out columns written at column n_out
-// (forward, [gate | up] rows); split = 2: K = 2 k_in, the second half of each
-// A row against W2 (backward dX, both expands added).
+// split = 2: K = 2 k_in, the second half of each A row against W2 (backward
+// dX, both expands added); split = 3: each tile holds n_out-columns halves of
+// gate and up (W2, LoRA set 2), C gets [gate | up] rows and hout = silu(gate) *
+// up (forward); split = 4: the product is dh (C nullable) and the epilogue
+// turns it into [dgate | dup] rows (dgu) from the saved [gate | up] rows (gu).
 struct MoePair {
   int split = 0;
   const uint16_t* W2 = nullptr;
   const uint16_t* planes2 = nullptr;
   const uint16_t* lmat2 = nullptr;
   const lora_adapter_desc* desc2 = nullptr;
+  uint16_t* hout = nullptr;
+  const uint16_t* gu = nullptr;
+  uint16_t* dgu = nullptr;
 };
 
 // One grouped expert projection over the sorted assignments: rows gathered
@@ -678,12 +682,18 @@ lora_status moe_project(const moe_shape& sh, const MoeWs& w, const uint16_t* A,
   f.vec2 = pair.planes2;
   f.lmat2 = pair.lmat2;
   f.desc2 = pair.desc2;
-  f.n_split = pair.split == 1;
-  f.c_off2 = pair.split == 1 ? n_out : 0;
   f.k_split = pair.split == 2 ? (int)k_in : 0;
+  f.glu = pair.split == 3 ? 1 : pair.split == 4 ? 2 : 0;
+  f.c_off2 = n_out;
+  f.hout = pair.hout;
+  f.ld_h = n_out;
+  f.gu = pair.gu;
+  f.ld_gu = 2 * n_out;
+  f.dgu = pair.dgu;
+  f.ld_dgu = 2 * n_out;
   const int64_t K = pair.split == 2 ? 2 * k_in : k_in;      // columns of A read
   const int64_t lda = a_rows ? k_in : K;                      // gathered rows: x itself
-  const int64_t ldc = pair.split == 1 ? 2 * n_out : n_out;
+  const int64_t ldc = pair.split == 3 ? 2 * n_out : n_out;
   f.a_rows = a_rows;
   f.a_rows_bound = a_rows_bound;
   f.rowscale = rowscale;
@@ -777,14 +787,14 @@ lora_status moe_forward(const moe_shape* shape, const uint16_t* x, const int32_t
                       w.offsets, w.pre32, n_keys, NK, sv.su[1], R, w.zero, s));
   }
   MoePair gu;
-  gu.split = 1;
+  gu.split = 3;
   gu.W2 = W_up;
   gu.planes2 = sv.su[1];
   gu.lmat2 = up_pack;
   gu.desc2 = w.desc[1];
+  gu.hout = sv.h;
   TRY(moe_project(sh, w, x, w.tokrow, sh.n_tokens, W_gate, F, H, sv.su[0], gate_pack, 1,
                   w.desc[0], nullptr, sv.gu, s, gu));
-  TRY(launch_swiglu_rows_fwd(NK, F, sv.gu, sv.h, s));
   // down, then the weighted combine back to tokens
   TRY(launch_shrink(sv.h, F, (int)F, down_pack, 0, w.desc[2], w.adpos, nullptr, nullptr, nullptr,
                     w.offsets, w.pre32, n_keys, NK, sv.su[2], R, w.zero, s));
@@ -838,8 +848,13 @@ lora_status moe_backward(const moe_shape* shape, const uint16_t* dy, const uint1
     // down: do_j = w_j dy_t.  v = s w B^T dy_t; dh = w (dy_t W_down) + A^T v
     TRY(launch_shrink(dy, H, (int)H, down_pack, 1, w.desc[2], w.adpos, w.tokrow, nullptr, w.wpos,
                       w.offsets, w.pre32, n_keys, NK, w.v[2], R, w.zero, s));
+    // dh = w (dy_t W_down) + A^T v, turned into [dgate | dup] in the epilogue
+    MoePair dg;
+    dg.split = 4;
+    dg.gu = sv.gu;
+    dg.dgu = w.dgu;
     TRY(moe_project(sh, w, dy, w.tokrow, sh.n_tokens, W_down_t, F, H, w.v[2], down_pack, 0,
-                    w.desc[2], w.wpos, w.dh, s));
+                    w.desc[2], w.wpos, w.dh, s, dg));
     // dB_down = sum dy_t (w s u)^T; dA_down = sum (s w v) h^T
     TRY(launch_planes_scale(sv.su[2], w.wpos, NK, R, w.uw, s));
   }
@@ -848,7 +863,6 @@ lora_status moe_backward(const moe_shape* shape, const uint16_t* dy, const uint1
   TRY(launch_grad(1, w.v[2], R, w.zero, sv.h, F, (int)F, w.desc[2], w.active, nullptr, 1,
                   w.offsets, w.prec, n_keys, NK, grads[2], w.partial, accumulate, s));
   if (NK > 0) {
-    TRY(launch_swiglu_rows_bwd(NK, F, w.dh, sv.gu, w.dgu, s));
     // gate and up: v = s B^T d per projection; dx_j = [dg | du] [W_gate; W_up]
     // (one K-concatenated GEMM) + A_gate^T v_gate + A_up^T v_up
     for (int i = 0; i < 2; ++i)

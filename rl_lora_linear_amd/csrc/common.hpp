@@ -55,6 +55,58 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
   return c.b;
 }
 
+// ---------------------------------------------------------------- SwiGLU
+// silu(z) = z * sigmoid(z), in fp32 from bf16 inputs, one rounding per output.
+// Shared by the elementwise kernels and the GEMM epilogues, so every path
+// produces the same bits.  sigmoid uses the hardware exp2 and reciprocal
+// (v_exp_f32, v_rcp_f32, ~1 ulp each): exp2 of a large argument is +inf and
+// its reciprocal 0, so both tails are exact.
+__device__ __forceinline__ float swiglu_sigmoid(float z) {
+  return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-z * 1.4426950408889634f));
+}
+// h = silu(g) * u
+__device__ __forceinline__ uint16_t swiglu_fwd1(uint16_t g, uint16_t u) {
+  const float z = bf2f(g);
+  const float sl = z * swiglu_sigmoid(z);
+  return f2bf(sl * bf2f(u));
+}
+// dg = dh * u * silu'(g), du = dh * silu(g)
+__device__ __forceinline__ void swiglu_bwd1(uint16_t dh, uint16_t g, uint16_t u, uint16_t& dg,
+                                            uint16_t& du) {
+  const float z = bf2f(g), uu = bf2f(u), d = bf2f(dh);
+  const float sg = swiglu_sigmoid(z);
+  const float sl = z * sg;
+  dg = f2bf(d * uu * (sg * (1.f + z * (1.f - sg))));
+  du = f2bf(d * sl);
+}
+__device__ __forceinline__ uint16_t lo16(uint32_t w) { return (uint16_t)(w & 0xFFFFu); }
+__device__ __forceinline__ uint16_t hi16(uint32_t w) { return (uint16_t)(w >> 16); }
+__device__ __forceinline__ uint32_t pk16(uint16_t a, uint16_t b) { return a | ((uint32_t)b << 16); }
+// 8 packed bf16 at once
+__device__ __forceinline__ uint4 swiglu_fwd8(uint4 g, uint4 u) {
+  const uint32_t gw[4] = {g.x, g.y, g.z, g.w}, uw[4] = {u.x, u.y, u.z, u.w};
+  uint32_t h[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    h[q] = pk16(swiglu_fwd1(lo16(gw[q]), lo16(uw[q])), swiglu_fwd1(hi16(gw[q]), hi16(uw[q])));
+  return make_uint4(h[0], h[1], h[2], h[3]);
+}
+__device__ __forceinline__ void swiglu_bwd8(uint4 dh, uint4 g, uint4 u, uint4& dg, uint4& du) {
+  const uint32_t dw[4] = {dh.x, dh.y, dh.z, dh.w}, gw[4] = {g.x, g.y, g.z, g.w},
+                 uw[4] = {u.x, u.y, u.z, u.w};
+  uint32_t a[4], b[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint16_t g0, u0, g1, u1;
+    swiglu_bwd1(lo16(dw[q]), lo16(gw[q]), lo16(uw[q]), g0, u0);
+    swiglu_bwd1(hi16(dw[q]), hi16(gw[q]), hi16(uw[q]), g1, u1);
+    a[q] = pk16(g0, g1);
+    b[q] = pk16(u0, u1);
+  }
+  dg = make_uint4(a[0], a[1], a[2], a[3]);
+  du = make_uint4(b[0], b[1], b[2], b[3]);
+}
+
 // ---------------------------------------------------------------- LDS transposing read
 // ds_read_b64_tr_b16: in each 16-lane group, lane 4q + j addresses row t0 + q,
 // columns 4j..4j+3 of a row-major bf16 tile; lane i of the group receives

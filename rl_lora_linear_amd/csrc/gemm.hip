@@ -61,19 +61,32 @@ struct GemmEpi {
   int64_t lmat_ld;
   const uint16_t* lmat;
   const lora_adapter_desc* desc;
-  // A second weight operand B2 (same ldb and group stride as B), two ways:
-  //   n_tiles1 > 0 (N split): column tiles >= n_tiles1 are the second product,
-  //     reading B2 and writing output columns c_off2 + n; its LoRA expand uses
-  //     the second set (vec2, lmat2, desc2);
-  //   k_split > 0 (K split, a multiple of 32): k >= k_split reads B2 at
-  //     column k - k_split, and both LoRA sets are added to every row.
+  // A second weight operand B2 (same ldb and group stride as B), for
+  //   k_split > 0 (K split, a multiple of 64): k >= k_split reads B2 at
+  //     column k - k_split, and both LoRA sets (vec/lmat/desc and
+  //     vec2/lmat2/desc2) are added to every row;
+  //   glu = 1 (below).
   const uint16_t* B2;
-  int n_tiles1;
   int64_t c_off2;
   int k_split;
   const uint16_t* vec2;
   const uint16_t* lmat2;
   const lora_adapter_desc* desc2;
+  // SwiGLU fused into the epilogue (EPI_BF16):
+  //   glu = 1: a 256-column tile holds 128 columns n0.. of the first product
+  //     (B, LoRA set 1) and the same 128 columns of the second (B2, set 2);
+  //     C gets [gate | up] rows (up at column c_off2) and hout[row][n] =
+  //     silu(gate) * up from the stored bf16 values;
+  //   glu = 2: the product is dh (C nullable: stored only when given); with
+  //     gu rows [gate | up] (stride ld_gu, up at c_off2) the epilogue writes
+  //     dgu rows [dgate | dup] (stride ld_dgu, dup at c_off2).
+  int glu;
+  uint16_t* hout;
+  int64_t ld_h;
+  const uint16_t* gu;
+  int64_t ld_gu;
+  uint16_t* dgu;
+  int64_t ld_dgu;
   const uint8_t* active;
   const int32_t* adpos;   // [M] adapter of each row position, -1 for rows without one
   int n_ad;
@@ -263,20 +276,16 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_nt_kernel(const uint16_t* __
     tm = first_m + in % gm;
     tn = in / gm;
   }
-  const bool second = ep.n_tiles1 > 0 && tn >= ep.n_tiles1;   // N split: second product
-  if (second) {
-    tn -= ep.n_tiles1;
-    B = ep.B2;
-  }
+  const bool glu1 = EPI == EPI_BF16 && ep.glu == 1;   // [gate | up] halves in one tile
   int m0 = tm * GBM;
-  const int n0 = tn * GBN;
+  const int n0 = tn * (glu1 ? GBN / 2 : GBN);
   int Mlim = M;   // positions >= Mlim are past this tile's row range
-  const uint16_t* B2g = ep.B2;   // K split: second operand of this tile's group
+  const uint16_t* B2g = ep.B2;   // second operand of this tile's group (K split, glu)
   if (ep.g_tile) {
     m0 = ep.g_off[g * ep.g_stride] + tm * GBM;
     Mlim = ep.g_off[(g + 1) * ep.g_stride];
     B += (int64_t)g * ep.ldb_group;
-    if (ep.k_split > 0) B2g = ep.B2 + (int64_t)g * ep.ldb_group;
+    if (ep.B2) B2g = ep.B2 + (int64_t)g * ep.ldb_group;
   }
 
   const int tid = threadIdx.x;
@@ -335,7 +344,9 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_nt_kernel(const uint16_t* __
   // chunk (L % 8) ^ lds_sw(row).
   uint32_t offA[DMA_PER_OP], offB[DMA_PER_OP];
   const uint16_t* baseA = ep.a_rows ? A : A + (int64_t)m0 * lda;
-  const uint16_t* baseB = B + (int64_t)n0 * ldb;
+  // glu: the waves loading tile rows 128.. load the second product's rows
+  const bool bhalf = glu1 && wave >= NWAVES / 2;
+  const uint16_t* baseB = (bhalf ? B2g : B) + (int64_t)n0 * ldb;
   // K split: k >= ksplit reads the second operand (same row offsets)
   const int ksplit = ep.k_split > 0 ? ep.k_split : K;
   const uint16_t* baseB2 = ep.k_split > 0 ? B2g + (int64_t)n0 * ldb : baseB;
@@ -345,7 +356,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_nt_kernel(const uint16_t* __
     const int row = (wave * DMA_PER_OP + i) * 8 + (lane >> 3);
     const int chunk = (lane & 7) ^ lds_sw(row);
     const int ra = min(m0 + row, Mlim - 1);
-    const int rb = min(n0 + row, N - 1);
+    const int rb = min(n0 + (glu1 ? (row & (GBN / 2 - 1)) : row), N - 1);
     const int64_t oa = ep.a_rows ? (int64_t)ep.a_rows[ra] * lda : (int64_t)(ra - m0) * lda;
     offA[i] = (uint32_t)((oa + chunk * 8) * 2);
     offB[i] = (uint32_t)(((int64_t)(rb - n0) * ldb + chunk * 8) * 2);
@@ -477,7 +488,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_nt_kernel(const uint16_t* __
   // s_row holds each staged row's destination (-1: not stored).
   char* T = (char*)g_stage;
   int* s_row = (int*)(T + EPI_ROW);
-  const int64_t cbase = second ? ep.c_off2 : 0;   // output column of this product's column 0
+  // glu = 1: staged columns 0..127 are the first product, 128..255 the second
   auto stage_rows = [&]() {
     if (wn == 0 && lane < 32) {
 #pragma unroll
@@ -489,15 +500,69 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_nt_kernel(const uint16_t* __
     const int chunk = wn * (WN / 8) + j * 4 + q;
     *(uint2*)(T + row * 512 + ((chunk ^ (row & 31)) << 4) + ((lane >> 5) << 3)) = v;
   };
+  auto staged = [&](int row, int c) {
+    return *(const uint4*)(T + row * 512 + ((c ^ (row & 31)) << 4));
+  };
+  constexpr int NIT = GBM / NWAVES / 2;   // store iterations per wave (2 rows each)
   auto store_rows = [&]() {
+    const int c = lane & 31;
+    if (EPI == EPI_BF16 && ep.glu == 2) {
+      // the saved [gate | up] values of every row this lane stores, loaded
+      // up front (the accumulators are dead by now) so their latency is paid
+      // once
+      uint4 gq[NIT], uq[NIT];
+#pragma unroll
+      for (int k = 0; k < NIT; ++k) {
+        const int row = wave * (GBM / NWAVES) + 2 * k + (lane >> 5);
+        const int crow = s_row[row];
+        const int col = n0 + c * 8;
+        gq[k] = uq[k] = make_uint4(0, 0, 0, 0);
+        if (crow >= 0 && col < N) {
+          const uint16_t* gp = ep.gu + (int64_t)crow * ep.ld_gu + col;
+          gq[k] = *(const uint4*)gp;
+          uq[k] = *(const uint4*)(gp + ep.c_off2);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < NIT; ++k) {
+        const int row = wave * (GBM / NWAVES) + 2 * k + (lane >> 5);
+        const int crow = s_row[row];
+        const int col = n0 + c * 8;
+        if (crow >= 0 && col < N) {
+          const uint4 v = staged(row, c);
+          if (ep.C) *(uint4*)(ep.C + (int64_t)crow * ep.ldc + col) = v;
+          uint4 dg, du;
+          swiglu_bwd8(v, gq[k], uq[k], dg, du);
+          uint16_t* dp = ep.dgu + (int64_t)crow * ep.ld_dgu + col;
+          *(uint4*)dp = dg;
+          *(uint4*)(dp + ep.c_off2) = du;
+        }
+      }
+      return;
+    }
 #pragma unroll 4
-    for (int k = 0; k < GBM / NWAVES / 2; ++k) {
+    for (int k = 0; k < NIT; ++k) {
       const int row = wave * (GBM / NWAVES) + 2 * k + (lane >> 5);
-      const int c = lane & 31;
       const int crow = s_row[row];
-      const int col = n0 + c * 8;
-      const uint4 v = *(const uint4*)(T + row * 512 + ((c ^ (row & 31)) << 4));
-      if (crow >= 0 && col < N) *(uint4*)(ep.C + (int64_t)crow * ep.ldc + cbase + col) = v;
+      const uint4 v = staged(row, c);
+      if (EPI == EPI_BF16 && ep.glu == 1) {
+        const int part = c >> 4;   // 0: gate, 1: up
+        const int col = n0 + (c & 15) * 8;
+        if (crow >= 0 && col < N) {
+          *(uint4*)(ep.C + (int64_t)crow * ep.ldc + part * ep.c_off2 + col) = v;
+          // h: every lane takes 4 columns, (c & 15) * 8 + 4 * part ..
+          const char* gp = T + row * 512 + (((c & 15) ^ (row & 31)) << 4) + part * 8;
+          const char* up = T + row * 512 + ((((c & 15) + 16) ^ (row & 31)) << 4) + part * 8;
+          const uint2 g4 = *(const uint2*)gp, u4 = *(const uint2*)up;
+          const uint2 h4 = make_uint2(
+              pk16(swiglu_fwd1(lo16(g4.x), lo16(u4.x)), swiglu_fwd1(hi16(g4.x), hi16(u4.x))),
+              pk16(swiglu_fwd1(lo16(g4.y), lo16(u4.y)), swiglu_fwd1(hi16(g4.y), hi16(u4.y))));
+          *(uint2*)(ep.hout + (int64_t)crow * ep.ld_h + col + 4 * part) = h4;
+        }
+      } else {
+        const int col = n0 + c * 8;
+        if (crow >= 0 && col < N) *(uint4*)(ep.C + (int64_t)crow * ep.ldc + col) = v;
+      }
     }
   };
 
@@ -512,15 +577,17 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_nt_kernel(const uint16_t* __
     }
     __syncthreads();   // every wave is done reading the ring
     if (ep.vec) {
-      // one expand (set 2 for the second product of an N split), or both sets
+      // one expand (set 2 for the second half of a glu tile), or both sets
       // for a K split; a loop, so the slab is instantiated once
       const int sets = (ep.k_split > 0 && ep.vec2) ? 2 : 1;
+      const bool upper = glu1 && wn >= NWN / 2;
+      const int wn_eff = glu1 ? wn % (NWN / 2) : wn;   // column slice within its product
       uint4* slab = (uint4*)(T + EPI_SLAB + wave * SLAB_BYTES);
 #pragma unroll 1
       for (int set = 0; set < sets; ++set) {
-        const bool two = second || set == 1;
+        const bool two = upper || set == 1;
         lora_slab(ep, two ? ep.vec2 : ep.vec, two ? ep.lmat2 : ep.lmat, two ? ep.desc2 : ep.desc,
-                  n0, N, wn, lane, slab, tok, ad, acc);
+                  n0, N, wn_eff, lane, slab, tok, ad, acc);
       }
     }
     stage_rows();
@@ -639,13 +706,17 @@ static lora_status launch_gemm(const uint16_t* A, const uint16_t* B, int M, int 
     return LORA_E_UNSUPPORTED;
   }
   const int tiles_m = ep.g_tile ? tiles_m_bound : (int)cdiv(M, GBM);
-  const int tiles_n = (int)cdiv(N, GBN) * (ep.n_tiles1 > 0 ? 2 : 1);
-  if (ep.k_split > 0 && (ep.k_split % SBK || ep.k_split >= K || !ep.B2)) {
-    set_error("gemm: K split %d must be a multiple of %d below K = %d, with B2", ep.k_split, SBK, K);
+  const int tiles_n = (int)cdiv(N, EPI == EPI_BF16 && ep.glu == 1 ? GBN / 2 : GBN);
+  if (EPI == EPI_BF16 && ep.glu == 1 && (!ep.B2 || !ep.hout || ep.k_split > 0)) {
+    set_error("gemm: glu needs B2 and hout, and no K split");
     return LORA_E_INVALID_ARG;
   }
-  if (ep.n_tiles1 > 0 && !ep.B2) {
-    set_error("gemm: N split needs B2");
+  if (EPI == EPI_BF16 && ep.glu == 2 && (!ep.gu || !ep.dgu || ep.vec2)) {
+    set_error("gemm: glu backward needs gu and dgu, one LoRA set");
+    return LORA_E_INVALID_ARG;
+  }
+  if (ep.k_split > 0 && (ep.k_split % SBK || ep.k_split >= K || !ep.B2)) {
+    set_error("gemm: K split %d must be a multiple of %d below K = %d, with B2", ep.k_split, SBK, K);
     return LORA_E_INVALID_ARG;
   }
   if (tiles_m <= 0) return LORA_OK;
@@ -693,12 +764,18 @@ lora_status gemm_nt_rows(const uint16_t* A, const uint16_t* B, uint16_t* C, int 
   ep.lmat = f.lmat;
   ep.desc = f.desc;
   ep.B2 = f.B2;
-  ep.n_tiles1 = f.n_split ? (int)cdiv(N, GBN) : 0;
   ep.c_off2 = f.c_off2;
   ep.k_split = f.k_split;
   ep.vec2 = f.vec2;
   ep.lmat2 = f.lmat2;
   ep.desc2 = f.desc2;
+  ep.glu = f.glu;
+  ep.hout = f.hout;
+  ep.ld_h = f.ld_h;
+  ep.gu = f.gu;
+  ep.ld_gu = f.ld_gu;
+  ep.dgu = f.dgu;
+  ep.ld_dgu = f.ld_dgu;
   ep.adpos = f.adpos;
   ep.n_ad = f.n_ad;
   return launch_gemm<EPI_BF16>(A, B, M, N, K, lda, ldb, ep, s, group_m, f.a_rows_bound,

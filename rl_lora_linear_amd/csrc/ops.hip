@@ -234,34 +234,22 @@ __global__ __launch_bounds__(256) void adam_multi_kernel(AdamSegs sg, float* __r
 }
 
 // ------------------------------------------------------------------ SwiGLU
-__device__ __forceinline__ float sigmoidf_(float z) { return 1.f / (1.f + exp2f(-z * kLog2eF)); }
 
-// Flat (F = 0): n elements, every array contiguous.  Rows (F > 0, a multiple
-// of 8, n = rows * F): gate/up rows at stride ld_in, dh rows contiguous
-// (stride F), outputs at stride ld_out.
 template <bool BWD>
 __global__ __launch_bounds__(256) void swiglu_kernel(int64_t n, const uint16_t* __restrict__ dh,
                                                      const uint16_t* __restrict__ gt,
                                                      const uint16_t* __restrict__ up,
                                                      uint16_t* __restrict__ o1,
-                                                     uint16_t* __restrict__ o2, int64_t F,
-                                                     int64_t ld_in, int64_t ld_out) {
+                                                     uint16_t* __restrict__ o2) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   const int64_t n8 = n / 8;
-  const uint32_t f8 = (uint32_t)(F / 8);
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8 + (n % 8 ? 1 : 0);
        i += stride) {
     const bool full = i < n8;
-    int64_t oin = i * 8, oc = i * 8, oout = i * 8;
-    if (F > 0) {   // n8 < 2^32 (checked by the host)
-      const uint32_t row = (uint32_t)i / f8, col = ((uint32_t)i - row * f8) * 8;
-      oin = (int64_t)row * ld_in + col;
-      oc = (int64_t)row * F + col;
-      oout = (int64_t)row * ld_out + col;
-    }
+    const int64_t o = i * 8;
     uint16_t G[8], U[8], D[8];
     if (full) {
-      const uint4 a = *(const uint4*)(gt + oin), b = *(const uint4*)(up + oin);
+      const uint4 a = *(const uint4*)(gt + o), b = *(const uint4*)(up + o);
       const uint32_t wa[4] = {a.x, a.y, a.z, a.w}, wb[4] = {b.x, b.y, b.z, b.w};
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
@@ -269,7 +257,7 @@ __global__ __launch_bounds__(256) void swiglu_kernel(int64_t n, const uint16_t* 
         U[q] = (uint16_t)(wb[q >> 1] >> ((q & 1) * 16));
       }
       if (BWD) {
-        const uint4 c = *(const uint4*)(dh + oc);
+        const uint4 c = *(const uint4*)(dh + o);
         const uint32_t wc[4] = {c.x, c.y, c.z, c.w};
 #pragma unroll
         for (int q = 0; q < 8; ++q) D[q] = (uint16_t)(wc[q >> 1] >> ((q & 1) * 16));
@@ -286,21 +274,13 @@ __global__ __launch_bounds__(256) void swiglu_kernel(int64_t n, const uint16_t* 
     uint16_t r1[8], r2[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      const float z = bf2f(G[q]), u = bf2f(U[q]);
-      const float sg = sigmoidf_(z);
-      const float sl = z * sg;
-      if (!BWD) {
-        r1[q] = f2bf(sl * u);
-      } else {
-        const float d = bf2f(D[q]);
-        r1[q] = f2bf(d * u * (sg * (1.f + z * (1.f - sg))));
-        r2[q] = f2bf(d * sl);
-      }
+      if (!BWD) r1[q] = swiglu_fwd1(G[q], U[q]);
+      else swiglu_bwd1(D[q], G[q], U[q], r1[q], r2[q]);
     }
     if (full) {
-      *(uint4*)(o1 + oout) = make_uint4(r1[0] | (r1[1] << 16), r1[2] | (r1[3] << 16), r1[4] | (r1[5] << 16), r1[6] | (r1[7] << 16));
+      *(uint4*)(o1 + o) = make_uint4(r1[0] | (r1[1] << 16), r1[2] | (r1[3] << 16), r1[4] | (r1[5] << 16), r1[6] | (r1[7] << 16));
       if (BWD)
-        *(uint4*)(o2 + oout) = make_uint4(r2[0] | (r2[1] << 16), r2[2] | (r2[3] << 16), r2[4] | (r2[5] << 16), r2[6] | (r2[7] << 16));
+        *(uint4*)(o2 + o) = make_uint4(r2[0] | (r2[1] << 16), r2[2] | (r2[3] << 16), r2[4] | (r2[5] << 16), r2[6] | (r2[7] << 16));
     } else {
       for (int q = 0; q < 8; ++q) {
         const int64_t e = i * 8 + q;
@@ -413,42 +393,15 @@ lora_status launch_swiglu_fwd(int64_t n, const uint16_t* g, const uint16_t* u, u
                               hipStream_t s) {
   if (n <= 0) return LORA_OK;
   hipLaunchKernelGGL(swiglu_kernel<false>, dim3(grid_for(cdiv(n, 8), 256)), dim3(256), 0, s, n,
-                     (const uint16_t*)nullptr, g, u, h, (uint16_t*)nullptr, (int64_t)0, (int64_t)0,
-                     (int64_t)0);
+                     (const uint16_t*)nullptr, g, u, h, (uint16_t*)nullptr);
   return launch_check("swiglu_fwd");
-}
-
-lora_status launch_swiglu_rows_fwd(int64_t rows, int64_t F, const uint16_t* gu, uint16_t* h,
-                                   hipStream_t s) {
-  const int64_t n = rows * F;
-  if (n <= 0) return LORA_OK;
-  if (F % 8 || n / 8 >= ((int64_t)1 << 32)) {
-    set_error("swiglu rows: F %lld must be a multiple of 8, rows * F / 8 < 2^32", (long long)F);
-    return LORA_E_INVALID_ARG;
-  }
-  hipLaunchKernelGGL(swiglu_kernel<false>, dim3(grid_for(n / 8, 256)), dim3(256), 0, s, n,
-                     (const uint16_t*)nullptr, gu, gu + F, h, (uint16_t*)nullptr, F, 2 * F, F);
-  return launch_check("swiglu_rows_fwd");
-}
-
-lora_status launch_swiglu_rows_bwd(int64_t rows, int64_t F, const uint16_t* dh,
-                                   const uint16_t* gu, uint16_t* dgu, hipStream_t s) {
-  const int64_t n = rows * F;
-  if (n <= 0) return LORA_OK;
-  if (F % 8 || n / 8 >= ((int64_t)1 << 32)) {
-    set_error("swiglu rows: F %lld must be a multiple of 8, rows * F / 8 < 2^32", (long long)F);
-    return LORA_E_INVALID_ARG;
-  }
-  hipLaunchKernelGGL(swiglu_kernel<true>, dim3(grid_for(n / 8, 256)), dim3(256), 0, s, n, dh, gu,
-                     gu + F, dgu, dgu + F, F, 2 * F, 2 * F);
-  return launch_check("swiglu_rows_bwd");
 }
 
 lora_status launch_swiglu_bwd(int64_t n, const uint16_t* dh, const uint16_t* g,
                               const uint16_t* u, uint16_t* dg, uint16_t* du, hipStream_t s) {
   if (n <= 0) return LORA_OK;
   hipLaunchKernelGGL(swiglu_kernel<true>, dim3(grid_for(cdiv(n, 8), 256)), dim3(256), 0, s, n, dh,
-                     g, u, dg, du, (int64_t)0, (int64_t)0, (int64_t)0);
+                     g, u, dg, du);
   return launch_check("swiglu_bwd");
 }
 

@@ -34,17 +34,26 @@ struct GemmRows {
   int64_t lmat_ld = 0;
   const uint16_t* lmat = nullptr;
   const lora_adapter_desc* desc = nullptr;
-  // Second weight operand B2 (same ldb / group stride as B), either
-  //   n_split: a second product of N columns in the same launch (B2, output
-  //            columns c_off2.., LoRA set 2), or
-  //   k_split: K = k_split + K2 with k >= k_split read from B2 (both LoRA sets).
+  // Second weight operand B2 (same ldb / group stride as B), for
+  //   k_split: K = k_split + K2 with k >= k_split read from B2 (both LoRA sets), or
+  //   glu = 1 (below).
   const uint16_t* B2 = nullptr;
-  int n_split = 0;
   int64_t c_off2 = 0;
   int k_split = 0;
   const uint16_t* vec2 = nullptr;
   const uint16_t* lmat2 = nullptr;
   const lora_adapter_desc* desc2 = nullptr;
+  // SwiGLU epilogue: glu = 1, one launch writes [gate | up] rows to C (up at
+  // column c_off2; B2 and LoRA set 2 for up) and hout = silu(gate) * up;
+  // glu = 2, the product is dh (C nullable) and the epilogue writes dgu rows
+  // [dgate | dup] from gu rows [gate | up] (second halves at c_off2).
+  int glu = 0;
+  uint16_t* hout = nullptr;
+  int64_t ld_h = 0;
+  const uint16_t* gu = nullptr;
+  int64_t ld_gu = 0;
+  uint16_t* dgu = nullptr;
+  int64_t ld_dgu = 0;
   const int32_t* adpos = nullptr;
   int n_ad = 0;
 };
@@ -107,12 +116,6 @@ lora_status launch_swiglu_fwd(int64_t n, const uint16_t* g, const uint16_t* u, u
                               hipStream_t s);
 lora_status launch_swiglu_bwd(int64_t n, const uint16_t* dh, const uint16_t* g,
                               const uint16_t* u, uint16_t* dg, uint16_t* du, hipStream_t s);
-// Rows of [gate | up] (gu [rows][2F]): h [rows][F] = silu(gate) * up; the
-// backward writes [dgate | dup] rows (dgu [rows][2F]) from dh [rows][F].
-lora_status launch_swiglu_rows_fwd(int64_t rows, int64_t F, const uint16_t* gu, uint16_t* h,
-                                   hipStream_t s);
-lora_status launch_swiglu_rows_bwd(int64_t rows, int64_t F, const uint16_t* dh,
-                                   const uint16_t* gu, uint16_t* dgu, hipStream_t s);
 lora_status launch_add_bf16(int64_t n, const uint16_t* a, const uint16_t* b, uint16_t* out,
                             hipStream_t s);
 lora_status launch_transpose_bf16(const uint16_t* src, uint16_t* dst, int64_t rows, int64_t cols,
