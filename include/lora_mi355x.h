@@ -380,6 +380,56 @@ lora_status moe_backward(const moe_shape* shape, const uint16_t* dy, const uint1
                          float* dgate_pack, float* dup_pack, float* ddown_pack, int accumulate,
                          uint16_t* trace, void* ws, size_t ws_bytes, void* stream);
 
+/* ---- SwiGLU MLP layer ------------------------------------------------ */
+
+/* The dense SwiGLU MLP with the token's LoRA adapter on each of its three
+ * projections (tinker-ticks, "How the SGMV kernel works": LoRA on every
+ * linear layer, one batch mixing adapters; TPU RL note, section 12, for the
+ * MLP's gate/up/down):
+ *   y_t = down(silu(gate x_t) * up x_t),  proj(z) = W z + s B_a (A_a z).
+ * It is the expert layer above with one expert and no routing: the same
+ * kernels, the same saved layout ("position order" = tokens stably sorted by
+ * adapter id, ids out of range last) and the same trace, with y and dx
+ * written to token rows.  Layouts (bf16): W_gate, W_up [F][H]; W_down [H][F];
+ * the backward takes W_gate_t, W_up_t [H][F] and W_down_t [F][H].  Descriptor
+ * tables [n_adapters] per projection; a token whose adapter id is out of range
+ * gets the base MLP only (LORA_FLAG_ID_RANGE); an adapter whose entry is
+ * invalid in any table carries no LoRA (LORA_FLAG_BAD_DESC), rank 0 silently. */
+typedef struct {
+  int64_t n_tokens;        /* N < 2^30 */
+  int64_t hidden;          /* H: multiple of 64 */
+  int64_t d_ff;            /* F: multiple of 64 */
+  int64_t gate_pack_elems; /* pack sizes, for descriptor bounds checks */
+  int64_t up_pack_elems;
+  int64_t down_pack_elems;
+  int32_t n_adapters;      /* 1 .. 16383 */
+  int32_t max_rank;        /* 16 .. 64, multiple of 16 */
+} mlp_shape;
+
+size_t mlp_workspace_bytes(const mlp_shape* shape);
+size_t mlp_saved_bytes(const mlp_shape* shape);
+
+/*   x bf16 [N][H], adapter_ids int32 [N]; y bf16 [N][H] out;
+ *   saved: mlp_saved_bytes bytes, 16-byte aligned, kept for mlp_backward. */
+lora_status mlp_forward(const mlp_shape* shape, const uint16_t* x, const int32_t* adapter_ids,
+                        const uint16_t* W_gate, const uint16_t* W_up, const uint16_t* W_down,
+                        const uint16_t* gate_pack, const uint16_t* up_pack,
+                        const uint16_t* down_pack, const lora_adapter_desc* gate_desc,
+                        const lora_adapter_desc* up_desc, const lora_adapter_desc* down_desc,
+                        uint16_t* y, void* saved, void* ws, size_t ws_bytes, void* stream);
+
+/*   dy bf16 [N][H]; dx bf16 [N][H] out; gradient packs and accumulate as for
+ *   moe_backward; trace (nullable) as for moe_backward with N*K = N. */
+lora_status mlp_backward(const mlp_shape* shape, const uint16_t* dy, const uint16_t* x,
+                         const int32_t* adapter_ids, const uint16_t* W_gate_t,
+                         const uint16_t* W_up_t, const uint16_t* W_down_t,
+                         const uint16_t* gate_pack, const uint16_t* up_pack,
+                         const uint16_t* down_pack, const lora_adapter_desc* gate_desc,
+                         const lora_adapter_desc* up_desc, const lora_adapter_desc* down_desc,
+                         const void* saved, uint16_t* dx, float* dgate_pack, float* dup_pack,
+                         float* ddown_pack, int accumulate, uint16_t* trace, void* ws,
+                         size_t ws_bytes, void* stream);
+
 /* ---- kernel timing (measurement) ------------------------------------- */
 
 /* When enabled, the library brackets each launch of the kernel classes below

@@ -582,7 +582,9 @@ MoeSaved carve_saved(const moe_shape& sh, void* p) {
   return m;
 }
 
-MoeWs carve_moe(const moe_shape& sh, void* ws, size_t bytes, bool backward) {
+// routed = false (the MLP layer): one expert, no routing weights; y and dx
+// are written straight to token rows, so there is no expert-output buffer.
+MoeWs carve_moe(const moe_shape& sh, void* ws, size_t bytes, bool backward, bool routed = true) {
   Carve cv(ws, bytes);
   MoeWs w{};
   const int64_t NK = std::max<int64_t>(sh.n_tokens * sh.top_k, 1);
@@ -603,13 +605,13 @@ MoeWs carve_moe(const moe_shape& sh, void* ws, size_t bytes, bool backward) {
   for (int i = 0; i < 3; ++i) w.desc[i] = cv.take<lora_adapter_desc>((size_t)n_keys);
   w.zero = cv.take<uint16_t>(128);
   if (!backward) {
-    w.o = cv.take<uint16_t>((size_t)NK * sh.hidden);
+    if (routed) w.o = cv.take<uint16_t>((size_t)NK * sh.hidden);
   } else {
     w.wpos = cv.take<float>(NK);
     for (int i = 0; i < 3; ++i) w.v[i] = cv.take<uint16_t>((size_t)2 * NK * sh.max_rank);
     w.uw = cv.take<uint16_t>((size_t)2 * NK * sh.max_rank);
     w.dgu = cv.take<uint16_t>((size_t)NK * 2 * sh.d_ff);
-    w.dxp = cv.take<uint16_t>((size_t)NK * sh.hidden);
+    if (routed) w.dxp = cv.take<uint16_t>((size_t)NK * sh.hidden);
     w.partial = cv.take<float>((size_t)grad_partial_floats(NK, n_keys,
                                                           std::max(sh.hidden, sh.d_ff),
                                                           2 * sh.max_rank));
@@ -675,9 +677,11 @@ lora_status moe_project(const moe_shape& sh, const MoeWs& w, const uint16_t* A,
                         int64_t n_out, int64_t k_in, const uint16_t* planes,
                         const uint16_t* lmat, int use_b_off, const lora_adapter_desc* desc,
                         const float* rowscale, uint16_t* C, hipStream_t s,
-                        const MoePair& pair = MoePair{}) {
+                        const MoePair& pair = MoePair{}, const int32_t* c_rows = nullptr) {
   const int64_t NK = sh.n_tokens * sh.top_k;
   GemmRows f;
+  f.c_rows = c_rows;        // output rows (the LoRA vectors stay in position order)
+  f.vec_by_pos = c_rows != nullptr;
   f.B2 = pair.W2;
   f.vec2 = pair.planes2;
   f.lmat2 = pair.lmat2;
@@ -743,31 +747,37 @@ size_t moe_saved_bytes(const moe_shape* shape) {
   return carve_saved(*shape, nullptr).total;
 }
 
-lora_status moe_forward(const moe_shape* shape, const uint16_t* x, const int32_t* experts,
-                        const float* weights, const int32_t* adapter_ids, const uint16_t* W_gate,
-                        const uint16_t* W_up, const uint16_t* W_down, const uint16_t* gate_pack,
-                        const uint16_t* up_pack, const uint16_t* down_pack,
-                        const lora_adapter_desc* gate_desc, const lora_adapter_desc* up_desc,
-                        const lora_adapter_desc* down_desc, uint16_t* y, void* saved, void* ws,
-                        size_t ws_bytes, void* stream) {
-  TRY(check_moe(shape));
-  const moe_shape& sh = *shape;
+}  // extern "C"
+
+namespace {
+
+// The SwiGLU expert layer behind moe_* (routed: experts and weights given)
+// and mlp_* (one expert, experts and weights null: y and dx go straight to
+// token rows, no combine).
+lora_status expert_forward(const moe_shape& sh, const uint16_t* x, const int32_t* experts,
+                           const float* weights, const int32_t* adapter_ids,
+                           const uint16_t* W_gate, const uint16_t* W_up, const uint16_t* W_down,
+                           const uint16_t* gate_pack, const uint16_t* up_pack,
+                           const uint16_t* down_pack, const lora_adapter_desc* gate_desc,
+                           const lora_adapter_desc* up_desc, const lora_adapter_desc* down_desc,
+                           uint16_t* y, void* saved, void* ws, size_t ws_bytes, hipStream_t s,
+                           const char* name) {
+  const bool routed = weights != nullptr;
   LORA_ARG_CHECK(W_gate && W_up && W_down && gate_pack && up_pack && down_pack && gate_desc &&
                      up_desc && down_desc,
-                 "weights, packs and descriptor tables must be non-NULL");
-  LORA_ARG_CHECK(sh.n_tokens == 0 || (x && experts && weights && adapter_ids && y && saved),
-                 "x, experts, weights, adapter_ids, y and saved must be non-NULL");
+                 "%s: weights, packs and descriptor tables must be non-NULL", name);
+  LORA_ARG_CHECK(sh.n_tokens == 0 || (x && adapter_ids && y && saved),
+                 "%s: x, adapter_ids, y and saved must be non-NULL", name);
   LORA_ARG_CHECK(aligned16(x) && aligned16(y) && aligned16(saved) && aligned16(W_gate) &&
                      aligned16(W_up) && aligned16(W_down) && aligned16(gate_pack) &&
                      aligned16(up_pack) && aligned16(down_pack),
-                 "activations, weights, packs and saved must be 16-byte aligned");
-  MoeWs w = carve_moe(sh, ws, ws_bytes, false);
+                 "%s: activations, weights, packs and saved must be 16-byte aligned", name);
+  MoeWs w = carve_moe(sh, ws, ws_bytes, false, routed);
   if (!ws || w.total > ws_bytes) {
-    set_error("moe_forward: workspace %zu bytes < %zu needed", ws_bytes, w.total);
+    set_error("%s: workspace %zu bytes < %zu needed", name, ws_bytes, w.total);
     return LORA_E_WORKSPACE;
   }
   if (sh.n_tokens == 0) return LORA_OK;
-  hipStream_t s = S(stream);
   const MoeSaved sv = carve_saved(sh, saved);
   const int64_t NK = sh.n_tokens * sh.top_k, H = sh.hidden, F = sh.d_ff;
   const int R = sh.max_rank;
@@ -775,7 +785,7 @@ lora_status moe_forward(const moe_shape* shape, const uint16_t* x, const int32_t
   const lora_adapter_desc* const descs[3] = {gate_desc, up_desc, down_desc};
   TRY(moe_segments(sh, experts, adapter_ids, descs, w, s));
   // gate and up: s*u planes from the gathered token rows (one pass over x when
-  // both fit one tile), then one grouped GEMM writing [gate | up] rows
+  // both fit one tile), then one grouped GEMM writing [gate | up] rows and h
   if (R <= 32) {
     TRY(launch_shrink(x, H, (int)H, gate_pack, 0, w.desc[0], w.adpos, w.tokrow, nullptr, nullptr,
                       w.offsets, w.pre32, n_keys, NK, sv.su[0], R, w.zero, s, up_pack, w.desc[1],
@@ -795,46 +805,48 @@ lora_status moe_forward(const moe_shape* shape, const uint16_t* x, const int32_t
   gu.hout = sv.h;
   TRY(moe_project(sh, w, x, w.tokrow, sh.n_tokens, W_gate, F, H, sv.su[0], gate_pack, 1,
                   w.desc[0], nullptr, sv.gu, s, gu));
-  // down, then the weighted combine back to tokens
   TRY(launch_shrink(sv.h, F, (int)F, down_pack, 0, w.desc[2], w.adpos, nullptr, nullptr, nullptr,
                     w.offsets, w.pre32, n_keys, NK, sv.su[2], R, w.zero, s));
+  if (!routed)   // down straight to the token rows
+    return moe_project(sh, w, sv.h, nullptr, NK, W_down, H, F, sv.su[2], down_pack, 1, w.desc[2],
+                       nullptr, y, s, MoePair{}, w.tokrow);
+  // down, then the weighted combine back to tokens
   TRY(moe_project(sh, w, sv.h, nullptr, NK, W_down, H, F, sv.su[2], down_pack, 1, w.desc[2],
                   nullptr, w.o, s));
   return launch_moe_combine(w.o, nullptr, weights, w.inv, w.keys, sh.n_tokens, sh.top_k, H, y, s);
 }
 
-lora_status moe_backward(const moe_shape* shape, const uint16_t* dy, const uint16_t* x,
-                         const int32_t* experts, const float* weights, const int32_t* adapter_ids,
-                         const uint16_t* W_gate_t, const uint16_t* W_up_t,
-                         const uint16_t* W_down_t, const uint16_t* gate_pack,
-                         const uint16_t* up_pack, const uint16_t* down_pack,
-                         const lora_adapter_desc* gate_desc, const lora_adapter_desc* up_desc,
-                         const lora_adapter_desc* down_desc, const void* saved, uint16_t* dx,
-                         float* dgate_pack, float* dup_pack, float* ddown_pack, int accumulate,
-                         uint16_t* trace, void* ws, size_t ws_bytes, void* stream) {
-  TRY(check_moe(shape));
-  const moe_shape& sh = *shape;
+lora_status expert_backward(const moe_shape& sh, const uint16_t* dy, const uint16_t* x,
+                            const int32_t* experts, const float* weights,
+                            const int32_t* adapter_ids, const uint16_t* W_gate_t,
+                            const uint16_t* W_up_t, const uint16_t* W_down_t,
+                            const uint16_t* gate_pack, const uint16_t* up_pack,
+                            const uint16_t* down_pack, const lora_adapter_desc* gate_desc,
+                            const lora_adapter_desc* up_desc, const lora_adapter_desc* down_desc,
+                            const void* saved, uint16_t* dx, float* dgate_pack, float* dup_pack,
+                            float* ddown_pack, int accumulate, uint16_t* trace, void* ws,
+                            size_t ws_bytes, hipStream_t s, const char* name) {
+  const bool routed = weights != nullptr;
   LORA_ARG_CHECK(W_gate_t && W_up_t && W_down_t && gate_pack && up_pack && down_pack &&
                      gate_desc && up_desc && down_desc && dgate_pack && dup_pack && ddown_pack,
-                 "weights, packs, descriptor tables and gradient packs must be non-NULL");
-  LORA_ARG_CHECK(sh.n_tokens == 0 || (dy && x && experts && weights && adapter_ids && saved && dx),
-                 "dy, x, experts, weights, adapter_ids, saved and dx must be non-NULL");
+                 "%s: weights, packs, descriptor tables and gradient packs must be non-NULL", name);
+  LORA_ARG_CHECK(sh.n_tokens == 0 || (dy && x && adapter_ids && saved && dx),
+                 "%s: dy, x, adapter_ids, saved and dx must be non-NULL", name);
   LORA_ARG_CHECK(aligned16(dy) && aligned16(x) && aligned16(dx) && aligned16(saved) &&
                      aligned16(W_gate_t) && aligned16(W_up_t) && aligned16(W_down_t) &&
                      aligned16(gate_pack) && aligned16(up_pack) && aligned16(down_pack) &&
                      aligned16(dgate_pack) && aligned16(dup_pack) && aligned16(ddown_pack),
-                 "activations, weights, packs and saved must be 16-byte aligned");
-  MoeWs w = carve_moe(sh, ws, ws_bytes, true);
+                 "%s: activations, weights, packs and saved must be 16-byte aligned", name);
+  MoeWs w = carve_moe(sh, ws, ws_bytes, true, routed);
   if (!ws || w.total > ws_bytes) {
-    set_error("moe_backward: workspace %zu bytes < %zu needed", ws_bytes, w.total);
+    set_error("%s: workspace %zu bytes < %zu needed", name, ws_bytes, w.total);
     return LORA_E_WORKSPACE;
   }
   if (trace) {   // the caller keeps dh and [dgate | dup]
-    LORA_ARG_CHECK(aligned16(trace), "trace must be 16-byte aligned");
+    LORA_ARG_CHECK(aligned16(trace), "%s: trace must be 16-byte aligned", name);
     w.dh = trace;
     w.dgu = trace + sh.n_tokens * sh.top_k * sh.d_ff;
   }
-  hipStream_t s = S(stream);
   const MoeSaved sv = carve_saved(sh, const_cast<void*>(saved));
   const int64_t NK = sh.n_tokens * sh.top_k, H = sh.hidden, F = sh.d_ff;
   const int R = sh.max_rank;
@@ -843,23 +855,25 @@ lora_status moe_backward(const moe_shape* shape, const uint16_t* dy, const uint1
   TRY(moe_segments(sh, experts, adapter_ids, descs, w, s));
   const uint16_t* packs[3] = {gate_pack, up_pack, down_pack};
   float* grads[3] = {dgate_pack, dup_pack, ddown_pack};
+  // routed: do_j = w_j dy_t, so v = s w B^T dy_t and u_down enters dB as w s u
+  const uint16_t* u_down = routed ? w.uw : sv.su[2];
   if (NK > 0) {
-    TRY(launch_moe_gather_w(weights, w.perm, NK, w.wpos, s));
-    // down: do_j = w_j dy_t.  v = s w B^T dy_t; dh = w (dy_t W_down) + A^T v
-    TRY(launch_shrink(dy, H, (int)H, down_pack, 1, w.desc[2], w.adpos, w.tokrow, nullptr, w.wpos,
-                      w.offsets, w.pre32, n_keys, NK, w.v[2], R, w.zero, s));
+    if (routed) TRY(launch_moe_gather_w(weights, w.perm, NK, w.wpos, s));
+    TRY(launch_shrink(dy, H, (int)H, down_pack, 1, w.desc[2], w.adpos, w.tokrow, nullptr,
+                      routed ? w.wpos : nullptr, w.offsets, w.pre32, n_keys, NK, w.v[2], R,
+                      w.zero, s));
     // dh = w (dy_t W_down) + A^T v, turned into [dgate | dup] in the epilogue
     MoePair dg;
     dg.split = 4;
     dg.gu = sv.gu;
     dg.dgu = w.dgu;
     TRY(moe_project(sh, w, dy, w.tokrow, sh.n_tokens, W_down_t, F, H, w.v[2], down_pack, 0,
-                    w.desc[2], w.wpos, w.dh, s, dg));
-    // dB_down = sum dy_t (w s u)^T; dA_down = sum (s w v) h^T
-    TRY(launch_planes_scale(sv.su[2], w.wpos, NK, R, w.uw, s));
+                    w.desc[2], routed ? w.wpos : nullptr, w.dh, s, dg));
+    if (routed) TRY(launch_planes_scale(sv.su[2], w.wpos, NK, R, w.uw, s));
   }
-  TRY(launch_grad(0, w.uw, R, w.zero, dy, H, (int)H, w.desc[2], w.active, w.tokrow, 1, w.offsets,
-                  w.prec, n_keys, NK, grads[2], w.partial, accumulate, s));
+  // dB_down = sum do_t (s u)^T; dA_down = sum (s v) h^T
+  TRY(launch_grad(0, u_down, R, w.zero, dy, H, (int)H, w.desc[2], w.active, w.tokrow, 1,
+                  w.offsets, w.prec, n_keys, NK, grads[2], w.partial, accumulate, s));
   TRY(launch_grad(1, w.v[2], R, w.zero, sv.h, F, (int)F, w.desc[2], w.active, nullptr, 1,
                   w.offsets, w.prec, n_keys, NK, grads[2], w.partial, accumulate, s));
   if (NK > 0) {
@@ -875,7 +889,7 @@ lora_status moe_backward(const moe_shape* shape, const uint16_t* dy, const uint1
     gu.lmat2 = up_pack;
     gu.desc2 = w.desc[1];
     TRY(moe_project(sh, w, w.dgu, nullptr, NK, W_gate_t, H, F, w.v[0], gate_pack, 0, w.desc[0],
-                    nullptr, w.dxp, s, gu));
+                    nullptr, routed ? w.dxp : dx, s, gu, routed ? nullptr : w.tokrow));
   }
   // dB = sum d (s u)^T; dA = sum (s v) x_t^T (gate and up in one pass over x
   // when both fit one tile)
@@ -891,8 +905,110 @@ lora_status moe_backward(const moe_shape* shape, const uint16_t* dy, const uint1
       TRY(launch_grad(1, w.v[i], R, w.zero, x, H, (int)H, w.desc[i], w.active, w.tokrow, 1,
                       w.offsets, w.prec, n_keys, NK, grads[i], w.partial, accumulate, s));
   }
+  if (!routed) return LORA_OK;
   return launch_moe_combine(w.dxp, nullptr, nullptr, w.inv, w.keys, sh.n_tokens, sh.top_k, H, dx,
                             s);
+}
+
+moe_shape mlp_as_moe(const mlp_shape& m) {
+  moe_shape sh{};
+  sh.n_tokens = m.n_tokens;
+  sh.hidden = m.hidden;
+  sh.d_ff = m.d_ff;
+  sh.gate_pack_elems = m.gate_pack_elems;
+  sh.up_pack_elems = m.up_pack_elems;
+  sh.down_pack_elems = m.down_pack_elems;
+  sh.n_experts = 1;
+  sh.top_k = 1;
+  sh.n_adapters = m.n_adapters;
+  sh.max_rank = m.max_rank;
+  return sh;
+}
+
+lora_status check_mlp(const mlp_shape* shape, moe_shape* out) {
+  LORA_ARG_CHECK(shape != nullptr, "mlp shape is NULL");
+  *out = mlp_as_moe(*shape);
+  return check_moe(out);
+}
+
+}  // namespace
+
+extern "C" {
+
+lora_status moe_forward(const moe_shape* shape, const uint16_t* x, const int32_t* experts,
+                        const float* weights, const int32_t* adapter_ids, const uint16_t* W_gate,
+                        const uint16_t* W_up, const uint16_t* W_down, const uint16_t* gate_pack,
+                        const uint16_t* up_pack, const uint16_t* down_pack,
+                        const lora_adapter_desc* gate_desc, const lora_adapter_desc* up_desc,
+                        const lora_adapter_desc* down_desc, uint16_t* y, void* saved, void* ws,
+                        size_t ws_bytes, void* stream) {
+  TRY(check_moe(shape));
+  LORA_ARG_CHECK(shape->n_tokens == 0 || (experts && weights),
+                 "moe_forward: experts and weights must be non-NULL");
+  return expert_forward(*shape, x, experts, weights, adapter_ids, W_gate, W_up, W_down, gate_pack,
+                        up_pack, down_pack, gate_desc, up_desc, down_desc, y, saved, ws, ws_bytes,
+                        S(stream), "moe_forward");
+}
+
+lora_status moe_backward(const moe_shape* shape, const uint16_t* dy, const uint16_t* x,
+                         const int32_t* experts, const float* weights, const int32_t* adapter_ids,
+                         const uint16_t* W_gate_t, const uint16_t* W_up_t,
+                         const uint16_t* W_down_t, const uint16_t* gate_pack,
+                         const uint16_t* up_pack, const uint16_t* down_pack,
+                         const lora_adapter_desc* gate_desc, const lora_adapter_desc* up_desc,
+                         const lora_adapter_desc* down_desc, const void* saved, uint16_t* dx,
+                         float* dgate_pack, float* dup_pack, float* ddown_pack, int accumulate,
+                         uint16_t* trace, void* ws, size_t ws_bytes, void* stream) {
+  TRY(check_moe(shape));
+  LORA_ARG_CHECK(shape->n_tokens == 0 || (experts && weights),
+                 "moe_backward: experts and weights must be non-NULL");
+  return expert_backward(*shape, dy, x, experts, weights, adapter_ids, W_gate_t, W_up_t, W_down_t,
+                         gate_pack, up_pack, down_pack, gate_desc, up_desc, down_desc, saved, dx,
+                         dgate_pack, dup_pack, ddown_pack, accumulate, trace, ws, ws_bytes,
+                         S(stream), "moe_backward");
+}
+
+size_t mlp_workspace_bytes(const mlp_shape* shape) {
+  moe_shape sh;
+  if (check_mlp(shape, &sh) != LORA_OK) return 0;
+  return std::max(carve_moe(sh, nullptr, 0, false, false).total,
+                  carve_moe(sh, nullptr, 0, true, false).total);
+}
+
+size_t mlp_saved_bytes(const mlp_shape* shape) {
+  moe_shape sh;
+  if (check_mlp(shape, &sh) != LORA_OK) return 0;
+  return carve_saved(sh, nullptr).total;
+}
+
+lora_status mlp_forward(const mlp_shape* shape, const uint16_t* x, const int32_t* adapter_ids,
+                        const uint16_t* W_gate, const uint16_t* W_up, const uint16_t* W_down,
+                        const uint16_t* gate_pack, const uint16_t* up_pack,
+                        const uint16_t* down_pack, const lora_adapter_desc* gate_desc,
+                        const lora_adapter_desc* up_desc, const lora_adapter_desc* down_desc,
+                        uint16_t* y, void* saved, void* ws, size_t ws_bytes, void* stream) {
+  moe_shape sh;
+  TRY(check_mlp(shape, &sh));
+  return expert_forward(sh, x, nullptr, nullptr, adapter_ids, W_gate, W_up, W_down, gate_pack,
+                        up_pack, down_pack, gate_desc, up_desc, down_desc, y, saved, ws, ws_bytes,
+                        S(stream), "mlp_forward");
+}
+
+lora_status mlp_backward(const mlp_shape* shape, const uint16_t* dy, const uint16_t* x,
+                         const int32_t* adapter_ids, const uint16_t* W_gate_t,
+                         const uint16_t* W_up_t, const uint16_t* W_down_t,
+                         const uint16_t* gate_pack, const uint16_t* up_pack,
+                         const uint16_t* down_pack, const lora_adapter_desc* gate_desc,
+                         const lora_adapter_desc* up_desc, const lora_adapter_desc* down_desc,
+                         const void* saved, uint16_t* dx, float* dgate_pack, float* dup_pack,
+                         float* ddown_pack, int accumulate, uint16_t* trace, void* ws,
+                         size_t ws_bytes, void* stream) {
+  moe_shape sh;
+  TRY(check_mlp(shape, &sh));
+  return expert_backward(sh, dy, x, nullptr, nullptr, adapter_ids, W_gate_t, W_up_t, W_down_t,
+                         gate_pack, up_pack, down_pack, gate_desc, up_desc, down_desc, saved, dx,
+                         dgate_pack, dup_pack, ddown_pack, accumulate, trace, ws, ws_bytes,
+                         S(stream), "mlp_backward");
 }
 
 lora_status bf16_add(int64_t n, const uint16_t* a, const uint16_t* b, uint16_t* out,

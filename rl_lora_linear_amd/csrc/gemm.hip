@@ -54,9 +54,11 @@ struct GemmEpi {
   // row at segment position m, owned by adapter a, add s_a * vec[tok] . M_a^T
   // with M_a [N][r_a] = B_a at b_off of the pack lmat (use_b_off = 1), or
   // M_a = A_a^T read in place from A_a [r_a][lmat_ld] at a_off (use_b_off = 0).
-  const uint16_t* vec;    // scaled vector, bf16 hi plane [tokens][vec_ld], token order
+  const uint16_t* vec;    // scaled vector, bf16 hi plane [rows][vec_ld]: row = the C row
+                          // (c_rows[m]), or the position m itself with vec_by_pos
   int64_t vec_plane;      // lo plane at vec + vec_plane
   int vec_ld;
+  int vec_by_pos;
   int use_b_off;
   int64_t lmat_ld;
   const uint16_t* lmat;
@@ -163,7 +165,7 @@ __device__ __forceinline__ void dma16s(uint32_t voff, const void* base, uint32_t
 __device__ __forceinline__ void lora_slab(const GemmEpi& ep, const uint16_t* vec,
                                           const uint16_t* lmat, const lora_adapter_desc* desc,
                                           int n0, int N, int wn, int lane, uint4* slab,
-                                          const int (&tok)[4], const int (&ad)[4],
+                                          const int (&vrow)[4], const int (&ad)[4],
                                           f32x16 (&acc)[4][NJ]) {
   const int m_l = lane & 31;
   const int half = lane >> 5;
@@ -193,7 +195,7 @@ __device__ __forceinline__ void lora_slab(const GemmEpi& ep, const uint16_t* vec
       for (int i = 0; i < 4; ++i) {
         h[i] = l[i] = make_uint4(0, 0, 0, 0);
         if (ad[i] == a && cok) {
-          const uint16_t* vp = vec + (int64_t)tok[i] * ep.vec_ld + c;
+          const uint16_t* vp = vec + (int64_t)vrow[i] * ep.vec_ld + c;
           h[i] = *(const uint4*)vp;
           l[i] = *(const uint4*)(vp + ep.vec_plane);
         }
@@ -260,13 +262,20 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_nt_kernel(const uint16_t* __
   int tm, tn, g = 0;
   if (ep.g_tile) {
     // grouped: tiles run group by group (group g owns tiles g_tile[g] * tiles_n
-    // .. g_tile[g + 1] * tiles_n), row tiles fastest, so the tiles one XCD runs
-    // at a time share their group's weight panels and row panels in its L2
+    // .. g_tile[g + 1] * tiles_n), row tiles fastest; a group of more than
+    // 2 group_m row tiles runs in blocks of group_m row tiles.  The tiles one
+    // XCD runs at a time then share their group's weight panels and row
+    // panels in its L2
     g = find_bucket(ep.g_tile, ep.n_groups + 1, t / tiles_n);
     const int nr = ep.g_tile[g + 1] - ep.g_tile[g];
+    const int bm = nr <= 2 * group_m ? nr : group_m;
     const int in = t - ep.g_tile[g] * tiles_n;
-    tm = in % nr;   // row tile within the group
-    tn = in / nr;
+    const int blk = in / (bm * tiles_n);
+    const int first = blk * bm;
+    const int gm = min(nr - first, bm);
+    const int r = in - blk * bm * tiles_n;
+    tm = first + r % gm;   // row tile within the group
+    tn = r / gm;
   } else {
     const int gsz = group_m * tiles_n;
     const int grp = t / gsz;
@@ -583,11 +592,14 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_nt_kernel(const uint16_t* __
       const bool upper = glu1 && wn >= NWN / 2;
       const int wn_eff = glu1 ? wn % (NWN / 2) : wn;   // column slice within its product
       uint4* slab = (uint4*)(T + EPI_SLAB + wave * SLAB_BYTES);
+      int vrow[4];   // vector row of each fragment row: its C row, or its position
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vrow[i] = ep.vec_by_pos ? m0 + wm * 128 + i * 32 + m_l : tok[i];
 #pragma unroll 1
       for (int set = 0; set < sets; ++set) {
         const bool two = upper || set == 1;
         lora_slab(ep, two ? ep.vec2 : ep.vec, two ? ep.lmat2 : ep.lmat, two ? ep.desc2 : ep.desc,
-                  n0, N, wn_eff, lane, slab, tok, ad, acc);
+                  n0, N, wn_eff, lane, slab, vrow, ad, acc);
       }
     }
     stage_rows();
@@ -759,6 +771,7 @@ lora_status gemm_nt_rows(const uint16_t* A, const uint16_t* B, uint16_t* C, int 
   ep.vec = f.vec;
   ep.vec_plane = f.vec_plane;
   ep.vec_ld = f.vec_ld;
+  ep.vec_by_pos = f.vec_by_pos;
   ep.use_b_off = f.use_b_off;
   ep.lmat_ld = f.lmat_ld;
   ep.lmat = f.lmat;

@@ -83,7 +83,7 @@ __global__ __launch_bounds__(256) void moe_keys_kernel(const int32_t* __restrict
                                                        int32_t* status) {
   const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (j >= n_assign) return;
-  const int e = experts[j];
+  const int e = experts ? experts[j] : 0;   // null: one expert
   int a = ids[j / K];
   int key = -1;   // expert out of range: dropped (the segment builder flags it)
   if (e >= 0 && e < E) {

@@ -30,6 +30,7 @@ struct GemmRows {
   const uint16_t* vec = nullptr;
   int64_t vec_plane = 0;
   int vec_ld = 0;
+  int vec_by_pos = 0;       // vec rows are positions (else the C rows)
   int use_b_off = 0;        // 1: M_a = B_a [N][r] at b_off; 0: A_a [r][lmat_ld] at a_off
   int64_t lmat_ld = 0;
   const uint16_t* lmat = nullptr;

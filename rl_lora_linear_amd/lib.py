@@ -32,7 +32,7 @@ EXPORTS = [
     "token_logprobs_backward_workspace_bytes", "token_logprobs_backward",
     "loss_grad_workspace_bytes", "loss_grad", "adam_step", "adam_step_multi", "swiglu_forward",
     "swiglu_backward", "bf16_add", "moe_route", "moe_workspace_bytes", "moe_saved_bytes", "moe_forward",
-    "moe_backward",
+    "moe_backward", "mlp_workspace_bytes", "mlp_saved_bytes", "mlp_forward", "mlp_backward",
     "lora_timing_enable", "lora_timing_reset", "lora_timing_read",
 ]
 
@@ -55,6 +55,13 @@ class MoeShape(ctypes.Structure):
                 ("gate_pack_elems", ctypes.c_int64), ("up_pack_elems", ctypes.c_int64),
                 ("down_pack_elems", ctypes.c_int64), ("n_experts", ctypes.c_int32),
                 ("top_k", ctypes.c_int32), ("n_adapters", ctypes.c_int32),
+                ("max_rank", ctypes.c_int32)]
+
+
+class MlpShape(ctypes.Structure):
+    _fields_ = [("n_tokens", ctypes.c_int64), ("hidden", ctypes.c_int64), ("d_ff", ctypes.c_int64),
+                ("gate_pack_elems", ctypes.c_int64), ("up_pack_elems", ctypes.c_int64),
+                ("down_pack_elems", ctypes.c_int64), ("n_adapters", ctypes.c_int32),
                 ("max_rank", ctypes.c_int32)]
 
 
@@ -108,6 +115,10 @@ def _load() -> ctypes.CDLL:
         "moe_saved_bytes": (_SZ, [ctypes.POINTER(MoeShape)]),
         "moe_forward": (_I32, [ctypes.POINTER(MoeShape)] + [_P] * 16 + [_SZ, _P]),
         "moe_backward": (_I32, [ctypes.POINTER(MoeShape)] + [_P] * 19 + [_I32, _P, _P, _SZ, _P]),
+        "mlp_workspace_bytes": (_SZ, [ctypes.POINTER(MlpShape)]),
+        "mlp_saved_bytes": (_SZ, [ctypes.POINTER(MlpShape)]),
+        "mlp_forward": (_I32, [ctypes.POINTER(MlpShape)] + [_P] * 14 + [_SZ, _P]),
+        "mlp_backward": (_I32, [ctypes.POINTER(MlpShape)] + [_P] * 17 + [_I32, _P, _P, _SZ, _P]),
         "swiglu_backward": (_I32, [_I64, _P, _P, _P, _P, _P, _P]),
         "lora_timing_enable": (None, [_I32]),
         "lora_timing_reset": (None, []),
@@ -308,6 +319,37 @@ def moe_backward(shape, dy, x, experts, weights, ids, W_gate_t, W_up_t, W_down_t
                             *[_ptr(p) for p in packs], *[_ptr(d) for d in descs], _ptr(saved),
                             _ptr(dx), *[_ptr(g) for g in grads], int(accumulate), _ptr(trace),
                             _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def mlp_workspace_bytes(shape: MlpShape) -> int:
+    n = LIB.mlp_workspace_bytes(ctypes.byref(shape))
+    if n == 0:
+        raise LoraError(LORA_E_INVALID_ARG, LIB.lora_last_error().decode())
+    return n
+
+
+def mlp_saved_bytes(shape: MlpShape) -> int:
+    n = LIB.mlp_saved_bytes(ctypes.byref(shape))
+    if n == 0:
+        raise LoraError(LORA_E_INVALID_ARG, LIB.lora_last_error().decode())
+    return n
+
+
+def mlp_forward(shape, x, ids, W_gate, W_up, W_down, packs, descs, y, saved, ws, stream=None):
+    """packs, descs: (gate, up, down) triples."""
+    _check(LIB.mlp_forward(ctypes.byref(shape), _ptr(x), _ptr(ids), _ptr(W_gate), _ptr(W_up),
+                           _ptr(W_down), *[_ptr(p) for p in packs], *[_ptr(d) for d in descs],
+                           _ptr(y), _ptr(saved), _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def mlp_backward(shape, dy, x, ids, W_gate_t, W_up_t, W_down_t, packs, descs, saved, dx, grads,
+                 accumulate, ws, trace=None, stream=None):
+    """packs, descs, grads: (gate, up, down) triples; trace: optional bf16 [3 * N * F]."""
+    _check(LIB.mlp_backward(ctypes.byref(shape), _ptr(dy), _ptr(x), _ptr(ids), _ptr(W_gate_t),
+                            _ptr(W_up_t), _ptr(W_down_t), *[_ptr(p) for p in packs],
+                            *[_ptr(d) for d in descs], _ptr(saved), _ptr(dx),
+                            *[_ptr(g) for g in grads], int(accumulate), _ptr(trace), _ptr(ws),
+                            _nbytes(ws), _stream(stream)))
 
 
 def swiglu_forward(gate, up, h, stream=None):
