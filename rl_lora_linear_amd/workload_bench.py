@@ -10,11 +10,9 @@ import torch
 
 from . import lib as L
 
+import workloads.device as WD
+
 PEAK_BF16_TFLOPS = 2500.0
-
-
-def _randn(gen, shape, std, dtype=torch.bfloat16):
-    return (torch.randn(shape, generator=gen, device="cuda", dtype=torch.float32) * std).to(dtype)
 
 
 def _timed(step, steps, warmup, log):
@@ -47,46 +45,23 @@ def _timer(tid):
     return tot / max(cnt, 1), cnt
 
 
-def _pack(gen, ranks, d_in, d_out):
-    """One projection's adapter pack (A_i then B_i per adapter) and its offsets."""
-    a_off, b_off, off = [], [], 0
-    for r in ranks:
-        a_off.append(off)
-        b_off.append(off + r * d_in)
-        off += r * (d_in + d_out)
-    pack = torch.empty(off, dtype=torch.bfloat16, device="cuda")
-    for i, r in enumerate(ranks):
-        pack[a_off[i]:b_off[i]] = ((torch.rand(r * d_in, generator=gen, device="cuda") * 2 - 1)
-                                   / np.sqrt(d_in)).to(torch.bfloat16)
-        pack[b_off[i]:b_off[i] + d_out * r] = _randn(gen, (d_out * r,), 0.01)
-    return pack, np.asarray(a_off), np.asarray(b_off)
-
-
 def mlp(steps, warmup, log, n=32768, d=4096, f=12288, n_ad=64):
     """SwiGLU MLP layer (mlp_forward + mlp_backward), 64 adapters with ranks from
     {8,16,32,64} on each projection, interleaved ids."""
-    gen = torch.Generator(device="cuda").manual_seed(3)
-    rng = np.random.default_rng(3)
-    ranks = rng.choice(np.asarray([8, 16, 32, 64]), size=n_ad).astype(np.int32)
-    scales = (32.0 / ranks).astype(np.float32)
-    ids = torch.from_numpy(rng.integers(0, n_ad, size=n).astype(np.int32)).cuda()
+    inp = WD.mlp_inputs(n, d, f, n_ad)
+    ranks, ids, xs, dys = inp["ranks"], inp["ids"], inp["xs"], inp["dys"]
     R = 64
-    Ws, Wts, packs, descs = [], [], [], []
-    for di, do in ((d, f), (d, f), (f, d)):          # gate, up, down
-        Wt = _randn(gen, (do, di), 0.02)
-        Wtt = torch.empty((di, do), dtype=torch.bfloat16, device="cuda")
+    Ws, packs = inp["W"], inp["packs"]
+    Wts, descs = [], []
+    for Wt, (ao, bo) in zip(Ws, inp["offs"]):
+        Wtt = torch.empty((Wt.shape[1], Wt.shape[0]), dtype=torch.bfloat16, device="cuda")
         L.lora_transpose_bf16(Wt, Wtt)
-        pack, ao, bo = _pack(gen, ranks, di, do)
-        Ws.append(Wt)
         Wts.append(Wtt)
-        packs.append(pack)
-        descs.append(L.make_desc(ao, bo, ranks, scales))
+        descs.append(L.make_desc(ao, bo, ranks, inp["scales"]))
     shape = L.MlpShape(n, d, f, packs[0].numel(), packs[1].numel(), packs[2].numel(), n_ad, R)
     ws = L.empty_workspace(L.mlp_workspace_bytes(shape))
     saved = torch.empty(L.mlp_saved_bytes(shape), dtype=torch.uint8, device="cuda")
     grads = [torch.zeros(p.numel(), dtype=torch.float32, device="cuda") for p in packs]
-    xs = [_randn(gen, (n, d), 1.0) for _ in range(2)]
-    dys = [_randn(gen, (n, d), 1.0) for _ in range(2)]
     y = torch.empty((n, d), dtype=torch.bfloat16, device="cuda")
     dx = torch.empty_like(y)
 
@@ -121,20 +96,11 @@ def mlp(steps, warmup, log, n=32768, d=4096, f=12288, n_ad=64):
 
 def logprob(steps, warmup, log, n_seq=64, seq=256, H=4096, V=151936, chunk=4096):
     """Fused lm_head logprob + PPO loss + logprob backward, 16 groups x 4 x 256."""
-    gen = torch.Generator(device="cuda").manual_seed(4)
-    n = n_seq * seq
-    hs = [_randn(gen, (n, H), 1.0) for _ in range(2)]
-    U = _randn(gen, (V, H), 0.02)
+    inp = WD.logprob_inputs(n_seq, seq, H, V)
+    n, hs, U, tg, act, adv, gen = (inp[k] for k in ("n", "hs", "U", "targets", "act", "adv", "gen"))
+    prompt = inp["prompt"]
     Ut = torch.empty((H, V), dtype=torch.bfloat16, device="cuda")
     L.lora_transpose_bf16(U, Ut)
-    tg = torch.randint(0, V, (n,), generator=gen, device="cuda", dtype=torch.int32)
-    prompt = int(0.4 * seq)
-    act = torch.zeros(n_seq, seq, device="cuda")
-    act[:, prompt:] = 1
-    act = act.reshape(-1).contiguous()
-    rew = (torch.rand(n_seq, generator=gen, device="cuda") < 0.3).float().reshape(16, 4)
-    adv = (rew - rew.mean(dim=1, keepdim=True)).reshape(n_seq, 1).expand(n_seq, seq).reshape(-1)
-    adv = (adv * act).contiguous()
     lp = torch.empty(n, device="cuda")
     lse = torch.empty(n, device="cuda")
     ws_f = L.empty_workspace(L.token_logprobs_workspace_bytes(n, V))
@@ -177,32 +143,22 @@ def logprob(steps, warmup, log, n_seq=64, seq=256, H=4096, V=151936, chunk=4096)
 def moe(steps, warmup, log, n=16384, H=2048, F=768, E=128, K=8, n_ad=8, r=32):
     """Qwen3-30B-A3B-style routed layer: top-8 of 128 experts, 8 rank-32 adapters
     on every expert's gate/up/down; route + forward + backward."""
-    gen = torch.Generator(device="cuda").manual_seed(5)
-    rng = np.random.default_rng(5)
-    logits = torch.randn((n, E), generator=gen, device="cuda")
-    ids = torch.from_numpy(rng.integers(0, n_ad, size=n).astype(np.int32)).cuda()
-    Wg, Wu = _randn(gen, (E, F, H), 0.02), _randn(gen, (E, F, H), 0.02)
-    Wd = _randn(gen, (E, H, F), 0.02)
+    inp = WD.moe_inputs(n, H, F, E, K, n_ad, r)
+    logits, ids, Wg, Wu, Wd, xs, dys = (inp[k] for k in ("logits", "ids", "Wg", "Wu", "Wd", "xs",
+                                                          "dys"))
     Wgt, Wut = (torch.empty((E, H, F), dtype=torch.bfloat16, device="cuda") for _ in range(2))
     Wdt = torch.empty((E, F, H), dtype=torch.bfloat16, device="cuda")
     for e in range(E):
         L.lora_transpose_bf16(Wg[e], Wgt[e])
         L.lora_transpose_bf16(Wu[e], Wut[e])
         L.lora_transpose_bf16(Wd[e], Wdt[e])
-    packs, descs = [], []
-    for (di, do) in ((H, F), (H, F), (F, H)):
-        per = r * (di + do)
-        pack = torch.empty(n_ad * E * per, dtype=torch.bfloat16, device="cuda")
-        pack.copy_(_randn(gen, (pack.numel(),), 0.01))
-        a_off = np.array([(a * E + e) * per for e in range(E) for a in range(n_ad)])
-        packs.append(pack)
-        descs.append(L.make_desc(a_off, a_off + r * di, np.full(a_off.size, r, np.int32),
-                                 np.full(a_off.size, 32.0 / r, np.float32)))
+    packs = inp["packs"]
+    descs = [L.make_desc(a_off, a_off + r * di, np.full(a_off.size, r, np.int32),
+                         np.full(a_off.size, 32.0 / r, np.float32))
+             for a_off, di in zip(inp["a_offs"], (H, H, F))]
     shape = L.MoeShape(n, H, F, packs[0].numel(), packs[1].numel(), packs[2].numel(), E, K, n_ad, r)
     ws = L.empty_workspace(L.moe_workspace_bytes(shape))
     saved = torch.empty(L.moe_saved_bytes(shape), dtype=torch.uint8, device="cuda")
-    xs = [_randn(gen, (n, H), 1.0) for _ in range(2)]
-    dys = [_randn(gen, (n, H), 1.0) for _ in range(2)]
     ex = torch.empty((n, K), dtype=torch.int32, device="cuda")
     w = torch.empty((n, K), device="cuda")
     y = torch.empty((n, H), dtype=torch.bfloat16, device="cuda")
