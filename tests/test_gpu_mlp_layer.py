@@ -88,3 +88,44 @@ def test_mlp_layer_equals_one_expert_moe_and_invalid_ids():
     for a, b in zip(g3, grads):
         np.testing.assert_allclose(torch.nan_to_num(a).cpu().numpy(),
                                    2 * torch.nan_to_num(b).cpu().numpy(), rtol=1e-6, atol=0)
+
+
+def test_empty_batch_moe_and_mlp():
+    """No tokens: both layers return at once, and the backward overwrites every
+    active pair's gradient region with zeros (accumulate = 0)."""
+    c = W.moe_layer(seed=44, n_tokens=64, hidden=128, d_ff=128, n_experts=3, top_k=2,
+                    n_adapters=2, rank=16)
+    dm = DevMoe(c)
+    for routed in (True, False):
+        grads = [torch.full((p.numel(),), float("nan"), dtype=torch.float32, device="cuda")
+                 for p in dm.packs]
+        empty = torch.empty((0, c.hidden), dtype=torch.bfloat16, device="cuda")
+        none = torch.empty(0, dtype=torch.int32, device="cuda")
+        if routed:
+            sh = L.MoeShape(0, c.hidden, c.d_ff, *(p.numel() for p in dm.packs), c.n_experts,
+                            c.top_k, c.n_adapters, dm.shape.max_rank)
+            ws = L.empty_workspace(L.moe_workspace_bytes(sh))
+            saved = torch.empty(L.moe_saved_bytes(sh), dtype=torch.uint8, device="cuda")
+            ex = torch.empty((0, c.top_k), dtype=torch.int32, device="cuda")
+            w = torch.empty((0, c.top_k), dtype=torch.float32, device="cuda")
+            L.moe_forward(sh, empty, ex, w, none, dm.Wg, dm.Wu, dm.Wd, dm.packs, dm.descs, empty,
+                          saved, ws)
+            L.moe_backward(sh, empty, empty, ex, w, none, dm.Wgt, dm.Wut, dm.Wdt, dm.packs,
+                           dm.descs, saved, empty, grads, 0, ws)
+        else:
+            dm1 = DevMoe(W.moe_layer(seed=45, n_tokens=64, hidden=128, d_ff=128, n_experts=1,
+                                     top_k=1, n_adapters=2, rank=16))
+            sh = L.MlpShape(0, c.hidden, c.d_ff, *(p.numel() for p in dm1.packs), 2,
+                            dm1.shape.max_rank)
+            ws = L.empty_workspace(L.mlp_workspace_bytes(sh))
+            saved = torch.empty(L.mlp_saved_bytes(sh), dtype=torch.uint8, device="cuda")
+            grads = [torch.full((p.numel(),), float("nan"), dtype=torch.float32, device="cuda")
+                     for p in dm1.packs]
+            L.mlp_forward(sh, empty, none, dm1.Wg, dm1.Wu, dm1.Wd, dm1.packs, dm1.descs, empty,
+                          saved, ws)
+            L.mlp_backward(sh, empty, empty, none, dm1.Wgt, dm1.Wut, dm1.Wdt, dm1.packs,
+                           dm1.descs, saved, empty, grads, 0, ws)
+        torch.cuda.synchronize()
+        assert L.lora_device_status(ws) == 0
+        for g in grads:
+            assert not torch.any(g != 0)          # NaN-poisoned before: all overwritten
