@@ -78,3 +78,33 @@ def test_workspace_sizes_monotone(L):
     assert L.lora_segments_workspace_bytes(0, 4) > 0 and L.lora_segments_workspace_bytes(-1, 4) == 0
     assert L.token_logprobs_backward_workspace_bytes(100, 1024, 255) == 0
     assert L.token_logprobs_backward_workspace_bytes(100, 1024, 256) >= 256 * 1024 * 2
+
+
+def test_expert_layer_size_queries_and_validation(L):
+    lib = L.LIB
+    mlp = L.MlpShape(256, 512, 1024, 1 << 16, 1 << 16, 1 << 16, 4, 16)
+    moe1 = L.MoeShape(256, 512, 1024, 1 << 16, 1 << 16, 1 << 16, 1, 1, 4, 16)
+    # The MLP layer is the one-expert layer without routing: same saved activations, no
+    # routed-copy buffers in its workspace.
+    assert L.mlp_saved_bytes(mlp) == L.moe_saved_bytes(moe1) > 0
+    assert 0 < L.mlp_workspace_bytes(mlp) <= L.moe_workspace_bytes(moe1)
+    bigger = L.MlpShape(1024, 512, 1024, 1 << 16, 1 << 16, 1 << 16, 4, 16)
+    assert L.mlp_saved_bytes(bigger) > L.mlp_saved_bytes(mlp)
+    for bad in (L.MlpShape(256, 500, 1024, 1, 1, 1, 4, 16),     # hidden not a multiple of 64
+                L.MlpShape(256, 512, 1024, 1, 1, 1, 4, 24),      # rank not a multiple of 16
+                L.MlpShape(-1, 512, 1024, 1, 1, 1, 4, 16),       # negative token count
+                L.MlpShape(256, 512, 1024, -1, 1, 1, 4, 16)):    # negative pack size
+        assert lib.mlp_workspace_bytes(ctypes.byref(bad)) == 0
+        assert lib.mlp_saved_bytes(ctypes.byref(bad)) == 0
+    for bad in (L.MoeShape(256, 512, 1024, 1, 1, 1, 8, 9, 4, 16),    # top_k > n_experts
+                L.MoeShape(256, 512, 1024, 1, 1, 1, 2048, 2, 4, 16)):  # too many experts
+        assert lib.moe_workspace_bytes(ctypes.byref(bad)) == 0
+    P = ctypes.c_void_p(16)     # never dereferenced: validation fails first
+    st = lib.moe_forward(ctypes.byref(moe1), P, None, None, P, P, P, P, P, P, P, P, P, P, P, P, P,
+                         1 << 30, None)
+    assert st == L.LORA_E_INVALID_ARG and b"experts and weights" in lib.lora_last_error()
+    st = lib.mlp_forward(ctypes.byref(mlp), P, P, P, P, P, P, P, P, P, P, P, P, P, P, 64, None)
+    assert st == L.LORA_E_WORKSPACE
+    st = lib.mlp_backward(ctypes.byref(mlp), P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P,
+                          0, None, P, 64, None)
+    assert st == L.LORA_E_WORKSPACE
