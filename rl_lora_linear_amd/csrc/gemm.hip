@@ -12,7 +12,7 @@
 // LDS by LDS-DMA into two stages of k = 64 (whole 128-byte lines per row:
 // with 64-byte rows the texture path stalled on twice the requests, and the
 // clock fell with it); all of the next stage's DMA issues in the first phase
-// of a step, one barrier per step.  LDS fragment reads run one 16-wide k
+// of a step (the first two stages in the prologue), one barrier per step.  LDS fragment reads run one 16-wide k
 // slice ahead of the MFMAs.  LDS rows are 128 B with their 16-byte chunks
 // XOR-swizzled (lds_sw) so the fragment reads of 16 consecutive rows hit
 // distinct banks.  The MFMA computes the transposed sub-tile so that each
@@ -156,7 +156,8 @@ __device__ __forceinline__ void dma16s(uint32_t voff, const void* base, uint32_t
 // The scaled vector is stored as bf16 hi and lo planes, one MFMA each, so the
 // slab keeps ~16 significant bits; M_a is bf16-exact.  tok[i] / ad[i] are the
 // token and adapter (-1: none) of this lane's fragment rows, loaded before
-// the k loop.
+// the k loop.  An adapter's MFMAs run only for the 32-row tiles holding rows
+// of it (a wave spanning two adapters pays for each about once, not twice).
 // With M_a = A_a^T (use_b_off = 0) the factor block of a 16-rank slice (16
 // rows of A_a x the wave's WN columns) is loaded row-wise into the wave's LDS
 // tile `slab` (rows padded by 16 bytes: the transposing reads of 4 rows hit
@@ -180,10 +181,13 @@ __device__ __forceinline__ void lora_slab(const GemmEpi& ep, const uint16_t* vec
   }
   const int a0 = __builtin_amdgcn_readfirstlane(lo), a1 = __builtin_amdgcn_readfirstlane(hi);
   for (int a = a0; a <= a1; ++a) {
-    bool mine = false;
+    bool tile_has[4], mine = false;   // wave-uniform: 32-row tiles holding rows of a
 #pragma unroll
-    for (int i = 0; i < 4; ++i) mine |= ad[i] == a;
-    if (!__any(mine)) continue;                     // adapter absent from this wave's rows
+    for (int i = 0; i < 4; ++i) {
+      tile_has[i] = __any(ad[i] == a);
+      mine |= tile_has[i];
+    }
+    if (!mine) continue;                            // adapter absent from this wave's rows
     const lora_adapter_desc d = desc[a];
     const int r = d.rank;
     const uint16_t* mat = lmat + (ep.use_b_off ? d.b_off : d.a_off);
@@ -232,12 +236,14 @@ __device__ __forceinline__ void lora_slab(const GemmEpi& ep, const uint16_t* vec
         }
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i) {
+        if (!tile_has[i]) continue;   // no row of adapter a in this 32-row tile
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
           acc[i][j] = mfma32(as_bf16x8(v[j]), as_bf16x8(h[i]), acc[i][j]);
           acc[i][j] = mfma32(as_bf16x8(v[j]), as_bf16x8(l[i]), acc[i][j]);
         }
+      }
     }
   }
 }
@@ -380,12 +386,24 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_nt_kernel(const uint16_t* __
     dma16s(offB[i], kb, ldsB + (uint32_t)(st * S_TILE + i * 64) * 16u);
   };
 
-  // prologue: stage 0 landed and visible to every wave
+  // prologue: stages 0 and 1 both in flight (every block starts at once, so
+  // the first loads queue behind the whole chip's); stage 0 landed and
+  // visible to every wave.  Step 0 issues no DMA: its barrier waits for
+  // stage 1.
+  static_assert(2 * DMA_PER_OP == 8, "the prologue wait counts one stage of DMA");
 #pragma unroll
   for (int i = 0; i < DMA_PER_OP; ++i) dmaA(0, i, baseA);
 #pragma unroll
   for (int i = 0; i < DMA_PER_OP; ++i) dmaB(0, i, bsrc(0));
-  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  if (KT > 1) {
+#pragma unroll
+    for (int i = 0; i < DMA_PER_OP; ++i) dmaA(1, i, baseA + SBK);
+#pragma unroll
+    for (int i = 0; i < DMA_PER_OP; ++i) dmaB(1, i, bsrc(SBK));
+    asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+  } else {
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  }
 
   const int frag_row = lane & 31;   // row within a 32-row MFMA tile
   const int frag_half = lane >> 5;  // which 8-wide k half of a 16-wide k slice
@@ -423,7 +441,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_nt_kernel(const uint16_t* __
     const uint4* Bt = sB + S * S_TILE;
     const uint4* An = sA + SN * S_TILE;
     const uint4* Bn = sB + SN * S_TILE;
-    const bool more = kt + 1 < KT;
+    const bool more = kt >= 1 && kt + 1 < KT;   // step 1 came with the prologue
     const int k0 = (more ? kt + 1 : kt) * SBK;
     const uint16_t* ka = baseA + k0;
     const uint16_t* kb = bsrc(k0);
@@ -477,7 +495,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_nt_kernel(const uint16_t* __
     if (kt < KT) step(std::integral_constant<int, 0>{}, kt);
   } else {
     for (; kt < KT; ++kt) {
-      if (kt + 1 < KT) {
+      if (kt >= 1 && kt + 1 < KT) {
         const int k0 = (kt + 1) * SBK;
         const int sn = (kt + 1) & 1;
 #pragma unroll

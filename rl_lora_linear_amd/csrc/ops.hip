@@ -10,22 +10,55 @@ constexpr float kLog2eF = 1.4426950408889634f;
 constexpr float kLn2F = 0.6931471805599453f;
 
 // ------------------------------------------------------------------ logsumexp merge
-// One thread per token: merge the per-vocab-tile (max, sum) pairs in tile order
-// (TPU RL note, section 10 item 3: lse = m + log sum exp(z - m)), then
-// logprob = z[target] - lse.  Out-of-range targets give NaN and a status flag.
-__global__ __launch_bounds__(256) void logprob_merge_kernel(
+// Merge of the per-vocab-tile (max, sum) pairs (TPU RL note, section 10 item 3:
+// lse = m + log sum exp(z - m)), then logprob = z[target] - lse.  Out-of-range
+// targets give NaN and a status flag.
+// A block owns 64 tokens (one per lane, so every load is 256 contiguous bytes)
+// and its 16 waves split the vocab tiles: wave w folds tiles w, w + 16, ... in
+// that order with the running rescale m' = max(m, m_i), s' = s e^(m - m') +
+// s_i e^(m_i - m'), eight tiles' loads in flight at a time; the 16 wave results
+// are folded the same way in wave order.  (One thread per token over all the
+// tiles left the chip nearly idle: 64 blocks for 16384 tokens.)
+constexpr int MERGE_WAVES = 16;
+constexpr int MERGE_BATCH = 8;
+
+__device__ __forceinline__ void lse_fold(float& mx, float& s, float m, float si) {
+  if (m > mx) {
+    s = s * exp2f((mx - m) * kLog2eF) + si;   // mx = -inf: s is still 0
+    mx = m;
+  } else if (m != -INFINITY) {
+    s += si * exp2f((m - mx) * kLog2eF);
+  }
+}
+
+__global__ __launch_bounds__(64 * MERGE_WAVES) void logprob_merge_kernel(
     const float* __restrict__ part_m, const float* __restrict__ part_s,
     const float* __restrict__ zt, const int32_t* __restrict__ targets, int64_t n, int tiles,
     int64_t vocab, float* __restrict__ logprobs, float* __restrict__ lse, int32_t* status) {
-  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= n) return;
-  float mx = -INFINITY;
-  for (int i = 0; i < tiles; ++i) mx = fmaxf(mx, part_m[(int64_t)i * n + t]);
-  float s = 0.f;
-  for (int i = 0; i < tiles; ++i) {
-    const float m = part_m[(int64_t)i * n + t];
-    if (m != -INFINITY) s += part_s[(int64_t)i * n + t] * exp2f((m - mx) * kLog2eF);
+  __shared__ float s_m[MERGE_WAVES][64], s_s[MERGE_WAVES][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t t = (int64_t)blockIdx.x * 64 + lane;
+  float mx = -INFINITY, s = 0.f;
+  if (t < n) {
+    for (int i0 = w; i0 < tiles; i0 += MERGE_BATCH * MERGE_WAVES) {
+      float mm[MERGE_BATCH], ss[MERGE_BATCH];
+#pragma unroll
+      for (int u = 0; u < MERGE_BATCH; ++u) {
+        const int i = i0 + u * MERGE_WAVES;
+        mm[u] = i < tiles ? part_m[(int64_t)i * n + t] : -INFINITY;
+        ss[u] = i < tiles ? part_s[(int64_t)i * n + t] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < MERGE_BATCH; ++u) lse_fold(mx, s, mm[u], ss[u]);
+    }
   }
+  s_m[w][lane] = mx;
+  s_s[w][lane] = s;
+  __syncthreads();
+  if (w != 0 || t >= n) return;
+  mx = -INFINITY;
+  s = 0.f;
+  for (int v = 0; v < MERGE_WAVES; ++v) lse_fold(mx, s, s_m[v][lane], s_s[v][lane]);
   const float l = mx + log2f(s) * kLn2F;
   lse[t] = l;
   const int32_t y = targets[t];
@@ -328,8 +361,8 @@ lora_status launch_logprob_merge(const float* part_m, const float* part_s, const
                                  const int32_t* targets, int64_t n, int tiles, int64_t vocab,
                                  float* logprobs, float* lse, int32_t* status, hipStream_t s) {
   if (n <= 0) return LORA_OK;
-  hipLaunchKernelGGL(logprob_merge_kernel, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, s, part_m,
-                     part_s, zt, targets, n, tiles, vocab, logprobs, lse, status);
+  hipLaunchKernelGGL(logprob_merge_kernel, dim3((unsigned)cdiv(n, 64)), dim3(64 * MERGE_WAVES), 0,
+                     s, part_m, part_s, zt, targets, n, tiles, vocab, logprobs, lse, status);
   return launch_check("logprob_merge");
 }
 

@@ -249,6 +249,35 @@ __global__ __launch_bounds__(1024) void seg_small_kernel(
       const int t = r * 1024 + tid;
       v[r] = t < n ? ids[t] : 0;
     }
+    // per key: descriptor validation, its loads issued behind the id loads so
+    // that both latencies overlap
+    for (int k = tid; k <= n_keys; k += 1024) {
+      lora_adapter_desc d[3];
+#pragma unroll
+      for (int i = 0; i < 3; ++i)
+        if (k < n_keys && i < tabs.n_tabs) d[i] = tabs.tab[i].desc[k];
+      bool on = true;
+      if (k < n_keys && tabs.n_tabs > 0) {
+#pragma unroll
+        for (int i = 0; i < 3; ++i) {
+          if (i >= tabs.n_tabs) break;
+          const lora_host::SegDescs& tb = tabs.tab[i];
+          const int64_t rk = d[i].rank;
+          if (rk == 0) {
+            on = false;
+            continue;
+          }
+          const bool ok = rk >= 8 && rk <= 64 && (rk % 8) == 0 && rk <= max_rank &&
+                          d[i].a_off >= 0 && d[i].b_off >= 0 && (d[i].a_off % 8) == 0 &&
+                          (d[i].b_off % 8) == 0 && d[i].a_off + rk * tb.d_in <= tb.a_elems &&
+                          d[i].b_off + tb.d_out * rk <= tb.b_elems;
+          if (!ok) set_flag(status, LORA_FLAG_BAD_DESC);
+          on = on && ok;
+        }
+        active[k] = on ? 1 : 0;
+      }
+      s_act[k] = on ? 1 : 0;
+    }
 #pragma unroll
     for (int r = 0; r < SEG_SMALL_N / 1024; ++r)
       if (r * 1024 + tid < n) s_ids[r * 1024 + tid] = v[r];
@@ -288,29 +317,6 @@ __global__ __launch_bounds__(1024) void seg_small_kernel(
       base += __shfl(x, 63);
     }
     if (lane == 0) s_off[k] = base;
-  }
-  __syncthreads();
-  // per key: validation
-  for (int k = tid; k <= n_keys; k += 1024) {
-    bool on = true;
-    if (k < n_keys && tabs.n_tabs > 0) {
-      for (int i = 0; i < tabs.n_tabs; ++i) {
-        const lora_host::SegDescs& tb = tabs.tab[i];
-        const lora_adapter_desc d = tb.desc[k];
-        const int64_t rk = d.rank;
-        if (rk == 0) {
-          on = false;
-          continue;
-        }
-        const bool ok = rk >= 8 && rk <= 64 && (rk % 8) == 0 && rk <= max_rank && d.a_off >= 0 &&
-                        d.b_off >= 0 && (d.a_off % 8) == 0 && (d.b_off % 8) == 0 &&
-                        d.a_off + rk * tb.d_in <= tb.a_elems && d.b_off + tb.d_out * rk <= tb.b_elems;
-        if (!ok) set_flag(status, LORA_FLAG_BAD_DESC);
-        on = on && ok;
-      }
-      active[k] = on ? 1 : 0;
-    }
-    s_act[k] = on ? 1 : 0;
   }
   __syncthreads();
   // exclusive scan over keys: offsets and the tile prefix arrays

@@ -71,10 +71,16 @@ def _case(kind):
     if kind == "big_chunks":  # an adapter with > 1024 tokens (several gradient chunks)
         ids = W.sorted_ids_from_lengths([2500, 700])
         return W.lora_layer(23, 3200, 256, 320, [32, 16], [32.0, 16.0], ids=ids)
+    if kind == "many":        # 130 one-token adapters, then three more: a tile half with more
+        # distinct adapters than the epilogue's tables hold, and factor blocks over several rounds
+        lengths = [1] * 130 + [40, 0, 90]
+        ids = W.sorted_ids_from_lengths(lengths)
+        ranks = [[64, 8, 32, 64, 16, 48][i % 6] for i in range(len(lengths))]
+        return W.lora_layer(24, len(ids), 192, 320, ranks, [float(r) for r in ranks], ids=ids)
     raise KeyError(kind)
 
 
-CASES = ["tiny", "ragged", "multi", "big_chunks"]
+CASES = ["tiny", "ragged", "multi", "big_chunks", "many"]
 
 
 @pytest.mark.parametrize("kind", CASES)
