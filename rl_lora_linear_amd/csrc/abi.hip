@@ -91,7 +91,8 @@ struct LayerWs {
   int32_t* prec;
   uint16_t* v;        // scaled v = s_a B_a^T dy as bf16 hi/lo planes [2][N][max_rank]
   uint16_t* zero;     // 256 zero bytes (source of the rows past a gradient chunk)
-  float* partial;
+  float* partial;     // dB chunk partials
+  float* partial_a;   // dA chunk partials
   size_t total;
 };
 
@@ -108,8 +109,11 @@ LayerWs carve_layer(const lora_shape& sh, void* ws, size_t bytes) {
   w.prec = cv.take<int32_t>((size_t)sh.n_adapters + 1);
   w.v = cv.take<uint16_t>((size_t)2 * std::max<int64_t>(sh.n_tokens, 1) * sh.max_rank);
   w.zero = cv.take<uint16_t>(128);
-  w.partial = cv.take<float>((size_t)grad_partial_floats(sh.n_tokens, sh.n_adapters,
-                                                         std::max(sh.d_in, sh.d_out), sh.max_rank));
+  // chunk partials of dB and of dA (reduced in one launch, so apart)
+  w.partial = cv.take<float>((size_t)grad_partial_floats(sh.n_tokens, sh.n_adapters, sh.d_out,
+                                                         sh.max_rank));
+  w.partial_a = cv.take<float>((size_t)grad_partial_floats(sh.n_tokens, sh.n_adapters, sh.d_in,
+                                                           sh.max_rank));
   w.total = cv.used;
   return w;
 }
@@ -313,11 +317,10 @@ lora_status lora_backward(const lora_shape* shape, const uint16_t* dy, const uin
     timer_end(LORA_TIMER_BASE_GEMM, s);
   }
   timer_begin(LORA_TIMER_GRAD, s);
-  TRY(launch_grad(0, u_saved, sh.max_rank, w.zero, dy, sh.d_out, (int)sh.d_out, desc, w.active,
-                  w.perm, 0, w.offsets, w.prec, sh.n_adapters, sh.n_tokens, dB_pack, w.partial,
-                  accumulate, s));
-  TRY(launch_grad(1, w.v, sh.max_rank, w.zero, x, sh.d_in, (int)sh.d_in, desc, w.active, w.perm, 0,
-                  w.offsets, w.prec, sh.n_adapters, sh.n_tokens, dA_pack, w.partial, accumulate, s));
+  // dB = s sum dy u^T and dA = s sum v x^T over each adapter's tokens, one launch
+  TRY(launch_grad_pair(u_saved, dy, sh.d_out, (int)sh.d_out, dB_pack, w.partial, w.v, x, sh.d_in,
+                       (int)sh.d_in, dA_pack, w.partial_a, sh.max_rank, w.zero, desc, w.active,
+                       w.perm, w.offsets, w.prec, sh.n_adapters, sh.n_tokens, accumulate, s));
   timer_end(LORA_TIMER_GRAD, s);
   return LORA_OK;
 }

@@ -19,6 +19,8 @@
 //            K(=token)-contiguous; P (fp32) is split hi+lo.  Adapters with one
 //            chunk write the result directly, others write chunk partials that
 //            `grad_finalize` sums in chunk order (deterministic, no atomics).
+#include <type_traits>
+
 #include "common.hpp"
 #include "sgmv.hpp"
 
@@ -603,15 +605,54 @@ __global__ __launch_bounds__(256) void grad_kernel(
   }
 }
 
+// One reduction of a paired launch (both over the same segments).
+struct GradSide {
+  const uint16_t* P;
+  const uint16_t* Q;
+  int64_t ld_q;
+  int D;
+  const lora_adapter_desc* desc;
+  float* out_pack;
+  float* partial;
+};
+
+// dB (mode 0) and dA (mode 1) of one layer in one launch: items of the first
+// side, then of the second, spread XCD-contiguously as in grad_kernel.  Both
+// sides share the segments, the plane stride and the rank bound.
+template <int PN>
+__global__ __launch_bounds__(256) void grad_pair_kernel(
+    GradSide s0, GradSide s1, int64_t plane, int r_max, const uint16_t* __restrict__ zero,
+    const int32_t* __restrict__ q_rows, int p_ident, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ chunk_pre, int n_ad, int accumulate) {
+  extern __shared__ uint4 gr_lds[];
+  __shared__ int32_t tok_s[GR_TC];
+  const int nc0 = (s0.D + GR_NJ - 1) / GR_NJ, nc1 = (s1.D + GR_NJ - 1) / GR_NJ;
+  const int n0 = chunk_pre[n_ad] * nc0;
+  const ItemRange ir = xcd_items(n0 + chunk_pre[n_ad] * nc1);
+  const GradDual none{nullptr, nullptr, 0};
+  for (int item = ir.first; item < ir.end; item += ir.step) {
+    if (item < n0) {
+      const int slot = item / nc0;
+      grad_item<0, PN>(s0.P, plane, r_max, zero, s0.Q, s0.ld_q, s0.D, s0.desc, q_rows, p_ident,
+                       offsets, chunk_pre, n_ad, s0.out_pack, s0.partial, accumulate, slot,
+                       (item - slot * nc0) * GR_NJ, tok_s, gr_lds, none);
+    } else {
+      const int it = item - n0, slot = it / nc1;
+      grad_item<1, PN>(s1.P, plane, r_max, zero, s1.Q, s1.ld_q, s1.D, s1.desc, q_rows, p_ident,
+                       offsets, chunk_pre, n_ad, s1.out_pack, s1.partial, accumulate, slot,
+                       (it - slot * nc1) * GR_NJ, tok_s, gr_lds, none);
+    }
+  }
+}
+
 // grid = (n_ad, blocks over D*r_max/1024).  Sums the chunk partials of
 // adapters with several chunks, in chunk order; with accumulate == 0 writes
 // zeros for active adapters that own no token.
-__global__ __launch_bounds__(256) void grad_finalize_kernel(
-    const lora_adapter_desc* __restrict__ desc, const uint8_t* __restrict__ active,
+__device__ __forceinline__ void grad_finalize_body(
+    int a, const lora_adapter_desc* __restrict__ desc, const uint8_t* __restrict__ active,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ chunk_pre, int D,
     int64_t slot_floats, int mode, float* __restrict__ out_pack, const float* __restrict__ partial,
     int accumulate) {
-  const int a = blockIdx.x;
   if (!active[a]) return;
   const int count = offsets[a + 1] - offsets[a];
   const int s0 = chunk_pre[a], ns = chunk_pre[a + 1] - s0;
@@ -635,6 +676,30 @@ __global__ __launch_bounds__(256) void grad_finalize_kernel(
     }
     *(float4*)(dst + e) = v;
   }
+}
+
+__global__ __launch_bounds__(256) void grad_finalize_kernel(
+    const lora_adapter_desc* __restrict__ desc, const uint8_t* __restrict__ active,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ chunk_pre, int D,
+    int64_t slot_floats, int mode, float* __restrict__ out_pack, const float* __restrict__ partial,
+    int accumulate) {
+  grad_finalize_body(blockIdx.x, desc, active, offsets, chunk_pre, D, slot_floats, mode, out_pack,
+                     partial, accumulate);
+}
+
+// Both sides of a paired launch: blocks x < n_ad finalize side 0 (mode 0),
+// the rest side 1 (mode 1).
+__global__ __launch_bounds__(256) void grad_finalize_pair_kernel(
+    GradSide s0, GradSide s1, const uint8_t* __restrict__ active,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ chunk_pre, int n_ad,
+    int r_max, int accumulate) {
+  const int a = blockIdx.x;
+  if (a < n_ad)
+    grad_finalize_body(a, s0.desc, active, offsets, chunk_pre, s0.D, (int64_t)s0.D * r_max, 0,
+                       s0.out_pack, s0.partial, accumulate);
+  else
+    grad_finalize_body(a - n_ad, s1.desc, active, offsets, chunk_pre, s1.D,
+                       (int64_t)s1.D * r_max, 1, s1.out_pack, s1.partial, accumulate);
 }
 
 }  // namespace lora
@@ -742,6 +807,43 @@ lora_status launch_grad(int mode, const uint16_t* P, int r_max, const void* zero
   hipLaunchKernelGGL(grad_finalize_kernel, dim3(n_ad, gy), dim3(256), 0, s, desc2, active, offsets,
                      chunk_pre, D, slot, mode, out2, partial + (int64_t)r_max * D, accumulate);
   return launch_check("grad_finalize");
+}
+
+lora_status launch_grad_pair(const uint16_t* u, const uint16_t* dy, int64_t ld_dy, int d_out,
+                             float* dB_pack, float* partial_b, const uint16_t* v,
+                             const uint16_t* x, int64_t ld_x, int d_in, float* dA_pack,
+                             float* partial_a, int r_max, const void* zero,
+                             const lora_adapter_desc* desc, const uint8_t* active,
+                             const int32_t* q_rows, const int32_t* offsets,
+                             const int32_t* chunk_pre, int n_ad, int64_t n_tokens, int accumulate,
+                             hipStream_t s) {
+  const GradSide s0{u, dy, ld_dy, d_out, desc, dB_pack, partial_b};
+  const GradSide s1{v, x, ld_x, d_in, desc, dA_pack, partial_a};
+  if (n_tokens > 0) {
+    const int64_t plane = n_tokens * r_max;
+    const uint16_t* z = (const uint16_t*)zero;
+    auto go = [&](auto pn) -> lora_status {
+      constexpr int PN = decltype(pn)::value;
+      const size_t lds = (size_t)GrP<PN>::NST * GrP<PN>::STAGE * sizeof(uint4);
+      static bool attr = false;
+      if (!attr) {
+        TRY_HIP(hipFuncSetAttribute((const void*)grad_pair_kernel<PN>,
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
+        attr = true;
+      }
+      hipLaunchKernelGGL(grad_pair_kernel<PN>, dim3(persistent_blocks()), dim3(256), lds, s, s0,
+                         s1, plane, r_max, z, q_rows, 0, offsets, chunk_pre, n_ad, accumulate);
+      return launch_check("grad_pair");
+    };
+    const lora_status st =
+        r_max <= 32 ? go(std::integral_constant<int, 1>{}) : go(std::integral_constant<int, 2>{});
+    if (st) return st;
+  }
+  const unsigned gy = (unsigned)std::max<int64_t>(
+      1, std::min<int64_t>(64, cdiv((int64_t)std::max(d_in, d_out) * r_max, 1024)));
+  hipLaunchKernelGGL(grad_finalize_pair_kernel, dim3(2 * n_ad, gy), dim3(256), 0, s, s0, s1,
+                     active, offsets, chunk_pre, n_ad, r_max, accumulate);
+  return launch_check("grad_finalize_pair");
 }
 
 int64_t grad_partial_floats(int64_t n_tokens, int n_ad, int64_t D, int r_max) {

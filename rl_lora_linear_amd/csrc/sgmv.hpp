@@ -95,6 +95,17 @@ lora_status launch_grad(int mode, const uint16_t* P, int r_max, const void* zero
 // with desc2 gives the second table's T into out2 in the same pass over Q;
 // the partial buffer then needs grad_partial_floats(.., 2 * r_max).
 int64_t grad_partial_floats(int64_t n_tokens, int n_ad, int64_t D, int r_max);
+// dB (mode 0 over u and dy, [d_out][r] at b_off) and dA (mode 1 over v and x,
+// [r][d_in] at a_off) of one layer in one launch, and one finalize launch;
+// each side takes its own partial buffer of grad_partial_floats(.., its D, r_max).
+lora_status launch_grad_pair(const uint16_t* u, const uint16_t* dy, int64_t ld_dy, int d_out,
+                             float* dB_pack, float* partial_b, const uint16_t* v,
+                             const uint16_t* x, int64_t ld_x, int d_in, float* dA_pack,
+                             float* partial_a, int r_max, const void* zero,
+                             const lora_adapter_desc* desc, const uint8_t* active,
+                             const int32_t* q_rows, const int32_t* offsets,
+                             const int32_t* chunk_pre, int n_ad, int64_t n_tokens, int accumulate,
+                             hipStream_t s);
 
 
 constexpr int kGradChunk = 1024;  // tokens per gradient chunk (matches the kernel)
