@@ -78,7 +78,8 @@ static inline hipStream_t S(void* p) { return (hipStream_t)p; }
 // ------------------------------------------------------------------ layer workspace
 namespace {
 
-constexpr int kTmShrink = 32;   // rows per shrink tile (matches the kernel)
+constexpr int kTmShrink = 32;       // rows per shrink tile (matches the kernel)
+constexpr int kTmShrinkTall = 128;  // rows per tall shrink tile (large batches)
 
 struct LayerWs {
   char* seg;          // status word + segment scratch
@@ -88,6 +89,7 @@ struct LayerWs {
   int32_t* offsets;
   uint8_t* active;
   int32_t* pre32;
+  int32_t* pre128;
   int32_t* prec;
   uint16_t* v;        // scaled v = s_a B_a^T dy as bf16 hi/lo planes [2][N][max_rank]
   uint16_t* zero;     // 256 zero bytes (source of the rows past a gradient chunk)
@@ -106,6 +108,7 @@ LayerWs carve_layer(const lora_shape& sh, void* ws, size_t bytes) {
   w.offsets = cv.take<int32_t>((size_t)sh.n_adapters + 1);
   w.active = cv.take<uint8_t>((size_t)sh.n_adapters);
   w.pre32 = cv.take<int32_t>((size_t)sh.n_adapters + 1);
+  w.pre128 = cv.take<int32_t>((size_t)sh.n_adapters + 1);
   w.prec = cv.take<int32_t>((size_t)sh.n_adapters + 1);
   w.v = cv.take<uint16_t>((size_t)2 * std::max<int64_t>(sh.n_tokens, 1) * sh.max_rank);
   w.zero = cv.take<uint16_t>(128);
@@ -150,8 +153,8 @@ lora_status layer_segments(const lora_shape& sh, const lora_adapter_desc* desc,
   ex.active = w.active;
   ex.tm[0] = kTmShrink;
   ex.pre[0] = w.pre32;
-  ex.tm[1] = 1;
-  ex.pre[1] = nullptr;
+  ex.tm[1] = kTmShrinkTall;
+  ex.pre[1] = w.pre128;
   ex.tm[2] = kGradChunk;
   ex.pre[2] = w.prec;
   ex.adpos = w.adpos;
@@ -249,7 +252,7 @@ lora_status lora_forward(const lora_shape* shape, const uint16_t* x, const uint1
   timer_begin(LORA_TIMER_SHRINK, s);
   TRY(launch_shrink(x, sh.d_in, (int)sh.d_in, A_pack, 0, desc, w.adpos, w.perm, w.perm, nullptr,
                     w.offsets, w.pre32, sh.n_adapters, sh.n_tokens, u_saved, sh.max_rank, w.zero,
-                    s));
+                    s, nullptr, nullptr, nullptr, w.pre128));
   timer_end(LORA_TIMER_SHRINK, s);
   // base GEMM over rows in segment order with the expand y += B_a (s u) fused
   GemmRows f;
@@ -297,7 +300,7 @@ lora_status lora_backward(const lora_shape* shape, const uint16_t* dy, const uin
     timer_begin(LORA_TIMER_SHRINK, s);
     TRY(launch_shrink(dy, sh.d_out, (int)sh.d_out, B_pack, 1, desc, w.adpos, w.perm, w.perm,
                       nullptr, w.offsets, w.pre32, sh.n_adapters, sh.n_tokens, w.v, sh.max_rank,
-                      w.zero, s));
+                      w.zero, s, nullptr, nullptr, nullptr, w.pre128));
     timer_end(LORA_TIMER_SHRINK, s);
     // dX = dY W over rows in segment order with the expand dX += A_a^T (s v) fused
     GemmRows f;
@@ -552,6 +555,7 @@ struct MoeWs {
   int32_t* offsets;  // [n_keys + 1]
   uint8_t* active;   // [n_keys]
   int32_t* pre32;
+  int32_t* pre128;
   int32_t* prec;
   int32_t* gpre;     // [E + 1]
   lora_adapter_desc* desc[3];  // per-key tables (gate, up, down) with "no adapter" entries
@@ -603,6 +607,7 @@ MoeWs carve_moe(const moe_shape& sh, void* ws, size_t bytes, bool backward, bool
   w.offsets = cv.take<int32_t>((size_t)n_keys + 1);
   w.active = cv.take<uint8_t>((size_t)n_keys);
   w.pre32 = cv.take<int32_t>((size_t)n_keys + 1);
+  w.pre128 = cv.take<int32_t>((size_t)n_keys + 1);
   w.prec = cv.take<int32_t>((size_t)n_keys + 1);
   w.gpre = cv.take<int32_t>((size_t)sh.n_experts + 1);
   for (int i = 0; i < 3; ++i) w.desc[i] = cv.take<lora_adapter_desc>((size_t)n_keys);
@@ -641,8 +646,8 @@ lora_status moe_segments(const moe_shape& sh, const int32_t* experts, const int3
   ex.active = w.active;
   ex.tm[0] = kTmShrink;
   ex.pre[0] = w.pre32;
-  ex.tm[1] = 1;
-  ex.pre[1] = nullptr;
+  ex.tm[1] = kTmShrinkTall;
+  ex.pre[1] = w.pre128;
   ex.tm[2] = kGradChunk;
   ex.pre[2] = w.prec;
   ex.adpos = w.adpos;
@@ -792,12 +797,14 @@ lora_status expert_forward(const moe_shape& sh, const uint16_t* x, const int32_t
   if (R <= 32) {
     TRY(launch_shrink(x, H, (int)H, gate_pack, 0, w.desc[0], w.adpos, w.tokrow, nullptr, nullptr,
                       w.offsets, w.pre32, n_keys, NK, sv.su[0], R, w.zero, s, up_pack, w.desc[1],
-                      sv.su[1]));
+                      sv.su[1], w.pre128));
   } else {
     TRY(launch_shrink(x, H, (int)H, gate_pack, 0, w.desc[0], w.adpos, w.tokrow, nullptr, nullptr,
-                      w.offsets, w.pre32, n_keys, NK, sv.su[0], R, w.zero, s));
+                      w.offsets, w.pre32, n_keys, NK, sv.su[0], R, w.zero, s, nullptr, nullptr,
+                      nullptr, w.pre128));
     TRY(launch_shrink(x, H, (int)H, up_pack, 0, w.desc[1], w.adpos, w.tokrow, nullptr, nullptr,
-                      w.offsets, w.pre32, n_keys, NK, sv.su[1], R, w.zero, s));
+                      w.offsets, w.pre32, n_keys, NK, sv.su[1], R, w.zero, s, nullptr, nullptr,
+                      nullptr, w.pre128));
   }
   MoePair gu;
   gu.split = 3;
@@ -809,7 +816,8 @@ lora_status expert_forward(const moe_shape& sh, const uint16_t* x, const int32_t
   TRY(moe_project(sh, w, x, w.tokrow, sh.n_tokens, W_gate, F, H, sv.su[0], gate_pack, 1,
                   w.desc[0], nullptr, sv.gu, s, gu));
   TRY(launch_shrink(sv.h, F, (int)F, down_pack, 0, w.desc[2], w.adpos, nullptr, nullptr, nullptr,
-                    w.offsets, w.pre32, n_keys, NK, sv.su[2], R, w.zero, s));
+                    w.offsets, w.pre32, n_keys, NK, sv.su[2], R, w.zero, s, nullptr, nullptr,
+                    nullptr, w.pre128));
   if (!routed)   // down straight to the token rows
     return moe_project(sh, w, sv.h, nullptr, NK, W_down, H, F, sv.su[2], down_pack, 1, w.desc[2],
                        nullptr, y, s, MoePair{}, w.tokrow);
@@ -864,7 +872,7 @@ lora_status expert_backward(const moe_shape& sh, const uint16_t* dy, const uint1
     if (routed) TRY(launch_moe_gather_w(weights, w.perm, NK, w.wpos, s));
     TRY(launch_shrink(dy, H, (int)H, down_pack, 1, w.desc[2], w.adpos, w.tokrow, nullptr,
                       routed ? w.wpos : nullptr, w.offsets, w.pre32, n_keys, NK, w.v[2], R,
-                      w.zero, s));
+                      w.zero, s, nullptr, nullptr, nullptr, w.pre128));
     // dh = w (dy_t W_down) + A^T v, turned into [dgate | dup] in the epilogue
     MoePair dg;
     dg.split = 4;
@@ -884,7 +892,8 @@ lora_status expert_backward(const moe_shape& sh, const uint16_t* dy, const uint1
     // (one K-concatenated GEMM) + A_gate^T v_gate + A_up^T v_up
     for (int i = 0; i < 2; ++i)
       TRY(launch_shrink(w.dgu + i * F, 2 * F, (int)F, packs[i], 1, w.desc[i], w.adpos, nullptr,
-                        nullptr, nullptr, w.offsets, w.pre32, n_keys, NK, w.v[i], R, w.zero, s));
+                        nullptr, nullptr, w.offsets, w.pre32, n_keys, NK, w.v[i], R, w.zero, s,
+                        nullptr, nullptr, nullptr, w.pre128));
     MoePair gu;
     gu.split = 2;
     gu.W2 = W_up_t;

@@ -272,9 +272,178 @@ __device__ __forceinline__ void shrink_tile(const uint16_t* __restrict__ in, int
   if (!KM && sec.mat) emit(sec.out, sec.c2, sec.r, sec.scale);
 }
 
-// One block per CU.  Blocks take the 32-row adapter tiles (pre32[n_ad] of
-// them) XCD-contiguously, then zero, grid-stride, the rows of tokens that
-// belong to no active adapter (adpos == -1), and block 0 clears `zero`.
+// The same product for large batches over 128-row adapter tiles: each factor
+// row then streams once per 128 rows instead of once per 32 (in the 32-row
+// kernel the factor is half of each CU's traffic).  Stages of k = 64, one
+// 128-byte line per row; wave w owns rows 32w .. 32w + 31 of the tile over
+// every k of a stage, so the partial products need no cross-wave sum.  LDS
+// rows are 128 B with 16-byte chunk c stored at c ^ ((row >> 1) & 7): the
+// fragment reads of 16 consecutive rows hit distinct banks.  The factor tile of
+// a stage holds FB = 2 (ranks <= 32) or 4 rank blocks of 16 (rows clamped to
+// the last rank; KM: a flat copy of the k slice, clamped to the factor's end),
+// so every wave issues the same DMA count.
+constexpr int ST_TM = 128;
+constexpr int ST_KC = 64;
+constexpr int ST_NST = 5;
+constexpr int ST_XSLOTS = ST_TM * 8;   // uint4 slots of the row tile per stage (16 KB)
+__device__ __forceinline__ int st_sw(int row) { return (row >> 1) & 7; }
+template <int NB> constexpr int st_fb() { return NB <= 2 ? 2 : 4; }
+
+template <int NB, bool KM>
+__device__ __forceinline__ void shrink_tall_tile(const uint16_t* __restrict__ in, int64_t ld_in,
+                                                 int K, const uint16_t* __restrict__ mat, int r,
+                                                 float scale, const ShrinkSecond sec,
+                                                 const ShrinkRows rm, int p0, int rows, uint4* lds,
+                                                 uint16_t* __restrict__ out, int64_t plane,
+                                                 int r_max) {
+  constexpr int FB = st_fb<NB>();
+  constexpr int MSLOTS = FB * 16 * 8;              // factor tile slots per stage
+  constexpr int STAGE = ST_XSLOTS + MSLOTS;
+  constexpr int PER_WAVE = 4 + FB / 2;             // DMA instructions per wave per stage
+  constexpr int NST = ST_NST;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int KT = K / ST_KC;
+
+  // DMA sources of this lane: 4 row instructions (this wave's 32 rows, 8 per
+  // instruction: lane L -> row L / 8, physical chunk L % 8), FB / 2 factor ones
+  const uint16_t* xsrc[4];
+  int xchunk[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = wave * 32 + i * 8 + (lane >> 3);
+    const int pr = p0 + (row < rows ? row : 0);
+    const int t = rm.in ? rm.in[pr] : pr;
+    xchunk[i] = (lane & 7) ^ st_sw(row);
+    xsrc[i] = in + (int64_t)t * ld_in;
+  }
+  const uint16_t* msrc[FB / 2];
+  int mchunk[FB / 2];
+#pragma unroll
+  for (int i = 0; i < FB / 2; ++i) {
+    const int ins = wave * (FB / 2) + i;             // factor instruction of the stage
+    if constexpr (KM) {
+      msrc[i] = mat;
+      mchunk[i] = (ins * 64 + lane) * 8;             // element offset within the k slice
+    } else {
+      const int c = ins * 8 + (lane >> 3);           // rank row
+      mchunk[i] = (lane & 7) ^ st_sw(c);
+      if (sec.mat && c >= sec.c2) {
+        const int c2 = c - sec.c2;
+        msrc[i] = sec.mat + (int64_t)(c2 < sec.r ? c2 : sec.r - 1) * K;
+      } else {
+        msrc[i] = mat + (int64_t)(c < r ? c : r - 1) * K;
+      }
+    }
+  }
+  const int64_t m_last = (int64_t)K * r - 8;   // KM: last 16-byte source of the factor
+  auto issue = [&](int st, int kt) {
+    const int k0 = kt * ST_KC;
+    uint4* base = lds + st * STAGE;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      dma16(xsrc[i] + k0 + xchunk[i] * 8,
+            __builtin_amdgcn_readfirstlane(lds_u32(base + (wave * 4 + i) * 64)));
+#pragma unroll
+    for (int i = 0; i < FB / 2; ++i) {
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(
+          lds_u32(base + ST_XSLOTS + (wave * (FB / 2) + i) * 64));
+      if constexpr (KM)
+        dma16(msrc[i] + min((int64_t)k0 * r + mchunk[i], m_last), dst);
+      else
+        dma16(msrc[i] + k0 + mchunk[i] * 8, dst);
+    }
+  };
+
+#pragma unroll
+  for (int st = 0; st < NST - 1; ++st) issue(st, min(st, KT - 1));
+  wait_vm_barrier<(NST - 2) * PER_WAVE>();
+
+  f32x4 acc[2][NB];
+#pragma unroll
+  for (int g = 0; g < 2; ++g)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[g][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int fr = lane & 15;
+  const int q = (lane >> 2) & 3, j = lane & 3;
+
+  for (int kt = 0; kt < KT; ++kt) {
+    const int st = kt % NST;
+    issue((kt + NST - 1) % NST, min(kt + NST - 1, KT - 1));
+    const uint4* xt = lds + st * STAGE;
+    const uint4* mt = xt + ST_XSLOTS;
+#pragma unroll
+    for (int sl = 0; sl < ST_KC / 32; ++sl) {
+      const int ch = 4 * sl + (lane >> 4);   // logical chunk of this lane's fragments
+      bf16x8 xa[2], mb[NB];
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const int row = wave * 32 + g * 16 + fr;
+        xa[g] = as_bf16x8(xt[row * 8 + (ch ^ st_sw(row))]);
+      }
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        if constexpr (KM) {
+          // rows k = 8 ch + {0..3} and {4..7} of the flat [64][r] slice; in
+          // each 16-lane group, lane 4q + j addresses row 8 ch + q, ranks
+          // 16 b + 4 j .. + 3, and receives rank 16 b + (lane & 15)
+          const uint32_t off = (uint32_t)(((8 * ch + q) * r + 16 * b + 4 * j) * 2);
+          const uint2 lo = tr_read(mt, off);
+          const uint2 hi = tr_read(mt, off + (uint32_t)(4 * r * 2));
+          mb[b] = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+        } else {
+          const int c = b * 16 + fr;
+          mb[b] = as_bf16x8(mt[c * 8 + (ch ^ st_sw(c))]);
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) acc[g][b] = mfma16(xa[g], mb[b], acc[g][b]);
+    }
+    wait_vm_barrier<(NST - 2) * PER_WAVE>();
+  }
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+
+  // acc[g][b][i] = D[32 wave + 16 g + 4 (lane / 16) + i][16 b + lane % 16]
+  float* red = (float*)lds;  // [ST_TM][64]
+#pragma unroll
+  for (int g = 0; g < 2; ++g)
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        red[(wave * 32 + g * 16 + 4 * (lane >> 4) + i) * 64 + b * 16 + (lane & 15)] = acc[g][b][i];
+  __syncthreads();
+  // tile ranks [c0, c0 + rr) scaled and split into the planes of dst
+  auto emit = [&](uint16_t* __restrict__ dst, int c0, int rr, float sc) {
+    for (int e = tid; e < ST_TM * (r_max / 4); e += 256) {
+      const int row = e / (r_max / 4), cg = (e % (r_max / 4)) * 4;
+      if (row >= rows) continue;
+      const int prow = p0 + row;
+      const float sc_row = rm.rowscale ? sc * rm.rowscale[prow] : sc;
+      float v[4];
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const int c = cg + qq;
+        v[qq] = c < rr ? sc_row * red[row * 64 + c0 + c] : 0.f;
+      }
+      uint32_t h01, l01, h23, l23;
+      split2_bf16(v[0], v[1], h01, l01);
+      split2_bf16(v[2], v[3], h23, l23);
+      uint16_t* o = dst + (int64_t)(rm.out ? rm.out[prow] : prow) * r_max + cg;
+      *(uint2*)o = make_uint2(h01, h23);
+      *(uint2*)(o + plane) = make_uint2(l01, l23);
+    }
+  };
+  emit(out, 0, r, scale);
+  if (!KM && sec.mat) emit(sec.out, sec.c2, sec.r, sec.scale);
+}
+
+// One block per CU.  Blocks take the adapter tiles (32 rows, or 128 with
+// TALL; pre[n_ad] of them) XCD-contiguously, then zero, grid-stride, the rows
+// of tokens that belong to no active adapter (adpos == -1), and block 0
+// clears `zero`.
+template <bool TALL>
 __global__ __launch_bounds__(256) void shrink_kernel(
     const uint16_t* __restrict__ in, int64_t ld_in, int K, const uint16_t* __restrict__ mat_pack,
     int from_b, const lora_adapter_desc* __restrict__ desc, const int32_t* __restrict__ adpos,
@@ -288,7 +457,7 @@ __global__ __launch_bounds__(256) void shrink_kernel(
   const ItemRange ir = xcd_items(pre32[n_ad]);
   for (int item = ir.first; item < ir.end; item += ir.step) {
     TileInfo ti;
-    tile_of(pre32, offsets, n_ad, item, SH_TM, ti);
+    tile_of(pre32, offsets, n_ad, item, TALL ? ST_TM : SH_TM, ti);
     const lora_adapter_desc d = desc[ti.a];
     const int r = d.rank;
     const uint16_t* mat = mat_pack + (from_b ? d.b_off : d.a_off);
@@ -304,8 +473,15 @@ __global__ __launch_bounds__(256) void shrink_kernel(
       nb += (d2.rank + 15) / 16;
     }
     __syncthreads();   // the previous item's LDS reads are done before the ring refills
-#define SHRINK_TILE(NB, KM) \
-  shrink_tile<NB, KM>(in, ld_in, K, mat, r, sc, sec, rm, ti.p0, ti.rows, sh_lds, out, plane, r_max)
+#define SHRINK_TILE(NB, KM)                                                                    \
+  do {                                                                                         \
+    if constexpr (TALL)                                                                        \
+      shrink_tall_tile<NB, KM>(in, ld_in, K, mat, r, sc, sec, rm, ti.p0, ti.rows, sh_lds, out, \
+                               plane, r_max);                                                  \
+    else                                                                                       \
+      shrink_tile<NB, KM>(in, ld_in, K, mat, r, sc, sec, rm, ti.p0, ti.rows, sh_lds, out,      \
+                          plane, r_max);                                                       \
+  } while (0)
     if (from_b) {
       if (nb == 1) SHRINK_TILE(1, true);
       else if (nb == 2) SHRINK_TILE(2, true);
@@ -372,24 +548,31 @@ __device__ __forceinline__ int gr_fq(int t) { return (2 * (t & 3)) | (8 * ((t >>
 // mode 1 (dA): out layout [r][D] (j fastest): MFMA M = j, N = c.
 // Dual P (mode 1): a second set of planes at element offset p2_off from P,
 // with the same row stride r_max; tile ranks [r_max, 2 r_max) come from it.
-template <int NCB, int MODE, int PN>
+// nblk column blocks (j0, j0 + 256, ..) stream as one sequence of stages
+// (the token stages of each block in turn), so the ring does not drain between
+// blocks; after a block's last stage write(j0 of the block) stores acc, which
+// then restarts from zero.
+// (MULTI = false: one block, the plain loop.)
+template <int NCB, int MODE, int PN, bool MULTI, class F>
 __device__ __forceinline__ void grad_tile(const uint16_t* __restrict__ P, int64_t plane, int r_max,
                                           int64_t p2_off, const uint16_t* __restrict__ zero,
                                           const uint16_t* __restrict__ Q, int64_t ld_q, int D,
                                           const int32_t* tok_s, int p_base, int rows, int j0,
-                                          uint4* lds, f32x4 (&acc)[4][4]) {
+                                          int nblk_, uint4* lds, f32x4 (&acc)[4][4], F&& write) {
   using G = GrP<PN>;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int KT = (rows + GR_TT - 1) / GR_TT;
+  const int nblk = MULTI ? nblk_ : 1;
+  const int total = nblk * KT;
   // DMA sources.  Q: instruction i of wave w fills rows (4w + i)*2 + L/32,
   // chunk L%32.  P: slot s = (w*PN + i)*64 + L holds plane s / (32*PW), token
   // row (s / PW) % 32, physical chunk s % PW.
-  int qrow[GR_QDMA], qcol[GR_QDMA];
+  int qrow[GR_QDMA], qcol[GR_QDMA];   // qcol: column within the 256-column block
 #pragma unroll
   for (int i = 0; i < GR_QDMA; ++i) {
     const int row = (wave * GR_QDMA + i) * 2 + (lane >> 5);
     qrow[i] = row;
-    qcol[i] = min(j0 + (((lane & 31) ^ gr_fq(row)) * 8), D - 8);
+    qcol[i] = ((lane & 31) ^ gr_fq(row)) * 8;
   }
   int prow[PN];
   int64_t poff[PN];
@@ -406,9 +589,11 @@ __device__ __forceinline__ void grad_tile(const uint16_t* __restrict__ P, int64_
     poff[i] = pl * plane + (second ? p2_off + (c - r_max / 8) * 8 : c * 8);
     pzoff[i] = c * 8;
   }
-  auto issue = [&](int st, int kt) {
+  auto issue = [&](int st, int sq) {   // stage sq of the sequence into ring slot st
     uint4* base = lds + st * G::STAGE;
-    const int t0 = kt * GR_TT;
+    const int blk = MULTI ? sq / KT : 0;
+    const int t0 = (sq - blk * KT) * GR_TT;
+    const int jb = j0 + blk * GR_NJ;
     int qt[GR_QDMA], pt[PN];
 #pragma unroll
     for (int i = 0; i < GR_QDMA; ++i) qt[i] = tok_s[min(t0 + qrow[i], rows - 1)];
@@ -421,7 +606,7 @@ __device__ __forceinline__ void grad_tile(const uint16_t* __restrict__ P, int64_
     }
 #pragma unroll
     for (int i = 0; i < GR_QDMA; ++i)
-      dma16(Q + (int64_t)qt[i] * ld_q + qcol[i],
+      dma16(Q + (int64_t)qt[i] * ld_q + min(jb + qcol[i], D - 8),
             __builtin_amdgcn_readfirstlane(lds_u32(base + (wave * GR_QDMA + i) * 64)));
 #pragma unroll
     for (int i = 0; i < PN; ++i) {
@@ -431,14 +616,16 @@ __device__ __forceinline__ void grad_tile(const uint16_t* __restrict__ P, int64_
   };
 
 #pragma unroll
-  for (int st = 0; st < G::NST - 1; ++st) issue(st, min(st, KT - 1));
+  for (int st = 0; st < G::NST - 1; ++st) issue(st, min(st, total - 1));
   wait_vm_barrier<(G::NST - 2) * G::PER_WAVE>();
 
   const int g16 = lane >> 4;   // 16-lane group: tokens 8*g16 .. 8*g16+7 of the stage
   const int li = lane & 15;
-  for (int kt = 0; kt < KT; ++kt) {
-    const int st = kt % G::NST;
-    issue((kt + G::NST - 1) % G::NST, min(kt + G::NST - 1, KT - 1));
+  int sq = 0;
+  for (int blk = 0; blk < nblk; ++blk) {
+  for (int kt = 0; kt < KT; ++kt, ++sq) {
+    const int st = sq % G::NST;
+    issue((sq + G::NST - 1) % G::NST, min(sq + G::NST - 1, total - 1));
     const uint4* qt = lds + st * G::STAGE;
     const uint4* ptile = qt + GR_QSLOTS;
     // Q fragments: 4 column sub-tiles of this wave's 64 columns
@@ -486,6 +673,14 @@ __device__ __forceinline__ void grad_tile(const uint16_t* __restrict__ P, int64_
       }
     wait_vm_barrier<(G::NST - 2) * G::PER_WAVE>();
   }
+  // the block's last token stage is done (the next block's first stages are
+  // in flight): store it and start the next one from zero
+  write(j0 + blk * GR_NJ);
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no DMA may outlive the block
 }
 
@@ -497,14 +692,14 @@ struct GradDual {
   int64_t p2_off;
 };
 
-template <int MODE, int PN>
+template <int MODE, int PN, bool MULTI>
 __device__ __forceinline__ void grad_item(
     const uint16_t* __restrict__ P, int64_t plane, int r_max, const uint16_t* __restrict__ zero,
     const uint16_t* __restrict__ Q, int64_t ld_q, int D,
     const lora_adapter_desc* __restrict__ desc, const int32_t* __restrict__ q_rows, int p_ident,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ chunk_pre, int n_ad,
     float* __restrict__ out_pack, float* __restrict__ partial, int accumulate, int slot, int j0,
-    int32_t* tok_s, uint4* gr_lds, const GradDual du) {
+    int nblk, int32_t* tok_s, uint4* gr_lds, const GradDual du) {
   TileInfo ti;
   tile_of(chunk_pre, offsets, n_ad, slot, GR_TC, ti);
   __syncthreads();   // every wave is done with the previous item's tokens and ring
@@ -526,8 +721,51 @@ __device__ __forceinline__ void grad_item(
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int ncb = dual ? (r_max + d2.rank + 15) / 16 : (r + 15) / 16;
-#define GRAD_TILE(NCB) \
-  grad_tile<NCB, MODE, PN>(P, plane, r_max, p2, zero, Q, ld_q, D, tok_s, p_base, ti.rows, j0, gr_lds, acc)
+
+  // ---- write of one 256-column block.  Region of this adapter: D*r floats.
+  const int64_t base = MODE == 0 ? d.b_off : d.a_off;
+  const bool direct = nchunks == 1;
+  float* dst = direct ? out_pack + base : partial + (int64_t)slot * D * rt;
+  // dual, direct: ranks >= r_max go to the second table's region
+  float* dst2 = direct && dual ? du.out2 + d2.a_off : nullptr;
+  auto write = [&](int jb) {
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        if (ct >= ncb) continue;
+        if (MODE == 0) {
+          // D[c][j]: lane holds c = ct*16 + 4*(lane/16) + i, j = jt*16 + lane%16
+          const int c = ct * 16 + 4 * (lane >> 4);
+          const int j = jb + wave * 64 + jt * 16 + (lane & 15);
+          if (c >= r || j >= D) continue;
+          float4* p = (float4*)(dst + (int64_t)j * r + c);
+          float4 v = make_float4(acc[jt][ct][0], acc[jt][ct][1], acc[jt][ct][2], acc[jt][ct][3]);
+          if (direct && accumulate) {
+            float4 o = *p;
+            v.x += o.x; v.y += o.y; v.z += o.z; v.w += o.w;
+          }
+          *p = v;
+        } else {
+          // D[j][c]: lane holds j = jt*16 + 4*(lane/16) + i, c = ct*16 + lane%16
+          const int j = jb + wave * 64 + jt * 16 + 4 * (lane >> 4);
+          const int c = ct * 16 + (lane & 15);
+          const bool hi = dual && c >= r_max;   // rank c - r_max of the second table
+          if ((hi ? c - r_max >= d2.rank : c >= r) || j >= D) continue;
+          float4* p = (float4*)(hi && direct ? dst2 + (int64_t)(c - r_max) * D + j
+                                             : dst + (int64_t)c * D + j);
+          float4 v = make_float4(acc[jt][ct][0], acc[jt][ct][1], acc[jt][ct][2], acc[jt][ct][3]);
+          if (direct && accumulate) {
+            float4 o = *p;
+            v.x += o.x; v.y += o.y; v.z += o.z; v.w += o.w;
+          }
+          *p = v;
+        }
+      }
+  };
+#define GRAD_TILE(NCB)                                                                       \
+  grad_tile<NCB, MODE, PN, MULTI>(P, plane, r_max, p2, zero, Q, ld_q, D, tok_s, p_base,         \
+                                  ti.rows, j0, nblk, gr_lds, acc, write)
   if (PN == 1) {
     if (ncb == 1) GRAD_TILE(1);
     else GRAD_TILE(2);
@@ -538,70 +776,35 @@ __device__ __forceinline__ void grad_item(
     else GRAD_TILE(4);
   }
 #undef GRAD_TILE
-
-  // ---- write.  Region of this adapter: D*r floats.
-  const int64_t base = MODE == 0 ? d.b_off : d.a_off;
-  const bool direct = nchunks == 1;
-  float* dst = direct ? out_pack + base : partial + (int64_t)slot * D * rt;
-  // dual, direct: ranks >= r_max go to the second table's region
-  float* dst2 = direct && dual ? du.out2 + d2.a_off : nullptr;
-#pragma unroll
-  for (int jt = 0; jt < 4; ++jt)
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      if (ct >= ncb) continue;
-      if (MODE == 0) {
-        // D[c][j]: lane holds c = ct*16 + 4*(lane/16) + i, j = jt*16 + lane%16
-        const int c = ct * 16 + 4 * (lane >> 4);
-        const int j = j0 + wave * 64 + jt * 16 + (lane & 15);
-        if (c >= r || j >= D) continue;
-        float4* p = (float4*)(dst + (int64_t)j * r + c);
-        float4 v = make_float4(acc[jt][ct][0], acc[jt][ct][1], acc[jt][ct][2], acc[jt][ct][3]);
-        if (direct && accumulate) {
-          float4 o = *p;
-          v.x += o.x; v.y += o.y; v.z += o.z; v.w += o.w;
-        }
-        *p = v;
-      } else {
-        // D[j][c]: lane holds j = jt*16 + 4*(lane/16) + i, c = ct*16 + lane%16
-        const int j = j0 + wave * 64 + jt * 16 + 4 * (lane >> 4);
-        const int c = ct * 16 + (lane & 15);
-        const bool hi = dual && c >= r_max;   // rank c - r_max of the second table
-        if ((hi ? c - r_max >= d2.rank : c >= r) || j >= D) continue;
-        float4* p = (float4*)(hi && direct ? dst2 + (int64_t)(c - r_max) * D + j
-                                           : dst + (int64_t)c * D + j);
-        float4 v = make_float4(acc[jt][ct][0], acc[jt][ct][1], acc[jt][ct][2], acc[jt][ct][3]);
-        if (direct && accumulate) {
-          float4 o = *p;
-          v.x += o.x; v.y += o.y; v.z += o.z; v.w += o.w;
-        }
-        *p = v;
-      }
-    }
 }
 
-// One block per CU.  Items are (gradient chunk, 256-column block) pairs,
-// column block fastest (the column blocks of a chunk read the same token
-// rows), taken XCD-contiguously.
-template <int MODE, int PN>
+// One block per CU.  Items are (gradient chunk, group of cpi 256-column
+// blocks) pairs, column groups fastest (the groups of a chunk read the same
+// token rows), taken XCD-contiguously.  Many small chunks (MoE segments of
+// ~128 tokens) take whole rows of column blocks per item (cpi = all), so an
+// item's fixed costs (its token ids, the ring's first stages) are paid once
+// per chunk rather than once per 256 columns.
+template <int MODE, int PN, bool MULTI>
 __global__ __launch_bounds__(256) void grad_kernel(
     const uint16_t* __restrict__ P, int64_t plane, int r_max, const uint16_t* __restrict__ zero,
     const uint16_t* __restrict__ Q, int64_t ld_q, int D,
     const lora_adapter_desc* __restrict__ desc, const int32_t* __restrict__ q_rows, int p_ident,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ chunk_pre, int n_ad,
-    float* __restrict__ out_pack, float* __restrict__ partial, int accumulate, GradDual du) {
+    float* __restrict__ out_pack, float* __restrict__ partial, int accumulate, GradDual du,
+    int cpi) {
   extern __shared__ uint4 gr_lds[];
   // the chunk's token ids, cached in LDS: the DMA loop may issue no
   // compiler-tracked global loads (their waits would also wait for the DMA)
   __shared__ int32_t tok_s[GR_TC];
   const int ncol = (D + GR_NJ - 1) / GR_NJ;
-  const ItemRange ir = xcd_items(chunk_pre[n_ad] * ncol);
+  const int ngrp = (ncol + cpi - 1) / cpi;
+  const ItemRange ir = xcd_items(chunk_pre[n_ad] * ngrp);
   for (int item = ir.first; item < ir.end; item += ir.step) {
-    const int slot = item / ncol;
-    const int j0 = (item - slot * ncol) * GR_NJ;
-    grad_item<MODE, PN>(P, plane, r_max, zero, Q, ld_q, D, desc, q_rows, p_ident, offsets,
-                        chunk_pre, n_ad,
-                        out_pack, partial, accumulate, slot, j0, tok_s, gr_lds, du);
+    const int slot = item / ngrp;
+    const int g = item - slot * ngrp;
+    grad_item<MODE, PN, MULTI>(P, plane, r_max, zero, Q, ld_q, D, desc, q_rows, p_ident,
+                               offsets, chunk_pre, n_ad, out_pack, partial, accumulate, slot,
+                               g * cpi * GR_NJ, min(cpi, ncol - g * cpi), tok_s, gr_lds, du);
   }
 }
 
@@ -619,28 +822,31 @@ struct GradSide {
 // dB (mode 0) and dA (mode 1) of one layer in one launch: items of the first
 // side, then of the second, spread XCD-contiguously as in grad_kernel.  Both
 // sides share the segments, the plane stride and the rank bound.
-template <int PN>
+template <int PN, bool MULTI>
 __global__ __launch_bounds__(256) void grad_pair_kernel(
     GradSide s0, GradSide s1, int64_t plane, int r_max, const uint16_t* __restrict__ zero,
     const int32_t* __restrict__ q_rows, int p_ident, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ chunk_pre, int n_ad, int accumulate) {
+    const int32_t* __restrict__ chunk_pre, int n_ad, int accumulate, int cpi) {
   extern __shared__ uint4 gr_lds[];
   __shared__ int32_t tok_s[GR_TC];
   const int nc0 = (s0.D + GR_NJ - 1) / GR_NJ, nc1 = (s1.D + GR_NJ - 1) / GR_NJ;
-  const int n0 = chunk_pre[n_ad] * nc0;
-  const ItemRange ir = xcd_items(n0 + chunk_pre[n_ad] * nc1);
+  const int ng0 = (nc0 + cpi - 1) / cpi, ng1 = (nc1 + cpi - 1) / cpi;
+  const int n0 = chunk_pre[n_ad] * ng0;
+  const ItemRange ir = xcd_items(n0 + chunk_pre[n_ad] * ng1);
   const GradDual none{nullptr, nullptr, 0};
   for (int item = ir.first; item < ir.end; item += ir.step) {
     if (item < n0) {
-      const int slot = item / nc0;
-      grad_item<0, PN>(s0.P, plane, r_max, zero, s0.Q, s0.ld_q, s0.D, s0.desc, q_rows, p_ident,
-                       offsets, chunk_pre, n_ad, s0.out_pack, s0.partial, accumulate, slot,
-                       (item - slot * nc0) * GR_NJ, tok_s, gr_lds, none);
+      const int slot = item / ng0, g = item - slot * ng0;
+      grad_item<0, PN, MULTI>(s0.P, plane, r_max, zero, s0.Q, s0.ld_q, s0.D, s0.desc, q_rows,
+                              p_ident, offsets, chunk_pre, n_ad, s0.out_pack, s0.partial,
+                              accumulate, slot, g * cpi * GR_NJ, min(cpi, nc0 - g * cpi), tok_s,
+                              gr_lds, none);
     } else {
-      const int it = item - n0, slot = it / nc1;
-      grad_item<1, PN>(s1.P, plane, r_max, zero, s1.Q, s1.ld_q, s1.D, s1.desc, q_rows, p_ident,
-                       offsets, chunk_pre, n_ad, s1.out_pack, s1.partial, accumulate, slot,
-                       (it - slot * nc1) * GR_NJ, tok_s, gr_lds, none);
+      const int it = item - n0, slot = it / ng1, g = it - slot * ng1;
+      grad_item<1, PN, MULTI>(s1.P, plane, r_max, zero, s1.Q, s1.ld_q, s1.D, s1.desc, q_rows,
+                              p_ident, offsets, chunk_pre, n_ad, s1.out_pack, s1.partial,
+                              accumulate, slot, g * cpi * GR_NJ, min(cpi, nc1 - g * cpi), tok_s,
+                              gr_lds, none);
     }
   }
 }
@@ -723,49 +929,74 @@ lora_status launch_shrink(const uint16_t* in, int64_t ld_in, int K, const uint16
                           const int32_t* offsets, const int32_t* pre32, int n_ad,
                           int64_t n_tokens, uint16_t* out, int r_max, void* zero, hipStream_t s,
                           const uint16_t* mat_pack2, const lora_adapter_desc* desc2,
-                          uint16_t* out2) {
+                          uint16_t* out2, const int32_t* pre128) {
   if (n_tokens <= 0) return LORA_OK;
   if (mat_pack2 && (from_b || r_max > 32 || !desc2 || !out2)) {
     set_error("shrink: a dual shrink takes two A tables with ranks <= 32");
     return LORA_E_INVALID_ARG;
   }
   const int nb_max = (mat_pack2 ? 2 : 1) * ((r_max + 15) / 16);
-  const size_t ring[4] = {(size_t)sh_nst<1>() * (SH_XSLOTS + 256) * 16,
-                          (size_t)sh_nst<2>() * (SH_XSLOTS + 512) * 16,
-                          (size_t)sh_nst<3>() * (SH_XSLOTS + 768) * 16,
-                          (size_t)sh_nst<4>() * (SH_XSLOTS + 1024) * 16};
-  size_t lds = (size_t)4 * SH_TM * 64 * sizeof(float);
-  for (int nb = 1; nb <= nb_max; ++nb) lds = std::max(lds, ring[nb - 1]);
-  static size_t attr = 0;
-  if (attr < lds) {
-    TRY_HIP(hipFuncSetAttribute((const void*)shrink_kernel,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
-    attr = lds;
+  // 128-row tiles once the batch gives every CU at least two of them (with
+  // about one per CU, 32768 rows, the 32-row tiles balance better)
+  const bool tall = pre128 != nullptr && n_tokens >= (int64_t)2 * ST_TM * persistent_blocks() &&
+                    K % ST_KC == 0;
+  size_t lds;
+  if (tall) {
+    lds = (size_t)ST_TM * 64 * sizeof(float);
+    for (int nb = 1; nb <= nb_max; ++nb)
+      lds = std::max(lds, (size_t)ST_NST * (ST_XSLOTS + (nb <= 2 ? 2 : 4) * 128) * 16);
+  } else {
+    const size_t ring[4] = {(size_t)sh_nst<1>() * (SH_XSLOTS + 256) * 16,
+                            (size_t)sh_nst<2>() * (SH_XSLOTS + 512) * 16,
+                            (size_t)sh_nst<3>() * (SH_XSLOTS + 768) * 16,
+                            (size_t)sh_nst<4>() * (SH_XSLOTS + 1024) * 16};
+    lds = (size_t)4 * SH_TM * 64 * sizeof(float);
+    for (int nb = 1; nb <= nb_max; ++nb) lds = std::max(lds, ring[nb - 1]);
   }
-  hipLaunchKernelGGL(shrink_kernel, dim3(persistent_blocks()), dim3(256), lds, s, in, ld_in, K,
-                     mat_pack, from_b, desc, adpos, ShrinkRows{in_rows, out_rows, rowscale},
-                     offsets, pre32, n_ad, n_tokens, out, r_max, (uint4*)zero, mat_pack2, desc2,
-                     out2);
-  return launch_check("shrink");
+  auto go = [&](auto tall_) -> lora_status {
+    constexpr bool T = decltype(tall_)::value;
+    static size_t attr = 0;
+    if (attr < lds) {
+      TRY_HIP(hipFuncSetAttribute((const void*)shrink_kernel<T>,
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
+      attr = lds;
+    }
+    hipLaunchKernelGGL(shrink_kernel<T>, dim3(persistent_blocks()), dim3(256), lds, s, in, ld_in,
+                       K, mat_pack, from_b, desc, adpos, ShrinkRows{in_rows, out_rows, rowscale},
+                       offsets, T ? pre128 : pre32, n_ad, n_tokens, out, r_max, (uint4*)zero,
+                       mat_pack2, desc2, out2);
+    return launch_check("shrink");
+  };
+  return tall ? go(std::true_type{}) : go(std::false_type{});
 }
 
-template <int MODE, int PN>
+// 256-column blocks per gradient item: all of them (one item per chunk) when
+// the chunks alone give every CU a few items, else one.  Chunks are about one
+// per key and one per 1024 tokens.
+static int grad_cols_per_item(int64_t n_tokens, int n_ad, int D) {
+  const int64_t chunks = std::min<int64_t>(n_ad, n_tokens) + n_tokens / GR_TC;
+  const int ncol = (D + GR_NJ - 1) / GR_NJ;
+  return chunks >= 2 * (int64_t)persistent_blocks() ? ncol : 1;
+}
+
+template <int MODE, int PN, bool MULTI>
 lora_status launch_grad_t(dim3 grid, const uint16_t* P, int64_t plane, int r_max,
                           const uint16_t* zero, const uint16_t* Q, int64_t ld_q, int D,
                           const lora_adapter_desc* desc, const int32_t* q_rows, int p_ident,
                           const int32_t* offsets, const int32_t* chunk_pre, int n_ad,
-                          float* out_pack, float* partial, int accumulate, GradDual du,
+                          float* out_pack, float* partial, int accumulate, GradDual du, int cpi,
                           hipStream_t s) {
   const size_t lds = (size_t)GrP<PN>::NST * GrP<PN>::STAGE * sizeof(uint4);
   static bool attr = false;
   if (!attr) {
-    TRY_HIP(hipFuncSetAttribute((const void*)grad_kernel<MODE, PN>,
+    TRY_HIP(hipFuncSetAttribute((const void*)grad_kernel<MODE, PN, MULTI>,
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
     attr = true;
   }
-  hipLaunchKernelGGL((grad_kernel<MODE, PN>), grid, dim3(256), lds, s, P, plane, r_max, zero, Q,
+  hipLaunchKernelGGL((grad_kernel<MODE, PN, MULTI>), grid, dim3(256), lds, s, P, plane, r_max,
+                     zero, Q,
                      ld_q, D, desc, q_rows, p_ident, offsets, chunk_pre, n_ad, out_pack, partial,
-                     accumulate, du);
+                     accumulate, du, cpi);
   return launch_check("grad");
 }
 
@@ -788,9 +1019,14 @@ lora_status launch_grad(int mode, const uint16_t* P, int r_max, const void* zero
     const uint16_t* z = (const uint16_t*)zero;
     const GradDual du{desc2, out2, dual ? (int64_t)(P2 - P) : 0};
     lora_status st;
-#define LAUNCH_GRAD(M, PN)                                                                     \
-  launch_grad_t<M, PN>(grid, P, plane, r_max, z, Q, ld_q, D, desc, q_rows, p_ident, offsets, \
-                       chunk_pre, n_ad, out_pack, partial, accumulate, du, s)
+    const int cpi = grad_cols_per_item(n_tokens, n_ad, D);
+#define LAUNCH_GRAD(M, PN)                                                                   \
+  (cpi > 1 ? launch_grad_t<M, PN, true>(grid, P, plane, r_max, z, Q, ld_q, D, desc, q_rows,  \
+                                         p_ident, offsets, chunk_pre, n_ad, out_pack, partial, \
+                                         accumulate, du, cpi, s)                               \
+           : launch_grad_t<M, PN, false>(grid, P, plane, r_max, z, Q, ld_q, D, desc, q_rows, \
+                                          p_ident, offsets, chunk_pre, n_ad, out_pack,        \
+                                          partial, accumulate, du, 1, s))
     if (rt <= 32)
       st = mode == 0 ? LAUNCH_GRAD(0, 1) : LAUNCH_GRAD(1, 1);
     else
@@ -822,21 +1058,27 @@ lora_status launch_grad_pair(const uint16_t* u, const uint16_t* dy, int64_t ld_d
   if (n_tokens > 0) {
     const int64_t plane = n_tokens * r_max;
     const uint16_t* z = (const uint16_t*)zero;
-    auto go = [&](auto pn) -> lora_status {
+    const int cpi = grad_cols_per_item(n_tokens, n_ad, std::min(d_in, d_out));
+    auto go = [&](auto pn, auto multi) -> lora_status {
       constexpr int PN = decltype(pn)::value;
+      constexpr bool MULTI = decltype(multi)::value;
       const size_t lds = (size_t)GrP<PN>::NST * GrP<PN>::STAGE * sizeof(uint4);
       static bool attr = false;
       if (!attr) {
-        TRY_HIP(hipFuncSetAttribute((const void*)grad_pair_kernel<PN>,
+        TRY_HIP(hipFuncSetAttribute((const void*)grad_pair_kernel<PN, MULTI>,
                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
         attr = true;
       }
-      hipLaunchKernelGGL(grad_pair_kernel<PN>, dim3(persistent_blocks()), dim3(256), lds, s, s0,
-                         s1, plane, r_max, z, q_rows, 0, offsets, chunk_pre, n_ad, accumulate);
+      hipLaunchKernelGGL((grad_pair_kernel<PN, MULTI>), dim3(persistent_blocks()), dim3(256), lds,
+                         s, s0, s1, plane, r_max, z, q_rows, 0, offsets, chunk_pre, n_ad,
+                         accumulate, MULTI ? cpi : 1);
       return launch_check("grad_pair");
     };
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
     const lora_status st =
-        r_max <= 32 ? go(std::integral_constant<int, 1>{}) : go(std::integral_constant<int, 2>{});
+        r_max <= 32 ? (cpi > 1 ? go(I1{}, std::true_type{}) : go(I1{}, std::false_type{}))
+                    : (cpi > 1 ? go(I2{}, std::true_type{}) : go(I2{}, std::false_type{}));
     if (st) return st;
   }
   const unsigned gy = (unsigned)std::max<int64_t>(

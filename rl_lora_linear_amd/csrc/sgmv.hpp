@@ -80,7 +80,10 @@ lora_status launch_shrink(const uint16_t* in, int64_t ld_in, int K, const uint16
                           const int32_t* offsets, const int32_t* pre32, int n_ad,
                           int64_t n_tokens, uint16_t* out, int r_max, void* zero, hipStream_t s,
                           const uint16_t* mat_pack2 = nullptr,
-                          const lora_adapter_desc* desc2 = nullptr, uint16_t* out2 = nullptr);
+                          const lora_adapter_desc* desc2 = nullptr, uint16_t* out2 = nullptr,
+                          const int32_t* pre128 = nullptr);
+// (pre128 nullable: the prefix of ceil(count / 128) per key; with it, large
+// batches run in 128-row tiles.)
 // Per key a: T_a = sum over a's positions p of P[p_row] Q[q_rows[p]]^T (mode 0:
 // [D][r] at b_off; mode 1: [r][D] at a_off), P the bf16 hi/lo planes.  P row:
 // the position itself with p_ident, else q_rows[p].  q_rows nullable.

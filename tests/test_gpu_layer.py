@@ -77,10 +77,18 @@ def _case(kind):
         ids = W.sorted_ids_from_lengths(lengths)
         ranks = [[64, 8, 32, 64, 16, 48][i % 6] for i in range(len(lengths))]
         return W.lora_layer(24, len(ids), 192, 320, ranks, [float(r) for r in ranks], ids=ids)
+    if kind == "tall":        # a batch large enough for 128-row shrink tiles: interleaved ids,
+        # mixed ranks, an adapter with no token, segments that end mid-tile
+        rng = np.random.default_rng(25)
+        ids = rng.integers(0, 8, size=65536).astype(np.int32)
+        ids[ids == 5] = 2                         # adapter 5 owns no token
+        ranks = [8, 64, 16, 40, 32, 24, 48, 56]
+        return W.lora_layer(25, 65536, 128, 192, ranks, [float(r) for r in ranks], ids=ids,
+                            order="interleaved")
     raise KeyError(kind)
 
 
-CASES = ["tiny", "ragged", "multi", "big_chunks", "many"]
+CASES = ["tiny", "ragged", "multi", "big_chunks", "many", "tall"]
 
 
 @pytest.mark.parametrize("kind", CASES)
