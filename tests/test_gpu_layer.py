@@ -85,10 +85,17 @@ def _case(kind):
         ranks = [8, 64, 16, 40, 32, 24, 48, 56]
         return W.lora_layer(25, 65536, 128, 192, ranks, [float(r) for r in ranks], ids=ids,
                             order="interleaved")
+    if kind == "small_segs":  # 600 adapters of 1-12 tokens: enough chunks that a reduction item
+        # takes all of a chunk's column blocks; column counts that end mid-block
+        rng = np.random.default_rng(26)
+        lengths = rng.integers(1, 13, size=600)
+        ids = W.sorted_ids_from_lengths(lengths)
+        ranks = [[8, 16, 24, 32, 40, 48, 56, 64][i % 8] for i in range(600)]
+        return W.lora_layer(26, len(ids), 320, 448, ranks, [float(r) for r in ranks], ids=ids)
     raise KeyError(kind)
 
 
-CASES = ["tiny", "ragged", "multi", "big_chunks", "many", "tall"]
+CASES = ["tiny", "ragged", "multi", "big_chunks", "many", "tall", "small_segs"]
 
 
 @pytest.mark.parametrize("kind", CASES)
