@@ -824,7 +824,7 @@ lora_status expert_forward(const moe_shape& sh, const uint16_t* x, const int32_t
   // down, then the weighted combine back to tokens
   TRY(moe_project(sh, w, sv.h, nullptr, NK, W_down, H, F, sv.su[2], down_pack, 1, w.desc[2],
                   nullptr, w.o, s));
-  return launch_moe_combine(w.o, nullptr, weights, w.inv, w.keys, sh.n_tokens, sh.top_k, H, y, s);
+  return launch_moe_combine(w.o, weights, w.inv, w.keys, sh.n_tokens, sh.top_k, H, y, s);
 }
 
 lora_status expert_backward(const moe_shape& sh, const uint16_t* dy, const uint16_t* x,
@@ -918,7 +918,7 @@ lora_status expert_backward(const moe_shape& sh, const uint16_t* dy, const uint1
                       w.offsets, w.prec, n_keys, NK, grads[i], w.partial, accumulate, s));
   }
   if (!routed) return LORA_OK;
-  return launch_moe_combine(w.dxp, nullptr, nullptr, w.inv, w.keys, sh.n_tokens, sh.top_k, H, dx,
+  return launch_moe_combine(w.dxp, nullptr, w.inv, w.keys, sh.n_tokens, sh.top_k, H, dx,
                             s);
 }
 

@@ -120,7 +120,6 @@ __global__ __launch_bounds__(256) void moe_gather_w_kernel(const float* __restri
 
 // One block per token; 8 columns (16 bytes of bf16) per thread and step.
 __global__ __launch_bounds__(256) void moe_combine_kernel(const uint16_t* __restrict__ a,
-                                                          const uint16_t* __restrict__ b,
                                                           const float* __restrict__ w,
                                                           const int32_t* __restrict__ inv,
                                                           const int32_t* __restrict__ keys,
@@ -131,25 +130,15 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const uint16_t* __rest
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int k = 0; k < K; ++k) {
       const int64_t j = t * K + k;
-      if (keys[j] < 0) continue;
+      if (keys[j] < 0) continue;   // dropped assignments (invalid expert) add nothing
       const int64_t p = inv[j];
       const float wk = w ? w[j] : 1.f;
       const uint4 va = *(const uint4*)(a + p * H + c);
       const uint32_t xa[4] = {va.x, va.y, va.z, va.w};
-      if (b) {
-        const uint4 vb = *(const uint4*)(b + p * H + c);
-        const uint32_t xb[4] = {vb.x, vb.y, vb.z, vb.w};
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          acc[2 * q] += wk * (bf2f_lo(xa[q]) + bf2f_lo(xb[q]));
-          acc[2 * q + 1] += wk * (bf2f_hi(xa[q]) + bf2f_hi(xb[q]));
-        }
-      } else {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          acc[2 * q] += wk * bf2f_lo(xa[q]);
-          acc[2 * q + 1] += wk * bf2f_hi(xa[q]);
-        }
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q] += wk * bf2f_lo(xa[q]);
+        acc[2 * q + 1] += wk * bf2f_hi(xa[q]);
       }
     }
     *(uint4*)(out + t * H + c) = make_uint4(pack2bf(acc[0], acc[1]), pack2bf(acc[2], acc[3]),
@@ -221,11 +210,11 @@ lora_status launch_moe_gather_w(const float* w, const int32_t* perm, int64_t n, 
   return launch_check("moe_gather_w");
 }
 
-lora_status launch_moe_combine(const uint16_t* a, const uint16_t* b, const float* w,
-                               const int32_t* inv, const int32_t* keys, int64_t n_tok, int K,
-                               int64_t H, uint16_t* out, hipStream_t s) {
+lora_status launch_moe_combine(const uint16_t* a, const float* w, const int32_t* inv,
+                               const int32_t* keys, int64_t n_tok, int K, int64_t H,
+                               uint16_t* out, hipStream_t s) {
   if (n_tok <= 0) return LORA_OK;
-  hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)n_tok), dim3(256), 0, s, a, b, w, inv, keys,
+  hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)n_tok), dim3(256), 0, s, a, w, inv, keys,
                      K, H, out);
   return launch_check("moe_combine");
 }

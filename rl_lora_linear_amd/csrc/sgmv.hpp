@@ -146,9 +146,9 @@ lora_status launch_moe_desc(const lora_adapter_desc* const src[3], lora_adapter_
                             int E, int n_ad, hipStream_t s);
 lora_status launch_moe_gather_w(const float* w, const int32_t* perm, int64_t n, float* wpos,
                                 hipStream_t s);
-lora_status launch_moe_combine(const uint16_t* a, const uint16_t* b, const float* w,
-                               const int32_t* inv, const int32_t* keys, int64_t n_tok, int K,
-                               int64_t H, uint16_t* out, hipStream_t s);
+lora_status launch_moe_combine(const uint16_t* a, const float* w, const int32_t* inv,
+                               const int32_t* keys, int64_t n_tok, int K, int64_t H,
+                               uint16_t* out, hipStream_t s);
 lora_status launch_planes_scale(const uint16_t* src, const float* wpos, int64_t n, int R,
                                 uint16_t* dst, hipStream_t s);
 
