@@ -128,14 +128,22 @@ constexpr int DMA_PER_OP = GBM / (8 * NWAVES);   // DMA instructions (8 rows eac
                                                  // operand and stage
 
 // After the k loop (and a barrier) the operand stages hold the epilogue's
-// scratch: the staged output tile, the per-wave LoRA slab tiles and the row
-// map (or the logsumexp partials).
+// scratch: first the staged LoRA expand operands (below), then the staged
+// output tile and the row map (or the logsumexp partials).
 constexpr int EPI_SLAB = GBM * 512;                        // bytes: after the staged tile
-constexpr int SLAB_LD = WN + 8;                            // bf16 per LDS row of a slab tile
-constexpr int SLAB_BYTES = 16 * SLAB_LD * 2;               // per wave
-constexpr int EPI_ROW = EPI_SLAB + NWAVES * SLAB_BYTES;
+constexpr int EPI_ROW = EPI_SLAB;
 constexpr int RING_BYTES = 2 * NSTAGE * S_TILE * 16;
-constexpr int LDS_BYTES = RING_BYTES > EPI_ROW + GBM * 4 ? RING_BYTES : EPI_ROW + GBM * 4;
+// LoRA expand staging: the tile's scaled vector rows (hi and lo planes, 256
+// rows x 64 ranks each, 16-byte chunks swizzled by row like the operand
+// stages), then the factor blocks of one batch of runs, then the row and run
+// tables.
+constexpr int X_LDS = 160 * 1024;
+constexpr int XV_PLANE = GBM * 128;                        // bytes per vector plane
+constexpr int XM_OFF = 2 * XV_PLANE;                       // factor blocks
+constexpr int X_TAB_OFF = X_LDS - 11 * 1024;               // tables (11 KB)
+constexpr int XM_CHUNKS = (X_TAB_OFF - XM_OFF) / 1024 * 64;   // 16-byte chunks, whole DMA rounds
+constexpr int LDS_BYTES = X_LDS;
+static_assert(RING_BYTES <= LDS_BYTES && EPI_ROW + GBM * 4 <= LDS_BYTES, "LDS block too small");
 static_assert(EPI_SLAB + NWN * GBM * 8 <= LDS_BYTES, "logsumexp partials exceed the LDS block");
 __shared__ uint4 g_stage[LDS_BYTES / 16];   // [A stages][B stages], then epilogue scratch
 
@@ -150,101 +158,234 @@ __device__ __forceinline__ void dma16s(uint32_t voff, const void* base, uint32_t
                : "memory");
 }
 
-// Fused LoRA expand: for every adapter a owning rows of this wave's 128 rows
-// (rows are segment positions, so they span one adapter or a few), add
-// (s_a u_tok) . M_a^T to the accumulators as an extra MFMA K-slab of depth r_a.
-// The scaled vector is stored as bf16 hi and lo planes, one MFMA each, so the
-// slab keeps ~16 significant bits; M_a is bf16-exact.  tok[i] / ad[i] are the
-// token and adapter (-1: none) of this lane's fragment rows, loaded before
-// the k loop.  An adapter's MFMAs run only for the 32-row tiles holding rows
-// of it (a wave spanning two adapters pays for each about once, not twice).
-// With M_a = A_a^T (use_b_off = 0) the factor block of a 16-rank slice (16
-// rows of A_a x the wave's WN columns) is loaded row-wise into the wave's LDS
-// tile `slab` (rows padded by 16 bytes: the transposing reads of 4 rows hit
-// distinct banks) and read back transposed, 8 consecutive ranks of one column
-// per lane.
-__device__ __forceinline__ void lora_slab(const GemmEpi& ep, const uint16_t* vec,
-                                          const uint16_t* lmat, const lora_adapter_desc* desc,
-                                          int n0, int N, int wn, int lane, uint4* slab,
-                                          const int (&vrow)[4], const int (&ad)[4],
-                                          f32x16 (&acc)[4][NJ]) {
-  const int m_l = lane & 31;
-  const int half = lane >> 5;
-  int lo = INT32_MAX, hi = -1;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    if (ad[i] >= 0) lo = min(lo, ad[i]), hi = max(hi, ad[i]);
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    lo = min(lo, __shfl_xor(lo, o));
-    hi = max(hi, __shfl_xor(hi, o));
-  }
-  const int a0 = __builtin_amdgcn_readfirstlane(lo), a1 = __builtin_amdgcn_readfirstlane(hi);
-  for (int a = a0; a <= a1; ++a) {
-    bool tile_has[4], mine = false;   // wave-uniform: 32-row tiles holding rows of a
+// One 16-byte LDS-DMA per lane from a per-lane 64-bit address:
+// global g -> LDS (m0v + 16 * lane).
+__device__ __forceinline__ void dma16v(const void* g, uint32_t m0v) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0v), "v"(g) : "memory");
+}
+
+// 16-byte chunks of one run's staged factor block: B_a rows n0.. (cols rows of
+// r ranks), or A_a's r rows over cols columns plus one pad chunk per row (the
+// transposing reads of 4 rows then hit distinct banks).
+__device__ __forceinline__ int xm_chunks(int r, int cols, int use_b_off) {
+  return use_b_off ? cols * (r >> 3) : r * (cols / 8 + 1);
+}
+
+// Fused LoRA expand, staged through LDS.  Every row m of the tile owned by
+// adapter a gets (s_a u_m) . M_a^T added to its accumulators: one extra MFMA
+// K-slab of depth r_a per plane (the scaled vector is stored as bf16 hi and lo
+// planes, so the slab keeps ~16 significant bits; M_a is bf16-exact).  With
+// M_a = B_a (use_b_off = 1) a staged row is one column's r_a ranks; with M_a =
+// A_a^T (use_b_off = 0) A_a's rows are staged over the tile's columns and read
+// back transposed, 8 consecutive ranks of one column per lane.
+//
+// Rows come in runs of one adapter (segment order).  Per LoRA set (a pass),
+// the tile's vector rows and the factor blocks of a batch of runs move to LDS
+// in one round of LDS-DMA, and every wave then runs its MFMAs from LDS: one
+// memory round trip per pass and batch, where loading operands per adapter
+// and 16-rank slice paid one per slice.  A run's MFMAs run only for the
+// 32-row tiles holding rows of it.  glu = 1 tiles run the first set in the
+// waves of the first column half and the second set in the others; a K split
+// runs both sets over every row.  Called by every thread of the block after
+// the k loop, with the ring free; ends with a barrier (LDS free again).
+__device__ __forceinline__ void lora_expand(const GemmEpi& ep, char* X, int n0, int N, int wave,
+                                            int lane, bool glu1, const int (&ad)[4],
+                                            const int (&vrow)[4], f32x16 (&acc)[4][NJ]) {
+  const int wm = wave / NWN, wn = wave % NWN;
+  const int m_l = lane & 31, half = lane >> 5;
+  int* s_ad = (int*)(X + X_TAB_OFF);   // adapter of each row (-1: none)
+  int* s_rid = s_ad + GBM;             // run of each row (-1: none)
+  int* s_vrow = s_rid + GBM;           // vector row of each row
+  int* s_rad = s_vrow + GBM;           // adapter of each run
+  int* s_rank = s_rad + GBM;           // [2][runs] rank per set
+  int64_t* s_moff = (int64_t*)(s_rank + 2 * GBM);   // [2][runs] factor offset per set
+  int* s_wc = (int*)(s_moff + 2 * GBM);             // runs started per 64 rows
+  static_assert(6 * GBM * 4 + 2 * GBM * 8 + 64 <= X_LDS - X_TAB_OFF, "expand tables");
+
+  if (wn == 0 && lane < 32) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      tile_has[i] = __any(ad[i] == a);
-      mine |= tile_has[i];
+      const int row = wm * 128 + i * 32 + lane;
+      s_ad[row] = ad[i];
+      s_vrow[row] = ad[i] >= 0 ? vrow[i] : 0;   // rows without an adapter read row 0 (unused)
     }
-    if (!mine) continue;                            // adapter absent from this wave's rows
-    const lora_adapter_desc d = desc[a];
-    const int r = d.rank;
-    const uint16_t* mat = lmat + (ep.use_b_off ? d.b_off : d.a_off);
-    for (int sl = 0; sl * 16 < r; ++sl) {
-      const int c = sl * 16 + 8 * half;
-      const bool cok = c < r;
-      uint4 h[4], l[4], v[NJ];
+  }
+  __syncthreads();
+
+  const int passes = ((glu1 || ep.k_split > 0) && ep.vec2) ? 2 : 1;
+  const int cols = glu1 ? GBN / 2 : GBN;
+  const int wn_eff = glu1 ? wn % (NWN / 2) : wn;
+  const int vch = ep.vec_ld / 8;
+  // both planes of a pass's vector rows: row r, logical chunk c at chunk
+  // r * 8 + (c ^ (r & 7)) of its plane
+  auto dma_vec = [&](const uint16_t* vec) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        h[i] = l[i] = make_uint4(0, 0, 0, 0);
-        if (ad[i] == a && cok) {
-          const uint16_t* vp = vec + (int64_t)vrow[i] * ep.vec_ld + c;
-          h[i] = *(const uint4*)vp;
-          l[i] = *(const uint4*)(vp + ep.vec_plane);
+    for (int pl = 0; pl < 2; ++pl)
+#pragma unroll
+      for (int i = 0; i < GBM * 8 / 64 / NWAVES; ++i) {
+        const int q = (wave * (GBM * 8 / 64 / NWAVES) + i) * 64 + lane;
+        const int row = q >> 3;
+        int c = (q & 7) ^ (row & 7);
+        if (c >= vch) c = 0;   // past the vector width: any chunk of the row (unused)
+        const uint16_t* src =
+            vec + (pl ? ep.vec_plane : 0) + (int64_t)s_vrow[row] * ep.vec_ld + c * 8;
+        dma16v(src, lds_addr((const uint4*)(X + pl * XV_PLANE + (q - lane) * 16)));
+      }
+  };
+  dma_vec(ep.vec);
+
+  // runs: a row starts one when its adapter differs from the previous row's
+  const int trow = wave * 64 + lane;   // rows 0..255 in waves 0..3
+  const int a_t = wave < GBM / 64 ? s_ad[trow] : -1;
+  const int a_p = (wave < GBM / 64 && trow > 0) ? s_ad[trow - 1] : -1;
+  const bool start = a_t >= 0 && a_t != a_p;
+  const uint64_t bal = __ballot(start);
+  const int incl = __popcll(bal & ((2ull << lane) - 1));
+  if (wave < GBM / 64 && lane == 0) s_wc[wave] = __popcll(bal);
+  __syncthreads();
+  int n_runs = 0, before = 0;
+#pragma unroll
+  for (int w = 0; w < GBM / 64; ++w) {
+    const int c = s_wc[w];
+    if (w < wave) before += c;
+    n_runs += c;
+  }
+  if (wave < GBM / 64) {
+    s_rid[trow] = a_t >= 0 ? before + incl - 1 : -1;
+    if (start) s_rad[before + incl - 1] = a_t;
+  }
+  __syncthreads();
+  for (int k = threadIdx.x; k < passes * n_runs; k += GTHREADS) {
+    const int p = k >= n_runs, kk = k - p * n_runs;
+    const lora_adapter_desc d = (p ? ep.desc2 : ep.desc)[s_rad[kk]];
+    s_rank[p * GBM + kk] = d.rank;
+    s_moff[p * GBM + kk] = ep.use_b_off ? d.b_off : d.a_off;
+  }
+  int rid[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) rid[i] = s_rid[wm * 128 + i * 32 + m_l];
+  __syncthreads();
+
+  const uint4* XV = (const uint4*)X;
+  const uint4* XL = (const uint4*)(X + XV_PLANE);
+  const uint4* XM = (const uint4*)(X + XM_OFF);
+#pragma unroll 1
+  for (int p = 0; p < passes; ++p) {
+    const uint16_t* lmat = p ? ep.lmat2 : ep.lmat;
+    const int* rk = s_rank + p * GBM;
+    const int64_t* mo = s_moff + p * GBM;
+    const bool mine = !glu1 || ((wn >= NWN / 2) == (p == 1));
+    if (p > 0 && n_runs > 0) dma_vec(ep.vec2);
+#pragma unroll 1
+    for (int k0 = 0; k0 < n_runs;) {
+      // the batch: runs k0 .. k1 - 1, as many as the factor area holds
+      int k1 = k0, used = 0;
+      while (k1 < n_runs) {
+        const int ch = xm_chunks(rk[k1], cols, ep.use_b_off);
+        if (k1 > k0 && used + ch > XM_CHUNKS) break;
+        used += ch;
+        ++k1;
+      }
+      // factor blocks: chunk q of the batch at XM + q
+      const int nins = (used + 63) / 64;
+      for (int t = wave; t < nins; t += NWAVES) {
+        const int q = t * 64 + lane;
+        int k = k0, base = 0, ch = xm_chunks(rk[k0], cols, ep.use_b_off);
+        while (k + 1 < k1 && q >= base + ch) {
+          base += ch;
+          ++k;
+          ch = xm_chunks(rk[k], cols, ep.use_b_off);
+        }
+        int c = q - base;
+        if (c >= ch) c = 0;   // past the batch: any chunk of its last run (unused)
+        const int r = rk[k];
+        const uint16_t* src;
+        if (ep.use_b_off) {
+          const int P = max(r >> 3, 1);
+          const int n = min(n0 + c / P, N - 1);   // columns past N feed no stored output
+          src = lmat + mo[k] + (int64_t)n * r + (c % P) * 8;
+        } else {
+          const int P = cols / 8 + 1;
+          const int rho = c / P;
+          int cc = c % P;
+          if (cc == P - 1) cc = 0;   // pad chunk
+          const int col = min(n0 + cc * 8, N - 8);
+          src = lmat + mo[k] + (int64_t)rho * ep.lmat_ld + col;
+        }
+        dma16v(src, lds_addr(XM + t * 64));
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+
+      if (mine) {
+        int base = 0;
+#pragma unroll 1
+        for (int k = k0; k < k1; ++k) {
+          const int r = rk[k];
+          bool th[4], any = false;   // wave-uniform: 32-row tiles holding rows of run k
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            th[i] = __any(rid[i] == k);
+            any |= th[i];
+          }
+          if (any) {
+#pragma unroll 1
+            for (int sl = 0; sl * 16 < r; ++sl) {
+              const int c = sl * 16 + 8 * half;
+              const bool cok = c < r;
+              uint4 h[4], l[4], v[NJ];
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int row = wm * 128 + i * 32 + m_l;
+                const int pc = row * 8 + ((c >> 3) ^ (row & 7));
+                h[i] = l[i] = make_uint4(0, 0, 0, 0);
+                if (rid[i] == k && cok) {
+                  h[i] = XV[pc];
+                  l[i] = XL[pc];
+                }
+              }
+              if (ep.use_b_off) {
+                const int P = r >> 3;
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                  const int col = wn_eff * WN + j * 32 + m_l;
+                  v[j] = cok ? XM[base + col * P + (c >> 3)] : make_uint4(0, 0, 0, 0);
+                }
+              } else {
+                // lane: column j*32 + m_l, ranks c .. c + 7 (rows of the staged A_a)
+                const int PB = cols + 8;   // bf16 per staged row
+                const int q = (lane >> 2) & 3, jj = lane & 3;
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                  const int col = wn_eff * WN + j * 32 + 16 * ((lane >> 4) & 1) + 4 * jj;
+                  const uint32_t off =
+                      (uint32_t)(XM_OFF + base * 16 + ((sl * 16 + 8 * half + q) * PB + col) * 2);
+                  const uint2 lo4 = tr_read((const uint4*)X, off);
+                  const uint2 hi4 = tr_read((const uint4*)X, off + 4 * PB * 2);
+                  v[j] = cok ? make_uint4(lo4.x, lo4.y, hi4.x, hi4.y) : make_uint4(0, 0, 0, 0);
+                }
+              }
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                if (!th[i]) continue;
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                  acc[i][j] = mfma32(as_bf16x8(v[j]), as_bf16x8(h[i]), acc[i][j]);
+                  acc[i][j] = mfma32(as_bf16x8(v[j]), as_bf16x8(l[i]), acc[i][j]);
+                }
+              }
+            }
+          }
+          base += xm_chunks(r, cols, ep.use_b_off);
         }
       }
-      if (ep.use_b_off) {
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          const int n = n0 + wn * WN + j * 32 + m_l;
-          v[j] = make_uint4(0, 0, 0, 0);
-          if (n < N && cok) v[j] = *(const uint4*)(mat + (int64_t)n * r + c);
-        }
-      } else {
-        // rows sl*16 .. +15 of A_a (zero past rank r), columns nw .. nw + WN - 1
-        // (zero past N), 16 bytes per lane and load
-        const int nw = n0 + wn * WN;
-#pragma unroll
-        for (int t = 0; t < NJ; ++t) {
-          const int q = lane + 64 * t;
-          const int row = q / (WN / 8), cc = q % (WN / 8);
-          uint4 val = make_uint4(0, 0, 0, 0);
-          if (sl * 16 + row < r && nw + cc * 8 < N)
-            val = *(const uint4*)(mat + (int64_t)(sl * 16 + row) * ep.lmat_ld + nw + cc * 8);
-          slab[row * (SLAB_LD / 8) + cc] = val;
-        }
-        // lane: column j*32 + m_l, ranks 8*half + 0..3 and 4..7 of the slice
-        const int q = (lane >> 2) & 3, jj = lane & 3;
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          const int col = j * 32 + 16 * ((lane >> 4) & 1) + 4 * jj;
-          const uint32_t off = (uint32_t)(((8 * half + q) * SLAB_LD + col) * 2);
-          const uint2 lo4 = tr_read(slab, off);
-          const uint2 hi4 = tr_read(slab, off + 4 * SLAB_LD * 2);
-          v[j] = make_uint4(lo4.x, lo4.y, hi4.x, hi4.y);
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (!tile_has[i]) continue;   // no row of adapter a in this 32-row tile
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          acc[i][j] = mfma32(as_bf16x8(v[j]), as_bf16x8(h[i]), acc[i][j]);
-          acc[i][j] = mfma32(as_bf16x8(v[j]), as_bf16x8(l[i]), acc[i][j]);
-        }
-      }
+      __syncthreads();   // every wave is done with the batch (and the pass's vectors)
+      k0 = k1;
     }
+  }
+  if (n_runs == 0) {   // no batch ran: the first pass's vector DMA lands before the LDS is reused
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
   }
 }
 
@@ -604,21 +745,10 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_nt_kernel(const uint16_t* __
     }
     __syncthreads();   // every wave is done reading the ring
     if (ep.vec) {
-      // one expand (set 2 for the second half of a glu tile), or both sets
-      // for a K split; a loop, so the slab is instantiated once
-      const int sets = (ep.k_split > 0 && ep.vec2) ? 2 : 1;
-      const bool upper = glu1 && wn >= NWN / 2;
-      const int wn_eff = glu1 ? wn % (NWN / 2) : wn;   // column slice within its product
-      uint4* slab = (uint4*)(T + EPI_SLAB + wave * SLAB_BYTES);
       int vrow[4];   // vector row of each fragment row: its C row, or its position
 #pragma unroll
       for (int i = 0; i < 4; ++i) vrow[i] = ep.vec_by_pos ? m0 + wm * 128 + i * 32 + m_l : tok[i];
-#pragma unroll 1
-      for (int set = 0; set < sets; ++set) {
-        const bool two = upper || set == 1;
-        lora_slab(ep, two ? ep.vec2 : ep.vec, two ? ep.lmat2 : ep.lmat, two ? ep.desc2 : ep.desc,
-                  n0, N, wn_eff, lane, slab, vrow, ad, acc);
-      }
+      lora_expand(ep, T, n0, N, wave, lane, glu1, ad, vrow, acc);
     }
     stage_rows();
 #pragma unroll
@@ -743,6 +873,13 @@ static lora_status launch_gemm(const uint16_t* A, const uint16_t* B, int M, int 
   }
   if (EPI == EPI_BF16 && ep.glu == 2 && (!ep.gu || !ep.dgu || ep.vec2)) {
     set_error("gemm: glu backward needs gu and dgu, one LoRA set");
+    return LORA_E_INVALID_ARG;
+  }
+  if (EPI == EPI_BF16 && ep.vec &&
+      (ep.vec_ld < 8 || ep.vec_ld > 64 || ep.vec_ld % 8 || ep.vec_plane % 8 || N % 8 ||
+       !ep.desc || !ep.lmat || !ep.adpos || ((ep.glu == 1 || ep.k_split > 0) && ep.vec2 && (!ep.desc2 || !ep.lmat2)))) {
+    set_error("gemm: LoRA expand needs vec_ld in 8..64 (a multiple of 8), 16-byte aligned "
+              "planes, N a multiple of 8 and both factor sets");
     return LORA_E_INVALID_ARG;
   }
   if (ep.k_split > 0 && (ep.k_split % SBK || ep.k_split >= K || !ep.B2)) {
