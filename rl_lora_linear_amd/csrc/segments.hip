@@ -216,16 +216,19 @@ __device__ __forceinline__ void block_scan4_1024(int32_t (&acc)[4], int32_t (*s_
 }
 
 // Lanes of this wave (among `active`) holding the same key as this lane.
-__device__ __forceinline__ uint64_t same_key_lanes(int key, uint64_t active) {
-  uint64_t mine = 0, rem = active;
-  while (rem) {
-    const int leader = __ffsll((long long)rem) - 1;
-    const int lk = __shfl(key, leader);
-    const uint64_t m = __ballot(key == lk) & active;
-    if (key == lk) mine = m;
-    rem &= ~m;
+__device__ __forceinline__ uint64_t same_key_lanes(int key, uint64_t active, int nbits) {
+  // one key in the whole wave (sorted ids): one ballot
+  const int k0 = __builtin_amdgcn_readfirstlane(key);
+  if (__ballot(key == k0) == ~0ull) return active;
+  // else the lanes whose key agrees with this lane's in every one of its nbits
+  // bits: one ballot per bit, no loop over the distinct keys of the wave
+  uint64_t m = active;
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (key >> b) & 1;
+    const uint64_t on = __ballot(bit);
+    m &= bit ? on : ~on;
   }
-  return mine;
+  return m;
 }
 
 __global__ __launch_bounds__(1024) void seg_small_kernel(
@@ -242,6 +245,7 @@ __global__ __launch_bounds__(1024) void seg_small_kernel(
   const int K1 = n_keys + 1;
   const int chunks = (n + 63) / 64;
   const int rounds = (n + 1023) / 1024;
+  const int nbits = 32 - __clz(n_keys);   // keys 0..n_keys (n_keys: ids out of range)
   {  // all id loads in flight at once, then into LDS
     int32_t v[SEG_SMALL_N / 1024];
 #pragma unroll
@@ -295,7 +299,7 @@ __global__ __launch_bounds__(1024) void seg_small_kernel(
       if (sorted && t + 1 < n && s_ids[t + 1] < id) set_flag(status, LORA_FLAG_UNSORTED);
     }
     const uint64_t act = __ballot(in);
-    const uint64_t same = same_key_lanes(key, act);
+    const uint64_t same = same_key_lanes(key, act, nbits);
     // the lowest lane of each key group writes the chunk's count
     if (in && (same & ((1ull << lane) - 1)) == 0) s_hist[(t >> 6) * K1 + key] = __popcll(same);
   }
@@ -401,7 +405,7 @@ __global__ __launch_bounds__(1024) void seg_small_kernel(
       const int32_t id = s_ids[t];
       key = (id >= 0 && id < n_keys) ? id : n_keys;
     }
-    const uint64_t same = same_key_lanes(key, __ballot(in));
+    const uint64_t same = same_key_lanes(key, __ballot(in), nbits);
     if (!in) continue;
     const int pos = s_off[key] + s_hist[(t >> 6) * K1 + key] + __popcll(same & ((1ull << lane) - 1));
     perm[pos] = t;
