@@ -188,31 +188,119 @@ __device__ __forceinline__ int xm_chunks(int r, int cols, int use_b_off) {
 // waves of the first column half and the second set in the others; a K split
 // runs both sets over every row.  Called by every thread of the block after
 // the k loop, with the ring free; ends with a barrier (LDS free again).
-__device__ __forceinline__ void lora_expand(const GemmEpi& ep, char* X, int n0, int N, int wave,
-                                            int lane, bool glu1, const int (&ad)[4],
-                                            const int (&vrow)[4], f32x16 (&acc)[4][NJ]) {
-  const int wm = wave / NWN, wn = wave % NWN;
-  const int m_l = lane & 31, half = lane >> 5;
-  int* s_ad = (int*)(X + X_TAB_OFF);   // adapter of each row (-1: none)
-  int* s_rid = s_ad + GBM;             // run of each row (-1: none)
-  int* s_vrow = s_rid + GBM;           // vector row of each row
-  int* s_rad = s_vrow + GBM;           // adapter of each run
-  int* s_rank = s_rad + GBM;           // [2][runs] rank per set
-  int64_t* s_moff = (int64_t*)(s_rank + 2 * GBM);   // [2][runs] factor offset per set
-  int* s_wc = (int*)(s_moff + 2 * GBM);             // runs started per 64 rows
-  static_assert(6 * GBM * 4 + 2 * GBM * 8 + 64 <= X_LDS - X_TAB_OFF, "expand tables");
+// LDS barrier without a wait on vector memory (DMA of operand stages may be
+// in flight): LDS writes before it are visible to every wave after it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
+// Expand tables in the LDS above the operand ring (untouched by the k loop).
+struct XTabs {
+  int* ad;        // adapter of each row (-1: none)
+  int* rid;       // run of each row (-1: none)
+  int* vrow;      // vector row of each row
+  int* rad;       // adapter of each run
+  int* rank;      // [2][runs] rank per set
+  int64_t* moff;  // [2][runs] factor offset per set
+  int* wc;        // runs started per 64 rows
+};
+__device__ __forceinline__ XTabs x_tabs(char* X) {
+  XTabs t;
+  t.ad = (int*)(X + X_TAB_OFF);
+  t.rid = t.ad + GBM;
+  t.vrow = t.rid + GBM;
+  t.rad = t.vrow + GBM;
+  t.rank = t.rad + GBM;
+  t.moff = (int64_t*)(t.rank + 2 * GBM);
+  t.wc = (int*)(t.moff + 2 * GBM);
+  return t;
+}
+static_assert(6 * GBM * 4 + 2 * GBM * 8 + 64 <= X_LDS - X_TAB_OFF, "expand tables");
+
+struct XDesc {
+  int rank;
+  int64_t moff;
+};
+
+__device__ __forceinline__ int x_passes(const GemmEpi& ep, bool glu1) {
+  return ((glu1 || ep.k_split > 0) && ep.vec2) ? 2 : 1;
+}
+
+// Before the k loop (the row metadata has landed with the first stage): the
+// tile's rows in runs of one adapter (a row starts a run when its adapter
+// differs from the previous row's), and the run descriptors of both LoRA sets
+// loaded into registers, one per thread (passes * runs <= 512), so that they
+// land during the k loop.  Returns the number of runs.
+__device__ __forceinline__ int expand_prep(const GemmEpi& ep, char* X, int wave, int lane,
+                                           bool glu1, const int (&ad)[4], const int (&vrow)[4],
+                                           XDesc& dk) {
+  const XTabs tb = x_tabs(X);
+  const int wm = wave / NWN, wn = wave % NWN;
   if (wn == 0 && lane < 32) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = wm * 128 + i * 32 + lane;
-      s_ad[row] = ad[i];
-      s_vrow[row] = ad[i] >= 0 ? vrow[i] : 0;   // rows without an adapter read row 0 (unused)
+      tb.ad[row] = ad[i];
+      tb.vrow[row] = ad[i] >= 0 ? vrow[i] : 0;   // rows without an adapter read row 0 (unused)
     }
   }
-  __syncthreads();
+  lds_barrier();
+  const int trow = wave * 64 + lane;   // rows 0..255 in waves 0..3
+  const int a_t = wave < GBM / 64 ? tb.ad[trow] : -1;
+  const int a_p = (wave < GBM / 64 && trow > 0) ? tb.ad[trow - 1] : -1;
+  const bool start = a_t >= 0 && a_t != a_p;
+  const uint64_t bal = __ballot(start);
+  const int incl = __popcll(bal & ((2ull << lane) - 1));
+  if (wave < GBM / 64 && lane == 0) tb.wc[wave] = __popcll(bal);
+  lds_barrier();
+  int n_runs = 0, before = 0;
+#pragma unroll
+  for (int w = 0; w < GBM / 64; ++w) {
+    const int c = tb.wc[w];
+    if (w < wave) before += c;
+    n_runs += c;
+  }
+  if (wave < GBM / 64) {
+    tb.rid[trow] = a_t >= 0 ? before + incl - 1 : -1;
+    if (start) tb.rad[before + incl - 1] = a_t;
+  }
+  lds_barrier();
+  dk.rank = 0;
+  dk.moff = 0;
+  const int k = threadIdx.x;
+  if (k < x_passes(ep, glu1) * n_runs) {
+    const int p = k >= n_runs, kk = k - p * n_runs;
+    const lora_adapter_desc d = (p ? ep.desc2 : ep.desc)[tb.rad[kk]];
+    dk.rank = d.rank;
+    dk.moff = ep.use_b_off ? d.b_off : d.a_off;
+  }
+  return n_runs;
+}
 
-  const int passes = ((glu1 || ep.k_split > 0) && ep.vec2) ? 2 : 1;
+// Fused LoRA expand, staged through LDS.  Every row m of the tile owned by
+// adapter a gets (s_a u_m) . M_a^T added to its accumulators: one extra MFMA
+// K-slab of depth r_a per plane (the scaled vector is stored as bf16 hi and lo
+// planes, so the slab keeps ~16 significant bits; M_a is bf16-exact).  With
+// M_a = B_a (use_b_off = 1) a staged row is one column's r_a ranks; with M_a =
+// A_a^T (use_b_off = 0) A_a's rows are staged over the tile's columns and read
+// back transposed, 8 consecutive ranks of one column per lane.
+//
+// Per LoRA set (a pass), the tile's vector rows and the factor blocks of a
+// batch of runs move to LDS in one round of LDS-DMA, and every wave then runs
+// its MFMAs from LDS: one memory round trip per pass and batch, where loading
+// operands per adapter and 16-rank slice paid one per slice.  A run's MFMAs
+// run only for the 32-row tiles holding rows of it.  glu = 1 tiles run the
+// first set in the waves of the first column half and the second set in the
+// others; a K split runs both sets over every row.  Called by every thread of
+// the block after the k loop, with the ring free, and with the tables of
+// expand_prep; ends with a barrier (LDS free again).
+__device__ __forceinline__ void lora_expand(const GemmEpi& ep, char* X, int n0, int N, int wave,
+                                            int lane, bool glu1, int n_runs, const XDesc& dk,
+                                            f32x16 (&acc)[4][NJ]) {
+  const int wm = wave / NWN, wn = wave % NWN;
+  const int m_l = lane & 31, half = lane >> 5;
+  const XTabs tb = x_tabs(X);
+  const int passes = x_passes(ep, glu1);
   const int cols = glu1 ? GBN / 2 : GBN;
   const int wn_eff = glu1 ? wn % (NWN / 2) : wn;
   const int vch = ep.vec_ld / 8;
@@ -228,43 +316,23 @@ __device__ __forceinline__ void lora_expand(const GemmEpi& ep, char* X, int n0, 
         int c = (q & 7) ^ (row & 7);
         if (c >= vch) c = 0;   // past the vector width: any chunk of the row (unused)
         const uint16_t* src =
-            vec + (pl ? ep.vec_plane : 0) + (int64_t)s_vrow[row] * ep.vec_ld + c * 8;
+            vec + (pl ? ep.vec_plane : 0) + (int64_t)tb.vrow[row] * ep.vec_ld + c * 8;
         dma16v(src, lds_addr((const uint4*)(X + pl * XV_PLANE + (q - lane) * 16)));
       }
   };
-  dma_vec(ep.vec);
-
-  // runs: a row starts one when its adapter differs from the previous row's
-  const int trow = wave * 64 + lane;   // rows 0..255 in waves 0..3
-  const int a_t = wave < GBM / 64 ? s_ad[trow] : -1;
-  const int a_p = (wave < GBM / 64 && trow > 0) ? s_ad[trow - 1] : -1;
-  const bool start = a_t >= 0 && a_t != a_p;
-  const uint64_t bal = __ballot(start);
-  const int incl = __popcll(bal & ((2ull << lane) - 1));
-  if (wave < GBM / 64 && lane == 0) s_wc[wave] = __popcll(bal);
-  __syncthreads();
-  int n_runs = 0, before = 0;
-#pragma unroll
-  for (int w = 0; w < GBM / 64; ++w) {
-    const int c = s_wc[w];
-    if (w < wave) before += c;
-    n_runs += c;
-  }
-  if (wave < GBM / 64) {
-    s_rid[trow] = a_t >= 0 ? before + incl - 1 : -1;
-    if (start) s_rad[before + incl - 1] = a_t;
-  }
-  __syncthreads();
-  for (int k = threadIdx.x; k < passes * n_runs; k += GTHREADS) {
-    const int p = k >= n_runs, kk = k - p * n_runs;
-    const lora_adapter_desc d = (p ? ep.desc2 : ep.desc)[s_rad[kk]];
-    s_rank[p * GBM + kk] = d.rank;
-    s_moff[p * GBM + kk] = ep.use_b_off ? d.b_off : d.a_off;
+  if (n_runs > 0) dma_vec(ep.vec);
+  {
+    const int k = threadIdx.x;
+    if (k < passes * n_runs) {
+      const int p = k >= n_runs, kk = k - p * n_runs;
+      tb.rank[p * GBM + kk] = dk.rank;
+      tb.moff[p * GBM + kk] = dk.moff;
+    }
   }
   int rid[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) rid[i] = s_rid[wm * 128 + i * 32 + m_l];
-  __syncthreads();
+  for (int i = 0; i < 4; ++i) rid[i] = tb.rid[wm * 128 + i * 32 + m_l];
+  lds_barrier();
 
   const uint4* XV = (const uint4*)X;
   const uint4* XL = (const uint4*)(X + XV_PLANE);
@@ -272,8 +340,8 @@ __device__ __forceinline__ void lora_expand(const GemmEpi& ep, char* X, int n0, 
 #pragma unroll 1
   for (int p = 0; p < passes; ++p) {
     const uint16_t* lmat = p ? ep.lmat2 : ep.lmat;
-    const int* rk = s_rank + p * GBM;
-    const int64_t* mo = s_moff + p * GBM;
+    const int* rk = tb.rank + p * GBM;
+    const int64_t* mo = tb.moff + p * GBM;
     const bool mine = !glu1 || ((wn >= NWN / 2) == (p == 1));
     if (p > 0 && n_runs > 0) dma_vec(ep.vec2);
 #pragma unroll 1
@@ -382,10 +450,6 @@ __device__ __forceinline__ void lora_expand(const GemmEpi& ep, char* X, int n0, 
       __syncthreads();   // every wave is done with the batch (and the pass's vectors)
       k0 = k1;
     }
-  }
-  if (n_runs == 0) {   // no batch ran: the first pass's vector DMA lands before the LDS is reused
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
   }
 }
 
@@ -544,6 +608,16 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_nt_kernel(const uint16_t* __
     asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
   } else {
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  }
+
+  // LoRA expand tables (the row metadata has landed with stage 0)
+  int x_runs = 0;
+  XDesc x_dk{0, 0};
+  if (EPI == EPI_BF16 && ep.vec) {
+    int vrow[4];   // vector row of each fragment row: its C row, or its position
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vrow[i] = ep.vec_by_pos ? m0 + wm * 128 + i * 32 + m_l : tok[i];
+    x_runs = expand_prep(ep, (char*)g_stage, wave, lane, glu1, ad, vrow, x_dk);
   }
 
   const int frag_row = lane & 31;   // row within a 32-row MFMA tile
@@ -745,10 +819,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_nt_kernel(const uint16_t* __
     }
     __syncthreads();   // every wave is done reading the ring
     if (ep.vec) {
-      int vrow[4];   // vector row of each fragment row: its C row, or its position
-#pragma unroll
-      for (int i = 0; i < 4; ++i) vrow[i] = ep.vec_by_pos ? m0 + wm * 128 + i * 32 + m_l : tok[i];
-      lora_expand(ep, T, n0, N, wave, lane, glu1, ad, vrow, acc);
+      lora_expand(ep, T, n0, N, wave, lane, glu1, x_runs, x_dk, acc);
     }
     stage_rows();
 #pragma unroll
