@@ -440,7 +440,7 @@ lora_status mlp_backward(const mlp_shape* shape, const uint16_t* dy, const uint1
 #define LORA_TIMER_LOGPROB_FWD   1   /* lm_head GEMM with online logsumexp */
 #define LORA_TIMER_LOGPROB_BWD   2   /* logit recompute + dh GEMMs */
 #define LORA_TIMER_SHRINK        3
-#define LORA_TIMER_EXPAND        4
+#define LORA_TIMER_EXPAND        4   /* reserved: the expand runs inside the base GEMMs */
 #define LORA_TIMER_GRAD          5   /* dA / dB reductions */
 #define LORA_TIMER_ADAM          6
 #define LORA_TIMER_COUNT         7
