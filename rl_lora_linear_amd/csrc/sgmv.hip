@@ -185,25 +185,30 @@ __device__ __forceinline__ void shrink_tile(const uint16_t* __restrict__ in, int
   for (int st = 0; st < NST - 1; ++st) issue(st, min(st, KT - 1));
   wait_vm_barrier<(NST - 2) * PER_WAVE>();
 
-  f32x4 acc[2][NB];
+  // wave w: rows 16 (w & 1) .. + 15, and the 32-k blocks of parity w >> 1
+  // (blocks kp and kp + 2 of each 128-k stage), so each row has an even-block
+  // and an odd-block partial sum, added once at the end: the order of the
+  // 128-row tile, whichever tile height the batch size selects
+  f32x4 acc[NB];
 #pragma unroll
-  for (int g = 0; g < 2; ++g)
-#pragma unroll
-    for (int b = 0; b < NB; ++b) acc[g][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int b = 0; b < NB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int fr = lane & 15;
-  const int ch = 4 * wave + (lane >> 4);  // logical chunk of this lane's fragments
+  const int rh = wave & 1, kp = wave >> 1;
 
   for (int kt = 0; kt < KT; ++kt) {
     const int st = kt % NST;
     issue((kt + NST - 1) % NST, min(kt + NST - 1, KT - 1));
     const uint4* xt = lds + st * STAGE;
     const uint4* mt = xt + SH_XSLOTS;
-    if (kt * SH_KC + wave * 32 < K) {
-      bf16x8 xa[2], mb[NB];
 #pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        const int row = g * 16 + fr;
-        xa[g] = as_bf16x8(xt[row * 16 + (ch ^ (row & 15))]);
+    for (int bi = 0; bi < 2; ++bi) {
+      const int bb = kp + 2 * bi;              // 32-k block of the stage
+      if (kt * SH_KC + bb * 32 >= K) continue;
+      const int ch = 4 * bb + (lane >> 4);     // logical chunk of this lane's fragments
+      bf16x8 xa, mb[NB];
+      {
+        const int row = rh * 16 + fr;
+        xa = as_bf16x8(xt[row * 16 + (ch ^ (row & 15))]);
       }
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
@@ -222,26 +227,25 @@ __device__ __forceinline__ void shrink_tile(const uint16_t* __restrict__ in, int
         }
       }
 #pragma unroll
-      for (int g = 0; g < 2; ++g)
-#pragma unroll
-        for (int b = 0; b < NB; ++b) acc[g][b] = mfma16(xa[g], mb[b], acc[g][b]);
+      for (int b = 0; b < NB; ++b) acc[b] = mfma16(xa, mb[b], acc[b]);
     }
     wait_vm_barrier<(NST - 2) * PER_WAVE>();
   }
   asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
 
-  // cross-wave reduction in wave order; acc[g][b][i] = D[16g + 4*(lane/16) + i][16b + lane%16]
-  float* red = (float*)lds;  // [4][SH_TM][64]
+  // acc[b][i] = D[16 rh + 4 (lane / 16) + i][16 b + lane % 16], the kp partial
+  float* red = (float*)lds;  // [2][SH_TM][64]
 #pragma unroll
-  for (int g = 0; g < 2; ++g)
+  for (int b = 0; b < NB; ++b)
 #pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        red[(wave * SH_TM + g * 16 + 4 * (lane >> 4) + i) * 64 + b * 16 + (lane & 15)] = acc[g][b][i];
+    for (int i = 0; i < 4; ++i)
+      red[(kp * SH_TM + rh * 16 + 4 * (lane >> 4) + i) * 64 + b * 16 + (lane & 15)] = acc[b][i];
   __syncthreads();
   // tile ranks [c0, c0 + rr) scaled and split into the planes of dst
   auto emit = [&](uint16_t* __restrict__ dst, int c0, int rr, float sc) {
+    // the scaled value is rounded to fp32 before the hi/lo split (no product
+    // fused into the residual), in both tile heights alike
+#pragma clang fp contract(off)
     for (int e = tid; e < SH_TM * (r_max / 4); e += 256) {
       const int row = e / (r_max / 4), cg = (e % (r_max / 4)) * 4;
       if (row >= rows) continue;
@@ -255,8 +259,6 @@ __device__ __forceinline__ void shrink_tile(const uint16_t* __restrict__ in, int
         if (c < rr) {
           const int rc = c0 + c;
           sacc = red[(0 * SH_TM + row) * 64 + rc] + red[(1 * SH_TM + row) * 64 + rc];
-          sacc += red[(2 * SH_TM + row) * 64 + rc];
-          sacc += red[(3 * SH_TM + row) * 64 + rc];
         }
         v[q] = sc_row * sacc;
       }
@@ -358,11 +360,16 @@ __device__ __forceinline__ void shrink_tall_tile(const uint16_t* __restrict__ in
   for (int st = 0; st < NST - 1; ++st) issue(st, min(st, KT - 1));
   wait_vm_barrier<(NST - 2) * PER_WAVE>();
 
-  f32x4 acc[2][NB];
+  // one partial sum per parity of the 32-k block (the stage's slice sl), added
+  // once at the end: the order of the 32-row tile, so a row's u has the same
+  // bits whichever tile height the batch size selects
+  f32x4 acc[2][2][NB];
 #pragma unroll
-  for (int g = 0; g < 2; ++g)
+  for (int h = 0; h < 2; ++h)
 #pragma unroll
-    for (int b = 0; b < NB; ++b) acc[g][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) acc[h][g][b] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int fr = lane & 15;
   const int q = (lane >> 2) & 3, j = lane & 3;
 
@@ -398,13 +405,14 @@ __device__ __forceinline__ void shrink_tall_tile(const uint16_t* __restrict__ in
 #pragma unroll
       for (int g = 0; g < 2; ++g)
 #pragma unroll
-        for (int b = 0; b < NB; ++b) acc[g][b] = mfma16(xa[g], mb[b], acc[g][b]);
+        for (int b = 0; b < NB; ++b) acc[sl][g][b] = mfma16(xa[g], mb[b], acc[sl][g][b]);
     }
     wait_vm_barrier<(NST - 2) * PER_WAVE>();
   }
   asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
 
-  // acc[g][b][i] = D[32 wave + 16 g + 4 (lane / 16) + i][16 b + lane % 16]
+  // acc[h][g][b][i] = D[32 wave + 16 g + 4 (lane / 16) + i][16 b + lane % 16],
+  // the even-block (h = 0) and odd-block partial sums
   float* red = (float*)lds;  // [ST_TM][64]
 #pragma unroll
   for (int g = 0; g < 2; ++g)
@@ -412,10 +420,14 @@ __device__ __forceinline__ void shrink_tall_tile(const uint16_t* __restrict__ in
     for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        red[(wave * 32 + g * 16 + 4 * (lane >> 4) + i) * 64 + b * 16 + (lane & 15)] = acc[g][b][i];
+        red[(wave * 32 + g * 16 + 4 * (lane >> 4) + i) * 64 + b * 16 + (lane & 15)] =
+            acc[0][g][b][i] + acc[1][g][b][i];
   __syncthreads();
   // tile ranks [c0, c0 + rr) scaled and split into the planes of dst
   auto emit = [&](uint16_t* __restrict__ dst, int c0, int rr, float sc) {
+    // the scaled value is rounded to fp32 before the hi/lo split (no product
+    // fused into the residual), in both tile heights alike
+#pragma clang fp contract(off)
     for (int e = tid; e < ST_TM * (r_max / 4); e += 256) {
       const int row = e / (r_max / 4), cg = (e % (r_max / 4)) * 4;
       if (row >= rows) continue;
