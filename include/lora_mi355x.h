@@ -80,6 +80,7 @@ typedef enum {
 #define LORA_FLAG_UNSORTED     0x2  /* ids decrease although LORA_IDS_SORTED was promised */
 #define LORA_FLAG_TARGET_RANGE 0x4  /* a target token id outside [0, vocab) */
 #define LORA_FLAG_BAD_DESC     0x8  /* an adapter descriptor with bad rank, offset or alignment */
+#define LORA_FLAG_NONFINITE_GRAD 0x10 /* AdamW skipped elements whose gradient was NaN or Inf */
 
 typedef enum { LORA_IDS_SORTED = 0, LORA_IDS_INTERLEAVED = 1 } lora_id_order;
 
@@ -268,10 +269,15 @@ lora_status loss_grad(int32_t kind, int64_t n, const float* logprobs, const floa
  *   p -= (lr / (1 - b1^step)) m / (sqrt(v) / sqrt(1 - b2^step) + eps)
  * step >= 1 is this adapter's own counter (bias factors are computed on the
  * host in double).  p, m, v updated in place; g read only.  p_bf16 (nullable)
- * receives bf16(p) -- the bf16 copy the layer kernels read.  n >= 0. */
+ * receives bf16(p) -- the bf16 copy the layer kernels read.  n >= 0.
+ * Non-finite gradients are contained (the pages give no rule for them; this
+ * is the plain reading of skipping a bad update): an element whose g is NaN or
+ * +-Inf is not updated -- its p, m, v and bf16 copy keep their values -- and
+ * LORA_FLAG_NONFINITE_GRAD is OR-ed into *status (a device int32, nullable:
+ * then the skip is silent).  Finite elements update exactly as above. */
 lora_status adam_step(int64_t n, float* p, const float* g, float* m, float* v, int64_t step,
                       float lr, float beta1, float beta2, float eps, float weight_decay,
-                      uint16_t* p_bf16, void* stream);
+                      uint16_t* p_bf16, int32_t* status, void* stream);
 
 /* Several adapters' AdamW steps in one launch: segment i updates elements
  * [offset, offset + count) of p, g, m, v (and p_bf16) exactly as adam_step
@@ -279,11 +285,12 @@ lora_status adam_step(int64_t n, float* p, const float* g, float* m, float* v, i
  * per-element arithmetic, so results are bitwise those of one adam_step call
  * per segment).  segs is a HOST array; segments must not overlap.  Each
  * adapter keeps its own step counter (OpenTinker, "3 Approach": optimizer
- * state local to each adapter).  n_seg >= 0. */
+ * state local to each adapter).  n_seg >= 0.  Non-finite gradient elements
+ * are skipped and flagged in *status (nullable) as in adam_step. */
 typedef struct { int64_t offset; int64_t count; int64_t step; } adam_segment;
 lora_status adam_step_multi(int32_t n_seg, const adam_segment* segs, float* p, const float* g,
                             float* m, float* v, float lr, float beta1, float beta2, float eps,
-                            float weight_decay, uint16_t* p_bf16, void* stream);
+                            float weight_decay, uint16_t* p_bf16, int32_t* status, void* stream);
 
 /* ---- MLP glue --------------------------------------------------------- */
 

@@ -454,7 +454,7 @@ lora_status loss_grad(int32_t kind, int64_t n, const float* logprobs, const floa
 // ------------------------------------------------------------------ Adam
 lora_status adam_step(int64_t n, float* p, const float* g, float* m, float* v, int64_t step,
                       float lr, float beta1, float beta2, float eps, float weight_decay,
-                      uint16_t* p_bf16, void* stream) {
+                      uint16_t* p_bf16, int32_t* status, void* stream) {
   LORA_ARG_CHECK(n >= 0, "n must be >= 0");
   LORA_ARG_CHECK(n == 0 || (p && g && m && v), "p/g/m/v NULL");
   LORA_ARG_CHECK(step >= 1, "step must be >= 1 (1-based per-adapter counter)");
@@ -466,14 +466,15 @@ lora_status adam_step(int64_t n, float* p, const float* g, float* m, float* v, i
   hipStream_t s = S(stream);
   timer_begin(LORA_TIMER_ADAM, s);
   TRY(launch_adam(n, p, g, m, v, lr, beta1, beta2, eps, weight_decay, step_size, inv_sqrt_bc2,
-                  p_bf16, s));
+                  p_bf16, status, s));
   timer_end(LORA_TIMER_ADAM, s);
   return LORA_OK;
 }
 
 lora_status adam_step_multi(int32_t n_seg, const adam_segment* segs, float* p, const float* g,
                             float* m, float* v, float lr, float beta1, float beta2, float eps,
-                            float weight_decay, uint16_t* p_bf16, void* stream) {
+                            float weight_decay, uint16_t* p_bf16, int32_t* status,
+                            void* stream) {
   LORA_ARG_CHECK(n_seg >= 0, "n_seg must be >= 0");
   if (n_seg == 0) return LORA_OK;
   LORA_ARG_CHECK(segs != nullptr, "segs is NULL");
@@ -494,7 +495,7 @@ lora_status adam_step_multi(int32_t n_seg, const adam_segment* segs, float* p, c
   hipStream_t s = S(stream);
   timer_begin(LORA_TIMER_ADAM, s);
   TRY(launch_adam_multi(n_seg, off.data(), cnt.data(), ss.data(), ib.data(), p, g, m, v, lr, beta1,
-                        beta2, eps, weight_decay, p_bf16, s));
+                        beta2, eps, weight_decay, p_bf16, status, s));
   timer_end(LORA_TIMER_ADAM, s);
   return LORA_OK;
 }

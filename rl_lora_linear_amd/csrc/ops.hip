@@ -146,14 +146,25 @@ __global__ __launch_bounds__(256) void loss_sum_kernel(const double* __restrict_
 }
 
 // ------------------------------------------------------------------ AdamW
+// An element whose gradient is not finite is not updated (p, m, v keep their
+// values, so a NaN or Inf cannot spread into the state); `bad` records it.
 __device__ __forceinline__ void adam_one(float& p, float g, float& m, float& v, float lr,
                                          float b1, float b2, float eps, float wd, float step_size,
-                                         float inv_sqrt_bc2) {
+                                         float inv_sqrt_bc2, bool& bad) {
+  if (!__builtin_isfinite(g)) {
+    bad = true;
+    return;
+  }
   m = b1 * m + (1.f - b1) * g;
   v = b2 * v + (1.f - b2) * g * g;
   p = p - lr * wd * p;
   const float denom = __fsqrt_rn(v) * inv_sqrt_bc2 + eps;
   p = p - step_size * __fdiv_rn(m, denom);
+}
+
+// one atomic per wave that skipped an element
+__device__ __forceinline__ void report_nonfinite(bool bad, int32_t* status) {
+  if (status && __any(bad) && (threadIdx.x & 63) == 0) atomicOr(status, LORA_FLAG_NONFINITE_GRAD);
 }
 
 template <bool VEC>
@@ -162,18 +173,20 @@ __global__ __launch_bounds__(256) void adam_kernel(int64_t n, float* __restrict_
                                                    float* __restrict__ m, float* __restrict__ v,
                                                    float lr, float b1, float b2, float eps,
                                                    float wd, float step_size, float inv_sqrt_bc2,
-                                                   uint16_t* __restrict__ pb) {
+                                                   uint16_t* __restrict__ pb,
+                                                   int32_t* __restrict__ status) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  bool bad = false;
   if (VEC) {
     const int64_t n4 = n / 4;
     for (int64_t i = i0; i < n4; i += stride) {
       float4 pp = ((float4*)p)[i], mm = ((float4*)m)[i], vv = ((float4*)v)[i];
       const float4 gg = ((const float4*)g)[i];
-      adam_one(pp.x, gg.x, mm.x, vv.x, lr, b1, b2, eps, wd, step_size, inv_sqrt_bc2);
-      adam_one(pp.y, gg.y, mm.y, vv.y, lr, b1, b2, eps, wd, step_size, inv_sqrt_bc2);
-      adam_one(pp.z, gg.z, mm.z, vv.z, lr, b1, b2, eps, wd, step_size, inv_sqrt_bc2);
-      adam_one(pp.w, gg.w, mm.w, vv.w, lr, b1, b2, eps, wd, step_size, inv_sqrt_bc2);
+      adam_one(pp.x, gg.x, mm.x, vv.x, lr, b1, b2, eps, wd, step_size, inv_sqrt_bc2, bad);
+      adam_one(pp.y, gg.y, mm.y, vv.y, lr, b1, b2, eps, wd, step_size, inv_sqrt_bc2, bad);
+      adam_one(pp.z, gg.z, mm.z, vv.z, lr, b1, b2, eps, wd, step_size, inv_sqrt_bc2, bad);
+      adam_one(pp.w, gg.w, mm.w, vv.w, lr, b1, b2, eps, wd, step_size, inv_sqrt_bc2, bad);
       ((float4*)p)[i] = pp;
       ((float4*)m)[i] = mm;
       ((float4*)v)[i] = vv;
@@ -181,18 +194,19 @@ __global__ __launch_bounds__(256) void adam_kernel(int64_t n, float* __restrict_
     }
     for (int64_t i = n4 * 4 + i0; i < n; i += stride) {
       float pp = p[i], mm = m[i], vv = v[i];
-      adam_one(pp, g[i], mm, vv, lr, b1, b2, eps, wd, step_size, inv_sqrt_bc2);
+      adam_one(pp, g[i], mm, vv, lr, b1, b2, eps, wd, step_size, inv_sqrt_bc2, bad);
       p[i] = pp; m[i] = mm; v[i] = vv;
       if (pb) pb[i] = f2bf(pp);
     }
   } else {
     for (int64_t i = i0; i < n; i += stride) {
       float pp = p[i], mm = m[i], vv = v[i];
-      adam_one(pp, g[i], mm, vv, lr, b1, b2, eps, wd, step_size, inv_sqrt_bc2);
+      adam_one(pp, g[i], mm, vv, lr, b1, b2, eps, wd, step_size, inv_sqrt_bc2, bad);
       p[i] = pp; m[i] = mm; v[i] = vv;
       if (pb) pb[i] = f2bf(pp);
     }
   }
+  report_nonfinite(bad, status);
 }
 
 // Batched AdamW: up to ADAM_SEGS segments per launch, described in the kernel
@@ -215,8 +229,10 @@ __global__ __launch_bounds__(256) void adam_multi_kernel(AdamSegs sg, float* __r
                                                          float* __restrict__ m,
                                                          float* __restrict__ v, float lr, float b1,
                                                          float b2, float eps, float wd,
-                                                         uint16_t* __restrict__ pb) {
+                                                         uint16_t* __restrict__ pb,
+                                                         int32_t* __restrict__ status) {
   const int b = blockIdx.x;
+  bool bad = false;
   int s = 0;
   while (s + 1 < sg.n && sg.blk0[s + 1] <= b) ++s;
   const int64_t base = sg.off[s];
@@ -232,10 +248,10 @@ __global__ __launch_bounds__(256) void adam_multi_kernel(AdamSegs sg, float* __r
         const int64_t i = (base + e) / 4;
         float4 pp = ((float4*)p)[i], mm = ((float4*)m)[i], vv = ((float4*)v)[i];
         const float4 gg = ((const float4*)g)[i];
-        adam_one(pp.x, gg.x, mm.x, vv.x, lr, b1, b2, eps, wd, ss, ib);
-        adam_one(pp.y, gg.y, mm.y, vv.y, lr, b1, b2, eps, wd, ss, ib);
-        adam_one(pp.z, gg.z, mm.z, vv.z, lr, b1, b2, eps, wd, ss, ib);
-        adam_one(pp.w, gg.w, mm.w, vv.w, lr, b1, b2, eps, wd, ss, ib);
+        adam_one(pp.x, gg.x, mm.x, vv.x, lr, b1, b2, eps, wd, ss, ib, bad);
+        adam_one(pp.y, gg.y, mm.y, vv.y, lr, b1, b2, eps, wd, ss, ib, bad);
+        adam_one(pp.z, gg.z, mm.z, vv.z, lr, b1, b2, eps, wd, ss, ib, bad);
+        adam_one(pp.w, gg.w, mm.w, vv.w, lr, b1, b2, eps, wd, ss, ib, bad);
         ((float4*)p)[i] = pp;
         ((float4*)m)[i] = mm;
         ((float4*)v)[i] = vv;
@@ -250,7 +266,7 @@ __global__ __launch_bounds__(256) void adam_multi_kernel(AdamSegs sg, float* __r
       } else {
         for (int64_t k = e; k < n && k < e + 4; ++k) {
           float pp = p[base + k], mm = m[base + k], vv = v[base + k];
-          adam_one(pp, g[base + k], mm, vv, lr, b1, b2, eps, wd, ss, ib);
+          adam_one(pp, g[base + k], mm, vv, lr, b1, b2, eps, wd, ss, ib, bad);
           p[base + k] = pp; m[base + k] = mm; v[base + k] = vv;
           if (pb) pb[base + k] = f2bf(pp);
         }
@@ -259,11 +275,12 @@ __global__ __launch_bounds__(256) void adam_multi_kernel(AdamSegs sg, float* __r
   } else {
     for (int64_t k = e0 + threadIdx.x; k < min(n, e0 + ADAM_BLOCK_ELEMS); k += 256) {
       float pp = p[base + k], mm = m[base + k], vv = v[base + k];
-      adam_one(pp, g[base + k], mm, vv, lr, b1, b2, eps, wd, ss, ib);
+      adam_one(pp, g[base + k], mm, vv, lr, b1, b2, eps, wd, ss, ib, bad);
       p[base + k] = pp; m[base + k] = mm; v[base + k] = vv;
       if (pb) pb[base + k] = f2bf(pp);
     }
   }
+  report_nonfinite(bad, status);
 }
 
 // ------------------------------------------------------------------ SwiGLU
@@ -382,24 +399,25 @@ lora_status launch_loss(int kind, int64_t n, const float* logp, const float* w, 
 
 lora_status launch_adam(int64_t n, float* p, const float* g, float* m, float* v, float lr,
                         float beta1, float beta2, float eps, float wd, float step_size,
-                        float inv_sqrt_bc2, uint16_t* p_bf16, hipStream_t s) {
+                        float inv_sqrt_bc2, uint16_t* p_bf16, int32_t* status, hipStream_t s) {
   if (n <= 0) return LORA_OK;
   const bool vec = ((uintptr_t)p | (uintptr_t)g | (uintptr_t)m | (uintptr_t)v) % 16 == 0 &&
                    (p_bf16 == nullptr || (uintptr_t)p_bf16 % 8 == 0);
   const unsigned grid = grid_for(vec ? n / 4 : n, 256, 2048);
   if (vec)
     hipLaunchKernelGGL(adam_kernel<true>, dim3(grid), dim3(256), 0, s, n, p, g, m, v, lr, beta1,
-                       beta2, eps, wd, step_size, inv_sqrt_bc2, p_bf16);
+                       beta2, eps, wd, step_size, inv_sqrt_bc2, p_bf16, status);
   else
     hipLaunchKernelGGL(adam_kernel<false>, dim3(grid), dim3(256), 0, s, n, p, g, m, v, lr, beta1,
-                       beta2, eps, wd, step_size, inv_sqrt_bc2, p_bf16);
+                       beta2, eps, wd, step_size, inv_sqrt_bc2, p_bf16, status);
   return launch_check("adam");
 }
 
 lora_status launch_adam_multi(int n_seg, const int64_t* off, const int64_t* cnt,
                               const float* step_size, const float* inv_sqrt_bc2, float* p,
                               const float* g, float* m, float* v, float lr, float beta1,
-                              float beta2, float eps, float wd, uint16_t* p_bf16, hipStream_t s) {
+                              float beta2, float eps, float wd, uint16_t* p_bf16, int32_t* status,
+                              hipStream_t s) {
   for (int s0 = 0; s0 < n_seg; s0 += ADAM_SEGS) {
     AdamSegs sg{};
     sg.n = std::min(ADAM_SEGS, n_seg - s0);
@@ -415,7 +433,7 @@ lora_status launch_adam_multi(int n_seg, const int64_t* off, const int64_t* cnt,
     sg.blk0[sg.n] = blocks;
     if (blocks == 0) continue;
     hipLaunchKernelGGL(adam_multi_kernel, dim3(blocks), dim3(256), 0, s, sg, p, g, m, v, lr, beta1,
-                       beta2, eps, wd, p_bf16);
+                       beta2, eps, wd, p_bf16, status);
     lora_status st = launch_check("adam_multi");
     if (st) return st;
   }

@@ -122,11 +122,12 @@ lora_status launch_loss(int kind, int64_t n, const float* logp, const float* w, 
                         double* partial, float* loss_out, float* dlogp, hipStream_t s);
 lora_status launch_adam(int64_t n, float* p, const float* g, float* m, float* v, float lr,
                         float beta1, float beta2, float eps, float wd, float step_size,
-                        float inv_sqrt_bc2, uint16_t* p_bf16, hipStream_t s);
+                        float inv_sqrt_bc2, uint16_t* p_bf16, int32_t* status, hipStream_t s);
 lora_status launch_adam_multi(int n_seg, const int64_t* off, const int64_t* cnt,
                               const float* step_size, const float* inv_sqrt_bc2, float* p,
                               const float* g, float* m, float* v, float lr, float beta1,
-                              float beta2, float eps, float wd, uint16_t* p_bf16, hipStream_t s);
+                              float beta2, float eps, float wd, uint16_t* p_bf16, int32_t* status,
+                              hipStream_t s);
 lora_status launch_swiglu_fwd(int64_t n, const uint16_t* g, const uint16_t* u, uint16_t* h,
                               hipStream_t s);
 lora_status launch_swiglu_bwd(int64_t n, const uint16_t* dh, const uint16_t* g,

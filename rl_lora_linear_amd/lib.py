@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(_HERE, "liblora_mi355x.so")
 # status codes and flags (include/lora_mi355x.h)
 LORA_OK, LORA_E_INVALID_ARG, LORA_E_UNSUPPORTED, LORA_E_WORKSPACE, LORA_E_HIP, LORA_E_DEVICE_CHECK = range(6)
 FLAG_ID_RANGE, FLAG_UNSORTED, FLAG_TARGET_RANGE, FLAG_BAD_DESC = 0x1, 0x2, 0x4, 0x8
+FLAG_NONFINITE_GRAD = 0x10
 IDS_SORTED, IDS_INTERLEAVED = 0, 1
 LOSS_CROSS_ENTROPY, LOSS_IMPORTANCE_SAMPLING, LOSS_PPO, LOSS_CUSTOM = range(4)
 TIMER_BASE_GEMM, TIMER_LOGPROB_FWD, TIMER_LOGPROB_BWD, TIMER_SHRINK, TIMER_EXPAND, TIMER_GRAD, TIMER_ADAM = range(7)
@@ -105,9 +106,9 @@ def _load() -> ctypes.CDLL:
         "loss_grad_workspace_bytes": (_SZ, [_I64]),
         "loss_grad": (_I32, [_I32, _I64, _P, _P, _P, _P, _P, ctypes.POINTER(LossConfig), _P, _P, _P,
                              _SZ, _P]),
-        "adam_step": (_I32, [_I64, _P, _P, _P, _P, _I64, _F, _F, _F, _F, _F, _P, _P]),
+        "adam_step": (_I32, [_I64, _P, _P, _P, _P, _I64, _F, _F, _F, _F, _F, _P, _P, _P]),
         "adam_step_multi": (_I32, [_I32, ctypes.POINTER(AdamSegment), _P, _P, _P, _P, _F, _F, _F, _F,
-                                   _F, _P, _P]),
+                                   _F, _P, _P, _P]),
         "swiglu_forward": (_I32, [_I64, _P, _P, _P, _P]),
         "bf16_add": (_I32, [_I64, _P, _P, _P, _P]),
         "moe_route": (_I32, [_I64, _I32, _I32, _P, _P, _P, _P]),
@@ -257,13 +258,15 @@ def loss_grad(kind, logprobs, weights, advantages, sampler_logprobs, custom_g, c
 
 
 def adam_step(p, g, m, v, step, lr, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0,
-              p_bf16=None, stream=None):
+              p_bf16=None, status=None, stream=None):
+    """status: optional device int32 tensor; FLAG_NONFINITE_GRAD is OR-ed into it
+    when elements with a NaN or Inf gradient were skipped."""
     _check(LIB.adam_step(p.numel(), _ptr(p), _ptr(g), _ptr(m), _ptr(v), int(step), lr, beta1,
-                         beta2, eps, weight_decay, _ptr(p_bf16), _stream(stream)))
+                         beta2, eps, weight_decay, _ptr(p_bf16), _ptr(status), _stream(stream)))
 
 
 def adam_step_multi(segments, p, g, m, v, lr, beta1=0.9, beta2=0.999, eps=1e-8,
-                    weight_decay=0.0, p_bf16=None, stream=None):
+                    weight_decay=0.0, p_bf16=None, status=None, stream=None):
     """segments: list of (offset, count, step) into the flat p/g/m/v buffers."""
     n = p.numel()
     for t in (g, m, v):
@@ -276,7 +279,8 @@ def adam_step_multi(segments, p, g, m, v, lr, beta1=0.9, beta2=0.999, eps=1e-8,
             raise LoraError(LORA_E_INVALID_ARG, f"segment ({o}, {c}) outside a buffer of {n}")
     arr = (AdamSegment * max(1, len(segments)))(*[AdamSegment(int(o), int(c), int(t)) for o, c, t in segments])
     _check(LIB.adam_step_multi(len(segments), arr, _ptr(p), _ptr(g), _ptr(m), _ptr(v), lr, beta1,
-                               beta2, eps, weight_decay, _ptr(p_bf16), _stream(stream)))
+                               beta2, eps, weight_decay, _ptr(p_bf16), _ptr(status),
+                               _stream(stream)))
 
 
 def bf16_add(a, b, out, stream=None):

@@ -226,3 +226,43 @@ def test_swiglu_parity():
     L.swiglu_backward(d, g, u, dg, du)
     rg, ru = OM.swiglu_backward(df, gf, uf)
     assert rel_err(f64_of(dg), rg) < TOL_BF16 and rel_err(f64_of(du), ru) < TOL_BF16
+
+
+@pytest.mark.parametrize("multi", [False, True])
+def test_adam_contains_nonfinite_gradients(multi):
+    """Elements whose gradient is NaN or +-Inf keep p, m, v (bit for bit) and
+    the bf16 copy of p; the status word gets FLAG_NONFINITE_GRAD; the other
+    elements match the oracle's step.  Finite gradients leave the status 0."""
+    rng = np.random.default_rng(9)
+    n = 1003
+    p0 = rng.standard_normal(n).astype(np.float32)
+    m0 = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+    v0 = (rng.random(n) * 1e-6).astype(np.float32)
+    g = (rng.standard_normal(n) * 1e-2).astype(np.float32)
+    bad = np.array([0, 5, 333, 502, 1002])
+    g[bad] = [np.nan, np.inf, -np.inf, np.nan, np.inf]
+    segs = [(0, 500, 3), (500, n - 500, 7)] if multi else [(0, n, 3)]
+    for gg, want in ((g, L.FLAG_NONFINITE_GRAD), (np.nan_to_num(g, posinf=0.1, neginf=-0.1), 0)):
+        p, m, v = dev_f32(p0), dev_f32(m0), dev_f32(v0)
+        pb = torch.zeros(n, dtype=torch.bfloat16, device="cuda")
+        st = torch.zeros(1, dtype=torch.int32, device="cuda")
+        if multi:
+            L.adam_step_multi(segs, p, dev_f32(gg), m, v, 1e-4, weight_decay=0.01, p_bf16=pb, status=st)
+        else:
+            L.adam_step(p, dev_f32(gg), m, v, 3, 1e-4, weight_decay=0.01, p_bf16=pb, status=st)
+        assert int(st.item()) == want
+        pn, mn, vn = p.cpu().numpy(), m.cpu().numpy(), v.cpu().numpy()
+        assert np.array_equal(bits_of(pb), W.to_bf16_bits(pn))
+        if want:
+            for a, a0 in ((pn, p0), (mn, m0), (vn, v0)):
+                assert np.array_equal(a[bad].view(np.int32), a0[bad].view(np.int32))
+        for o, c, t in segs:
+            po, mo, vo, skipped = OA.adam_step_flagged(p0[o:o + c], gg[o:o + c], m0[o:o + c],
+                                                       v0[o:o + c], t, 1e-4, weight_decay=0.01)
+            ok = np.isfinite(gg[o:o + c])
+            assert skipped == (not ok.all())
+            dp, dp_ref = (pn[o:o + c] - p0[o:o + c])[ok], (po - p0[o:o + c])[ok]
+            scale = np.maximum(np.abs(dp_ref), np.sqrt(np.mean(dp_ref ** 2)))
+            ulp = np.spacing(np.abs(po[ok]).astype(np.float32)).astype(np.float64)
+            assert np.all(np.abs(dp - dp_ref) <= TOL_F32 * scale + ulp)
+            assert rel_err(mn[o:o + c][ok], mo[ok]) < TOL_F32 and rel_err(vn[o:o + c][ok], vo[ok]) < TOL_F32

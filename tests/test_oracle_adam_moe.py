@@ -162,3 +162,33 @@ def test_moe_backward_finite_differences():
                     fd = (pert(1) - pert(-1)) / (2 * eps)
                     an = np.sum(G[p][a][ex] * DM)
                     assert abs(fd - an) < 1e-7 * max(1, abs(fd)), (p, a, ex, which)
+
+
+def test_adam_skips_nonfinite_gradients():
+    """NaN and +-Inf gradient elements keep p, m, v as they were; every other
+    element takes the ordinary step, checked against torch AdamW run on those
+    elements alone from the same state (step 3)."""
+    rng = np.random.default_rng(5)
+    n = 64
+    p0, m0, v0 = rng.standard_normal(n), rng.standard_normal(n) * 1e-3, rng.random(n) * 1e-4
+    g = rng.standard_normal(n)
+    bad = [3, 17, 40]
+    g[bad] = [np.nan, np.inf, -np.inf]
+    p, m, v, skipped = OA.adam_step_flagged(p0, g, m0, v0, 3, 1e-3, weight_decay=0.01)
+    assert skipped
+    for a, a0 in ((p, p0), (m, m0), (v, v0)):
+        assert np.array_equal(a[bad], a0[bad])
+    ok = np.isfinite(g)
+    prm = torch.nn.Parameter(torch.tensor(p0[ok]))
+    opt = torch.optim.AdamW([prm], lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.01,
+                            foreach=False)
+    opt.state[prm] = {"step": torch.tensor(2.0, dtype=torch.float64),
+                      "exp_avg": torch.tensor(m0[ok]), "exp_avg_sq": torch.tensor(v0[ok])}
+    prm.grad = torch.tensor(g[ok])
+    opt.step()
+    np.testing.assert_allclose(p[ok] - p0[ok], prm.detach().numpy() - p0[ok], rtol=1e-12, atol=2e-15)
+    np.testing.assert_allclose(m[ok], opt.state[prm]["exp_avg"].numpy(), rtol=1e-14, atol=0)
+    np.testing.assert_allclose(v[ok], opt.state[prm]["exp_avg_sq"].numpy(), rtol=1e-14, atol=0)
+    # all finite: nothing skipped, and the plain step
+    p2, m2, v2, skipped2 = OA.adam_step_flagged(p0, np.where(ok, g, 0.5), m0, v0, 3, 1e-3)
+    assert not skipped2 and np.all(np.isfinite(p2))
