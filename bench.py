@@ -63,9 +63,11 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target wall time of the oracle sample")
-    ap.add_argument("--workload", default="qo_proj", choices=["qo_proj", "mlp", "logprob", "moe"],
+    ap.add_argument("--workload", default="qo_proj",
+                    choices=["qo_proj", "mlp", "logprob", "moe", "decode"],
                     help="qo_proj (default): the q/o projection step the headline metric is "
-                         "quoted on; mlp / logprob / moe: the other workloads, one JSON line each "
+                         "quoted on; mlp / logprob / moe / decode: the other workloads, one JSON "
+                         "line each "
                          "(no CPU baseline)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
                     help="only run a plain device copy of MB megabytes 5 times (calibrates "

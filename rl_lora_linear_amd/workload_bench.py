@@ -13,6 +13,7 @@ from . import lib as L
 import workloads.device as WD
 
 PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
 
 
 def _timed(step, steps, warmup, log):
@@ -137,6 +138,43 @@ def logprob(steps, warmup, log, n_seq=64, seq=256, H=4096, V=151936, chunk=4096)
         "kernels": {"logprob_backward": {"ms_per_step": round(b_step_ms, 4), "chunks": b_n // steps,
                                          "TFLOP_s": round(tf_b, 1),
                                          "frac_mfma": round(tf_b / PEAK_BF16_TFLOPS, 4)}},
+    }
+
+
+def decode(steps, warmup, log, n=256, d=4096, n_ad=64):
+    """Rollout-shaped mixed-adapter forward (lora_forward only): 256 tokens, one
+    per sequence of a decode step, over 64 adapters with ranks from
+    {8,16,32,64}, interleaved ids, d 4096 -> 4096.  The base GEMM at this
+    height reads the whole weight for few rows, so its bound is HBM."""
+    inp = WD.decode_inputs(n, d, n_ad)
+    R = 64
+    shape = L.make_shape(n, d, d, inp["pack"].numel(), inp["pack"].numel(), n_ad, R,
+                         L.IDS_INTERLEAVED)
+    desc = L.make_desc(inp["a_off"], inp["b_off"], inp["ranks"], inp["scales"])
+    ws = L.empty_workspace(L.lora_workspace_bytes(shape))
+    y = torch.empty((n, d), dtype=torch.bfloat16, device="cuda")
+    u = torch.empty((2, n, R), dtype=torch.bfloat16, device="cuda")
+
+    def step(k):
+        L.lora_forward(shape, inp["xs"][k % 4], inp["W"], inp["pack"], inp["pack"], desc,
+                       inp["ids"], y, u, ws)
+
+    log(f"[bench] decode forward {n} tokens, d {d}, {n_ad} adapters")
+    ms, ms_instr = _timed(step, steps, warmup, log)
+    if L.lora_device_status(ws):
+        raise RuntimeError("device status flags set")
+    gemm_ms, gemm_n = _timer(L.TIMER_BASE_GEMM)
+    gemm_bytes = d * d * 2 + 2 * n * d * 2   # W once, x and y
+    gbs = gemm_bytes / (gemm_ms / 1e3) / 1e9
+    return {
+        "metric": "tokens/s mixed-adapter LoRA forward at decode batch",
+        "value": round(n / (ms / 1e3), 1), "unit": "tokens/s", "ms_per_step": round(ms, 4),
+        "ms_per_step_instrumented": round(ms_instr, 4),
+        "config": {"workload": f"decode-step forward: {n} tokens (one per sequence), {n_ad} "
+                               f"adapters r8-64 alpha 32, interleaved ids, d {d} -> {d}"},
+        "roofline": {"bound": "hbm", "kernel": "base GEMM with the fused expand (W read once)",
+                     "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "avg_ms": round(gemm_ms, 4)},
     }
 
 

@@ -65,6 +65,24 @@ def mlp_inputs(n=32768, d=4096, f=12288, n_ad=64, seed=3, rank_choices=(8, 16, 3
                 packs=packs, offs=offs, xs=xs, dys=dys)
 
 
+def decode_inputs(n=256, d=4096, n_ad=64, seed=7, rank_choices=(8, 16, 32, 64)):
+    """Rollout-shaped forward: n tokens (one per sequence in a decode step) over
+    n_ad adapters with ranks from rank_choices (alpha 32), interleaved ids, one
+    Qwen3-8B-width projection d -> d.  Returns a dict: ids, ranks, scales, W
+    ([d][d]), pack, a_off, b_off, xs (four rotated sets)."""
+    torch = _torch()
+    gen = torch.Generator(device="cuda").manual_seed(seed)
+    rng = np.random.default_rng(seed)
+    ranks = rng.choice(np.asarray(rank_choices), size=n_ad).astype(np.int32)
+    scales = (32.0 / ranks).astype(np.float32)
+    ids = torch.from_numpy(rng.integers(0, n_ad, size=n).astype(np.int32)).cuda()
+    W = randn(gen, (d, d), 0.02)
+    pack, a_off, b_off = adapter_pack(gen, ranks, d, d)
+    xs = [randn(gen, (n, d), 1.0) for _ in range(4)]
+    return dict(n=n, d=d, n_ad=n_ad, ids=ids, ranks=ranks, scales=scales, W=W, pack=pack,
+                a_off=a_off, b_off=b_off, xs=xs)
+
+
 def moe_inputs(n=16384, H=2048, F=768, E=128, K=8, n_ad=8, r=32, seed=5):
     """Qwen3-30B-A3B-style routed layer: E experts, top-K, rank-r LoRA (alpha 32)
     on every expert's gate/up/down for each of n_ad adapters, random ids.
