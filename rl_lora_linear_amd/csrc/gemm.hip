@@ -918,6 +918,109 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_nt_kernel(const uint16_t* __
   }
 }
 
+// ---- skinny GEMM for few rows (decode-shaped batches)
+//
+// With M of a few hundred rows the 256x256 tiles leave most CUs idle (256 rows
+// and 4096 columns make 16 blocks).  Here one wave owns 32 rows x 64 columns
+// over the whole K and loads its fragments straight from global memory (the
+// operands are small and L2-resident), so M = 256, N = 4096 runs 512 waves.
+// Each output element is accumulated exactly as in gemm_nt_kernel: the same
+// v_mfma_f32_32x32x16_bf16 with the same operand order and lane layout, k in
+// 16-wide slices in increasing order, then the LoRA expand per adapter and
+// 16-rank slice (hi, then lo), so a row gets the same bits from either kernel
+// (rows of other adapters only receive exact zeros).  Plain epilogue only:
+// bf16 store, rows through a_rows / c_rows, expand from B_a (use_b_off = 1).
+constexpr int SK_TM = 32, SK_TN = 64, SK_KU = 8;   // rows, columns, k slices per batch of loads
+
+__global__ __launch_bounds__(64) void gemm_skinny_kernel(const uint16_t* __restrict__ A,
+                                                         const uint16_t* __restrict__ B, int M,
+                                                         int N, int K, int64_t lda, int64_t ldb,
+                                                         GemmEpi ep) {
+  const int lane = threadIdx.x;
+  const int m0 = blockIdx.x * SK_TM, n0 = blockIdx.y * SK_TN;
+  const int rl = lane & 31, half = lane >> 5;
+  const int m = m0 + rl;
+  const int ma = min(m, M - 1);   // rows past M load row M - 1 and are not stored
+  const uint16_t* arow = A + (int64_t)(ep.a_rows ? ep.a_rows[ma] : ma) * lda + 8 * half;
+  const uint16_t* brow[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) brow[j] = B + (int64_t)min(n0 + 32 * j + rl, N - 1) * ldb + 8 * half;
+
+  f32x16 acc[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int g = 0; g < 16; ++g) acc[j][g] = 0.f;
+  for (int k0 = 0; k0 < K; k0 += 16 * SK_KU) {
+    uint4 fa[SK_KU], fb[SK_KU][2];
+#pragma unroll
+    for (int u = 0; u < SK_KU; ++u) {
+      const int k = min(k0 + 16 * u, K - 16);   // K is a multiple of 64: never clamps
+      fa[u] = *(const uint4*)(arow + k);
+      fb[u][0] = *(const uint4*)(brow[0] + k);
+      fb[u][1] = *(const uint4*)(brow[1] + k);
+    }
+#pragma unroll
+    for (int u = 0; u < SK_KU; ++u) {
+      if (k0 + 16 * u >= K) break;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[j] = mfma32(as_bf16x8(fb[u][j]), as_bf16x8(fa[u]), acc[j]);
+    }
+  }
+
+  const int crow = m < M ? (ep.c_rows ? ep.c_rows[m] : m) : -1;
+  if (ep.vec) {
+    const int ad = m < M ? ep.adpos[m] : -1;
+    const int vrow = ep.vec_by_pos ? m : crow;
+    // present adapters in increasing order (wave-uniform walk)
+    int prev = -1;
+    while (true) {
+      int nxt = ad > prev ? ad : INT32_MAX;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) nxt = min(nxt, __shfl_xor(nxt, o));
+      const int a = __builtin_amdgcn_readfirstlane(nxt);
+      if (a == INT32_MAX) break;
+      prev = a;
+      const lora_adapter_desc d = ep.desc[a];
+      const int r = d.rank;
+      const uint16_t* mat = ep.lmat + d.b_off;
+      for (int sl = 0; sl * 16 < r; ++sl) {
+        const int c = sl * 16 + 8 * half;
+        const bool cok = c < r;
+        uint4 h = make_uint4(0, 0, 0, 0), lo = h, v[2];
+        if (ad == a && cok) {
+          const uint16_t* vp = ep.vec + (int64_t)vrow * ep.vec_ld + c;
+          h = *(const uint4*)vp;
+          lo = *(const uint4*)(vp + ep.vec_plane);
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int n = n0 + 32 * j + rl;
+          v[j] = make_uint4(0, 0, 0, 0);
+          if (n < N && cok) v[j] = *(const uint4*)(mat + (int64_t)n * r + c);
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          acc[j] = mfma32(as_bf16x8(v[j]), as_bf16x8(h), acc[j]);
+          acc[j] = mfma32(as_bf16x8(v[j]), as_bf16x8(lo), acc[j]);
+        }
+      }
+    }
+  }
+  if (crow < 0) return;
+  // register g of acc[j]: column n0 + 32 j + 8 (g / 4) + 4 half + g % 4
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int n = n0 + 32 * j + 8 * q + 4 * half;
+      if (n < N)
+        *(uint2*)(ep.C + (int64_t)crow * ep.ldc + n) =
+            make_uint2(pack2bf(acc[j][4 * q], acc[j][4 * q + 1]),
+                       pack2bf(acc[j][4 * q + 2], acc[j][4 * q + 3]));
+    }
+}
+
 }  // namespace lora
 
 namespace lora_host {
@@ -958,6 +1061,17 @@ static lora_status launch_gemm(const uint16_t* A, const uint16_t* B, int M, int 
     return LORA_E_INVALID_ARG;
   }
   if (tiles_m <= 0) return LORA_OK;
+  // few rows (a plain product, or with the expand from B_a): the skinny kernel
+  // keeps every CU busy where the 256x256 tiles would not
+  if constexpr (EPI == EPI_BF16) {
+    if (!ep.g_tile && ep.glu == 0 && ep.k_split == 0 && !ep.rowscale &&
+        (!ep.vec || ep.use_b_off) && (int64_t)tiles_m * tiles_n < 64 && K % 64 == 0 &&
+        N % 4 == 0 && ep.ldc % 4 == 0) {
+      hipLaunchKernelGGL(gemm_skinny_kernel, dim3((unsigned)cdiv(M, SK_TM), (unsigned)cdiv(N, SK_TN)),
+                         dim3(64), 0, s, A, B, M, N, K, lda, ldb, ep);
+      return launch_check("gemm_skinny");
+    }
+  }
   if (group_m <= 0) group_m = pick_group_m(tiles_m);
   if (group_m > tiles_m) group_m = tiles_m;
   const size_t lds = 0;  // operand tiles are static LDS objects

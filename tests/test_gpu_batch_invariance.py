@@ -7,7 +7,7 @@ needs batch-invariant kernels").
 Each test runs a large batch and a prefix of it as a batch of its own and
 compares the prefix rows bitwise: the dense layer's y, saved u and dx, with the
 large batch past the size at which the shrink switches from 32-row to 128-row
-tiles; the routed-expert layer's y and dx, likewise past the switch in
+tiles and a prefix small enough for the few-row GEMM; the routed-expert layer's y and dx, likewise past the switch in
 (expert, adapter) assignments; the lm_head logprob, logsumexp and dh.
 Per-adapter gradient sums are sums over the batch and are not compared."""
 import numpy as np
@@ -34,8 +34,11 @@ def _assert_same_bits(a, b, what):
     assert bad.size == 0, f"{what}: {len(bad)} elements differ, first at {bad[0].tolist()}"
 
 
-def test_dense_layer_rows_batch_invariant():
-    n_big, n_small = TALL_ROWS + 4096, 4096
+# the 256-row prefix runs its forward GEMM in the few-row kernel, the batch in
+# the 256x256-tile kernel
+@pytest.mark.parametrize("n_small", [4096, 256])
+def test_dense_layer_rows_batch_invariant(n_small):
+    n_big = TALL_ROWS + 4096
     c = W.lora_layer(seed=27, n_tokens=n_big, d_in=256, d_out=320, ranks=[8, 64, 16, 32, 48],
                      alphas=[16.0, 32.0, 8.0, 64.0, 32.0], order="interleaved")
     dl = DevLayer(c)
