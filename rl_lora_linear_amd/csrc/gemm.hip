@@ -930,41 +930,79 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_nt_kernel(const uint16_t* __
 // 16-rank slice (hi, then lo), so a row gets the same bits from either kernel
 // (rows of other adapters only receive exact zeros).  Plain epilogue only:
 // bf16 store, rows through a_rows / c_rows, expand from B_a (use_b_off = 1).
-constexpr int SK_TM = 32, SK_TN = 64, SK_KU = 8;   // rows, columns, k slices per batch of loads
+constexpr int SK_TM = 32, SK_TN = 64, SK_KC = 4;    // rows, columns, 64-wide k chunks per batch of loads
+constexpr int SK_NJ = SK_TN / 32;                  // 32-column MFMA tiles per wave
 
 __global__ __launch_bounds__(64) void gemm_skinny_kernel(const uint16_t* __restrict__ A,
                                                          const uint16_t* __restrict__ B, int M,
                                                          int N, int K, int64_t lda, int64_t ldb,
                                                          GemmEpi ep) {
   const int lane = threadIdx.x;
-  const int m0 = blockIdx.x * SK_TM, n0 = blockIdx.y * SK_TN;
+  // blocks go round-robin over the 8 XCDs: give each XCD a contiguous run of
+  // tiles, row tiles fastest, so the row tiles of one weight panel share that
+  // XCD's L2 (with the row tile fastest across XCDs every XCD read all of W)
+  const int tiles_m = (M + SK_TM - 1) / SK_TM, tiles_n = (N + SK_TN - 1) / SK_TN;
+  const int num = tiles_m * tiles_n;
+  const int b = blockIdx.x, xcd = b & 7, loc = b >> 3;
+  const int per = num >> 3, rem = num & 7;
+  if (loc >= per + (xcd < rem ? 1 : 0)) return;
+  const int t = (xcd < rem) ? xcd * (per + 1) + loc : rem * (per + 1) + (xcd - rem) * per + loc;
+  const int m0 = (t % tiles_m) * SK_TM, n0 = (t / tiles_m) * SK_TN;
   const int rl = lane & 31, half = lane >> 5;
   const int m = m0 + rl;
   const int ma = min(m, M - 1);   // rows past M load row M - 1 and are not stored
-  const uint16_t* arow = A + (int64_t)(ep.a_rows ? ep.a_rows[ma] : ma) * lda + 8 * half;
-  const uint16_t* brow[2];
+  // each lane reads 64 contiguous bytes of its row per 64-wide k chunk (k
+  // 32 half .. + 31), so a row's line is fetched once; two lane-half swaps
+  // then give the MFMA layout of each 16-wide slice (half 0: k 16 s .. + 7,
+  // half 1: k 16 s + 8 .. + 15)
+  const uint16_t* arow = A + (int64_t)(ep.a_rows ? ep.a_rows[ma] : ma) * lda + 32 * half;
+  const uint16_t* brow[SK_NJ];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) brow[j] = B + (int64_t)min(n0 + 32 * j + rl, N - 1) * ldb + 8 * half;
+  for (int j = 0; j < SK_NJ; ++j) brow[j] = B + (int64_t)min(n0 + 32 * j + rl, N - 1) * ldb + 32 * half;
 
-  f32x16 acc[2];
+  f32x16 acc[SK_NJ];
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int j = 0; j < SK_NJ; ++j)
 #pragma unroll
     for (int g = 0; g < 16; ++g) acc[j][g] = 0.f;
-  for (int k0 = 0; k0 < K; k0 += 16 * SK_KU) {
-    uint4 fa[SK_KU], fb[SK_KU][2];
+  // chunks c0, c1 of both lane halves -> the fragments of slices s0 (into c0)
+  // and s0 + 2 (into c1)
+  auto swap_halves = [](uint4& c0, uint4& c1) {
+    auto x = __builtin_amdgcn_permlane32_swap(c0.x, c1.x, false, false);
+    auto y = __builtin_amdgcn_permlane32_swap(c0.y, c1.y, false, false);
+    auto z = __builtin_amdgcn_permlane32_swap(c0.z, c1.z, false, false);
+    auto w = __builtin_amdgcn_permlane32_swap(c0.w, c1.w, false, false);
+    c0 = make_uint4(x[0], y[0], z[0], w[0]);
+    c1 = make_uint4(x[1], y[1], z[1], w[1]);
+  };
+  for (int k0 = 0; k0 < K; k0 += 64 * SK_KC) {
+    uint4 fa[SK_KC][4], fb[SK_KC][SK_NJ][4];
 #pragma unroll
-    for (int u = 0; u < SK_KU; ++u) {
-      const int k = min(k0 + 16 * u, K - 16);   // K is a multiple of 64: never clamps
-      fa[u] = *(const uint4*)(arow + k);
-      fb[u][0] = *(const uint4*)(brow[0] + k);
-      fb[u][1] = *(const uint4*)(brow[1] + k);
+    for (int u = 0; u < SK_KC; ++u) {
+      const int k = min(k0 + 64 * u, K - 64);   // K is a multiple of 64: clamps only past K
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        fa[u][e] = *(const uint4*)(arow + k + 8 * e);
+#pragma unroll
+        for (int j = 0; j < SK_NJ; ++j) fb[u][j][e] = *(const uint4*)(brow[j] + k + 8 * e);
+      }
     }
 #pragma unroll
-    for (int u = 0; u < SK_KU; ++u) {
-      if (k0 + 16 * u >= K) break;
+    for (int u = 0; u < SK_KC; ++u) {
+      if (k0 + 64 * u >= K) break;
+      swap_halves(fa[u][0], fa[u][1]);   // slices 0, 2
+      swap_halves(fa[u][2], fa[u][3]);   // slices 1, 3
 #pragma unroll
-      for (int j = 0; j < 2; ++j) acc[j] = mfma32(as_bf16x8(fb[u][j]), as_bf16x8(fa[u]), acc[j]);
+      for (int j = 0; j < SK_NJ; ++j) {
+        swap_halves(fb[u][j][0], fb[u][j][1]);
+        swap_halves(fb[u][j][2], fb[u][j][3]);
+      }
+      constexpr int e_of_slice[4] = {0, 2, 1, 3};
+#pragma unroll
+      for (int sl = 0; sl < 4; ++sl)
+#pragma unroll
+        for (int j = 0; j < SK_NJ; ++j)
+          acc[j] = mfma32(as_bf16x8(fb[u][j][e_of_slice[sl]]), as_bf16x8(fa[u][e_of_slice[sl]]), acc[j]);
     }
   }
 
@@ -972,45 +1010,67 @@ __global__ __launch_bounds__(64) void gemm_skinny_kernel(const uint16_t* __restr
   if (ep.vec) {
     const int ad = m < M ? ep.adpos[m] : -1;
     const int vrow = ep.vec_by_pos ? m : crow;
-    // present adapters in increasing order (wave-uniform walk)
-    int prev = -1;
-    while (true) {
+    // this row's scaled vector (both planes, every 16-rank slice), loaded once
+    constexpr int SL = 4;   // slices of the largest rank (64)
+    uint4 hb[SL], lb[SL];
+#pragma unroll
+    for (int sl = 0; sl < SL; ++sl) {
+      const int c = sl * 16 + 8 * half;
+      hb[sl] = lb[sl] = make_uint4(0, 0, 0, 0);
+      if (ad >= 0 && c < ep.vec_ld) {
+        const uint16_t* vp = ep.vec + (int64_t)vrow * ep.vec_ld + c;
+        hb[sl] = *(const uint4*)vp;
+        lb[sl] = *(const uint4*)(vp + ep.vec_plane);
+      }
+    }
+    // present adapters in increasing order (wave-uniform walk); the next
+    // adapter's descriptor is in flight while this one's factor slices load
+    auto next_after = [&](int prev) {
       int nxt = ad > prev ? ad : INT32_MAX;
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) nxt = min(nxt, __shfl_xor(nxt, o));
-      const int a = __builtin_amdgcn_readfirstlane(nxt);
-      if (a == INT32_MAX) break;
-      prev = a;
-      const lora_adapter_desc d = ep.desc[a];
+      return __builtin_amdgcn_readfirstlane(nxt);
+    };
+    int a = next_after(-1);
+    lora_adapter_desc d{};
+    if (a != INT32_MAX) d = ep.desc[a];
+    while (a != INT32_MAX) {
+      const int an = next_after(a);
+      lora_adapter_desc dn{};
+      if (an != INT32_MAX) dn = ep.desc[an];
       const int r = d.rank;
       const uint16_t* mat = ep.lmat + d.b_off;
-      for (int sl = 0; sl * 16 < r; ++sl) {
+      uint4 v[SL][SK_NJ];
+#pragma unroll
+      for (int sl = 0; sl < SL; ++sl) {
         const int c = sl * 16 + 8 * half;
-        const bool cok = c < r;
-        uint4 h = make_uint4(0, 0, 0, 0), lo = h, v[2];
-        if (ad == a && cok) {
-          const uint16_t* vp = ep.vec + (int64_t)vrow * ep.vec_ld + c;
-          h = *(const uint4*)vp;
-          lo = *(const uint4*)(vp + ep.vec_plane);
-        }
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < SK_NJ; ++j) {
           const int n = n0 + 32 * j + rl;
-          v[j] = make_uint4(0, 0, 0, 0);
-          if (n < N && cok) v[j] = *(const uint4*)(mat + (int64_t)n * r + c);
-        }
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          acc[j] = mfma32(as_bf16x8(v[j]), as_bf16x8(h), acc[j]);
-          acc[j] = mfma32(as_bf16x8(v[j]), as_bf16x8(lo), acc[j]);
+          v[sl][j] = make_uint4(0, 0, 0, 0);
+          if (c < r && n < N) v[sl][j] = *(const uint4*)(mat + (int64_t)n * r + c);
         }
       }
+#pragma unroll
+      for (int sl = 0; sl < SL; ++sl) {
+        if (sl * 16 >= r) break;
+        const bool mine = ad == a && sl * 16 + 8 * half < r;
+        const uint4 h = mine ? hb[sl] : make_uint4(0, 0, 0, 0);
+        const uint4 lo = mine ? lb[sl] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < SK_NJ; ++j) {
+          acc[j] = mfma32(as_bf16x8(v[sl][j]), as_bf16x8(h), acc[j]);
+          acc[j] = mfma32(as_bf16x8(v[sl][j]), as_bf16x8(lo), acc[j]);
+        }
+      }
+      a = an;
+      d = dn;
     }
   }
   if (crow < 0) return;
   // register g of acc[j]: column n0 + 32 j + 8 (g / 4) + 4 half + g % 4
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int j = 0; j < SK_NJ; ++j)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int n = n0 + 32 * j + 8 * q + 4 * half;
@@ -1067,7 +1127,7 @@ static lora_status launch_gemm(const uint16_t* A, const uint16_t* B, int M, int 
     if (!ep.g_tile && ep.glu == 0 && ep.k_split == 0 && !ep.rowscale &&
         (!ep.vec || ep.use_b_off) && (int64_t)tiles_m * tiles_n < 64 && K % 64 == 0 &&
         N % 4 == 0 && ep.ldc % 4 == 0) {
-      hipLaunchKernelGGL(gemm_skinny_kernel, dim3((unsigned)cdiv(M, SK_TM), (unsigned)cdiv(N, SK_TN)),
+      hipLaunchKernelGGL(gemm_skinny_kernel, dim3((unsigned)(cdiv(M, SK_TM) * cdiv(N, SK_TN))),
                          dim3(64), 0, s, A, B, M, N, K, lda, ldb, ep);
       return launch_check("gemm_skinny");
     }
