@@ -9,9 +9,10 @@
 // kernels gather rows through perm.
 //
 //   shrink   out[t][c] = sum_k in[t][k] M_a[c][k]      (u = A_a x, v = B_a^T g)
-//            32 rows per block streamed through an LDS-DMA ring.
+//            32 rows per block streamed through an LDS-DMA ring (128 rows for
+//            large batches, same per-row summation order).
 //   (the expand y += s B_a u / dx += s A_a^T v runs inside the base GEMM's
-//    epilogue: gemm.hip, lora_slab)
+//    epilogue: gemm.hip, lora_expand; few-row batches: gemm_skinny_kernel)
 //   grad     T[c][j] = s_a sum_{t in chunk} P[t][c] Q[t][j]  (dB_a, dA_a)
 //            one block per (token chunk of an adapter, 256 columns); Q and P
 //            stream through an LDS-DMA ring and Q is transposed on the LDS
@@ -962,7 +963,7 @@ lora_status launch_shrink(const uint16_t* in, int64_t ld_in, int K, const uint16
                             (size_t)sh_nst<2>() * (SH_XSLOTS + 512) * 16,
                             (size_t)sh_nst<3>() * (SH_XSLOTS + 768) * 16,
                             (size_t)sh_nst<4>() * (SH_XSLOTS + 1024) * 16};
-    lds = (size_t)4 * SH_TM * 64 * sizeof(float);
+    lds = (size_t)2 * SH_TM * 64 * sizeof(float);   // the even/odd partial sums
     for (int nb = 1; nb <= nb_max; ++nb) lds = std::max(lds, ring[nb - 1]);
   }
   auto go = [&](auto tall_) -> lora_status {
