@@ -15,15 +15,7 @@ router and the combine weights are treated as constants in the backward.
 Containers: W_gate, W_up [E, F, H]; W_down [E, H, F]; A[p][a][e], B[p][a][e]
 for p in ("gate", "up", "down") with gate/up A [r, H], B [F, r] and down
 A [r, F], B [H, r].
-`store(name, js, value)` (default: return value) is called wherever an
-implementation keeps a per-assignment intermediate: name is one of "g", "u"
-(gate/up pre-activations), "h", "o" (expert output), "dh", "dg", "du",
-"dx_e" (the assignment's dx, gate and up parts summed); js are the assignment
-indices of the rows.  Whatever it
-returns is used from there on, so a test can continue the oracle from a
-device layer's own stored bits (per-call parity through a fused layer) and
-compare each intermediate on the way; with the default the functions are the
-plain definitions above.
+The functions are the plain definitions above, in float64 throughout.
 """
 from __future__ import annotations
 
@@ -65,13 +57,8 @@ def _groups(experts, ids):
     return {key: np.asarray(v, np.int64) for key, v in out.items()}
 
 
-def _ident(name, js, a):
-    return a
-
-
-def moe_forward(x, experts, weights, ids, Wg, Wu, Wd, A, B, scale, store=None):
+def moe_forward(x, experts, weights, ids, Wg, Wu, Wd, A, B, scale):
     """Return (y [N, H], saved dict with per-assignment g_pre, u_pre, h)."""
-    st = store or _ident
     x = np.asarray(x, np.float64)
     n, H = x.shape
     k = experts.shape[1]
@@ -82,18 +69,17 @@ def moe_forward(x, experts, weights, ids, Wg, Wu, Wd, A, B, scale, store=None):
     out = np.zeros((n * k, H))
     for (e, a), js in _groups(experts, ids).items():
         xs = x[js // k]
-        g = st("g", js, xs @ Wg[e].T + scale * (xs @ A["gate"][a][e].T) @ B["gate"][a][e].T)
-        u = st("u", js, xs @ Wu[e].T + scale * (xs @ A["up"][a][e].T) @ B["up"][a][e].T)
-        h = st("h", js, _silu(g) * u)
-        o = st("o", js, h @ Wd[e].T + scale * (h @ A["down"][a][e].T) @ B["down"][a][e].T)
+        g = xs @ Wg[e].T + scale * (xs @ A["gate"][a][e].T) @ B["gate"][a][e].T
+        u = xs @ Wu[e].T + scale * (xs @ A["up"][a][e].T) @ B["up"][a][e].T
+        h = _silu(g) * u
+        o = h @ Wd[e].T + scale * (h @ A["down"][a][e].T) @ B["down"][a][e].T
         gpre[js], upre[js], hmid[js], out[js] = g, u, h, o
     y = (out.reshape(n, k, H) * np.asarray(weights)[:, :, None]).sum(axis=1)
     return y, {"gpre": gpre, "upre": upre, "h": hmid}
 
 
-def moe_backward(dy, x, experts, weights, ids, Wg, Wu, Wd, A, B, scale, saved, store=None):
+def moe_backward(dy, x, experts, weights, ids, Wg, Wu, Wd, A, B, scale, saved):
     """Return (dx [N, H], dA, dB) with dA[p][a][e], dB[p][a][e] like A, B."""
-    st = store or _ident
     dy = np.asarray(dy, np.float64)
     x = np.asarray(x, np.float64)
     n, H = x.shape
@@ -109,11 +95,11 @@ def moe_backward(dy, x, experts, weights, ids, Wg, Wu, Wd, A, B, scale, saved, s
         g, u, h = saved["gpre"][js], saved["upre"][js], saved["h"][js]
         Ad, Bd = A["down"][a][e], B["down"][a][e]
         vd = do @ Bd
-        dh = st("dh", js, do @ Wd[e] + scale * vd @ Ad)
+        dh = do @ Wd[e] + scale * vd @ Ad
         dB["down"][a][e] += scale * do.T @ (h @ Ad.T)
         dA["down"][a][e] += scale * vd.T @ h
-        dg = st("dg", js, dh * u * _dsilu(g))
-        du = st("du", js, dh * _silu(g))
+        dg = dh * u * _dsilu(g)
+        du = dh * _silu(g)
         dxs = np.zeros_like(xs)
         for p, Wp, d in (("gate", Wg, dg), ("up", Wu, du)):
             Ap, Bp = A[p][a][e], B[p][a][e]
@@ -121,5 +107,5 @@ def moe_backward(dy, x, experts, weights, ids, Wg, Wu, Wd, A, B, scale, saved, s
             dxs += d @ Wp[e] + scale * vp @ Ap
             dB[p][a][e] += scale * d.T @ (xs @ Ap.T)
             dA[p][a][e] += scale * vp.T @ xs
-        np.add.at(dx, ts, st("dx_e", js, dxs))
+        np.add.at(dx, ts, dxs)
     return dx, dA, dB

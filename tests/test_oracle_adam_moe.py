@@ -164,31 +164,115 @@ def test_moe_backward_finite_differences():
                     assert abs(fd - an) < 1e-7 * max(1, abs(fd)), (p, a, ex, which)
 
 
-def test_adam_skips_nonfinite_gradients():
-    """NaN and +-Inf gradient elements keep p, m, v as they were; every other
-    element takes the ordinary step, checked against torch AdamW run on those
-    elements alone from the same state (step 3)."""
-    rng = np.random.default_rng(5)
-    n = 64
-    p0, m0, v0 = rng.standard_normal(n), rng.standard_normal(n) * 1e-3, rng.random(n) * 1e-4
-    g = rng.standard_normal(n)
-    bad = [3, 17, 40]
-    g[bad] = [np.nan, np.inf, -np.inf]
-    p, m, v, skipped = OA.adam_step_flagged(p0, g, m0, v0, 3, 1e-3, weight_decay=0.01)
-    assert skipped
-    for a, a0 in ((p, p0), (m, m0), (v, v0)):
-        assert np.array_equal(a[bad], a0[bad])
-    ok = np.isfinite(g)
-    prm = torch.nn.Parameter(torch.tensor(p0[ok]))
-    opt = torch.optim.AdamW([prm], lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.01,
+def _torch_adamw_from(p0, m0, v0, g, prev_steps, lr, wd):
+    """torch.optim.AdamW (CPU, float64) one step from a given state; returns
+    (p, m, v) after the step."""
+    prm = torch.nn.Parameter(torch.tensor(p0))
+    opt = torch.optim.AdamW([prm], lr=lr, betas=(0.9, 0.999), eps=1e-8, weight_decay=wd,
                             foreach=False)
-    opt.state[prm] = {"step": torch.tensor(2.0, dtype=torch.float64),
-                      "exp_avg": torch.tensor(m0[ok]), "exp_avg_sq": torch.tensor(v0[ok])}
-    prm.grad = torch.tensor(g[ok])
+    opt.state[prm] = {"step": torch.tensor(float(prev_steps), dtype=torch.float64),
+                      "exp_avg": torch.tensor(m0), "exp_avg_sq": torch.tensor(v0)}
+    prm.grad = torch.tensor(g)
     opt.step()
-    np.testing.assert_allclose(p[ok] - p0[ok], prm.detach().numpy() - p0[ok], rtol=1e-12, atol=2e-15)
-    np.testing.assert_allclose(m[ok], opt.state[prm]["exp_avg"].numpy(), rtol=1e-14, atol=0)
-    np.testing.assert_allclose(v[ok], opt.state[prm]["exp_avg_sq"].numpy(), rtol=1e-14, atol=0)
-    # all finite: nothing skipped, and the plain step
-    p2, m2, v2, skipped2 = OA.adam_step_flagged(p0, np.where(ok, g, 0.5), m0, v0, 3, 1e-3)
-    assert not skipped2 and np.all(np.isfinite(p2))
+    st = opt.state[prm]
+    return prm.detach().numpy(), st["exp_avg"].numpy(), st["exp_avg_sq"].numpy()
+
+
+def test_adam_skips_whole_adapter_on_nonfinite_gradient():
+    """TPU RL note, section 12: a non-finite optimizer update is skipped
+    outright.  Five adapters in one flat buffer; adapter 3's gradient holds one
+    NaN (and, in a second round, one -Inf): all of adapter 3 -- p, m and v,
+    including every finite element -- stays bit-identical, while each other
+    adapter takes the ordinary step, checked against torch AdamW run on that
+    adapter alone from the same state.  A per-element skip would move adapter
+    3's finite elements and fail here."""
+    rng = np.random.default_rng(5)
+    counts = [40, 17, 64, 33, 9]
+    offs = np.concatenate([[0], np.cumsum(counts)[:-1]])
+    n = int(sum(counts))
+    steps = [3, 1, 7, 4, 2]
+    p0, m0, v0 = rng.standard_normal(n), rng.standard_normal(n) * 1e-3, rng.random(n) * 1e-4
+    for bad_value in (np.nan, -np.inf):
+        g = rng.standard_normal(n)
+        g[offs[3] + 11] = bad_value
+        segs = [(int(o), c, t) for o, c, t in zip(offs, counts, steps)]
+        p, m, v, skipped = OA.adam_step_multi(segs, p0, g, m0, v0, 1e-3, weight_decay=0.01)
+        assert skipped == [False, False, False, True, False]
+        sl3 = slice(offs[3], offs[3] + counts[3])
+        for a, a0 in ((p, p0), (m, m0), (v, v0)):
+            assert np.array_equal(a[sl3], a0[sl3])
+        for i in (0, 1, 2, 4):
+            sl = slice(offs[i], offs[i] + counts[i])
+            tp, tm, tv = _torch_adamw_from(p0[sl], m0[sl], v0[sl], g[sl], steps[i] - 1, 1e-3, 0.01)
+            np.testing.assert_allclose(p[sl] - p0[sl], tp - p0[sl], rtol=1e-12, atol=2e-15)
+            np.testing.assert_allclose(m[sl], tm, rtol=1e-14, atol=0)
+            np.testing.assert_allclose(v[sl], tv, rtol=1e-14, atol=0)
+            assert not np.array_equal(p[sl], p0[sl])
+    # one adapter alone: +Inf anywhere skips it, all finite steps it
+    g1 = rng.standard_normal(8)
+    g1[0] = np.inf
+    p1, m1, v1, sk = OA.adam_step_flagged(p0[:8], g1, m0[:8], v0[:8], 2, 1e-3)
+    assert sk and np.array_equal(p1, p0[:8]) and np.array_equal(m1, m0[:8]) and np.array_equal(v1, v0[:8])
+    g1[0] = 0.5
+    p1, _, _, sk = OA.adam_step_flagged(p0[:8], g1, m0[:8], v0[:8], 2, 1e-3)
+    assert not sk and np.all(p1 != p0[:8])
+
+
+def test_moe_brute_force_tiny_e4_k2():
+    """Brute force on a tiny layer (4 experts, top-2, 2 adapters): per token,
+    Python loops pick the two largest logits by scanning (ties to the lower
+    index), form their softmax weights from the full softmax, and evaluate each
+    chosen expert's SwiGLU MLP with its (expert, adapter) LoRA element by
+    element.  Independent of the oracle's grouping by (expert, adapter)."""
+    import math
+    rng = np.random.default_rng(31)
+    n, H, F, E, k, r, s = 7, 5, 6, 4, 2, 2, 0.75
+    R = rng.standard_normal((n, E))
+    R[2, 1] = R[2, 3] = R[2].max() + 0.5                  # a tie for first place
+    ids = rng.integers(0, 2, size=n)
+    Wg, Wu = rng.standard_normal((E, F, H)), rng.standard_normal((E, F, H))
+    Wd = rng.standard_normal((E, H, F))
+    A = {p: [[rng.standard_normal((r, F if p == "down" else H)) for _ in range(E)] for _ in range(2)]
+         for p in ("gate", "up", "down")}
+    B = {p: [[rng.standard_normal((H if p == "down" else F, r)) for _ in range(E)] for _ in range(2)]
+         for p in ("gate", "up", "down")}
+    x = rng.standard_normal((n, H))
+
+    def proj(Wm, Am, Bm, z):
+        out = []
+        for o in range(len(Wm)):
+            acc = sum(Wm[o][i] * z[i] for i in range(len(z)))
+            for q in range(r):
+                acc += s * Bm[o][q] * sum(Am[q][i] * z[i] for i in range(len(z)))
+            out.append(acc)
+        return out
+
+    experts, weights = OE.moe_route(R, k)
+    y = OE.moe_forward(x, experts, weights, ids, Wg, Wu, Wd, A, B, s)[0]
+    for t in range(n):
+        row = list(R[t])
+        picked = []
+        for _ in range(k):
+            best = None
+            for e in range(E):
+                if e in picked:
+                    continue
+                if best is None or row[e] > row[best]:
+                    best = e
+            picked.append(best)
+        assert list(experts[t]) == picked
+        mx = max(row)
+        z = sum(math.exp(v - mx) for v in row)
+        p = [math.exp(row[e] - mx) / z for e in picked]
+        wts = [q / sum(p) for q in p]
+        a = int(ids[t])
+        want = [0.0] * H
+        for e, wk in zip(picked, wts):
+            gg = proj(Wg[e], A["gate"][a][e], B["gate"][a][e], x[t])
+            uu = proj(Wu[e], A["up"][a][e], B["up"][a][e], x[t])
+            h = [gi / (1.0 + math.exp(-gi)) * ui for gi, ui in zip(gg, uu)]
+            o = proj(Wd[e], A["down"][a][e], B["down"][a][e], h)
+            want = [wv + wk * ov for wv, ov in zip(want, o)]
+        np.testing.assert_allclose(y[t], want, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(weights[t], wts, rtol=1e-12)
+    assert list(experts[2]) == [1, 3]

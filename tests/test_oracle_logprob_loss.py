@@ -189,3 +189,45 @@ def test_masked_nonfinite_rows_are_exact_zeros():
     for kind in range(4):
         L, dl = OLs.loss_grad(kind, l, m, adv=A, samp=s, g=np.where(m != 0, 1.0, np.nan))
         assert np.isfinite(L) and np.all(dl[:4] == 0.0) and np.isfinite(dl).all()
+
+
+def test_sentinel_removes_kept_rows_with_nonfinite_inputs():
+    """TPU RL note, section 12: a kept row whose own inputs hold NaN or +-Inf is
+    neutralised (dl = 0, no loss term) and reported, for every kind; the other
+    rows' results equal those of the batch with the bad rows masked out, and a
+    bad value in an input the kind does not read changes nothing."""
+    l, s, A, m, rng = _rl(12)
+    m[:] = 1.0
+    g = rng.standard_normal(len(l))
+    plant = {  # kind -> rows and inputs to poison
+        OLs.CROSS_ENTROPY: [("l", 3, np.nan), ("w", 9, np.inf)],
+        OLs.IMPORTANCE_SAMPLING: [("l", 3, -np.inf), ("s", 9, np.nan), ("A", 20, np.inf)],
+        OLs.PPO: [("s", 3, -np.inf), ("A", 9, np.nan), ("l", 20, np.nan)],
+        OLs.CUSTOM: [("g", 3, np.nan), ("l", 9, np.inf)],
+    }
+    for kind, items in plant.items():
+        arrs = {"l": l.copy(), "s": s.copy(), "A": A.copy(), "w": m.copy(), "g": g.copy()}
+        rows = []
+        for name, row, val in items:
+            arrs[name][row] = val
+            rows.append(row)
+        L1, dl1, flag = OLs.loss_grad_flagged(kind, arrs["l"], arrs["w"], adv=arrs["A"],
+                                              samp=arrs["s"], g=arrs["g"])
+        assert flag and np.isfinite(L1) and np.all(np.isfinite(dl1))
+        assert np.all(dl1[rows] == 0.0)
+        # same as masking those rows by hand on clean inputs
+        mm = m.copy()
+        mm[rows] = 0.0
+        L2, dl2, flag2 = OLs.loss_grad_flagged(kind, l, mm, adv=A, samp=s, g=g)
+        assert not flag2
+        assert L1 == L2 and np.array_equal(dl1, dl2)
+    # inputs a kind does not read: CE ignores A, l_sampler and g
+    L1, dl1, flag = OLs.loss_grad_flagged(OLs.CROSS_ENTROPY, l, m, adv=np.full(len(l), np.nan),
+                                          samp=np.full(len(l), np.inf), g=np.full(len(l), np.nan))
+    assert not flag and np.array_equal(dl1, -m)
+    # masked rows never raise the sentinel
+    mm = m.copy()
+    mm[5] = 0.0
+    ll = l.copy()
+    ll[5] = np.nan
+    assert not OLs.loss_grad_flagged(OLs.PPO, ll, mm, adv=A, samp=s)[2]

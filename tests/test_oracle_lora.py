@@ -201,3 +201,25 @@ def test_closed_form_flop_overhead():
     assert round(100 * lora / base, 1) == g["lora_flop_overhead"]["printed_percent"]
     s = g["sgmv_calls_per_forward"]
     assert s["projections_per_layer"] * s["layers"] == s["calls"]
+
+
+def test_u_is_pinned_by_the_merged_weight_with_identity_B():
+    """u_t = A_a x_t: with d_out = r and B_a = I the merged weight W + s A_a
+    gives y_t - W x_t = s u_t, so u is checked against the merged form, which
+    never forms u."""
+    rng = np.random.default_rng(41)
+    n, d_in, r = 30, 12, 4
+    ids = rng.integers(-1, 3, size=n)                 # includes an invalid id
+    A = [rng.standard_normal((r, d_in)) for _ in range(3)]
+    B = [np.eye(r) for _ in range(3)]
+    s = np.array([2.0, 0.5, 1.25])
+    x = rng.standard_normal((n, d_in))
+    Wb = rng.standard_normal((r, d_in))
+    _, u = OL.lora_forward(x, Wb, A, B, s, ids)
+    y_m = OL.merged_forward(x, Wb, A, B, s, ids)
+    for t in range(n):
+        a = int(ids[t])
+        if 0 <= a < 3:
+            np.testing.assert_allclose(u[t], (y_m[t] - Wb @ x[t]) / s[a], rtol=0, atol=1e-12)
+        else:
+            assert not u[t].any()
