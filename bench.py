@@ -180,6 +180,7 @@ def main():
     m = torch.zeros_like(master)
     v = torch.zeros_like(master)
     ranges = [case.adapter_range(i) for i in range(n_ad)]
+    ws_adam = L.empty_workspace(L.adam_workspace_bytes(n_ad))
     steps_done = [0]
 
     def step(k):
@@ -190,7 +191,7 @@ def main():
         t = steps_done[0] + 1
         # every adapter in the batch takes its own AdamW step, one launch
         L.adam_step_multi([(a0, a1 - a0, t) for (a0, a1) in ranges], master, grad, m, v, 1e-4,
-                          0.9, 0.999, 1e-8, 0.0, p_bf16=dl.pack)
+                          0.9, 0.999, 1e-8, 0.0, p_bf16=dl.pack, ws=ws_adam)
         steps_done[0] = t
 
     log(f"[bench] warmup {args.warmup}")

@@ -80,7 +80,8 @@ typedef enum {
 #define LORA_FLAG_UNSORTED     0x2  /* ids decrease although LORA_IDS_SORTED was promised */
 #define LORA_FLAG_TARGET_RANGE 0x4  /* a target token id outside [0, vocab) */
 #define LORA_FLAG_BAD_DESC     0x8  /* an adapter descriptor with bad rank, offset or alignment */
-#define LORA_FLAG_NONFINITE_GRAD 0x10 /* AdamW skipped elements whose gradient was NaN or Inf */
+#define LORA_FLAG_NONFINITE_GRAD 0x10 /* AdamW skipped an adapter whose gradient held NaN or Inf */
+#define LORA_FLAG_NONFINITE_LOSS 0x20 /* loss_grad removed kept rows whose inputs held NaN or Inf */
 
 typedef enum { LORA_IDS_SORTED = 0, LORA_IDS_INTERLEAVED = 1 } lora_id_order;
 
@@ -253,7 +254,16 @@ typedef struct { float clip_low, clip_high; } loss_config;
  *   cfg      host pointer (PPO; else may be NULL)
  *   loss_out fp32 [1] out (device): deterministic sum, fixed order in fp64
  *   dlogp    fp32 [n] out
- * Workspace: loss_grad_workspace_bytes(n). */
+ * Sentinel (TPU RL note, section 12 "The instability I have not solved": a
+ * NaN logprob is caught and its token gets a zero weight and a neutralised
+ * value): a kept row any of whose inputs to its own term is NaN or +-Inf --
+ * logprobs and weights for every kind, advantages and sampler_logprobs for
+ * IS and PPO, custom_g for CUSTOM -- is removed by selection exactly like a
+ * masked row (dlogp = 0, no loss term), and LORA_FLAG_NONFINITE_LOSS is set
+ * in the workspace status word (read it with lora_device_status).  Inputs a
+ * kind does not read are never inspected.  A finite row whose ratio
+ * exp(l - l_s) overflows fp32 still follows IEEE 754.
+ * Workspace: loss_grad_workspace_bytes(n); word 0 is the status word. */
 size_t loss_grad_workspace_bytes(int64_t n);
 lora_status loss_grad(int32_t kind, int64_t n, const float* logprobs, const float* weights,
                       const float* advantages, const float* sampler_logprobs,
@@ -270,27 +280,35 @@ lora_status loss_grad(int32_t kind, int64_t n, const float* logprobs, const floa
  * step >= 1 is this adapter's own counter (bias factors are computed on the
  * host in double).  p, m, v updated in place; g read only.  p_bf16 (nullable)
  * receives bf16(p) -- the bf16 copy the layer kernels read.  n >= 0.
- * Non-finite gradients are contained (the pages give no rule for them; this
- * is the plain reading of skipping a bad update): an element whose g is NaN or
- * +-Inf is not updated -- its p, m, v and bf16 copy keep their values -- and
- * LORA_FLAG_NONFINITE_GRAD is OR-ed into *status (a device int32, nullable:
- * then the skip is silent).  Finite elements update exactly as above. */
+ * Non-finite gradients (TPU RL note, section 12 "The instability I have not
+ * solved": a non-finite optimizer update is skipped outright): if ANY element
+ * of g is NaN or +-Inf, the whole update is skipped -- p, m, v and the bf16
+ * copy keep every value -- LORA_FLAG_NONFINITE_GRAD is OR-ed into the
+ * workspace status word, and the segment's skip flag (below) is 1; the caller
+ * then keeps its step counter where it was.
+ * Workspace: adam_workspace_bytes(n_seg) bytes (n_seg = 1 for adam_step).
+ * Word 0 is the sticky status word (lora_device_status reads and clears it);
+ * the int32 at byte offset 256 + 4 i is segment i's skip flag of the latest
+ * call (1 = skipped, 0 = stepped), rewritten by every call.  Three launches:
+ * clear the flags, scan g, update. */
+size_t adam_workspace_bytes(int32_t n_seg);
 lora_status adam_step(int64_t n, float* p, const float* g, float* m, float* v, int64_t step,
                       float lr, float beta1, float beta2, float eps, float weight_decay,
-                      uint16_t* p_bf16, int32_t* status, void* stream);
+                      uint16_t* p_bf16, void* ws, size_t ws_bytes, void* stream);
 
-/* Several adapters' AdamW steps in one launch: segment i updates elements
- * [offset, offset + count) of p, g, m, v (and p_bf16) exactly as adam_step
- * with step = segs[i].step would (same host-side bias factors, same
+/* Several adapters' AdamW steps in one set of launches: segment i updates
+ * elements [offset, offset + count) of p, g, m, v (and p_bf16) exactly as
+ * adam_step with step = segs[i].step would (same host-side bias factors, same
  * per-element arithmetic, so results are bitwise those of one adam_step call
- * per segment).  segs is a HOST array; segments must not overlap.  Each
- * adapter keeps its own step counter (OpenTinker, "3 Approach": optimizer
- * state local to each adapter).  n_seg >= 0.  Non-finite gradient elements
- * are skipped and flagged in *status (nullable) as in adam_step. */
+ * per segment), and its skip decision is its own: a non-finite element in one
+ * adapter's gradient skips that adapter only.  segs is a HOST array; segments
+ * must not overlap.  Each adapter keeps its own step counter (OpenTinker,
+ * "3 Approach": optimizer state local to each adapter).  n_seg >= 0. */
 typedef struct { int64_t offset; int64_t count; int64_t step; } adam_segment;
 lora_status adam_step_multi(int32_t n_seg, const adam_segment* segs, float* p, const float* g,
                             float* m, float* v, float lr, float beta1, float beta2, float eps,
-                            float weight_decay, uint16_t* p_bf16, int32_t* status, void* stream);
+                            float weight_decay, uint16_t* p_bf16, void* ws, size_t ws_bytes,
+                            void* stream);
 
 /* ---- MLP glue --------------------------------------------------------- */
 
@@ -442,7 +460,8 @@ lora_status mlp_backward(const mlp_shape* shape, const uint16_t* dy, const uint1
 /* When enabled, the library brackets each launch of the kernel classes below
  * with HIP events on the launch stream.  lora_timing_read synchronises on the
  * recorded events and returns the summed duration (ms) and launch count since
- * the last reset.  Not thread-safe; off by default. */
+ * the last reset.  The timers are per host thread (enable, reset and read on
+ * the thread that makes the calls); off by default. */
 #define LORA_TIMER_BASE_GEMM     0   /* y = x W^T and dx = dy W GEMMs */
 #define LORA_TIMER_LOGPROB_FWD   1   /* lm_head GEMM with online logsumexp */
 #define LORA_TIMER_LOGPROB_BWD   2   /* logit recompute + dh GEMMs */

@@ -34,12 +34,15 @@ lora_status hip_check(hipError_t e, const char* what) {
 lora_status launch_check(const char* what) { return hip_check(hipGetLastError(), what); }
 
 // ------------------------------------------------------------------ timing
+// Measurement hooks, per host thread: each thread that enables timing keeps its
+// own event pairs (created on first use, kept until the process ends), so the
+// calls stay free of shared mutable state.
 struct TimerState {
   bool on = false;
   std::vector<std::pair<hipEvent_t, hipEvent_t>> pairs[LORA_TIMER_COUNT];
   size_t used[LORA_TIMER_COUNT] = {};
 };
-static TimerState g_tim;
+static thread_local TimerState g_tim;
 
 void timer_begin(int timer, hipStream_t s) {
   if (!g_tim.on) return;
@@ -50,7 +53,7 @@ void timer_begin(int timer, hipStream_t s) {
     if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) return;
     v.emplace_back(a, b);
   }
-  hipEventRecord(v[u].first, s);
+  (void)hipEventRecord(v[u].first, s);
 }
 
 void timer_end(int timer, hipStream_t s) {
@@ -58,7 +61,7 @@ void timer_end(int timer, hipStream_t s) {
   auto& v = g_tim.pairs[timer];
   size_t& u = g_tim.used[timer];
   if (u >= v.size()) return;
-  hipEventRecord(v[u].second, s);
+  (void)hipEventRecord(v[u].second, s);
   ++u;
 }
 
@@ -448,56 +451,67 @@ lora_status loss_grad(int32_t kind, int64_t n, const float* logprobs, const floa
     return LORA_E_WORKSPACE;
   }
   return launch_loss(kind, n, logprobs, weights, advantages, sampler_logprobs, custom_g, lo, hi,
-                     (double*)((char*)ws + 256), loss_out, dlogp, S(stream));
+                     (double*)((char*)ws + 256), loss_out, dlogp, (int32_t*)ws, S(stream));
 }
 
 // ------------------------------------------------------------------ Adam
-lora_status adam_step(int64_t n, float* p, const float* g, float* m, float* v, int64_t step,
-                      float lr, float beta1, float beta2, float eps, float weight_decay,
-                      uint16_t* p_bf16, int32_t* status, void* stream) {
-  LORA_ARG_CHECK(n >= 0, "n must be >= 0");
-  LORA_ARG_CHECK(n == 0 || (p && g && m && v), "p/g/m/v NULL");
-  LORA_ARG_CHECK(step >= 1, "step must be >= 1 (1-based per-adapter counter)");
+size_t adam_workspace_bytes(int32_t n_seg) {
+  if (n_seg < 0) return 0;
+  return 256 + (size_t)lora::align_up(std::max<int64_t>(1, n_seg) * 4, 256);
+}
+
+static lora_status adam_run(int32_t n_seg, const int64_t* off, const int64_t* cnt,
+                            const int64_t* step, float* p, const float* g, float* m, float* v,
+                            float lr, float beta1, float beta2, float eps, float weight_decay,
+                            uint16_t* p_bf16, void* ws, size_t ws_bytes, hipStream_t s) {
   LORA_ARG_CHECK(beta1 >= 0.f && beta1 < 1.f && beta2 >= 0.f && beta2 < 1.f, "betas must lie in [0, 1)");
-  const double bc1 = 1.0 - std::pow((double)beta1, (double)step);
-  const double bc2 = 1.0 - std::pow((double)beta2, (double)step);
-  const float step_size = (float)((double)lr / bc1);
-  const float inv_sqrt_bc2 = (float)(1.0 / std::sqrt(bc2));
-  hipStream_t s = S(stream);
+  std::vector<float> ss(n_seg), ib(n_seg);
+  for (int i = 0; i < n_seg; ++i) {
+    LORA_ARG_CHECK(off[i] >= 0 && cnt[i] >= 0, "segment %d: negative offset/count", i);
+    LORA_ARG_CHECK(step[i] >= 1, "segment %d: step must be >= 1 (1-based per-adapter counter)", i);
+    const double bc1 = 1.0 - std::pow((double)beta1, (double)step[i]);
+    const double bc2 = 1.0 - std::pow((double)beta2, (double)step[i]);
+    ss[i] = (float)((double)lr / bc1);
+    ib[i] = (float)(1.0 / std::sqrt(bc2));
+  }
+  if (!ws || ws_bytes < adam_workspace_bytes(n_seg)) {
+    set_error("adam: workspace too small (need adam_workspace_bytes(%d))", n_seg);
+    return LORA_E_WORKSPACE;
+  }
+  if (n_seg == 0) return LORA_OK;
   timer_begin(LORA_TIMER_ADAM, s);
-  TRY(launch_adam(n, p, g, m, v, lr, beta1, beta2, eps, weight_decay, step_size, inv_sqrt_bc2,
-                  p_bf16, status, s));
+  TRY(launch_adam_multi(n_seg, off, cnt, ss.data(), ib.data(), p, g, m, v, lr, beta1, beta2, eps,
+                        weight_decay, p_bf16, (int32_t*)((char*)ws + 256), (int32_t*)ws, s));
   timer_end(LORA_TIMER_ADAM, s);
   return LORA_OK;
 }
 
+lora_status adam_step(int64_t n, float* p, const float* g, float* m, float* v, int64_t step,
+                      float lr, float beta1, float beta2, float eps, float weight_decay,
+                      uint16_t* p_bf16, void* ws, size_t ws_bytes, void* stream) {
+  LORA_ARG_CHECK(n >= 0, "n must be >= 0");
+  LORA_ARG_CHECK(n == 0 || (p && g && m && v), "p/g/m/v NULL");
+  const int64_t off = 0;
+  return adam_run(1, &off, &n, &step, p, g, m, v, lr, beta1, beta2, eps, weight_decay, p_bf16, ws,
+                  ws_bytes, S(stream));
+}
+
 lora_status adam_step_multi(int32_t n_seg, const adam_segment* segs, float* p, const float* g,
                             float* m, float* v, float lr, float beta1, float beta2, float eps,
-                            float weight_decay, uint16_t* p_bf16, int32_t* status,
+                            float weight_decay, uint16_t* p_bf16, void* ws, size_t ws_bytes,
                             void* stream) {
   LORA_ARG_CHECK(n_seg >= 0, "n_seg must be >= 0");
   if (n_seg == 0) return LORA_OK;
   LORA_ARG_CHECK(segs != nullptr, "segs is NULL");
   LORA_ARG_CHECK(p && g && m && v, "p/g/m/v NULL");
-  LORA_ARG_CHECK(beta1 >= 0.f && beta1 < 1.f && beta2 >= 0.f && beta2 < 1.f, "betas must lie in [0, 1)");
-  std::vector<int64_t> off(n_seg), cnt(n_seg);
-  std::vector<float> ss(n_seg), ib(n_seg);
+  std::vector<int64_t> off(n_seg), cnt(n_seg), step(n_seg);
   for (int i = 0; i < n_seg; ++i) {
-    LORA_ARG_CHECK(segs[i].offset >= 0 && segs[i].count >= 0, "segment %d: negative offset/count", i);
-    LORA_ARG_CHECK(segs[i].step >= 1, "segment %d: step must be >= 1", i);
     off[i] = segs[i].offset;
     cnt[i] = segs[i].count;
-    const double bc1 = 1.0 - std::pow((double)beta1, (double)segs[i].step);
-    const double bc2 = 1.0 - std::pow((double)beta2, (double)segs[i].step);
-    ss[i] = (float)((double)lr / bc1);
-    ib[i] = (float)(1.0 / std::sqrt(bc2));
+    step[i] = segs[i].step;
   }
-  hipStream_t s = S(stream);
-  timer_begin(LORA_TIMER_ADAM, s);
-  TRY(launch_adam_multi(n_seg, off.data(), cnt.data(), ss.data(), ib.data(), p, g, m, v, lr, beta1,
-                        beta2, eps, weight_decay, p_bf16, status, s));
-  timer_end(LORA_TIMER_ADAM, s);
-  return LORA_OK;
+  return adam_run(n_seg, off.data(), cnt.data(), step.data(), p, g, m, v, lr, beta1, beta2, eps,
+                  weight_decay, p_bf16, ws, ws_bytes, S(stream));
 }
 
 // ------------------------------------------------------------------ SwiGLU

@@ -1134,14 +1134,8 @@ static lora_status launch_gemm(const uint16_t* A, const uint16_t* B, int M, int 
   }
   if (group_m <= 0) group_m = pick_group_m(tiles_m);
   if (group_m > tiles_m) group_m = tiles_m;
-  const size_t lds = 0;  // operand tiles are static LDS objects
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipFuncSetAttribute((const void*)gemm_nt_kernel<EPI>,
-                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    attr_set = true;
-  }
-  hipLaunchKernelGGL(gemm_nt_kernel<EPI>, dim3(tiles_m * tiles_n), dim3(GTHREADS), lds, s, A, B, M, N,
+  // operand tiles are static LDS objects: no dynamic LDS
+  hipLaunchKernelGGL(gemm_nt_kernel<EPI>, dim3(tiles_m * tiles_n), dim3(GTHREADS), 0, s, A, B, M, N,
                      K, lda, ldb, ep, tiles_m, tiles_n, group_m);
   return launch_check("gemm_nt");
 }

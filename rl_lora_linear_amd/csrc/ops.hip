@@ -1,6 +1,8 @@
 // Bandwidth-bound kernels of the hot path on gfx950: the logsumexp merge, the
 // token loss, per-adapter AdamW, the SwiGLU glue, and a bf16 transpose for
 // keeping frozen operands in both layouts.
+#include <vector>
+
 #include "common.hpp"
 #include "sgmv.hpp"
 
@@ -74,7 +76,14 @@ __global__ __launch_bounds__(64 * MERGE_WAVES) void logprob_merge_kernel(
 // 1024 rows per block (4 per thread); the block's loss terms are summed in
 // fp64 by a fixed tree; a second single-block pass sums the block partials in
 // block order.  The result depends only on n and the inputs.
+// Rows are kept where the weight / mask is non-zero.  A kept row whose own
+// inputs to its loss term are not all finite (l, and w, A, l_sampler or g as
+// the kind reads them) is removed by selection like a masked row and raises
+// LORA_FLAG_NONFINITE_LOSS (TPU RL note, section 12: NaN-logprob sentinel,
+// weight zeroed and value neutralised).
 constexpr int LOSS_ROWS = 1024;
+
+__device__ __forceinline__ bool fin(float x) { return __builtin_isfinite(x); }
 
 __global__ __launch_bounds__(256) void loss_rows_kernel(int kind, int64_t n,
                                                         const float* __restrict__ logp,
@@ -83,9 +92,11 @@ __global__ __launch_bounds__(256) void loss_rows_kernel(int kind, int64_t n,
                                                         const float* __restrict__ samp,
                                                         const float* __restrict__ g, float clip_lo,
                                                         float clip_hi, double* __restrict__ partial,
-                                                        float* __restrict__ dlogp) {
+                                                        float* __restrict__ dlogp,
+                                                        int32_t* __restrict__ status) {
   __shared__ double red[256];
   double acc = 0.0;
+  bool sentinel = false;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int64_t t = (int64_t)blockIdx.x * LOSS_ROWS + q * 256 + threadIdx.x;
@@ -96,32 +107,45 @@ __global__ __launch_bounds__(256) void loss_rows_kernel(int kind, int64_t n,
     if (wt != 0.f) {  // masked rows are removed by selection
       const float l = logp[t];
       if (kind == LOSS_CROSS_ENTROPY) {
-        d = -wt;
-        term = -(double)wt * (double)l;
+        if (fin(l) && fin(wt)) {
+          d = -wt;
+          term = -(double)wt * (double)l;
+        } else {
+          sentinel = true;
+        }
       } else if (kind == LOSS_CUSTOM) {
         const float gg = g[t];
-        d = gg;
-        term = (double)gg * (double)l;
-      } else {
-        const float A = adv[t];
-        const float rho = exp2f((l - samp[t]) * kLog2eF);
-        const float ra = rho * A;
-        if (kind == LOSS_IMPORTANCE_SAMPLING) {
-          d = -ra;
-          term = -(double)ra;
+        if (fin(l) && fin(wt) && fin(gg)) {
+          d = gg;
+          term = (double)gg * (double)l;
         } else {
-          const float lo = 1.f - clip_lo, hi = 1.f + clip_hi;
-          const float rc = fminf(fmaxf(rho, lo), hi);
-          const float obj = fminf(ra, rc * A);
-          const bool inactive = (A > 0.f && rho > hi) || (A < 0.f && rho < lo);
-          d = inactive ? 0.f : -ra;
-          term = -(double)obj;
+          sentinel = true;
+        }
+      } else {
+        const float A = adv[t], ls = samp[t];
+        if (fin(l) && fin(wt) && fin(A) && fin(ls)) {
+          const float rho = exp2f((l - ls) * kLog2eF);
+          const float ra = rho * A;
+          if (kind == LOSS_IMPORTANCE_SAMPLING) {
+            d = -ra;
+            term = -(double)ra;
+          } else {
+            const float lo = 1.f - clip_lo, hi = 1.f + clip_hi;
+            const float rc = fminf(fmaxf(rho, lo), hi);
+            const float obj = fminf(ra, rc * A);
+            const bool inactive = (A > 0.f && rho > hi) || (A < 0.f && rho < lo);
+            d = inactive ? 0.f : -ra;
+            term = -(double)obj;
+          }
+        } else {
+          sentinel = true;
         }
       }
     }
     dlogp[t] = d;
     acc += term;
   }
+  if (__any(sentinel) && (threadIdx.x & 63) == 0) set_flag(status, LORA_FLAG_NONFINITE_LOSS);
   red[threadIdx.x] = acc;
   __syncthreads();
   for (int o = 128; o > 0; o >>= 1) {
@@ -146,15 +170,15 @@ __global__ __launch_bounds__(256) void loss_sum_kernel(const double* __restrict_
 }
 
 // ------------------------------------------------------------------ AdamW
-// An element whose gradient is not finite is not updated (p, m, v keep their
-// values, so a NaN or Inf cannot spread into the state); `bad` records it.
+// One adapter's update is all or nothing (TPU RL note, section 12: a
+// non-finite optimizer update is skipped outright).  Three launches: clear the
+// per-segment skip flags, scan each segment's gradient for NaN/Inf (any block
+// that sees one sets its segment's flag and the status word), then update
+// every segment whose flag is clear.  The scan costs one extra read of g
+// (4 of the 34 bytes moved per parameter).
 __device__ __forceinline__ void adam_one(float& p, float g, float& m, float& v, float lr,
                                          float b1, float b2, float eps, float wd, float step_size,
-                                         float inv_sqrt_bc2, bool& bad) {
-  if (!__builtin_isfinite(g)) {
-    bad = true;
-    return;
-  }
+                                         float inv_sqrt_bc2) {
   m = b1 * m + (1.f - b1) * g;
   v = b2 * v + (1.f - b2) * g * g;
   p = p - lr * wd * p;
@@ -162,57 +186,10 @@ __device__ __forceinline__ void adam_one(float& p, float g, float& m, float& v, 
   p = p - step_size * __fdiv_rn(m, denom);
 }
 
-// one atomic per wave that skipped an element
-__device__ __forceinline__ void report_nonfinite(bool bad, int32_t* status) {
-  if (status && __any(bad) && (threadIdx.x & 63) == 0) atomicOr(status, LORA_FLAG_NONFINITE_GRAD);
-}
-
-template <bool VEC>
-__global__ __launch_bounds__(256) void adam_kernel(int64_t n, float* __restrict__ p,
-                                                   const float* __restrict__ g,
-                                                   float* __restrict__ m, float* __restrict__ v,
-                                                   float lr, float b1, float b2, float eps,
-                                                   float wd, float step_size, float inv_sqrt_bc2,
-                                                   uint16_t* __restrict__ pb,
-                                                   int32_t* __restrict__ status) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  bool bad = false;
-  if (VEC) {
-    const int64_t n4 = n / 4;
-    for (int64_t i = i0; i < n4; i += stride) {
-      float4 pp = ((float4*)p)[i], mm = ((float4*)m)[i], vv = ((float4*)v)[i];
-      const float4 gg = ((const float4*)g)[i];
-      adam_one(pp.x, gg.x, mm.x, vv.x, lr, b1, b2, eps, wd, step_size, inv_sqrt_bc2, bad);
-      adam_one(pp.y, gg.y, mm.y, vv.y, lr, b1, b2, eps, wd, step_size, inv_sqrt_bc2, bad);
-      adam_one(pp.z, gg.z, mm.z, vv.z, lr, b1, b2, eps, wd, step_size, inv_sqrt_bc2, bad);
-      adam_one(pp.w, gg.w, mm.w, vv.w, lr, b1, b2, eps, wd, step_size, inv_sqrt_bc2, bad);
-      ((float4*)p)[i] = pp;
-      ((float4*)m)[i] = mm;
-      ((float4*)v)[i] = vv;
-      if (pb) ((uint2*)pb)[i] = make_uint2(pack2bf(pp.x, pp.y), pack2bf(pp.z, pp.w));
-    }
-    for (int64_t i = n4 * 4 + i0; i < n; i += stride) {
-      float pp = p[i], mm = m[i], vv = v[i];
-      adam_one(pp, g[i], mm, vv, lr, b1, b2, eps, wd, step_size, inv_sqrt_bc2, bad);
-      p[i] = pp; m[i] = mm; v[i] = vv;
-      if (pb) pb[i] = f2bf(pp);
-    }
-  } else {
-    for (int64_t i = i0; i < n; i += stride) {
-      float pp = p[i], mm = m[i], vv = v[i];
-      adam_one(pp, g[i], mm, vv, lr, b1, b2, eps, wd, step_size, inv_sqrt_bc2, bad);
-      p[i] = pp; m[i] = mm; v[i] = vv;
-      if (pb) pb[i] = f2bf(pp);
-    }
-  }
-  report_nonfinite(bad, status);
-}
-
-// Batched AdamW: up to ADAM_SEGS segments per launch, described in the kernel
-// arguments.  Block b belongs to the segment whose block range holds it; each
-// block streams 4 x 256 x 4 elements with float4 vectors (scalar path if a
-// segment is not 16-byte aligned).
+// Up to ADAM_SEGS segments per launch, described in the kernel arguments.
+// Block b belongs to the segment whose block range holds it; each block covers
+// 4 x 256 x 4 elements with float4 vectors (scalar path if a segment is not
+// 16-byte aligned).
 constexpr int ADAM_SEGS = 64;
 constexpr int ADAM_BLOCK_ELEMS = 4096;
 struct AdamSegs {
@@ -222,7 +199,46 @@ struct AdamSegs {
   float step_size[ADAM_SEGS];
   float inv_sqrt_bc2[ADAM_SEGS];
   int32_t n;
+  int32_t seg0;   // index of segment 0 of this launch in the caller's list (flag slot)
 };
+
+__device__ __forceinline__ int adam_seg_of(const AdamSegs& sg, int b) {
+  int s = 0;
+  while (s + 1 < sg.n && sg.blk0[s + 1] <= b) ++s;
+  return s;
+}
+
+__global__ __launch_bounds__(256) void adam_check_kernel(AdamSegs sg, const float* __restrict__ g,
+                                                         int32_t* __restrict__ skip,
+                                                         int32_t* __restrict__ status) {
+  const int b = blockIdx.x;
+  const int s = adam_seg_of(sg, b);
+  const int64_t base = sg.off[s];
+  const int64_t n = sg.cnt[s];
+  const int64_t e0 = (int64_t)(b - sg.blk0[s]) * ADAM_BLOCK_ELEMS;
+  bool bad = false;
+  if (((base & 3) == 0) && ((uintptr_t)g % 16 == 0)) {
+#pragma unroll
+    for (int q = 0; q < ADAM_BLOCK_ELEMS / 1024; ++q) {
+      const int64_t e = e0 + ((int64_t)q * 256 + threadIdx.x) * 4;
+      if (e + 4 <= n) {
+        const float4 gg = ((const float4*)(g + base))[e / 4];
+        bad |= !__builtin_isfinite(gg.x) || !__builtin_isfinite(gg.y) ||
+               !__builtin_isfinite(gg.z) || !__builtin_isfinite(gg.w);
+      } else {
+        for (int64_t k = e; k < n && k < e + 4; ++k) bad |= !__builtin_isfinite(g[base + k]);
+      }
+    }
+  } else {
+    for (int64_t k = e0 + threadIdx.x; k < min(n, e0 + ADAM_BLOCK_ELEMS); k += 256)
+      bad |= !__builtin_isfinite(g[base + k]);
+  }
+  // one store per wave that saw a bad element (every writer stores the same 1)
+  if (__any(bad) && (threadIdx.x & 63) == 0) {
+    skip[sg.seg0 + s] = 1;
+    if (status) set_flag(status, LORA_FLAG_NONFINITE_GRAD);
+  }
+}
 
 __global__ __launch_bounds__(256) void adam_multi_kernel(AdamSegs sg, float* __restrict__ p,
                                                          const float* __restrict__ g,
@@ -230,11 +246,10 @@ __global__ __launch_bounds__(256) void adam_multi_kernel(AdamSegs sg, float* __r
                                                          float* __restrict__ v, float lr, float b1,
                                                          float b2, float eps, float wd,
                                                          uint16_t* __restrict__ pb,
-                                                         int32_t* __restrict__ status) {
+                                                         const int32_t* __restrict__ skip) {
   const int b = blockIdx.x;
-  bool bad = false;
-  int s = 0;
-  while (s + 1 < sg.n && sg.blk0[s + 1] <= b) ++s;
+  const int s = adam_seg_of(sg, b);
+  if (skip[sg.seg0 + s]) return;   // block-uniform: this adapter's update is skipped
   const int64_t base = sg.off[s];
   const int64_t n = sg.cnt[s];
   const float ss = sg.step_size[s], ib = sg.inv_sqrt_bc2[s];
@@ -248,10 +263,10 @@ __global__ __launch_bounds__(256) void adam_multi_kernel(AdamSegs sg, float* __r
         const int64_t i = (base + e) / 4;
         float4 pp = ((float4*)p)[i], mm = ((float4*)m)[i], vv = ((float4*)v)[i];
         const float4 gg = ((const float4*)g)[i];
-        adam_one(pp.x, gg.x, mm.x, vv.x, lr, b1, b2, eps, wd, ss, ib, bad);
-        adam_one(pp.y, gg.y, mm.y, vv.y, lr, b1, b2, eps, wd, ss, ib, bad);
-        adam_one(pp.z, gg.z, mm.z, vv.z, lr, b1, b2, eps, wd, ss, ib, bad);
-        adam_one(pp.w, gg.w, mm.w, vv.w, lr, b1, b2, eps, wd, ss, ib, bad);
+        adam_one(pp.x, gg.x, mm.x, vv.x, lr, b1, b2, eps, wd, ss, ib);
+        adam_one(pp.y, gg.y, mm.y, vv.y, lr, b1, b2, eps, wd, ss, ib);
+        adam_one(pp.z, gg.z, mm.z, vv.z, lr, b1, b2, eps, wd, ss, ib);
+        adam_one(pp.w, gg.w, mm.w, vv.w, lr, b1, b2, eps, wd, ss, ib);
         ((float4*)p)[i] = pp;
         ((float4*)m)[i] = mm;
         ((float4*)v)[i] = vv;
@@ -266,7 +281,7 @@ __global__ __launch_bounds__(256) void adam_multi_kernel(AdamSegs sg, float* __r
       } else {
         for (int64_t k = e; k < n && k < e + 4; ++k) {
           float pp = p[base + k], mm = m[base + k], vv = v[base + k];
-          adam_one(pp, g[base + k], mm, vv, lr, b1, b2, eps, wd, ss, ib, bad);
+          adam_one(pp, g[base + k], mm, vv, lr, b1, b2, eps, wd, ss, ib);
           p[base + k] = pp; m[base + k] = mm; v[base + k] = vv;
           if (pb) pb[base + k] = f2bf(pp);
         }
@@ -275,12 +290,11 @@ __global__ __launch_bounds__(256) void adam_multi_kernel(AdamSegs sg, float* __r
   } else {
     for (int64_t k = e0 + threadIdx.x; k < min(n, e0 + ADAM_BLOCK_ELEMS); k += 256) {
       float pp = p[base + k], mm = m[base + k], vv = v[base + k];
-      adam_one(pp, g[base + k], mm, vv, lr, b1, b2, eps, wd, ss, ib, bad);
+      adam_one(pp, g[base + k], mm, vv, lr, b1, b2, eps, wd, ss, ib);
       p[base + k] = pp; m[base + k] = mm; v[base + k] = vv;
       if (pb) pb[base + k] = f2bf(pp);
     }
   }
-  report_nonfinite(bad, status);
 }
 
 // ------------------------------------------------------------------ SwiGLU
@@ -385,11 +399,12 @@ lora_status launch_logprob_merge(const float* part_m, const float* part_s, const
 
 lora_status launch_loss(int kind, int64_t n, const float* logp, const float* w, const float* adv,
                         const float* samp, const float* g, float clip_lo, float clip_hi,
-                        double* partial, float* loss_out, float* dlogp, hipStream_t s) {
+                        double* partial, float* loss_out, float* dlogp, int32_t* status,
+                        hipStream_t s) {
   const int64_t nb = cdiv(n, LOSS_ROWS);
   if (nb > 0) {
     hipLaunchKernelGGL(loss_rows_kernel, dim3((unsigned)nb), dim3(256), 0, s, kind, n, logp, w,
-                       adv, samp, g, clip_lo, clip_hi, partial, dlogp);
+                       adv, samp, g, clip_lo, clip_hi, partial, dlogp, status);
     lora_status st = launch_check("loss_rows");
     if (st) return st;
   }
@@ -397,30 +412,19 @@ lora_status launch_loss(int kind, int64_t n, const float* logp, const float* w, 
   return launch_check("loss_sum");
 }
 
-lora_status launch_adam(int64_t n, float* p, const float* g, float* m, float* v, float lr,
-                        float beta1, float beta2, float eps, float wd, float step_size,
-                        float inv_sqrt_bc2, uint16_t* p_bf16, int32_t* status, hipStream_t s) {
-  if (n <= 0) return LORA_OK;
-  const bool vec = ((uintptr_t)p | (uintptr_t)g | (uintptr_t)m | (uintptr_t)v) % 16 == 0 &&
-                   (p_bf16 == nullptr || (uintptr_t)p_bf16 % 8 == 0);
-  const unsigned grid = grid_for(vec ? n / 4 : n, 256, 2048);
-  if (vec)
-    hipLaunchKernelGGL(adam_kernel<true>, dim3(grid), dim3(256), 0, s, n, p, g, m, v, lr, beta1,
-                       beta2, eps, wd, step_size, inv_sqrt_bc2, p_bf16, status);
-  else
-    hipLaunchKernelGGL(adam_kernel<false>, dim3(grid), dim3(256), 0, s, n, p, g, m, v, lr, beta1,
-                       beta2, eps, wd, step_size, inv_sqrt_bc2, p_bf16, status);
-  return launch_check("adam");
-}
-
 lora_status launch_adam_multi(int n_seg, const int64_t* off, const int64_t* cnt,
                               const float* step_size, const float* inv_sqrt_bc2, float* p,
                               const float* g, float* m, float* v, float lr, float beta1,
-                              float beta2, float eps, float wd, uint16_t* p_bf16, int32_t* status,
-                              hipStream_t s) {
+                              float beta2, float eps, float wd, uint16_t* p_bf16, int32_t* skip,
+                              int32_t* status, hipStream_t s) {
+  lora_status st = launch_fill_i32(skip, n_seg, 0, s);
+  if (st) return st;
+  std::vector<AdamSegs> launches;
+  std::vector<int32_t> blocks_of;
   for (int s0 = 0; s0 < n_seg; s0 += ADAM_SEGS) {
     AdamSegs sg{};
     sg.n = std::min(ADAM_SEGS, n_seg - s0);
+    sg.seg0 = s0;
     int32_t blocks = 0;
     for (int i = 0; i < sg.n; ++i) {
       sg.off[i] = off[s0 + i];
@@ -432,9 +436,19 @@ lora_status launch_adam_multi(int n_seg, const int64_t* off, const int64_t* cnt,
     }
     sg.blk0[sg.n] = blocks;
     if (blocks == 0) continue;
-    hipLaunchKernelGGL(adam_multi_kernel, dim3(blocks), dim3(256), 0, s, sg, p, g, m, v, lr, beta1,
-                       beta2, eps, wd, p_bf16, status);
-    lora_status st = launch_check("adam_multi");
+    launches.push_back(sg);
+    blocks_of.push_back(blocks);
+  }
+  for (size_t i = 0; i < launches.size(); ++i) {
+    hipLaunchKernelGGL(adam_check_kernel, dim3(blocks_of[i]), dim3(256), 0, s, launches[i], g, skip,
+                       status);
+    st = launch_check("adam_check");
+    if (st) return st;
+  }
+  for (size_t i = 0; i < launches.size(); ++i) {
+    hipLaunchKernelGGL(adam_multi_kernel, dim3(blocks_of[i]), dim3(256), 0, s, launches[i], p, g, m,
+                       v, lr, beta1, beta2, eps, wd, p_bf16, skip);
+    st = launch_check("adam_multi");
     if (st) return st;
   }
   return LORA_OK;

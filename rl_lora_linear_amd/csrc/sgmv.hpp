@@ -119,15 +119,14 @@ lora_status launch_logprob_merge(const float* part_m, const float* part_s, const
                                  float* logprobs, float* lse, int32_t* status, hipStream_t s);
 lora_status launch_loss(int kind, int64_t n, const float* logp, const float* w, const float* adv,
                         const float* samp, const float* g, float clip_lo, float clip_hi,
-                        double* partial, float* loss_out, float* dlogp, hipStream_t s);
-lora_status launch_adam(int64_t n, float* p, const float* g, float* m, float* v, float lr,
-                        float beta1, float beta2, float eps, float wd, float step_size,
-                        float inv_sqrt_bc2, uint16_t* p_bf16, int32_t* status, hipStream_t s);
+                        double* partial, float* loss_out, float* dlogp, int32_t* status,
+                        hipStream_t s);
+// skip: n_seg int32 per-segment flags (cleared, then 1 where the update is skipped)
 lora_status launch_adam_multi(int n_seg, const int64_t* off, const int64_t* cnt,
                               const float* step_size, const float* inv_sqrt_bc2, float* p,
                               const float* g, float* m, float* v, float lr, float beta1,
-                              float beta2, float eps, float wd, uint16_t* p_bf16, int32_t* status,
-                              hipStream_t s);
+                              float beta2, float eps, float wd, uint16_t* p_bf16, int32_t* skip,
+                              int32_t* status, hipStream_t s);
 lora_status launch_swiglu_fwd(int64_t n, const uint16_t* g, const uint16_t* u, uint16_t* h,
                               hipStream_t s);
 lora_status launch_swiglu_bwd(int64_t n, const uint16_t* dh, const uint16_t* g,

@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_HERE, "liblora_mi355x.so")
 # status codes and flags (include/lora_mi355x.h)
 LORA_OK, LORA_E_INVALID_ARG, LORA_E_UNSUPPORTED, LORA_E_WORKSPACE, LORA_E_HIP, LORA_E_DEVICE_CHECK = range(6)
 FLAG_ID_RANGE, FLAG_UNSORTED, FLAG_TARGET_RANGE, FLAG_BAD_DESC = 0x1, 0x2, 0x4, 0x8
-FLAG_NONFINITE_GRAD = 0x10
+FLAG_NONFINITE_GRAD, FLAG_NONFINITE_LOSS = 0x10, 0x20
 IDS_SORTED, IDS_INTERLEAVED = 0, 1
 LOSS_CROSS_ENTROPY, LOSS_IMPORTANCE_SAMPLING, LOSS_PPO, LOSS_CUSTOM = range(4)
 TIMER_BASE_GEMM, TIMER_LOGPROB_FWD, TIMER_LOGPROB_BWD, TIMER_SHRINK, TIMER_EXPAND, TIMER_GRAD, TIMER_ADAM = range(7)
@@ -31,7 +31,8 @@ EXPORTS = [
     "lora_segments_workspace_bytes", "lora_segments", "lora_transpose_bf16", "lora_forward",
     "lora_backward", "token_logprobs_workspace_bytes", "token_logprobs",
     "token_logprobs_backward_workspace_bytes", "token_logprobs_backward",
-    "loss_grad_workspace_bytes", "loss_grad", "adam_step", "adam_step_multi", "swiglu_forward",
+    "loss_grad_workspace_bytes", "loss_grad", "adam_workspace_bytes", "adam_step",
+    "adam_step_multi", "swiglu_forward",
     "swiglu_backward", "bf16_add", "moe_route", "moe_workspace_bytes", "moe_saved_bytes", "moe_forward",
     "moe_backward", "mlp_workspace_bytes", "mlp_saved_bytes", "mlp_forward", "mlp_backward",
     "lora_timing_enable", "lora_timing_reset", "lora_timing_read",
@@ -106,9 +107,10 @@ def _load() -> ctypes.CDLL:
         "loss_grad_workspace_bytes": (_SZ, [_I64]),
         "loss_grad": (_I32, [_I32, _I64, _P, _P, _P, _P, _P, ctypes.POINTER(LossConfig), _P, _P, _P,
                              _SZ, _P]),
-        "adam_step": (_I32, [_I64, _P, _P, _P, _P, _I64, _F, _F, _F, _F, _F, _P, _P, _P]),
+        "adam_workspace_bytes": (_SZ, [_I32]),
+        "adam_step": (_I32, [_I64, _P, _P, _P, _P, _I64, _F, _F, _F, _F, _F, _P, _P, _SZ, _P]),
         "adam_step_multi": (_I32, [_I32, ctypes.POINTER(AdamSegment), _P, _P, _P, _P, _F, _F, _F, _F,
-                                   _F, _P, _P, _P]),
+                                   _F, _P, _P, _SZ, _P]),
         "swiglu_forward": (_I32, [_I64, _P, _P, _P, _P]),
         "bf16_add": (_I32, [_I64, _P, _P, _P, _P]),
         "moe_route": (_I32, [_I64, _I32, _I32, _P, _P, _P, _P]),
@@ -257,17 +259,34 @@ def loss_grad(kind, logprobs, weights, advantages, sampler_logprobs, custom_g, c
                          _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
+def adam_workspace_bytes(n_seg: int) -> int:
+    return LIB.adam_workspace_bytes(n_seg)
+
+
+def adam_skip_flags(ws: torch.Tensor, n_seg: int) -> np.ndarray:
+    """Per-segment skip flags of the latest AdamW call on this workspace
+    (int32 at byte 256 + 4 i: 1 = skipped, 0 = stepped); synchronises."""
+    torch.cuda.synchronize()
+    return ws[256:256 + 4 * n_seg].cpu().numpy().view(np.int32).copy()
+
+
 def adam_step(p, g, m, v, step, lr, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0,
-              p_bf16=None, status=None, stream=None):
-    """status: optional device int32 tensor; FLAG_NONFINITE_GRAD is OR-ed into it
-    when elements with a NaN or Inf gradient were skipped."""
+              p_bf16=None, ws=None, stream=None):
+    """ws: workspace of adam_workspace_bytes(1) (a fresh zeroed one if None).
+    A gradient holding NaN or Inf skips the whole step and sets
+    FLAG_NONFINITE_GRAD in the workspace status word."""
+    if ws is None:
+        ws = empty_workspace(adam_workspace_bytes(1), device=p.device)
     _check(LIB.adam_step(p.numel(), _ptr(p), _ptr(g), _ptr(m), _ptr(v), int(step), lr, beta1,
-                         beta2, eps, weight_decay, _ptr(p_bf16), _ptr(status), _stream(stream)))
+                         beta2, eps, weight_decay, _ptr(p_bf16), _ptr(ws), _nbytes(ws),
+                         _stream(stream)))
+    return ws
 
 
 def adam_step_multi(segments, p, g, m, v, lr, beta1=0.9, beta2=0.999, eps=1e-8,
-                    weight_decay=0.0, p_bf16=None, status=None, stream=None):
-    """segments: list of (offset, count, step) into the flat p/g/m/v buffers."""
+                    weight_decay=0.0, p_bf16=None, ws=None, stream=None):
+    """segments: list of (offset, count, step) into the flat p/g/m/v buffers.
+    ws: workspace of adam_workspace_bytes(len(segments)) (fresh if None)."""
     n = p.numel()
     for t in (g, m, v):
         if t.numel() != n:
@@ -277,10 +296,13 @@ def adam_step_multi(segments, p, g, m, v, lr, beta1=0.9, beta2=0.999, eps=1e-8,
     for o, c, _ in segments:
         if o < 0 or c < 0 or o + c > n:
             raise LoraError(LORA_E_INVALID_ARG, f"segment ({o}, {c}) outside a buffer of {n}")
+    if ws is None:
+        ws = empty_workspace(adam_workspace_bytes(len(segments)), device=p.device)
     arr = (AdamSegment * max(1, len(segments)))(*[AdamSegment(int(o), int(c), int(t)) for o, c, t in segments])
     _check(LIB.adam_step_multi(len(segments), arr, _ptr(p), _ptr(g), _ptr(m), _ptr(v), lr, beta1,
-                               beta2, eps, weight_decay, _ptr(p_bf16), _ptr(status),
+                               beta2, eps, weight_decay, _ptr(p_bf16), _ptr(ws), _nbytes(ws),
                                _stream(stream)))
+    return ws
 
 
 def bf16_add(a, b, out, stream=None):

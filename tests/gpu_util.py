@@ -26,6 +26,26 @@ def rel_err(gpu, ora) -> float:
     return float(np.max(np.abs(g - o) / den))
 
 
+def l2_rel(gpu, ora) -> float:
+    """||gpu - ora||_2 / ||ora||_2 (0 for an all-zero reference matched exactly)."""
+    g = np.asarray(gpu, np.float64).reshape(-1)
+    o = np.asarray(ora, np.float64).reshape(-1)
+    n = float(np.linalg.norm(o))
+    d = float(np.linalg.norm(g - o))
+    return d / n if n > 0 else d
+
+
+def check_chained(gpu, ora, what=""):
+    """An fp32 result that the fused layers derive from bf16 stage tensors,
+    against the plain float64 definition: the norm-wise relative error within
+    the bf16 tolerance, and no element beyond 2.5x that tolerance (the
+    elementwise metric's maximum over ~10^6 elements of a sum of bf16 rounding
+    errors reaches ~4.5 standard deviations)."""
+    m, l2 = rel_err(gpu, ora), l2_rel(gpu, ora)
+    print(f"[chained] {what}: max {m:.3g} l2 {l2:.3g}", flush=True)
+    assert l2 < TOL_BF16 and m < 2.5 * TOL_BF16, (what, m, l2)
+
+
 def dev_bf16(bits: np.ndarray, device="cuda") -> torch.Tensor:
     bits = np.ascontiguousarray(bits, dtype=np.uint16)
     return torch.from_numpy(bits.view(np.int16)).to(device).view(torch.bfloat16)

@@ -65,7 +65,10 @@ def test_host_validation_returns_before_any_launch(L):
     assert lib.token_logprobs(10, 128, 1024, P, P, P, P, P, P, 16, None) == L.LORA_E_WORKSPACE
     assert lib.loss_grad(9, 10, P, P, P, P, P, None, P, P, P, 1 << 20, None) == L.LORA_E_INVALID_ARG
     assert lib.loss_grad(L.LOSS_PPO, 10, P, P, P, P, P, None, P, P, P, 1 << 20, None) == L.LORA_E_INVALID_ARG
-    assert lib.adam_step(10, P, P, P, P, 0, 1e-3, 0.9, 0.999, 1e-8, 0.0, None, None, None) == L.LORA_E_INVALID_ARG
+    assert lib.adam_step(10, P, P, P, P, 0, 1e-3, 0.9, 0.999, 1e-8, 0.0, None, P, 1 << 12, None) == L.LORA_E_INVALID_ARG
+    assert lib.adam_step(10, P, P, P, P, 1, 1e-3, 0.9, 0.999, 1e-8, 0.0, None, P, 16, None) == L.LORA_E_WORKSPACE
+    assert lib.adam_step(10, P, P, P, P, 1, 1e-3, 0.9, 0.999, 1e-8, 0.0, None, None, 1 << 12, None) == L.LORA_E_WORKSPACE
+    assert lib.adam_workspace_bytes(70) >= 256 + 4 * 70 and lib.adam_workspace_bytes(-1) == 0
     assert lib.lora_segments(P, 10, 0, 0, P, P, P, 1 << 20, None) == L.LORA_E_INVALID_ARG
     assert lib.lora_transpose_bf16(P, ctypes.c_void_p(32), 100, 64, None) == L.LORA_E_UNSUPPORTED
     assert lib.lora_timing_read(99, None, None) == L.LORA_E_INVALID_ARG

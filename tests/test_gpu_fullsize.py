@@ -3,8 +3,9 @@ same inputs and launch configuration, checked on sampled outputs the oracle
 computes one by one.  Rows are independent through every projection, so a
 sampled row's output is exact from the row alone; an adapter's (or an
 (expert, adapter) pair's) gradient is the sum over its own rows, computed
-whole.  Through the fused expert and MLP layers the oracle continues from the
-GPU's stored stage bits, as in the small-size tests."""
+whole.  The fused expert and MLP layers are compared with the plain oracle
+(end to end, bf16 tolerance) and, per stage, with oracle.lora / oracle.mlp
+calls on the GPU's own stored stage bits, as in the small-size tests."""
 import numpy as np
 import pytest
 import torch
@@ -15,16 +16,13 @@ import oracle.lora as OL
 import oracle.moe as OE
 import workloads as W
 import workloads.device as WD
-from gpu_util import TOL_BF16, TOL_F32, DevLayer, f64_of, rel_err
+from gpu_util import TOL_BF16, TOL_F32, DevLayer, check_chained, f64_of, rel_err
+from test_gpu_moe import staged_parity
 
 pytestmark = pytest.mark.gpu
 if not torch.cuda.is_available():
     pytest.skip("needs a GPU", allow_module_level=True)
 L = pytest.importorskip("rl_lora_linear_amd.lib")
-
-
-def _bf16(v):
-    return W.bf16_bits_to_f64(W.to_bf16_bits(v))
 
 
 # ---------------------------------------------------------------- q/o projection
@@ -52,28 +50,6 @@ def test_qo_proj_full_size():
 
 
 # ---------------------------------------------------------------- expert layers
-class _Stage:
-    """oracle.moe store hook over a subset batch: subset assignment j is the
-    layer's position posmap[j]; stages the layer keeps continue from its bits
-    (and are recorded for comparison), the others are rounded to bf16."""
-
-    def __init__(self, posmap, fetch):
-        self.posmap, self.fetch, self.rec = posmap, fetch, {}
-
-    def __call__(self, name, js, v):
-        if name in self.fetch:
-            g = self.fetch[name](self.posmap[js])
-            self.rec.setdefault(name, []).append((g, v))
-            return g
-        return _bf16(v)
-
-    def check(self):
-        for name, pairs in self.rec.items():
-            g = np.concatenate([a for a, _ in pairs])
-            v = np.concatenate([b for _, b in pairs])
-            assert rel_err(g, v) < TOL_BF16, name
-
-
 def _stage_fetch(saved, trace, NK, F):
     """Row fetchers (positions -> float64 rows) for the saved [gate | up] and h
     rows and the backward trace (dh, [dgate | dup])."""
@@ -158,20 +134,25 @@ class _PairAB:
 def _expert_parity(x, dy, experts, weights, ids, y, dx, grads, Wg, Wu, Wd, pair, scale_of,
                    pos, fetch, n_ad, K, tokens, pair_key, grad_view):
     """Sampled tokens (y, dx, every stage of their assignments) and one (expert,
-    adapter) pair's dA, dB, all against oracle.moe on subset batches."""
+    adapter) pair's dA, dB: against oracle.moe's plain definition on subset
+    batches (gpu_util.check_chained: the results carry the layer's bf16 stage
+    roundings), and per stage against oracle.lora / oracle.mlp on the GPU's own
+    stage bits (bf16 stages at the bf16 tolerance, the pair's gradients at the
+    fp32 tolerance)."""
     # sampled tokens, all K assignments each
     ts = np.asarray(tokens)
     posmap = pos[(ts[:, None] * K + np.arange(K)[None, :]).reshape(-1)]
     params, ex_l, ids_l, _, _ = _subset_params(Wg, Wu, Wd, pair, experts[ts], ids[ts],
                                                scale_of(int(ids[ts][0])))
-    st = _Stage(posmap, fetch)
     x_s = f64_of(x[torch.from_numpy(ts).cuda()])
     dy_s = f64_of(dy[torch.from_numpy(ts).cuda()])
-    y_ref, saved = OE.moe_forward(x_s, ex_l, weights[ts], ids_l, *params, store=st)
-    assert rel_err(f64_of(y)[ts], y_ref) < TOL_BF16
-    dx_ref, _, _ = OE.moe_backward(dy_s, x_s, ex_l, weights[ts], ids_l, *params, saved, store=st)
-    assert rel_err(f64_of(dx)[ts], dx_ref) < TOL_BF16
-    st.check()
+    y_ref, saved = OE.moe_forward(x_s, ex_l, weights[ts], ids_l, *params)
+    check_chained(f64_of(y)[ts], y_ref, "y")
+    dx_ref, _, _ = OE.moe_backward(dy_s, x_s, ex_l, weights[ts], ids_l, *params, saved)
+    check_chained(f64_of(dx)[ts], dx_ref, "dx")
+    Wg_l, Wu_l, Wd_l, A, B, s = params
+    staged_parity(x_s, dy_s, ex_l, weights[ts], ids_l, Wg_l, Wu_l, Wd_l, A, B, lambda a: s,
+                  lambda nm, js: fetch[nm](posmap[js]), f64_of(y)[ts], f64_of(dx)[ts])
     # one pair: all of its assignments, as a top-1 batch on that expert
     e0, a0 = pair_key
     J = np.nonzero((experts.reshape(-1) == e0) & (np.repeat(ids, K) == a0))[0]
@@ -179,16 +160,19 @@ def _expert_parity(x, dy, experts, weights, ids, y, dx, grads, Wg, Wu, Wd, pair,
     ex1 = np.full((tp.size, 1), e0)
     w1 = weights.reshape(-1)[J][:, None]
     params, ex_l, ids_l, _, _ = _subset_params(Wg, Wu, Wd, pair, ex1, ids[tp], scale_of(a0))
-    st = _Stage(pos[J], fetch)
     x_p = f64_of(x[torch.from_numpy(tp).cuda()])
     dy_p = f64_of(dy[torch.from_numpy(tp).cuda()])
-    _, saved = OE.moe_forward(x_p, ex_l, w1, ids_l, *params, store=st)
-    _, dA, dB = OE.moe_backward(dy_p, x_p, ex_l, w1, ids_l, *params, saved, store=st)
-    st.check()
+    _, saved = OE.moe_forward(x_p, ex_l, w1, ids_l, *params)
+    _, dA, dB = OE.moe_backward(dy_p, x_p, ex_l, w1, ids_l, *params, saved)
     for i, p in enumerate(("gate", "up", "down")):
         gA, gB = grad_view(i, e0, a0)
-        assert rel_err(gA, dA[p][0][0]) < TOL_F32, (p, "dA")
-        assert rel_err(gB, dB[p][0][0]) < TOL_F32, (p, "dB")
+        check_chained(gA, dA[p][0][0], f"{p} dA")
+        check_chained(gB, dB[p][0][0], f"{p} dB")
+    Wg_l, Wu_l, Wd_l, A, B, s = params
+    checked = staged_parity(x_p, dy_p, ex_l, w1, ids_l, Wg_l, Wu_l, Wd_l, A, B, lambda a: s,
+                            lambda nm, js: fetch[nm](pos[J][js]), None, None,
+                            grad_of=lambda p, e, a: grad_view(("gate", "up", "down").index(p), e0, a0))
+    assert checked == 1
     return J.size
 
 

@@ -228,41 +228,120 @@ def test_swiglu_parity():
     assert rel_err(f64_of(dg), rg) < TOL_BF16 and rel_err(f64_of(du), ru) < TOL_BF16
 
 
-@pytest.mark.parametrize("multi", [False, True])
-def test_adam_contains_nonfinite_gradients(multi):
-    """Elements whose gradient is NaN or +-Inf keep p, m, v (bit for bit) and
-    the bf16 copy of p; the status word gets FLAG_NONFINITE_GRAD; the other
-    elements match the oracle's step.  Finite gradients leave the status 0."""
+def _adam_close(pn, mn, vn, p0, po, mo, vo):
+    """Delta p at 1e-4 of its scale plus what the fp32 parameter cannot resolve:
+    p is rounded twice (after the decay, after the step), half an ulp each, of
+    the larger of the old and new magnitudes."""
+    p0 = np.asarray(p0, np.float64)
+    dp, dp_ref = np.asarray(pn, np.float64) - p0, po - p0
+    scale = np.maximum(np.abs(dp_ref), np.sqrt(np.mean(dp_ref ** 2)))
+    ulp = np.spacing(np.maximum(np.abs(p0), np.abs(po)).astype(np.float32)).astype(np.float64)
+    assert np.all(np.abs(dp - dp_ref) <= TOL_F32 * scale + ulp)
+    assert rel_err(mn, mo) < TOL_F32 and rel_err(vn, vo) < TOL_F32
+
+
+@pytest.mark.parametrize("layout", ["five", "seventy", "single_big"])
+def test_adam_skips_whole_adapter_on_nonfinite_gradient(layout):
+    """TPU RL note, section 12: a non-finite optimizer update is skipped
+    outright.  An adapter whose gradient holds one NaN or Inf keeps ALL of its
+    p, m, v and bf16 copy bit for bit; every other adapter steps as the oracle
+    does; the status word gets FLAG_NONFINITE_GRAD and the workspace's skip
+    flags name exactly the skipped adapters.  five: one launch, adapter 3 bad;
+    seventy: two launches' worth of segments with unaligned offsets, bad ones in
+    both launches; single_big: adam_step on one 262149-element adapter whose
+    only bad element sits in its last block.  A second call on the same
+    workspace with clean gradients steps everything and clears the flags."""
     rng = np.random.default_rng(9)
-    n = 1003
+    if layout == "five":
+        counts, gaps, bad_segs = [1003, 4096, 17, 5000, 64], [0] * 5, [3]
+    elif layout == "seventy":
+        counts = [int(c) for c in rng.integers(1, 3000, 70)]
+        gaps, bad_segs = [int(x) for x in rng.integers(0, 3, 70)], [2, 40, 66]
+    else:
+        counts, gaps, bad_segs = [262149], [0], [0]
+    segs, off = [], 3 if layout == "seventy" else 0
+    for i, (c, gp) in enumerate(zip(counts, gaps)):
+        segs.append((off, c, 1 + (i * 5) % 11))
+        off += c + gp
+    n = off + 7
     p0 = rng.standard_normal(n).astype(np.float32)
     m0 = (rng.standard_normal(n) * 1e-3).astype(np.float32)
     v0 = (rng.random(n) * 1e-6).astype(np.float32)
+    pb0 = W.to_bf16_bits(p0)
     g = (rng.standard_normal(n) * 1e-2).astype(np.float32)
-    bad = np.array([0, 5, 333, 502, 1002])
-    g[bad] = [np.nan, np.inf, -np.inf, np.nan, np.inf]
-    segs = [(0, 500, 3), (500, n - 500, 7)] if multi else [(0, n, 3)]
-    for gg, want in ((g, L.FLAG_NONFINITE_GRAD), (np.nan_to_num(g, posinf=0.1, neginf=-0.1), 0)):
+    for j, i in enumerate(bad_segs):
+        o, c, _ = segs[i]
+        g[o + c - 1 - (j % c)] = [np.nan, np.inf, -np.inf][j % 3]
+    ws = L.empty_workspace(L.adam_workspace_bytes(len(segs)))
+    for gg, bad in ((g, set(bad_segs)), (np.nan_to_num(g, nan=0.3, posinf=0.1, neginf=-0.1), set())):
         p, m, v = dev_f32(p0), dev_f32(m0), dev_f32(v0)
-        pb = torch.zeros(n, dtype=torch.bfloat16, device="cuda")
-        st = torch.zeros(1, dtype=torch.int32, device="cuda")
-        if multi:
-            L.adam_step_multi(segs, p, dev_f32(gg), m, v, 1e-4, weight_decay=0.01, p_bf16=pb, status=st)
+        pb = dev_bf16(pb0)
+        if layout == "single_big":
+            o, c, t = segs[0]
+            L.adam_step(p[o:o + c], dev_f32(gg[o:o + c]), m[o:o + c], v[o:o + c], t, 1e-4,
+                        weight_decay=0.01, p_bf16=pb[o:o + c], ws=ws)
         else:
-            L.adam_step(p, dev_f32(gg), m, v, 3, 1e-4, weight_decay=0.01, p_bf16=pb, status=st)
-        assert int(st.item()) == want
-        pn, mn, vn = p.cpu().numpy(), m.cpu().numpy(), v.cpu().numpy()
-        assert np.array_equal(bits_of(pb), W.to_bf16_bits(pn))
-        if want:
-            for a, a0 in ((pn, p0), (mn, m0), (vn, v0)):
-                assert np.array_equal(a[bad].view(np.int32), a0[bad].view(np.int32))
-        for o, c, t in segs:
-            po, mo, vo, skipped = OA.adam_step_flagged(p0[o:o + c], gg[o:o + c], m0[o:o + c],
-                                                       v0[o:o + c], t, 1e-4, weight_decay=0.01)
-            ok = np.isfinite(gg[o:o + c])
-            assert skipped == (not ok.all())
-            dp, dp_ref = (pn[o:o + c] - p0[o:o + c])[ok], (po - p0[o:o + c])[ok]
-            scale = np.maximum(np.abs(dp_ref), np.sqrt(np.mean(dp_ref ** 2)))
-            ulp = np.spacing(np.abs(po[ok]).astype(np.float32)).astype(np.float64)
-            assert np.all(np.abs(dp - dp_ref) <= TOL_F32 * scale + ulp)
-            assert rel_err(mn[o:o + c][ok], mo[ok]) < TOL_F32 and rel_err(vn[o:o + c][ok], vo[ok]) < TOL_F32
+            L.adam_step_multi(segs, p, dev_f32(gg), m, v, 1e-4, weight_decay=0.01, p_bf16=pb, ws=ws)
+        flags = L.adam_skip_flags(ws, len(segs))
+        assert L.lora_device_status(ws) == (L.FLAG_NONFINITE_GRAD if bad else 0)
+        assert set(np.nonzero(flags)[0].tolist()) == bad and set(flags.tolist()) <= {0, 1}
+        pn, mn, vn, pbn = p.cpu().numpy(), m.cpu().numpy(), v.cpu().numpy(), bits_of(pb)
+        for i, (o, c, t) in enumerate(segs):
+            sl = slice(o, o + c)
+            po, mo, vo, skipped = OA.adam_step_flagged(p0[sl], gg[sl], m0[sl], v0[sl], t, 1e-4,
+                                                       weight_decay=0.01)
+            assert skipped == (i in bad)
+            if i in bad:
+                for a, a0 in ((pn, p0), (mn, m0), (vn, v0)):
+                    assert np.array_equal(a[sl].view(np.int32), a0[sl].view(np.int32)), i
+                assert np.array_equal(pbn[sl], pb0[sl])
+            else:
+                _adam_close(pn[sl], mn[sl], vn[sl], p0[sl], po, mo, vo)
+                assert np.array_equal(pbn[sl], W.to_bf16_bits(pn[sl]))
+        inside = np.zeros(n, bool)
+        for o, c, _ in segs:
+            inside[o:o + c] = True
+        assert np.array_equal(pn[~inside].view(np.int32), p0[~inside].view(np.int32))
+
+
+@pytest.mark.parametrize("kind", [0, 1, 2, 3])
+def test_loss_grad_sentinel(kind):
+    """TPU RL note, section 12: kept rows whose inputs hold NaN or +-Inf (in
+    every input the kind reads) are removed by selection -- dlogp 0, no loss
+    term -- and FLAG_NONFINITE_LOSS is raised; the rest matches the oracle.  A
+    clean batch leaves the flag clear."""
+    c = _lp_case(44)
+    n = c.n_tokens
+    rng = np.random.default_rng(10 + kind)
+    lp = (-rng.random(n) * 8).astype(np.float32)
+    samp = c.sampler_logprobs(lp).astype(np.float32)
+    w = c.action.astype(np.float32).copy()
+    adv, g = c.advantages.astype(np.float32).copy(), c.custom_g.astype(np.float32).copy()
+    kept = np.nonzero(w != 0)[0]
+    rows = kept[[3, 50, 100, 200, 300]]
+    arrs = {"l": lp.copy(), "w": w.copy(), "A": adv.copy(), "s": samp.copy(), "g": g.copy()}
+    names = {0: ["l", "w", "l"], 1: ["l", "A", "s", "w"], 2: ["s", "A", "l", "w", "s"],
+             3: ["g", "l", "w"]}[kind]
+    vals = [np.nan, np.inf, -np.inf]
+    for j, (r, nm) in enumerate(zip(rows, names)):
+        arrs[nm][r] = vals[j % 3]
+    ws = L.empty_workspace(L.loss_grad_workspace_bytes(n))
+    for clean in (False, True):
+        src = {"l": lp, "w": w, "A": adv, "s": samp, "g": g} if clean else arrs
+        loss = torch.empty(1, dtype=torch.float32, device="cuda")
+        dl = torch.empty(n, dtype=torch.float32, device="cuda")
+        L.loss_grad(kind, dev_f32(src["l"]), dev_f32(src["w"]), dev_f32(src["A"]), dev_f32(src["s"]),
+                    dev_f32(src["g"]), (0.2, 0.2), loss, dl, ws)
+        L_ref, dl_ref, flag = OLs.loss_grad_flagged(kind, src["l"], src["w"], adv=src["A"],
+                                                    samp=src["s"], g=src["g"])
+        assert flag == (not clean)
+        assert L.lora_device_status(ws) == (0 if clean else L.FLAG_NONFINITE_LOSS)
+        dlg = dl.cpu().numpy().astype(np.float64)
+        assert np.isfinite(dlg).all() and np.isfinite(loss.item())
+        if not clean:
+            assert np.all(dlg[rows[:len(names)]] == 0.0)
+        rho = np.exp(src["l"].astype(np.float64) - src["s"])
+        near = (np.abs(rho - 0.8) < 1e-5) | (np.abs(rho - 1.2) < 1e-5) if kind == OLs.PPO else \
+            np.zeros(n, bool)
+        assert rel_err(dlg[~near], dl_ref[~near]) < TOL_F32
+        assert abs(float(loss.item()) - L_ref) <= TOL_F32 * max(abs(L_ref), 1e-3)

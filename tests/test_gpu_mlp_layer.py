@@ -1,11 +1,13 @@
 """The fused SwiGLU MLP layer (mlp_forward / mlp_backward) on the GPU.
 
 It is the expert layer with one expert and no routing, so the oracle is
-oracle.moe with every token routed to expert 0 at weight 1 (per-stage parity
-as for the routed layer: the oracle continues from the GPU's stored stage
-bits), and the layer must equal moe_forward / moe_backward with one expert,
-top-1, weight 1: y, dx and the gate/up gradients bit for bit (the routed
-combine of one weight-1 expert is a copy)."""
+oracle.moe with every token routed to expert 0 at weight 1, which is the plain
+SwiGLU MLP with a LoRA on each projection: compared end to end (y, dx, every
+adapter's dA and dB at the bf16 tolerance) and per stage from the GPU's own
+stored stage bits, as for the routed layer.  The layer must also equal
+moe_forward / moe_backward with one expert, top-1, weight 1: y, dx and the
+gate/up gradients bit for bit (the routed combine of one weight-1 expert is a
+copy)."""
 import numpy as np
 import pytest
 import torch
