@@ -479,12 +479,12 @@ lora_status run_segments(const int32_t* ids, int64_t n, int32_t n_keys, int32_t 
       chunks64 * (n_keys + 1) <= SEG_SMALL_HIST) {
     // one launch
     const size_t hl = (size_t)chunks64 * (n_keys + 1) * sizeof(int32_t);
-    static size_t attr = 0;
-    if (attr < hl) {
-      TRY_HIP(hipFuncSetAttribute((const void*)seg_small_kernel,
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)hl));
-      attr = hl;
-    }
+    // the kernel's dynamic LDS bound, raised once to the largest histogram this
+    // path takes (a thread-safe one-time initialisation, then read-only)
+    static const hipError_t attr_err = hipFuncSetAttribute(
+        (const void*)seg_small_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+        (int)(SEG_SMALL_HIST * sizeof(int32_t)));
+    TRY_HIP(attr_err);
     hipLaunchKernelGGL(seg_small_kernel, dim3(1), dim3(1024), hl, s, ids, (int)n, n_keys,
                        order == LORA_IDS_SORTED ? 1 : 0, tabs, ex ? ex->max_rank : 0,
                        ex ? ex->active : nullptr, tl, offsets, perm, ex ? ex->adpos : nullptr,
