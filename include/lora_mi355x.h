@@ -455,6 +455,29 @@ lora_status mlp_backward(const mlp_shape* shape, const uint16_t* dy, const uint1
                          float* ddown_pack, int accumulate, uint16_t* trace, void* ws,
                          size_t ws_bytes, void* stream);
 
+/* ---- forward without allocation ------------------------------------- */
+
+/* For callers that cannot allocate device memory or hand in a workspace: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  Computes exactly what lora_forward computes, with the same
+ * kernels (same bits), but its scratch (segment tables, tile prefixes, status
+ * word) is a fixed device array inside the library: lora_forward_noalloc_
+ * scratch_bytes() = 2 MiB on each GPU the library runs on, held from the
+ * library's load until the process ends.  Nothing is allocated on any path.
+ *   status  int32 (device, nullable): this call's content flags (LORA_FLAG_*,
+ *           as lora_forward would set in its workspace) are OR-ed into it.
+ * A shape whose scratch exceeds the array (for example more than 65536
+ * tokens with 1024 adapters) returns LORA_E_UNSUPPORTED before anything is
+ * enqueued; other host errors as lora_forward.  The stream must belong to
+ * the current device.  All calls on one GPU share that GPU's array and it
+ * keeps the last call's contents: calls that overlap on one GPU (two streams
+ * or two threads) race, so serialise them. */
+size_t lora_forward_noalloc_scratch_bytes(void);
+lora_status lora_forward_noalloc(const lora_shape* shape, const uint16_t* x, const uint16_t* W,
+                                 const uint16_t* A_pack, const uint16_t* B_pack,
+                                 const lora_adapter_desc* desc, const int32_t* adapter_ids,
+                                 uint16_t* y, uint16_t* u_saved, int32_t* status, void* stream);
+
 /* ---- kernel timing (measurement) ------------------------------------- */
 
 /* When enabled, the library brackets each launch of the kernel classes below

@@ -4,6 +4,7 @@
 #include <stdio.h>
 
 #include <cmath>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -101,7 +102,8 @@ struct LayerWs {
   size_t total;
 };
 
-LayerWs carve_layer(const lora_shape& sh, void* ws, size_t bytes) {
+// fwd_only: the forward's part alone (no v planes, no gradient partials)
+LayerWs carve_layer(const lora_shape& sh, void* ws, size_t bytes, bool fwd_only = false) {
   Carve cv(ws, bytes);
   LayerWs w{};
   w.seg_bytes = segments_ws_bytes(sh.n_tokens, sh.n_adapters);
@@ -113,8 +115,13 @@ LayerWs carve_layer(const lora_shape& sh, void* ws, size_t bytes) {
   w.pre32 = cv.take<int32_t>((size_t)sh.n_adapters + 1);
   w.pre128 = cv.take<int32_t>((size_t)sh.n_adapters + 1);
   w.prec = cv.take<int32_t>((size_t)sh.n_adapters + 1);
-  w.v = cv.take<uint16_t>((size_t)2 * std::max<int64_t>(sh.n_tokens, 1) * sh.max_rank);
   w.zero = cv.take<uint16_t>(128);
+  if (fwd_only) {
+    w.v = nullptr;
+    w.total = cv.used;
+    return w;
+  }
+  w.v = cv.take<uint16_t>((size_t)2 * std::max<int64_t>(sh.n_tokens, 1) * sh.max_rank);
   // chunk partials of dB and of dA (reduced in one launch, so apart)
   w.partial = cv.take<float>((size_t)grad_partial_floats(sh.n_tokens, sh.n_adapters, sh.d_out,
                                                          sh.max_rank));
@@ -231,10 +238,10 @@ lora_status lora_transpose_bf16(const uint16_t* src, uint16_t* dst, int64_t rows
   return launch_transpose_bf16(src, dst, rows, cols, S(stream));
 }
 
-lora_status lora_forward(const lora_shape* shape, const uint16_t* x, const uint16_t* W,
-                         const uint16_t* A_pack, const uint16_t* B_pack,
-                         const lora_adapter_desc* desc, const int32_t* adapter_ids, uint16_t* y,
-                         uint16_t* u_saved, void* ws, size_t ws_bytes, void* stream) {
+static lora_status forward_checks(const lora_shape* shape, const uint16_t* x, const uint16_t* W,
+                                  const uint16_t* A_pack, const uint16_t* B_pack,
+                                  const lora_adapter_desc* desc, const int32_t* adapter_ids,
+                                  uint16_t* y, uint16_t* u_saved) {
   TRY(check_shape(shape));
   const lora_shape& sh = *shape;
   LORA_ARG_CHECK(W && A_pack && B_pack && desc, "W, A_pack, B_pack and desc must be non-NULL");
@@ -243,12 +250,16 @@ lora_status lora_forward(const lora_shape* shape, const uint16_t* x, const uint1
   LORA_ARG_CHECK(sh.n_tokens == 0 || (aligned16(x) && aligned16(y) && aligned16(u_saved)),
                  "x, y and u_saved must be 16-byte aligned");
   LORA_ARG_CHECK(aligned16(W) && aligned16(A_pack) && aligned16(B_pack), "W and the packs must be 16-byte aligned");
-  LayerWs w = carve_layer(sh, ws, ws_bytes);
-  if (!ws || w.total > ws_bytes) {
-    set_error("lora_forward: workspace %zu bytes < %zu needed", ws_bytes, w.total);
-    return LORA_E_WORKSPACE;
-  }
-  hipStream_t s = S(stream);
+  return LORA_OK;
+}
+
+// The forward's launches on a carved workspace (segments, shrink, GEMM with the
+// fused expand); every part of `w` it reads it has written earlier in the call,
+// except the sticky status word.
+static lora_status forward_core(const lora_shape& sh, const uint16_t* x, const uint16_t* W,
+                                const uint16_t* A_pack, const uint16_t* B_pack,
+                                const lora_adapter_desc* desc, const int32_t* adapter_ids,
+                                uint16_t* y, uint16_t* u_saved, const LayerWs& w, hipStream_t s) {
   const int N = (int)sh.n_tokens;
   TRY(layer_segments(sh, desc, adapter_ids, w, s));
   if (N == 0) return LORA_OK;
@@ -273,6 +284,19 @@ lora_status lora_forward(const lora_shape* shape, const uint16_t* x, const uint1
   TRY(gemm_nt_rows(x, W, y, N, (int)sh.d_out, (int)sh.d_in, sh.d_in, sh.d_in, sh.d_out, f, s));
   timer_end(LORA_TIMER_BASE_GEMM, s);
   return LORA_OK;
+}
+
+lora_status lora_forward(const lora_shape* shape, const uint16_t* x, const uint16_t* W,
+                         const uint16_t* A_pack, const uint16_t* B_pack,
+                         const lora_adapter_desc* desc, const int32_t* adapter_ids, uint16_t* y,
+                         uint16_t* u_saved, void* ws, size_t ws_bytes, void* stream) {
+  TRY(forward_checks(shape, x, W, A_pack, B_pack, desc, adapter_ids, y, u_saved));
+  LayerWs w = carve_layer(*shape, ws, ws_bytes);
+  if (!ws || w.total > ws_bytes) {
+    set_error("lora_forward: workspace %zu bytes < %zu needed", ws_bytes, w.total);
+    return LORA_E_WORKSPACE;
+  }
+  return forward_core(*shape, x, W, A_pack, B_pack, desc, adapter_ids, y, u_saved, w, S(stream));
 }
 
 lora_status lora_backward(const lora_shape* shape, const uint16_t* dy, const uint16_t* x,
@@ -1067,6 +1091,75 @@ lora_status lora_timing_read(int32_t timer, double* total_ms, int64_t* launches)
   }
   *total_ms = tot;
   *launches = (int64_t)u;
+  return LORA_OK;
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------------ forward without allocation
+// lora_forward_noalloc runs lora_forward's kernels on a fixed device array of
+// this file instead of a caller workspace.  Each GPU holds its own copy of the
+// array (kScratchBytes) from the library's load until the process ends; its
+// device address is looked up once per device (hipGetSymbolAddress, with that
+// device current) and kept in g_scratch below -- the array's name in host code
+// is only a host-side stand-in and is never handed to a kernel.
+namespace {
+constexpr size_t kScratchBytes = (size_t)2 << 20;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+}  // namespace
+
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+namespace {
+lora_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  TRY(hip_check(hipGetDevice(&dev), "hipGetDevice"));
+  if (dev < 0 || dev >= kMaxDevices) {
+    set_error("lora_forward_noalloc: device %d outside the %d the scratch table holds", dev,
+              kMaxDevices);
+    return LORA_E_UNSUPPORTED;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void* p = nullptr;
+    TRY(hip_check(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)"));
+    if (p == nullptr) {
+      set_error("lora_forward_noalloc: no device address for the scratch array");
+      return LORA_E_HIP;
+    }
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return LORA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+size_t lora_forward_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+lora_status lora_forward_noalloc(const lora_shape* shape, const uint16_t* x, const uint16_t* W,
+                                 const uint16_t* A_pack, const uint16_t* B_pack,
+                                 const lora_adapter_desc* desc, const int32_t* adapter_ids,
+                                 uint16_t* y, uint16_t* u_saved, int32_t* status, void* stream) {
+  TRY(forward_checks(shape, x, W, A_pack, B_pack, desc, adapter_ids, y, u_saved));
+  const LayerWs need = carve_layer(*shape, nullptr, 0, true);
+  if (need.total > kScratchBytes) {
+    set_error("lora_forward_noalloc: this shape needs %zu bytes of scratch; the fixed array "
+              "holds %zu (e.g. up to 65536 tokens with 1024 adapters)", need.total, kScratchBytes);
+    return LORA_E_UNSUPPORTED;
+  }
+  void* ptr = nullptr;
+  TRY(scratch_of_current_device(&ptr));
+  const LayerWs w = carve_layer(*shape, ptr, kScratchBytes, true);
+  hipStream_t s = S(stream);
+  // the status word is the one part of the scratch read before this call writes
+  // it: clear it (a fill kernel, so the call can be captured in a graph)
+  TRY(launch_fill_i32((int32_t*)ptr, 1, 0, s));
+  TRY(forward_core(*shape, x, W, A_pack, B_pack, desc, adapter_ids, y, u_saved, w, s));
+  if (status) TRY(launch_or_status((const int32_t*)ptr, status, s));
   return LORA_OK;
 }
 

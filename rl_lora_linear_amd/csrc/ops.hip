@@ -370,6 +370,10 @@ __global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __r
   for (int i = ty; i < 64; i += 4) dst[(c0 + i) * rows + r0 + tx] = tile[tx][i];
 }
 
+__global__ void or_status_kernel(const int32_t* __restrict__ src, int32_t* __restrict__ dst) {
+  if (threadIdx.x == 0 && *src) set_flag(dst, *src);
+}
+
 __global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
        i += (int64_t)gridDim.x * blockDim.x)
@@ -502,6 +506,11 @@ lora_status launch_transpose_bf16(const uint16_t* src, uint16_t* dst, int64_t ro
   hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)(cols / 64), (unsigned)(rows / 64)),
                      dim3(256), 0, s, src, dst, rows, cols);
   return launch_check("transpose_bf16");
+}
+
+lora_status launch_or_status(const int32_t* src, int32_t* dst, hipStream_t s) {
+  hipLaunchKernelGGL(or_status_kernel, dim3(1), dim3(64), 0, s, src, dst);
+  return launch_check("or_status");
 }
 
 lora_status launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s) {

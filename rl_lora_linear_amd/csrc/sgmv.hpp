@@ -136,6 +136,8 @@ lora_status launch_add_bf16(int64_t n, const uint16_t* a, const uint16_t* b, uin
 lora_status launch_transpose_bf16(const uint16_t* src, uint16_t* dst, int64_t rows, int64_t cols,
                                   hipStream_t s);
 lora_status launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
+// *dst |= *src (a status word into another), one tiny launch
+lora_status launch_or_status(const int32_t* src, int32_t* dst, hipStream_t s);
 
 // moe.hip
 lora_status launch_moe_route(const float* logits, int64_t n, int E, int K, int32_t* experts,

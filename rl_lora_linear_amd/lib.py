@@ -36,6 +36,7 @@ EXPORTS = [
     "swiglu_backward", "bf16_add", "moe_route", "moe_workspace_bytes", "moe_saved_bytes", "moe_forward",
     "moe_backward", "mlp_workspace_bytes", "mlp_saved_bytes", "mlp_forward", "mlp_backward",
     "lora_timing_enable", "lora_timing_reset", "lora_timing_read",
+    "lora_forward_noalloc_scratch_bytes", "lora_forward_noalloc",
 ]
 
 
@@ -123,6 +124,9 @@ def _load() -> ctypes.CDLL:
         "mlp_forward": (_I32, [ctypes.POINTER(MlpShape)] + [_P] * 14 + [_SZ, _P]),
         "mlp_backward": (_I32, [ctypes.POINTER(MlpShape)] + [_P] * 17 + [_I32, _P, _P, _SZ, _P]),
         "swiglu_backward": (_I32, [_I64, _P, _P, _P, _P, _P, _P]),
+        "lora_forward_noalloc_scratch_bytes": (_SZ, []),
+        "lora_forward_noalloc": (_I32, [ctypes.POINTER(LoraShape), _P, _P, _P, _P, _P, _P, _P, _P,
+                                        _P, _P]),
         "lora_timing_enable": (None, [_I32]),
         "lora_timing_reset": (None, []),
         "lora_timing_read": (_I32, [_I32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I64)]),
@@ -213,6 +217,19 @@ def lora_forward(shape, x, W, A_pack, B_pack, desc, ids, y, u_saved, ws, stream=
     _check(LIB.lora_forward(ctypes.byref(shape), _ptr(x), _ptr(W), _ptr(A_pack), _ptr(B_pack),
                             _ptr(desc), _ptr(ids), _ptr(y), _ptr(u_saved), _ptr(ws), _nbytes(ws),
                             _stream(stream)))
+
+
+def lora_forward_noalloc_scratch_bytes() -> int:
+    return LIB.lora_forward_noalloc_scratch_bytes()
+
+
+def lora_forward_noalloc(shape, x, W, A_pack, B_pack, desc, ids, y, u_saved, status=None,
+                         stream=None):
+    """lora_forward on the library's fixed scratch array (no workspace); status:
+    optional device int32 tensor the call's flags are OR-ed into."""
+    _check(LIB.lora_forward_noalloc(ctypes.byref(shape), _ptr(x), _ptr(W), _ptr(A_pack),
+                                    _ptr(B_pack), _ptr(desc), _ptr(ids), _ptr(y), _ptr(u_saved),
+                                    _ptr(status), _stream(stream)))
 
 
 def lora_backward(shape, dy, x, W_t, A_pack, B_pack, desc, ids, u_saved, dx, dA_pack, dB_pack,
