@@ -1,21 +1,25 @@
-"""Benchmark of the mixed-adapter LoRA training step on one MI355X.
+"""Benchmark of the mixed-adapter LoRA training hot path on one MI355X.
 
-One step = one pass of the hot path over a Qwen3-8B-width q/o projection
-(4096 -> 4096, bf16, fp32 accumulate): 16 rank-32 adapters (alpha 32) over
-8192 tokens in sorted 512-token segments; segment build, shrink and the base
-GEMM with the LoRA expand in its epilogue (forward), the same for dX plus the
-adapter-gradient reductions (backward), and one AdamW step per adapter (lr 1e-4, betas 0.9/0.999, eps 1e-8) writing the
-bf16 copy the next forward reads.  Inputs are seeded synthetic data resident in
-HBM before timing; four rotated copies of (x, dY) keep the 256 MB Infinity
-Cache from serving repeat reads.
+Headline step (`value`): one pass of the hot path over a Qwen3-8B-width q/o
+projection (4096 -> 4096, bf16, fp32 accumulate) with 16 rank-32 adapters
+(alpha 32) over 8192 tokens in sorted 512-token segments -- segment build,
+shrink and the base GEMM with the LoRA expand in its epilogue (forward), the
+same for dX plus the adapter-gradient reductions (backward), and one AdamW
+step per adapter (lr 1e-4, betas 0.9/0.999, eps 1e-8) writing the bf16 copy
+the next forward reads.  Inputs are seeded synthetic data resident in HBM
+before timing; four rotated copies of (x, dY) keep the 256 MB Infinity Cache
+from serving repeat reads.  `tokens_per_s_fwd_bwd` times the same step
+without the AdamW launch (tokens / (t_fwd + t_bwd)).
 
-Prints ONE JSON line on stdout.  `value` = tokens/s of the whole step, timed
-with no instrumentation.  `roofline` is for the dominant kernel (the base
-GEMM), timed live with HIP events the library records around each of its
-launches, on the launch stream, in a second pass of the same number of steps
-(each timed event stalls the queue for a few microseconds, so the instrumented
-pass is reported separately as ms_per_step_instrumented).  `cpu_baseline`
-times the oracle (NumPy float64) on the host cores.
+Prints ONE JSON line on stdout.  `roofline` is for the dominant kernel (the
+base GEMM), timed live with HIP events the library records around each of its
+launches on the launch stream, in a second pass of the same number of steps
+(reported as ms_per_step_instrumented).  `cpu_baseline` times the oracle
+(NumPy float64) on the host cores.  Unless --quick, `configs` carries the MLP,
+fused logprob + RL loss (with the custom-loss path timed two ways), routed
+expert and decode workloads, each with its own roofline and CPU baseline,
+`adam_whole_model` an AdamW step over a whole rank-32 Qwen3-8B adapter, and
+`measured_peaks` the chip's own MFMA and copy rates (bench_workloads.py).
 """
 from __future__ import annotations
 
@@ -64,11 +68,12 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target wall time of the oracle sample")
     ap.add_argument("--workload", default="qo_proj",
-                    choices=["qo_proj", "mlp", "logprob", "moe", "decode"],
-                    help="qo_proj (default): the q/o projection step the headline metric is "
-                         "quoted on; mlp / logprob / moe / decode: the other workloads, one JSON "
-                         "line each "
-                         "(no CPU baseline)")
+                    choices=["qo_proj", "mlp", "logprob", "moe", "decode", "adam", "peaks"],
+                    help="qo_proj (default): the headline step, with every other workload in "
+                         "`configs` unless --quick; mlp / logprob / moe / decode / adam / peaks: "
+                         "that workload alone, one JSON line")
+    ap.add_argument("--quick", action="store_true",
+                    help="headline step only (no other workloads, no measured peaks)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
                     help="only run a plain device copy of MB megabytes 5 times (calibrates "
                          "the FETCH_SIZE / WRITE_SIZE counters against known bytes) and exit")
@@ -78,11 +83,7 @@ def parse():
 def cpu_baseline(case, target_s):
     """Time the oracle's forward + backward (+ Adam prorated) on the host."""
     import numpy as np
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
+    import bench_workloads as BW
     import oracle.adam as OA
     import oracle.lora as OL
 
@@ -118,9 +119,12 @@ def cpu_baseline(case, target_s):
     t_adam_one = time.perf_counter() - ts
     t_adam_per_token = t_adam_one * case.n_adapters / case.n_tokens
     tps = tokens_done / (t_layer + t_adam_per_token * tokens_done)
-    return {"value": tps, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{reps} adapter segments x {per} tokens of the same workload "
-                      f"(fp64 NumPy fwd+bwd, {t_layer:.1f} s) + one adapter's AdamW prorated per token"}
+    out = {"value": round(tps, 2), "unit": "tokens/s", "kind": "oracle",
+           "sample": f"{reps} adapter segments x {per} tokens of the same workload "
+                     f"(fp64 NumPy fwd+bwd, {t_layer:.1f} s) + one adapter's AdamW prorated per token",
+           "tokens_per_s_fwd_bwd": round(tokens_done / t_layer, 2)}
+    out.update(BW.host_info())
+    return out
 
 
 def main():
@@ -143,13 +147,17 @@ def main():
         print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "launches": 5}))
         return
 
+    import bench_workloads as BW
+    cpu_s = 0.0 if args.no_cpu_baseline else 8.0
     if args.workload != "qo_proj":
-        import rl_lora_linear_amd.workload_bench as WB
         torch.cuda.set_device(0)
-        out = getattr(WB, args.workload)(args.steps, args.warmup, log)
-        out.update({"n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-                    "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-                    "dtype": "bf16", "data": "synthetic (seeded, generated on the device)"})
+        if args.workload == "peaks":
+            out = BW.peaks(log)
+        else:
+            out = getattr(BW, args.workload)(args.steps, args.warmup, log, None, cpu_s)
+        out.update({"workload": args.workload, "n_gpus": 1, "steps": args.steps,
+                    "warmup": args.warmup, "dtype": "bf16",
+                    "data": "synthetic (seeded, generated on the device)"})
         print(json.dumps(out), flush=True)
         return
 
@@ -158,57 +166,69 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    peaks = None if args.quick else BW.peaks(log)
     log(f"[bench] generating inputs ({args.tokens} tokens)")
     case = W.attn_proj(seed=2, n_tokens=args.tokens)
-    sys.path.insert(0, os.path.join(ROOT, "tests"))
-    from gpu_util import DevLayer, dev_bf16
-
-    dl = DevLayer(case)
     N, d_in, d_out = case.n_tokens, case.d_in, case.d_out
     n_ad = case.n_adapters
+    max_rank = max(16, -(-int(case.ranks.max()) // 16) * 16)
+
+    def dev_bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    shape = L.make_shape(N, d_in, d_out, case.pack_elems, case.pack_elems, n_ad, max_rank,
+                         L.IDS_SORTED)
+    x0, dy0, Wm = dev_bf16(case.x_bits), dev_bf16(case.dy_bits), dev_bf16(case.W_bits)
+    Wt = torch.empty((d_in, d_out), dtype=torch.bfloat16, device=dev)
+    L.lora_transpose_bf16(Wm, Wt)
+    pack = dev_bf16(case.pack_bits)
+    desc = L.make_desc(case.a_off, case.b_off, case.ranks, case.scales.astype(np.float32))
+    ids = torch.from_numpy(case.ids.astype(np.int32)).to(dev)
+    ws = L.empty_workspace(L.lora_workspace_bytes(shape))
     # rotated input sets
     sets = []
     for k in range(4):
-        xs = torch.roll(dl.x, shifts=k * 97, dims=0).contiguous()
-        dys = torch.roll(dl.dy, shifts=k * 89, dims=0).contiguous()
+        xs = torch.roll(x0, shifts=k * 97, dims=0).contiguous()
+        dys = torch.roll(dy0, shifts=k * 89, dims=0).contiguous()
         sets.append((xs, dys))
     y = torch.empty((N, d_out), dtype=torch.bfloat16, device=dev)
-    u = torch.empty((2, N, dl.max_rank), dtype=torch.bfloat16, device=dev)   # hi/lo planes
+    u = torch.empty((2, N, max_rank), dtype=torch.bfloat16, device=dev)   # hi/lo planes
     dx = torch.empty((N, d_in), dtype=torch.bfloat16, device=dev)
     grad = torch.zeros(case.pack_elems, dtype=torch.float32, device=dev)
-    master = dl.pack.float().clone()
+    master = pack.float().clone()
     m = torch.zeros_like(master)
     v = torch.zeros_like(master)
     ranges = [case.adapter_range(i) for i in range(n_ad)]
     ws_adam = L.empty_workspace(L.adam_workspace_bytes(n_ad))
     steps_done = [0]
 
-    def step(k):
+    def step(k, with_adam=True):
         xs, dys = sets[k % len(sets)]
-        L.lora_forward(dl.shape, xs, dl.W, dl.pack, dl.pack, dl.desc, dl.ids, y, u, dl.ws)
-        L.lora_backward(dl.shape, dys, xs, dl.Wt, dl.pack, dl.pack, dl.desc, dl.ids, u, dx, grad,
-                        grad, 0, dl.ws)
+        L.lora_forward(shape, xs, Wm, pack, pack, desc, ids, y, u, ws)
+        L.lora_backward(shape, dys, xs, Wt, pack, pack, desc, ids, u, dx, grad, grad, 0, ws)
+        if not with_adam:
+            return
         t = steps_done[0] + 1
-        # every adapter in the batch takes its own AdamW step, one launch
+        # every adapter in the batch takes its own AdamW step
         L.adam_step_multi([(a0, a1 - a0, t) for (a0, a1) in ranges], master, grad, m, v, 1e-4,
-                          0.9, 0.999, 1e-8, 0.0, p_bf16=dl.pack, ws=ws_adam)
+                          0.9, 0.999, 1e-8, 0.0, p_bf16=pack, ws=ws_adam)
         steps_done[0] = t
 
     log(f"[bench] warmup {args.warmup}")
     for k in range(args.warmup):
         step(k)
     torch.cuda.synchronize()
-    flags = L.lora_device_status(dl.ws)
+    flags = L.lora_device_status(ws) | L.lora_device_status(ws_adam)
     if flags:
         raise RuntimeError(f"device status flags {flags:#x}")
 
-    def timed(instrumented):
+    def timed(instrumented, with_adam=True):
         L.lora_timing_reset()
         L.lora_timing_enable(instrumented)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for k in range(args.steps):
-            step(k)
+            step(k, with_adam)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
         L.lora_timing_enable(False)
@@ -217,6 +237,8 @@ def main():
     log(f"[bench] timing {args.steps} steps")
     ms_step = timed(False)
     tokens_s = N / (ms_step / 1e3)
+    log(f"[bench] timing {args.steps} steps without the AdamW launch")
+    ms_fwd_bwd = timed(False, with_adam=False)
     log(f"[bench] timing {args.steps} instrumented steps (kernel durations)")
     ms_step_instr = timed(True)
 
@@ -232,9 +254,9 @@ def main():
 
     # algorithmic bytes of the HBM-bound kernels (per launch)
     r = int(case.ranks[0])
-    shrink_bytes = (N * d_in * 2 + n_ad * r * d_in * 2 + N * dl.max_rank * 4)
-    grad_bytes = (N * d_out * 2 + N * dl.max_rank * 4 + n_ad * d_out * r * 4) + \
-                 (N * d_in * 2 + N * dl.max_rank * 4 + n_ad * r * d_in * 4)
+    shrink_bytes = (N * d_in * 2 + n_ad * r * d_in * 2 + N * max_rank * 4)
+    grad_bytes = (N * d_out * 2 + N * max_rank * 4 + n_ad * d_out * r * 4) + \
+                 (N * d_in * 2 + N * max_rank * 4 + n_ad * r * d_in * 4)
     adam_bytes = 30 * sum(a1 - a0 for a0, a1 in ranges)   # p,m,v r+w, g r, bf16 copy w
 
     def kentry(name, bytes_per_launch, launches_per_step):
@@ -260,6 +282,8 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
         "ms_per_step_instrumented": round(ms_step_instr, 4),
+        "tokens_per_s_fwd_bwd": round(N / (ms_fwd_bwd / 1e3), 1),
+        "ms_fwd_bwd": round(ms_fwd_bwd, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -274,9 +298,22 @@ def main():
                      "traffic_unit": "HBM bytes per launch (rocprofv3 counters)"},
         "kernels": kernels,
     }
+    if peaks:
+        out["measured_peaks"] = peaks
+        out["roofline"]["measured_peak"] = peaks["mfma_bf16_tflops"]
+        out["roofline"]["frac_measured_peak"] = round(achieved / peaks["mfma_bf16_tflops"], 4)
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")
         out["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+    if not args.quick:
+        del sets, y, u, dx, grad, master, m, v, ws
+        torch.cuda.empty_cache()
+        cfgs = {}
+        for name in ("mlp", "logprob", "moe", "decode"):
+            cfgs[name] = getattr(BW, name)(args.steps, args.warmup, log, peaks, cpu_s)
+        out["configs"] = cfgs
+        out["adam_whole_model"] = BW.adam(args.steps, args.warmup, log, peaks,
+                                          0.0 if args.no_cpu_baseline else 3.0)
     print(json.dumps(out), flush=True)
 
 

@@ -478,6 +478,22 @@ lora_status lora_forward_noalloc(const lora_shape* shape, const uint16_t* x, con
                                  const lora_adapter_desc* desc, const int32_t* adapter_ids,
                                  uint16_t* y, uint16_t* u_saved, int32_t* status, void* stream);
 
+/* ---- measurement probes ----------------------------------------------- */
+
+/* The chip's own peaks, for reporting the kernels' fractions against measured
+ * as well as published figures.  lora_probe_mfma runs `blocks` blocks of 8
+ * waves, each wave `iters` rounds of 4 independent v_mfma_f32_32x32x16_bf16
+ * on register operands (no memory traffic); its flop count is
+ * lora_probe_mfma_flops_per_iter(blocks) * iters.  sink: device float[blocks]
+ * (written, meaningless).  lora_probe_copy copies `bytes` (a multiple of 16,
+ * 16-byte aligned buffers) with a streaming kernel: 2 * bytes of HBM traffic.
+ * lora_probe_read streams `bytes` of src through the chip (reads only; sink:
+ * one device uint32, almost never written). */
+int64_t lora_probe_mfma_flops_per_iter(int32_t blocks);
+lora_status lora_probe_mfma(int64_t iters, int32_t blocks, float* sink, void* stream);
+lora_status lora_probe_copy(const void* src, void* dst, int64_t bytes, void* stream);
+lora_status lora_probe_read(const void* src, int64_t bytes, void* sink, void* stream);
+
 /* ---- kernel timing (measurement) ------------------------------------- */
 
 /* When enabled, the library brackets each launch of the kernel classes below

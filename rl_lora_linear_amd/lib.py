@@ -37,6 +37,7 @@ EXPORTS = [
     "moe_backward", "mlp_workspace_bytes", "mlp_saved_bytes", "mlp_forward", "mlp_backward",
     "lora_timing_enable", "lora_timing_reset", "lora_timing_read",
     "lora_forward_noalloc_scratch_bytes", "lora_forward_noalloc",
+    "lora_probe_mfma_flops_per_iter", "lora_probe_mfma", "lora_probe_copy", "lora_probe_read",
 ]
 
 
@@ -127,6 +128,10 @@ def _load() -> ctypes.CDLL:
         "lora_forward_noalloc_scratch_bytes": (_SZ, []),
         "lora_forward_noalloc": (_I32, [ctypes.POINTER(LoraShape), _P, _P, _P, _P, _P, _P, _P, _P,
                                         _P, _P]),
+        "lora_probe_mfma_flops_per_iter": (_I64, [_I32]),
+        "lora_probe_mfma": (_I32, [_I64, _I32, _P, _P]),
+        "lora_probe_copy": (_I32, [_P, _P, _I64, _P]),
+        "lora_probe_read": (_I32, [_P, _I64, _P, _P]),
         "lora_timing_enable": (None, [_I32]),
         "lora_timing_reset": (None, []),
         "lora_timing_read": (_I32, [_I32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I64)]),
@@ -402,6 +407,22 @@ def swiglu_forward(gate, up, h, stream=None):
 def swiglu_backward(dh, gate, up, dgate, dup, stream=None):
     _check(LIB.swiglu_backward(gate.numel(), _ptr(dh), _ptr(gate), _ptr(up), _ptr(dgate), _ptr(dup),
                                _stream(stream)))
+
+
+def lora_probe_mfma(iters, blocks, sink, stream=None):
+    """Register-only bf16 MFMA loop; returns its flop count."""
+    _check(LIB.lora_probe_mfma(int(iters), int(blocks), _ptr(sink), _stream(stream)))
+    return LIB.lora_probe_mfma_flops_per_iter(int(blocks)) * int(iters)
+
+
+def lora_probe_copy(src, dst, stream=None):
+    """Streaming device copy of src's bytes into dst."""
+    _check(LIB.lora_probe_copy(_ptr(src), _ptr(dst), _nbytes(src), _stream(stream)))
+
+
+def lora_probe_read(src, sink, stream=None):
+    """Read-only stream over src's bytes (sink: a device int32 tensor)."""
+    _check(LIB.lora_probe_read(_ptr(src), _nbytes(src), _ptr(sink), _stream(stream)))
 
 
 def lora_timing_enable(on: bool):
