@@ -918,94 +918,161 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_nt_kernel(const uint16_t* __
   }
 }
 
-// ---- skinny GEMM for few rows (decode-shaped batches)
+// ---- few-row GEMM (decode-shaped batches)
 //
 // With M of a few hundred rows the 256x256 tiles leave most CUs idle (256 rows
-// and 4096 columns make 16 blocks).  Here one wave owns 32 rows x 64 columns
-// over the whole K and loads its fragments straight from global memory (the
-// operands are small and L2-resident), so M = 256, N = 4096 runs 512 waves.
-// Each output element is accumulated exactly as in gemm_nt_kernel: the same
-// v_mfma_f32_32x32x16_bf16 with the same operand order and lane layout, k in
-// 16-wide slices in increasing order, then the LoRA expand per adapter and
-// 16-rank slice (hi, then lo), so a row gets the same bits from either kernel
-// (rows of other adapters only receive exact zeros).  Plain epilogue only:
-// bf16 store, rows through a_rows / c_rows, expand from B_a (use_b_off = 1).
-constexpr int SK_TM = 32, SK_TN = 64, SK_KC = 4;    // rows, columns, 64-wide k chunks per batch of loads
-constexpr int SK_NJ = SK_TN / 32;                  // 32-column MFMA tiles per wave
+// and 4096 columns make 16 blocks) and the product is bound by reading the
+// weight once.  Here a block of 4 waves owns a 64 x 64 output tile over the
+// whole K -- 256 rows x 4096 columns make 256 blocks, one per CU -- and streams
+// its 64 operand rows of each side through a ring of FR_NST LDS-DMA stages of
+// k = 128 (32 KB each; steps of 8 MFMAs per wave amortise the per-step wait,
+// barrier and DMA issue), so every CU keeps ~96 KB of loads in flight.
+// The 4 row tiles of one weight panel run on the same XCD (row tile fastest
+// within an XCD's contiguous range), so the panel comes from HBM once and the
+// other three read it from that XCD's L2; x is L2-resident.  Per (row tile,
+// column tile) pair that is (64 + 64) x K x 2 bytes per CU, the least for 256
+// blocks of this shape.
+// Each output element is accumulated exactly as in gemm_nt_kernel: one
+// v_mfma_f32_32x32x16_bf16 accumulator per 32 x 32 sub-tile with the same
+// operand order and lane layout, k in 16-wide slices in increasing order, then
+// the LoRA expand per adapter and 16-rank slice (hi, then lo), so a row gets
+// the same bits from either kernel (rows of other adapters only receive exact
+// zeros).  Plain epilogue only: bf16 store, rows through a_rows / c_rows,
+// expand from B_a (use_b_off = 1).
+constexpr int FR_TM = 64, FR_TN = 64;      // block tile
+constexpr int FR_KH = 2;                   // 64-wide k halves per stage (k = 128 per stage)
+constexpr int FR_NST = 5;                  // ring stages (5 x 32 KB)
+constexpr int FR_SUB = (FR_TM + FR_TN) * S_CH;     // uint4 per k half of a stage (16 KB)
+constexpr int FR_STAGE = FR_KH * FR_SUB;           // uint4 per stage (32 KB)
+constexpr int FR_DMA = 4 * FR_KH;          // DMA instructions per wave per stage
+__shared__ uint4 fr_ring[FR_NST * FR_STAGE];
 
-__global__ __launch_bounds__(64) void gemm_skinny_kernel(const uint16_t* __restrict__ A,
-                                                         const uint16_t* __restrict__ B, int M,
-                                                         int N, int K, int64_t lda, int64_t ldb,
-                                                         GemmEpi ep) {
-  const int lane = threadIdx.x;
-  // blocks go round-robin over the 8 XCDs: give each XCD a contiguous run of
-  // tiles, row tiles fastest, so the row tiles of one weight panel share that
-  // XCD's L2 (with the row tile fastest across XCDs every XCD read all of W)
-  const int tiles_m = (M + SK_TM - 1) / SK_TM, tiles_n = (N + SK_TN - 1) / SK_TN;
+// s_waitcnt vmcnt(FR_DMA n): at most n stages of this wave's DMA outstanding
+__device__ __forceinline__ void fr_wait(int n) {
+  if (n >= 3) asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
+  else if (n == 2) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  else if (n == 1) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+static_assert(FR_DMA == 8 && FR_NST - 2 <= 3, "fr_wait counts 8 DMA per stage, up to 3 stages");
+
+__global__ __launch_bounds__(256, 1) void gemm_fewrow_kernel(const uint16_t* __restrict__ A,
+                                                             const uint16_t* __restrict__ B, int M,
+                                                             int N, int K, int64_t lda,
+                                                             int64_t ldb, GemmEpi ep) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;   // 32-row, 32-column sub-tile of this wave
+  const int tiles_m = (M + FR_TM - 1) / FR_TM, tiles_n = (N + FR_TN - 1) / FR_TN;
   const int num = tiles_m * tiles_n;
   const int b = blockIdx.x, xcd = b & 7, loc = b >> 3;
   const int per = num >> 3, rem = num & 7;
   if (loc >= per + (xcd < rem ? 1 : 0)) return;
   const int t = (xcd < rem) ? xcd * (per + 1) + loc : rem * (per + 1) + (xcd - rem) * per + loc;
-  const int m0 = (t % tiles_m) * SK_TM, n0 = (t / tiles_m) * SK_TN;
-  const int rl = lane & 31, half = lane >> 5;
-  const int m = m0 + rl;
-  const int ma = min(m, M - 1);   // rows past M load row M - 1 and are not stored
-  // each lane reads 64 contiguous bytes of its row per 64-wide k chunk (k
-  // 32 half .. + 31), so a row's line is fetched once; two lane-half swaps
-  // then give the MFMA layout of each 16-wide slice (half 0: k 16 s .. + 7,
-  // half 1: k 16 s + 8 .. + 15)
-  const uint16_t* arow = A + (int64_t)(ep.a_rows ? ep.a_rows[ma] : ma) * lda + 32 * half;
-  const uint16_t* brow[SK_NJ];
-#pragma unroll
-  for (int j = 0; j < SK_NJ; ++j) brow[j] = B + (int64_t)min(n0 + 32 * j + rl, N - 1) * ldb + 32 * half;
+  const int m0 = (t % tiles_m) * FR_TM, n0 = (t / tiles_m) * FR_TN;
 
-  f32x16 acc[SK_NJ];
+  // DMA sources: instruction i = 4 h + j of wave w fills k half h of a stage:
+  // rows 8 (2 w + j) .. + 7 of A (j < 2) or of B (j >= 2, j - 2 for the row);
+  // lane L lands in row L / 8, physical chunk L % 8, i.e. logical chunk
+  // (L % 8) ^ lds_sw(row).  Rows past the edge are clamped: they only feed
+  // outputs that are never stored.
+  uint32_t off[4];
 #pragma unroll
-  for (int j = 0; j < SK_NJ; ++j)
-#pragma unroll
-    for (int g = 0; g < 16; ++g) acc[j][g] = 0.f;
-  // chunks c0, c1 of both lane halves -> the fragments of slices s0 (into c0)
-  // and s0 + 2 (into c1)
-  auto swap_halves = [](uint4& c0, uint4& c1) {
-    auto x = __builtin_amdgcn_permlane32_swap(c0.x, c1.x, false, false);
-    auto y = __builtin_amdgcn_permlane32_swap(c0.y, c1.y, false, false);
-    auto z = __builtin_amdgcn_permlane32_swap(c0.z, c1.z, false, false);
-    auto w = __builtin_amdgcn_permlane32_swap(c0.w, c1.w, false, false);
-    c0 = make_uint4(x[0], y[0], z[0], w[0]);
-    c1 = make_uint4(x[1], y[1], z[1], w[1]);
-  };
-  for (int k0 = 0; k0 < K; k0 += 64 * SK_KC) {
-    uint4 fa[SK_KC][4], fb[SK_KC][SK_NJ][4];
-#pragma unroll
-    for (int u = 0; u < SK_KC; ++u) {
-      const int k = min(k0 + 64 * u, K - 64);   // K is a multiple of 64: clamps only past K
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        fa[u][e] = *(const uint4*)(arow + k + 8 * e);
-#pragma unroll
-        for (int j = 0; j < SK_NJ; ++j) fb[u][j][e] = *(const uint4*)(brow[j] + k + 8 * e);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < SK_KC; ++u) {
-      if (k0 + 64 * u >= K) break;
-      swap_halves(fa[u][0], fa[u][1]);   // slices 0, 2
-      swap_halves(fa[u][2], fa[u][3]);   // slices 1, 3
-#pragma unroll
-      for (int j = 0; j < SK_NJ; ++j) {
-        swap_halves(fb[u][j][0], fb[u][j][1]);
-        swap_halves(fb[u][j][2], fb[u][j][3]);
-      }
-      constexpr int e_of_slice[4] = {0, 2, 1, 3};
-#pragma unroll
-      for (int sl = 0; sl < 4; ++sl)
-#pragma unroll
-        for (int j = 0; j < SK_NJ; ++j)
-          acc[j] = mfma32(as_bf16x8(fb[u][j][e_of_slice[sl]]), as_bf16x8(fa[u][e_of_slice[sl]]), acc[j]);
+  for (int j = 0; j < 4; ++j) {
+    const int row = 8 * (2 * wave + (j & 1)) + (lane >> 3);
+    const int chunk = (lane & 7) ^ lds_sw(row);
+    if (j < 2) {
+      const int ra = min(m0 + row, M - 1);
+      const int64_t oa = ep.a_rows ? (int64_t)ep.a_rows[ra] * lda : (int64_t)(ra - m0) * lda;
+      off[j] = (uint32_t)((oa + chunk * 8) * 2);
+    } else {
+      const int rb = min(n0 + row, N - 1);
+      off[j] = (uint32_t)(((int64_t)(rb - n0) * ldb + chunk * 8) * 2);
     }
   }
+  const uint16_t* baseA = ep.a_rows ? A : A + (int64_t)m0 * lda;
+  const uint16_t* baseB = B + (int64_t)n0 * ldb;
+  // LDS destination of instruction j within a k half: A rows at offset 0, B
+  // rows after the FR_TM A rows
+  uint32_t ldsd[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    ldsd[j] = __builtin_amdgcn_readfirstlane(
+        lds_addr(fr_ring + ((j < 2 ? 0 : FR_TM) + 8 * (2 * wave + (j & 1))) * S_CH));
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // only DMA is counted from here on
+  const int KT = K / (SBK * FR_KH);   // K is a multiple of 128 here
+  auto issue = [&](int s) {
+    const uint32_t so = (uint32_t)((s % FR_NST) * FR_STAGE) * 16u;
+#pragma unroll
+    for (int h = 0; h < FR_KH; ++h) {
+      const int k0 = (s * FR_KH + h) * SBK;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        dma16s(off[j], (j < 2 ? baseA : baseB) + k0, ldsd[j] + so + (uint32_t)(h * FR_SUB) * 16u);
+    }
+  };
+  // The ring holds FR_NST stages; stage s goes to slot s % FR_NST.  Step kt
+  // runs the MFMAs of stage kt on fragments read during step kt - 1, after
+  // waiting for stage kt + 1, a barrier and the reads of stage kt + 1, so the
+  // LDS latency and the barrier overlap the MFMA chain.  After that barrier
+  // every wave has issued the MFMAs of step kt - 1 (so its reads of stage
+  // kt - 1 are complete): that slot takes stage kt + FR_NST - 1.
+#pragma unroll
+  for (int s = 0; s < FR_NST - 1; ++s)
+    if (s < KT) issue(s);
 
+  const int frag_row = lane & 31, frag_half = lane >> 5;
+  const int ra_l = (wm * 32 + frag_row) * S_CH;             // A row of this lane's fragments
+  const int rb_l = (FR_TM + wn * 32 + frag_row) * S_CH;     // B row
+  const int sw = lds_sw(frag_row);                          // rows 32 apart share the swizzle
+  // two fragment sets: a step's MFMAs read one while the next stage's
+  // fragments land in the other (no register copies between steps)
+  bf16x8 fa[2][FR_KH][4], fb[2][FR_KH][4];
+  auto read_frags = [&](auto S_, int s) {
+    constexpr int S = decltype(S_)::value;
+#pragma unroll
+    for (int h = 0; h < FR_KH; ++h) {
+      const uint4* st = fr_ring + (s % FR_NST) * FR_STAGE + h * FR_SUB;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int c = (2 * q + frag_half) ^ sw;
+        fa[S][h][q] = as_bf16x8(st[ra_l + c]);
+        fb[S][h][q] = as_bf16x8(st[rb_l + c]);
+      }
+    }
+  };
+  f32x16 acc;
+#pragma unroll
+  for (int g = 0; g < 16; ++g) acc[g] = 0.f;
+  fr_wait(min(FR_NST - 2, KT - 1));
+  __builtin_amdgcn_s_barrier();   // stage 0 landed for every wave
+  read_frags(std::integral_constant<int, 0>{}, 0);
+  auto step = [&](auto S_, int kt) {
+    constexpr int S = decltype(S_)::value;
+    // this step's fragments were read a step ago: wait for them here, where it
+    // costs nothing, in a form the compiler sees (s_waitcnt lgkmcnt(0))
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    if (kt + 1 < KT) {
+      fr_wait(min(FR_NST - 3, KT - 2 - kt));   // stage kt + 1 landed (this wave)
+      __builtin_amdgcn_s_barrier();            // ... for every wave; stage kt - 1 consumed by all
+      if (kt + FR_NST - 1 < KT) issue(kt + FR_NST - 1);   // into stage kt - 1's slot
+      read_frags(std::integral_constant<int, 1 - S>{}, kt + 1);
+    }
+#pragma unroll
+    for (int h = 0; h < FR_KH; ++h)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc = mfma32(fb[S][h][q], fa[S][h][q], acc);
+  };
+  int kt = 0;
+  for (; kt + 2 <= KT; kt += 2) {
+    step(std::integral_constant<int, 0>{}, kt);
+    step(std::integral_constant<int, 1>{}, kt + 1);
+  }
+  if (kt < KT) step(std::integral_constant<int, 0>{}, kt);
+
+  const int rl = frag_row, half = frag_half;
+  const int m = m0 + wm * 32 + rl;
+  const int nb = n0 + wn * 32;        // first column of this wave
   const int crow = m < M ? (ep.c_rows ? ep.c_rows[m] : m) : -1;
   if (ep.vec) {
     const int ad = m < M ? ep.adpos[m] : -1;
@@ -1023,62 +1090,81 @@ __global__ __launch_bounds__(64) void gemm_skinny_kernel(const uint16_t* __restr
         lb[sl] = *(const uint4*)(vp + ep.vec_plane);
       }
     }
-    // present adapters in increasing order (wave-uniform walk); the next
-    // adapter's descriptor is in flight while this one's factor slices load
+    // the adapters present in the wave's rows, in increasing order (a
+    // wave-uniform walk), XB at a time: their descriptors, then all of their
+    // factor slices, are loaded together, so a batch costs two memory round
+    // trips rather than two per adapter.  A row changes only in its own
+    // adapter's MFMAs (the others add exact zeros), slice by slice, hi then lo.
     auto next_after = [&](int prev) {
       int nxt = ad > prev ? ad : INT32_MAX;
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) nxt = min(nxt, __shfl_xor(nxt, o));
       return __builtin_amdgcn_readfirstlane(nxt);
     };
-    int a = next_after(-1);
-    lora_adapter_desc d{};
-    if (a != INT32_MAX) d = ep.desc[a];
-    while (a != INT32_MAX) {
-      const int an = next_after(a);
-      lora_adapter_desc dn{};
-      if (an != INT32_MAX) dn = ep.desc[an];
-      const int r = d.rank;
-      const uint16_t* mat = ep.lmat + d.b_off;
-      uint4 v[SL][SK_NJ];
+    constexpr int XB = 8;
+    int prev = -1;
+    for (;;) {
+      int as[XB];
+      int na = 0;
 #pragma unroll
-      for (int sl = 0; sl < SL; ++sl) {
-        const int c = sl * 16 + 8 * half;
+      for (int i = 0; i < XB; ++i) {
+        as[i] = next_after(prev);
+        if (as[i] != INT32_MAX) {
+          prev = as[i];
+          na = i + 1;
+        } else {
+          prev = INT32_MAX - 1;   // later slots find nothing
+        }
+      }
+      if (na == 0) break;
+      int64_t boff[XB];
+      int rk[XB];
 #pragma unroll
-        for (int j = 0; j < SK_NJ; ++j) {
-          const int n = n0 + 32 * j + rl;
-          v[sl][j] = make_uint4(0, 0, 0, 0);
-          if (c < r && n < N) v[sl][j] = *(const uint4*)(mat + (int64_t)n * r + c);
+      for (int i = 0; i < XB; ++i) {
+        boff[i] = 0;
+        rk[i] = 0;
+        if (i < na) {
+          boff[i] = ep.desc[as[i]].b_off;
+          rk[i] = ep.desc[as[i]].rank;
+        }
+      }
+      uint4 v[XB][SL];
+#pragma unroll
+      for (int i = 0; i < XB; ++i) {
+#pragma unroll
+        for (int sl = 0; sl < SL; ++sl) {
+          const int c = sl * 16 + 8 * half;
+          const int n = nb + rl;
+          v[i][sl] = make_uint4(0, 0, 0, 0);
+          if (i < na && c < rk[i] && n < N)
+            v[i][sl] = *(const uint4*)(ep.lmat + boff[i] + (int64_t)n * rk[i] + c);
         }
       }
 #pragma unroll
-      for (int sl = 0; sl < SL; ++sl) {
-        if (sl * 16 >= r) break;
-        const bool mine = ad == a && sl * 16 + 8 * half < r;
-        const uint4 h = mine ? hb[sl] : make_uint4(0, 0, 0, 0);
-        const uint4 lo = mine ? lb[sl] : make_uint4(0, 0, 0, 0);
+      for (int i = 0; i < XB; ++i) {
 #pragma unroll
-        for (int j = 0; j < SK_NJ; ++j) {
-          acc[j] = mfma32(as_bf16x8(v[sl][j]), as_bf16x8(h), acc[j]);
-          acc[j] = mfma32(as_bf16x8(v[sl][j]), as_bf16x8(lo), acc[j]);
+        for (int sl = 0; sl < SL; ++sl) {
+          if (i < na && sl * 16 < rk[i]) {
+            const bool mine = ad == as[i] && sl * 16 + 8 * half < rk[i];
+            const uint4 h = mine ? hb[sl] : make_uint4(0, 0, 0, 0);
+            const uint4 lo = mine ? lb[sl] : make_uint4(0, 0, 0, 0);
+            acc = mfma32(as_bf16x8(v[i][sl]), as_bf16x8(h), acc);
+            acc = mfma32(as_bf16x8(v[i][sl]), as_bf16x8(lo), acc);
+          }
         }
       }
-      a = an;
-      d = dn;
+      if (na < XB) break;
     }
   }
   if (crow < 0) return;
-  // register g of acc[j]: column n0 + 32 j + 8 (g / 4) + 4 half + g % 4
+  // register g of acc: column nb + 8 (g / 4) + 4 half + g % 4
 #pragma unroll
-  for (int j = 0; j < SK_NJ; ++j)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int n = n0 + 32 * j + 8 * q + 4 * half;
-      if (n < N)
-        *(uint2*)(ep.C + (int64_t)crow * ep.ldc + n) =
-            make_uint2(pack2bf(acc[j][4 * q], acc[j][4 * q + 1]),
-                       pack2bf(acc[j][4 * q + 2], acc[j][4 * q + 3]));
-    }
+  for (int q = 0; q < 4; ++q) {
+    const int n = nb + 8 * q + 4 * half;
+    if (n < N)
+      *(uint2*)(ep.C + (int64_t)crow * ep.ldc + n) =
+          make_uint2(pack2bf(acc[4 * q], acc[4 * q + 1]), pack2bf(acc[4 * q + 2], acc[4 * q + 3]));
+  }
 }
 
 }  // namespace lora
@@ -1121,15 +1207,15 @@ static lora_status launch_gemm(const uint16_t* A, const uint16_t* B, int M, int 
     return LORA_E_INVALID_ARG;
   }
   if (tiles_m <= 0) return LORA_OK;
-  // few rows (a plain product, or with the expand from B_a): the skinny kernel
+  // few rows (a plain product, or with the expand from B_a): the few-row kernel
   // keeps every CU busy where the 256x256 tiles would not
   if constexpr (EPI == EPI_BF16) {
     if (!ep.g_tile && ep.glu == 0 && ep.k_split == 0 && !ep.rowscale &&
-        (!ep.vec || ep.use_b_off) && (int64_t)tiles_m * tiles_n < 64 && K % 64 == 0 &&
+        (!ep.vec || ep.use_b_off) && (int64_t)tiles_m * tiles_n < 64 && K % 128 == 0 &&
         N % 4 == 0 && ep.ldc % 4 == 0) {
-      hipLaunchKernelGGL(gemm_skinny_kernel, dim3((unsigned)(cdiv(M, SK_TM) * cdiv(N, SK_TN))),
-                         dim3(64), 0, s, A, B, M, N, K, lda, ldb, ep);
-      return launch_check("gemm_skinny");
+      hipLaunchKernelGGL(gemm_fewrow_kernel, dim3((unsigned)(cdiv(M, FR_TM) * cdiv(N, FR_TN))),
+                         dim3(256), 0, s, A, B, M, N, K, lda, ldb, ep);
+      return launch_check("gemm_fewrow");
     }
   }
   if (group_m <= 0) group_m = pick_group_m(tiles_m);

@@ -12,7 +12,7 @@
 //            32 rows per block streamed through an LDS-DMA ring (128 rows for
 //            large batches, same per-row summation order).
 //   (the expand y += s B_a u / dx += s A_a^T v runs inside the base GEMM's
-//    epilogue: gemm.hip, lora_expand; few-row batches: gemm_skinny_kernel)
+//    epilogue: gemm.hip, lora_expand; few-row batches: gemm_fewrow_kernel)
 //   grad     T[c][j] = s_a sum_{t in chunk} P[t][c] Q[t][j]  (dB_a, dA_a)
 //            one block per (token chunk of an adapter, 256 columns); Q and P
 //            stream through an LDS-DMA ring and Q is transposed on the LDS
