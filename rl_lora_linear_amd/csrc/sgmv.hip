@@ -968,12 +968,15 @@ lora_status launch_shrink(const uint16_t* in, int64_t ld_in, int K, const uint16
   }
   auto go = [&](auto tall_) -> lora_status {
     constexpr bool T = decltype(tall_)::value;
-    static size_t attr = 0;
-    if (attr < lds) {
-      TRY_HIP(hipFuncSetAttribute((const void*)shrink_kernel<T>,
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
-      attr = lds;
-    }
+    // the dynamic LDS bound, raised once to the largest ring this kernel takes
+    // (a thread-safe one-time initialisation, then read-only)
+    static const hipError_t attr_err = hipFuncSetAttribute(
+        (const void*)shrink_kernel<T>, hipFuncAttributeMaxDynamicSharedMemorySize,
+        (int)(T ? std::max((size_t)ST_TM * 64 * sizeof(float),
+                           (size_t)ST_NST * (ST_XSLOTS + 4 * 128) * 16)
+                : std::max((size_t)2 * SH_TM * 64 * sizeof(float),
+                           (size_t)sh_nst<4>() * (SH_XSLOTS + 1024) * 16)));
+    TRY_HIP(attr_err);
     hipLaunchKernelGGL(shrink_kernel<T>, dim3(persistent_blocks()), dim3(256), lds, s, in, ld_in,
                        K, mat_pack, from_b, desc, adpos, ShrinkRows{in_rows, out_rows, rowscale},
                        offsets, T ? pre128 : pre32, n_ad, n_tokens, out, r_max, (uint4*)zero,
@@ -1000,12 +1003,10 @@ lora_status launch_grad_t(dim3 grid, const uint16_t* P, int64_t plane, int r_max
                           float* out_pack, float* partial, int accumulate, GradDual du, int cpi,
                           hipStream_t s) {
   const size_t lds = (size_t)GrP<PN>::NST * GrP<PN>::STAGE * sizeof(uint4);
-  static bool attr = false;
-  if (!attr) {
-    TRY_HIP(hipFuncSetAttribute((const void*)grad_kernel<MODE, PN, MULTI>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
-    attr = true;
-  }
+  static const hipError_t attr_err = hipFuncSetAttribute(
+      (const void*)grad_kernel<MODE, PN, MULTI>, hipFuncAttributeMaxDynamicSharedMemorySize,
+      (int)lds);   // once, thread-safely
+  TRY_HIP(attr_err);
   hipLaunchKernelGGL((grad_kernel<MODE, PN, MULTI>), grid, dim3(256), lds, s, P, plane, r_max,
                      zero, Q,
                      ld_q, D, desc, q_rows, p_ident, offsets, chunk_pre, n_ad, out_pack, partial,
@@ -1076,12 +1077,10 @@ lora_status launch_grad_pair(const uint16_t* u, const uint16_t* dy, int64_t ld_d
       constexpr int PN = decltype(pn)::value;
       constexpr bool MULTI = decltype(multi)::value;
       const size_t lds = (size_t)GrP<PN>::NST * GrP<PN>::STAGE * sizeof(uint4);
-      static bool attr = false;
-      if (!attr) {
-        TRY_HIP(hipFuncSetAttribute((const void*)grad_pair_kernel<PN, MULTI>,
-                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
-        attr = true;
-      }
+      static const hipError_t attr_err = hipFuncSetAttribute(
+          (const void*)grad_pair_kernel<PN, MULTI>, hipFuncAttributeMaxDynamicSharedMemorySize,
+          (int)lds);   // once, thread-safely
+      TRY_HIP(attr_err);
       hipLaunchKernelGGL((grad_pair_kernel<PN, MULTI>), dim3(persistent_blocks()), dim3(256), lds,
                          s, s0, s1, plane, r_max, z, q_rows, 0, offsets, chunk_pre, n_ad,
                          accumulate, MULTI ? cpi : 1);

@@ -4,7 +4,9 @@ Argument marshalling only: every function below forwards torch tensors'
 device pointers, sizes and the current HIP stream to the C entry point of the
 same name and raises LoraError on a non-zero status.  All computation runs in
 the library's gfx950 kernels; there is no fallback path.  If the library is
-missing the import of this module raises, loudly.
+missing the import of this module raises, loudly.  LORA_MI355X_LIB, when set,
+names another build of the same library to load instead (the host-sanitizer
+build of `python -m rl_lora_linear_amd.build --host-asan`).
 """
 from __future__ import annotations
 
@@ -16,7 +18,7 @@ import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "liblora_mi355x.so")
+LIB_PATH = os.environ.get("LORA_MI355X_LIB") or os.path.join(_HERE, "liblora_mi355x.so")
 
 # status codes and flags (include/lora_mi355x.h)
 LORA_OK, LORA_E_INVALID_ARG, LORA_E_UNSUPPORTED, LORA_E_WORKSPACE, LORA_E_HIP, LORA_E_DEVICE_CHECK = range(6)
