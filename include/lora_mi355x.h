@@ -52,9 +52,14 @@
  *     contributes to no gradient; an invalid descriptor makes its adapter
  *     inactive (zero delta, zero gradient); an out-of-range target gives a NaN
  *     logprob and a zero dh row.
- *   - Non-finite values propagate per IEEE 754 except where a row is masked:
- *     masked rows are removed by selection, never by multiplying by zero
- *     (TPU RL note, section 12: inf * 0 is NaN).
+ *   - Non-finite values propagate per IEEE 754 through the projections and the
+ *     logprob path.  Three places contain them (TPU RL note, section 12 "The
+ *     instability I have not solved"): masked loss rows are removed by
+ *     selection, never by multiplying by zero (inf * 0 is NaN); a kept loss
+ *     row whose own inputs are non-finite is removed the same way and
+ *     LORA_FLAG_NONFINITE_LOSS is set; an adapter whose gradient holds a
+ *     non-finite element is not updated by AdamW at all and
+ *     LORA_FLAG_NONFINITE_GRAD is set.
  */
 #ifndef LORA_MI355X_H
 #define LORA_MI355X_H
