@@ -99,10 +99,13 @@ struct LayerWs {
   uint16_t* zero;     // 256 zero bytes (source of the rows past a gradient chunk)
   float* partial;     // dB chunk partials
   float* partial_a;   // dA chunk partials
+  float* shpart;      // chunk sums of a K-split shrink (null: the shrinks do not split)
+  size_t shpart_floats;
   size_t total;
 };
 
-// fwd_only: the forward's part alone (no v planes, no gradient partials)
+// fwd_only: the forward's part alone (no v planes, no gradient partials, no
+// K-split shrink buffer: its shrink runs unsplit, with the same bits)
 LayerWs carve_layer(const lora_shape& sh, void* ws, size_t bytes, bool fwd_only = false) {
   Carve cv(ws, bytes);
   LayerWs w{};
@@ -127,6 +130,9 @@ LayerWs carve_layer(const lora_shape& sh, void* ws, size_t bytes, bool fwd_only 
                                                          sh.max_rank));
   w.partial_a = cv.take<float>((size_t)grad_partial_floats(sh.n_tokens, sh.n_adapters, sh.d_in,
                                                            sh.max_rank));
+  w.shpart_floats = std::max(shrink_part_floats(sh.n_tokens, sh.n_adapters, (int)sh.d_in),
+                             shrink_part_floats(sh.n_tokens, sh.n_adapters, (int)sh.d_out));
+  w.shpart = w.shpart_floats ? cv.take<float>(w.shpart_floats) : nullptr;
   w.total = cv.used;
   return w;
 }
@@ -266,7 +272,7 @@ static lora_status forward_core(const lora_shape& sh, const uint16_t* x, const u
   timer_begin(LORA_TIMER_SHRINK, s);
   TRY(launch_shrink(x, sh.d_in, (int)sh.d_in, A_pack, 0, desc, w.adpos, w.perm, w.perm, nullptr,
                     w.offsets, w.pre32, sh.n_adapters, sh.n_tokens, u_saved, sh.max_rank, w.zero,
-                    s, nullptr, nullptr, nullptr, w.pre128));
+                    s, nullptr, nullptr, nullptr, w.pre128, w.shpart, w.shpart_floats));
   timer_end(LORA_TIMER_SHRINK, s);
   // base GEMM over rows in segment order with the expand y += B_a (s u) fused
   GemmRows f;
@@ -327,7 +333,7 @@ lora_status lora_backward(const lora_shape* shape, const uint16_t* dy, const uin
     timer_begin(LORA_TIMER_SHRINK, s);
     TRY(launch_shrink(dy, sh.d_out, (int)sh.d_out, B_pack, 1, desc, w.adpos, w.perm, w.perm,
                       nullptr, w.offsets, w.pre32, sh.n_adapters, sh.n_tokens, w.v, sh.max_rank,
-                      w.zero, s, nullptr, nullptr, nullptr, w.pre128));
+                      w.zero, s, nullptr, nullptr, nullptr, w.pre128, w.shpart, w.shpart_floats));
     timer_end(LORA_TIMER_SHRINK, s);
     // dX = dY W over rows in segment order with the expand dX += A_a^T (s v) fused
     GemmRows f;

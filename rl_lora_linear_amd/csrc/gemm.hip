@@ -477,7 +477,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_nt_kernel(const uint16_t* __
     // 2 group_m row tiles runs in blocks of group_m row tiles.  The tiles one
     // XCD runs at a time then share their group's weight panels and row
     // panels in its L2
-    g = find_bucket(ep.g_tile, ep.n_groups + 1, t / tiles_n);
+    g = find_bucket_wave(ep.g_tile, ep.n_groups + 1, t / tiles_n);   // whole waves, uniform t
     const int nr = ep.g_tile[g + 1] - ep.g_tile[g];
     const int bm = nr <= 2 * group_m ? nr : group_m;
     const int in = t - ep.g_tile[g] * tiles_n;

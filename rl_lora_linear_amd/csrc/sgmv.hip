@@ -39,7 +39,7 @@ struct TileInfo {
 __device__ __forceinline__ bool tile_of(const int32_t* pre, const int32_t* offsets, int n_ad,
                                         int tile, int tm, TileInfo& ti) {
   if (tile >= pre[n_ad]) return false;
-  const int a = find_bucket(pre, n_ad + 1, tile);
+  const int a = find_bucket_wave(pre, n_ad + 1, tile);   // every caller: whole waves
   ti.a = a;
   ti.p0 = offsets[a] + (tile - pre[a]) * tm;
   ti.rows = min(tm, offsets[a + 1] - ti.p0);
@@ -114,18 +114,63 @@ struct ShrinkSecond {
   uint16_t* out;
 };
 
+// Summation order of every shrink, whatever its tile height or K split: k
+// falls into chunks of SHRINK_KCH; within a chunk the 32-k blocks of even and
+// of odd parity each form one MFMA chain in increasing k, and the chunk's sum
+// is S_c = even + odd; the row's value is T = (((0 + S_0) + S_1) + ...) in
+// chunk order, scaled by s_a (rounded to fp32) and then split into the hi/lo
+// planes.  So a row's u has the same bits in the 32-row and 128-row tiles and
+// in a launch that splits K over blocks (the chunk sums then go through
+// `part` to shrink_fold_kernel, which folds them in the same order).
+constexpr int SHRINK_KCH = 1024;
+
+// Scale and split tile ranks [c0, c0 + rr) of the rows of one tile into the
+// planes of dst; val(row, c) is the row's folded sum T for rank c0 + c.
+template <class V>
+__device__ __forceinline__ void shrink_emit(V&& val, uint16_t* __restrict__ dst, int c0, int rr,
+                                            float sc, const ShrinkRows& rm, int p0, int rows,
+                                            int tm, int64_t plane, int r_max) {
+  // the scaled value is rounded to fp32 before the hi/lo split (no product
+  // fused into the residual), in every tile height alike
+#pragma clang fp contract(off)
+  for (int e = threadIdx.x; e < tm * (r_max / 4); e += blockDim.x) {
+    const int row = e / (r_max / 4), cg = (e % (r_max / 4)) * 4;
+    if (row >= rows) continue;
+    const int prow = p0 + row;
+    const float sc_row = rm.rowscale ? sc * rm.rowscale[prow] : sc;
+    float v[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int c = cg + q;
+      v[q] = c < rr ? sc_row * val(row, c0 + c) : 0.f;
+    }
+    uint32_t h01, l01, h23, l23;
+    split2_bf16(v[0], v[1], h01, l01);
+    split2_bf16(v[2], v[3], h23, l23);
+    uint16_t* o = dst + (int64_t)(rm.out ? rm.out[prow] : prow) * r_max + cg;
+    *(uint2*)o = make_uint2(h01, h23);
+    *(uint2*)(o + plane) = make_uint2(l01, l23);
+  }
+}
+
+// Chunks [c0, c1) of one 32-row tile.  part == nullptr: every chunk of K, the
+// sums folded here and written as planes.  Otherwise the chunk sums S_c go to
+// part[c][row][64] (fp32) and nothing else is written.
 template <int NB, bool KM>
 __device__ __forceinline__ void shrink_tile(const uint16_t* __restrict__ in, int64_t ld_in, int K,
                                             const uint16_t* __restrict__ mat, int r, float scale,
                                             const ShrinkSecond sec, const ShrinkRows rm, int p0,
                                             int rows, uint4* lds, uint16_t* __restrict__ out,
-                                            int64_t plane, int r_max) {
+                                            int64_t plane, int r_max, int c0, int c1,
+                                            float* __restrict__ part) {
   constexpr int MSLOTS = NB * 16 * 16;                 // factor tile slots per stage
   constexpr int STAGE = SH_XSLOTS + MSLOTS;
   constexpr int PER_WAVE = 2 + NB;                     // DMA instructions per wave per stage
   constexpr int NST = sh_nst<NB>();
+  constexpr int CST = SHRINK_KCH / SH_KC;              // stages per chunk
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int KT = (K + SH_KC - 1) / SH_KC;
+  const int kt0 = c0 * CST, kt1 = min(KT, c1 * CST);   // this call's stages
 
   // DMA sources of this lane: 2 row-tile instructions, NB factor instructions
   const uint16_t* xsrc[2];
@@ -183,96 +228,101 @@ __device__ __forceinline__ void shrink_tile(const uint16_t* __restrict__ in, int
   };
 
 #pragma unroll
-  for (int st = 0; st < NST - 1; ++st) issue(st, min(st, KT - 1));
+  for (int st = 0; st < NST - 1; ++st) issue(st, min(kt0 + st, kt1 - 1));
   wait_vm_barrier<(NST - 2) * PER_WAVE>();
 
   // wave w: rows 16 (w & 1) .. + 15, and the 32-k blocks of parity w >> 1
-  // (blocks kp and kp + 2 of each 128-k stage), so each row has an even-block
-  // and an odd-block partial sum, added once at the end: the order of the
-  // 128-row tile, whichever tile height the batch size selects
-  f32x4 acc[NB];
+  // (blocks kp and kp + 2 of each 128-k stage): each row has an even-block and
+  // an odd-block chain per chunk.  Between chunks the odd waves hand their
+  // chains to the even waves through LDS (fo), which add them (S_c) and fold
+  // S_c into tot, or store it to part.
+  f32x4 acc[NB], tot[NB];
 #pragma unroll
-  for (int b = 0; b < NB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int b = 0; b < NB; ++b) acc[b] = tot[b] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int fr = lane & 15;
   const int rh = wave & 1, kp = wave >> 1;
+  float* fo = (float*)(lds + NST * STAGE);   // [SH_TM][64], past the ring
 
-  for (int kt = 0; kt < KT; ++kt) {
-    const int st = kt % NST;
-    issue((kt + NST - 1) % NST, min(kt + NST - 1, KT - 1));
-    const uint4* xt = lds + st * STAGE;
-    const uint4* mt = xt + SH_XSLOTS;
+  int kt = kt0;
+  for (int c = c0; c < c1; ++c) {
+    const int kte = min(kt1, (c + 1) * CST);
+    for (; kt < kte; ++kt) {
+      const int st = (kt - kt0) % NST;
+      issue((kt - kt0 + NST - 1) % NST, min(kt + NST - 1, kt1 - 1));
+      const uint4* xt = lds + st * STAGE;
+      const uint4* mt = xt + SH_XSLOTS;
 #pragma unroll
-    for (int bi = 0; bi < 2; ++bi) {
-      const int bb = kp + 2 * bi;              // 32-k block of the stage
-      if (kt * SH_KC + bb * 32 >= K) continue;
-      const int ch = 4 * bb + (lane >> 4);     // logical chunk of this lane's fragments
-      bf16x8 xa, mb[NB];
-      {
-        const int row = rh * 16 + fr;
-        xa = as_bf16x8(xt[row * 16 + (ch ^ (row & 15))]);
-      }
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        if constexpr (KM) {
-          // rows k = 8 ch + {0..3} and {4..7}; in each 16-lane group, lane 4q + j
-          // addresses row k0 + q, ranks 16 b + 4 j .. + 3, and receives rank
-          // 16 b + (lane & 15) of the four rows
-          const int q = (lane >> 2) & 3, j = lane & 3;
-          const uint32_t off = (uint32_t)(((8 * ch + q) * r + 16 * b + 4 * j) * 2);
-          const uint2 lo = tr_read(mt, off);
-          const uint2 hi = tr_read(mt, off + (uint32_t)(4 * r * 2));
-          mb[b] = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
-        } else {
-          const int c = b * 16 + fr;
-          mb[b] = as_bf16x8(mt[c * 16 + (ch ^ (c & 15))]);
+      for (int bi = 0; bi < 2; ++bi) {
+        const int bb = kp + 2 * bi;              // 32-k block of the stage
+        if (kt * SH_KC + bb * 32 >= K) continue;
+        const int ch = 4 * bb + (lane >> 4);     // logical chunk of this lane's fragments
+        bf16x8 xa, mb[NB];
+        {
+          const int row = rh * 16 + fr;
+          xa = as_bf16x8(xt[row * 16 + (ch ^ (row & 15))]);
         }
-      }
 #pragma unroll
-      for (int b = 0; b < NB; ++b) acc[b] = mfma16(xa, mb[b], acc[b]);
+        for (int b = 0; b < NB; ++b) {
+          if constexpr (KM) {
+            // rows k = 8 ch + {0..3} and {4..7}; in each 16-lane group, lane 4q + j
+            // addresses row k0 + q, ranks 16 b + 4 j .. + 3, and receives rank
+            // 16 b + (lane & 15) of the four rows
+            const int q = (lane >> 2) & 3, j = lane & 3;
+            const uint32_t off = (uint32_t)(((8 * ch + q) * r + 16 * b + 4 * j) * 2);
+            const uint2 lo = tr_read(mt, off);
+            const uint2 hi = tr_read(mt, off + (uint32_t)(4 * r * 2));
+            mb[b] = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+          } else {
+            const int cc = b * 16 + fr;
+            mb[b] = as_bf16x8(mt[cc * 16 + (ch ^ (cc & 15))]);
+          }
+        }
+#pragma unroll
+        for (int b = 0; b < NB; ++b) acc[b] = mfma16(xa, mb[b], acc[b]);
+      }
+      wait_vm_barrier<(NST - 2) * PER_WAVE>();
     }
-    wait_vm_barrier<(NST - 2) * PER_WAVE>();
+    // chunk c's end.  acc[b][i] = chain of D[16 rh + 4 (lane / 16) + i][16 b + lane % 16]
+    if (kp == 1) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          fo[(rh * 16 + 4 * (lane >> 4) + i) * 64 + b * 16 + (lane & 15)] = acc[b][i];
+    }
+    __syncthreads();
+    if (kp == 0) {
+      float* pc = part ? part + (size_t)c * (SH_TM * 64) : nullptr;
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int idx = (rh * 16 + 4 * (lane >> 4) + i) * 64 + b * 16 + (lane & 15);
+          const float sc_sum = acc[b][i] + fo[idx];
+          if (pc) pc[idx] = sc_sum;
+          else tot[b][i] = tot[b][i] + sc_sum;
+        }
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // (fo is written again at the next chunk's end, after that chunk's stage
+    // barriers, which the even waves reach after these reads)
   }
   asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  if (part) return;
 
-  // acc[b][i] = D[16 rh + 4 (lane / 16) + i][16 b + lane % 16], the kp partial
-  float* red = (float*)lds;  // [2][SH_TM][64]
+  float* red = (float*)lds;  // [SH_TM][64]: the folded sums
+  if (kp == 0) {
 #pragma unroll
-  for (int b = 0; b < NB; ++b)
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      red[(kp * SH_TM + rh * 16 + 4 * (lane >> 4) + i) * 64 + b * 16 + (lane & 15)] = acc[b][i];
+      for (int i = 0; i < 4; ++i)
+        red[(rh * 16 + 4 * (lane >> 4) + i) * 64 + b * 16 + (lane & 15)] = tot[b][i];
+  }
   __syncthreads();
-  // tile ranks [c0, c0 + rr) scaled and split into the planes of dst
-  auto emit = [&](uint16_t* __restrict__ dst, int c0, int rr, float sc) {
-    // the scaled value is rounded to fp32 before the hi/lo split (no product
-    // fused into the residual), in both tile heights alike
-#pragma clang fp contract(off)
-    for (int e = tid; e < SH_TM * (r_max / 4); e += 256) {
-      const int row = e / (r_max / 4), cg = (e % (r_max / 4)) * 4;
-      if (row >= rows) continue;
-      const int prow = p0 + row;
-      const float sc_row = rm.rowscale ? sc * rm.rowscale[prow] : sc;
-      float v[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int c = cg + q;
-        float sacc = 0.f;
-        if (c < rr) {
-          const int rc = c0 + c;
-          sacc = red[(0 * SH_TM + row) * 64 + rc] + red[(1 * SH_TM + row) * 64 + rc];
-        }
-        v[q] = sc_row * sacc;
-      }
-      uint32_t h01, l01, h23, l23;
-      split2_bf16(v[0], v[1], h01, l01);
-      split2_bf16(v[2], v[3], h23, l23);
-      uint16_t* o = dst + (int64_t)(rm.out ? rm.out[prow] : prow) * r_max + cg;
-      *(uint2*)o = make_uint2(h01, h23);
-      *(uint2*)(o + plane) = make_uint2(l01, l23);
-    }
-  };
-  emit(out, 0, r, scale);
-  if (!KM && sec.mat) emit(sec.out, sec.c2, sec.r, sec.scale);
+  auto val = [&](int row, int c) { return red[row * 64 + c]; };
+  shrink_emit(val, out, 0, r, scale, rm, p0, rows, SH_TM, plane, r_max);
+  if (!KM && sec.mat) shrink_emit(val, sec.out, sec.c2, sec.r, sec.scale, rm, p0, rows, SH_TM, plane, r_max);
 }
 
 // The same product for large batches over 128-row adapter tiles: each factor
@@ -304,6 +354,7 @@ __device__ __forceinline__ void shrink_tall_tile(const uint16_t* __restrict__ in
   constexpr int STAGE = ST_XSLOTS + MSLOTS;
   constexpr int PER_WAVE = 4 + FB / 2;             // DMA instructions per wave per stage
   constexpr int NST = ST_NST;
+  constexpr int CST = SHRINK_KCH / ST_KC;   // stages per chunk
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int KT = K / ST_KC;
 
@@ -361,16 +412,15 @@ __device__ __forceinline__ void shrink_tall_tile(const uint16_t* __restrict__ in
   for (int st = 0; st < NST - 1; ++st) issue(st, min(st, KT - 1));
   wait_vm_barrier<(NST - 2) * PER_WAVE>();
 
-  // one partial sum per parity of the 32-k block (the stage's slice sl), added
-  // once at the end: the order of the 32-row tile, so a row's u has the same
-  // bits whichever tile height the batch size selects
-  f32x4 acc[2][2][NB];
+  // one chain per parity of the 32-k block (the stage's slice sl) per chunk;
+  // at a chunk's end tot += even + odd (the summation order of every shrink)
+  f32x4 acc[2][2][NB], tot[2][NB];
 #pragma unroll
   for (int h = 0; h < 2; ++h)
 #pragma unroll
     for (int g = 0; g < 2; ++g)
 #pragma unroll
-      for (int b = 0; b < NB; ++b) acc[h][g][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int b = 0; b < NB; ++b) acc[h][g][b] = tot[g][b] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int fr = lane & 15;
   const int q = (lane >> 2) & 3, j = lane & 3;
 
@@ -409,11 +459,20 @@ __device__ __forceinline__ void shrink_tall_tile(const uint16_t* __restrict__ in
         for (int b = 0; b < NB; ++b) acc[sl][g][b] = mfma16(xa[g], mb[b], acc[sl][g][b]);
     }
     wait_vm_barrier<(NST - 2) * PER_WAVE>();
+    if ((kt + 1) % CST == 0 || kt + 1 == KT) {   // chunk end
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) tot[g][b][i] = tot[g][b][i] + (acc[0][g][b][i] + acc[1][g][b][i]);
+          acc[0][g][b] = acc[1][g][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
   }
   asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
 
-  // acc[h][g][b][i] = D[32 wave + 16 g + 4 (lane / 16) + i][16 b + lane % 16],
-  // the even-block (h = 0) and odd-block partial sums
+  // tot[g][b][i] = T[32 wave + 16 g + 4 (lane / 16) + i][16 b + lane % 16]
   float* red = (float*)lds;  // [ST_TM][64]
 #pragma unroll
   for (int g = 0; g < 2; ++g)
@@ -421,41 +480,19 @@ __device__ __forceinline__ void shrink_tall_tile(const uint16_t* __restrict__ in
     for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        red[(wave * 32 + g * 16 + 4 * (lane >> 4) + i) * 64 + b * 16 + (lane & 15)] =
-            acc[0][g][b][i] + acc[1][g][b][i];
+        red[(wave * 32 + g * 16 + 4 * (lane >> 4) + i) * 64 + b * 16 + (lane & 15)] = tot[g][b][i];
   __syncthreads();
-  // tile ranks [c0, c0 + rr) scaled and split into the planes of dst
-  auto emit = [&](uint16_t* __restrict__ dst, int c0, int rr, float sc) {
-    // the scaled value is rounded to fp32 before the hi/lo split (no product
-    // fused into the residual), in both tile heights alike
-#pragma clang fp contract(off)
-    for (int e = tid; e < ST_TM * (r_max / 4); e += 256) {
-      const int row = e / (r_max / 4), cg = (e % (r_max / 4)) * 4;
-      if (row >= rows) continue;
-      const int prow = p0 + row;
-      const float sc_row = rm.rowscale ? sc * rm.rowscale[prow] : sc;
-      float v[4];
-#pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        const int c = cg + qq;
-        v[qq] = c < rr ? sc_row * red[row * 64 + c0 + c] : 0.f;
-      }
-      uint32_t h01, l01, h23, l23;
-      split2_bf16(v[0], v[1], h01, l01);
-      split2_bf16(v[2], v[3], h23, l23);
-      uint16_t* o = dst + (int64_t)(rm.out ? rm.out[prow] : prow) * r_max + cg;
-      *(uint2*)o = make_uint2(h01, h23);
-      *(uint2*)(o + plane) = make_uint2(l01, l23);
-    }
-  };
-  emit(out, 0, r, scale);
-  if (!KM && sec.mat) emit(sec.out, sec.c2, sec.r, sec.scale);
+  auto val = [&](int row, int c) { return red[row * 64 + c]; };
+  shrink_emit(val, out, 0, r, scale, rm, p0, rows, ST_TM, plane, r_max);
+  if (!KM && sec.mat) shrink_emit(val, sec.out, sec.c2, sec.r, sec.scale, rm, p0, rows, ST_TM, plane, r_max);
 }
 
-// One block per CU.  Blocks take the adapter tiles (32 rows, or 128 with
-// TALL; pre[n_ad] of them) XCD-contiguously, then zero, grid-stride, the rows
-// of tokens that belong to no active adapter (adpos == -1), and block 0
-// clears `zero`.
+// One block per CU.  Blocks take the work items XCD-contiguously -- the
+// adapter tiles (32 rows, or 128 with TALL; pre[n_ad] of them), each cut into
+// n_parts ranges of the nch k chunks (n_parts > 1: 32-row tiles only, chunk
+// sums to part[tile][chunk][32][64], folded by shrink_fold_kernel) -- then
+// zero, grid-stride, the rows of tokens that belong to no active adapter
+// (adpos == -1), and block 0 clears `zero`.
 template <bool TALL>
 __global__ __launch_bounds__(256) void shrink_kernel(
     const uint16_t* __restrict__ in, int64_t ld_in, int K, const uint16_t* __restrict__ mat_pack,
@@ -463,14 +500,18 @@ __global__ __launch_bounds__(256) void shrink_kernel(
     const ShrinkRows rm, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ pre32, int n_ad, int64_t n_tokens, uint16_t* __restrict__ out,
     int r_max, uint4* __restrict__ zero, const uint16_t* __restrict__ mat_pack2,
-    const lora_adapter_desc* __restrict__ desc2, uint16_t* __restrict__ out2) {
+    const lora_adapter_desc* __restrict__ desc2, uint16_t* __restrict__ out2, int n_parts,
+    int nch, float* __restrict__ part) {
   extern __shared__ uint4 sh_lds[];
   const int tid = threadIdx.x;
   const int64_t plane = n_tokens * r_max;
-  const ItemRange ir = xcd_items(pre32[n_ad]);
+  const ItemRange ir = xcd_items(pre32[n_ad] * n_parts);
   for (int item = ir.first; item < ir.end; item += ir.step) {
+    const int tile = item / n_parts, pp = item - tile * n_parts;
+    const int c0 = pp * nch / n_parts, c1 = (pp + 1) * nch / n_parts;
+    float* pt = n_parts > 1 ? part + (size_t)tile * nch * (SH_TM * 64) : nullptr;
     TileInfo ti;
-    tile_of(pre32, offsets, n_ad, item, TALL ? ST_TM : SH_TM, ti);
+    tile_of(pre32, offsets, n_ad, tile, TALL ? ST_TM : SH_TM, ti);
     const lora_adapter_desc d = desc[ti.a];
     const int r = d.rank;
     const uint16_t* mat = mat_pack + (from_b ? d.b_off : d.a_off);
@@ -493,7 +534,7 @@ __global__ __launch_bounds__(256) void shrink_kernel(
                                plane, r_max);                                                  \
     else                                                                                       \
       shrink_tile<NB, KM>(in, ld_in, K, mat, r, sc, sec, rm, ti.p0, ti.rows, sh_lds, out,      \
-                          plane, r_max);                                                       \
+                          plane, r_max, c0, c1, pt);                                           \
   } while (0)
     if (from_b) {
       if (nb == 1) SHRINK_TILE(1, true);
@@ -517,6 +558,35 @@ __global__ __launch_bounds__(256) void shrink_kernel(
       uint4* o = (uint4*)(ob + orow * r_max);
       uint4* ol = (uint4*)(ob + plane + orow * r_max);
       for (int c = 0; c < r_max / 8; ++c) o[c] = ol[c] = make_uint4(0, 0, 0, 0);
+    }
+  }
+}
+
+// After a split shrink: per 32-row tile, T = fold of its nch chunk sums in
+// chunk order, scaled and split into the planes exactly as an unsplit tile
+// does it (shrink_emit), for the first table and, dual, the second.
+__global__ __launch_bounds__(256) void shrink_fold_kernel(
+    const float* __restrict__ part, int nch, const lora_adapter_desc* __restrict__ desc,
+    const ShrinkRows rm, const int32_t* __restrict__ offsets, const int32_t* __restrict__ pre32,
+    int n_ad, int64_t n_tokens, uint16_t* __restrict__ out, int r_max,
+    const lora_adapter_desc* __restrict__ desc2, uint16_t* __restrict__ out2) {
+  const int64_t plane = n_tokens * r_max;
+  const ItemRange ir = xcd_items(pre32[n_ad]);
+  for (int tile = ir.first; tile < ir.end; tile += ir.step) {
+    TileInfo ti;
+    tile_of(pre32, offsets, n_ad, tile, SH_TM, ti);
+    const lora_adapter_desc d = desc[ti.a];
+    const float* pt = part + (size_t)tile * nch * (SH_TM * 64);
+    auto val = [&](int row, int c) {
+      float t = 0.f;
+      for (int ch = 0; ch < nch; ++ch) t = t + pt[(size_t)ch * (SH_TM * 64) + row * 64 + c];
+      return t;
+    };
+    shrink_emit(val, out, 0, d.rank, d.scale, rm, ti.p0, ti.rows, SH_TM, plane, r_max);
+    if (desc2) {
+      const lora_adapter_desc d2 = desc2[ti.a];
+      shrink_emit(val, out2, 16 * ((d.rank + 15) / 16), d2.rank, d2.scale, rm, ti.p0, ti.rows,
+                  SH_TM, plane, r_max);
     }
   }
 }
@@ -936,13 +1006,31 @@ static unsigned persistent_blocks() {
   return (unsigned)(cus & ~7);
 }
 
+// Parts per 32-row tile of a K-split shrink: about 256 / (bound on the tiles)
+// when that bound is at most 128 (n_tokens / 32 + n_ad, one partial tile per
+// adapter), capped by the number of k chunks; else 1.  A fixed 256, not the
+// device's CU count, so that workspace sizes do not depend on the device.
+int shrink_split_parts(int64_t n_tokens, int n_ad, int K) {
+  const int nch = (K + SHRINK_KCH - 1) / SHRINK_KCH;
+  const int64_t tiles = (n_tokens + SH_TM - 1) / SH_TM + n_ad;
+  if (n_tokens <= 0 || nch < 2 || tiles > 128) return 1;
+  return (int)std::min<int64_t>(nch, (256 + tiles - 1) / tiles);
+}
+
+size_t shrink_part_floats(int64_t n_tokens, int n_ad, int K) {
+  if (shrink_split_parts(n_tokens, n_ad, K) <= 1) return 0;
+  const int64_t tiles = (n_tokens + SH_TM - 1) / SH_TM + n_ad;
+  return (size_t)tiles * ((K + SHRINK_KCH - 1) / SHRINK_KCH) * SH_TM * 64;
+}
+
 lora_status launch_shrink(const uint16_t* in, int64_t ld_in, int K, const uint16_t* mat_pack,
                           int from_b, const lora_adapter_desc* desc, const int32_t* adpos,
                           const int32_t* in_rows, const int32_t* out_rows, const float* rowscale,
                           const int32_t* offsets, const int32_t* pre32, int n_ad,
                           int64_t n_tokens, uint16_t* out, int r_max, void* zero, hipStream_t s,
                           const uint16_t* mat_pack2, const lora_adapter_desc* desc2,
-                          uint16_t* out2, const int32_t* pre128) {
+                          uint16_t* out2, const int32_t* pre128, float* part,
+                          size_t part_floats) {
   if (n_tokens <= 0) return LORA_OK;
   if (mat_pack2 && (from_b || r_max > 32 || !desc2 || !out2)) {
     set_error("shrink: a dual shrink takes two A tables with ranks <= 32");
@@ -959,12 +1047,22 @@ lora_status launch_shrink(const uint16_t* in, int64_t ld_in, int K, const uint16
     for (int nb = 1; nb <= nb_max; ++nb)
       lds = std::max(lds, (size_t)ST_NST * (ST_XSLOTS + (nb <= 2 ? 2 : 4) * 128) * 16);
   } else {
+    // the ring, then the odd chains' hand-over area [SH_TM][64] floats
     const size_t ring[4] = {(size_t)sh_nst<1>() * (SH_XSLOTS + 256) * 16,
                             (size_t)sh_nst<2>() * (SH_XSLOTS + 512) * 16,
                             (size_t)sh_nst<3>() * (SH_XSLOTS + 768) * 16,
                             (size_t)sh_nst<4>() * (SH_XSLOTS + 1024) * 16};
-    lds = (size_t)2 * SH_TM * 64 * sizeof(float);   // the even/odd partial sums
-    for (int nb = 1; nb <= nb_max; ++nb) lds = std::max(lds, ring[nb - 1]);
+    lds = ring[nb_max - 1] + (size_t)SH_TM * 64 * sizeof(float);
+  }
+  // K split (32-row tiles, when the tiles alone leave most CUs idle): parts of
+  // the k chunks per tile, so that tiles x parts covers about every CU
+  const int nch = (K + SHRINK_KCH - 1) / SHRINK_KCH;
+  int n_parts = 1;
+  if (!tall && part) {
+    n_parts = shrink_split_parts(n_tokens, n_ad, K);
+    if (n_parts > 1 &&
+        part_floats < shrink_part_floats(n_tokens, n_ad, K))
+      n_parts = 1;
   }
   auto go = [&](auto tall_) -> lora_status {
     constexpr bool T = decltype(tall_)::value;
@@ -974,14 +1072,19 @@ lora_status launch_shrink(const uint16_t* in, int64_t ld_in, int K, const uint16
         (const void*)shrink_kernel<T>, hipFuncAttributeMaxDynamicSharedMemorySize,
         (int)(T ? std::max((size_t)ST_TM * 64 * sizeof(float),
                            (size_t)ST_NST * (ST_XSLOTS + 4 * 128) * 16)
-                : std::max((size_t)2 * SH_TM * 64 * sizeof(float),
-                           (size_t)sh_nst<4>() * (SH_XSLOTS + 1024) * 16)));
+                : (size_t)sh_nst<4>() * (SH_XSLOTS + 1024) * 16 + (size_t)SH_TM * 64 * 4));
     TRY_HIP(attr_err);
+    const ShrinkRows rmap{in_rows, out_rows, rowscale};
     hipLaunchKernelGGL(shrink_kernel<T>, dim3(persistent_blocks()), dim3(256), lds, s, in, ld_in,
-                       K, mat_pack, from_b, desc, adpos, ShrinkRows{in_rows, out_rows, rowscale},
-                       offsets, T ? pre128 : pre32, n_ad, n_tokens, out, r_max, (uint4*)zero,
-                       mat_pack2, desc2, out2);
-    return launch_check("shrink");
+                       K, mat_pack, from_b, desc, adpos, rmap, offsets, T ? pre128 : pre32, n_ad,
+                       n_tokens, out, r_max, (uint4*)zero, mat_pack2, desc2, out2, n_parts, nch,
+                       part);
+    const lora_status st = launch_check("shrink");
+    if (st != LORA_OK || n_parts == 1) return st;
+    hipLaunchKernelGGL(shrink_fold_kernel, dim3(persistent_blocks()), dim3(256), 0, s, part, nch,
+                       desc, rmap, offsets, pre32, n_ad, n_tokens, out, r_max,
+                       mat_pack2 ? desc2 : nullptr, out2);
+    return launch_check("shrink_fold");
   };
   return tall ? go(std::true_type{}) : go(std::false_type{});
 }

@@ -81,9 +81,15 @@ lora_status launch_shrink(const uint16_t* in, int64_t ld_in, int K, const uint16
                           int64_t n_tokens, uint16_t* out, int r_max, void* zero, hipStream_t s,
                           const uint16_t* mat_pack2 = nullptr,
                           const lora_adapter_desc* desc2 = nullptr, uint16_t* out2 = nullptr,
-                          const int32_t* pre128 = nullptr);
+                          const int32_t* pre128 = nullptr, float* part = nullptr,
+                          size_t part_floats = 0);
 // (pre128 nullable: the prefix of ceil(count / 128) per key; with it, large
-// batches run in 128-row tiles.)
+// batches run in 128-row tiles.  part nullable: with part_floats >=
+// shrink_part_floats(n_tokens, n_ad, K) floats there, small batches split K
+// over blocks and fold the chunk sums in a second launch; the bits of the
+// result are the same either way.)
+int shrink_split_parts(int64_t n_tokens, int n_ad, int K);
+size_t shrink_part_floats(int64_t n_tokens, int n_ad, int K);
 // Per key a: T_a = sum over a's positions p of P[p_row] Q[q_rows[p]]^T (mode 0:
 // [D][r] at b_off; mode 1: [r][D] at a_off), P the bf16 hi/lo planes.  P row:
 // the position itself with p_ident, else q_rows[p].  q_rows nullable.

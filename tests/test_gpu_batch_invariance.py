@@ -35,11 +35,15 @@ def _assert_same_bits(a, b, what):
 
 
 # the 256-row prefix runs its forward GEMM in the few-row kernel, the batch in
-# the 256x256-tile kernel
+# the 256x256-tile kernel.  With d_in 2048 and d_out 3072 the shrinks sum over
+# 2 and 3 k chunks: the batch in 128-row tiles, the 4096-row prefix in 32-row
+# tiles, and the 256-row prefix with K split over blocks (chunk sums folded in
+# a second launch), forward and backward.
 @pytest.mark.parametrize("n_small", [4096, 256])
-def test_dense_layer_rows_batch_invariant(n_small):
+@pytest.mark.parametrize("d_in,d_out", [(256, 320), (2048, 3072)])
+def test_dense_layer_rows_batch_invariant(n_small, d_in, d_out):
     n_big = TALL_ROWS + 4096
-    c = W.lora_layer(seed=27, n_tokens=n_big, d_in=256, d_out=320, ranks=[8, 64, 16, 32, 48],
+    c = W.lora_layer(seed=27, n_tokens=n_big, d_in=d_in, d_out=d_out, ranks=[8, 64, 16, 32, 48],
                      alphas=[16.0, 32.0, 8.0, 64.0, 32.0], order="interleaved")
     dl = DevLayer(c)
     y_b, u_b = dl.forward()
