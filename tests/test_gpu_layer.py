@@ -92,10 +92,17 @@ def _case(kind):
         ids = W.sorted_ids_from_lengths(lengths)
         ranks = [[8, 16, 24, 32, 40, 48, 56, 64][i % 8] for i in range(600)]
         return W.lora_layer(26, len(ids), 320, 448, ranks, [float(r) for r in ranks], ids=ids)
+    if kind == "split_k":     # few tokens over many adapters, K over 2 and 3 chunks of 1024
+        # with partial last chunks: both shrinks split K over blocks and fold the chunk sums
+        rng = np.random.default_rng(27)
+        ids = rng.integers(0, 24, size=300).astype(np.int32)
+        ids[ids == 7] = 3                         # adapter 7 owns no token
+        ranks = [[8, 16, 24, 32, 40, 48, 56, 64][i % 8] for i in range(24)]
+        return W.lora_layer(27, 300, 1536, 2560, ranks, [32.0] * 24, ids=ids, order="interleaved")
     raise KeyError(kind)
 
 
-CASES = ["tiny", "ragged", "multi", "big_chunks", "many", "tall", "small_segs"]
+CASES = ["tiny", "ragged", "multi", "big_chunks", "many", "tall", "small_segs", "split_k"]
 
 
 @pytest.mark.parametrize("kind", CASES)
