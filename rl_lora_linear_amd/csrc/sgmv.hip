@@ -68,8 +68,9 @@ __device__ __forceinline__ ItemRange xcd_items(int total) {
 // stages ahead, explicit vmcnt waits; the compiler cannot track which stage a
 // DMA writes).  Each LDS row of the token tile is 256 B = 16 chunks, chunk c
 // stored at c ^ (row & 15), so the fragment reads of 16 consecutive rows are
-// conflict-free.  Wave w multiplies k-sub-block w (32 k) of every stage; the
-// four partial products are summed in LDS in wave order at the end.
+// conflict-free.  Waves 0, 1 take rows 0..15, 16..31 over the even 32-k
+// blocks of every stage, waves 2, 3 the same rows over the odd blocks; the
+// two chains of a row meet once per 1024-k chunk (the summation order below).
 // The factor is either A_a (KM = false: [r][K], one LDS row per rank, stored
 // like the token rows) or B_a read in place for M_a = B_a^T (KM = true:
 // B_a is [K][r], so a k slice is one contiguous block of 128 x r values; it
