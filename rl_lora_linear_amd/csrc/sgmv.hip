@@ -935,9 +935,9 @@ __global__ __launch_bounds__(256) void grad_pair_kernel(
   }
 }
 
-// grid = (n_ad, blocks over D*r_max/1024).  Sums the chunk partials of
-// adapters with several chunks, in chunk order; with accumulate == 0 writes
-// zeros for active adapters that own no token.
+// Slice blockIdx.y of one key's result (grid y: blocks over D*r_max/1024).
+// Sums the chunk partials of adapters with several chunks, in chunk order;
+// with accumulate == 0 writes zeros for active adapters that own no token.
 __device__ __forceinline__ void grad_finalize_body(
     int a, const lora_adapter_desc* __restrict__ desc, const uint8_t* __restrict__ active,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ chunk_pre, int D,
@@ -968,27 +968,57 @@ __device__ __forceinline__ void grad_finalize_body(
   }
 }
 
-__global__ __launch_bounds__(256) void grad_finalize_kernel(
-    const lora_adapter_desc* __restrict__ desc, const uint8_t* __restrict__ active,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ chunk_pre, int D,
-    int64_t slot_floats, int mode, float* __restrict__ out_pack, const float* __restrict__ partial,
-    int accumulate) {
-  grad_finalize_body(blockIdx.x, desc, active, offsets, chunk_pre, D, slot_floats, mode, out_pack,
-                     partial, accumulate);
+// Block (x, y) finalizes slice y of keys [x kpb, (x + 1) kpb) (kpb <= 256):
+// the block's threads first check one key each, so that a group of keys with
+// nothing to do (one chunk, or tokens and no zero fill) costs one round of
+// loads; the keys with work are then done in key order.
+__device__ __forceinline__ void grad_finalize_keys(
+    int a0, int kpb, int n_ad, const lora_adapter_desc* __restrict__ desc,
+    const uint8_t* __restrict__ active, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ chunk_pre, int D, int64_t slot_floats, int mode,
+    float* __restrict__ out_pack, const float* __restrict__ partial, int accumulate) {
+  if (kpb == 1) {   // one key per block: its own early exits are the check
+    grad_finalize_body(a0, desc, active, offsets, chunk_pre, D, slot_floats, mode, out_pack,
+                       partial, accumulate);
+    return;
+  }
+  __shared__ uint64_t s_work[4];   // bit k: key a0 + k has work
+  const int k = threadIdx.x, a = a0 + k;
+  bool work = false;
+  if (k < kpb && a < n_ad && active[a]) {
+    const bool empty = offsets[a + 1] == offsets[a];
+    work = (empty && !accumulate) || (!empty && chunk_pre[a + 1] - chunk_pre[a] >= 2);
+  }
+  const uint64_t bal = __ballot(work);
+  if ((k & 63) == 0) s_work[k >> 6] = bal;
+  __syncthreads();
+  for (int w = 0; w < 4; ++w)
+    for (uint64_t m = s_work[w]; m; m &= m - 1)
+      grad_finalize_body(a0 + 64 * w + __ffsll((long long)m) - 1, desc, active, offsets,
+                         chunk_pre, D, slot_floats, mode, out_pack, partial, accumulate);
 }
 
-// Both sides of a paired launch: blocks x < n_ad finalize side 0 (mode 0),
-// the rest side 1 (mode 1).
+__global__ __launch_bounds__(256) void grad_finalize_kernel(
+    const lora_adapter_desc* __restrict__ desc, const uint8_t* __restrict__ active,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ chunk_pre, int n_ad,
+    int kpb, int D, int64_t slot_floats, int mode, float* __restrict__ out_pack,
+    const float* __restrict__ partial, int accumulate) {
+  grad_finalize_keys(blockIdx.x * kpb, kpb, n_ad, desc, active, offsets, chunk_pre, D,
+                     slot_floats, mode, out_pack, partial, accumulate);
+}
+
+// Both sides of a paired launch: blocks x < nb0 finalize side 0 (mode 0), the
+// rest side 1 (mode 1).
 __global__ __launch_bounds__(256) void grad_finalize_pair_kernel(
     GradSide s0, GradSide s1, const uint8_t* __restrict__ active,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ chunk_pre, int n_ad,
-    int r_max, int accumulate) {
-  const int a = blockIdx.x;
-  if (a < n_ad)
-    grad_finalize_body(a, s0.desc, active, offsets, chunk_pre, s0.D, (int64_t)s0.D * r_max, 0,
-                       s0.out_pack, s0.partial, accumulate);
+    int kpb, int nb0, int r_max, int accumulate) {
+  const int x = blockIdx.x;
+  if (x < nb0)
+    grad_finalize_keys(x * kpb, kpb, n_ad, s0.desc, active, offsets, chunk_pre, s0.D,
+                       (int64_t)s0.D * r_max, 0, s0.out_pack, s0.partial, accumulate);
   else
-    grad_finalize_body(a - n_ad, s1.desc, active, offsets, chunk_pre, s1.D,
+    grad_finalize_keys((x - nb0) * kpb, kpb, n_ad, s1.desc, active, offsets, chunk_pre, s1.D,
                        (int64_t)s1.D * r_max, 1, s1.out_pack, s1.partial, accumulate);
 }
 
@@ -1090,6 +1120,14 @@ lora_status launch_shrink(const uint16_t* in, int64_t ld_in, int K, const uint16
   return tall ? go(std::true_type{}) : go(std::false_type{});
 }
 
+// Keys per finalize block: 256 when the keys average under a quarter of a
+// gradient chunk of tokens (most have one chunk and nothing to fold, so a
+// block checks many; at most a quarter of them can have several chunks), else
+// 1 (every key's chunk partials get blocks of their own).
+static int finalize_keys_per_block(int64_t n_tokens, int n_ad) {
+  return n_tokens < (int64_t)n_ad * (GR_TC / 4) ? 256 : 1;
+}
+
 // 256-column blocks per gradient item: all of them (one item per chunk) when
 // the chunks alone give every CU a few items, else one.  Chunks are about one
 // per key and one per 1024 tokens.
@@ -1154,12 +1192,15 @@ lora_status launch_grad(int mode, const uint16_t* P, int r_max, const void* zero
   }
   const int64_t slot = (int64_t)D * rt;   // floats per chunk partial
   const unsigned gy = (unsigned)std::max<int64_t>(1, std::min<int64_t>(64, cdiv((int64_t)D * r_max, 1024)));
-  hipLaunchKernelGGL(grad_finalize_kernel, dim3(n_ad, gy), dim3(256), 0, s, desc, active, offsets,
-                     chunk_pre, D, slot, mode, out_pack, partial, accumulate);
+  const int kpb = finalize_keys_per_block(n_tokens, n_ad);
+  const unsigned gx = (unsigned)cdiv(n_ad, kpb);
+  hipLaunchKernelGGL(grad_finalize_kernel, dim3(gx, gy), dim3(256), 0, s, desc, active, offsets,
+                     chunk_pre, n_ad, kpb, D, slot, mode, out_pack, partial, accumulate);
   lora_status st = launch_check("grad_finalize");
   if (st || !dual) return st;
-  hipLaunchKernelGGL(grad_finalize_kernel, dim3(n_ad, gy), dim3(256), 0, s, desc2, active, offsets,
-                     chunk_pre, D, slot, mode, out2, partial + (int64_t)r_max * D, accumulate);
+  hipLaunchKernelGGL(grad_finalize_kernel, dim3(gx, gy), dim3(256), 0, s, desc2, active, offsets,
+                     chunk_pre, n_ad, kpb, D, slot, mode, out2, partial + (int64_t)r_max * D,
+                     accumulate);
   return launch_check("grad_finalize");
 }
 
@@ -1199,8 +1240,10 @@ lora_status launch_grad_pair(const uint16_t* u, const uint16_t* dy, int64_t ld_d
   }
   const unsigned gy = (unsigned)std::max<int64_t>(
       1, std::min<int64_t>(64, cdiv((int64_t)std::max(d_in, d_out) * r_max, 1024)));
-  hipLaunchKernelGGL(grad_finalize_pair_kernel, dim3(2 * n_ad, gy), dim3(256), 0, s, s0, s1,
-                     active, offsets, chunk_pre, n_ad, r_max, accumulate);
+  const int kpb = finalize_keys_per_block(n_tokens, n_ad);
+  const int nb0 = (int)cdiv(n_ad, kpb);
+  hipLaunchKernelGGL(grad_finalize_pair_kernel, dim3(2 * nb0, gy), dim3(256), 0, s, s0, s1,
+                     active, offsets, chunk_pre, n_ad, kpb, nb0, r_max, accumulate);
   return launch_check("grad_finalize_pair");
 }
 

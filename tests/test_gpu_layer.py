@@ -99,10 +99,17 @@ def _case(kind):
         ids[ids == 7] = 3                         # adapter 7 owns no token
         ranks = [[8, 16, 24, 32, 40, 48, 56, 64][i % 8] for i in range(24)]
         return W.lora_layer(27, 300, 1536, 2560, ranks, [32.0] * 24, ids=ids, order="interleaved")
+    if kind == "mixed_chunks":   # many small adapters (finalize blocks check 256 keys each)
+        # with one adapter over two gradient chunks and one with no token
+        lengths = [1500] + [190] * 19 + [0] + [190] * 19
+        ids = W.sorted_ids_from_lengths(lengths)
+        ranks = [[16, 32, 8, 64][i % 4] for i in range(len(lengths))]
+        return W.lora_layer(28, len(ids), 256, 320, ranks, [32.0] * len(lengths), ids=ids)
     raise KeyError(kind)
 
 
-CASES = ["tiny", "ragged", "multi", "big_chunks", "many", "tall", "small_segs", "split_k"]
+CASES = ["tiny", "ragged", "multi", "big_chunks", "many", "tall", "small_segs", "split_k",
+         "mixed_chunks"]
 
 
 @pytest.mark.parametrize("kind", CASES)
