@@ -286,6 +286,41 @@ __global__ __launch_bounds__(1024) void seg_small_kernel(
     for (int r = 0; r < SEG_SMALL_N / 1024; ++r)
       if (r * 1024 + tid < n) s_ids[r * 1024 + tid] = v[r];
   }
+  __syncthreads();
+  // Sorted ids that are all in range and non-decreasing (the promise kept):
+  // the stable order is the identity, and each key's count is the distance
+  // between the first positions of consecutive keys.  No histogram, no
+  // scatter; the results are those of the general path below.
+  bool fast = false;
+  if (sorted) {
+    int bad = 0;
+    for (int r = 0; r < rounds; ++r) {
+      const int t = r * 1024 + tid;
+      if (t < n) {
+        const int32_t id = s_ids[t];
+        bad |= (id < 0 || id >= n_keys || (t + 1 < n && s_ids[t + 1] < id)) ? 1 : 0;
+      }
+    }
+    fast = __syncthreads_or(bad) == 0;
+  }
+  if (fast) {
+    // s_off[k] = first position whose id >= k (k = 0..n_keys): each key is
+    // written by the one position where the ids step over it
+    for (int r = 0; r < rounds; ++r) {
+      const int t = r * 1024 + tid;
+      if (t < n) {
+        const int32_t id = s_ids[t], prev = t ? s_ids[t - 1] : -1;
+        for (int k = prev + 1; k <= id; ++k) s_off[k] = t;
+        if (t == n - 1)
+          for (int k = id + 1; k <= n_keys; ++k) s_off[k] = n;
+      }
+    }
+    __syncthreads();
+    const int cnt = tid < n_keys ? s_off[tid + 1] - s_off[tid] : 0;
+    __syncthreads();
+    if (tid < n_keys) s_off[tid] = cnt;   // counts, as the general path leaves them
+    __syncthreads();
+  } else {
   for (int i = tid; i < chunks * K1; i += 1024) s_hist[i] = 0;
   __syncthreads();
   for (int r = 0; r < rounds; ++r) {
@@ -323,6 +358,7 @@ __global__ __launch_bounds__(1024) void seg_small_kernel(
     if (lane == 0) s_off[k] = base;
   }
   __syncthreads();
+  }
   // exclusive scan over keys: offsets and the tile prefix arrays
   if (n_keys <= 64) {   // one wave, no barriers
     if (tid < 64) {
@@ -395,6 +431,20 @@ __global__ __launch_bounds__(1024) void seg_small_kernel(
       if (tl.pre[i]) tl.pre[i][n_keys] = s_v[1 + i][1023];
   }
   __syncthreads();
+  }
+  if (fast) {   // the identity order
+    for (int r = 0; r < rounds; ++r) {
+      const int t = r * 1024 + tid;
+      if (t >= n) continue;
+      const int32_t id = s_ids[t];
+      perm[t] = t;
+      if (adpos) adpos[t] = s_act[id] ? id : -1;
+      if (row_div > 0) {
+        tokrow[t] = t / row_div;
+        inv[t] = t;
+      }
+    }
+    return;
   }
   // scatter, stable within each key
   for (int r = 0; r < rounds; ++r) {
