@@ -36,10 +36,14 @@ struct TileInfo {
   int rows;   // rows in this tile
 };
 
+// WAVE: the bucket search by a whole wave's ballots (fewer dependent loads;
+// the shrink's lookup sits on its critical path), else the binary search
+// (fewer registers; the gradient items measured no faster with the wave one).
+template <bool WAVE = true>
 __device__ __forceinline__ bool tile_of(const int32_t* pre, const int32_t* offsets, int n_ad,
                                         int tile, int tm, TileInfo& ti) {
   if (tile >= pre[n_ad]) return false;
-  const int a = find_bucket_wave(pre, n_ad + 1, tile);   // every caller: whole waves
+  const int a = WAVE ? find_bucket_wave(pre, n_ad + 1, tile) : find_bucket(pre, n_ad + 1, tile);
   ti.a = a;
   ti.p0 = offsets[a] + (tile - pre[a]) * tm;
   ti.rows = min(tm, offsets[a + 1] - ti.p0);
@@ -785,7 +789,7 @@ __device__ __forceinline__ void grad_item(
     float* __restrict__ out_pack, float* __restrict__ partial, int accumulate, int slot, int j0,
     int nblk, int32_t* tok_s, uint4* gr_lds, const GradDual du) {
   TileInfo ti;
-  tile_of(chunk_pre, offsets, n_ad, slot, GR_TC, ti);
+  tile_of<false>(chunk_pre, offsets, n_ad, slot, GR_TC, ti);
   __syncthreads();   // every wave is done with the previous item's tokens and ring
   for (int i = threadIdx.x; i < ti.rows; i += 256) tok_s[i] = q_rows ? q_rows[ti.p0 + i] : ti.p0 + i;
   const int p_base = p_ident ? ti.p0 : -1;
