@@ -130,8 +130,8 @@ def cpu_baseline(case, target_s):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); every box here has "
-              "one MI355X, and the multi-GPU path is a design (DESIGN.md), not a measured run.",
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the path runs on "
+              "one MI355X; sharding it over several GPUs is designed, not built or measured.",
               file=sys.stderr)
         sys.exit(2)
     import numpy as np
