@@ -105,11 +105,18 @@ def _case(kind):
         ids = W.sorted_ids_from_lengths(lengths)
         ranks = [[16, 32, 8, 64][i % 4] for i in range(len(lengths))]
         return W.lora_layer(28, len(ids), 256, 320, ranks, [32.0] * len(lengths), ids=ids)
+    if kind == "huge_keys":   # 5000 adapters of 0-3 tokens: the tile -> adapter lookups
+        # search a 5001-entry prefix array (three rounds of the wave search)
+        rng = np.random.default_rng(29)
+        lengths = rng.integers(0, 4, size=5000)
+        ids = W.sorted_ids_from_lengths(lengths)
+        ranks = [[8, 16, 32, 64][i % 4] for i in range(5000)]
+        return W.lora_layer(29, len(ids), 128, 192, ranks, [16.0] * 5000, ids=ids)
     raise KeyError(kind)
 
 
 CASES = ["tiny", "ragged", "multi", "big_chunks", "many", "tall", "small_segs", "split_k",
-         "mixed_chunks"]
+         "mixed_chunks", "huge_keys"]
 
 
 @pytest.mark.parametrize("kind", CASES)
