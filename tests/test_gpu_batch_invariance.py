@@ -20,7 +20,7 @@ from gpu_util import DevLayer
 pytestmark = pytest.mark.gpu
 L = pytest.importorskip("rl_lora_linear_amd.lib")
 
-TALL_ROWS = 2 * 128 * 256   # rows from which the shrink takes 128-row tiles (256 CUs)
+TALL_ROWS = 128 * 256 // 2   # rows from which the shrink takes 128-row tiles (256 CUs)
 
 
 def _bits(t):
