@@ -214,7 +214,8 @@ lora_status lora_backward(const lora_shape* shape, const uint16_t* dy, const uin
  * merged in a fixed order.
  *   h bf16 [n][hidden]; lm_head bf16 [vocab][hidden]; targets int32 [n]
  *   logprobs, lse fp32 [n] out
- * hidden and vocab multiples of 64; n >= 0. */
+ * hidden and vocab multiples of 64 below 2^30; 0 <= n < 2^30.  The size
+ * queries return 0 for any n or vocab outside these ranges. */
 size_t token_logprobs_workspace_bytes(int64_t n, int64_t vocab);
 lora_status token_logprobs(int64_t n, int64_t hidden, int64_t vocab, const uint16_t* h,
                            const uint16_t* lm_head, const int32_t* targets, float* logprobs,
@@ -228,7 +229,8 @@ lora_status token_logprobs(int64_t n, int64_t hidden, int64_t vocab, const uint1
  *   lse fp32 [n] from token_logprobs;  dlogp fp32 [n];  dh bf16 [n][hidden] out
  * The chunk is the largest multiple of 256 rows whose G fits the workspace;
  * token_logprobs_backward_workspace_bytes(n, vocab, rows) sizes one for a
- * chunk of `rows` (>= 256). */
+ * chunk of `rows` (>= 256) rounded up to 256, capped at n rounded up to 256
+ * (the longest chunk the call runs). */
 size_t token_logprobs_backward_workspace_bytes(int64_t n, int64_t vocab, int64_t chunk_rows);
 lora_status token_logprobs_backward(int64_t n, int64_t hidden, int64_t vocab, const uint16_t* h,
                                     const uint16_t* lm_head, const uint16_t* lm_head_t,
@@ -268,6 +270,7 @@ typedef struct { float clip_low, clip_high; } loss_config;
  * in the workspace status word (read it with lora_device_status).  Inputs a
  * kind does not read are never inspected.  A finite row whose ratio
  * exp(l - l_s) overflows fp32 still follows IEEE 754.
+ * 0 <= n < 2^30 (the size query returns 0 outside it).
  * Workspace: loss_grad_workspace_bytes(n); word 0 is the status word. */
 size_t loss_grad_workspace_bytes(int64_t n);
 lora_status loss_grad(int32_t kind, int64_t n, const float* logprobs, const float* weights,

@@ -374,8 +374,14 @@ static size_t logprob_ws(int64_t n, int64_t vocab, float** pm, float** ps, float
   return cv.used;
 }
 
+// The size queries accept exactly the n and vocab the entry points accept
+// (check_lp below) and return 0 for anything else.
+static bool lp_sizes_ok(int64_t n, int64_t vocab) {
+  return n >= 0 && n <= INT32_MAX / 2 && vocab > 0 && vocab % 64 == 0 && vocab <= INT32_MAX / 2;
+}
+
 size_t token_logprobs_workspace_bytes(int64_t n, int64_t vocab) {
-  if (n < 0 || vocab <= 0) return 0;
+  if (!lp_sizes_ok(n, vocab)) return 0;
   return logprob_ws(n, vocab, nullptr, nullptr, nullptr, nullptr, 0);
 }
 
@@ -412,10 +418,13 @@ lora_status token_logprobs(int64_t n, int64_t hidden, int64_t vocab, const uint1
 }
 
 size_t token_logprobs_backward_workspace_bytes(int64_t n, int64_t vocab, int64_t chunk_rows) {
-  if (n < 0 || vocab <= 0 || chunk_rows < 256) return 0;
+  if (!lp_sizes_ok(n, vocab) || chunk_rows < 256) return 0;
+  // The entry point never runs a chunk longer than n rounded up to 256 rows.
+  const int64_t rows = std::min(lora::align_up(std::min<int64_t>(chunk_rows, INT32_MAX / 2), 256),
+                                lora::align_up(std::max<int64_t>(n, 1), 256));
   Carve cv(nullptr, 0);
   cv.take<int32_t>(64);
-  cv.take<uint16_t>((size_t)lora::align_up(chunk_rows, 256) * vocab);
+  cv.take<uint16_t>((size_t)rows * vocab);
   return cv.used;
 }
 
@@ -453,7 +462,7 @@ lora_status token_logprobs_backward(int64_t n, int64_t hidden, int64_t vocab, co
 
 // ------------------------------------------------------------------ loss
 size_t loss_grad_workspace_bytes(int64_t n) {
-  if (n < 0) return 0;
+  if (n < 0 || n > INT32_MAX / 2) return 0;
   return 256 + (size_t)std::max<int64_t>(1, cdiv(n, 1024)) * sizeof(double);
 }
 
@@ -462,7 +471,7 @@ lora_status loss_grad(int32_t kind, int64_t n, const float* logprobs, const floa
                       const float* custom_g, const loss_config* cfg, float* loss_out,
                       float* dlogp, void* ws, size_t ws_bytes, void* stream) {
   LORA_ARG_CHECK(kind >= LOSS_CROSS_ENTROPY && kind <= LOSS_CUSTOM, "unknown loss kind %d", kind);
-  LORA_ARG_CHECK(n >= 0, "n must be >= 0");
+  LORA_ARG_CHECK(n >= 0 && n <= INT32_MAX / 2, "n %lld outside [0, 2^30)", (long long)n);
   LORA_ARG_CHECK(loss_out != nullptr, "loss_out is NULL");
   LORA_ARG_CHECK(n == 0 || (logprobs && weights && dlogp), "logprobs/weights/dlogp NULL");
   if (kind == LOSS_IMPORTANCE_SAMPLING || kind == LOSS_PPO)

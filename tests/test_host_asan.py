@@ -1,9 +1,10 @@
 """The library's host code under AddressSanitizer (CPU only).
 
 Builds the library with its host pass instrumented (device code as usual) and
-runs the host-side checks of test_abi_host.py against it in a child process
-with the ASan runtime preloaded: symbol lookup, every entry point's argument
-validation, the workspace size queries and the workspace carving they share.
+runs the host-side checks of test_abi_host.py and the property checks of
+test_abi_fuzz.py against it in a child process with the ASan runtime preloaded:
+symbol lookup, every entry point's argument validation, the workspace size
+queries and the workspace carving they share.
 An invalid read or write, a use after free or a double free in any of them
 aborts the child with an AddressSanitizer report.  Leak detection is off: the
 Python interpreter itself keeps allocations alive at exit.
@@ -33,7 +34,8 @@ def test_host_code_clean_under_asan():
     env.update(LD_PRELOAD=rt, LORA_MI355X_LIB=lib,
                ASAN_OPTIONS="detect_leaks=0:abort_on_error=0:halt_on_error=1")
     res = subprocess.run([sys.executable, "-m", "pytest", "-q", "-p", "no:cacheprovider",
-                          os.path.join(ROOT, "tests", "test_abi_host.py")],
+                          os.path.join(ROOT, "tests", "test_abi_host.py"),
+                          os.path.join(ROOT, "tests", "test_abi_fuzz.py")],
                          cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     out = res.stdout + res.stderr
     assert "AddressSanitizer" not in out, out[-4000:]
