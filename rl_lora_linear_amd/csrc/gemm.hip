@@ -270,9 +270,11 @@ __device__ __forceinline__ int expand_prep(const GemmEpi& ep, char* X, int wave,
   const int k = threadIdx.x;
   if (k < x_passes(ep, glu1) * n_runs) {
     const int p = k >= n_runs, kk = k - p * n_runs;
-    const lora_adapter_desc d = (p ? ep.desc2 : ep.desc)[tb.rad[kk]];
-    dk.rank = d.rank;
-    dk.moff = ep.use_b_off ? d.b_off : d.a_off;
+    // the field's address is chosen, not its value, so nothing waits on the
+    // loads before the expand uses them
+    const lora_adapter_desc* d = (p ? ep.desc2 : ep.desc) + tb.rad[kk];
+    dk.rank = d->rank;
+    dk.moff = *(ep.use_b_off ? &d->b_off : &d->a_off);
   }
   return n_runs;
 }
@@ -524,31 +526,25 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_nt_kernel(const uint16_t* __
 #pragma unroll
       for (int g = 0; g < 16; ++g) acc[i][j][g] = 0.f;
 
-  // epilogue row metadata, loaded now so its latency hides under the k loop
+  // Gathered A rows of this wave's DMA (instruction i fills rows 8 (w DMA_PER_OP
+  // + i) .. + 7 of a stage; lane L takes row L / 8), loaded first and in one
+  // batch: the first DMA waits on them, and nothing else.
+  int arow[DMA_PER_OP];
+#pragma unroll
+  for (int i = 0; i < DMA_PER_OP; ++i)
+    arow[i] = min(m0 + (wave * DMA_PER_OP + i) * 8 + (lane >> 3), Mlim - 1);
+  if (ep.a_rows) {
+#pragma unroll
+    for (int i = 0; i < DMA_PER_OP; ++i) arow[i] = ep.a_rows[arow[i]];
+  }
+
+  // epilogue row metadata (loaded with the prologue's first stage)
   const int m_l = lane & 31;
   const int n_q = 4 * (lane >> 5);
   int tok[4], ad[4];
   float rs[4];
   int gy[4];          // EPI_LSE / EPI_GRAD: target; EPI_GRAD: dlogp, lse of the rows
   float gd[4], gl[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = m0 + wm * 128 + i * 32 + m_l;
-    tok[i] = row < Mlim ? (ep.c_rows ? ep.c_rows[row] : row) : -1;
-    ad[i] = (EPI == EPI_BF16 && ep.vec && row < Mlim) ? ep.adpos[row] : -1;
-    rs[i] = (EPI == EPI_BF16 && ep.rowscale && row < Mlim) ? ep.rowscale[row] : 1.f;
-    gy[i] = -1;
-    gd[i] = 0.f;
-    gl[i] = 0.f;
-    if (EPI == EPI_LSE && row < M) gy[i] = ep.targets[row];
-    if (EPI == EPI_GRAD && row < M) {
-      gy[i] = ep.targets[row];
-      gd[i] = ep.dlogp[row];
-      gl[i] = ep.lse[row];
-      if (gy[i] < 0 || gy[i] >= N) gd[i] = 0.f;   // invalid target: zero row
-    }
-  }
-
   const int KT = K / SBK;
   uint4* sA = g_stage;
   uint4* sB = g_stage + NSTAGE * S_TILE;
@@ -575,9 +571,8 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_nt_kernel(const uint16_t* __
   for (int i = 0; i < DMA_PER_OP; ++i) {
     const int row = (wave * DMA_PER_OP + i) * 8 + (lane >> 3);
     const int chunk = (lane & 7) ^ lds_sw(row);
-    const int ra = min(m0 + row, Mlim - 1);
     const int rb = min(n0 + (glu1 ? (row & (GBN / 2 - 1)) : row), N - 1);
-    const int64_t oa = ep.a_rows ? (int64_t)ep.a_rows[ra] * lda : (int64_t)(ra - m0) * lda;
+    const int64_t oa = ep.a_rows ? (int64_t)arow[i] * lda : (int64_t)(arow[i] - m0) * lda;
     offA[i] = (uint32_t)((oa + chunk * 8) * 2);
     offB[i] = (uint32_t)(((int64_t)(rb - n0) * ldb + chunk * 8) * 2);
   }
@@ -600,6 +595,25 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_nt_kernel(const uint16_t* __
   for (int i = 0; i < DMA_PER_OP; ++i) dmaA(0, i, baseA);
 #pragma unroll
   for (int i = 0; i < DMA_PER_OP; ++i) dmaB(0, i, bsrc(0));
+  // The row metadata, issued between the two stages' DMA: it lands with stage
+  // 0 (the prologue's wait covers it) and does not delay stage 0.
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = m0 + wm * 128 + i * 32 + m_l;
+    tok[i] = row < Mlim ? (ep.c_rows ? ep.c_rows[row] : row) : -1;
+    ad[i] = (EPI == EPI_BF16 && ep.vec && row < Mlim) ? ep.adpos[row] : -1;
+    rs[i] = (EPI == EPI_BF16 && ep.rowscale && row < Mlim) ? ep.rowscale[row] : 1.f;
+    gy[i] = -1;
+    gd[i] = 0.f;
+    gl[i] = 0.f;
+    if (EPI == EPI_LSE && row < M) gy[i] = ep.targets[row];
+    if (EPI == EPI_GRAD && row < M) {
+      gy[i] = ep.targets[row];
+      gd[i] = ep.dlogp[row];
+      gl[i] = ep.lse[row];
+      if (gy[i] < 0 || gy[i] >= N) gd[i] = 0.f;   // invalid target: zero row
+    }
+  }
   if (KT > 1) {
 #pragma unroll
     for (int i = 0; i < DMA_PER_OP; ++i) dmaA(1, i, baseA + SBK);
@@ -610,15 +624,21 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_nt_kernel(const uint16_t* __
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
   }
 
-  // LoRA expand tables (the row metadata has landed with stage 0)
+  // LoRA expand tables, built after the first k step, whose barrier has waited
+  // for every load so far: built before it, the wait for the row metadata
+  // would also wait for the second stage's DMA (issued later), and the first
+  // step's MFMAs could not run while that stage lands.  Every wave of the
+  // block calls it at that point.
   int x_runs = 0;
   XDesc x_dk{0, 0};
-  if (EPI == EPI_BF16 && ep.vec) {
-    int vrow[4];   // vector row of each fragment row: its C row, or its position
+  auto prep = [&]() {
+    if (EPI == EPI_BF16 && ep.vec) {
+      int vrow[4];   // vector row of each fragment row: its C row, or its position
 #pragma unroll
-    for (int i = 0; i < 4; ++i) vrow[i] = ep.vec_by_pos ? m0 + wm * 128 + i * 32 + m_l : tok[i];
-    x_runs = expand_prep(ep, (char*)g_stage, wave, lane, glu1, ad, vrow, x_dk);
-  }
+      for (int i = 0; i < 4; ++i) vrow[i] = ep.vec_by_pos ? m0 + wm * 128 + i * 32 + m_l : tok[i];
+      x_runs = expand_prep(ep, (char*)g_stage, wave, lane, glu1, ad, vrow, x_dk);
+    }
+  };
 
   const int frag_row = lane & 31;   // row within a 32-row MFMA tile
   const int frag_half = lane >> 5;  // which 8-wide k half of a 16-wide k slice
@@ -703,11 +723,13 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_nt_kernel(const uint16_t* __
   const bool live = m0 + wm * 128 < Mlim;
   int kt = 0;
   if (live) {
-    for (; kt + 2 <= KT; kt += 2) {
-      step(std::integral_constant<int, 0>{}, kt);
-      step(std::integral_constant<int, 1>{}, kt + 1);
+    step(std::integral_constant<int, 0>{}, 0);
+    prep();
+    for (kt = 1; kt + 2 <= KT; kt += 2) {
+      step(std::integral_constant<int, 1>{}, kt);
+      step(std::integral_constant<int, 0>{}, kt + 1);
     }
-    if (kt < KT) step(std::integral_constant<int, 0>{}, kt);
+    if (kt < KT) step(std::integral_constant<int, 1>{}, kt);
   } else {
     for (; kt < KT; ++kt) {
       if (kt >= 1 && kt + 1 < KT) {
@@ -719,6 +741,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_nt_kernel(const uint16_t* __
         for (int i = 0; i < DMA_PER_OP; ++i) dmaB(sn, i, bsrc(k0));
       }
       asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+      if (kt == 0) prep();
     }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no DMA may outlive the block
