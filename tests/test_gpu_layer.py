@@ -112,11 +112,20 @@ def _case(kind):
         ids = W.sorted_ids_from_lengths(lengths)
         ranks = [[8, 16, 32, 64][i % 4] for i in range(5000)]
         return W.lora_layer(29, len(ids), 128, 192, ranks, [16.0] * 5000, ids=ids)
+    if kind == "wide":        # 8192 interleaved tokens over 8 adapters at d 2048 -> 2560: the
+        # headline tiling (32-row shrink tiles, about one per CU; 256x256 GEMM tiles) with a
+        # partial last k chunk in the backward shrink; an adapter with no token
+        rng = np.random.default_rng(30)
+        ids = rng.integers(0, 8, size=8192).astype(np.int32)
+        ids[ids == 6] = 1                         # adapter 6 owns no token
+        ranks = [16, 64, 8, 32, 24, 48, 40, 56]
+        return W.lora_layer(30, 8192, 2048, 2560, ranks, [float(r) for r in ranks], ids=ids,
+                            order="interleaved")
     raise KeyError(kind)
 
 
 CASES = ["tiny", "ragged", "multi", "big_chunks", "many", "tall", "small_segs", "split_k",
-         "mixed_chunks", "huge_keys"]
+         "mixed_chunks", "huge_keys", "wide"]
 
 
 @pytest.mark.parametrize("kind", CASES)
