@@ -279,6 +279,21 @@ __device__ __forceinline__ int expand_prep(const GemmEpi& ep, char* X, int wave,
   return n_runs;
 }
 
+// Each run's rank and factor offset, per set, into the tables above the ring:
+// written after the k loop (the descriptor loads of expand_prep have landed)
+// and before the barrier that precedes lora_expand, so that the expand issues
+// its first DMA round without a barrier of its own.
+__device__ __forceinline__ void x_tables(const GemmEpi& ep, bool glu1, char* X, int n_runs,
+                                         const XDesc& dk) {
+  const XTabs tb = x_tabs(X);
+  const int k = threadIdx.x;
+  if (k < x_passes(ep, glu1) * n_runs) {
+    const int p = k >= n_runs, kk = k - p * n_runs;
+    tb.rank[p * GBM + kk] = dk.rank;
+    tb.moff[p * GBM + kk] = dk.moff;
+  }
+}
+
 // Fused LoRA expand, staged through LDS.  Every row m of the tile owned by
 // adapter a gets (s_a u_m) . M_a^T added to its accumulators: one extra MFMA
 // K-slab of depth r_a per plane (the scaled vector is stored as bf16 hi and lo
@@ -294,10 +309,10 @@ __device__ __forceinline__ int expand_prep(const GemmEpi& ep, char* X, int wave,
 // run only for the 32-row tiles holding rows of it.  glu = 1 tiles run the
 // first set in the waves of the first column half and the second set in the
 // others; a K split runs both sets over every row.  Called by every thread of
-// the block after the k loop, with the ring free, and with the tables of
-// expand_prep; ends with a barrier (LDS free again).
+// the block after the k loop and a barrier, with the ring free and the tables
+// of expand_prep and x_tables visible; ends with a barrier (LDS free again).
 __device__ __forceinline__ void lora_expand(const GemmEpi& ep, char* X, int n0, int N, int wave,
-                                            int lane, bool glu1, int n_runs, const XDesc& dk,
+                                            int lane, bool glu1, int n_runs,
                                             f32x16 (&acc)[4][NJ]) {
   const int wm = wave / NWN, wn = wave % NWN;
   const int m_l = lane & 31, half = lane >> 5;
@@ -322,19 +337,9 @@ __device__ __forceinline__ void lora_expand(const GemmEpi& ep, char* X, int n0, 
         dma16v(src, lds_addr((const uint4*)(X + pl * XV_PLANE + (q - lane) * 16)));
       }
   };
-  if (n_runs > 0) dma_vec(ep.vec);
-  {
-    const int k = threadIdx.x;
-    if (k < passes * n_runs) {
-      const int p = k >= n_runs, kk = k - p * n_runs;
-      tb.rank[p * GBM + kk] = dk.rank;
-      tb.moff[p * GBM + kk] = dk.moff;
-    }
-  }
   int rid[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) rid[i] = tb.rid[wm * 128 + i * 32 + m_l];
-  lds_barrier();
 
   const uint4* XV = (const uint4*)X;
   const uint4* XL = (const uint4*)(X + XV_PLANE);
@@ -345,7 +350,8 @@ __device__ __forceinline__ void lora_expand(const GemmEpi& ep, char* X, int n0, 
     const int* rk = tb.rank + p * GBM;
     const int64_t* mo = tb.moff + p * GBM;
     const bool mine = !glu1 || ((wn >= NWN / 2) == (p == 1));
-    if (p > 0 && n_runs > 0) dma_vec(ep.vec2);
+    // the pass's vector rows go out with its first batch's factor blocks
+    if (n_runs > 0) dma_vec(p ? ep.vec2 : ep.vec);
 #pragma unroll 1
     for (int k0 = 0; k0 < n_runs;) {
       // the batch: runs k0 .. k1 - 1, as many as the factor area holds
@@ -840,10 +846,9 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_nt_kernel(const uint16_t* __
 #pragma unroll
           for (int g = 0; g < 16; ++g) acc[i][j][g] *= rs[i];
     }
-    __syncthreads();   // every wave is done reading the ring
-    if (ep.vec) {
-      lora_expand(ep, T, n0, N, wave, lane, glu1, x_runs, x_dk, acc);
-    }
+    if (ep.vec) x_tables(ep, glu1, T, x_runs, x_dk);
+    __syncthreads();   // every wave is done reading the ring; the run tables are visible
+    if (ep.vec) lora_expand(ep, T, n0, N, wave, lane, glu1, x_runs, acc);
     stage_rows();
 #pragma unroll
     for (int i = 0; i < 4; ++i)
