@@ -3,6 +3,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <atomic>
 #include <cmath>
 #include <mutex>
 #include <string>
@@ -33,6 +34,20 @@ lora_status hip_check(hipError_t e, const char* what) {
 }
 
 lora_status launch_check(const char* what) { return hip_check(hipGetLastError(), what); }
+
+int device_cus() {
+  static std::atomic<int> cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cus[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
 
 // ------------------------------------------------------------------ timing
 // Measurement hooks, per host thread: each thread that enables timing keeps its

@@ -188,6 +188,8 @@ namespace lora_host {
 void set_error(const char* fmt, ...);
 lora_status hip_check(hipError_t e, const char* what);
 lora_status launch_check(const char* what);
+// Compute units of the current device (queried once per device).
+int device_cus();
 
 // Kernel timing hooks (no-ops unless lora_timing_enable(1)).
 void timer_begin(int timer, hipStream_t s);

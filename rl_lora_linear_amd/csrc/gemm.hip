@@ -461,23 +461,12 @@ __device__ __forceinline__ void lora_expand(const GemmEpi& ep, char* X, int n0, 
   }
 }
 
+// One 256 x 256 output tile t of gemm_nt_kernel (live_m: live row tiles).
 template <int EPI>
-__global__ __launch_bounds__(GTHREADS, 1) void gemm_nt_kernel(const uint16_t* __restrict__ A,
-                                                         const uint16_t* __restrict__ B, int M,
-                                                         int N, int K, int64_t lda, int64_t ldb,
-                                                         GemmEpi ep, int tiles_m, int tiles_n,
-                                                         int group_m) {
-  // ---- tile id: XCD-contiguous, then grouped along M.  Grouped launches are
-  // sized for a bound on the row tiles; the live count comes from the device
-  // prefix, and the live tiles are split evenly over the XCDs (the surplus
-  // blocks of every XCD exit), so no XCD is left with only dead tiles.
-  const int live_m = ep.g_tile ? ep.g_tile[ep.n_groups] : tiles_m;   // <= tiles_m
-  const int num = live_m * tiles_n;
-  const int bid = blockIdx.x;
-  const int xcd = bid & 7, loc = bid >> 3;
-  const int per = num >> 3, rem = num & 7;
-  if (loc >= per + (xcd < rem ? 1 : 0)) return;
-  const int t = (xcd < rem) ? xcd * (per + 1) + loc : rem * (per + 1) + (xcd - rem) * per + loc;
+__device__ __forceinline__ void gemm_nt_tile(const uint16_t* __restrict__ A,
+                                             const uint16_t* __restrict__ B, int M, int N, int K,
+                                             int64_t lda, int64_t ldb, const GemmEpi& ep,
+                                             int tiles_n, int group_m, int live_m, int t) {
   int tm, tn, g = 0;
   if (ep.g_tile) {
     // grouped: tiles run group by group (group g owns tiles g_tile[g] * tiles_n
@@ -516,7 +505,10 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_nt_kernel(const uint16_t* __
     if (ep.B2) B2g = ep.B2 + (int64_t)g * ep.ldb_group;
   }
 
-  const int tid = threadIdx.x;
+  // Opaque per tile: the lane-derived addresses are recomputed for each tile
+  // rather than hoisted out of the tile loop and held across the epilogue.
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / NWN, wn = wave % NWN;
@@ -946,6 +938,48 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_nt_kernel(const uint16_t* __
   }
 }
 
+// Kernel arguments of gemm_nt_kernel, one struct so that the kernel can read
+// them back from the argument segment.
+struct GemmArgs {
+  const uint16_t* A;
+  const uint16_t* B;
+  int M, N, K;
+  int64_t lda, ldb;
+  GemmEpi ep;
+  int tiles_m, tiles_n, group_m;
+};
+
+// Persistent over the tiles: tile ids are XCD-contiguous (XCD x runs a
+// contiguous range of them, grouped along M as gemm_nt_tile maps them), and
+// the blocks of one XCD take its range round robin.  Grouped launches are
+// sized for a bound on the row tiles; the live count comes from the device
+// prefix and the live tiles are split evenly over the XCDs, so no XCD is left
+// with only dead tiles.  A block's loop ends when its XCD's range is done
+// (surplus blocks exit at once).  Each tile reads the arguments afresh from
+// the argument segment (scalar loads through a pointer the compiler cannot
+// prove loop-invariant): held across the loop they would not fit in the
+// scalar registers beside the k loop's own.
+template <int EPI>
+__global__ __launch_bounds__(GTHREADS, 1) void gemm_nt_kernel(GemmArgs args) {
+  typedef const __attribute__((address_space(4))) GemmArgs* KPtr;
+  const KPtr kbase = (KPtr)__builtin_amdgcn_kernarg_segment_ptr();
+  const int live_m = args.ep.g_tile ? args.ep.g_tile[args.ep.n_groups] : args.tiles_m;
+  const int num = live_m * args.tiles_n;
+  const int xcd = blockIdx.x & 7, loc = blockIdx.x >> 3;
+  const int per = num >> 3, rem = num & 7;
+  const int cnt = per + (xcd < rem ? 1 : 0);
+  const int first = xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per;
+  const int nb = (int)(gridDim.x >> 3) + (xcd < (int)(gridDim.x & 7) ? 1 : 0);   // this XCD's blocks
+  for (int j = loc; j < cnt; j += nb) {
+    KPtr kp = kbase;
+    asm volatile("" : "+s"(kp));
+    const GemmArgs& a = *(const GemmArgs*)kp;
+    gemm_nt_tile<EPI>(a.A, a.B, a.M, a.N, a.K, a.lda, a.ldb, a.ep, a.tiles_n, a.group_m, live_m,
+                      first + j);
+    __syncthreads();   // the epilogue's LDS reads are done before the next tile's DMA
+  }
+}
+
 // ---- few-row GEMM (decode-shaped batches)
 //
 // With M of a few hundred rows the 256x256 tiles leave most CUs idle (256 rows
@@ -1249,8 +1283,10 @@ static lora_status launch_gemm(const uint16_t* A, const uint16_t* B, int M, int 
   if (group_m <= 0) group_m = pick_group_m(tiles_m);
   if (group_m > tiles_m) group_m = tiles_m;
   // operand tiles are static LDS objects: no dynamic LDS
-  hipLaunchKernelGGL(gemm_nt_kernel<EPI>, dim3(tiles_m * tiles_n), dim3(GTHREADS), 0, s, A, B, M, N,
-                     K, lda, ldb, ep, tiles_m, tiles_n, group_m);
+  // one resident block per CU (the LDS block is a whole CU's), each looping over tiles
+  const int grid = (int)std::min<int64_t>((int64_t)tiles_m * tiles_n, std::max(device_cus(), 8));
+  const GemmArgs args{A, B, M, N, K, lda, ldb, ep, tiles_m, tiles_n, group_m};
+  hipLaunchKernelGGL(gemm_nt_kernel<EPI>, dim3(grid), dim3(GTHREADS), 0, s, args);
   return launch_check("gemm_nt");
 }
 
