@@ -50,11 +50,14 @@ def _mlp_run(dm, ids=None, trace=None, grads=None, accumulate=False):
     return y, dx, grads, saved, ws
 
 
-# the third case: 200 rank-64 adapters over 2000 tokens, so a 256-row tile holds
+# the last two cases: 200 adapters over 2000 tokens, so a 256-row tile holds
 # ~25 adapter runs and the fused LoRA expand stages their factor blocks in
-# several batches in every launch (gate/up, down, dh, the K-split dX)
+# several batches in every launch (gate/up, down, dh, the K-split dX); at rank 32
+# the gate/up and K-split launches stage both LoRA sets per round, at rank 64
+# one set per round
 @pytest.mark.parametrize("n,H,F,n_ad,r,seed", [(600, 256, 320, 5, 32, 41), (777, 192, 256, 3, 48, 42),
-                                               (2000, 256, 320, 200, 64, 43)])
+                                               (2000, 256, 320, 200, 64, 43),
+                                               (2000, 256, 320, 200, 32, 44)])
 def test_mlp_layer_parity(n, H, F, n_ad, r, seed):
     c = W.moe_layer(seed=seed, n_tokens=n, hidden=H, d_ff=F, n_experts=1, top_k=1,
                     n_adapters=n_ad, rank=r)
