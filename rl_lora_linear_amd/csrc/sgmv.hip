@@ -1033,13 +1033,7 @@ using namespace lora;
 
 // Blocks of a one-block-per-CU grid: the device's CU count rounded down to a
 // multiple of 8 (one stretch per XCD).
-static unsigned persistent_blocks() {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8)
-    cus = 256;
-  return (unsigned)(cus & ~7);
-}
+static unsigned persistent_blocks() { return (unsigned)(std::max(device_cus(), 8) & ~7); }
 
 // Parts per 32-row tile of a K-split shrink: about 256 / (bound on the tiles)
 // when that bound is at most 128 (n_tokens / 32 + n_ad, one partial tile per
