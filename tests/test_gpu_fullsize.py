@@ -311,7 +311,13 @@ def test_logprob_full_size():
                                   clip_low=0.2, clip_high=0.2)
     dlg = dl.cpu().numpy().astype(np.float64)
     rho = np.exp(lp_g.astype(np.float64) - samp.cpu().numpy())
+    # where fp32 and fp64 can take the clip decision differently (ratio within
+    # 1e-5 of a bound), either valid gradient (clipped: 0; unclipped: -rho A on a
+    # kept row) is accepted; every other row is compared
     near = (np.abs(rho - 0.8) < 1e-5) | (np.abs(rho - 1.2) < 1e-5)
+    alt = np.where(act != 0, -rho * adv, 0.0)
+    ok = (np.abs(dlg - dl_ref) < 1e-5) | (np.abs(dlg - alt) < 1e-5) | (np.abs(dlg) < 1e-30)
+    assert ok[near].all()
     assert rel_err(dlg[~near], dl_ref[~near]) < TOL_F32
     assert abs(float(loss.item()) - L_ref) <= TOL_F32 * max(abs(L_ref), 1e-3)
     dh_ref = OP.token_logprobs_backward(h64, U64, t_np, dlg, rows=rows)
