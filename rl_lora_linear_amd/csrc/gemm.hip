@@ -1269,6 +1269,10 @@ static lora_status launch_gemm(const uint16_t* A, const uint16_t* B, int M, int 
     return LORA_E_INVALID_ARG;
   }
   if (tiles_m <= 0) return LORA_OK;
+  if ((int64_t)tiles_m * tiles_n > INT32_MAX) {   // tile ids are 32-bit in the kernels
+    set_error("gemm: %lld x %lld output tiles exceed 2^31", (long long)tiles_m, (long long)tiles_n);
+    return LORA_E_UNSUPPORTED;
+  }
   // few rows (a plain product, or with the expand from B_a): the few-row kernel
   // keeps every CU busy where the 256x256 tiles would not
   if constexpr (EPI == EPI_BF16) {
