@@ -706,6 +706,11 @@ __device__ __forceinline__ void gemm_nt_tile(const uint16_t* __restrict__ A,
             else fb[nxt][t - 4] = as_bf16x8(Bn[b_row[t - 4] + cq[0]]);
           }
         }
+        // The first phase issues the next stage's DMA: this wave takes issue
+        // priority over the other wave of its SIMD for that phase, so the DMA
+        // leaves as early as possible and has the most time to land.
+        if (q == 0 && g == 0) __builtin_amdgcn_s_setprio(2);
+        if (q == 1 && g == 0) __builtin_amdgcn_s_setprio(0);
         if (q == 0 && more) {   // the whole next stage as early as possible
           if (g < DMA_PER_OP) dmaA(SN, g, ka);
           else dmaB(SN, g - DMA_PER_OP, kb);
