@@ -662,11 +662,12 @@ __device__ __forceinline__ void gemm_nt_tile(const uint16_t* __restrict__ A,
   // groups, and the step's 2 DMA_PER_OP DMA instructions (the other stage, k
   // step kt + 1) one per group of the first phase, so the vector-memory, LDS
   // and scalar work issues in the shadow of the matrix pipe and the DMA has
-  // most of the step to land.  The step's one barrier sits in the middle of
-  // its last phase, whose second half reads the next stage's first slice
-  // under the remaining MFMAs.  sched_barrier keeps the groups
-  // in this order.  After the wait and the barrier the next stage is visible
-  // and its first slice is read.
+  // most of the step to land.  The step's one barrier sits after the third
+  // group of its last phase (XBAR), whose remaining groups read the next
+  // stage's first slice under their MFMAs (measured against groups 0..6: the
+  // q/o GEMM is fastest here, with the DMA phase's issue priority below).
+  // sched_barrier keeps the groups in this order.  After the wait and the
+  // barrier the next stage is visible and its first slice is read.
   auto step = [&](auto S_, int kt) {
     constexpr int S = decltype(S_)::value;
     constexpr int SN = 1 - S;
@@ -679,6 +680,7 @@ __device__ __forceinline__ void gemm_nt_tile(const uint16_t* __restrict__ A,
     const uint16_t* ka = baseA + k0;
     const uint16_t* kb = bsrc(k0);
     constexpr int G = 4 * NJ;   // MFMA groups per phase
+    constexpr int XBAR = 2;     // group of the last phase that holds the barrier
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int cur = q & 1, nxt = cur ^ 1;
@@ -686,7 +688,7 @@ __device__ __forceinline__ void gemm_nt_tile(const uint16_t* __restrict__ A,
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         const int i = g / NJ, j = g % NJ;
-        if (q == 3 && g == G / 2) {
+        if (q == 3 && g == XBAR) {
           // this wave's reads of stage S are complete and its DMA of stage SN
           // has landed; after the barrier both hold for every wave, so the
           // rest of the phase reads the next stage's first slice and the next
@@ -697,11 +699,11 @@ __device__ __forceinline__ void gemm_nt_tile(const uint16_t* __restrict__ A,
         if (q < 3) {
           if (g < 4) fa[nxt][g] = as_bf16x8(At[a_row[g] + cq[q + 1]]);
           else if (g < 4 + NJ) fb[nxt][g - 4] = as_bf16x8(Bt[b_row[g - 4] + cq[q + 1]]);
-        } else if (g >= G / 2) {
-          // 4 + NJ reads over the last G / 2 groups
+        } else if (g >= XBAR) {
+          // 4 + NJ reads over the groups after the barrier
 #pragma unroll
           for (int t = 0; t < 4 + NJ; ++t) {
-            if (t * (G / 2) / (4 + NJ) != g - G / 2) continue;
+            if (t * (G - XBAR) / (4 + NJ) != g - XBAR) continue;
             if (t < 4) fa[nxt][t] = as_bf16x8(An[a_row[t] + cq[0]]);
             else fb[nxt][t - 4] = as_bf16x8(Bn[b_row[t - 4] + cq[0]]);
           }
