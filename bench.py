@@ -41,7 +41,7 @@ METRIC = "tokens/s mixed-adapter LoRA fwd+bwd at 8B shapes; % MFMA / HBM peak"
 # WRITE_SIZE passes scaled by a 512 MiB copy's readings (x2 fetch, x1 write):
 # profiles/gemm_nt_traffic_8192x4096x4096.md.  Valid only for the kernel source the
 # counters were taken on (sha256 prefix of gemm.hip + common.hpp); else reported null.
-GEMM_TRAFFIC = {"bytes_per_launch": 476.7e6, "src_sha256": "d23cf46ad1f077a0"}
+GEMM_TRAFFIC = {"bytes_per_launch": 476.6e6, "src_sha256": "24e916bb20ed11bf"}
 
 
 def gemm_traffic():
